@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs for the KDA forward and decode workloads.
+
+This module only draws random numbers and rounds them to the I/O dtype; it holds
+none of the method's arithmetic.  The tests feed the very same tensors to the
+HIP library and to the fp64 oracle, and the benchmark uses the same recipes.
+
+Recipe (per token and head unless stated):
+  * q, k ~ N(0, 1), L2-normalised over d_k, then rounded to the I/O dtype (RNE);
+  * v ~ N(0, 1);
+  * beta = sigmoid(N(0, 1));
+  * log_alpha = -softplus(N(0, 1)) per channel ("softplus" gate), or
+    log(U(0.5, 0.9999)) per channel ("uniform" gate: per-channel decay between
+    0.5 and 0.9999), or the same uniform draw held constant over time per
+    (head, channel) ("uniform_const", the long-memory variant);
+  * h0 = N(0, 0.1^2) per sequence when requested, else absent (zeros);
+  * varlen lengths are integers drawn uniformly from [lo, hi] inclusive.
+Draw order for one call: lengths, q, k, v, beta, log_alpha, h0.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class ChunkConfig:
+    name: str
+    io: str            # "f32" or "bf16": dtype of q, k, v, o
+    gate_io: str       # dtype of log_alpha and beta
+    H: int
+    dk: int
+    dv: int
+    T: int = 0         # tokens per sequence when lengths is None
+    B: int = 1         # equal-length sequences (packed into one batch)
+    lengths: Optional[tuple] = None   # (count, lo, hi): varlen batch
+    gate: str = "softplus"
+    h0: bool = False
+    seed: int = 1000
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    io: str
+    gate_io: str
+    B: int
+    H: int
+    dk: int
+    dv: int
+    steps: int
+    seed: int = 2000
+
+
+# The five workloads of the path.
+C0 = ChunkConfig("fp32 B=1 H=2 T=256 d=64", "f32", "f32", H=2, dk=64, dv=64, T=256, seed=1000)
+C1 = ChunkConfig("bf16 B=1 H=16 T=4096 d=128", "bf16", "bf16", H=16, dk=128, dv=128, T=4096,
+                 seed=1001)
+C2 = ChunkConfig("bf16 varlen N=32 L~U[512,8192] H=32 d=128 h0~N(0,0.1)", "bf16", "bf16", H=32,
+                 dk=128, dv=128, lengths=(32, 512, 8192), h0=True, seed=1002)
+C3 = ChunkConfig("bf16 B=1 H=32 T=65536 d=128 decay U(0.5,0.9999)", "bf16", "bf16", H=32,
+                 dk=128, dv=128, T=65536, gate="uniform", seed=1003)
+C4 = DecodeConfig("decode bf16 B=256 H=32 d=128 fp32 S~N(0,0.1)", "bf16", "bf16", B=256, H=32,
+                  dk=128, dv=128, steps=1000, seed=2000)
+CHUNK_CONFIGS = {"c0": C0, "c1": C1, "c2": C2, "c3": C3}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, g, device):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def _unit_rows(x):
+    return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+
+
+def draw_gate(shape, gate: str, g, device):
+    """log_alpha draws (fp32, all <= 0)."""
+    if gate == "softplus":
+        return -torch.nn.functional.softplus(_randn(shape, g, device))
+    if gate == "uniform":
+        u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+        return torch.log(0.5 + u * (0.9999 - 0.5))
+    if gate == "uniform_const":
+        T = shape[0]
+        u = torch.rand((1,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32)
+        return torch.log(0.5 + u * (0.9999 - 0.5)).expand((T,) + tuple(shape[1:])).contiguous()
+    raise ValueError("unknown gate " + gate)
+
+
+def seq_lengths(cfg: ChunkConfig, g=None, device="cpu"):
+    if cfg.lengths is None:
+        return [cfg.T] * cfg.B
+    n, lo, hi = cfg.lengths
+    if g is None:
+        g = _gen(cfg.seed, device)
+    return torch.randint(lo, hi + 1, (n,), generator=g, device=device).tolist()
+
+
+def make_chunk_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None,
+                      lengths: Optional[list] = None, gate: Optional[str] = None,
+                      h0: Optional[bool] = None):
+    """Returns a dict with q, k, v, log_alpha, beta, h0 (or None), cu_seqlens
+    (int32, on `device`), lengths (list) -- all contiguous, packed as [T_total, H, d]."""
+    seed = cfg.seed if seed is None else seed
+    g = _gen(seed, device)
+    if lengths is None:
+        lengths = seq_lengths(cfg, g, device)
+    gate = cfg.gate if gate is None else gate
+    want_h0 = cfg.h0 if h0 is None else h0
+    T = int(sum(lengths))
+    H, dk, dv = cfg.H, cfg.dk, cfg.dv
+    io, gio = _DT[cfg.io], _DT[cfg.gate_io]
+    q = _unit_rows(_randn((T, H, dk), g, device)).to(io)
+    k = _unit_rows(_randn((T, H, dk), g, device)).to(io)
+    v = _randn((T, H, dv), g, device).to(io)
+    beta = torch.sigmoid(_randn((T, H), g, device)).to(gio)
+    la = draw_gate((T, H, dk), gate, g, device).to(gio)
+    h0_t = None
+    if want_h0:
+        h0_t = (0.1 * _randn((len(lengths), H, dk, dv), g, device)).contiguous()
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, h0=h0_t,
+                cu_seqlens=cu.to(torch.int32).to(device), lengths=list(lengths))
+
+
+def make_decode_state(cfg: DecodeConfig, device="cpu", seed: Optional[int] = None):
+    g = _gen(cfg.seed if seed is None else seed, device)
+    return (0.1 * _randn((cfg.B, cfg.H, cfg.dk, cfg.dv), g, device)).contiguous()
+
+
+def make_decode_step_inputs(cfg: DecodeConfig, step: int, device="cpu", steps: int = 1):
+    """Inputs of `steps` consecutive decode steps starting at `step`, stacked on a
+    leading axis: q, k, log_alpha [steps, B, H, dk]; v [steps, B, H, dv];
+    beta [steps, B, H].  Each step s is drawn from its own seed (cfg.seed + 1 + s)."""
+    io, gio = _DT[cfg.io], _DT[cfg.gate_io]
+    B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
+    out = {n: [] for n in ("q", "k", "v", "beta", "log_alpha")}
+    for s in range(step, step + steps):
+        g = _gen(cfg.seed + 1 + s, device)
+        out["q"].append(_unit_rows(_randn((B, H, dk), g, device)).to(io))
+        out["k"].append(_unit_rows(_randn((B, H, dk), g, device)).to(io))
+        out["v"].append(_randn((B, H, dv), g, device).to(io))
+        out["beta"].append(torch.sigmoid(_randn((B, H), g, device)).to(gio))
+        out["log_alpha"].append(draw_gate((B, H, dk), "softplus", g, device).to(gio))
+    return {n: torch.stack(xs).contiguous() for n, xs in out.items()}

@@ -1,0 +1,207 @@
+/*
+ * kda_oracle.c -- plain fp64 CPU oracle for Kimi Delta Attention (KDA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this library.  The product path (the HIP
+ * library under gated_delta_rule_chunkwise_amd/) never links, loads or calls
+ * it, and this file shares no code, header or table with that path.
+ *
+ * What it computes (one independent chain per (sequence, head)):
+ *
+ *   KimiLinear article (intl.cloud.baidu.com), section 2.3 "KDA's
+ *   Fine-Grained Gating Design": the state is decayed by a per-dimension gate
+ *   vector a_t that acts on the rows of the state (one forgetting rate per key
+ *   feature), then corrected by the delta rule of section 2.1 with strength
+ *   beta_t.  Section 2.1 gives the delta-rule erase and write with the same
+ *   scalar beta_t.  The pages print the write term as v k^T, which only type-
+ *   checks with the identity operator on the left when d_k = d_v; with the gate
+ *   on rows the state is d_k x d_v and the write term is k v^T (reading of the
+ *   garbled orientation).  The read-out is not on the pages; the reading taken
+ *   is o_t = S_t^T q_t, inclusive of token t, with no scale.
+ *
+ *   Per token, in this order:
+ *       S <- Diag(exp(log_alpha_t)) S                     (decay first)
+ *       S <- S - b_t k_t (k_t^T S) + w_t k_t v_t^T         (erase, write)
+ *       o_t <- S^T q_t
+ *   KDA is b_t = w_t = beta_t.  The generalised form with separate erase and
+ *   write strengths (b_t, w_t) is the decoupled-gate variant that the Kimi
+ *   Linear CoChat record quotes from citing papers ("Claims other papers make
+ *   about this one"); it is kept here only so that a test can pin the pure
+ *   linear-attention form of section 2.1 (b = 0, w = 1, a = 1) exactly.
+ *
+ * Everything is fp64, with plain loops and no BLAS, no blocking and no
+ * reordering beyond the three steps above.  Chains run in parallel threads;
+ * each chain is computed by exactly one thread, so the result does not depend
+ * on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Layouts (all row-major, contiguous):
+ *   q, k, log_alpha : [T_total, H, dk]
+ *   v               : [T_total, H, dv]
+ *   b_erase, w_write: [T_total, H]
+ *   h0, hT          : [N, H, dk, dv]   (h0 may be NULL: zero initial state)
+ *   o               : [T_total, H, dv]
+ *   cu_seqlens      : [N + 1], cu_seqlens[0] = 0, non-decreasing
+ */
+typedef struct {
+    const double *q, *k, *v, *log_alpha, *b_erase, *w_write, *h0;
+    const int64_t *cu_seqlens;
+    int64_t num_seqs, H, dk, dv;
+    double *o, *hT;
+    int64_t next_chain;           /* shared work counter, guarded by mu */
+    pthread_mutex_t mu;
+    int failed;
+} oracle_job;
+
+/* Runs one (sequence, head) chain token by token. Returns 0 or -1 (no memory). */
+static int run_chain(const oracle_job *J, int64_t n, int64_t h)
+{
+    const int64_t H = J->H, dk = J->dk, dv = J->dv;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+    double *kS = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!S || !kS) { free(S); free(kS); return -1; }
+
+    if (J->h0) memcpy(S, J->h0 + (n * H + h) * dk * dv, sizeof(double) * (size_t)(dk * dv));
+    else memset(S, 0, sizeof(double) * (size_t)(dk * dv));
+
+    for (int64_t t = J->cu_seqlens[n]; t < J->cu_seqlens[n + 1]; ++t) {
+        const double *qt = J->q + (t * H + h) * dk;
+        const double *kt = J->k + (t * H + h) * dk;
+        const double *vt = J->v + (t * H + h) * dv;
+        const double *lat = J->log_alpha + (t * H + h) * dk;
+        const double bt = J->b_erase[t * H + h];
+        const double wt = J->w_write[t * H + h];
+
+        /* decay: row c of S is scaled by a_t[c] = exp(log_alpha_t[c]) */
+        for (int64_t c = 0; c < dk; ++c) {
+            const double a = exp(lat[c]);
+            for (int64_t j = 0; j < dv; ++j) S[c * dv + j] *= a;
+        }
+        /* erase and write: S += k (w v - b k^T S)^T */
+        for (int64_t j = 0; j < dv; ++j) kS[j] = 0.0;
+        for (int64_t c = 0; c < dk; ++c)
+            for (int64_t j = 0; j < dv; ++j) kS[j] += kt[c] * S[c * dv + j];
+        for (int64_t c = 0; c < dk; ++c)
+            for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += kt[c] * (wt * vt[j] - bt * kS[j]);
+        /* read-out: o_t = S^T q_t */
+        double *ot = J->o + (t * H + h) * dv;
+        for (int64_t j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < dk; ++c) acc += qt[c] * S[c * dv + j];
+            ot[j] = acc;
+        }
+    }
+    if (J->hT) memcpy(J->hT + (n * H + h) * dk * dv, S, sizeof(double) * (size_t)(dk * dv));
+    free(S);
+    free(kS);
+    return 0;
+}
+
+static void *worker(void *arg)
+{
+    oracle_job *J = (oracle_job *)arg;
+    const int64_t total = J->num_seqs * J->H;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        const int64_t id = J->next_chain++;
+        pthread_mutex_unlock(&J->mu);
+        if (id >= total) break;
+        if (run_chain(J, id / J->H, id % J->H) != 0) {
+            pthread_mutex_lock(&J->mu);
+            J->failed = 1;
+            pthread_mutex_unlock(&J->mu);
+        }
+    }
+    return NULL;
+}
+
+static int run_all(oracle_job *J, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 1024) nthreads = 1024;
+    pthread_mutex_init(&J->mu, NULL);
+    J->next_chain = 0;
+    J->failed = 0;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid) return -1;
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, worker, J) != 0) break;
+        ++started;
+    }
+    if (started == 0) worker(J); /* no thread could start: run inline */
+    for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+    free(tid);
+    pthread_mutex_destroy(&J->mu);
+    return J->failed ? -1 : 0;
+}
+
+static int check_seqlens(const int64_t *cu, int64_t N)
+{
+    if (!cu || N < 0) return -2;
+    if (cu[0] != 0) return -2;
+    for (int64_t n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n]) return -2;
+    return 0;
+}
+
+/* Generalised recurrence (separate erase strength b and write strength w).
+ * Returns 0 on success, -1 on allocation failure, -2 on bad arguments. */
+int kda_oracle_gen_fwd(const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *b_erase,
+                       const double *w_write, const double *h0,
+                       const int64_t *cu_seqlens, int64_t num_seqs, int64_t H,
+                       int64_t dk, int64_t dv, double *o, double *hT,
+                       int nthreads)
+{
+    if (H <= 0 || dk <= 0 || dv <= 0) return -2;
+    if (check_seqlens(cu_seqlens, num_seqs) != 0) return -2;
+    if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !log_alpha || !b_erase || !w_write || !o))
+        return -2;
+    oracle_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha;
+    J.b_erase = b_erase; J.w_write = w_write; J.h0 = h0;
+    J.cu_seqlens = cu_seqlens; J.num_seqs = num_seqs; J.H = H; J.dk = dk; J.dv = dv;
+    J.o = o; J.hT = hT;
+    return run_all(&J, nthreads);
+}
+
+/* KDA forward over a packed batch: the generalised recurrence with
+ * b_t = w_t = beta_t. */
+int kda_oracle_fwd(const double *q, const double *k, const double *v,
+                   const double *log_alpha, const double *beta, const double *h0,
+                   const int64_t *cu_seqlens, int64_t num_seqs, int64_t H,
+                   int64_t dk, int64_t dv, double *o, double *hT, int nthreads)
+{
+    return kda_oracle_gen_fwd(q, k, v, log_alpha, beta, beta, h0, cu_seqlens,
+                              num_seqs, H, dk, dv, o, hT, nthreads);
+}
+
+/* One recurrent decode step for B independent sequences: every sequence is a
+ * chain of length one whose initial state is S[b]; S is overwritten with the
+ * new state.  q, k, log_alpha: [B, H, dk]; v: [B, H, dv]; beta: [B, H];
+ * S: [B, H, dk, dv] (in/out); o: [B, H, dv]. */
+int kda_oracle_decode(const double *q, const double *k, const double *v,
+                      const double *log_alpha, const double *beta, double *S,
+                      int64_t B, int64_t H, int64_t dk, int64_t dv, double *o,
+                      int nthreads)
+{
+    if (B < 0 || !S) return -2;
+    int64_t *cu = (int64_t *)malloc(sizeof(int64_t) * (size_t)(B + 1));
+    double *S_out = (double *)malloc(sizeof(double) * (size_t)(B * H * dk * dv + 1));
+    if (!cu || !S_out) { free(cu); free(S_out); return -1; }
+    for (int64_t b = 0; b <= B; ++b) cu[b] = b;
+    int rc = kda_oracle_fwd(q, k, v, log_alpha, beta, S, cu, B, H, dk, dv, o, S_out, nthreads);
+    if (rc == 0) memcpy(S, S_out, sizeof(double) * (size_t)(B * H * dk * dv));
+    free(cu);
+    free(S_out);
+    return rc;
+}
+
+int kda_oracle_version(void) { return 1; }
