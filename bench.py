@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One "step" is one kda_chunk_fwd call over the long-context prefill workload
+(bf16, B=1, H=32, T=65536, d_k=d_v=128, chunk 64, per-channel decay in
+[0.5, 0.9999]); inputs are seeded, synthetic and resident in HBM before timing.
+The decode step (B=256 resident fp32 states, H=32, d=128, 1000 steps with fresh
+inputs) is timed in the same run and reported under "decode".
+
+Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix peak, published
+METRIC = "KDA chunk_fwd tokens/s + % MFMA peak; decode step HBM GB/s (1×MI355X)"
+
+
+def chunk_alg_bytes(tok_heads, n_states, dk, dv, io_b=2, gate_b=2):
+    """Algorithmic HBM bytes of one chunk_fwd launch: q, k, log_alpha (d_k each),
+    v and o (d_v each), beta (1) per token-head, plus h_T (and h0) per state."""
+    per = 2 * dk * io_b + dk * gate_b + 2 * dv * io_b + gate_b
+    return tok_heads * per + n_states * dk * dv * 4
+
+
+def chunk_alg_flops(tok_heads, dk, dv, C=64):
+    """Algorithmic flops per token-head (triangles counted as triangles):
+    A and P Gram blocks, the UT transform, U, the three state products and P.U."""
+    per = 2 * ((C - 1) / 2 * dk + (C + 1) / 2 * dk + C * C / 6 + (C - 1) / 2 * (dk + dv)
+               + 3 * dk * dv + (C + 1) / 2 * dv)
+    return tok_heads * per
+
+
+def decode_alg_bytes(B, H, dk, dv, io_b=2, gate_b=2):
+    per_state = 2 * dk * dv * 4 + (2 * dk + 2 * dv) * io_b + dk * gate_b + gate_b
+    return B * H * per_state
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("kda_chunk.hip", "kda_device.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_chunkwise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, digest):
+    """Counter-measured HBM bytes per launch, from a committed rocprofv3 summary;
+    None when absent or when the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, stream):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return per, wall
+
+
+def cpu_baseline_chunk(d, heads, T_sample, H_total):
+    """Times the fp64 oracle (as it stands) on host cores on a bounded sample of
+    the same workload: `heads` whole chains over the first T_sample tokens."""
+    import oracle
+    oracle.build(force=False)
+    sl = slice(0, T_sample)
+    f = lambda x: x[sl][:, :heads].to("cpu", torch.float64).numpy()
+    q, k, v, la, be = (np.ascontiguousarray(f(d[x])) for x in ("q", "k", "v", "log_alpha", "beta"))
+    nthreads = min(heads, oracle.default_threads())
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, la, be, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    tok_heads = heads * T_sample
+    return {"value": tok_heads / H_total / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": "fp64 per-token recurrence, %d heads x first %d tokens of the same inputs "
+                      "(%d token-heads, %.1f s); tokens/s = token-heads/s / %d heads"
+                      % (heads, T_sample, tok_heads, dt, H_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import gated_delta_rule_chunkwise_amd as kda
+    from gated_delta_rule_chunkwise_amd import inputs as I
+    kda.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- chunk_fwd on the long-context prefill workload
+    cfg = I.C3
+    d = I.make_chunk_inputs(cfg, device=dev)
+    T, H, dk, dv = sum(d["lengths"]), cfg.H, cfg.dk, cfg.dv
+    o = torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
+    args_c = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
+    fn = lambda: kda.kda_chunk_fwd(*args_c, o=o, h_T=hT)
+    per, wall = time_launches(fn, args.steps, args.warmup, stream)
+    ms = float(np.mean(per))
+    print("chunk_fwd per-launch ms: mean %.4f median %.4f min %.4f" % (ms, np.median(per), min(per)),
+          file=sys.stderr, flush=True)
+    tok_heads = T * H
+    alg_b = chunk_alg_bytes(tok_heads, H, dk, dv)
+    alg_f = chunk_alg_flops(tok_heads, dk, dv)
+    digest = source_digest()
+    traffic = load_traffic("chunk_fwd_kernel_c3_traffic.json", digest)
+    roof = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "chunk_fwd_kernel<128,16,bf16,bf16>", "alg_bytes_per_launch": alg_b}
+    mfma = {"alg_flops_per_launch": alg_f, "achieved_tflops": alg_f / (ms * 1e-3) / 1e12,
+            "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+            "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+
+    out = {"metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "kda_chunk_fwd bf16 B=1 H=32 T=65536 d_k=d_v=128 chunk=64, "
+                                  "log_alpha=log U(0.5,0.9999)",
+                      "B": 1, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": 64,
+                      "parallelism": "single GPU"},
+           "roofline": roof, "mfma": mfma, "source_digest": digest}
+
+    # ---------------- decode step
+    if not args.no_decode:
+        dcfg = I.C4
+        S = I.make_decode_state(dcfg, device=dev)
+        nst = args.decode_steps
+        xs = I.make_decode_step_inputs(dcfg, 0, device=dev, steps=nst)
+        od = torch.empty((dcfg.B, dcfg.H, dcfg.dv), dtype=torch.bfloat16, device=dev)
+        names = ("q", "k", "v", "log_alpha", "beta")
+        for s in range(min(3, nst)):
+            kda.kda_decode_step(*(xs[n][s] for n in names), S, o=od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(nst):
+            kda.kda_decode_step(*(xs[n][s] for n in names), S, o=od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / nst
+        db = decode_alg_bytes(dcfg.B, dcfg.H, dcfg.dk, dcfg.dv)
+        gbs = db / (dms * 1e-3) / 1e9
+        out["decode"] = {"workload": "kda_decode_step bf16 B=256 H=32 d=128 fp32 S (512 MiB), "
+                                     "%d steps with fresh inputs" % nst,
+                         "ms_per_step": dms, "tokens_per_s": dcfg.B / (dms * 1e-3),
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                      "traffic": load_traffic("decode_step_kernel_c4_traffic.json",
+                                                              digest),
+                                      "alg_bytes_per_launch": db}}
+        del xs, S
+
+    # ---------------- CPU baseline: the oracle on a bounded sample
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_chunk(d, args.cpu_heads, args.cpu_tokens, H)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+"""libkda Python binding: Kimi Delta Attention forward on MI355X (gfx950).
+
+A thin ctypes layer over the C ABI declared in ``include/kda.h``.  It only
+marshals torch tensors (device memory and the current HIP stream) into the C
+calls; every step of the computation runs in the HIP kernels of ``libkda.so``.
+There is no fallback: if the library is missing or fails to load, every entry
+point raises.
+
+Entry points (same names as the C ABI):
+    kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, ...)
+    kda_decode_step(q, k, v, log_alpha, beta, S, o=None)
+    kda_chunk_fwd_workspace_size(...), kda_status_string(code), kda_abi_version()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
+                    "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str = ""):
+        self.code = code
+        msg = "%s failed: %s" % (where, kda_status_string(code))
+        if detail:
+            msg += " (%s)" % detail
+        super().__init__(msg)
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libkda.so and declares the C signatures.  Raises OSError if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError("libkda.so is not built (%s); run "
+                      "`python -m gated_delta_rule_chunkwise_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = i32
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_hip_error.argtypes = []
+    lib.kda_last_hip_error.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                  ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                    ctypes.c_int, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def kda_abi_version() -> int:
+    return int(load_library().kda_abi_version())
+
+
+def kda_status_string(code: int) -> str:
+    return load_library().kda_status_string(int(code)).decode()
+
+
+def kda_last_hip_error() -> str:
+    return load_library().kda_last_hip_error().decode()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_of(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_dev(name, t, device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, num_seqs=0, io_dtype=KDA_BF16) -> int:
+    return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, num_seqs, io_dtype))
+
+
+def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None, h_T=None,
+                  output_final_state=True, workspace=None):
+    """Chunkwise KDA forward.
+
+    q, k, log_alpha: [B, T, H, d_k] (or [T, H, d_k] for B = 1); v: [B, T, H, d_v];
+    beta: [B, T, H]; h0: [N, H, d_k, d_v] fp32 or None; cu_seqlens: int32 [N+1]
+    on the device (B must be 1) or None.  Returns (o, h_T) with h_T None when
+    output_final_state is False.  Runs asynchronously on the current stream.
+    """
+    import torch
+    lib = load_library()
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v, log_alpha, beta = (x.unsqueeze(0) for x in (q, k, v, log_alpha, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _check_dev(name, t, dev)
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:3] != (B, T, H) \
+            or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch among q, k, v, log_alpha, beta")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != log_alpha.dtype:
+        raise TypeError("q, k, v share one dtype; log_alpha and beta share one dtype")
+    if cu_seqlens is not None:
+        _check_dev("cu_seqlens", cu_seqlens, dev)
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if h0 is not None:
+        _check_dev("h0", h0, dev)
+        if h0.dtype != torch.float32 or tuple(h0.shape) != (N, H, dk, dv):
+            raise ValueError("h0 must be fp32 [N, H, d_k, d_v]")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if h_T is None and output_final_state:
+        h_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    io, gt = _dtype_code(q), _dtype_code(log_alpha)
+    ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, N if cu_seqlens is not None else 0, io)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                           _ptr(cu_seqlens), N if cu_seqlens is not None else 0, _ptr(o), _ptr(h_T),
+                           B, T, H, dk, dv, io, gt, _ptr(workspace),
+                           0 if workspace is None else workspace.numel() * workspace.element_size(),
+                           _stream_of(q))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_fwd", kda_last_hip_error())
+    if squeeze:
+        o = o.squeeze(0)
+    return o, h_T
+
+
+def kda_decode_step(q, k, v, log_alpha, beta, S, o=None):
+    """One decode step.  q, k, log_alpha: [B, H, d_k]; v: [B, H, d_v];
+    beta: [B, H]; S: [B, H, d_k, d_v] fp32, updated in place.  Returns o."""
+    import torch
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("S", S)):
+        _check_dev(name, t, dev)
+    if S.dtype != torch.float32 or tuple(S.shape) != (B, H, dk, dv):
+        raise ValueError("S must be fp32 [B, H, d_k, d_v]")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                             _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha),
+                             _stream_of(q))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_decode_step", kda_last_hip_error())
+    return o
+
+
+chunk_fwd = kda_chunk_fwd
+decode_step = kda_decode_step

@@ -1,0 +1,127 @@
+// Host side of the libkda C ABI: argument validation, status strings and
+// dispatch to the HIP launchers.  Every check here runs before any HIP call,
+// so invalid arguments never reach the device.
+#include "kda.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_hip_error[512] = "";
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool supported_dim(int32_t d) { return d == 64 || d == 128; }
+bool valid_dtype(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
+uintptr_t dsize(kda_dtype_t t) { return t == KDA_F32 ? 4 : 2; }
+
+// Products of the sizes must stay well inside int64 for device indexing.
+bool sizes_fit(int64_t a, int64_t b, int64_t c) {
+    const int64_t lim = (int64_t)1 << 50;
+    if (a > lim || b > lim || c > lim) return false;
+    if (a != 0 && b > lim / a) return false;
+    if (a * b != 0 && c > lim / (a * b)) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return 1; }
+
+const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char *kda_last_hip_error(void) { return g_hip_error; }
+
+size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                    int32_t num_seqs, kda_dtype_t io_dtype) {
+    (void)io_dtype;
+    if (B <= 0 || T < 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
+    const int64_t n = num_seqs > 0 ? num_seqs : B;
+    return kda::chunk_fwd_workspace_bytes((int64_t)B * T, H, d_k, d_v, n);
+}
+
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *beta, const float *h0, const int32_t *cu_seqlens,
+                           int32_t num_seqs, void *o, float *h_T, int32_t B, int32_t T,
+                           int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                           kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (!sizes_fit((int64_t)B * T, H, (d_k > d_v ? d_k : d_v))) return KDA_ERR_INVALID_ARGUMENT;
+    int64_t N;
+    if (cu_seqlens) {
+        if (B != 1 || num_seqs <= 0) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned_to(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
+        N = num_seqs;
+    } else {
+        if (num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARGUMENT;
+        N = B;
+    }
+    if (!sizes_fit(N, H, (int64_t)d_k * d_v)) return KDA_ERR_INVALID_ARGUMENT;
+    const bool have_tokens = (int64_t)B * T > 0;
+    if (have_tokens) {
+        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+            !aligned16(o))
+            return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned_to(beta, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((h0 && !aligned16(h0)) || (h_T && !aligned16(h_T))) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t need = kda::chunk_fwd_workspace_bytes((int64_t)B * T, H, d_k, d_v, N);
+    if (need > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!have_tokens && !h_T) return KDA_OK;  // nothing to compute or write
+
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+    a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
+    a.num_seqs = N; a.seq_len = T; a.total_tokens = (int64_t)B * T;
+    a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    g_hip_error[0] = '\0';
+    if (kda::launch_chunk_fwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
+                             const void *beta, float *S, void *o, int32_t B, int32_t H,
+                             int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                             kda_dtype_t gate_dtype, void *stream) {
+    if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (!sizes_fit(B, H, (int64_t)d_k * d_v)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+        !aligned16(S) || !aligned16(o))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned_to(beta, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S; a.o = o;
+    a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
+    g_hip_error[0] = '\0';
+    if (kda::launch_decode_step(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// kda_decode.hip -- one recurrent KDA step over B*H resident states (decode).
+//
+// Per (b, h) and every value column j (columns evolve independently):
+//   s_j <- alpha (.) s_j                      (per-row decay; KimiLinear article, sec. 2.3)
+//   u_j  = beta (v_j - k^T s_j)               (delta-rule correction, sec. 2.1)
+//   s_j <- s_j + u_j k                        (write)
+//   o_j  = q^T s_j                            (read-out, inclusive of this token)
+// Both reductions are taken on the decayed column a_j = k^T (alpha.s_j),
+// b_j = q^T (alpha.s_j), so o_j = b_j + u_j (q.k) and the state is read once and
+// written once.  The kernel is bound by HBM bandwidth: S is 4*d_k*d_v bytes per
+// (b, h) each way, everything else is O(d).
+#include "kda_device.h"
+#include "kda_launch.h"
+
+#include <stdio.h>
+
+namespace kda {
+namespace {
+
+constexpr int kDecodeThreads = 256;
+
+template <int DK, int DV, typename IO, typename GT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, float *__restrict__ S,
+    IO *__restrict__ o) {
+    constexpr int NCG = DV / 4;                 // groups of 4 value columns
+    constexpr int NRG = kDecodeThreads / NCG;   // row groups
+    constexpr int RPT = DK / NRG;               // key rows per thread
+    static_assert(RPT >= 1 && RPT * NRG == DK, "bad decode tiling");
+
+    __shared__ float red[NRG][NCG][8];
+    __shared__ float red_qk[NRG];
+
+    const int64_t bh = blockIdx.x;
+    const int t = threadIdx.x;
+    const int cg = t % NCG, rg = t / NCG;
+    const int row0 = rg * RPT;
+
+    float *Sp = S + bh * (int64_t)(DK * DV) + 4 * cg;
+    float4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const float4 *>(Sp + (row0 + i) * DV);
+
+    float kk[RPT], qq[RPT], al[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        kk[i] = to_f32(k[bh * DK + row0 + i]);
+        qq[i] = to_f32(q[bh * DK + row0 + i]);
+        al[i] = __expf(to_f32(log_alpha[bh * DK + row0 + i]));
+    }
+
+    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f}, pqk = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        s[i].x *= al[i]; s[i].y *= al[i]; s[i].z *= al[i]; s[i].w *= al[i];
+        pa[0] += kk[i] * s[i].x; pa[1] += kk[i] * s[i].y; pa[2] += kk[i] * s[i].z; pa[3] += kk[i] * s[i].w;
+        pb[0] += qq[i] * s[i].x; pb[1] += qq[i] * s[i].y; pb[2] += qq[i] * s[i].z; pb[3] += qq[i] * s[i].w;
+        pqk += qq[i] * kk[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        red[rg][cg][j] = pa[j];
+        red[rg][cg][4 + j] = pb[j];
+    }
+    if (cg == 0) red_qk[rg] = pqk;
+    __syncthreads();
+
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRG; ++r) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[j] += red[r][cg][j];
+            b[j] += red[r][cg][4 + j];
+        }
+        qk += red_qk[r];
+    }
+    const float bt = to_f32(beta[bh]);
+    float u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = bt * (to_f32(v[bh * DV + 4 * cg + j]) - a[j]);
+
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        float4 r;
+        r.x = s[i].x + kk[i] * u[0];
+        r.y = s[i].y + kk[i] * u[1];
+        r.z = s[i].z + kk[i] * u[2];
+        r.w = s[i].w + kk[i] * u[3];
+        *reinterpret_cast<float4 *>(Sp + (row0 + i) * DV) = r;
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[bh * DV + 4 * cg + j] = from_f32<IO>(b[j] + u[j] * qk);
+    }
+}
+
+template <int DK, int DV, typename IO, typename GT>
+hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
+    const int64_t nb = a.B * (int64_t)a.H;
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT>), dim3((unsigned)nb), dim3(kDecodeThreads),
+                       0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+                       (const GT *)a.log_alpha, (const GT *)a.beta, a.S, (IO *)a.o);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const DecodeArgs &a, hipStream_t st) {
+    if (a.io_bf16) {
+        return a.gate_bf16 ? launch_t<DK, DV, bf16_t, bf16_t>(a, st) : launch_t<DK, DV, bf16_t, float>(a, st);
+    }
+    return a.gate_bf16 ? launch_t<DK, DV, float, bf16_t>(a, st) : launch_t<DK, DV, float, float>(a, st);
+}
+
+}  // namespace
+
+int launch_decode_step(const DecodeArgs &a, void *stream, char *err, size_t err_len) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (a.B * (int64_t)a.H > 0x7fffffffLL) {
+        snprintf(err, err_len, "decode grid too large");
+        return -1;
+    }
+    hipError_t e;
+    if (a.d_k == 128 && a.d_v == 128) e = launch_dims<128, 128>(a, st);
+    else if (a.d_k == 128 && a.d_v == 64) e = launch_dims<128, 64>(a, st);
+    else if (a.d_k == 64 && a.d_v == 128) e = launch_dims<64, 128>(a, st);
+    else e = launch_dims<64, 64>(a, st);
+    if (e != hipSuccess) {
+        snprintf(err, err_len, "%s", hipGetErrorString(e));
+        return -1;
+    }
+    return 0;
+}
+
+}  // namespace kda

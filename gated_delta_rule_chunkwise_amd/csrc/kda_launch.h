@@ -1,0 +1,40 @@
+// Internal interface between the host-side C ABI (kda_api.cpp) and the HIP
+// launchers (kda_chunk.hip, kda_decode.hip).  Not part of the public ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkArgs {
+    const void *q, *k, *v, *log_alpha, *beta;
+    const float *h0;
+    const int32_t *cu_seqlens;  // device, or nullptr (equal-length batch)
+    void *o;
+    float *h_T;
+    int64_t num_seqs;           // N
+    int64_t seq_len;            // T when cu_seqlens == nullptr
+    int64_t total_tokens;       // B*T
+    int32_t H, d_k, d_v;
+    int32_t io_bf16, gate_bf16; // 1 = bf16, 0 = fp32
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v, *log_alpha, *beta;
+    float *S;
+    void *o;
+    int64_t B;
+    int32_t H, d_k, d_v;
+    int32_t io_bf16, gate_bf16;
+};
+
+// Both return 0 when the launch was enqueued, or -1 after a HIP error whose
+// text is copied into err (err_len bytes, NUL-terminated).
+int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len);
+int launch_decode_step(const DecodeArgs &a, void *stream, char *err, size_t err_len);
+size_t chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t H, int32_t d_k, int32_t d_v,
+                                 int64_t num_seqs);
+
+}  // namespace kda

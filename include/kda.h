@@ -1,0 +1,137 @@
+/*
+ * kda.h -- C ABI of libkda: Kimi Delta Attention (KDA) forward on MI355X (gfx950).
+ *
+ * KDA is the gated delta rule with a per-channel (diagonal) forget gate.  Per
+ * (sequence, head) chain the state S is d_k x d_v; for each token t:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * Source: KimiLinear article (intl.cloud.baidu.com), section 2.3 (update with a
+ * per-dimension gate vector acting on the rows of the state) and section 2.1
+ * (delta-rule erase and write).  The pages print the write term as v k^T; with
+ * the gate on rows the state is d_k x d_v and the write is k v^T.  The read-out
+ * o_t = S_t^T q_t (inclusive of token t, no scale, no normalisation, no output
+ * gate) is not on the pages; it is the reading this library implements.
+ * alpha_t = exp(log_alpha_t) is passed in log form.
+ *
+ * Conventions for every call:
+ *  - All tensors are caller-owned DEVICE memory, contiguous and row-major with
+ *    the shapes given below; base pointers must be 16-byte aligned, except beta
+ *    and cu_seqlens, which need only their natural alignment.  The library never
+ *    allocates, frees or retains a pointer, and keeps no global mutable state.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ *    the legacy default stream).  KDA_OK means "validated and enqueued".
+ *  - Every argument check runs on the host before any HIP call; on error nothing
+ *    is enqueued and no memory is touched.  Device-resident values (cu_seqlens,
+ *    tensor contents) are not read by the host and are trusted: see the
+ *    preconditions of each call.
+ *  - Outputs must not alias inputs, except where a call says otherwise.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad size, misalignment */
+    KDA_ERR_UNSUPPORTED = 2,      /* d_k or d_v not in {64, 128}, unknown dtype    */
+    KDA_ERR_WORKSPACE = 3,        /* workspace smaller than the size query         */
+    KDA_ERR_HIP = 4               /* a HIP launch reported an error                */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int32_t kda_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *kda_status_string(kda_status_t status);
+
+/* Text of the last KDA_ERR_HIP reported on the calling thread ("" if none). */
+const char *kda_last_hip_error(void);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none).
+ * Arguments as for kda_chunk_fwd; num_seqs is the number of sequences (B when
+ * no cu_seqlens is given).
+ */
+size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                    int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+
+/*
+ * kda_chunk_fwd -- chunkwise KDA forward over a batch of sequences (prefill).
+ *
+ * Computes, for every sequence and head, the per-token recurrence above, using
+ * the chunkwise parallel form of section 3.1 of the KimiLinear article (chunks
+ * of C = 64 tokens: intra-chunk interactions by matrix products, inter-chunk
+ * contribution carried by the state) and the specialised DPLR / WY form named
+ * in the Kimi Linear abstract (CoChat record): one decay-weighted key Gram block
+ * per chunk and a unit-lower-triangular solve.  Results equal the per-token
+ * recurrence up to rounding.
+ *
+ *   q, k        [B, T, H, d_k]  io_dtype
+ *   v           [B, T, H, d_v]  io_dtype
+ *   log_alpha   [B, T, H, d_k]  gate_dtype; precondition: finite and <= 0
+ *   beta        [B, T, H]       gate_dtype; any finite value
+ *   h0          [N, H, d_k, d_v] fp32 initial state per sequence, or NULL (zeros)
+ *   cu_seqlens  device int32 [N+1] or NULL.  When given, B must be 1 and the
+ *               batch is the packed concatenation of N = num_seqs sequences:
+ *               sequence n covers tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ *               Precondition: cu_seqlens[0] = 0, non-decreasing, last = T.
+ *               When NULL, N = B and num_seqs must be B (or 0, meaning B).
+ *   o           [B, T, H, d_v]  io_dtype (out)
+ *   h_T         [N, H, d_k, d_v] fp32 final state per sequence (out), or NULL.
+ *               h_T may alias h0 exactly (same pointer): each sequence's h0 is
+ *               read before its h_T is written.  A zero-length sequence gives
+ *               h_T = h0 (or zeros).  h_T has the layout of decode's S, so a
+ *               prefill can hand its state to kda_decode_step without a copy.
+ *   d_k, d_v    each 64 or 128
+ *   io_dtype    KDA_BF16 or KDA_F32; gate_dtype likewise
+ *   workspace   device scratch of at least kda_chunk_fwd_workspace_size()
+ *               bytes (may be NULL when that size is 0)
+ *
+ * Numerics: the state and every accumulation are fp32; products of chunk
+ * operands run on bf16 matrix cores with hi/lo-split operands where precision
+ * needs it; o is rounded to io_dtype with round-to-nearest-even.  Accuracy is
+ * specified for log_alpha >= -30 per token; smaller values act as a reset.
+ * Deterministic: the same inputs give bitwise identical outputs.
+ */
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *beta, const float *h0, const int32_t *cu_seqlens,
+                           int32_t num_seqs, void *o, float *h_T, int32_t B, int32_t T,
+                           int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                           kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * kda_decode_step -- one recurrent KDA step for B resident states (decode).
+ *
+ * Applies the per-token update once to every (b, h) state in place and writes
+ * the read-out: constant work per token with a fixed-size state and no history
+ * (KimiLinear article, section 4.2).
+ *
+ *   q, k        [B, H, d_k]  io_dtype
+ *   v           [B, H, d_v]  io_dtype
+ *   log_alpha   [B, H, d_k]  gate_dtype; precondition: finite and <= 0
+ *   beta        [B, H]       gate_dtype
+ *   S           [B, H, d_k, d_v] fp32, read and overwritten in place
+ *   o           [B, H, d_v]  io_dtype (out)
+ *
+ * S is streamed once (one read, one write per element).
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
+                             const void *beta, float *S, void *o, int32_t B, int32_t H,
+                             int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                             kda_dtype_t gate_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,104 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every symbol its
+header declares, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import gated_delta_rule_chunkwise_amd as kda
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_chunkwise_amd import build
+        build.build()
+    kda.load_library()
+    return kda
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(kda):
+    names = header_functions()
+    assert "kda_chunk_fwd" in names and "kda_decode_step" in names
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kda.EXPORTED_SYMBOLS)
+
+
+def test_version_and_status_strings(kda):
+    assert kda.kda_abi_version() == 1
+    assert kda.kda_status_string(0) == "KDA_OK"
+    assert kda.kda_status_string(2) == "KDA_ERR_UNSUPPORTED"
+    assert kda.kda_status_string(99) == "KDA_ERR_UNKNOWN"
+    assert kda.kda_last_hip_error() == ""
+
+
+def test_workspace_size(kda):
+    assert kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_fwd_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
+
+
+P = 1 << 20   # a fake, 16-byte aligned "device" address; never dereferenced
+
+
+def chunk(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+             dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"], a["N"],
+                             a["o"], a["hT"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"],
+                             a["gt"], a["ws"], a["wsb"], None)
+
+
+def decode(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, S=P, o=P, B=4, H=2, dk=128, dv=128, io=1, gt=1)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["la"], a["beta"], a["S"], a["o"], a["B"],
+                               a["H"], a["dk"], a["dv"], a["io"], a["gt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), 2), (dict(dv=32), 2), (dict(dk=0), 1), (dict(io=5), 2), (dict(gt=-1), 2),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1),
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(la=None), 1),
+    (dict(beta=None), 1), (dict(o=None), 1),
+    (dict(q=P + 4), 1), (dict(o=P + 8), 1), (dict(h0=P + 2), 1), (dict(hT=P + 4), 1),
+    (dict(beta=P + 1), 1), (dict(beta=P + 2, gt=0), 1),
+    (dict(cu=P, N=2, B=2), 1), (dict(cu=P, N=0), 1), (dict(cu=P + 2, N=2), 1),
+    (dict(N=3), 1), (dict(B=2, N=3), 1),
+    (dict(T=1 << 30, H=1 << 20), 1),
+])
+def test_chunk_fwd_rejects(kda, kw, code):
+    lib = kda.load_library()
+    assert chunk(lib, **kw) == code
+
+
+def test_chunk_fwd_empty_without_state_is_noop(kda):
+    lib = kda.load_library()
+    assert chunk(lib, T=0, q=None, k=None, v=None, la=None, beta=None, o=None, hT=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=32), 2), (dict(dv=256), 2), (dict(B=0), 1), (dict(H=-1), 1), (dict(io=3), 2),
+    (dict(S=None), 1), (dict(q=None), 1), (dict(o=None), 1), (dict(beta=None), 1),
+    (dict(S=P + 4), 1), (dict(k=P + 2), 1), (dict(beta=P + 1), 1),
+])
+def test_decode_rejects(kda, kw, code):
+    lib = kda.load_library()
+    assert decode(lib, **kw) == code
+
+
+def test_binding_raises_without_gpu_tensors(kda):
+    import torch
+    x = torch.zeros(1, 64, 2, 64)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(x, x, x, x, torch.zeros(1, 64, 2))

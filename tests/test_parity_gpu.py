@@ -1,0 +1,240 @@
+"""GPU parity: libkda (through the C ABI) against the fp64 oracle on the same
+seeded inputs.  Tolerances: bf16 I/O max-abs 5e-3 and relative Frobenius 1e-2;
+fp32 I/O 1e-4 relative; on o and on the final state."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kda_testutil import assert_close, errors, f64, to_oracle
+
+from gated_delta_rule_chunkwise_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_chunkwise_amd as kda
+    kda.load_library()
+    return kda
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(kda, d, with_h0=True):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    o, hT = kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                              h0=dev["h0"] if with_h0 else None, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return o.cpu(), hT.cpu()
+
+
+def check_against_oracle(kda, d, io, seqs=None, heads=None, what=""):
+    o, hT = run_gpu(kda, d)
+    ref = to_oracle(d, seqs, heads)
+    ro, rh = oracle.fwd(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], h0=ref["h0"],
+                        cu_seqlens=ref["cu_seqlens"])
+    hs = slice(None) if heads is None else list(heads)
+    rows = torch.from_numpy(ref["rows"])
+    go = o.reshape(-1, *o.shape[-2:])[rows][:, hs]
+    sq = list(range(len(d["lengths"]))) if seqs is None else list(seqs)
+    gh = hT[sq][:, hs]
+    eo = assert_close(go, ro, io, what + " o")
+    eh = assert_close(gh, rh, io, what + " h_T")
+    log(what, "o", eo, "h_T", eh)
+    return eo, eh
+
+
+# ------------------------------------------------------------------ the workloads
+def test_c0_fp32_full(kda):
+    d = I.make_chunk_inputs(I.C0)
+    check_against_oracle(kda, d, "f32", what="c0")
+
+
+def test_c1_bf16_full(kda):
+    d = I.make_chunk_inputs(I.C1)
+    check_against_oracle(kda, d, "bf16", what="c1")
+
+
+def test_c2_varlen_sampled(kda):
+    """Full-size varlen batch (32 sequences, h0 != 0) in the launch the benchmark
+    times; the oracle checks 3 whole sequences (all heads), incl. the longest."""
+    d = I.make_chunk_inputs(I.C2)
+    lens = d["lengths"]
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7})
+    check_against_oracle(kda, d, "bf16", seqs=seqs, what="c2 seqs %s" % seqs)
+
+
+@pytest.mark.parametrize("bv", ["16", "32"])
+def test_block_width_variants(kda, bv, monkeypatch):
+    """Both value-column block widths of the kernel, on the c1 shape and a
+    ragged varlen batch with h0."""
+    monkeypatch.setenv("LIBKDA_BLOCK_V", bv)
+    d = I.make_chunk_inputs(I.C1, lengths=[2000])
+    check_against_oracle(kda, d, "bf16", what="c1-like BV=%s" % bv)
+    cfg = I.ChunkConfig("bv", "bf16", "bf16", H=4, dk=128, dv=128, h0=True, seed=19)
+    d = I.make_chunk_inputs(cfg, lengths=[5, 700, 64, 129])
+    check_against_oracle(kda, d, "bf16", what="ragged BV=%s" % bv)
+    cfg = I.ChunkConfig("bv64", "f32", "f32", H=2, dk=64, dv=128, h0=True, seed=20)
+    d = I.make_chunk_inputs(cfg, lengths=[300, 17])
+    check_against_oracle(kda, d, "f32", what="fp32 d_k=64 BV=%s" % bv)
+
+
+def test_c3_long_sampled_heads(kda):
+    """Full-size T = 65536 prefill; the oracle checks 2 whole heads end to end."""
+    d = I.make_chunk_inputs(I.C3)
+    check_against_oracle(kda, d, "bf16", heads=[0, 31], what="c3 heads 0,31")
+
+
+def test_c3_constant_decay_variant(kda):
+    """Long-memory variant: one decay per (head, channel) held over time."""
+    d = I.make_chunk_inputs(I.C3, lengths=[8192], gate="uniform_const")
+    check_against_oracle(kda, d, "bf16", heads=[0, 5, 31], what="c3const")
+
+
+# ------------------------------------------------------------------ shapes / edge cases
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_ragged_varlen_dims(kda, dk, dv, io):
+    cfg = I.ChunkConfig("edge", io, io, H=3, dk=dk, dv=dv, h0=True, seed=11)
+    lens = [1, 63, 64, 65, 0, 130, 200, 7]
+    d = I.make_chunk_inputs(cfg, lengths=lens)
+    check_against_oracle(kda, d, io, what="ragged dk=%d dv=%d %s" % (dk, dv, io))
+
+
+def test_bf16_io_fp32_gates(kda):
+    cfg = I.ChunkConfig("mixed", "bf16", "f32", H=4, dk=128, dv=128, T=333, seed=12, h0=True)
+    d = I.make_chunk_inputs(cfg)
+    check_against_oracle(kda, d, "bf16", what="bf16 io f32 gates")
+
+
+def test_strong_decay_takes_exact_path(kda):
+    """Gates so strong that a chunk's total decay exceeds the matrix-core range
+    (near-resets): those chunks run token by token; results still match."""
+    cfg = I.ChunkConfig("strong", "f32", "f32", H=2, dk=64, dv=64, T=300, seed=13, h0=True)
+    d = I.make_chunk_inputs(cfg)
+    la = d["log_alpha"].clone()
+    la[10] = -30.0
+    la[70:75] = -28.0
+    la[200:264, 0, :5] = -3.0
+    d["log_alpha"] = la
+    check_against_oracle(kda, d, "f32", what="strong decay")
+
+
+def test_beta_negative_eigenvalue_range(kda):
+    cfg = I.ChunkConfig("beta2", "f32", "f32", H=2, dk=128, dv=128, T=257, seed=14)
+    d = I.make_chunk_inputs(cfg)
+    d["beta"] = (d["beta"] * 1.9).contiguous()
+    check_against_oracle(kda, d, "f32", what="beta in (0,1.9)")
+
+
+def test_zero_decay_and_tiny_sequences(kda):
+    cfg = I.ChunkConfig("nodecay", "bf16", "bf16", H=2, dk=128, dv=128, h0=True, seed=15)
+    d = I.make_chunk_inputs(cfg, lengths=[1, 2, 3, 64])
+    d["log_alpha"] = torch.zeros_like(d["log_alpha"])
+    check_against_oracle(kda, d, "bf16", what="alpha=1")
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+def test_split_chaining_and_alias(kda):
+    cfg = I.ChunkConfig("chain", "f32", "f32", H=2, dk=128, dv=128, T=500, seed=16, h0=True)
+    d = I.make_chunk_inputs(cfg)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    o, hT = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=g["h0"])
+    s = 190
+    o1, h1 = kda.kda_chunk_fwd(*(g[x][:s] for x in ("q", "k", "v", "log_alpha", "beta")), h0=g["h0"])
+    # h_T aliasing h0: the second half writes its final state over its own h0.
+    h1c = h1.clone()
+    o2, h2 = kda.kda_chunk_fwd(*(g[x][s:].contiguous() for x in ("q", "k", "v", "log_alpha", "beta")),
+                               h0=h1c, h_T=h1c)
+    torch.cuda.synchronize()
+    assert_close(torch.cat([o1, o2]), o, "f32", "split o")
+    assert_close(h1c, hT, "f32", "split h_T")
+
+
+def test_bitwise_determinism(kda):
+    d = I.make_chunk_inputs(I.C1, lengths=[1000])
+    a = run_gpu(kda, d)
+    b = run_gpu(kda, d)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_varlen_equals_separate_calls(kda):
+    cfg = I.ChunkConfig("sep", "bf16", "bf16", H=2, dk=128, dv=128, h0=True, seed=17)
+    lens = [100, 64, 1, 250]
+    d = I.make_chunk_inputs(cfg, lengths=lens)
+    o, hT = run_gpu(kda, d)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    for n in range(len(lens)):
+        sub = dict(d)
+        for x in ("q", "k", "v", "log_alpha", "beta"):
+            sub[x] = d[x][cu[n]:cu[n + 1]].contiguous()
+        sub["h0"] = d["h0"][n:n + 1].contiguous()
+        sub["lengths"] = [lens[n]]
+        on, hn = run_gpu(kda, sub)
+        assert torch.equal(on.reshape(-1, *on.shape[-2:]), o.reshape(-1, *o.shape[-2:])[cu[n]:cu[n + 1]])
+        assert torch.equal(hn[0], hT[n])
+
+
+# ------------------------------------------------------------------ decode
+def test_decode_full_size_three_steps(kda):
+    cfg = I.C4
+    S = I.make_decode_state(cfg)
+    Sg = S.to(DEV)
+    Sref = f64(S)
+    steps = I.make_decode_step_inputs(cfg, 0, steps=3)
+    for s in range(3):
+        x = {n: t[s] for n, t in steps.items()}
+        o = kda.kda_decode_step(*(x[n].to(DEV) for n in ("q", "k", "v", "log_alpha", "beta")), Sg)
+        ro, Sref = oracle.decode(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["log_alpha"]),
+                                 f64(x["beta"]), Sref)
+        torch.cuda.synchronize()
+        e = assert_close(o.cpu(), ro, "bf16", "decode step %d o" % s)
+        log("decode step", s, e)
+    e = assert_close(Sg.cpu(), Sref, "bf16", "decode S")
+    eS = errors(Sg.cpu(), Sref)
+    assert eS["rel_fro"] < 1e-5, eS
+    log("decode S", eS)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_decode_dims_fp32(kda, dk, dv):
+    cfg = I.DecodeConfig("d", "f32", "f32", B=5, H=3, dk=dk, dv=dv, steps=4, seed=2100)
+    S = I.make_decode_state(cfg)
+    Sg, Sref = S.to(DEV), f64(S)
+    steps = I.make_decode_step_inputs(cfg, 0, steps=4)
+    for s in range(4):
+        x = {n: t[s] for n, t in steps.items()}
+        o = kda.kda_decode_step(*(x[n].to(DEV) for n in ("q", "k", "v", "log_alpha", "beta")), Sg)
+        ro, Sref = oracle.decode(*(f64(x[n]) for n in ("q", "k", "v", "log_alpha", "beta")), Sref)
+        assert_close(o.cpu(), ro, "f32", "decode o")
+    assert_close(Sg.cpu(), Sref, "f32", "decode S")
+
+
+def test_decode_steps_equal_chunk_fwd(kda):
+    """T decode steps from h0 give the chunkwise forward's outputs and state."""
+    cfg = I.ChunkConfig("dec-vs-fwd", "f32", "f32", H=2, dk=128, dv=128, B=3, T=70, seed=18, h0=True)
+    B, T = 3, 70
+    d = I.make_chunk_inputs(cfg)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    q, k, v, la, be = (g[x].reshape(B, T, *g[x].shape[1:]) for x in ("q", "k", "v", "log_alpha", "beta"))
+    o, hT = kda.kda_chunk_fwd(q, k, v, la, be, h0=g["h0"])
+    S = g["h0"].clone()
+    outs = []
+    for t in range(T):
+        outs.append(kda.kda_decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                                        la[:, t].contiguous(), be[:, t].contiguous(), S))
+    torch.cuda.synchronize()
+    assert_close(torch.stack(outs, 1), o, "f32", "decode vs fwd o")
+    assert_close(S, hT, "f32", "decode vs fwd state")
