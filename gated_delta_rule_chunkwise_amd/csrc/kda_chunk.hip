@@ -17,21 +17,25 @@
 // differences are split around a per-channel anchor m = g_n / 2:
 //   e^{G_r - G_i} = e^{G_r - m} e^{m - G_i},
 // so both factors lie in [e^{-D/2}, e^{D/2}] with D = max_c(-g_n).  While
-// D <= 120 every factor is a normal fp32/bf16 number and the products run on the
-// matrix cores; a chunk with a larger in-chunk decay (a near-reset gate) is
-// processed token by token instead (exact, slow, never taken by ordinary gates).
-// (K.e^G) S is formed as (K.e^{G-m}) (Diag(e^m) S) and K.e^{g_n-G} as
-// (K.e^{m-G}) Diag(e^{g_n-m}), so one set of decayed operands serves all products.
+// D <= 80 every factor (and every single-token gate) is a normal fp32/bf16
+// number and the products run on the matrix cores; a chunk with a larger
+// in-chunk decay (a near-reset gate) is processed token by token instead (exact,
+// slower, not taken by ordinary gates).  (K.e^G) S is formed as
+// (K.e^{G-m}) (Diag(e^m) S) and K.e^{g_n-G} as (K.e^{m-G}) Diag(e^{g_n-m}), so
+// one set of decayed operands serves every product.
 //
-// Work decomposition: one workgroup (4 waves) per (sequence, head, block of BV
+// Work decomposition: one workgroup of 8 waves per (sequence, head, block of BV
 // value columns).  The value columns of the state evolve independently, so the
 // blocks need no communication; the d_v-independent part (G, A, P, T) is
-// recomputed per block.  The state block stays in fp32 registers for the whole
-// sequence.
+// recomputed per block.  Waves 0-3 hold the state block in fp32 registers for
+// the whole sequence; waves 4-7 form (K.e^G)S and (Q.e^G)S and the output while
+// waves 0-3 invert the diagonal blocks of (I + A) and update the state.  The
+// next chunk's inputs are loaded into registers while the current one is
+// processed.
 //
-// Precision: products that feed the recurrence (S, T, X, U, P) always use
-// hi/lo-split bf16 operands (hi*hi + hi*lo + lo*hi on the matrix cores).  With
-// bf16 I/O the decayed key/query operands are single bf16; with fp32 I/O they
+// Precision: products that feed the recurrence (T, X, U, P) use hi/lo-split
+// bf16 operands (hi*hi + hi*lo + lo*hi on the matrix cores).  With bf16 I/O the
+// decayed key/query operands and Diag(e^m) S are single bf16; with fp32 I/O they
 // are split too (SPLIT instances).  For fp32 I/O with d_k = 128 the split
 // operands do not fit in LDS, and that instance runs the exact token-by-token
 // update for every chunk.
@@ -47,12 +51,14 @@ namespace kda {
 namespace {
 
 constexpr int kC = 64;            // chunk length (tokens)
-constexpr int kThreads = 256;     // 4 waves
-constexpr float kMaxRange = 120.f;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaxRange2 = 80.f * kLog2e;   // max in-chunk decay (log2 units) on the fast path
 
 template <int DK, int BV, bool SPLIT>
-struct ChunkSmem {
-    static constexpr int NP = SPLIT ? 2 : 1;   // planes of the decayed operands
+struct alignas(16) ChunkSmem {
+    static constexpr int NP = SPLIT ? 2 : 1;   // planes of the decayed operands and of S'
     static constexpr int KS = DK + 8;          // padded stride of d_k-long bf16 rows
     static constexpr int TS = kC + 8;          // padded stride of token-long bf16 rows
     static constexpr int FS = 68;              // fp32 stride of 64x64 matrices (16 B aligned)
@@ -60,27 +66,29 @@ struct ChunkSmem {
     bf16_t QA[NP][kC][KS];                     // Q . e^{G-m}
     union {
         bf16_t KI[NP][kC][KS];                 // K . e^{m-G}: Gram phase only
-        float Tf[kC][FS];                      // (I + A)^{-1} in fp32 while it is formed
-        bf16_t U[2][BV][TS];                   // hi/lo of U^T, from the U phase on
+        bf16_t Tt[2][kC][kC + 4];              // hi/lo of (I + A)^{-1}, transposed (diagonal blocks)
     };
     bf16_t KIt[NP][DK][TS];                    // transpose of K . e^{m-G}
     union {
         float A[kC][FS];                       // beta-scaled strictly lower A (upper: scratch)
-        bf16_t X[2][BV][TS];                   // hi/lo of X^T, X = diag(beta)(V - (K.e^G) S)
+        bf16_t U[2][BV][TS];                   // hi/lo of U^T, after the inversion
     };
+    bf16_t X[2][BV][TS];                       // hi/lo of X^T, X = diag(beta)(V - (K.e^G) S)
     bf16_t T[2][kC][TS];                       // hi/lo of (I + A)^{-1}
     bf16_t P[2][kC][TS];                       // hi/lo of P
-    bf16_t S[2][BV][KS];                       // hi/lo of (Diag(e^m) S)^T, this column block
+    bf16_t S[NP][BV][KS];                      // (Diag(e^m) S)^T of this column block
     float beta[kC];
     float colM[DK];                            // e^{m}
     float colGn[DK];                           // e^{g_n}
     float colGnM[DK];                          // e^{g_n - m}
-    float tot[4][DK];                          // per-16-row-block sums of log_alpha
+    float tot[DK][kWaves];                     // per-8-row sums of log2(alpha)
     float red[4][2 * BV + 1];                  // token path: cross-wave partial sums
+    float T8[4][2][8][8];                      // 8x8 diagonal inverses, per wave
+    float W8[4][8][8];                         // 8x8 merge scratch, per wave
 };
 
 template <int BV>
-struct ExactSmem {
+struct alignas(16) ExactSmem {
     float red[4][2 * BV + 1];
 };
 
@@ -92,8 +100,16 @@ __device__ __forceinline__ void lower_block(int idx, int &R, int &I) {
 }
 
 template <bool ACCURATE>
-__device__ __forceinline__ float kexp(float x) {
-    return ACCURATE ? expf(x) : __expf(x);
+__device__ __forceinline__ float kexp2(float x) {
+    return ACCURATE ? exp2f(x) : __builtin_amdgcn_exp2f(x);
+}
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load, which would stall the next chunk's prefetched inputs
+// at the first barrier; here only LDS operations are drained before s_barrier.
+// Global memory is never exchanged between waves of a workgroup in this kernel.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // acc += A * B for one 32-wide k-step; `lo` pointers are read only when that
@@ -108,75 +124,224 @@ __device__ __forceinline__ f32x4_t mma(f32x4_t acc, const bf16_t *ah, const bf16
     return acc;
 }
 
+__device__ __forceinline__ void store_split4(bf16_t *hi, bf16_t *lo, const f32x4_t &x) {
+    bf16x4_t hv, lv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16_t hh, ll;
+        split_bf16(x[e], hh, ll);
+        hv[e] = hh;
+        lv[e] = ll;
+    }
+    *reinterpret_cast<bf16x4_t *>(hi) = hv;
+    *reinterpret_cast<bf16x4_t *>(lo) = lv;
+}
+
+// Epilogue of one 16x16 Gram tile (R, I): A (beta-scaled, strictly lower, fp32)
+// or P (lower including the diagonal, hi/lo bf16).
+template <typename Sm>
+__device__ __forceinline__ void gram_store(Sm &sm, bool isP, int R, int I, const f32x4_t &acc, int lr, int lg) {
+    const int i = 16 * I + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 16 * R + 4 * lg + e;
+        if (!isP) {
+            sm.A[r][i] = (i < r) ? sm.beta[r] * acc[e] : 0.f;
+        } else {
+            bf16_t hh, ll;
+            split_bf16((i <= r) ? acc[e] : 0.f, hh, ll);
+            sm.P[0][r][i] = hh;
+            sm.P[1][r][i] = ll;
+        }
+    }
+}
+
+// Orders this wave's earlier LDS stores before its later LDS loads (lanes of one
+// wave exchanging data through LDS; no other wave is involved).
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x4_t lds_ld4(const bf16_t *p) {
+    return *reinterpret_cast<const bf16x4_t *>(p);
+}
+
+// Four consecutive fp32 values from LDS, split into hi/lo bf16.
+__device__ __forceinline__ void load_split4(const float *p, bf16x4_t &hi, bf16x4_t &lo) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16_t hh, ll;
+        split_bf16(x[e], hh, ll);
+        hi[e] = hh;
+        lo[e] = ll;
+    }
+}
+
+__device__ __forceinline__ void split4(const f32x4_t &x, bf16x4_t &hi, bf16x4_t &lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16_t hh, ll;
+        split_bf16(x[e], hh, ll);
+        hi[e] = hh;
+        lo[e] = ll;
+    }
+}
+
+// D(16x16) += A(16x16) B(16x16) with hi/lo-split operands on the 16x16x16 bf16
+// matrix core.  Lane l holds A[l%16][4*(l/16)+i], B[4*(l/16)+i][l%16] and
+// D[4*(l/16)+i][l%16]: an accumulator tile is already laid out as a B operand.
+__device__ __forceinline__ f32x4_t mma4(f32x4_t acc, const bf16x4_t &ah, const bf16x4_t &al,
+                                        const bf16x4_t &bh, const bf16x4_t &bl) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+    return acc;
+}
+
+// Stores an accumulator tile (rows r0 + 4*lg + e, column c0 + lr) as hi/lo bf16.
+__device__ __forceinline__ void store_tile_split(bf16_t *hi, bf16_t *lo, int ld, int r0, int c0, const f32x4_t &x,
+                                                 int lr, int lg) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16_t hh, ll;
+        split_bf16(x[e], hh, ll);
+        hi[(r0 + 4 * lg + e) * ld + c0 + lr] = hh;
+        lo[(r0 + 4 * lg + e) * ld + c0 + lr] = ll;
+    }
+}
+
+// State tiles of one workgroup: (d_k/16) x (BV/16) tiles of 16x16, four waves
+// (0-3) own ST/4 each; tile st covers key rows 16*(st/NT) + 4*lg + e and value
+// column col0 + 16*(st%NT) + lr (MFMA accumulator layout).
+template <int DK, int BV> struct StateTiles {
+    static constexpr int NT = BV / 16;
+    static constexpr int ST = (DK / 16) * NT;
+    static constexpr int STW = ST / 4;
+};
+
 // One exact token update of this workgroup's state block (the per-token rule of
-// the KimiLinear article, section 2.3, with the read-out o = S^T q).  The state
-// is in the MFMA accumulator layout: wave w, tile mt holds key rows
-// (w*MT+mt)*16 + 4*lg + e and value column col0 + nt*16 + lr.
+// the KimiLinear article, section 2.3, with the read-out o = S^T q).  Waves 0-3
+// hold the state; all waves take part in the two barriers.
 template <int DK, int BV, typename IO, typename GT>
-__device__ __forceinline__ void token_update(f32x4_t (&Sacc)[DK / 64][BV / 16], float (*red)[2 * BV + 1],
+__device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 16) / 4], float (*red)[2 * BV + 1],
                                              const IO *__restrict__ q, const IO *__restrict__ k,
                                              const IO *__restrict__ v, const GT *__restrict__ log_alpha,
                                              const GT *__restrict__ beta, IO *__restrict__ o, int64_t tk,
                                              int H, int h, int DV, int col0, int w, int lg, int lr) {
-    constexpr int MT = DK / 64, NT = BV / 16;
-    const int64_t kb = (tk * H + h) * (int64_t)DK;
-    float kc[MT][4], qc[MT][4], ac[MT][4];
-    float pqk = 0.f;
+    constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
+    float kc[STW][4];
+    if (w < 4) {
+        const int64_t kb = (tk * H + h) * (int64_t)DK;
+        float pa[NT], pb[NT], pqk = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int nt = 0; nt < NT; ++nt) pa[nt] = pb[nt] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = (w * MT + mt) * 16 + 4 * lg + e;
-            kc[mt][e] = to_f32(k[kb + c]);
-            qc[mt][e] = to_f32(q[kb + c]);
-            ac[mt][e] = expf(to_f32(log_alpha[kb + c]));
-            pqk += qc[mt][e] * kc[mt][e];
-        }
-    float pa[NT], pb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        pa[nt] = 0.f;
-        pb[nt] = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < STW; ++i) {
+            const int st = w * STW + i, mt = st / NT, nt = st % NT;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Sacc[mt][nt][e] *= ac[mt][e];
-                pa[nt] += kc[mt][e] * Sacc[mt][nt][e];
-                pb[nt] += qc[mt][e] * Sacc[mt][nt][e];
+                const int c = 16 * mt + 4 * lg + e;
+                const float kv = to_f32(k[kb + c]), qv = to_f32(q[kb + c]);
+                const float av = expf(to_f32(log_alpha[kb + c]));
+                kc[i][e] = kv;
+                Sacc[i][e] *= av;
+                pa[nt] += kv * Sacc[i][e];
+                pb[nt] += qv * Sacc[i][e];
+                if (nt == 0) pqk += qv * kv;
             }
-        pa[nt] += __shfl_xor(pa[nt], 16);
-        pa[nt] += __shfl_xor(pa[nt], 32);
-        pb[nt] += __shfl_xor(pb[nt], 16);
-        pb[nt] += __shfl_xor(pb[nt], 32);
-    }
-    pqk += __shfl_xor(pqk, 16);
-    pqk += __shfl_xor(pqk, 32);
-    if (lg == 0) {
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            red[w][nt * 16 + lr] = pa[nt];
-            red[w][BV + nt * 16 + lr] = pb[nt];
+            pa[nt] += __shfl_xor(pa[nt], 16);
+            pa[nt] += __shfl_xor(pa[nt], 32);
+            pb[nt] += __shfl_xor(pb[nt], 16);
+            pb[nt] += __shfl_xor(pb[nt], 32);
         }
-        if (lr == 0) red[w][2 * BV] = pqk;
+        pqk += __shfl_xor(pqk, 16);
+        pqk += __shfl_xor(pqk, 32);
+        if (lg == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                red[w][nt * 16 + lr] = pa[nt];
+                red[w][BV + nt * 16 + lr] = pb[nt];
+            }
+            if (lr == 0) red[w][2 * BV] = pqk;
+        }
     }
-    __syncthreads();
-    const float qk = red[0][2 * BV] + red[1][2 * BV] + red[2][2 * BV] + red[3][2 * BV];
-    const float bt = to_f32(beta[tk * H + h]);
+    lds_barrier();
+    if (w < 4) {
+        const float qk = red[0][2 * BV] + red[1][2 * BV] + red[2][2 * BV] + red[3][2 * BV];
+        const float bt = to_f32(beta[tk * H + h]);
+        float u[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int jl = nt * 16 + lr;
-        const float a = red[0][jl] + red[1][jl] + red[2][jl] + red[3][jl];
-        const float b = red[0][BV + jl] + red[1][BV + jl] + red[2][BV + jl] + red[3][BV + jl];
-        const float u = bt * (to_f32(v[(tk * H + h) * (int64_t)DV + col0 + jl]) - a);
+        for (int nt = 0; nt < NT; ++nt) {
+            const int jl = nt * 16 + lr;
+            const float a = red[0][jl] + red[1][jl] + red[2][jl] + red[3][jl];
+            const float b = red[0][BV + jl] + red[1][BV + jl] + red[2][BV + jl] + red[3][BV + jl];
+            u[nt] = bt * (to_f32(v[(tk * H + h) * (int64_t)DV + col0 + jl]) - a);
+            if (w == 0 && lg == 0) o[(tk * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(b + u[nt] * qk);
+        }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < STW; ++i) {
+            const int nt = (w * STW + i) % NT;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Sacc[mt][nt][e] += kc[mt][e] * u;
-        if (w == 0 && lg == 0) o[(tk * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(b + u * qk);
+            for (int e = 0; e < 4; ++e) Sacc[i][e] += kc[i][e] * u[nt];
+        }
     }
-    __syncthreads();
+    lds_barrier();
 }
+
+// Raw inputs of one chunk held in registers (packed as loaded): wave w holds
+// rows 8w..8w+7 of log_alpha, k and q for key channels l*CPL..; waves 4-7 hold
+// the value rows their output tile needs; wave 0 holds beta (lane = token).
+template <typename T, int N> struct VecT;
+template <typename T> struct VecT<T, 1> { typedef T type; };
+template <> struct VecT<bf16_t, 2> { typedef bf16x2_t type; };
+template <> struct VecT<float, 2> { typedef float2 type; };
+template <typename V> __device__ __forceinline__ float vget(const V &x, int i);
+template <> __device__ __forceinline__ float vget<bf16_t>(const bf16_t &x, int) { return (float)x; }
+template <> __device__ __forceinline__ float vget<float>(const float &x, int) { return x; }
+template <> __device__ __forceinline__ float vget<bf16x2_t>(const bf16x2_t &x, int i) { return (float)x[i]; }
+template <> __device__ __forceinline__ float vget<float2>(const float2 &x, int i) { return i ? x.y : x.x; }
+
+template <int DK, int BV, typename IO, typename GT>
+struct ChunkRegs {
+    static constexpr int CPL = DK / 64, NT = BV / 16;
+    typedef typename VecT<GT, CPL>::type GV;
+    typedef typename VecT<IO, CPL>::type IV;
+    GV la[8];
+    IV kk[8], qq[8];
+    float vv[NT][4];
+    float bt;
+
+    __device__ __forceinline__ void load(const IO *__restrict__ q, const IO *__restrict__ k,
+                                         const IO *__restrict__ v, const GT *__restrict__ log_alpha,
+                                         const GT *__restrict__ beta, int64_t tbase, int nv, int H, int h,
+                                         int DV, int col0, int w, int l, int lg, int lr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * w + i;
+            const int rr = r < nv ? r : nv - 1;
+            const int64_t base = ((tbase + rr) * H + h) * (int64_t)DK + l * CPL;
+            la[i] = *reinterpret_cast<const GV *>(log_alpha + base);
+            kk[i] = *reinterpret_cast<const IV *>(k + base);
+            qq[i] = *reinterpret_cast<const IV *>(q + base);
+        }
+        if (w >= 4) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * (w - 4) + 4 * lg + e;
+                    const int rr = r < nv ? r : nv - 1;
+                    vv[nt][e] = to_f32(v[((tbase + rr) * H + h) * (int64_t)DV + col0 + nt * 16 + lr]);
+                }
+        }
+        if (w == 0) bt = to_f32(beta[(tbase + (l < nv ? l : nv - 1)) * H + h]);
+    }
+};
 
 template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
@@ -186,14 +351,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     int64_t seq_len, int32_t H, int32_t DV, int64_t num_chains) {
     constexpr int CPL = DK / 64;    // key channels per lane in the load phase
     constexpr int NKS = DK / 32;    // 32-wide k-steps over d_k
-    constexpr int MT = DK / 64;     // 16-row state tiles per wave
     constexpr int NT = BV / 16;     // 16-column tiles per block
+    constexpr int STW = StateTiles<DK, BV>::STW;
     typedef ChunkSmem<DK, BV, SPLIT> Sm;
     typedef typename std::conditional<EXACT, ExactSmem<BV>, Sm>::type Smem;
     __shared__ Smem smem;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
+    const int l = tid & 63;
     const int lr = l & 15, lg = l >> 4;   // MFMA row/col within tile, lane group
 
     const int64_t wg = blockIdx.x;
@@ -211,18 +377,18 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     }
     const int col0 = jb * BV;   // first value column of this block
 
-    // ---- state block in registers (MFMA accumulator layout) ------------------
-    f32x4_t Sacc[MT][NT];
+    // ---- state block in registers of waves 0-3 ---------------------------------
+    f32x4_t Sacc[STW];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int i = 0; i < STW; ++i) {
+        const int st = w * STW + i, mt = st / NT, nt = st % NT;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = (w * MT + mt) * 16 + 4 * lg + e;
-                const int j = col0 + nt * 16 + lr;
-                Sacc[mt][nt][e] = h0 ? h0[((n * H + h) * DK + c) * (int64_t)DV + j] : 0.f;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int c = 16 * mt + 4 * lg + e;
+            const int j = col0 + nt * 16 + lr;
+            Sacc[i][e] = (h0 && w < 4) ? h0[((n * H + h) * DK + c) * (int64_t)DV + j] : 0.f;
+        }
+    }
 
     if constexpr (EXACT) {
         for (int64_t tk = bos; tk < eos; ++tk)
@@ -235,123 +401,150 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             (&sm.T[0][0][0])[idx] = (bf16_t)0.f;
             (&sm.P[0][0][0])[idx] = (bf16_t)0.f;
         }
+        ChunkRegs<DK, BV, IO, GT> in;
+        if (bos < eos) {
+            const int nv0 = (int)((eos - bos) < kC ? (eos - bos) : kC);
+            in.load(q, k, v, log_alpha, beta, bos, nv0, H, h, DV, col0, w, l, lg, lr);
+        }
+        f32x4_t accZ[NT];
 
         for (int64_t tbase = bos; tbase < eos; tbase += kC) {
             const int nv = (int)((eos - tbase) < kC ? (eos - tbase) : kC);
-            __syncthreads();
+            // Lane indices are re-derived from an opaque copy of the thread id each
+            // chunk, so the compiler recomputes LDS addresses here instead of keeping
+            // dozens of them live across the whole loop (which spills).
+            int tl_;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
+            const int l = tl_ & 63, lr = l & 15, lg = l >> 4;
+            const bool has_next = tbase + kC < eos;
+            const int nv_next = has_next ? (int)((eos - tbase - kC) < kC ? (eos - tbase - kC) : kC) : 0;
+            lds_barrier();
 
-            // ======== phase L: cumsum of log_alpha, anchors, decayed operands ========
-            // All global loads of the chunk are issued here, unconditionally: rows
-            // past the end of the sequence read the last valid row and are zeroed
-            // afterwards, so no load sits behind a branch and they overlap.
-            const int r0 = 16 * w;
-            float g[16][CPL];
-            IO kraw[16][CPL], qraw[16][CPL];
-            float vraw[NT][4];
+            // ======== phase L: log2-decay cumsum, anchors, decayed operands ========
+            const bool partial = nv < kC;
+            float csum[8][CPL];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = r0 + i;
-                const int rr = r < nv ? r : nv - 1;
-                const int64_t base = ((tbase + rr) * H + h) * (int64_t)DK + l * CPL;
+            for (int cc = 0; cc < CPL; ++cc) {
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    g[i][cc] = to_f32(log_alpha[base + cc]);
-                    kraw[i][cc] = k[base + cc];
-                    qraw[i][cc] = q[base + cc];
+                for (int i = 0; i < 8; ++i) {
+                    float x = vget(in.la[i], cc) * kLog2e;
+                    if (partial && 8 * w + i >= nv) x = 0.f;
+                    csum[i][cc] = i ? csum[i - 1][cc] + x : x;
                 }
+                sm.tot[l * CPL + cc][w] = csum[7][cc];
             }
+            float vcur[NT][4];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * w + 4 * lg + e;
-                    const int rr = r < nv ? r : nv - 1;
-                    vraw[nt][e] = to_f32(v[((tbase + rr) * H + h) * (int64_t)DV + col0 + nt * 16 + lr]);
-                }
-            const float bload = to_f32(beta[(tbase + (l < nv ? l : nv - 1)) * H + h]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) g[i][cc] = (r0 + i < nv) ? g[i][cc] : 0.f;
-#pragma unroll
-            for (int i = 1; i < 16; ++i)
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) g[i][cc] += g[i - 1][cc];
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) sm.tot[w][l * CPL + cc] = g[15][cc];
-            if (w == 0) sm.beta[l] = (l < nv) ? bload : 0.f;
-            __syncthreads();
-            float m[CPL], gn[CPL];
-            float dmax = 0.f;
+                for (int e = 0; e < 4; ++e) vcur[nt][e] = in.vv[nt][e];
+            if (w == 0) sm.beta[l] = (l < nv) ? in.bt : 0.f;
+            lds_barrier();
+            float m2[CPL];
+            bool big = false;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 const int c = l * CPL + cc;
-                const float t0 = sm.tot[0][c], t1 = sm.tot[1][c], t2 = sm.tot[2][c], t3 = sm.tot[3][c];
-                const float pre = (w > 0 ? t0 : 0.f) + (w > 1 ? t1 : 0.f) + (w > 2 ? t2 : 0.f);
-                gn[cc] = ((t0 + t1) + t2) + t3;
-                m[cc] = 0.5f * gn[cc];
+                const float4 ta = reinterpret_cast<const float4 *>(&sm.tot[c][0])[0];
+                const float4 tb = reinterpret_cast<const float4 *>(&sm.tot[c][0])[1];
+                const float tw[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+                float pre = 0.f, all = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) g[i][cc] += pre;
-                dmax = fmaxf(dmax, -gn[cc]);
-            }
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    all += tw[ww];
+                    if (ww < w) pre += tw[ww];
+                }
+                m2[cc] = 0.5f * all;
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, off));
-            const bool slow = !(dmax <= kMaxRange);   // uniform over the workgroup; catches NaN
-
-            if (w == 0) {
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const int c = l * CPL + cc;
-                    sm.colM[c] = kexp<SPLIT>(m[cc]);
-                    sm.colGn[c] = kexp<SPLIT>(gn[cc]);
-                    sm.colGnM[c] = kexp<SPLIT>(gn[cc] - m[cc]);
+                for (int i = 0; i < 8; ++i) csum[i][cc] += pre;
+                big = big || !(-all <= kMaxRange2);   // also true for NaN
+                if (w == 0) {
+                    sm.colM[c] = kexp2<SPLIT>(m2[cc]);
+                    sm.colGn[c] = kexp2<SPLIT>(all);
+                    sm.colGnM[c] = kexp2<SPLIT>(all - m2[cc]);
                 }
             }
+            // Every wave sees the same totals, so this vote is uniform over the workgroup.
+            const bool slow = __ballot(big) != 0;
 
             if (!slow) {
-                bf16_t kit[Sm::NP][CPL][16];
+                // e1[i] = 2^{G[i]-m}, e2[i] = 2^{m-G[i]}: one exact exp at each end of
+                // the wave's 8 rows, then products with alpha = 2^{lam} (|.| <= 2^{58}).
+                float e1[8][CPL], e2[8][CPL];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = r0 + i;
+                for (int cc = 0; cc < CPL; ++cc) {
+                    float al[8];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) {
+                        float x = vget(in.la[i], cc) * kLog2e;
+                        if (partial && 8 * w + i >= nv) x = 0.f;
+                        al[i] = kexp2<SPLIT>(x);
+                    }
+                    e1[0][cc] = kexp2<SPLIT>(csum[0][cc] - m2[cc]);
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) e1[i][cc] = e1[i - 1][cc] * al[i];
+                    e2[7][cc] = kexp2<SPLIT>(m2[cc] - csum[7][cc]);
+#pragma unroll
+                    for (int i = 6; i >= 0; --i) e2[i][cc] = e2[i + 1][cc] * al[i + 1];
+                }
+                if (partial) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (8 * w + i >= nv) {
+#pragma unroll
+                            for (int cc = 0; cc < CPL; ++cc) e1[i][cc] = e2[i][cc] = 0.f;
+                        }
+                }
+                bf16x8_t kit[Sm::NP][CPL];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 8 * w + i;
+                    float ka[CPL], qa[CPL], ki[CPL];
 #pragma unroll
                     for (int cc = 0; cc < CPL; ++cc) {
-                        const int c = l * CPL + cc;
-                        const float kv = (r < nv) ? to_f32(kraw[i][cc]) : 0.f;
-                        const float qv = (r < nv) ? to_f32(qraw[i][cc]) : 0.f;
-                        const float e1 = kexp<SPLIT>(g[i][cc] - m[cc]);
-                        const float e2 = kexp<SPLIT>(m[cc] - g[i][cc]);
-                        const float ka = kv * e1, qa = qv * e1, ki = kv * e2;
-                        if constexpr (SPLIT) {
+                        const float kv = vget(in.kk[i], cc), qv = vget(in.qq[i], cc);
+                        ka[cc] = kv * e1[i][cc];
+                        qa[cc] = qv * e1[i][cc];
+                        ki[cc] = kv * e2[i][cc];
+                    }
+                    if constexpr (SPLIT) {
+#pragma unroll
+                        for (int cc = 0; cc < CPL; ++cc) {
+                            const int c = l * CPL + cc;
                             bf16_t hh, ll;
-                            split_bf16(ka, hh, ll); sm.KA[0][r][c] = hh; sm.KA[1][r][c] = ll;
-                            split_bf16(qa, hh, ll); sm.QA[0][r][c] = hh; sm.QA[1][r][c] = ll;
-                            split_bf16(ki, hh, ll); sm.KI[0][r][c] = hh; sm.KI[1][r][c] = ll;
+                            split_bf16(ka[cc], hh, ll); sm.KA[0][r][c] = hh; sm.KA[1][r][c] = ll;
+                            split_bf16(qa[cc], hh, ll); sm.QA[0][r][c] = hh; sm.QA[1][r][c] = ll;
+                            split_bf16(ki[cc], hh, ll); sm.KI[0][r][c] = hh; sm.KI[1][r][c] = ll;
                             kit[0][cc][i] = hh;
-                            kit[1][cc][i] = ll;
-                        } else {
-                            sm.KA[0][r][c] = (bf16_t)ka;
-                            sm.QA[0][r][c] = (bf16_t)qa;
-                            const bf16_t kib = (bf16_t)ki;
-                            sm.KI[0][r][c] = kib;
-                            kit[0][cc][i] = kib;
+                            kit[Sm::NP - 1][cc][i] = ll;
                         }
+                    } else if constexpr (CPL == 2) {
+                        bf16x2_t p;
+                        p[0] = (bf16_t)ka[0]; p[1] = (bf16_t)ka[1];
+                        *reinterpret_cast<bf16x2_t *>(&sm.KA[0][r][2 * l]) = p;
+                        p[0] = (bf16_t)qa[0]; p[1] = (bf16_t)qa[1];
+                        *reinterpret_cast<bf16x2_t *>(&sm.QA[0][r][2 * l]) = p;
+                        p[0] = (bf16_t)ki[0]; p[1] = (bf16_t)ki[1];
+                        *reinterpret_cast<bf16x2_t *>(&sm.KI[0][r][2 * l]) = p;
+                        kit[0][0][i] = p[0];
+                        kit[0][1][i] = p[1];
+                    } else {
+                        sm.KA[0][r][l] = (bf16_t)ka[0];
+                        sm.QA[0][r][l] = (bf16_t)qa[0];
+                        const bf16_t kib = (bf16_t)ki[0];
+                        sm.KI[0][r][l] = kib;
+                        kit[0][0][i] = kib;
                     }
                 }
 #pragma unroll
                 for (int pl = 0; pl < Sm::NP; ++pl)
 #pragma unroll
-                    for (int cc = 0; cc < CPL; ++cc) {
-                        bf16x8_t lo8, hi8;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            lo8[i] = kit[pl][cc][i];
-                            hi8[i] = kit[pl][cc][8 + i];
-                        }
-                        *reinterpret_cast<bf16x8_t *>(&sm.KIt[pl][l * CPL + cc][r0]) = lo8;
-                        *reinterpret_cast<bf16x8_t *>(&sm.KIt[pl][l * CPL + cc][r0 + 8]) = hi8;
-                    }
+                    for (int cc = 0; cc < CPL; ++cc)
+                        *reinterpret_cast<bf16x8_t *>(&sm.KIt[pl][l * CPL + cc][8 * w]) = kit[pl][cc];
             }
-            __syncthreads();
+            // the next chunk's inputs go in flight now
+            if (has_next) in.load(q, k, v, log_alpha, beta, tbase + kC, nv_next, H, h, DV, col0, w, l, lg, lr);
+            lds_barrier();
 
             if (slow) {
                 // exact token-by-token path for a chunk with a huge in-chunk decay
@@ -361,217 +554,246 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 continue;
             }
 
-            // ======== phase AP: S' = Diag(e^m) S (hi/lo), Gram blocks A and P ========
+            // ======== phase AP: S' = Diag(e^m) S, Gram blocks A and P ========
+            if (w < 4) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int c = (w * MT + mt) * 16 + 4 * lg;
+                for (int i = 0; i < STW; ++i) {
+                    const int st = w * STW + i, mt = st / NT, nt = st % NT;
+                    const int c = 16 * mt + 4 * lg;
                     bf16x4_t hi, lo;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         bf16_t hh, ll;
-                        split_bf16(sm.colM[c + e] * Sacc[mt][nt][e], hh, ll);
+                        split_bf16(sm.colM[c + e] * Sacc[i][e], hh, ll);
                         hi[e] = hh;
                         lo[e] = ll;
                     }
                     *reinterpret_cast<bf16x4_t *>(&sm.S[0][nt * 16 + lr][c]) = hi;
-                    *reinterpret_cast<bf16x4_t *>(&sm.S[1][nt * 16 + lr][c]) = lo;
-                }
-            for (int tile = w; tile < 20; tile += 4) {
-                const bool isP = tile >= 10;
-                int R, I;
-                lower_block(isP ? tile - 10 : tile, R, I);
-                const bf16_t *ah = isP ? &sm.QA[0][16 * R + lr][8 * lg] : &sm.KA[0][16 * R + lr][8 * lg];
-                const bf16_t *al = ah + (SPLIT ? kC * Sm::KS : 0);
-                const bf16_t *bh = &sm.KI[0][16 * I + lr][8 * lg];
-                const bf16_t *bl = bh + (SPLIT ? kC * Sm::KS : 0);
-                f32x4_t acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    acc = mma<SPLIT, SPLIT>(acc, ah + 32 * ks, al + 32 * ks, bh + 32 * ks, bl + 32 * ks);
-                const int i = 16 * I + lr;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * R + 4 * lg + e;
-                    if (!isP) {
-                        sm.A[r][i] = (i < r) ? sm.beta[r] * acc[e] : 0.f;
-                    } else {
-                        bf16_t hh, ll;
-                        split_bf16((i <= r) ? acc[e] : 0.f, hh, ll);
-                        sm.P[0][r][i] = hh;
-                        sm.P[1][r][i] = ll;
-                    }
+                    if constexpr (SPLIT) *reinterpret_cast<bf16x4_t *>(&sm.S[Sm::NP - 1][nt * 16 + lr][c]) = lo;
                 }
             }
-            __syncthreads();
-
-            // ======== phase T: (I + A)^{-1} by blocked forward substitution (fp32) ========
             {
-                // T1: diagonal 16x16 blocks, one per wave; lane j < 16 solves column j.
+                // 20 Gram tiles: wave w takes tiles w and w + 8 together (two independent
+                // MFMA chains), and waves 0-3 also tile w + 16.
+                int RA, IA, RB, IB;
+                const int tA = w, tB = w + 8;
+                lower_block(tA, RA, IA);
+                lower_block(tB >= 10 ? tB - 10 : tB, RB, IB);
+                const bool pB = tB >= 10;
+                const bf16_t *aAh = &sm.KA[0][16 * RA + lr][8 * lg];
+                const bf16_t *aBh = pB ? &sm.QA[0][16 * RB + lr][8 * lg] : &sm.KA[0][16 * RB + lr][8 * lg];
+                const bf16_t *bAh = &sm.KI[0][16 * IA + lr][8 * lg];
+                const bf16_t *bBh = &sm.KI[0][16 * IB + lr][8 * lg];
+                constexpr int PL = SPLIT ? kC * Sm::KS : 0;
+                f32x4_t accA = zero4(), accB = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int o32 = 32 * ks;
+                    accA = mma<SPLIT, SPLIT>(accA, aAh + o32, aAh + PL + o32, bAh + o32, bAh + PL + o32);
+                    accB = mma<SPLIT, SPLIT>(accB, aBh + o32, aBh + PL + o32, bBh + o32, bBh + PL + o32);
+                }
+                gram_store(sm, false, RA, IA, accA, lr, lg);
+                gram_store(sm, pB, RB, IB, accB, lr, lg);
+                if (w < 4) {
+                    int RC, IC;
+                    lower_block(w + 6, RC, IC);   // tiles 16..19 are P blocks 6..9
+                    const bf16_t *aCh = &sm.QA[0][16 * RC + lr][8 * lg];
+                    const bf16_t *bCh = &sm.KI[0][16 * IC + lr][8 * lg];
+                    f32x4_t accC = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int o32 = 32 * ks;
+                        accC = mma<SPLIT, SPLIT>(accC, aCh + o32, aCh + PL + o32, bCh + o32, bCh + PL + o32);
+                    }
+                    gram_store(sm, true, RC, IC, accC, lr, lg);
+                }
+            }
+            lds_barrier();
+
+            // ======== waves 0-3: diagonal blocks of (I + A)^{-1};  waves 4-7: Y, Z, X ========
+            if (w < 4) {
+                // Block R = w of the inverse, 16x16, from two 8x8 forward substitutions
+                // merged in the wave: [[Ta, 0], [-Tb A_ba Ta, Tb]].  fp32 throughout.
                 const int R = w;
-                const int j = lr;
-                float t[16];
+                float (*t8)[8][8] = sm.T8[R];
+                float (*w8)[8] = sm.W8[R];
+                if (l < 16) {
+                    const int sb = l >> 3, j = l & 7, base = 16 * R + 8 * sb;
+                    float a[8][8];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float s = (r == j) ? 1.f : 0.f;
+                    for (int r = 1; r < 8; ++r) {
+                        const float4 a0 = *reinterpret_cast<const float4 *>(&sm.A[base + r][base]);
+                        const float4 a1 = *reinterpret_cast<const float4 *>(&sm.A[base + r][base + 4]);
+                        a[r][0] = a0.x; a[r][1] = a0.y; a[r][2] = a0.z; a[r][3] = a0.w;
+                        a[r][4] = a1.x; a[r][5] = a1.y; a[r][6] = a1.z; a[r][7] = a1.w;
+                    }
+                    float t[8];
 #pragma unroll
-                    for (int mm = 0; mm < r; ++mm) s -= sm.A[16 * R + r][16 * R + mm] * t[mm];
-                    t[r] = s;
-                }
-                if (lg == 0) {
+                    for (int r = 0; r < 8; ++r) {
+                        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        sm.Tf[16 * R + r][16 * R + j] = t[r];
-#pragma unroll
-                        for (int I = R + 1; I < 4; ++I) sm.Tf[16 * R + r][16 * I + j] = 0.f;
+                        for (int mm = 0; mm < r; ++mm) {
+                            if (mm & 1) s1 -= a[r][mm] * t[mm];
+                            else s0 -= a[r][mm] * t[mm];
+                        }
+                        t[r] = s0 + s1;
+                        t8[sb][r][j] = t[r];
                     }
                 }
-            }
-            __syncthreads();
-            // T2: T[R+1][R] = -T[R+1][R+1] A[R+1][R] T[R][R] for R = 0, 2 (waves 0, 1);
-            // the product A[R+1][R] T[R][R] is staged in A's unused block (R, R+1).
-            if (w < 2) {
-                const int R = 2 * w;
-                float (*Wsc)[Sm::FS] = reinterpret_cast<float (*)[Sm::FS]>(&sm.A[16 * R][16 * (R + 1)]);
+                wave_lds_sync();
+                const int i8 = l >> 3, j8 = l & 7;
+                {
+                    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * lg + e;
-                    float s = 0.f;
+                    for (int mm = 0; mm < 8; mm += 2) {
+                        s0 += sm.A[16 * R + 8 + i8][16 * R + mm] * t8[0][mm][j8];
+                        s1 += sm.A[16 * R + 8 + i8][16 * R + mm + 1] * t8[0][mm + 1][j8];
+                    }
+                    w8[i8][j8] = s0 + s1;
+                }
+                wave_lds_sync();
+                float tba;
+                {
+                    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-                    for (int mm = 0; mm < 16; ++mm)
-                        s += sm.A[16 * (R + 1) + r][16 * R + mm] * sm.Tf[16 * R + mm][16 * R + lr];
-                    Wsc[r][lr] = s;
+                    for (int mm = 0; mm < 8; mm += 2) {
+                        s0 += t8[1][i8][mm] * w8[mm][j8];
+                        s1 += t8[1][i8][mm + 1] * w8[mm + 1][j8];
+                    }
+                    tba = -(s0 + s1);
                 }
-            }
-            __syncthreads();
-            if (w < 2) {
-                const int R = 2 * w;
-                float (*Wsc)[Sm::FS] = reinterpret_cast<float (*)[Sm::FS]>(&sm.A[16 * R][16 * (R + 1)]);
+                // lane (i8, j8) writes entries (i8, j8), (i8, 8+j8), (8+i8, j8), (8+i8, 8+j8)
+                // of the 16x16 block, row-major (T) and transposed (Tt).
+                const float vals[4] = {t8[0][i8][j8], 0.f, tba, t8[1][i8][j8]};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * lg + e;
-                    float s = 0.f;
-#pragma unroll
-                    for (int mm = 0; mm < 16; ++mm) s += sm.Tf[16 * (R + 1) + r][16 * (R + 1) + mm] * Wsc[mm][lr];
-                    sm.Tf[16 * (R + 1) + r][16 * R + lr] = -s;
-                }
-            }
-            __syncthreads();
-            // T3: lower-left 32x32 = -T[23][23] A[23][01] T[01][01]; A's upper-right 32x32 is scratch.
-            {
-                const int r = tid >> 3;          // 0..31
-                const int j4 = 4 * (tid & 7);    // 0..28
-                float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll 8
-                for (int mm = 0; mm < 32; ++mm) {
-                    const float a = sm.A[32 + r][mm];
-                    const float4 tv = *reinterpret_cast<const float4 *>(&sm.Tf[mm][j4]);
-                    s0 += a * tv.x; s1 += a * tv.y; s2 += a * tv.z; s3 += a * tv.w;
-                }
-                float4 wv = {s0, s1, s2, s3};
-                *reinterpret_cast<float4 *>(&sm.A[r][32 + j4]) = wv;
-            }
-            __syncthreads();
-            {
-                const int r = tid >> 3;
-                const int j4 = 4 * (tid & 7);
-                float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll 8
-                for (int mm = 0; mm < 32; ++mm) {
-                    const float a = sm.Tf[32 + r][32 + mm];
-                    const float4 wv = *reinterpret_cast<const float4 *>(&sm.A[mm][32 + j4]);
-                    s0 += a * wv.x; s1 += a * wv.y; s2 += a * wv.z; s3 += a * wv.w;
-                }
-                float4 tv = {-s0, -s1, -s2, -s3};
-                *reinterpret_cast<float4 *>(&sm.Tf[32 + r][j4]) = tv;
-            }
-            __syncthreads();
-
-            // ======== phase Y: Y = (K.e^G) S, Z = (Q.e^G) S; X = diag(beta)(V - Y); T -> hi/lo ========
-            for (int idx = tid; idx < kC * kC; idx += kThreads) {
-                const int r = idx >> 6, i = idx & 63;
-                if ((i >> 4) <= (r >> 4)) {
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int rr = 16 * R + 8 * (qd >> 1) + i8, cc = 16 * R + 8 * (qd & 1) + j8;
                     bf16_t hh, ll;
-                    split_bf16(sm.Tf[r][i], hh, ll);
-                    sm.T[0][r][i] = hh;
-                    sm.T[1][r][i] = ll;
+                    split_bf16(vals[qd], hh, ll);
+                    sm.T[0][rr][cc] = hh;
+                    sm.T[1][rr][cc] = ll;
+                    sm.Tt[0][cc][rr] = hh;
+                    sm.Tt[1][cc][rr] = ll;
                 }
-            }
-            f32x4_t accZ[NT], accY[NT];
-            {
-                const bf16_t *kah = &sm.KA[0][16 * w + lr][8 * lg];
-                const bf16_t *qah = &sm.QA[0][16 * w + lr][8 * lg];
+            } else {
+                const int rb = w - 4;
+                const bf16_t *kah = &sm.KA[0][16 * rb + lr][8 * lg];
+                const bf16_t *qah = &sm.QA[0][16 * rb + lr][8 * lg];
                 const bf16_t *kal = kah + (SPLIT ? kC * Sm::KS : 0);
                 const bf16_t *qal = qah + (SPLIT ? kC * Sm::KS : 0);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const bf16_t *sh = &sm.S[0][nt * 16 + lr][8 * lg];
-                    const bf16_t *sl = &sm.S[1][nt * 16 + lr][8 * lg];
-                    accY[nt] = zero4();
+                    const bf16_t *sl = sh + (SPLIT ? BV * Sm::KS : 0);
+                    f32x4_t accY = zero4();
                     accZ[nt] = zero4();
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
                         const int o32 = 32 * ks;
-                        accY[nt] = mma<SPLIT, true>(accY[nt], kah + o32, kal + o32, sh + o32, sl + o32);
-                        accZ[nt] = mma<SPLIT, true>(accZ[nt], qah + o32, qal + o32, sh + o32, sl + o32);
+                        accY = mma<SPLIT, SPLIT>(accY, kah + o32, kal + o32, sh + o32, sl + o32);
+                        accZ[nt] = mma<SPLIT, SPLIT>(accZ[nt], qah + o32, qal + o32, sh + o32, sl + o32);
                     }
-                }
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int jl = nt * 16 + lr;
-                bf16x4_t hi, lo;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * w + 4 * lg + e;
-                    const float vv = (r < nv) ? vraw[nt][e] : 0.f;
-                    bf16_t hh, ll;
-                    split_bf16(sm.beta[r] * (vv - accY[nt][e]), hh, ll);
-                    hi[e] = hh;
-                    lo[e] = ll;
-                }
-                *reinterpret_cast<bf16x4_t *>(&sm.X[0][jl][16 * w + 4 * lg]) = hi;
-                *reinterpret_cast<bf16x4_t *>(&sm.X[1][jl][16 * w + 4 * lg]) = lo;
-            }
-            __syncthreads();
-
-            // ======== phase U: U = T X ========
-            {
-                const int nks = (w >> 1) + 1;
-                const bf16_t *th = &sm.T[0][16 * w + lr][8 * lg];
-                const bf16_t *tl = &sm.T[1][16 * w + lr][8 * lg];
-                f32x4_t accU[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const bf16_t *xh = &sm.X[0][nt * 16 + lr][8 * lg];
-                    const bf16_t *xl = &sm.X[1][nt * 16 + lr][8 * lg];
-                    accU[nt] = zero4();
-                    for (int ks = 0; ks < nks; ++ks)
-                        accU[nt] = mma<true, true>(accU[nt], th + 32 * ks, tl + 32 * ks, xh + 32 * ks, xl + 32 * ks);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int jl = nt * 16 + lr;
-                    bf16x4_t hi, lo;
+                    f32x4_t x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        bf16_t hh, ll;
-                        split_bf16(accU[nt][e], hh, ll);
-                        hi[e] = hh;
-                        lo[e] = ll;
+                        const int r = 16 * rb + 4 * lg + e;
+                        x[e] = sm.beta[r] * (vcur[nt][e] - accY[e]);
                     }
-                    *reinterpret_cast<bf16x4_t *>(&sm.U[0][jl][16 * w + 4 * lg]) = hi;
-                    *reinterpret_cast<bf16x4_t *>(&sm.U[1][jl][16 * w + 4 * lg]) = lo;
+                    const int jl = nt * 16 + lr;
+                    store_split4(&sm.X[0][jl][16 * rb + 4 * lg], &sm.X[1][jl][16 * rb + 4 * lg], x);
                 }
             }
-            __syncthreads();
+            lds_barrier();
 
-            // ======== phase O: O = Z + P U (store); phase S: state update ========
-            {
-                const int nks = (w >> 1) + 1;
-                const bf16_t *ph = &sm.P[0][16 * w + lr][8 * lg];
-                const bf16_t *pl = &sm.P[1][16 * w + lr][8 * lg];
+            // ======== off-diagonal blocks of (I + A)^{-1}: waves 0 and 1, matrix cores ========
+            // T[R+1][R] = -T[R+1][R+1] (A[R+1][R] T[R][R]) for R = 0, 2 (both waves compute
+            // both; the stores are identical), then wave b forms the lower-left column block
+            // b of -T[23][23] (A[23][01] T[01][01]).  16x16x16 products with hi/lo-split
+            // operands; an accumulator tile is directly the B operand of the next product.
+            if (w < 2) {
+                const int b = w;
+                f32x4_t t10, t32;
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int R = 2 * pr;
+                    bf16x4_t ah, al;
+                    load_split4(&sm.A[16 * (R + 1) + lr][16 * R + 4 * lg], ah, al);
+                    f32x4_t wacc = mma4(zero4(), ah, al, lds_ld4(&sm.Tt[0][16 * R + lr][16 * R + 4 * lg]),
+                                        lds_ld4(&sm.Tt[1][16 * R + lr][16 * R + 4 * lg]));
+                    bf16x4_t wh, wl;
+                    split4(wacc, wh, wl);
+                    f32x4_t tacc = mma4(zero4(), lds_ld4(&sm.T[0][16 * (R + 1) + lr][16 * (R + 1) + 4 * lg]),
+                                        lds_ld4(&sm.T[1][16 * (R + 1) + lr][16 * (R + 1) + 4 * lg]), wh, wl);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tacc[e] = -tacc[e];
+                    store_tile_split(&sm.T[0][0][0], &sm.T[1][0][0], Sm::TS, 16 * (R + 1), 16 * R, tacc, lr, lg);
+                    if (pr == 0) t10 = tacc;
+                    else t32 = tacc;
+                }
+                (void)t32;
+                wave_lds_sync();
+                // W2[a][b] = sum_m A[a][m] T[m][b], a = 2, 3 (T[0][1] = 0)
+                f32x4_t w2[2];
+#pragma unroll
+                for (int a2 = 0; a2 < 2; ++a2) {
+                    const int a = 2 + a2;
+                    bf16x4_t ah, al;
+                    w2[a2] = zero4();
+                    if (b == 0) {
+                        load_split4(&sm.A[16 * a + lr][4 * lg], ah, al);
+                        w2[a2] = mma4(w2[a2], ah, al, lds_ld4(&sm.Tt[0][lr][4 * lg]), lds_ld4(&sm.Tt[1][lr][4 * lg]));
+                        bf16x4_t th, tl;
+                        split4(t10, th, tl);
+                        load_split4(&sm.A[16 * a + lr][16 + 4 * lg], ah, al);
+                        w2[a2] = mma4(w2[a2], ah, al, th, tl);
+                    } else {
+                        load_split4(&sm.A[16 * a + lr][16 + 4 * lg], ah, al);
+                        w2[a2] = mma4(w2[a2], ah, al, lds_ld4(&sm.Tt[0][16 + lr][16 + 4 * lg]),
+                                      lds_ld4(&sm.Tt[1][16 + lr][16 + 4 * lg]));
+                    }
+                }
+                bf16x4_t w2h[2], w2l[2];
+                split4(w2[0], w2h[0], w2l[0]);
+                split4(w2[1], w2h[1], w2l[1]);
+                // T[2][b] = -T[2][2] W2[2][b];  T[3][b] = -(T[3][2] W2[2][b] + T[3][3] W2[3][b])
+                f32x4_t t2b = mma4(zero4(), lds_ld4(&sm.T[0][32 + lr][32 + 4 * lg]),
+                                   lds_ld4(&sm.T[1][32 + lr][32 + 4 * lg]), w2h[0], w2l[0]);
+                f32x4_t t3b = mma4(zero4(), lds_ld4(&sm.T[0][48 + lr][32 + 4 * lg]),
+                                   lds_ld4(&sm.T[1][48 + lr][32 + 4 * lg]), w2h[0], w2l[0]);
+                t3b = mma4(t3b, lds_ld4(&sm.T[0][48 + lr][48 + 4 * lg]), lds_ld4(&sm.T[1][48 + lr][48 + 4 * lg]),
+                           w2h[1], w2l[1]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    t2b[e] = -t2b[e];
+                    t3b[e] = -t3b[e];
+                }
+                store_tile_split(&sm.T[0][0][0], &sm.T[1][0][0], Sm::TS, 32, 16 * b, t2b, lr, lg);
+                store_tile_split(&sm.T[0][0][0], &sm.T[1][0][0], Sm::TS, 48, 16 * b, t3b, lr, lg);
+            }
+            lds_barrier();
+
+            // ======== phase U: U = T X ========
+            if (w < 4 * NT) {
+                const int R = w & 3, nt = w >> 2;
+                const int nks = (R >> 1) + 1;
+                const bf16_t *th = &sm.T[0][16 * R + lr][8 * lg];
+                const bf16_t *tl = &sm.T[1][16 * R + lr][8 * lg];
+                const bf16_t *xh = &sm.X[0][nt * 16 + lr][8 * lg];
+                const bf16_t *xl = &sm.X[1][nt * 16 + lr][8 * lg];
+                f32x4_t acc = zero4();
+                for (int ks = 0; ks < nks; ++ks)
+                    acc = mma<true, true>(acc, th + 32 * ks, tl + 32 * ks, xh + 32 * ks, xl + 32 * ks);
+                const int jl = nt * 16 + lr;
+                store_split4(&sm.U[0][jl][16 * R + 4 * lg], &sm.U[1][jl][16 * R + 4 * lg], acc);
+            }
+            lds_barrier();
+
+            // ======== waves 4-7: O = Z + P U (store);  waves 0-3: state update ========
+            if (w >= 4) {
+                const int rb = w - 4;
+                const int nks = (rb >> 1) + 1;
+                const bf16_t *ph = &sm.P[0][16 * rb + lr][8 * lg];
+                const bf16_t *pl = &sm.P[1][16 * rb + lr][8 * lg];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const bf16_t *uh = &sm.U[0][nt * 16 + lr][8 * lg];
@@ -582,18 +804,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                     const int jl = nt * 16 + lr;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * w + 4 * lg + e;
+                        const int r = 16 * rb + 4 * lg + e;
                         if (r < nv) o[((tbase + r) * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(acc[e]);
                     }
                 }
-            }
+            } else {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int c16 = (w * MT + mt) * 16;
-                const bf16_t *kh = &sm.KIt[0][c16 + lr][8 * lg];
-                const bf16_t *kl = kh + (SPLIT ? DK * Sm::TS : 0);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
+                for (int i = 0; i < STW; ++i) {
+                    const int st = w * STW + i, mt = st / NT, nt = st % NT;
+                    const bf16_t *kh = &sm.KIt[0][16 * mt + lr][8 * lg];
+                    const bf16_t *kl = kh + (SPLIT ? DK * Sm::TS : 0);
                     const bf16_t *uh = &sm.U[0][nt * 16 + lr][8 * lg];
                     const bf16_t *ul = &sm.U[1][nt * 16 + lr][8 * lg];
                     f32x4_t acc = zero4();
@@ -602,25 +822,25 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                         acc = mma<SPLIT, true>(acc, kh + 32 * ks, kl + 32 * ks, uh + 32 * ks, ul + 32 * ks);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int c = c16 + 4 * lg + e;
-                        Sacc[mt][nt][e] = sm.colGn[c] * Sacc[mt][nt][e] + sm.colGnM[c] * acc[e];
+                        const int c = 16 * mt + 4 * lg + e;
+                        Sacc[i][e] = sm.colGn[c] * Sacc[i][e] + sm.colGnM[c] * acc[e];
                     }
                 }
             }
         }
     }
 
-    if (h_T) {
+    if (h_T && w < 4) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < STW; ++i) {
+            const int st = w * STW + i, mt = st / NT, nt = st % NT;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = (w * MT + mt) * 16 + 4 * lg + e;
-                    const int j = col0 + nt * 16 + lr;
-                    h_T[((n * H + h) * DK + c) * (int64_t)DV + j] = Sacc[mt][nt][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * mt + 4 * lg + e;
+                const int j = col0 + nt * 16 + lr;
+                h_T[((n * H + h) * DK + c) * (int64_t)DV + j] = Sacc[i][e];
+            }
+        }
     }
 }
 
