@@ -50,8 +50,15 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
                                     int32_t num_seqs, kda_dtype_t io_dtype) {
     (void)io_dtype;
     if (B <= 0 || T < 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
-    const int64_t n = num_seqs > 0 ? num_seqs : B;
-    return kda::chunk_fwd_workspace_bytes((int64_t)B * T, H, d_k, d_v, n);
+    if (!valid_dtype(io_dtype)) return 0;
+    kda::ChunkArgs a = {};
+    a.varlen = num_seqs > 0;
+    a.num_seqs = num_seqs > 0 ? num_seqs : B;
+    a.seq_len = T;
+    a.total_tokens = (int64_t)B * T;
+    a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.io_bf16 = io_dtype == KDA_BF16;
+    return kda::chunk_fwd_workspace_bytes(a);
 }
 
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
@@ -83,17 +90,18 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
         if (!aligned_to(beta, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
     }
     if ((h0 && !aligned16(h0)) || (h_T && !aligned16(h_T))) return KDA_ERR_INVALID_ARGUMENT;
-    const size_t need = kda::chunk_fwd_workspace_bytes((int64_t)B * T, H, d_k, d_v, N);
+    kda::ChunkArgs a = {};
+    a.varlen = cu_seqlens != nullptr;
+    a.num_seqs = N; a.seq_len = T; a.total_tokens = (int64_t)B * T;
+    a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
+    const size_t need = kda::chunk_fwd_workspace_bytes(a);
     if (need > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
     if (!have_tokens && !h_T) return KDA_OK;  // nothing to compute or write
 
-    kda::ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
-    a.num_seqs = N; a.seq_len = T; a.total_tokens = (int64_t)B * T;
-    a.H = H; a.d_k = d_k; a.d_v = d_v;
-    a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     g_hip_error[0] = '\0';
     if (kda::launch_chunk_fwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)

@@ -1,0 +1,848 @@
+// kda_chunk2.hip -- chunkwise KDA forward for bf16 I/O in two kernels.
+//
+// The chunkwise form (KimiLinear article, section 3.1) splits each chunk's work
+// into a part that does not depend on the state -- the in-chunk log-decay
+// cumsum, the decayed key/query operands, the decay-weighted Gram blocks A and
+// P and the UT transform T = (I + A)^{-1} -- and a part that carries the state
+// from chunk to chunk.  Only the second part is sequential.  Here:
+//
+//   chunk_prep_kernel   one workgroup per (chunk, head), all chunks in parallel:
+//                       computes the state-independent part once and writes a
+//                       compact record per chunk-head to the workspace;
+//   chunk_state_kernel  one workgroup per (sequence, head, block of BV value
+//                       columns): walks the chunks of its sequence, keeping the
+//                       fp32 state block in registers, and reads the records.
+//
+// Per chunk with start state S, with the operands of the record
+// (m = g_n / 2 per channel, see kda_chunk.hip for the derivation):
+//   Y = KA (e^m . S),  Z = QA (e^m . S)            KA = K.e^{G-m}, QA = Q.e^{G-m}
+//   X = diag(beta) (V - Y),  U = T X
+//   O = Z + P U
+//   S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) (KI^T U)    KI = K.e^{m-G}
+// Chunks whose in-chunk decay exceeds the matrix-core range are flagged by the
+// prep kernel and run token by token in the state kernel.
+//
+// Record layout (bytes, for d_k = DK): KA bf16[64][DK], QA bf16[64][DK],
+// KIt bf16[DK][64], T hi/lo bf16[2][64][64], P hi/lo bf16[2][64][64],
+// e^m, e^{g_n}, e^{g_n-m} fp32[3][DK], beta fp32[64], flags int32[4]; padded
+// to a multiple of 256 bytes.  Upper 16x16 blocks of T and P that the state
+// kernel's 32-wide k-steps touch are stored as zeros.
+#include "kda_chunk_common.h"
+#include "kda_launch.h"
+
+#include <stdio.h>
+#include <stdlib.h>
+
+namespace kda {
+namespace {
+
+template <int DK> struct Rec {
+    static constexpr size_t KA = 0;
+    static constexpr size_t QA = KA + (size_t)kC * DK * 2;
+    static constexpr size_t KIT = QA + (size_t)kC * DK * 2;
+    static constexpr size_t T = KIT + (size_t)DK * kC * 2;
+    static constexpr size_t P = T + 2 * (size_t)kC * kC * 2;
+    static constexpr size_t COL = P + 2 * (size_t)kC * kC * 2;
+    static constexpr size_t BETA = COL + 3 * (size_t)DK * 4;
+    static constexpr size_t FLAG = BETA + (size_t)kC * 4;
+    static constexpr size_t BYTES = ((FLAG + 16) + 255) / 256 * 256;
+};
+
+constexpr size_t kHeaderBytes = 256;
+
+size_t plan_bytes(int64_t num_seqs) { return ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256; }
+
+int64_t max_chunks(const ChunkArgs &a) {
+    if (a.varlen) return (a.total_tokens + kC - 1) / kC + a.num_seqs;
+    return a.num_seqs * ((a.seq_len + kC - 1) / kC);
+}
+
+// chunk_off[n] = number of chunks of sequences 0..n-1 (exclusive prefix sum of
+// ceil(L_n / 64)); chunk_off[N] = total.  One workgroup.
+__global__ __launch_bounds__(256) void chunk_plan_kernel(const int32_t *__restrict__ cu, int64_t N,
+                                                         int32_t *__restrict__ chunk_off) {
+    __shared__ int32_t part[256];
+    __shared__ int32_t carry;
+    const int t = threadIdx.x;
+    if (t == 0) carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base <= N; base += 256) {
+        const int64_t n = base + t;
+        int32_t cnt = 0;
+        if (n < N) cnt = (cu[n + 1] - cu[n] + kC - 1) / kC;
+        part[t] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {   // inclusive Hillis-Steele scan
+            const int32_t x = t >= off ? part[t - off] : 0;
+            __syncthreads();
+            part[t] += x;
+            __syncthreads();
+        }
+        if (n <= N) chunk_off[n] = carry + part[t] - cnt;
+        __syncthreads();
+        if (t == 255) carry += part[255];
+        __syncthreads();
+    }
+}
+
+// Finds the sequence and token range of chunk `chunk`; false if past the end.
+__device__ __forceinline__ bool locate_chunk(int64_t chunk, const int32_t *__restrict__ cu,
+                                             const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
+                                             int64_t &n, int64_t &t0, int &nv) {
+    if (cu) {
+        if (chunk >= chunk_off[N]) return false;
+        int64_t lo = 0, hi = N - 1;   // largest n with chunk_off[n] <= chunk (and a non-empty sequence)
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (chunk_off[mid] <= chunk) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+        t0 = cu[n] + (int64_t)kC * (chunk - chunk_off[n]);
+        const int64_t rem = cu[n + 1] - t0;
+        nv = (int)(rem < kC ? rem : kC);
+        return true;
+    }
+    const int64_t cps = (T + kC - 1) / kC;
+    n = chunk / cps;
+    const int64_t c = chunk % cps;
+    t0 = n * T + (int64_t)kC * c;
+    const int64_t rem = T - (int64_t)kC * c;
+    nv = (int)(rem < kC ? rem : kC);
+    return true;
+}
+
+template <int DK>
+struct alignas(16) PrepSmem {
+    static constexpr int KS = DK + 8;
+    static constexpr int TS = kC + 8;
+    static constexpr int FS = 68;
+    union {
+        struct {
+            bf16_t KA[kC][KS];
+            bf16_t QA[kC][KS];
+        } g;                                   // Gram phase
+        struct {
+            bf16_t T[2][kC][TS];               // hi/lo of (I + A)^{-1}
+            float T8[4][2][8][8];
+            float W8[4][8][8];
+        } t;                                   // inversion phase
+    };
+    union {
+        bf16_t KI[kC][KS];                     // K . e^{m-G}
+        bf16_t Tt[2][kC][kC + 4];              // transposed diagonal blocks of T
+    };
+    float A[kC][FS];
+    float tot[DK][kWaves];
+    float beta[kC];
+};
+
+// ---------------------------------------------------------------------------------
+// Prep: one workgroup (8 waves) per (chunk, head).
+template <int DK, typename IO, typename GT>
+__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const GT *__restrict__ log_alpha,
+    const GT *__restrict__ beta, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+    uint8_t *__restrict__ recs, int64_t N, int64_t T, int32_t H) {
+    constexpr int CPL = DK / 64;
+    constexpr int NKS = DK / 32;
+    typedef PrepSmem<DK> Sm;
+    typedef Rec<DK> RL;
+    __shared__ Sm sm;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int64_t chunk = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    int64_t n, t0;
+    int nv;
+    if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
+    uint8_t *rec = recs + (size_t)blockIdx.x * RL::BYTES;
+    bf16_t *gKA = reinterpret_cast<bf16_t *>(rec + RL::KA);
+    bf16_t *gQA = reinterpret_cast<bf16_t *>(rec + RL::QA);
+    bf16_t *gKIt = reinterpret_cast<bf16_t *>(rec + RL::KIT);
+    bf16_t *gT = reinterpret_cast<bf16_t *>(rec + RL::T);
+    bf16_t *gP = reinterpret_cast<bf16_t *>(rec + RL::P);
+    float *gCol = reinterpret_cast<float *>(rec + RL::COL);
+    float *gBeta = reinterpret_cast<float *>(rec + RL::BETA);
+    int32_t *gFlag = reinterpret_cast<int32_t *>(rec + RL::FLAG);
+
+    // ---- load this chunk (rows past the end read the last row and are zeroed)
+    ChunkRegs<DK, 16, IO, GT> in;
+    in.load(q, k, q, log_alpha, beta, t0, nv, H, h, 0, 0, w, l, lg, lr, false);
+    const bool partial = nv < kC;
+    float csum[8][CPL];
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float x = vget(in.la[i], cc) * kLog2e;
+            if (partial && 8 * w + i >= nv) x = 0.f;
+            csum[i][cc] = i ? csum[i - 1][cc] + x : x;
+        }
+        sm.tot[l * CPL + cc][w] = csum[7][cc];
+    }
+    if (w == 0) {
+        const float b = (l < nv) ? in.bt : 0.f;
+        sm.beta[l] = b;
+        gBeta[l] = b;
+    }
+    lds_barrier();
+    float m2[CPL];
+    bool big = false;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        const int c = l * CPL + cc;
+        const float4 ta = reinterpret_cast<const float4 *>(&sm.tot[c][0])[0];
+        const float4 tb = reinterpret_cast<const float4 *>(&sm.tot[c][0])[1];
+        const float tw[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+        float pre = 0.f, all = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            all += tw[ww];
+            if (ww < w) pre += tw[ww];
+        }
+        m2[cc] = 0.5f * all;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) csum[i][cc] += pre;
+        big = big || !(-all <= kMaxRange2);
+        if (w == 0) {
+            gCol[c] = kexp2<false>(m2[cc]);
+            gCol[DK + c] = kexp2<false>(all);
+            gCol[2 * DK + c] = kexp2<false>(all - m2[cc]);
+        }
+    }
+    const bool slow = __ballot(big) != 0;   // same totals in every wave: uniform
+    if (tid == 0) gFlag[0] = slow ? 1 : 0;
+    if (slow) return;                        // the state kernel runs this chunk token by token
+
+    // ---- decayed operands: LDS for the Gram products, record for the state kernel
+    {
+        float e1[8][CPL], e2[8][CPL];
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            float al[8];
+            al[0] = 1.f;
+#pragma unroll
+            for (int i = 1; i < 8; ++i) {
+                float x = vget(in.la[i], cc) * kLog2e;
+                if (partial && 8 * w + i >= nv) x = 0.f;
+                al[i] = kexp2<false>(x);
+            }
+            e1[0][cc] = kexp2<false>(csum[0][cc] - m2[cc]);
+#pragma unroll
+            for (int i = 1; i < 8; ++i) e1[i][cc] = e1[i - 1][cc] * al[i];
+            e2[7][cc] = kexp2<false>(m2[cc] - csum[7][cc]);
+#pragma unroll
+            for (int i = 6; i >= 0; --i) e2[i][cc] = e2[i + 1][cc] * al[i + 1];
+        }
+        if (partial) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (8 * w + i >= nv) {
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc) e1[i][cc] = e2[i][cc] = 0.f;
+                }
+        }
+        bf16x8_t kit[CPL];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * w + i;
+            bf16_t ka[CPL], qa[CPL], ki[CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float kv = vget(in.kk[i], cc), qv = vget(in.qq[i], cc);
+                ka[cc] = (bf16_t)(kv * e1[i][cc]);
+                qa[cc] = (bf16_t)(qv * e1[i][cc]);
+                ki[cc] = (bf16_t)(kv * e2[i][cc]);
+                kit[cc][i] = ki[cc];
+            }
+            if constexpr (CPL == 2) {
+                bf16x2_t p;
+                p[0] = ka[0]; p[1] = ka[1];
+                *reinterpret_cast<bf16x2_t *>(&sm.g.KA[r][2 * l]) = p;
+                *reinterpret_cast<bf16x2_t *>(&gKA[r * DK + 2 * l]) = p;
+                p[0] = qa[0]; p[1] = qa[1];
+                *reinterpret_cast<bf16x2_t *>(&sm.g.QA[r][2 * l]) = p;
+                *reinterpret_cast<bf16x2_t *>(&gQA[r * DK + 2 * l]) = p;
+                p[0] = ki[0]; p[1] = ki[1];
+                *reinterpret_cast<bf16x2_t *>(&sm.KI[r][2 * l]) = p;
+            } else {
+                sm.g.KA[r][l] = ka[0];
+                gKA[r * DK + l] = ka[0];
+                sm.g.QA[r][l] = qa[0];
+                gQA[r * DK + l] = qa[0];
+                sm.KI[r][l] = ki[0];
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+            *reinterpret_cast<bf16x8_t *>(&gKIt[(l * CPL + cc) * kC + 8 * w]) = kit[cc];
+    }
+    lds_barrier();
+
+    // ---- Gram blocks: A (fp32, LDS) and P (hi/lo, record)
+    {
+        auto gram = [&](int tile, f32x4_t &acc, bool &isP, int &R, int &I) {
+            isP = tile >= 10;
+            lower_block(isP ? tile - 10 : tile, R, I);
+            const bf16_t *ah = isP ? &sm.g.QA[16 * R + lr][8 * lg] : &sm.g.KA[16 * R + lr][8 * lg];
+            const bf16_t *bh = &sm.KI[16 * I + lr][8 * lg];
+            acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) acc = mfma16(lds_ld8(ah + 32 * ks), lds_ld8(bh + 32 * ks), acc);
+        };
+        auto finish = [&](bool isP, int R, int I, const f32x4_t &acc) {
+            const int i = 16 * I + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * lg + e;
+                if (!isP) {
+                    sm.A[r][i] = (i < r) ? sm.beta[r] * acc[e] : 0.f;
+                } else {
+                    bf16_t hh, ll;
+                    split_bf16((i <= r) ? acc[e] : 0.f, hh, ll);
+                    gP[r * kC + i] = hh;
+                    gP[kC * kC + r * kC + i] = ll;
+                }
+            }
+        };
+        f32x4_t a0, a1;
+        bool p0, p1;
+        int R0, I0, R1, I1;
+        gram(w, a0, p0, R0, I0);
+        gram(w + 8, a1, p1, R1, I1);
+        finish(p0, R0, I0, a0);
+        finish(p1, R1, I1, a1);
+        if (w < 4) {
+            gram(w + 16, a0, p0, R0, I0);
+            finish(p0, R0, I0, a0);
+        } else {
+            // zeros for the upper blocks (0,1) and (2,3) of P, read by 32-wide k-steps
+            const int blk = w - 4;                       // 0..3: (block, plane)
+            const int r0 = (blk & 1) ? 32 : 0, c0 = r0 + 16, pl = blk >> 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gP[pl * kC * kC + (r0 + 4 * lg + e) * kC + c0 + lr] = (bf16_t)0.f;
+        }
+    }
+    lds_barrier();
+
+    // ---- diagonal 16x16 blocks of T (waves 0-3)
+    if (w < 4) {
+        const int R = w;
+        float (*t8)[8][8] = sm.t.T8[R];
+        float (*w8)[8] = sm.t.W8[R];
+        if (l < 16) {
+            const int sb = l >> 3, j = l & 7, base = 16 * R + 8 * sb;
+            float a[8][8];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) {
+                const float4 x0 = *reinterpret_cast<const float4 *>(&sm.A[base + r][base]);
+                const float4 x1 = *reinterpret_cast<const float4 *>(&sm.A[base + r][base + 4]);
+                a[r][0] = x0.x; a[r][1] = x0.y; a[r][2] = x0.z; a[r][3] = x0.w;
+                a[r][4] = x1.x; a[r][5] = x1.y; a[r][6] = x1.z; a[r][7] = x1.w;
+            }
+            float t[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+                for (int mm = 0; mm < r; ++mm) {
+                    if (mm & 1) s1 -= a[r][mm] * t[mm];
+                    else s0 -= a[r][mm] * t[mm];
+                }
+                t[r] = s0 + s1;
+                t8[sb][r][j] = t[r];
+            }
+        }
+        wave_lds_sync();
+        const int i8 = l >> 3, j8 = l & 7;
+        {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < 8; mm += 2) {
+                s0 += sm.A[16 * R + 8 + i8][16 * R + mm] * t8[0][mm][j8];
+                s1 += sm.A[16 * R + 8 + i8][16 * R + mm + 1] * t8[0][mm + 1][j8];
+            }
+            w8[i8][j8] = s0 + s1;
+        }
+        wave_lds_sync();
+        float tba;
+        {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < 8; mm += 2) {
+                s0 += t8[1][i8][mm] * w8[mm][j8];
+                s1 += t8[1][i8][mm + 1] * w8[mm + 1][j8];
+            }
+            tba = -(s0 + s1);
+        }
+        const float vals[4] = {t8[0][i8][j8], 0.f, tba, t8[1][i8][j8]};
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const int rr = 16 * R + 8 * (qd >> 1) + i8, cc = 16 * R + 8 * (qd & 1) + j8;
+            bf16_t hh, ll;
+            split_bf16(vals[qd], hh, ll);
+            sm.t.T[0][rr][cc] = hh;
+            sm.t.T[1][rr][cc] = ll;
+            sm.Tt[0][cc][rr] = hh;
+            sm.Tt[1][cc][rr] = ll;
+        }
+    }
+    lds_barrier();
+
+    // ---- off-diagonal blocks of T (waves 0 and 1, matrix cores)
+    if (w < 2) {
+        const int b = w;
+        f32x4_t t10 = zero4();
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const int R = 2 * pr;
+            bf16x4_t ah, al;
+            load_split4(&sm.A[16 * (R + 1) + lr][16 * R + 4 * lg], ah, al);
+            f32x4_t wacc = mma4(zero4(), ah, al, lds_ld4(&sm.Tt[0][16 * R + lr][16 * R + 4 * lg]),
+                                lds_ld4(&sm.Tt[1][16 * R + lr][16 * R + 4 * lg]));
+            bf16x4_t wh, wl;
+            split4(wacc, wh, wl);
+            f32x4_t tacc = mma4(zero4(), lds_ld4(&sm.t.T[0][16 * (R + 1) + lr][16 * (R + 1) + 4 * lg]),
+                                lds_ld4(&sm.t.T[1][16 * (R + 1) + lr][16 * (R + 1) + 4 * lg]), wh, wl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tacc[e] = -tacc[e];
+            store_tile_split(&sm.t.T[0][0][0], &sm.t.T[1][0][0], Sm::TS, 16 * (R + 1), 16 * R, tacc, lr, lg);
+            if (pr == 0) t10 = tacc;
+        }
+        wave_lds_sync();
+        f32x4_t w2[2];
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+            const int a = 2 + a2;
+            bf16x4_t ah, al;
+            w2[a2] = zero4();
+            if (b == 0) {
+                load_split4(&sm.A[16 * a + lr][4 * lg], ah, al);
+                w2[a2] = mma4(w2[a2], ah, al, lds_ld4(&sm.Tt[0][lr][4 * lg]), lds_ld4(&sm.Tt[1][lr][4 * lg]));
+                bf16x4_t th, tl;
+                split4(t10, th, tl);
+                load_split4(&sm.A[16 * a + lr][16 + 4 * lg], ah, al);
+                w2[a2] = mma4(w2[a2], ah, al, th, tl);
+            } else {
+                load_split4(&sm.A[16 * a + lr][16 + 4 * lg], ah, al);
+                w2[a2] = mma4(w2[a2], ah, al, lds_ld4(&sm.Tt[0][16 + lr][16 + 4 * lg]),
+                              lds_ld4(&sm.Tt[1][16 + lr][16 + 4 * lg]));
+            }
+        }
+        bf16x4_t w2h[2], w2l[2];
+        split4(w2[0], w2h[0], w2l[0]);
+        split4(w2[1], w2h[1], w2l[1]);
+        f32x4_t t2b = mma4(zero4(), lds_ld4(&sm.t.T[0][32 + lr][32 + 4 * lg]), lds_ld4(&sm.t.T[1][32 + lr][32 + 4 * lg]),
+                           w2h[0], w2l[0]);
+        f32x4_t t3b = mma4(zero4(), lds_ld4(&sm.t.T[0][48 + lr][32 + 4 * lg]), lds_ld4(&sm.t.T[1][48 + lr][32 + 4 * lg]),
+                           w2h[0], w2l[0]);
+        t3b = mma4(t3b, lds_ld4(&sm.t.T[0][48 + lr][48 + 4 * lg]), lds_ld4(&sm.t.T[1][48 + lr][48 + 4 * lg]), w2h[1],
+                   w2l[1]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            t2b[e] = -t2b[e];
+            t3b[e] = -t3b[e];
+        }
+        store_tile_split(&sm.t.T[0][0][0], &sm.t.T[1][0][0], Sm::TS, 32, 16 * b, t2b, lr, lg);
+        store_tile_split(&sm.t.T[0][0][0], &sm.t.T[1][0][0], Sm::TS, 48, 16 * b, t3b, lr, lg);
+    }
+    lds_barrier();
+
+    // ---- T (both planes, zeros above the block diagonal) to the record
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = tid + kThreads * it;         // 0..1023: (plane, row, 16-byte column group)
+        const int pl = idx >> 9, r = (idx >> 3) & 63, cg = idx & 7;
+        bf16x8_t v = lds_ld8(&sm.t.T[pl][r][8 * cg]);
+        if ((cg >> 1) > (r >> 4)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (bf16_t)0.f;
+        }
+        *reinterpret_cast<bf16x8_t *>(&gT[pl * kC * kC + r * kC + 8 * cg]) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// State: one workgroup (8 waves) per (sequence, head, BV value columns).
+template <int DK, int BV>
+struct alignas(16) StateSmem {
+    static constexpr int KS = DK + 8;
+    static constexpr int TS = kC + 8;
+    bf16_t S[BV][KS];          // (Diag(e^m) S)^T, single bf16
+    bf16_t X[2][BV][TS];       // hi/lo of X^T
+    bf16_t U[2][BV][TS];       // hi/lo of U^T
+    float red[4][2 * BV + 1];  // token path
+};
+
+// Record operands one wave needs for one chunk, held in registers.  Waves 4-7
+// (output role) and waves 0-3 (state role) interpret the same 16-byte slots
+// differently, so one register set serves both roles.  Each group is reloaded
+// for the next chunk right after the current chunk has consumed it, giving every
+// load about one chunk of time to arrive.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DK, int BV> struct StateRegs {
+    static constexpr int NKS = DK / 32, NT = BV / 16, STW = StateTiles<DK, BV>::STW;
+    // output role: ka[NKS] qa[NKS] ph[2] pl[2] vv[NT] bt
+    static constexpr int O_KA = 0, O_QA = NKS, O_PH = 2 * NKS, O_PL = 2 * NKS + 2, O_VV = 2 * NKS + 4,
+                         O_BT = 2 * NKS + 4 + NT, O_END = 2 * NKS + 5 + NT;
+    // state role: th[2] tl[2] kit[STW][2] cm[STW] cg[STW] cgm[STW]
+    static constexpr int S_TH = 0, S_TL = 2, S_KIT = 4, S_CM = 4 + 2 * STW, S_CG = 4 + 3 * STW,
+                         S_CGM = 4 + 4 * STW, S_END = 4 + 5 * STW;
+    static constexpr int NSLOT = O_END > S_END ? O_END : S_END;
+    u32x4_t s[NSLOT];
+    int slow;
+
+    __device__ __forceinline__ bf16x8_t b8(int i) const { return __builtin_bit_cast(bf16x8_t, s[i]); }
+    // The element is copied to a scalar before the cast: clang's __builtin_bit_cast
+    // of a vector-element lvalue reads element 0 whatever the index.
+    __device__ __forceinline__ float f(int i, int e) const {
+        const unsigned u = s[i][e];
+        return __builtin_bit_cast(float, u);
+    }
+    __device__ __forceinline__ void put8(int i, const bf16_t *p) {
+        s[i] = __builtin_bit_cast(u32x4_t, *reinterpret_cast<const bf16x8_t *>(p));
+    }
+    __device__ __forceinline__ void putf(int i, int e, float x) { s[i][e] = __builtin_bit_cast(unsigned, x); }
+
+    // flag (all waves) and e^m (state role)
+    __device__ __forceinline__ void load_flag_cm(const uint8_t *rec, int w, int lg) {
+        slow = *reinterpret_cast<const int32_t *>(rec + Rec<DK>::FLAG);
+        if (w < 4) {
+            const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int mt = (w * STW + i) / NT;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) putf(S_CM + i, e, col[16 * mt + 4 * lg + e]);
+            }
+        }
+    }
+    // decayed keys/queries of row block w - 4 (output role)
+    __device__ __forceinline__ void load_kq(const uint8_t *rec, int w, int lr, int lg) {
+        if (w >= 4) {
+            const int rb = w - 4;
+            const bf16_t *a = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KA) + (16 * rb + lr) * DK + 8 * lg;
+            const bf16_t *b = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::QA) + (16 * rb + lr) * DK + 8 * lg;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                put8(O_KA + ks, a + 32 * ks);
+                put8(O_QA + ks, b + 32 * ks);
+            }
+        }
+    }
+    // values and beta of row block w - 4 (output role)
+    template <typename IO>
+    __device__ __forceinline__ void load_vb(const uint8_t *rec, const IO *__restrict__ v, int64_t tbase, int nv,
+                                            int H, int h, int DV, int col0, int w, int lr, int lg) {
+        if (w >= 4) {
+            const int rb = w - 4;
+            const float *b = reinterpret_cast<const float *>(rec + Rec<DK>::BETA) + 16 * rb + 4 * lg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) putf(O_BT, e, b[e]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * lg + e;
+                    const int rr = r < nv ? r : nv - 1;
+                    putf(O_VV + nt, e, to_f32(v[((tbase + rr) * H + h) * (int64_t)DV + col0 + nt * 16 + lr]));
+                }
+        }
+    }
+    // rows of T (state role)
+    __device__ __forceinline__ void load_t(const uint8_t *rec, int w, int lr, int lg) {
+        if (w < 4) {
+            const bf16_t *t = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::T) + (16 * w + lr) * kC + 8 * lg;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                put8(S_TH + ks, t + 32 * ks);
+                put8(S_TL + ks, t + kC * kC + 32 * ks);
+            }
+        }
+    }
+    // rows of P (output role)
+    __device__ __forceinline__ void load_p(const uint8_t *rec, int w, int lr, int lg) {
+        if (w >= 4) {
+            const bf16_t *p = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::P) + (16 * (w - 4) + lr) * kC + 8 * lg;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                put8(O_PH + ks, p + 32 * ks);
+                put8(O_PL + ks, p + kC * kC + 32 * ks);
+            }
+        }
+    }
+    // transposed decayed keys and the state-update scales (state role)
+    __device__ __forceinline__ void load_kit(const uint8_t *rec, int w, int lr, int lg) {
+        if (w < 4) {
+            const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int mt = (w * STW + i) / NT;
+                const bf16_t *kt = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KIT) + (16 * mt + lr) * kC + 8 * lg;
+                put8(S_KIT + 2 * i, kt);
+                put8(S_KIT + 2 * i + 1, kt + 32);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * mt + 4 * lg + e;
+                    putf(S_CG + i, e, col[DK + c]);
+                    putf(S_CGM + i, e, col[2 * DK + c]);
+                }
+            }
+        }
+    }
+};
+
+template <int DK, int BV, typename IO, typename GT>
+__global__ __launch_bounds__(kThreads) void chunk_state_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ chunk_off,
+    const uint8_t *__restrict__ recs, IO *__restrict__ o, float *__restrict__ h_T, int64_t seq_len,
+    int32_t H, int32_t DV, int64_t num_chains) {
+    constexpr int NKS = DK / 32;
+    constexpr int NT = BV / 16;
+    constexpr int STW = StateTiles<DK, BV>::STW;
+    typedef StateSmem<DK, BV> Sm;
+    typedef Rec<DK> RL;
+    __shared__ Sm sm;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t wg = blockIdx.x;
+    const int64_t chain = wg % num_chains;
+    const int jb = (int)(wg / num_chains);
+    const int64_t n = chain / H;
+    const int h = (int)(chain % H);
+    int64_t bos, eos, c0;
+    if (cu_seqlens) {
+        bos = cu_seqlens[n];
+        eos = cu_seqlens[n + 1];
+        c0 = chunk_off[n];
+    } else {
+        bos = n * seq_len;
+        eos = bos + seq_len;
+        c0 = n * ((seq_len + kC - 1) / kC);
+    }
+    const int col0 = jb * BV;
+    const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
+
+    f32x4_t Sacc[STW];
+#pragma unroll
+    for (int i = 0; i < STW; ++i) {
+        const int st = w * STW + i, mt = st / NT, nt = st % NT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 16 * mt + 4 * lg0 + e;
+            const int j = col0 + nt * 16 + lr0;
+            Sacc[i][e] = (h0 && w < 4) ? h0[((n * H + h) * DK + c) * (int64_t)DV + j] : 0.f;
+        }
+    }
+
+    StateRegs<DK, BV> R;
+    if (bos < eos) {
+        const uint8_t *rec = recs + (size_t)(c0 * H + h) * RL::BYTES;
+        const int nv0 = (int)((eos - bos) < kC ? (eos - bos) : kC);
+        R.load_flag_cm(rec, w, lg0);
+        R.load_kq(rec, w, lr0, lg0);
+        R.template load_vb<IO>(rec, v, bos, nv0, H, h, DV, col0, w, lr0, lg0);
+        R.load_t(rec, w, lr0, lg0);
+        R.load_p(rec, w, lr0, lg0);
+        R.load_kit(rec, w, lr0, lg0);
+    }
+    f32x4_t accZ[NT];
+    int64_t ci = c0;
+    for (int64_t tbase = bos; tbase < eos; tbase += kC, ++ci) {
+        int tl_;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
+        const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
+        const int nv = (int)((eos - tbase) < kC ? (eos - tbase) : kC);
+        const bool has_next = tbase + kC < eos;
+        const int nvn = has_next ? (int)((eos - tbase - kC) < kC ? (eos - tbase - kC) : kC) : 0;
+        const uint8_t *recn = recs + (size_t)((ci + 1) * H + h) * RL::BYTES;
+        lds_barrier();
+        const bool slow = __builtin_amdgcn_readfirstlane(R.slow) != 0;
+        if (slow) {
+            for (int r = 0; r < nv; ++r)
+                token_update<DK, BV, IO, GT>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h, DV, col0,
+                                             w, lg, lr);
+            if (has_next) {
+                R.load_flag_cm(recn, w, lg);
+                R.load_kq(recn, w, lr, lg);
+                R.template load_vb<IO>(recn, v, tbase + kC, nvn, H, h, DV, col0, w, lr, lg);
+                R.load_t(recn, w, lr, lg);
+                R.load_p(recn, w, lr, lg);
+                R.load_kit(recn, w, lr, lg);
+            }
+            continue;
+        }
+        // ---- S' = Diag(e^m) S (waves 0-3)
+        if (w < 4) {
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int st = w * STW + i, mt = st / NT, nt = st % NT;
+                bf16x4_t sv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[e] = (bf16_t)(R.f(StateRegs<DK, BV>::S_CM + i, e) * Sacc[i][e]);
+                *reinterpret_cast<bf16x4_t *>(&sm.S[nt * 16 + lr][16 * mt + 4 * lg]) = sv;
+            }
+        }
+        if (has_next) R.load_flag_cm(recn, w, lg);
+        lds_barrier();
+        // ---- Y, Z, X (waves 4-7)
+        if (w >= 4) {
+            const int rb = w - 4;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bf16_t *sh = &sm.S[nt * 16 + lr][8 * lg];
+                f32x4_t accY = zero4();
+                accZ[nt] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const bf16x8_t sb = lds_ld8(sh + 32 * ks);
+                    accY = mfma16(R.b8(StateRegs<DK, BV>::O_KA + ks), sb, accY);
+                    accZ[nt] = mfma16(R.b8(StateRegs<DK, BV>::O_QA + ks), sb, accZ[nt]);
+                }
+                f32x4_t x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * lg + e;
+                    x[e] = (r < nv) ? R.f(StateRegs<DK, BV>::O_BT, e) * (R.f(StateRegs<DK, BV>::O_VV + nt, e) - accY[e]) : 0.f;
+                }
+                const int jl = nt * 16 + lr;
+                store_split4(&sm.X[0][jl][16 * rb + 4 * lg], &sm.X[1][jl][16 * rb + 4 * lg], x);
+            }
+            if (has_next) {
+                R.load_kq(recn, w, lr, lg);
+                R.template load_vb<IO>(recn, v, tbase + kC, nvn, H, h, DV, col0, w, lr, lg);
+            }
+        }
+        lds_barrier();
+        // ---- U = T X (waves 0-3: row block R = w)
+        if (w < 4) {
+            const int nks = (w >> 1) + 1;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bf16_t *xh = &sm.X[0][nt * 16 + lr][8 * lg];
+                const bf16_t *xl = &sm.X[1][nt * 16 + lr][8 * lg];
+                f32x4_t acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks < nks) {
+                        const bf16x8_t bh = lds_ld8(xh + 32 * ks), bl = lds_ld8(xl + 32 * ks);
+                        acc = mfma16(R.b8(StateRegs<DK, BV>::S_TH + ks), bh, acc);
+                        acc = mfma16(R.b8(StateRegs<DK, BV>::S_TH + ks), bl, acc);
+                        acc = mfma16(R.b8(StateRegs<DK, BV>::S_TL + ks), bh, acc);
+                    }
+                }
+                const int jl = nt * 16 + lr;
+                store_split4(&sm.U[0][jl][16 * w + 4 * lg], &sm.U[1][jl][16 * w + 4 * lg], acc);
+            }
+            if (has_next) R.load_t(recn, w, lr, lg);
+        }
+        lds_barrier();
+        // ---- O = Z + P U (waves 4-7);  state update (waves 0-3)
+        if (w >= 4) {
+            const int rb = w - 4;
+            const int nks = (rb >> 1) + 1;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bf16_t *uh = &sm.U[0][nt * 16 + lr][8 * lg];
+                const bf16_t *ul = &sm.U[1][nt * 16 + lr][8 * lg];
+                f32x4_t acc = accZ[nt];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks < nks) {
+                        const bf16x8_t bh = lds_ld8(uh + 32 * ks), bl = lds_ld8(ul + 32 * ks);
+                        acc = mfma16(R.b8(StateRegs<DK, BV>::O_PH + ks), bh, acc);
+                        acc = mfma16(R.b8(StateRegs<DK, BV>::O_PH + ks), bl, acc);
+                        acc = mfma16(R.b8(StateRegs<DK, BV>::O_PL + ks), bh, acc);
+                    }
+                }
+                const int jl = nt * 16 + lr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * lg + e;
+                    if (r < nv) o[((tbase + r) * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(acc[e]);
+                }
+            }
+            if (has_next) R.load_p(recn, w, lr, lg);
+        } else {
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int st = w * STW + i, nt = st % NT;
+                const bf16_t *uh = &sm.U[0][nt * 16 + lr][8 * lg];
+                const bf16_t *ul = &sm.U[1][nt * 16 + lr][8 * lg];
+                f32x4_t acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    acc = mfma16(R.b8(StateRegs<DK, BV>::S_KIT + 2 * i + ks), lds_ld8(uh + 32 * ks), acc);
+                    acc = mfma16(R.b8(StateRegs<DK, BV>::S_KIT + 2 * i + ks), lds_ld8(ul + 32 * ks), acc);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sacc[i][e] = R.f(StateRegs<DK, BV>::S_CG + i, e) * Sacc[i][e] + R.f(StateRegs<DK, BV>::S_CGM + i, e) * acc[e];
+            }
+            if (has_next) R.load_kit(recn, w, lr, lg);
+        }
+    }
+
+    if (h_T && w < 4) {
+#pragma unroll
+        for (int i = 0; i < STW; ++i) {
+            const int st = w * STW + i, mt = st / NT, nt = st % NT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * mt + 4 * lg0 + e;
+                const int j = col0 + nt * 16 + lr0;
+                h_T[((n * H + h) * DK + c) * (int64_t)DV + j] = Sacc[i][e];
+            }
+        }
+    }
+}
+
+template <int DK, typename IO, typename GT>
+hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
+    uint8_t *ws = reinterpret_cast<uint8_t *>(a.workspace);
+    int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + kHeaderBytes);
+    uint8_t *recs = ws + kHeaderBytes + plan_bytes(a.num_seqs);
+    if (a.varlen)
+        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
+    const int64_t nprep = max_chunks(a) * a.H;
+    if (nprep > 0)
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, IO, GT>), dim3((unsigned)nprep), dim3(kThreads), 0, st,
+                           (const IO *)a.q, (const IO *)a.k, (const GT *)a.log_alpha, (const GT *)a.beta,
+                           a.cu_seqlens, (const int32_t *)chunk_off, recs, a.num_seqs, a.seq_len, a.H);
+    const int64_t chains = a.num_seqs * (int64_t)a.H;
+    if (bv == 32)
+        hipLaunchKernelGGL((chunk_state_kernel<DK, 32, IO, GT>), dim3((unsigned)(chains * (a.d_v / 32))),
+                           dim3(kThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+                           (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
+                           (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains);
+    else
+        hipLaunchKernelGGL((chunk_state_kernel<DK, 16, IO, GT>), dim3((unsigned)(chains * (a.d_v / 16))),
+                           dim3(kThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+                           (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
+                           (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t two_kernel_workspace_bytes(const ChunkArgs &a) {
+    if (a.total_tokens <= 0) return 0;
+    const size_t rec = a.d_k == 128 ? Rec<128>::BYTES : Rec<64>::BYTES;
+    return kHeaderBytes + plan_bytes(a.num_seqs) + (size_t)max_chunks(a) * a.H * rec;
+}
+
+hipError_t launch_chunk_fwd_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
+    if (a.d_k == 128)
+        return a.gate_bf16 ? launch_two_kernel<128, bf16_t, bf16_t>(a, bv, st)
+                           : launch_two_kernel<128, bf16_t, float>(a, bv, st);
+    return a.gate_bf16 ? launch_two_kernel<64, bf16_t, bf16_t>(a, bv, st)
+                       : launch_two_kernel<64, bf16_t, float>(a, bv, st);
+}
+
+}  // namespace kda

@@ -17,6 +17,7 @@ struct ChunkArgs {
     int64_t total_tokens;       // B*T
     int32_t H, d_k, d_v;
     int32_t io_bf16, gate_bf16; // 1 = bf16, 0 = fp32
+    int32_t varlen;             // cu_seqlens given (sequences packed along T)
     void *workspace;
     size_t workspace_bytes;
 };
@@ -34,7 +35,7 @@ struct DecodeArgs {
 // text is copied into err (err_len bytes, NUL-terminated).
 int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len);
 int launch_decode_step(const DecodeArgs &a, void *stream, char *err, size_t err_len);
-size_t chunk_fwd_workspace_bytes(int64_t total_tokens, int32_t H, int32_t d_k, int32_t d_v,
-                                 int64_t num_seqs);
+// Workspace for these arguments (pointers are not read).
+size_t chunk_fwd_workspace_bytes(const ChunkArgs &a);
 
 }  // namespace kda

@@ -60,7 +60,11 @@ const char *kda_last_hip_error(void);
 /*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none).
  * Arguments as for kda_chunk_fwd; num_seqs is the number of sequences (B when
- * no cu_seqlens is given).
+ * no cu_seqlens is given).  With bf16 I/O the forward runs in two passes and
+ * the workspace holds, per (chunk, head), the chunk's decayed operands, its
+ * UT-transform matrix and intra-chunk score block (about 82 KiB at d_k = 128,
+ * i.e. about 1.3 KiB per token-head); fp32 I/O needs none.  The size depends
+ * only on the arguments, never on tensor contents.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                     int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
@@ -95,7 +99,10 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
  *   d_k, d_v    each 64 or 128
  *   io_dtype    KDA_BF16 or KDA_F32; gate_dtype likewise
  *   workspace   device scratch of at least kda_chunk_fwd_workspace_size()
- *               bytes (may be NULL when that size is 0)
+ *               bytes (may be NULL when that size is 0), 16-byte aligned,
+ *               owned by the caller; its contents on entry do not matter and
+ *               on return are unspecified.  Two calls in flight at once on
+ *               different streams must not share one workspace.
  *
  * Numerics: the state and every accumulation are fp32; products of chunk
  * operands run on bf16 matrix cores with hi/lo-split operands where precision

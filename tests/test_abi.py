@@ -43,8 +43,24 @@ def test_version_and_status_strings(kda):
 
 
 def test_workspace_size(kda):
-    assert kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_BF16) == 0
+    # bf16 I/O: one per-chunk record per (chunk, head) plus a small header;
+    # fp32 I/O needs none; unsupported sizes report 0.
+    big = kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_BF16)
+    assert big >= 1024 * 32 * 80000
+    assert kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_F32) == 0
     assert kda.kda_chunk_fwd_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
+    # varlen: room for one partial chunk per sequence
+    v1 = kda.kda_chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
+    v0 = kda.kda_chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 0, kda.KDA_BF16)
+    assert v1 > v0 > 0
+
+
+def test_chunk_fwd_requires_workspace(kda):
+    lib = kda.load_library()
+    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    assert chunk(lib, ws=None, wsb=0) == 3
+    assert chunk(lib, ws=P, wsb=need - 1) == 3
+    assert chunk(lib, ws=P + 8, wsb=need) == 1   # misaligned workspace
 
 
 P = 1 << 20   # a fake, 16-byte aligned "device" address; never dereferenced
