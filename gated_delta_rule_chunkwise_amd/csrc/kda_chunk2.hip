@@ -466,7 +466,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// State: one workgroup (8 waves) per (sequence, head, BV value columns).
+// State: one workgroup (8 waves) per (sequence, head, BV value columns).  The
+// waves split into two roles with the same barrier sequence per chunk:
+//   state role  (waves 0-3): own the fp32 state tiles; write e^m.S to LDS, form
+//                            U = T X, update the state with KI^T U;
+//   output role (waves 4-7): row block w-4 of the chunk: Y, Z, X and O = Z + P U.
+// Each role runs its own loop, so each keeps only its own record operands in
+// registers and its loads retire in a fixed order: every operand is reloaded for
+// the next chunk right after its last use, about one chunk ahead of its next use.
 template <int DK, int BV>
 struct alignas(16) StateSmem {
     static constexpr int KS = DK + 8;
@@ -477,159 +484,107 @@ struct alignas(16) StateSmem {
     float red[4][2 * BV + 1];  // token path
 };
 
-// Record operands one wave needs for one chunk, held in registers.  Waves 4-7
-// (output role) and waves 0-3 (state role) interpret the same 16-byte slots
-// differently, so one register set serves both roles.  Each group is reloaded
-// for the next chunk right after the current chunk has consumed it, giving every
-// load about one chunk of time to arrive.
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// The flag is read through a lane-dependent address (always element 0) so that
+// it arrives by a vector load, counted in order with the other record loads,
+// and not by a scalar load that every LDS barrier would wait for.
+__device__ __forceinline__ int load_flag(const uint8_t *rec, size_t off, int tl) {
+    return reinterpret_cast<const int32_t *>(rec + off)[tl >> 10];
+}
 
-template <int DK, int BV> struct StateRegs {
-    static constexpr int NKS = DK / 32, NT = BV / 16, STW = StateTiles<DK, BV>::STW;
-    // output role: ka[NKS] qa[NKS] ph[2] pl[2] vv[NT] bt
-    static constexpr int O_KA = 0, O_QA = NKS, O_PH = 2 * NKS, O_PL = 2 * NKS + 2, O_VV = 2 * NKS + 4,
-                         O_BT = 2 * NKS + 4 + NT, O_END = 2 * NKS + 5 + NT;
-    // state role: th[2] tl[2] kit[STW][2] cm[STW] cg[STW] cgm[STW]
-    static constexpr int S_TH = 0, S_TL = 2, S_KIT = 4, S_CM = 4 + 2 * STW, S_CG = 4 + 3 * STW,
-                         S_CGM = 4 + 4 * STW, S_END = 4 + 5 * STW;
-    static constexpr int NSLOT = O_END > S_END ? O_END : S_END;
-    u32x4_t s[NSLOT];
-    int slow;
+template <int DK, int BV> struct StateRole {
+    static constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
+    bf16x8_t th[2], tl[2];    // rows 16w.. of T (hi, lo)
+    bf16x8_t kit[STW][2];     // KI^T rows of the wave's state tiles
+    f32x4_t cm[STW], cg[STW], cgm[STW];
+    int flag;
 
-    __device__ __forceinline__ bf16x8_t b8(int i) const { return __builtin_bit_cast(bf16x8_t, s[i]); }
-    // The element is copied to a scalar before the cast: clang's __builtin_bit_cast
-    // of a vector-element lvalue reads element 0 whatever the index.
-    __device__ __forceinline__ float f(int i, int e) const {
-        const unsigned u = s[i][e];
-        return __builtin_bit_cast(float, u);
-    }
-    __device__ __forceinline__ void put8(int i, const bf16_t *p) {
-        s[i] = __builtin_bit_cast(u32x4_t, *reinterpret_cast<const bf16x8_t *>(p));
-    }
-    __device__ __forceinline__ void putf(int i, int e, float x) { s[i][e] = __builtin_bit_cast(unsigned, x); }
-
-    // flag (all waves) and e^m (state role)
-    __device__ __forceinline__ void load_flag_cm(const uint8_t *rec, int w, int lg) {
-        slow = *reinterpret_cast<const int32_t *>(rec + Rec<DK>::FLAG);
-        if (w < 4) {
-            const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
+    __device__ __forceinline__ void load_cm(const uint8_t *rec, int w, int lg, int tid) {
+        const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
 #pragma unroll
-            for (int i = 0; i < STW; ++i) {
-                const int mt = (w * STW + i) / NT;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) putf(S_CM + i, e, col[16 * mt + 4 * lg + e]);
-            }
+        for (int i = 0; i < STW; ++i) {
+            const int mt = (w * STW + i) / NT;
+            cm[i] = *reinterpret_cast<const f32x4_t *>(col + 16 * mt + 4 * lg);
         }
+        flag = load_flag(rec, Rec<DK>::FLAG, tid);
     }
-    // decayed keys/queries of row block w - 4 (output role)
-    __device__ __forceinline__ void load_kq(const uint8_t *rec, int w, int lr, int lg) {
-        if (w >= 4) {
-            const int rb = w - 4;
-            const bf16_t *a = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KA) + (16 * rb + lr) * DK + 8 * lg;
-            const bf16_t *b = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::QA) + (16 * rb + lr) * DK + 8 * lg;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                put8(O_KA + ks, a + 32 * ks);
-                put8(O_QA + ks, b + 32 * ks);
-            }
-        }
-    }
-    // values and beta of row block w - 4 (output role)
-    template <typename IO>
-    __device__ __forceinline__ void load_vb(const uint8_t *rec, const IO *__restrict__ v, int64_t tbase, int nv,
-                                            int H, int h, int DV, int col0, int w, int lr, int lg) {
-        if (w >= 4) {
-            const int rb = w - 4;
-            const float *b = reinterpret_cast<const float *>(rec + Rec<DK>::BETA) + 16 * rb + 4 * lg;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) putf(O_BT, e, b[e]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rb + 4 * lg + e;
-                    const int rr = r < nv ? r : nv - 1;
-                    putf(O_VV + nt, e, to_f32(v[((tbase + rr) * H + h) * (int64_t)DV + col0 + nt * 16 + lr]));
-                }
-        }
-    }
-    // rows of T (state role)
     __device__ __forceinline__ void load_t(const uint8_t *rec, int w, int lr, int lg) {
-        if (w < 4) {
-            const bf16_t *t = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::T) + (16 * w + lr) * kC + 8 * lg;
+        const bf16_t *t = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::T) + (16 * w + lr) * kC + 8 * lg;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                put8(S_TH + ks, t + 32 * ks);
-                put8(S_TL + ks, t + kC * kC + 32 * ks);
-            }
+        for (int ks = 0; ks < 2; ++ks) {
+            th[ks] = *reinterpret_cast<const bf16x8_t *>(t + 32 * ks);
+            tl[ks] = *reinterpret_cast<const bf16x8_t *>(t + kC * kC + 32 * ks);
         }
     }
-    // rows of P (output role)
-    __device__ __forceinline__ void load_p(const uint8_t *rec, int w, int lr, int lg) {
-        if (w >= 4) {
-            const bf16_t *p = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::P) + (16 * (w - 4) + lr) * kC + 8 * lg;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                put8(O_PH + ks, p + 32 * ks);
-                put8(O_PL + ks, p + kC * kC + 32 * ks);
-            }
-        }
-    }
-    // transposed decayed keys and the state-update scales (state role)
     __device__ __forceinline__ void load_kit(const uint8_t *rec, int w, int lr, int lg) {
-        if (w < 4) {
-            const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
+        const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
 #pragma unroll
-            for (int i = 0; i < STW; ++i) {
-                const int mt = (w * STW + i) / NT;
-                const bf16_t *kt = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KIT) + (16 * mt + lr) * kC + 8 * lg;
-                put8(S_KIT + 2 * i, kt);
-                put8(S_KIT + 2 * i + 1, kt + 32);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = 16 * mt + 4 * lg + e;
-                    putf(S_CG + i, e, col[DK + c]);
-                    putf(S_CGM + i, e, col[2 * DK + c]);
-                }
-            }
+        for (int i = 0; i < STW; ++i) {
+            const int mt = (w * STW + i) / NT;
+            const bf16_t *kt = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KIT) + (16 * mt + lr) * kC + 8 * lg;
+            kit[i][0] = *reinterpret_cast<const bf16x8_t *>(kt);
+            kit[i][1] = *reinterpret_cast<const bf16x8_t *>(kt + 32);
+            cg[i] = *reinterpret_cast<const f32x4_t *>(col + DK + 16 * mt + 4 * lg);
+            cgm[i] = *reinterpret_cast<const f32x4_t *>(col + 2 * DK + 16 * mt + 4 * lg);
         }
     }
 };
 
-template <int DK, int BV, typename IO, typename GT>
-__global__ __launch_bounds__(kThreads) void chunk_state_kernel(
-    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
-    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
-    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ chunk_off,
-    const uint8_t *__restrict__ recs, IO *__restrict__ o, float *__restrict__ h_T, int64_t seq_len,
-    int32_t H, int32_t DV, int64_t num_chains) {
-    constexpr int NKS = DK / 32;
-    constexpr int NT = BV / 16;
-    constexpr int STW = StateTiles<DK, BV>::STW;
-    typedef StateSmem<DK, BV> Sm;
-    typedef Rec<DK> RL;
-    __shared__ Sm sm;
+template <int DK, int BV, typename IO> struct OutRole {
+    static constexpr int NKS = DK / 32, NT = BV / 16;
+    bf16x8_t ka[NKS], qa[NKS];  // rows 16rb.. of KA, QA
+    bf16x8_t ph[2], pl[2];      // rows 16rb.. of P (hi, lo)
+    IO vv[NT][4];               // values of the rows this lane produces, as loaded
+    f32x4_t bt;                 // beta of those rows
+    int flag;
 
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t wg = blockIdx.x;
-    const int64_t chain = wg % num_chains;
-    const int jb = (int)(wg / num_chains);
-    const int64_t n = chain / H;
-    const int h = (int)(chain % H);
-    int64_t bos, eos, c0;
-    if (cu_seqlens) {
-        bos = cu_seqlens[n];
-        eos = cu_seqlens[n + 1];
-        c0 = chunk_off[n];
-    } else {
-        bos = n * seq_len;
-        eos = bos + seq_len;
-        c0 = n * ((seq_len + kC - 1) / kC);
+    __device__ __forceinline__ void load_kqvb(const uint8_t *rec, const IO *__restrict__ v, int64_t tbase, int nv,
+                                              int H, int h, int DV, int col0, int rb, int lr, int lg, int tid) {
+        const bf16_t *a = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KA) + (16 * rb + lr) * DK + 8 * lg;
+        const bf16_t *b = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::QA) + (16 * rb + lr) * DK + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            ka[ks] = *reinterpret_cast<const bf16x8_t *>(a + 32 * ks);
+            qa[ks] = *reinterpret_cast<const bf16x8_t *>(b + 32 * ks);
+        }
+        bt = *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(rec + Rec<DK>::BETA) + 16 * rb + 4 * lg);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rb + 4 * lg + e;
+                const int rr = r < nv ? r : nv - 1;
+                vv[nt][e] = v[((tbase + rr) * H + h) * (int64_t)DV + col0 + nt * 16 + lr];
+            }
+        flag = load_flag(rec, Rec<DK>::FLAG, tid);
     }
-    const int col0 = jb * BV;
-    const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
+    __device__ __forceinline__ void load_p(const uint8_t *rec, int rb, int lr, int lg) {
+        const bf16_t *p = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::P) + (16 * rb + lr) * kC + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            ph[ks] = *reinterpret_cast<const bf16x8_t *>(p + 32 * ks);
+            pl[ks] = *reinterpret_cast<const bf16x8_t *>(p + kC * kC + 32 * ks);
+        }
+    }
+};
 
+// Chunk geometry of one state workgroup.
+struct ChainRange {
+    int64_t bos, eos, c0;  // token range, index of the first chunk record
+    int64_t n;             // sequence
+    int h, col0;
+};
+
+template <int DK, int BV, typename IO, typename GT>
+__device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const ChainRange &cr,
+                                                const IO *__restrict__ q, const IO *__restrict__ k,
+                                                const IO *__restrict__ v, const GT *__restrict__ log_alpha,
+                                                const GT *__restrict__ beta, const float *__restrict__ h0,
+                                                const uint8_t *__restrict__ recs, IO *__restrict__ o,
+                                                float *__restrict__ h_T, int H, int DV, int w, int tid) {
+    constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
+    typedef Rec<DK> RL;
+    const int h = cr.h, col0 = cr.col0;
+    const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
     f32x4_t Sacc[STW];
 #pragma unroll
     for (int i = 0; i < STW; ++i) {
@@ -637,92 +592,51 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = 16 * mt + 4 * lg0 + e;
-            const int j = col0 + nt * 16 + lr0;
-            Sacc[i][e] = (h0 && w < 4) ? h0[((n * H + h) * DK + c) * (int64_t)DV + j] : 0.f;
+            Sacc[i][e] = h0 ? h0[((cr.n * H + h) * DK + c) * (int64_t)DV + col0 + nt * 16 + lr0] : 0.f;
         }
     }
-
-    StateRegs<DK, BV> R;
-    if (bos < eos) {
-        const uint8_t *rec = recs + (size_t)(c0 * H + h) * RL::BYTES;
-        const int nv0 = (int)((eos - bos) < kC ? (eos - bos) : kC);
-        R.load_flag_cm(rec, w, lg0);
-        R.load_kq(rec, w, lr0, lg0);
-        R.template load_vb<IO>(rec, v, bos, nv0, H, h, DV, col0, w, lr0, lg0);
+    StateRole<DK, BV> R;
+    if (cr.bos < cr.eos) {
+        const uint8_t *rec = recs + (size_t)(cr.c0 * H + h) * RL::BYTES;
+        R.load_cm(rec, w, lg0, tid);
         R.load_t(rec, w, lr0, lg0);
-        R.load_p(rec, w, lr0, lg0);
         R.load_kit(rec, w, lr0, lg0);
     }
-    f32x4_t accZ[NT];
-    int64_t ci = c0;
-    for (int64_t tbase = bos; tbase < eos; tbase += kC, ++ci) {
+    // Each operand group has a single load site per chunk, right after its last
+    // use; the token path of a flagged chunk runs right after the first barrier
+    // and the matrix-core steps are skipped, so both paths share the loads.
+    int64_t ci = cr.c0;
+    for (int64_t tbase = cr.bos; tbase < cr.eos; tbase += kC, ++ci) {
         int tl_;
         asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
         const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
-        const int nv = (int)((eos - tbase) < kC ? (eos - tbase) : kC);
-        const bool has_next = tbase + kC < eos;
-        const int nvn = has_next ? (int)((eos - tbase - kC) < kC ? (eos - tbase - kC) : kC) : 0;
-        const uint8_t *recn = recs + (size_t)((ci + 1) * H + h) * RL::BYTES;
-        lds_barrier();
-        const bool slow = __builtin_amdgcn_readfirstlane(R.slow) != 0;
+        const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
+        // next chunk's record (the current one again on the last chunk, so that
+        // every load is issued on every path and the wait counts stay exact)
+        const int64_t cn = tbase + kC < cr.eos ? ci + 1 : ci;
+        const uint8_t *recn = recs + (size_t)(cn * H + h) * RL::BYTES;
+        lds_barrier();  // B0
+        const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
         if (slow) {
             for (int r = 0; r < nv; ++r)
                 token_update<DK, BV, IO, GT>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h, DV, col0,
                                              w, lg, lr);
-            if (has_next) {
-                R.load_flag_cm(recn, w, lg);
-                R.load_kq(recn, w, lr, lg);
-                R.template load_vb<IO>(recn, v, tbase + kC, nvn, H, h, DV, col0, w, lr, lg);
-                R.load_t(recn, w, lr, lg);
-                R.load_p(recn, w, lr, lg);
-                R.load_kit(recn, w, lr, lg);
-            }
-            continue;
-        }
-        // ---- S' = Diag(e^m) S (waves 0-3)
-        if (w < 4) {
+        } else {
+            // S' = Diag(e^m) S, transposed, to LDS
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
                 const int st = w * STW + i, mt = st / NT, nt = st % NT;
                 bf16x4_t sv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[e] = (bf16_t)(R.f(StateRegs<DK, BV>::S_CM + i, e) * Sacc[i][e]);
+                for (int e = 0; e < 4; ++e) sv[e] = (bf16_t)(R.cm[i][e] * Sacc[i][e]);
                 *reinterpret_cast<bf16x4_t *>(&sm.S[nt * 16 + lr][16 * mt + 4 * lg]) = sv;
             }
         }
-        if (has_next) R.load_flag_cm(recn, w, lg);
-        lds_barrier();
-        // ---- Y, Z, X (waves 4-7)
-        if (w >= 4) {
-            const int rb = w - 4;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bf16_t *sh = &sm.S[nt * 16 + lr][8 * lg];
-                f32x4_t accY = zero4();
-                accZ[nt] = zero4();
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8_t sb = lds_ld8(sh + 32 * ks);
-                    accY = mfma16(R.b8(StateRegs<DK, BV>::O_KA + ks), sb, accY);
-                    accZ[nt] = mfma16(R.b8(StateRegs<DK, BV>::O_QA + ks), sb, accZ[nt]);
-                }
-                f32x4_t x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rb + 4 * lg + e;
-                    x[e] = (r < nv) ? R.f(StateRegs<DK, BV>::O_BT, e) * (R.f(StateRegs<DK, BV>::O_VV + nt, e) - accY[e]) : 0.f;
-                }
-                const int jl = nt * 16 + lr;
-                store_split4(&sm.X[0][jl][16 * rb + 4 * lg], &sm.X[1][jl][16 * rb + 4 * lg], x);
-            }
-            if (has_next) {
-                R.load_kq(recn, w, lr, lg);
-                R.template load_vb<IO>(recn, v, tbase + kC, nvn, H, h, DV, col0, w, lr, lg);
-            }
-        }
-        lds_barrier();
-        // ---- U = T X (waves 0-3: row block R = w)
-        if (w < 4) {
+        R.load_cm(recn, w, lg, tl_);
+        lds_barrier();  // B1: S' visible
+        lds_barrier();  // B2: X visible
+        if (!slow) {
+            // U = T X for row block w (T is lower triangular: blocks right of w are zero)
             const int nks = (w >> 1) + 1;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -733,20 +647,115 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(
                 for (int ks = 0; ks < 2; ++ks) {
                     if (ks < nks) {
                         const bf16x8_t bh = lds_ld8(xh + 32 * ks), bl = lds_ld8(xl + 32 * ks);
-                        acc = mfma16(R.b8(StateRegs<DK, BV>::S_TH + ks), bh, acc);
-                        acc = mfma16(R.b8(StateRegs<DK, BV>::S_TH + ks), bl, acc);
-                        acc = mfma16(R.b8(StateRegs<DK, BV>::S_TL + ks), bh, acc);
+                        acc = mfma16(R.th[ks], bh, acc);
+                        acc = mfma16(R.th[ks], bl, acc);
+                        acc = mfma16(R.tl[ks], bh, acc);
                     }
                 }
                 const int jl = nt * 16 + lr;
                 store_split4(&sm.U[0][jl][16 * w + 4 * lg], &sm.U[1][jl][16 * w + 4 * lg], acc);
             }
-            if (has_next) R.load_t(recn, w, lr, lg);
         }
-        lds_barrier();
-        // ---- O = Z + P U (waves 4-7);  state update (waves 0-3)
-        if (w >= 4) {
-            const int rb = w - 4;
+        R.load_t(recn, w, lr, lg);
+        lds_barrier();  // B3: U visible
+        if (!slow) {
+            // S <- Diag(e^{g_n}) S + Diag(e^{g_n - m}) KI^T U
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int nt = (w * STW + i) % NT;
+                const bf16_t *uh = &sm.U[0][nt * 16 + lr][8 * lg];
+                const bf16_t *ul = &sm.U[1][nt * 16 + lr][8 * lg];
+                f32x4_t acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    acc = mfma16(R.kit[i][ks], lds_ld8(uh + 32 * ks), acc);
+                    acc = mfma16(R.kit[i][ks], lds_ld8(ul + 32 * ks), acc);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sacc[i][e] = R.cg[i][e] * Sacc[i][e] + R.cgm[i][e] * acc[e];
+            }
+        }
+        R.load_kit(recn, w, lr, lg);
+    }
+    if (h_T) {
+#pragma unroll
+        for (int i = 0; i < STW; ++i) {
+            const int st = w * STW + i, mt = st / NT, nt = st % NT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * mt + 4 * lg0 + e;
+                h_T[((cr.n * H + h) * DK + c) * (int64_t)DV + col0 + nt * 16 + lr0] = Sacc[i][e];
+            }
+        }
+    }
+}
+
+template <int DK, int BV, typename IO>
+__device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const ChainRange &cr,
+                                                 const IO *__restrict__ v, const uint8_t *__restrict__ recs,
+                                                 IO *__restrict__ o, int H, int DV, int rb, int tid) {
+    constexpr int NKS = DK / 32, NT = BV / 16;
+    typedef Rec<DK> RL;
+    const int h = cr.h, col0 = cr.col0;
+    OutRole<DK, BV, IO> R;
+    if (cr.bos < cr.eos) {
+        const uint8_t *rec = recs + (size_t)(cr.c0 * H + h) * RL::BYTES;
+        const int nv0 = (int)((cr.eos - cr.bos) < kC ? (cr.eos - cr.bos) : kC);
+        const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
+        R.load_kqvb(rec, v, cr.bos, nv0, H, h, DV, col0, rb, lr0, lg0, tid);
+        R.load_p(rec, rb, lr0, lg0);
+    }
+    f32x4_t accZ[NT];
+    int64_t ci = cr.c0;
+    for (int64_t tbase = cr.bos; tbase < cr.eos; tbase += kC, ++ci) {
+        int tl_;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
+        const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
+        const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
+        // next chunk (the current one again on the last chunk: loads on every path)
+        const bool has_next = tbase + kC < cr.eos;
+        const int64_t cn = has_next ? ci + 1 : ci;
+        const int64_t tn = has_next ? tbase + kC : tbase;
+        const int nvn = (int)((cr.eos - tn) < kC ? (cr.eos - tn) : kC);
+        const uint8_t *recn = recs + (size_t)(cn * H + h) * RL::BYTES;
+        lds_barrier();  // B0
+        const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
+        if (slow) {
+            // the state role runs the chunk token by token: two barriers per token
+            for (int r = 0; r < nv; ++r) {
+                lds_barrier();
+                lds_barrier();
+            }
+        }
+        lds_barrier();  // B1: S' visible
+        if (!slow) {
+            // Y = KA S', Z = QA S', X = diag(beta) (V - Y) for rows 16rb..16rb+15
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bf16_t *sh = &sm.S[nt * 16 + lr][8 * lg];
+                f32x4_t accY = zero4();
+                accZ[nt] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const bf16x8_t sb = lds_ld8(sh + 32 * ks);
+                    accY = mfma16(R.ka[ks], sb, accY);
+                    accZ[nt] = mfma16(R.qa[ks], sb, accZ[nt]);
+                }
+                f32x4_t x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * lg + e;
+                    x[e] = (r < nv) ? R.bt[e] * (to_f32(R.vv[nt][e]) - accY[e]) : 0.f;
+                }
+                const int jl = nt * 16 + lr;
+                store_split4(&sm.X[0][jl][16 * rb + 4 * lg], &sm.X[1][jl][16 * rb + 4 * lg], x);
+            }
+        }
+        R.load_kqvb(recn, v, tn, nvn, H, h, DV, col0, rb, lr, lg, tl_);
+        lds_barrier();  // B2: X visible
+        lds_barrier();  // B3: U visible
+        if (!slow) {
+            // O = Z + P U
             const int nks = (rb >> 1) + 1;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -757,9 +766,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(
                 for (int ks = 0; ks < 2; ++ks) {
                     if (ks < nks) {
                         const bf16x8_t bh = lds_ld8(uh + 32 * ks), bl = lds_ld8(ul + 32 * ks);
-                        acc = mfma16(R.b8(StateRegs<DK, BV>::O_PH + ks), bh, acc);
-                        acc = mfma16(R.b8(StateRegs<DK, BV>::O_PH + ks), bl, acc);
-                        acc = mfma16(R.b8(StateRegs<DK, BV>::O_PL + ks), bh, acc);
+                        acc = mfma16(R.ph[ks], bh, acc);
+                        acc = mfma16(R.ph[ks], bl, acc);
+                        acc = mfma16(R.pl[ks], bh, acc);
                     }
                 }
                 const int jl = nt * 16 + lr;
@@ -769,38 +778,40 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(
                     if (r < nv) o[((tbase + r) * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(acc[e]);
                 }
             }
-            if (has_next) R.load_p(recn, w, lr, lg);
-        } else {
-#pragma unroll
-            for (int i = 0; i < STW; ++i) {
-                const int st = w * STW + i, nt = st % NT;
-                const bf16_t *uh = &sm.U[0][nt * 16 + lr][8 * lg];
-                const bf16_t *ul = &sm.U[1][nt * 16 + lr][8 * lg];
-                f32x4_t acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    acc = mfma16(R.b8(StateRegs<DK, BV>::S_KIT + 2 * i + ks), lds_ld8(uh + 32 * ks), acc);
-                    acc = mfma16(R.b8(StateRegs<DK, BV>::S_KIT + 2 * i + ks), lds_ld8(ul + 32 * ks), acc);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Sacc[i][e] = R.f(StateRegs<DK, BV>::S_CG + i, e) * Sacc[i][e] + R.f(StateRegs<DK, BV>::S_CGM + i, e) * acc[e];
-            }
-            if (has_next) R.load_kit(recn, w, lr, lg);
         }
+        R.load_p(recn, rb, lr, lg);
     }
+}
 
-    if (h_T && w < 4) {
-#pragma unroll
-        for (int i = 0; i < STW; ++i) {
-            const int st = w * STW + i, mt = st / NT, nt = st % NT;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = 16 * mt + 4 * lg0 + e;
-                const int j = col0 + nt * 16 + lr0;
-                h_T[((n * H + h) * DK + c) * (int64_t)DV + j] = Sacc[i][e];
-            }
-        }
+template <int DK, int BV, typename IO, typename GT>
+__global__ __launch_bounds__(kThreads) void chunk_state_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ chunk_off,
+    const uint8_t *__restrict__ recs, IO *__restrict__ o, float *__restrict__ h_T, int64_t seq_len,
+    int32_t H, int32_t DV, int64_t num_chains) {
+    __shared__ StateSmem<DK, BV> sm;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t wg = blockIdx.x;
+    const int64_t chain = wg % num_chains;
+    ChainRange cr;
+    cr.n = chain / H;
+    cr.h = (int)(chain % H);
+    cr.col0 = (int)(wg / num_chains) * BV;
+    if (cu_seqlens) {
+        cr.bos = cu_seqlens[cr.n];
+        cr.eos = cu_seqlens[cr.n + 1];
+        cr.c0 = chunk_off[cr.n];
+    } else {
+        cr.bos = cr.n * seq_len;
+        cr.eos = cr.bos + seq_len;
+        cr.c0 = cr.n * ((seq_len + kC - 1) / kC);
     }
+    if (w < 4)
+        state_role_loop<DK, BV, IO, GT>(sm, cr, q, k, v, log_alpha, beta, h0, recs, o, h_T, H, DV, w, tid);
+    else
+        output_role_loop<DK, BV, IO>(sm, cr, v, recs, o, H, DV, w - 4, tid);
 }
 
 template <int DK, typename IO, typename GT>
