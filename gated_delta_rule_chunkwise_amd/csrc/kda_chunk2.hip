@@ -22,11 +22,19 @@
 // Chunks whose in-chunk decay exceeds the matrix-core range are flagged by the
 // prep kernel and run token by token in the state kernel.
 //
-// Record layout (bytes, for d_k = DK): KA bf16[64][DK], QA bf16[64][DK],
-// KIt bf16[DK][64], T hi/lo bf16[2][64][64], P hi/lo bf16[2][64][64],
-// e^m, e^{g_n}, e^{g_n-m} fp32[3][DK], beta fp32[64], flags int32[4]; padded
-// to a multiple of 256 bytes.  Upper 16x16 blocks of T and P that the state
-// kernel's 32-wide k-steps touch are stored as zeros.
+// Record layout: matrix operands are stored in the order the state kernel's
+// lanes hold them, so that every wave-wide load reads one contiguous 1 KiB (or
+// 512 B) run.  A "fragment" is one 16x32 bf16 operand of the 16x16x32 matrix
+// instruction, lane l holding row l%16, columns 8*(l/16)..+7 (16 bytes at l*16).
+//   KA, QA   fragments (row block rb, k-step ks), rb*NKS + ks, NKS = DK/32
+//   KIt      fragments (key block mt, token k-step ks) of KI^T, mt*2 + ks
+//   T        the six fragments (R, ks <= R/2) of T that a 32-wide k-step reads,
+//            each as hi then lo; blocks above the diagonal inside them are zero
+//   PT       the ten lower tiles (R, I <= R) of P, transposed and in the 16x16x16
+//            operand layout (lane l: P[16R + l%16][16I + 4*(l/16)..+3], 8 bytes),
+//            each as hi then lo
+//   e^m, e^{g_n}, e^{g_n-m} fp32[3][DK], beta fp32[64], flags int32[4];
+// padded to a multiple of 256 bytes.
 #include "kda_chunk_common.h"
 #include "kda_launch.h"
 
@@ -37,16 +45,28 @@ namespace kda {
 namespace {
 
 template <int DK> struct Rec {
+    static constexpr int NKS = DK / 32;
+    static constexpr size_t FRAG = 1024;                          // 64 lanes x 16 bytes
+    static constexpr size_t TILE = 512;                           // 64 lanes x 8 bytes
     static constexpr size_t KA = 0;
-    static constexpr size_t QA = KA + (size_t)kC * DK * 2;
-    static constexpr size_t KIT = QA + (size_t)kC * DK * 2;
-    static constexpr size_t T = KIT + (size_t)DK * kC * 2;
-    static constexpr size_t P = T + 2 * (size_t)kC * kC * 2;
-    static constexpr size_t COL = P + 2 * (size_t)kC * kC * 2;
+    static constexpr size_t QA = KA + 4 * NKS * FRAG;
+    static constexpr size_t KIT = QA + 4 * NKS * FRAG;
+    static constexpr size_t T = KIT + (DK / 16) * 2 * FRAG;
+    static constexpr size_t PT = T + 6 * 2 * FRAG;
+    static constexpr size_t COL = PT + 10 * 2 * TILE;
     static constexpr size_t BETA = COL + 3 * (size_t)DK * 4;
     static constexpr size_t FLAG = BETA + (size_t)kC * 4;
     static constexpr size_t BYTES = ((FLAG + 16) + 255) / 256 * 256;
 };
+
+// Index of the stored T fragment (row block R, k-step ks); k-steps right of the
+// diagonal block are never read and map to ks = 0 (a harmless duplicate load).
+__device__ __forceinline__ int t_frag(int R, int ks) {
+    ks = ks <= (R >> 1) ? ks : 0;
+    return R < 2 ? R : 2 + 2 * (R - 2) + ks;
+}
+// Slot of the lower tile (R, I), I <= R; I > R maps to I = R.
+__device__ __forceinline__ int p_tile(int R, int I) { return (R * (R + 1)) / 2 + (I <= R ? I : R); }
 
 constexpr size_t kHeaderBytes = 256;
 
@@ -159,11 +179,6 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     int nv;
     if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
     uint8_t *rec = recs + (size_t)blockIdx.x * RL::BYTES;
-    bf16_t *gKA = reinterpret_cast<bf16_t *>(rec + RL::KA);
-    bf16_t *gQA = reinterpret_cast<bf16_t *>(rec + RL::QA);
-    bf16_t *gKIt = reinterpret_cast<bf16_t *>(rec + RL::KIT);
-    bf16_t *gT = reinterpret_cast<bf16_t *>(rec + RL::T);
-    bf16_t *gP = reinterpret_cast<bf16_t *>(rec + RL::P);
     float *gCol = reinterpret_cast<float *>(rec + RL::COL);
     float *gBeta = reinterpret_cast<float *>(rec + RL::BETA);
     int32_t *gFlag = reinterpret_cast<int32_t *>(rec + RL::FLAG);
@@ -262,50 +277,72 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
                 bf16x2_t p;
                 p[0] = ka[0]; p[1] = ka[1];
                 *reinterpret_cast<bf16x2_t *>(&sm.g.KA[r][2 * l]) = p;
-                *reinterpret_cast<bf16x2_t *>(&gKA[r * DK + 2 * l]) = p;
                 p[0] = qa[0]; p[1] = qa[1];
                 *reinterpret_cast<bf16x2_t *>(&sm.g.QA[r][2 * l]) = p;
-                *reinterpret_cast<bf16x2_t *>(&gQA[r * DK + 2 * l]) = p;
                 p[0] = ki[0]; p[1] = ki[1];
                 *reinterpret_cast<bf16x2_t *>(&sm.KI[r][2 * l]) = p;
             } else {
                 sm.g.KA[r][l] = ka[0];
-                gKA[r * DK + l] = ka[0];
                 sm.g.QA[r][l] = qa[0];
-                gQA[r * DK + l] = qa[0];
                 sm.KI[r][l] = ki[0];
             }
         }
+        // KI^T: this lane holds 8 consecutive tokens 8w.. of key channel c, i.e. the
+        // 16-byte piece of lane (c%16 + 16*(w%4)) of fragment (c/16, w/4)
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
-            *reinterpret_cast<bf16x8_t *>(&gKIt[(l * CPL + cc) * kC + 8 * w]) = kit[cc];
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int c = l * CPL + cc;
+            const int f = (c >> 4) * 2 + (w >> 2), ln = (c & 15) + 16 * (w & 3);
+            *reinterpret_cast<bf16x8_t *>(rec + RL::KIT + f * RL::FRAG + ln * 16) = kit[cc];
+        }
     }
     lds_barrier();
 
+    // ---- KA and QA to the record, fragment by fragment (1 KiB per wave-wide store)
+#pragma unroll
+    for (int it = 0; it < (2 * 4 * NKS * 64) / kThreads; ++it) {
+        const int pc = tid + kThreads * it;
+        const int mat = pc / (4 * NKS * 64);
+        const int f = (pc >> 6) % (4 * NKS), ln = pc & 63;
+        const int rb = f / NKS, ks = f % NKS;
+        const int r = 16 * rb + (ln & 15), c = 32 * ks + 8 * (ln >> 4);
+        const bf16x8_t x = lds_ld8(mat ? &sm.g.QA[r][c] : &sm.g.KA[r][c]);
+        *reinterpret_cast<bf16x8_t *>(rec + (mat ? RL::QA : RL::KA) + f * RL::FRAG + ln * 16) = x;
+    }
+
     // ---- Gram blocks: A (fp32, LDS) and P (hi/lo, record)
     {
+        // A tiles as A[r][i] (rows of KA, columns of KI); P tiles transposed,
+        // P^T[i][r] (rows of KI, columns of QA), so that the accumulator is the
+        // 16x16x16 operand layout the record stores
         auto gram = [&](int tile, f32x4_t &acc, bool &isP, int &R, int &I) {
             isP = tile >= 10;
             lower_block(isP ? tile - 10 : tile, R, I);
-            const bf16_t *ah = isP ? &sm.g.QA[16 * R + lr][8 * lg] : &sm.g.KA[16 * R + lr][8 * lg];
-            const bf16_t *bh = &sm.KI[16 * I + lr][8 * lg];
+            const bf16_t *xh = isP ? &sm.g.QA[16 * R + lr][8 * lg] : &sm.g.KA[16 * R + lr][8 * lg];
+            const bf16_t *kh = &sm.KI[16 * I + lr][8 * lg];
             acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) acc = mfma16(lds_ld8(ah + 32 * ks), lds_ld8(bh + 32 * ks), acc);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8_t xa = lds_ld8(xh + 32 * ks), kb = lds_ld8(kh + 32 * ks);
+                acc = isP ? mfma16(kb, xa, acc) : mfma16(xa, kb, acc);
+            }
         };
         auto finish = [&](bool isP, int R, int I, const f32x4_t &acc) {
-            const int i = 16 * I + lr;
+            if (!isP) {
+                const int i = 16 * I + lr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * R + 4 * lg + e;
-                if (!isP) {
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * R + 4 * lg + e;
                     sm.A[r][i] = (i < r) ? sm.beta[r] * acc[e] : 0.f;
-                } else {
-                    bf16_t hh, ll;
-                    split_bf16((i <= r) ? acc[e] : 0.f, hh, ll);
-                    gP[r * kC + i] = hh;
-                    gP[kC * kC + r * kC + i] = ll;
                 }
+            } else {
+                // lane holds P^T[16I + 4lg + e][16R + lr] = P[r][i], kept for i <= r
+                const int r = 16 * R + lr;
+                f32x4_t x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (16 * I + 4 * lg + e <= r) ? acc[e] : 0.f;
+                uint8_t *dst = rec + RL::PT + (size_t)p_tile(R, I) * 2 * RL::TILE + l * 8;
+                store_split4(reinterpret_cast<bf16_t *>(dst), reinterpret_cast<bf16_t *>(dst + RL::TILE), x);
             }
         };
         f32x4_t a0, a1;
@@ -318,12 +355,6 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
         if (w < 4) {
             gram(w + 16, a0, p0, R0, I0);
             finish(p0, R0, I0, a0);
-        } else {
-            // zeros for the upper blocks (0,1) and (2,3) of P, read by 32-wide k-steps
-            const int blk = w - 4;                       // 0..3: (block, plane)
-            const int r0 = (blk & 1) ? 32 : 0, c0 = r0 + 16, pl = blk >> 1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gP[pl * kC * kC + (r0 + 4 * lg + e) * kC + c0 + lr] = (bf16_t)0.f;
         }
     }
     lds_barrier();
@@ -451,17 +482,21 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     }
     lds_barrier();
 
-    // ---- T (both planes, zeros above the block diagonal) to the record
+    // ---- the six stored fragments of T, both planes, zeros above the block diagonal
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        const int idx = tid + kThreads * it;         // 0..1023: (plane, row, 16-byte column group)
-        const int pl = idx >> 9, r = (idx >> 3) & 63, cg = idx & 7;
-        bf16x8_t v = lds_ld8(&sm.t.T[pl][r][8 * cg]);
-        if ((cg >> 1) > (r >> 4)) {
+        const int pc = tid + kThreads * it;          // 0..767: (fragment, plane, lane)
+        if (pc < 6 * 2 * 64) {
+            const int fp = pc >> 6, f = fp >> 1, pl = fp & 1, ln = pc & 63;
+            const int R = f < 2 ? f : 2 + ((f - 2) >> 1), ks = f < 2 ? 0 : ((f - 2) & 1);
+            const int r = 16 * R + (ln & 15), c = 32 * ks + 8 * (ln >> 4);
+            bf16x8_t v = lds_ld8(&sm.t.T[pl][r][c]);
+            if ((c >> 4) > R) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (bf16_t)0.f;
+                for (int e = 0; e < 8; ++e) v[e] = (bf16_t)0.f;
+            }
+            *reinterpret_cast<bf16x8_t *>(rec + RL::T + (size_t)fp * RL::FRAG + ln * 16) = v;
         }
-        *reinterpret_cast<bf16x8_t *>(&gT[pl * kC * kC + r * kC + 8 * cg]) = v;
     }
 }
 
@@ -507,22 +542,22 @@ template <int DK, int BV> struct StateRole {
         }
         flag = load_flag(rec, Rec<DK>::FLAG, tid);
     }
-    __device__ __forceinline__ void load_t(const uint8_t *rec, int w, int lr, int lg) {
-        const bf16_t *t = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::T) + (16 * w + lr) * kC + 8 * lg;
+    __device__ __forceinline__ void load_t(const uint8_t *rec, int w, int ln) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            th[ks] = *reinterpret_cast<const bf16x8_t *>(t + 32 * ks);
-            tl[ks] = *reinterpret_cast<const bf16x8_t *>(t + kC * kC + 32 * ks);
+            const uint8_t *t = rec + Rec<DK>::T + (size_t)t_frag(w, ks) * 2 * Rec<DK>::FRAG + ln * 16;
+            th[ks] = *reinterpret_cast<const bf16x8_t *>(t);
+            tl[ks] = *reinterpret_cast<const bf16x8_t *>(t + Rec<DK>::FRAG);
         }
     }
-    __device__ __forceinline__ void load_kit(const uint8_t *rec, int w, int lr, int lg) {
+    __device__ __forceinline__ void load_kit(const uint8_t *rec, int w, int ln, int lg) {
         const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
 #pragma unroll
         for (int i = 0; i < STW; ++i) {
             const int mt = (w * STW + i) / NT;
-            const bf16_t *kt = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KIT) + (16 * mt + lr) * kC + 8 * lg;
+            const uint8_t *kt = rec + Rec<DK>::KIT + (size_t)(2 * mt) * Rec<DK>::FRAG + ln * 16;
             kit[i][0] = *reinterpret_cast<const bf16x8_t *>(kt);
-            kit[i][1] = *reinterpret_cast<const bf16x8_t *>(kt + 32);
+            kit[i][1] = *reinterpret_cast<const bf16x8_t *>(kt + Rec<DK>::FRAG);
             cg[i] = *reinterpret_cast<const f32x4_t *>(col + DK + 16 * mt + 4 * lg);
             cgm[i] = *reinterpret_cast<const f32x4_t *>(col + 2 * DK + 16 * mt + 4 * lg);
         }
@@ -531,20 +566,20 @@ template <int DK, int BV> struct StateRole {
 
 template <int DK, int BV, typename IO> struct OutRole {
     static constexpr int NKS = DK / 32, NT = BV / 16;
-    bf16x8_t ka[NKS], qa[NKS];  // rows 16rb.. of KA, QA
-    bf16x8_t ph[2], pl[2];      // rows 16rb.. of P (hi, lo)
+    bf16x8_t ka[NKS], qa[NKS];  // fragments (rb, ks) of KA, QA
+    bf16x4_t ph[4], pl[4];      // tiles (rb, I) of P^T, I <= rb (hi, lo)
     IO vv[NT][4];               // values of the rows this lane produces, as loaded
     f32x4_t bt;                 // beta of those rows
     int flag;
 
     __device__ __forceinline__ void load_kqvb(const uint8_t *rec, const IO *__restrict__ v, int64_t tbase, int nv,
                                               int H, int h, int DV, int col0, int rb, int lr, int lg, int tid) {
-        const bf16_t *a = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::KA) + (16 * rb + lr) * DK + 8 * lg;
-        const bf16_t *b = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::QA) + (16 * rb + lr) * DK + 8 * lg;
+        const uint8_t *a = rec + Rec<DK>::KA + (size_t)(rb * NKS) * Rec<DK>::FRAG + (tid & 63) * 16;
+        const uint8_t *b = rec + Rec<DK>::QA + (size_t)(rb * NKS) * Rec<DK>::FRAG + (tid & 63) * 16;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            ka[ks] = *reinterpret_cast<const bf16x8_t *>(a + 32 * ks);
-            qa[ks] = *reinterpret_cast<const bf16x8_t *>(b + 32 * ks);
+            ka[ks] = *reinterpret_cast<const bf16x8_t *>(a + ks * Rec<DK>::FRAG);
+            qa[ks] = *reinterpret_cast<const bf16x8_t *>(b + ks * Rec<DK>::FRAG);
         }
         bt = *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(rec + Rec<DK>::BETA) + 16 * rb + 4 * lg);
 #pragma unroll
@@ -557,12 +592,12 @@ template <int DK, int BV, typename IO> struct OutRole {
             }
         flag = load_flag(rec, Rec<DK>::FLAG, tid);
     }
-    __device__ __forceinline__ void load_p(const uint8_t *rec, int rb, int lr, int lg) {
-        const bf16_t *p = reinterpret_cast<const bf16_t *>(rec + Rec<DK>::P) + (16 * rb + lr) * kC + 8 * lg;
+    __device__ __forceinline__ void load_p(const uint8_t *rec, int rb, int ln) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            ph[ks] = *reinterpret_cast<const bf16x8_t *>(p + 32 * ks);
-            pl[ks] = *reinterpret_cast<const bf16x8_t *>(p + kC * kC + 32 * ks);
+        for (int I = 0; I < 4; ++I) {
+            const uint8_t *p = rec + Rec<DK>::PT + (size_t)p_tile(rb, I) * 2 * Rec<DK>::TILE + ln * 8;
+            ph[I] = *reinterpret_cast<const bf16x4_t *>(p);
+            pl[I] = *reinterpret_cast<const bf16x4_t *>(p + Rec<DK>::TILE);
         }
     }
 };
@@ -599,8 +634,8 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const Cha
     if (cr.bos < cr.eos) {
         const uint8_t *rec = recs + (size_t)(cr.c0 * H + h) * RL::BYTES;
         R.load_cm(rec, w, lg0, tid);
-        R.load_t(rec, w, lr0, lg0);
-        R.load_kit(rec, w, lr0, lg0);
+        R.load_t(rec, w, tid & 63);
+        R.load_kit(rec, w, tid & 63, lg0);
     }
     // Each operand group has a single load site per chunk, right after its last
     // use; the token path of a flagged chunk runs right after the first barrier
@@ -656,7 +691,7 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const Cha
                 store_split4(&sm.U[0][jl][16 * w + 4 * lg], &sm.U[1][jl][16 * w + 4 * lg], acc);
             }
         }
-        R.load_t(recn, w, lr, lg);
+        R.load_t(recn, w, tl_ & 63);
         lds_barrier();  // B3: U visible
         if (!slow) {
             // S <- Diag(e^{g_n}) S + Diag(e^{g_n - m}) KI^T U
@@ -675,7 +710,7 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const Cha
                 for (int e = 0; e < 4; ++e) Sacc[i][e] = R.cg[i][e] * Sacc[i][e] + R.cgm[i][e] * acc[e];
             }
         }
-        R.load_kit(recn, w, lr, lg);
+        R.load_kit(recn, w, tl_ & 63, lg);
     }
     if (h_T) {
 #pragma unroll
@@ -694,6 +729,7 @@ template <int DK, int BV, typename IO>
 __device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const ChainRange &cr,
                                                  const IO *__restrict__ v, const uint8_t *__restrict__ recs,
                                                  IO *__restrict__ o, int H, int DV, int rb, int tid) {
+    static_assert(sizeof(IO) == 2, "the two-kernel path stores bf16 outputs");
     constexpr int NKS = DK / 32, NT = BV / 16;
     typedef Rec<DK> RL;
     const int h = cr.h, col0 = cr.col0;
@@ -703,7 +739,7 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const Ch
         const int nv0 = (int)((cr.eos - cr.bos) < kC ? (cr.eos - cr.bos) : kC);
         const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
         R.load_kqvb(rec, v, cr.bos, nv0, H, h, DV, col0, rb, lr0, lg0, tid);
-        R.load_p(rec, rb, lr0, lg0);
+        R.load_p(rec, rb, tid & 63);
     }
     f32x4_t accZ[NT];
     int64_t ci = cr.c0;
@@ -739,7 +775,7 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const Ch
                 for (int ks = 0; ks < NKS; ++ks) {
                     const bf16x8_t sb = lds_ld8(sh + 32 * ks);
                     accY = mfma16(R.ka[ks], sb, accY);
-                    accZ[nt] = mfma16(R.qa[ks], sb, accZ[nt]);
+                    accZ[nt] = mfma16(sb, R.qa[ks], accZ[nt]);   // Z^T[j][r]
                 }
                 f32x4_t x;
 #pragma unroll
@@ -755,31 +791,26 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const Ch
         lds_barrier();  // B2: X visible
         lds_barrier();  // B3: U visible
         if (!slow) {
-            // O = Z + P U
-            const int nks = (rb >> 1) + 1;
+            // O^T = Z^T + U^T P^T: lane holds O[16rb + lr][16nt + 4lg + e]
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const bf16_t *uh = &sm.U[0][nt * 16 + lr][8 * lg];
-                const bf16_t *ul = &sm.U[1][nt * 16 + lr][8 * lg];
+                const bf16_t *uh = &sm.U[0][nt * 16 + lr][4 * lg];
+                const bf16_t *ul = &sm.U[1][nt * 16 + lr][4 * lg];
                 f32x4_t acc = accZ[nt];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks < nks) {
-                        const bf16x8_t bh = lds_ld8(uh + 32 * ks), bl = lds_ld8(ul + 32 * ks);
-                        acc = mfma16(R.ph[ks], bh, acc);
-                        acc = mfma16(R.ph[ks], bl, acc);
-                        acc = mfma16(R.pl[ks], bh, acc);
-                    }
+                for (int I = 0; I < 4; ++I) {
+                    if (I <= rb) acc = mma4(acc, lds_ld4(uh + 16 * I), lds_ld4(ul + 16 * I), R.ph[I], R.pl[I]);
                 }
-                const int jl = nt * 16 + lr;
+                const int r = 16 * rb + lr;
+                if (r < nv) {
+                    bf16x4_t ov;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rb + 4 * lg + e;
-                    if (r < nv) o[((tbase + r) * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(acc[e]);
+                    for (int e = 0; e < 4; ++e) ov[e] = from_f32<bf16_t>(acc[e]);
+                    *reinterpret_cast<bf16x4_t *>(&o[((tbase + r) * H + h) * (int64_t)DV + col0 + nt * 16 + 4 * lg]) = ov;
                 }
             }
         }
-        R.load_p(recn, rb, lr, lg);
+        R.load_p(recn, rb, tl_ & 63);
     }
 }
 

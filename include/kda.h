@@ -62,8 +62,8 @@ const char *kda_last_hip_error(void);
  * Arguments as for kda_chunk_fwd; num_seqs is the number of sequences (B when
  * no cu_seqlens is given).  With bf16 I/O the forward runs in two passes and
  * the workspace holds, per (chunk, head), the chunk's decayed operands, its
- * UT-transform matrix and intra-chunk score block (about 82 KiB at d_k = 128,
- * i.e. about 1.3 KiB per token-head); fp32 I/O needs none.  The size depends
+ * UT-transform matrix and intra-chunk score block (about 72 KiB at d_k = 128,
+ * i.e. about 1.1 KiB per token-head); fp32 I/O needs none.  The size depends
  * only on the arguments, never on tensor contents.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
