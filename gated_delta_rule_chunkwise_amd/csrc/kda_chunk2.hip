@@ -1,39 +1,44 @@
 // kda_chunk2.hip -- chunkwise KDA forward for bf16 I/O in two kernels.
 //
 // The chunkwise form (KimiLinear article, section 3.1) splits each chunk's work
-// into a part that does not depend on the state -- the in-chunk log-decay
-// cumsum, the decayed key/query operands, the decay-weighted Gram blocks A and
-// P and the UT transform T = (I + A)^{-1} -- and a part that carries the state
-// from chunk to chunk.  Only the second part is sequential.  Here:
+// into a part that does not depend on the state and a part that carries the
+// state from chunk to chunk; only the second part is sequential.  With the
+// in-chunk log-decay cumsum G (per token and key channel), its chunk total g_n
+// and the per-channel anchor m = g_n / 2, the decayed operands
+//     KA = K.e^{G-m},  QA = Q.e^{G-m},  KI = K.e^{m-G}
+// give the intra-chunk blocks A = strictly-lower(diag(beta) KA KI^T),
+// P = lower(QA KI^T) and the UT transform T = (I + A)^{-1} (WY form of the
+// delta rule, section 3.1 and the DPLR discussion of the same article).  The
+// state-independent factors of the chunk update are folded here into
+//     Tb = T diag(beta),   W = Tb KA,   U0 = Tb V,
+// so that, with S' = Diag(e^m) S, one chunk of the recurrence is
+//     U = U0 - W S'                       (rows written into the state)
+//     O = QA S' + P U
+//     S <- Diag(e^{g_n}) S + Diag(e^{g_n - m}) KI^T U.
+// This is the same U = T diag(beta) (V - K.e^G S) as the WY/UT form; only the
+// rounding points differ.
 //
 //   chunk_prep_kernel   one workgroup per (chunk, head), all chunks in parallel:
-//                       computes the state-independent part once and writes a
-//                       compact record per chunk-head to the workspace;
+//                       computes the state-independent operands once and writes
+//                       a compact record per chunk-head to the workspace;
 //   chunk_state_kernel  one workgroup per (sequence, head, block of BV value
 //                       columns): walks the chunks of its sequence, keeping the
-//                       fp32 state block in registers, and reads the records.
-//
-// Per chunk with start state S, with the operands of the record
-// (m = g_n / 2 per channel, see kda_chunk.hip for the derivation):
-//   Y = KA (e^m . S),  Z = QA (e^m . S)            KA = K.e^{G-m}, QA = Q.e^{G-m}
-//   X = diag(beta) (V - Y),  U = T X
-//   O = Z + P U
-//   S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) (KI^T U)    KI = K.e^{m-G}
+//                       fp32 state block in registers, and streams the records.
 // Chunks whose in-chunk decay exceeds the matrix-core range are flagged by the
 // prep kernel and run token by token in the state kernel.
 //
 // Record layout: matrix operands are stored in the order the state kernel's
-// lanes hold them, so that every wave-wide load reads one contiguous 1 KiB (or
+// lanes hold them, so that each wave-wide load reads one contiguous 1 KiB (or
 // 512 B) run.  A "fragment" is one 16x32 bf16 operand of the 16x16x32 matrix
 // instruction, lane l holding row l%16, columns 8*(l/16)..+7 (16 bytes at l*16).
-//   KA, QA   fragments (row block rb, k-step ks), rb*NKS + ks, NKS = DK/32
-//   KIt      fragments (key block mt, token k-step ks) of KI^T, mt*2 + ks
-//   T        the six fragments (R, ks <= R/2) of T that a 32-wide k-step reads,
-//            each as hi then lo; blocks above the diagonal inside them are zero
-//   PT       the ten lower tiles (R, I <= R) of P, transposed and in the 16x16x16
-//            operand layout (lane l: P[16R + l%16][16I + 4*(l/16)..+3], 8 bytes),
-//            each as hi then lo
-//   e^m, e^{g_n}, e^{g_n-m} fp32[3][DK], beta fp32[64], flags int32[4];
+//   WN    fragments (row block rb, k-step ks) of -W, rb*NKS + ks, NKS = DK/32
+//   QA    fragments (rb, ks) of QA
+//   KIt   fragments (key block mt, token k-step ks) of KI^T, mt*2 + ks
+//   PT    the ten lower tiles (R, I <= R) of P in the 16x16x16 operand layout
+//         (lane l: P[16R + l%16][16I + 4*(l/16)..+3], 8 bytes), hi then lo
+//   U0    accumulator tiles (rb, value block nt) of U0, fp32: lane l holds
+//         U0[16rb + 4*(l/16) + e][16nt + l%16], e = 0..3 (16 bytes)
+//   e^m, e^{g_n}, e^{g_n-m} fp32[3][DK]; flags int32[4]
 // padded to a multiple of 256 bytes.
 #include "kda_chunk_common.h"
 #include "kda_launch.h"
@@ -44,28 +49,24 @@
 namespace kda {
 namespace {
 
-template <int DK> struct Rec {
+template <int DK, int DV> struct Rec {
     static constexpr int NKS = DK / 32;
     static constexpr size_t FRAG = 1024;                          // 64 lanes x 16 bytes
     static constexpr size_t TILE = 512;                           // 64 lanes x 8 bytes
-    static constexpr size_t KA = 0;
-    static constexpr size_t QA = KA + 4 * NKS * FRAG;
+    static constexpr size_t WN = 0;
+    static constexpr size_t QA = WN + 4 * NKS * FRAG;
     static constexpr size_t KIT = QA + 4 * NKS * FRAG;
-    static constexpr size_t T = KIT + (DK / 16) * 2 * FRAG;
-    static constexpr size_t PT = T + 6 * 2 * FRAG;
-    static constexpr size_t COL = PT + 10 * 2 * TILE;
-    static constexpr size_t BETA = COL + 3 * (size_t)DK * 4;
-    static constexpr size_t FLAG = BETA + (size_t)kC * 4;
+    static constexpr size_t PT = KIT + (DK / 16) * 2 * FRAG;
+    static constexpr size_t U0 = PT + 10 * 2 * TILE;
+    static constexpr size_t COL = U0 + 4 * (DV / 16) * FRAG;
+    static constexpr size_t FLAG = COL + 3 * (size_t)DK * 4;
     static constexpr size_t BYTES = ((FLAG + 16) + 255) / 256 * 256;
 };
 
-// Index of the stored T fragment (row block R, k-step ks); k-steps right of the
-// diagonal block are never read and map to ks = 0 (a harmless duplicate load).
-__device__ __forceinline__ int t_frag(int R, int ks) {
-    ks = ks <= (R >> 1) ? ks : 0;
-    return R < 2 ? R : 2 + 2 * (R - 2) + ks;
-}
-// Slot of the lower tile (R, I), I <= R; I > R maps to I = R.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Slot of the lower tile (R, I), I <= R; I > R maps to I = R (a harmless
+// duplicate load: those tiles are never used).
 __device__ __forceinline__ int p_tile(int R, int I) { return (R * (R + 1)) / 2 + (I <= R ? I : R); }
 
 constexpr size_t kHeaderBytes = 256;
@@ -132,18 +133,16 @@ __device__ __forceinline__ bool locate_chunk(int64_t chunk, const int32_t *__res
     return true;
 }
 
-template <int DK>
+template <int DK, int DV>
 struct alignas(16) PrepSmem {
     static constexpr int KS = DK + 8;
     static constexpr int TS = kC + 8;
     static constexpr int FS = 68;
+    bf16_t KA[kC][KS];                         // KA; after the UT transform, -W
     union {
+        bf16_t QA[kC][KS];                     // Gram phase
         struct {
-            bf16_t KA[kC][KS];
-            bf16_t QA[kC][KS];
-        } g;                                   // Gram phase
-        struct {
-            bf16_t T[2][kC][TS];               // hi/lo of (I + A)^{-1}
+            bf16_t T[2][kC][TS];               // hi/lo of (I + A)^{-1}, then of T diag(beta)
             float T8[4][2][8][8];
             float W8[4][8][8];
         } t;                                   // inversion phase
@@ -151,23 +150,28 @@ struct alignas(16) PrepSmem {
     union {
         bf16_t KI[kC][KS];                     // K . e^{m-G}
         bf16_t Tt[2][kC][kC + 4];              // transposed diagonal blocks of T
+        bf16_t KAt[DK][TS];                    // KA^T
     };
-    float A[kC][FS];
+    union {
+        float A[kC][FS];
+        bf16_t Vt[DV][TS];                     // V^T
+    };
     float tot[DK][kWaves];
     float beta[kC];
 };
 
 // ---------------------------------------------------------------------------------
 // Prep: one workgroup (8 waves) per (chunk, head).
-template <int DK, typename IO, typename GT>
-__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
-    const IO *__restrict__ q, const IO *__restrict__ k, const GT *__restrict__ log_alpha,
-    const GT *__restrict__ beta, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
-    uint8_t *__restrict__ recs, int64_t N, int64_t T, int32_t H) {
+template <int DK, int DV, typename IO, typename GT>
+__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, uint8_t *__restrict__ recs, int64_t N, int64_t T, int32_t H) {
     constexpr int CPL = DK / 64;
+    constexpr int CPV = DV / 64;
     constexpr int NKS = DK / 32;
-    typedef PrepSmem<DK> Sm;
-    typedef Rec<DK> RL;
+    typedef PrepSmem<DK, DV> Sm;
+    typedef Rec<DK, DV> RL;
     __shared__ Sm sm;
 
     const int tid = threadIdx.x;
@@ -180,12 +184,20 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
     uint8_t *rec = recs + (size_t)blockIdx.x * RL::BYTES;
     float *gCol = reinterpret_cast<float *>(rec + RL::COL);
-    float *gBeta = reinterpret_cast<float *>(rec + RL::BETA);
     int32_t *gFlag = reinterpret_cast<int32_t *>(rec + RL::FLAG);
 
-    // ---- load this chunk (rows past the end read the last row and are zeroed)
+    // ---- load this chunk (rows past the end read the last row; their gates,
+    // keys and beta are zeroed below, so they contribute nothing)
     ChunkRegs<DK, 16, IO, GT> in;
     in.load(q, k, q, log_alpha, beta, t0, nv, H, h, 0, 0, w, l, lg, lr, false);
+    typedef typename VecT<IO, CPV>::type VV;
+    VV vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 8 * w + i;
+        const int rr = r < nv ? r : nv - 1;
+        vr[i] = *reinterpret_cast<const VV *>(v + ((t0 + rr) * H + h) * (int64_t)DV + l * CPV);
+    }
     const bool partial = nv < kC;
     float csum[8][CPL];
 #pragma unroll
@@ -198,11 +210,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
         }
         sm.tot[l * CPL + cc][w] = csum[7][cc];
     }
-    if (w == 0) {
-        const float b = (l < nv) ? in.bt : 0.f;
-        sm.beta[l] = b;
-        gBeta[l] = b;
-    }
+    if (w == 0) sm.beta[l] = (l < nv) ? in.bt : 0.f;
     lds_barrier();
     float m2[CPL];
     bool big = false;
@@ -232,7 +240,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     if (tid == 0) gFlag[0] = slow ? 1 : 0;
     if (slow) return;                        // the state kernel runs this chunk token by token
 
-    // ---- decayed operands: LDS for the Gram products, record for the state kernel
+    // ---- decayed operands: LDS for the Gram products, KI^T to the record
+    bf16_t kak[8][CPL];                      // this lane's KA values, for KA^T later
     {
         float e1[8][CPL], e2[8][CPL];
 #pragma unroll
@@ -272,18 +281,19 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
                 qa[cc] = (bf16_t)(qv * e1[i][cc]);
                 ki[cc] = (bf16_t)(kv * e2[i][cc]);
                 kit[cc][i] = ki[cc];
+                kak[i][cc] = ka[cc];
             }
             if constexpr (CPL == 2) {
                 bf16x2_t p;
                 p[0] = ka[0]; p[1] = ka[1];
-                *reinterpret_cast<bf16x2_t *>(&sm.g.KA[r][2 * l]) = p;
+                *reinterpret_cast<bf16x2_t *>(&sm.KA[r][2 * l]) = p;
                 p[0] = qa[0]; p[1] = qa[1];
-                *reinterpret_cast<bf16x2_t *>(&sm.g.QA[r][2 * l]) = p;
+                *reinterpret_cast<bf16x2_t *>(&sm.QA[r][2 * l]) = p;
                 p[0] = ki[0]; p[1] = ki[1];
                 *reinterpret_cast<bf16x2_t *>(&sm.KI[r][2 * l]) = p;
             } else {
-                sm.g.KA[r][l] = ka[0];
-                sm.g.QA[r][l] = qa[0];
+                sm.KA[r][l] = ka[0];
+                sm.QA[r][l] = qa[0];
                 sm.KI[r][l] = ki[0];
             }
         }
@@ -298,16 +308,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     }
     lds_barrier();
 
-    // ---- KA and QA to the record, fragment by fragment (1 KiB per wave-wide store)
+    // ---- QA to the record, fragment by fragment (1 KiB per wave-wide store)
 #pragma unroll
-    for (int it = 0; it < (2 * 4 * NKS * 64) / kThreads; ++it) {
+    for (int it = 0; it < (4 * NKS * 64) / kThreads; ++it) {
         const int pc = tid + kThreads * it;
-        const int mat = pc / (4 * NKS * 64);
-        const int f = (pc >> 6) % (4 * NKS), ln = pc & 63;
+        const int f = pc >> 6, ln = pc & 63;
         const int rb = f / NKS, ks = f % NKS;
-        const int r = 16 * rb + (ln & 15), c = 32 * ks + 8 * (ln >> 4);
-        const bf16x8_t x = lds_ld8(mat ? &sm.g.QA[r][c] : &sm.g.KA[r][c]);
-        *reinterpret_cast<bf16x8_t *>(rec + (mat ? RL::QA : RL::KA) + f * RL::FRAG + ln * 16) = x;
+        const bf16x8_t x = lds_ld8(&sm.QA[16 * rb + (ln & 15)][32 * ks + 8 * (ln >> 4)]);
+        *reinterpret_cast<bf16x8_t *>(rec + RL::QA + f * RL::FRAG + ln * 16) = x;
     }
 
     // ---- Gram blocks: A (fp32, LDS) and P (hi/lo, record)
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
         auto gram = [&](int tile, f32x4_t &acc, bool &isP, int &R, int &I) {
             isP = tile >= 10;
             lower_block(isP ? tile - 10 : tile, R, I);
-            const bf16_t *xh = isP ? &sm.g.QA[16 * R + lr][8 * lg] : &sm.g.KA[16 * R + lr][8 * lg];
+            const bf16_t *xh = isP ? &sm.QA[16 * R + lr][8 * lg] : &sm.KA[16 * R + lr][8 * lg];
             const bf16_t *kh = &sm.KI[16 * I + lr][8 * lg];
             acc = zero4();
 #pragma unroll
@@ -482,122 +490,219 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     }
     lds_barrier();
 
-    // ---- the six stored fragments of T, both planes, zeros above the block diagonal
+    // ---- Tb = T diag(beta) in place (hi/lo); KA^T and V^T to LDS
+    {
+        const int r = tid >> 3, i0 = 8 * (tid & 7);
+        const bf16x8_t hv = lds_ld8(&sm.t.T[0][r][i0]), lv = lds_ld8(&sm.t.T[1][r][i0]);
+        bf16x8_t h2, l2;
+        // blocks above the diagonal were never written (stale LDS): zero
+        const bool upper = (i0 >> 4) > (r >> 4);
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int pc = tid + kThreads * it;          // 0..767: (fragment, plane, lane)
-        if (pc < 6 * 2 * 64) {
-            const int fp = pc >> 6, f = fp >> 1, pl = fp & 1, ln = pc & 63;
-            const int R = f < 2 ? f : 2 + ((f - 2) >> 1), ks = f < 2 ? 0 : ((f - 2) & 1);
-            const int r = 16 * R + (ln & 15), c = 32 * ks + 8 * (ln >> 4);
-            bf16x8_t v = lds_ld8(&sm.t.T[pl][r][c]);
-            if ((c >> 4) > R) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = (bf16_t)0.f;
-            }
-            *reinterpret_cast<bf16x8_t *>(rec + RL::T + (size_t)fp * RL::FRAG + ln * 16) = v;
+        for (int e = 0; e < 8; ++e) {
+            const float x = upper ? 0.f : ((float)hv[e] + (float)lv[e]) * sm.beta[i0 + e];
+            bf16_t hh, ll;
+            split_bf16(x, hh, ll);
+            h2[e] = hh;
+            l2[e] = ll;
         }
+        *reinterpret_cast<bf16x8_t *>(&sm.t.T[0][r][i0]) = h2;
+        *reinterpret_cast<bf16x8_t *>(&sm.t.T[1][r][i0]) = l2;
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        bf16x8_t x;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = kak[i][cc];
+        *reinterpret_cast<bf16x8_t *>(&sm.KAt[l * CPL + cc][8 * w]) = x;
+    }
+#pragma unroll
+    for (int cv = 0; cv < CPV; ++cv) {
+        bf16x8_t x;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (bf16_t)vget(vr[i], cv);
+        *reinterpret_cast<bf16x8_t *>(&sm.Vt[l * CPV + cv][8 * w]) = x;
+    }
+    lds_barrier();
+
+    // ---- W = Tb KA (stored negated, bf16, to LDS) and U0 = Tb V (fp32, record)
+    {
+        constexpr int NW = 4 * (DK / 16), NU = 4 * (DV / 16);
+        for (int t = w; t < NW + NU; t += kWaves) {
+            const bool isW = t < NW;
+            const int tt = isW ? t : t - NW;
+            const int rb = tt & 3, ct = tt >> 2;
+            const bf16_t *bsrc = isW ? &sm.KAt[16 * ct + lr][8 * lg] : &sm.Vt[16 * ct + lr][8 * lg];
+            f32x4_t acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks <= (rb >> 1)) {   // Tb is lower triangular
+                    const bf16x8_t b = lds_ld8(bsrc + 32 * ks);
+                    acc = mfma16(lds_ld8(&sm.t.T[0][16 * rb + lr][32 * ks + 8 * lg]), b, acc);
+                    acc = mfma16(lds_ld8(&sm.t.T[1][16 * rb + lr][32 * ks + 8 * lg]), b, acc);
+                }
+            }
+            if (isW) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.KA[16 * rb + 4 * lg + e][16 * ct + lr] = (bf16_t)(-acc[e]);
+            } else {
+                *reinterpret_cast<f32x4_t *>(rec + RL::U0 + (size_t)(rb * (DV / 16) + ct) * RL::FRAG + l * 16) = acc;
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- -W to the record, fragment by fragment
+#pragma unroll
+    for (int it = 0; it < (4 * NKS * 64) / kThreads; ++it) {
+        const int pc = tid + kThreads * it;
+        const int f = pc >> 6, ln = pc & 63;
+        const int rb = f / NKS, ks = f % NKS;
+        const bf16x8_t x = lds_ld8(&sm.KA[16 * rb + (ln & 15)][32 * ks + 8 * (ln >> 4)]);
+        *reinterpret_cast<bf16x8_t *>(rec + RL::WN + f * RL::FRAG + ln * 16) = x;
     }
 }
 
 // ---------------------------------------------------------------------------------
-// State: one workgroup (8 waves) per (sequence, head, BV value columns).  The
-// waves split into two roles with the same barrier sequence per chunk:
-//   state role  (waves 0-3): own the fp32 state tiles; write e^m.S to LDS, form
-//                            U = T X, update the state with KI^T U;
-//   output role (waves 4-7): row block w-4 of the chunk: Y, Z, X and O = Z + P U.
-// Each role runs its own loop, so each keeps only its own record operands in
-// registers and its loads retire in a fixed order: every operand is reloaded for
-// the next chunk right after its last use, about one chunk ahead of its next use.
-template <int DK, int BV>
+// State: one workgroup of 16 waves per (sequence, head, BV value columns).  The
+// waves split into three roles with the same barrier sequence per chunk:
+//   state role  (waves 0-3):  own the fp32 state tiles; write e^m.S to LDS and
+//                             update the state with KI^T U;
+//   output role (waves 4-7):  row block w-4 of the chunk: U = U0 - W S' (to LDS),
+//                             Z = QA S' and O = Z + P U;
+//   loader role (waves 8-15): stream this workgroup's part of each chunk record
+//                             from global memory into a two-slot LDS ring, two
+//                             records ahead.
+// The loaders absorb the stalls of the global-load pipe, spreading the fetch of
+// each record over the three phases of a chunk so that the pipe stays busy.
+// Slot j%2 receives record j during chunk j-1 (it held record j-2, whose last
+// reads were in chunk j-2): the part read first (e^m, -W, QA, U0) right after
+// B0, complete at B2, and the rest (P, KI^T) right after B2, complete at B0 of
+// chunk j.  The other roles read the first part right after B2 of chunk j-1 and
+// the rest right after B0 of chunk j, each read issued ahead of compute that
+// hides its latency.
+constexpr int kStateWaves = 16;
+constexpr int kStateThreads = 64 * kStateWaves;
+constexpr int kLoaderLanes = 512;
+
+// This workgroup's part of a record, in LDS, ordered by when it is first read:
+// -W and QA, the U0 tiles of its value columns and the column scales and flags
+// (read after B2 of the chunk before), then KI^T and P (read after B0).
+template <int DK, int DV, int BV> struct Slot {
+    typedef Rec<DK, DV> RL;
+    static constexpr int NT = BV / 16;
+    static constexpr int P_WQ = (int)(RL::KIT / 16);                   // -W, QA: as in the record
+    static constexpr int P_U = P_WQ + 4 * NT * 64;                       // + U0 tiles of this block
+    static constexpr int P_C = P_U + (int)((3 * DK * 4 + 16) / 16);      // + scales, flags
+    static constexpr int NP = P_C + (int)((RL::U0 - RL::KIT) / 16);      // + KI^T, P
+    static constexpr size_t U0 = (size_t)P_WQ * 16;
+    static constexpr size_t COL = (size_t)P_U * 16;
+    static constexpr size_t FLAG = COL + 3 * (size_t)DK * 4;
+    static constexpr size_t KIT = (size_t)P_C * 16;
+    static constexpr size_t PT = KIT + (RL::PT - RL::KIT);
+    static constexpr size_t BYTES = (size_t)NP * 16;
+    static constexpr int ITERS = (NP + kLoaderLanes - 1) / kLoaderLanes;
+    // loader schedule per chunk, in units of ITERS: the first W_EARLY are written
+    // after B0, the rest after B2; fetches of the record two chunks ahead are
+    // spread over the three phases, each after the write of the same registers
+    static constexpr int W_EARLY = (P_C + kLoaderLanes - 1) / kLoaderLanes;
+    static constexpr int F1 = ITERS / 4;
+    static constexpr int F2 = (ITERS / 2 < W_EARLY) ? ITERS / 2 : W_EARLY;
+    // 16-byte piece p: its offset in the global record and in the slot
+    __device__ __forceinline__ static void piece(int p, int nt0, size_t &g, size_t &s) {
+        if (p < P_WQ) {
+            g = s = (size_t)p * 16;
+        } else if (p < P_U) {
+            const int q = p - P_WQ, rb = q / (NT * 64), rem = q % (NT * 64);
+            g = RL::U0 + (size_t)(rb * (DV / 16) + nt0) * RL::FRAG + (size_t)rem * 16;
+            s = U0 + (size_t)q * 16;
+        } else if (p < P_C) {
+            const int q = p - P_U;
+            g = RL::COL + (size_t)q * 16;
+            s = COL + (size_t)q * 16;
+        } else {
+            const int q = p - P_C;
+            g = RL::KIT + (size_t)q * 16;
+            s = KIT + (size_t)q * 16;
+        }
+    }
+};
+
+template <int DK, int DV, int BV>
 struct alignas(16) StateSmem {
     static constexpr int KS = DK + 8;
     static constexpr int TS = kC + 8;
+    uint8_t ring[2][Slot<DK, DV, BV>::BYTES];
     bf16_t S[BV][KS];          // (Diag(e^m) S)^T, single bf16
-    bf16_t X[2][BV][TS];       // hi/lo of X^T
     bf16_t U[2][BV][TS];       // hi/lo of U^T
     float red[4][2 * BV + 1];  // token path
 };
 
-// The flag is read through a lane-dependent address (always element 0) so that
-// it arrives by a vector load, counted in order with the other record loads,
-// and not by a scalar load that every LDS barrier would wait for.
-__device__ __forceinline__ int load_flag(const uint8_t *rec, size_t off, int tl) {
-    return reinterpret_cast<const int32_t *>(rec + off)[tl >> 10];
+// Barrier for a wave whose outstanding LDS operations (ring writes) need not be
+// complete yet; a later lds_barrier() orders them.
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int slot_flag(const uint8_t *slot, size_t off) {
+    return *reinterpret_cast<const int32_t *>(slot + off);
 }
 
-template <int DK, int BV> struct StateRole {
+template <int DK, int DV, int BV> struct StateRole {
+    typedef Slot<DK, DV, BV> SL;
     static constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
-    bf16x8_t th[2], tl[2];    // rows 16w.. of T (hi, lo)
-    bf16x8_t kit[STW][2];     // KI^T rows of the wave's state tiles
+    bf16x8_t kit[STW][2];     // KI^T fragments of the wave's state tiles
     f32x4_t cm[STW], cg[STW], cgm[STW];
     int flag;
 
-    __device__ __forceinline__ void load_cm(const uint8_t *rec, int w, int lg, int tid) {
-        const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
+    __device__ __forceinline__ void load_cm(const uint8_t *slot, int w, int lg) {
+        const float *col = reinterpret_cast<const float *>(slot + SL::COL);
 #pragma unroll
         for (int i = 0; i < STW; ++i) {
             const int mt = (w * STW + i) / NT;
             cm[i] = *reinterpret_cast<const f32x4_t *>(col + 16 * mt + 4 * lg);
         }
-        flag = load_flag(rec, Rec<DK>::FLAG, tid);
+        flag = slot_flag(slot, SL::FLAG);
     }
-    __device__ __forceinline__ void load_t(const uint8_t *rec, int w, int ln) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint8_t *t = rec + Rec<DK>::T + (size_t)t_frag(w, ks) * 2 * Rec<DK>::FRAG + ln * 16;
-            th[ks] = *reinterpret_cast<const bf16x8_t *>(t);
-            tl[ks] = *reinterpret_cast<const bf16x8_t *>(t + Rec<DK>::FRAG);
-        }
-    }
-    __device__ __forceinline__ void load_kit(const uint8_t *rec, int w, int ln, int lg) {
-        const float *col = reinterpret_cast<const float *>(rec + Rec<DK>::COL);
+    __device__ __forceinline__ void load_kit(const uint8_t *slot, int w, int ln, int lg) {
+        const float *col = reinterpret_cast<const float *>(slot + SL::COL);
 #pragma unroll
         for (int i = 0; i < STW; ++i) {
             const int mt = (w * STW + i) / NT;
-            const uint8_t *kt = rec + Rec<DK>::KIT + (size_t)(2 * mt) * Rec<DK>::FRAG + ln * 16;
+            const uint8_t *kt = slot + SL::KIT + (size_t)(2 * mt) * SL::RL::FRAG + ln * 16;
             kit[i][0] = *reinterpret_cast<const bf16x8_t *>(kt);
-            kit[i][1] = *reinterpret_cast<const bf16x8_t *>(kt + Rec<DK>::FRAG);
+            kit[i][1] = *reinterpret_cast<const bf16x8_t *>(kt + SL::RL::FRAG);
             cg[i] = *reinterpret_cast<const f32x4_t *>(col + DK + 16 * mt + 4 * lg);
             cgm[i] = *reinterpret_cast<const f32x4_t *>(col + 2 * DK + 16 * mt + 4 * lg);
         }
     }
 };
 
-template <int DK, int BV, typename IO> struct OutRole {
+template <int DK, int DV, int BV> struct OutRole {
+    typedef Slot<DK, DV, BV> SL;
+    typedef Rec<DK, DV> RL;
     static constexpr int NKS = DK / 32, NT = BV / 16;
-    bf16x8_t ka[NKS], qa[NKS];  // fragments (rb, ks) of KA, QA
+    bf16x8_t wn[NKS], qa[NKS];  // fragments (rb, ks) of -W and QA
     bf16x4_t ph[4], pl[4];      // tiles (rb, I) of P^T, I <= rb (hi, lo)
-    IO vv[NT][4];               // values of the rows this lane produces, as loaded
-    f32x4_t bt;                 // beta of those rows
+    f32x4_t u0[NT];             // accumulator tiles (rb, nt) of U0
     int flag;
 
-    __device__ __forceinline__ void load_kqvb(const uint8_t *rec, const IO *__restrict__ v, int64_t tbase, int nv,
-                                              int H, int h, int DV, int col0, int rb, int lr, int lg, int tid) {
-        const uint8_t *a = rec + Rec<DK>::KA + (size_t)(rb * NKS) * Rec<DK>::FRAG + (tid & 63) * 16;
-        const uint8_t *b = rec + Rec<DK>::QA + (size_t)(rb * NKS) * Rec<DK>::FRAG + (tid & 63) * 16;
+    __device__ __forceinline__ void load_wq(const uint8_t *slot, int rb, int ln) {
+        const uint8_t *a = slot + RL::WN + (size_t)(rb * NKS) * RL::FRAG + ln * 16;
+        const uint8_t *b = slot + RL::QA + (size_t)(rb * NKS) * RL::FRAG + ln * 16;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            ka[ks] = *reinterpret_cast<const bf16x8_t *>(a + ks * Rec<DK>::FRAG);
-            qa[ks] = *reinterpret_cast<const bf16x8_t *>(b + ks * Rec<DK>::FRAG);
+            wn[ks] = *reinterpret_cast<const bf16x8_t *>(a + ks * RL::FRAG);
+            qa[ks] = *reinterpret_cast<const bf16x8_t *>(b + ks * RL::FRAG);
         }
-        bt = *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(rec + Rec<DK>::BETA) + 16 * rb + 4 * lg);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rb + 4 * lg + e;
-                const int rr = r < nv ? r : nv - 1;
-                vv[nt][e] = v[((tbase + rr) * H + h) * (int64_t)DV + col0 + nt * 16 + lr];
-            }
-        flag = load_flag(rec, Rec<DK>::FLAG, tid);
+            u0[nt] = *reinterpret_cast<const f32x4_t *>(slot + SL::U0 + (size_t)(rb * NT + nt) * RL::FRAG + ln * 16);
+        flag = slot_flag(slot, SL::FLAG);
     }
-    __device__ __forceinline__ void load_p(const uint8_t *rec, int rb, int ln) {
+    __device__ __forceinline__ void load_p(const uint8_t *slot, int rb, int ln) {
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const uint8_t *p = rec + Rec<DK>::PT + (size_t)p_tile(rb, I) * 2 * Rec<DK>::TILE + ln * 8;
+            const uint8_t *p = slot + SL::PT + (size_t)p_tile(rb, I) * 2 * RL::TILE + ln * 8;
             ph[I] = *reinterpret_cast<const bf16x4_t *>(p);
-            pl[I] = *reinterpret_cast<const bf16x4_t *>(p + Rec<DK>::TILE);
+            pl[I] = *reinterpret_cast<const bf16x4_t *>(p + RL::TILE);
         }
     }
 };
@@ -609,15 +714,15 @@ struct ChainRange {
     int h, col0;
 };
 
-template <int DK, int BV, typename IO, typename GT>
-__device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const ChainRange &cr,
+__device__ __forceinline__ int chunk_count(const ChainRange &cr) { return (int)((cr.eos - cr.bos + kC - 1) / kC); }
+
+template <int DK, int DV, int BV, typename IO, typename GT>
+__device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const ChainRange &cr,
                                                 const IO *__restrict__ q, const IO *__restrict__ k,
                                                 const IO *__restrict__ v, const GT *__restrict__ log_alpha,
                                                 const GT *__restrict__ beta, const float *__restrict__ h0,
-                                                const uint8_t *__restrict__ recs, IO *__restrict__ o,
-                                                float *__restrict__ h_T, int H, int DV, int w, int tid) {
+                                                IO *__restrict__ o, float *__restrict__ h_T, int H, int w, int tid) {
     constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
-    typedef Rec<DK> RL;
     const int h = cr.h, col0 = cr.col0;
     const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
     f32x4_t Sacc[STW];
@@ -630,28 +735,19 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const Cha
             Sacc[i][e] = h0 ? h0[((cr.n * H + h) * DK + c) * (int64_t)DV + col0 + nt * 16 + lr0] : 0.f;
         }
     }
-    StateRole<DK, BV> R;
-    if (cr.bos < cr.eos) {
-        const uint8_t *rec = recs + (size_t)(cr.c0 * H + h) * RL::BYTES;
-        R.load_cm(rec, w, lg0, tid);
-        R.load_t(rec, w, tid & 63);
-        R.load_kit(rec, w, tid & 63, lg0);
-    }
-    // Each operand group has a single load site per chunk, right after its last
-    // use; the token path of a flagged chunk runs right after the first barrier
-    // and the matrix-core steps are skipped, so both paths share the loads.
-    int64_t ci = cr.c0;
-    for (int64_t tbase = cr.bos; tbase < cr.eos; tbase += kC, ++ci) {
+    const int nch = chunk_count(cr);
+    lds_barrier();  // ring slot 0 holds record 0
+    StateRole<DK, DV, BV> R;
+    if (nch > 0) R.load_cm(sm.ring[0], w, lg0);
+    for (int j = 0; j < nch; ++j) {
         int tl_;
         asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
         const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
+        const int64_t tbase = cr.bos + (int64_t)j * kC;
         const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-        // next chunk's record (the current one again on the last chunk, so that
-        // every load is issued on every path and the wait counts stay exact)
-        const int64_t cn = tbase + kC < cr.eos ? ci + 1 : ci;
-        const uint8_t *recn = recs + (size_t)(cn * H + h) * RL::BYTES;
         lds_barrier();  // B0
         const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
+        R.load_kit(sm.ring[j & 1], w, tl_ & 63, lg);
         if (slow) {
             for (int r = 0; r < nv; ++r)
                 token_update<DK, BV, IO, GT>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h, DV, col0,
@@ -667,32 +763,9 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const Cha
                 *reinterpret_cast<bf16x4_t *>(&sm.S[nt * 16 + lr][16 * mt + 4 * lg]) = sv;
             }
         }
-        R.load_cm(recn, w, lg, tl_);
         lds_barrier();  // B1: S' visible
-        lds_barrier();  // B2: X visible
-        if (!slow) {
-            // U = T X for row block w (T is lower triangular: blocks right of w are zero)
-            const int nks = (w >> 1) + 1;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bf16_t *xh = &sm.X[0][nt * 16 + lr][8 * lg];
-                const bf16_t *xl = &sm.X[1][nt * 16 + lr][8 * lg];
-                f32x4_t acc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks < nks) {
-                        const bf16x8_t bh = lds_ld8(xh + 32 * ks), bl = lds_ld8(xl + 32 * ks);
-                        acc = mfma16(R.th[ks], bh, acc);
-                        acc = mfma16(R.th[ks], bl, acc);
-                        acc = mfma16(R.tl[ks], bh, acc);
-                    }
-                }
-                const int jl = nt * 16 + lr;
-                store_split4(&sm.U[0][jl][16 * w + 4 * lg], &sm.U[1][jl][16 * w + 4 * lg], acc);
-            }
-        }
-        R.load_t(recn, w, tl_ & 63);
-        lds_barrier();  // B3: U visible
+        lds_barrier();  // B2: U visible; slot (j+1)%2 holds record j+1
+        R.load_cm(sm.ring[(j + 1) & 1], w, lg);
         if (!slow) {
             // S <- Diag(e^{g_n}) S + Diag(e^{g_n - m}) KI^T U
 #pragma unroll
@@ -710,7 +783,6 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const Cha
                 for (int e = 0; e < 4; ++e) Sacc[i][e] = R.cg[i][e] * Sacc[i][e] + R.cgm[i][e] * acc[e];
             }
         }
-        R.load_kit(recn, w, tl_ & 63, lg);
     }
     if (h_T) {
 #pragma unroll
@@ -725,37 +797,26 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, BV> &sm, const Cha
     }
 }
 
-template <int DK, int BV, typename IO>
-__device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const ChainRange &cr,
-                                                 const IO *__restrict__ v, const uint8_t *__restrict__ recs,
-                                                 IO *__restrict__ o, int H, int DV, int rb, int tid) {
+template <int DK, int DV, int BV, typename IO>
+__device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, const ChainRange &cr,
+                                                 IO *__restrict__ o, int H, int rb, int tid) {
     static_assert(sizeof(IO) == 2, "the two-kernel path stores bf16 outputs");
     constexpr int NKS = DK / 32, NT = BV / 16;
-    typedef Rec<DK> RL;
     const int h = cr.h, col0 = cr.col0;
-    OutRole<DK, BV, IO> R;
-    if (cr.bos < cr.eos) {
-        const uint8_t *rec = recs + (size_t)(cr.c0 * H + h) * RL::BYTES;
-        const int nv0 = (int)((cr.eos - cr.bos) < kC ? (cr.eos - cr.bos) : kC);
-        const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
-        R.load_kqvb(rec, v, cr.bos, nv0, H, h, DV, col0, rb, lr0, lg0, tid);
-        R.load_p(rec, rb, tid & 63);
-    }
+    const int nch = chunk_count(cr);
+    lds_barrier();  // ring slot 0 holds record 0
+    OutRole<DK, DV, BV> R;
+    if (nch > 0) R.load_wq(sm.ring[0], rb, tid & 63);
     f32x4_t accZ[NT];
-    int64_t ci = cr.c0;
-    for (int64_t tbase = cr.bos; tbase < cr.eos; tbase += kC, ++ci) {
+    for (int j = 0; j < nch; ++j) {
         int tl_;
         asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
         const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
+        const int64_t tbase = cr.bos + (int64_t)j * kC;
         const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-        // next chunk (the current one again on the last chunk: loads on every path)
-        const bool has_next = tbase + kC < cr.eos;
-        const int64_t cn = has_next ? ci + 1 : ci;
-        const int64_t tn = has_next ? tbase + kC : tbase;
-        const int nvn = (int)((cr.eos - tn) < kC ? (cr.eos - tn) : kC);
-        const uint8_t *recn = recs + (size_t)(cn * H + h) * RL::BYTES;
         lds_barrier();  // B0
         const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
+        R.load_p(sm.ring[j & 1], rb, tl_ & 63);
         if (slow) {
             // the state role runs the chunk token by token: two barriers per token
             for (int r = 0; r < nv; ++r) {
@@ -765,31 +826,24 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const Ch
         }
         lds_barrier();  // B1: S' visible
         if (!slow) {
-            // Y = KA S', Z = QA S', X = diag(beta) (V - Y) for rows 16rb..16rb+15
+            // U = U0 - W S' (rows 16rb..16rb+15, to LDS) and Z^T = S'^T QA^T
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const bf16_t *sh = &sm.S[nt * 16 + lr][8 * lg];
-                f32x4_t accY = zero4();
+                f32x4_t accU = R.u0[nt];
                 accZ[nt] = zero4();
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const bf16x8_t sb = lds_ld8(sh + 32 * ks);
-                    accY = mfma16(R.ka[ks], sb, accY);
+                    accU = mfma16(R.wn[ks], sb, accU);
                     accZ[nt] = mfma16(sb, R.qa[ks], accZ[nt]);   // Z^T[j][r]
                 }
-                f32x4_t x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rb + 4 * lg + e;
-                    x[e] = (r < nv) ? R.bt[e] * (to_f32(R.vv[nt][e]) - accY[e]) : 0.f;
-                }
                 const int jl = nt * 16 + lr;
-                store_split4(&sm.X[0][jl][16 * rb + 4 * lg], &sm.X[1][jl][16 * rb + 4 * lg], x);
+                store_split4(&sm.U[0][jl][16 * rb + 4 * lg], &sm.U[1][jl][16 * rb + 4 * lg], accU);
             }
         }
-        R.load_kqvb(recn, v, tn, nvn, H, h, DV, col0, rb, lr, lg, tl_);
-        lds_barrier();  // B2: X visible
-        lds_barrier();  // B3: U visible
+        lds_barrier();  // B2: U visible; slot (j+1)%2 holds record j+1
+        R.load_wq(sm.ring[(j + 1) & 1], rb, tl_ & 63);
         if (!slow) {
             // O^T = Z^T + U^T P^T: lane holds O[16rb + lr][16nt + 4lg + e]
 #pragma unroll
@@ -810,18 +864,110 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, BV> &sm, const Ch
                 }
             }
         }
-        R.load_p(recn, rb, tl_ & 63);
     }
 }
 
-template <int DK, int BV, typename IO, typename GT>
-__global__ __launch_bounds__(kThreads) void chunk_state_kernel(
+// Loader: register buffers A and B alternate between two records in flight.
+// Entering chunk j, the buffer for j+1 holds (or is receiving) record j+1 and
+// the other record j+2; during chunk j the first is written to slot (j+1)%2 and
+// refilled with record j+3.  Records past the last chunk re-read the last one.
+template <int DK, int DV, int BV, int I0, int I1, int N>
+__device__ __forceinline__ void loader_fetch(u32x4_t (&buf)[N], const uint8_t *rec, int nt0, int lid) {
+    typedef Slot<DK, DV, BV> SL;
+    static_assert(N == SL::ITERS, "loader buffer size");
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+        const int p = lid + kLoaderLanes * i;
+        if (i + 1 < SL::ITERS || p < SL::NP) {
+            size_t g, s;
+            SL::piece(p, nt0, g, s);
+            buf[i] = *reinterpret_cast<const u32x4_t *>(rec + g);
+        }
+    }
+}
+
+template <int DK, int DV, int BV, int I0, int I1, int N>
+__device__ __forceinline__ void loader_store(const u32x4_t (&buf)[N], uint8_t *slot, int nt0, int lid) {
+    typedef Slot<DK, DV, BV> SL;
+    static_assert(N == SL::ITERS, "loader buffer size");
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+        const int p = lid + kLoaderLanes * i;
+        if (i + 1 < SL::ITERS || p < SL::NP) {
+            size_t g, s;
+            SL::piece(p, nt0, g, s);
+            *reinterpret_cast<u32x4_t *>(slot + s) = buf[i];
+        }
+    }
+}
+
+// One chunk of the loader: the barrier sequence of the other roles, with the
+// ring write of record j+1 and the fetch of record j+3 spread over it.
+template <int DK, int DV, int BV, int N>
+__device__ __forceinline__ void loader_chunk(StateSmem<DK, DV, BV> &sm, u32x4_t (&buf)[N], const uint8_t *rec3,
+                                             int jj, int nv, int nt0, int lid) {
+    typedef Slot<DK, DV, BV> SL;
+    lds_barrier();  // B0
+    const bool slow = __builtin_amdgcn_readfirstlane(slot_flag(sm.ring[jj & 1], SL::FLAG)) != 0;
+    uint8_t *dst = sm.ring[(jj + 1) & 1];
+    loader_store<DK, DV, BV, 0, SL::W_EARLY>(buf, dst, nt0, lid);
+    loader_fetch<DK, DV, BV, 0, SL::F1>(buf, rec3, nt0, lid);
+    // the early writes need to be complete only at B2, the late ones at B0
+    if (slow) {
+        for (int r = 0; r < nv; ++r) {
+            plain_barrier();
+            plain_barrier();
+        }
+    }
+    plain_barrier();  // B1
+    loader_fetch<DK, DV, BV, SL::F1, SL::F2>(buf, rec3, nt0, lid);
+    lds_barrier();    // B2
+    loader_store<DK, DV, BV, SL::W_EARLY, SL::ITERS>(buf, dst, nt0, lid);
+    loader_fetch<DK, DV, BV, SL::F2, SL::ITERS>(buf, rec3, nt0, lid);
+}
+
+template <int DK, int DV, int BV>
+__device__ __forceinline__ void loader_role_loop(StateSmem<DK, DV, BV> &sm, const ChainRange &cr,
+                                                 const uint8_t *__restrict__ recs, int H, int lid) {
+    typedef Rec<DK, DV> RL;
+    typedef Slot<DK, DV, BV> SL;
+    const int nch = chunk_count(cr);
+    const int nt0 = cr.col0 / 16;
+    auto rec_of = [&](int j) -> const uint8_t * {
+        const int jj = j < nch ? j : nch - 1;
+        return recs + (size_t)((cr.c0 + jj) * H + cr.h) * RL::BYTES;
+    };
+    u32x4_t a[SL::ITERS], b[SL::ITERS];
+    if (nch > 0) {
+        loader_fetch<DK, DV, BV, 0, SL::ITERS>(a, rec_of(0), nt0, lid);
+        loader_store<DK, DV, BV, 0, SL::ITERS>(a, sm.ring[0], nt0, lid);
+        loader_fetch<DK, DV, BV, 0, SL::ITERS>(a, rec_of(1), nt0, lid);
+        loader_fetch<DK, DV, BV, 0, SL::ITERS>(b, rec_of(2), nt0, lid);
+    }
+    lds_barrier();  // ring slot 0 holds record 0
+    // two chunks per iteration so that the buffers keep fixed registers
+    for (int j = 0; j < nch; j += 2) {
+        {
+            const int64_t tbase = cr.bos + (int64_t)j * kC;
+            const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
+            loader_chunk<DK, DV, BV>(sm, a, rec_of(j + 3), j, nv, nt0, lid);
+        }
+        if (j + 1 < nch) {
+            const int64_t tbase = cr.bos + (int64_t)(j + 1) * kC;
+            const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
+            loader_chunk<DK, DV, BV>(sm, b, rec_of(j + 4), j + 1, nv, nt0, lid);
+        }
+    }
+}
+
+template <int DK, int DV, int BV, typename IO, typename GT>
+__global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ chunk_off,
     const uint8_t *__restrict__ recs, IO *__restrict__ o, float *__restrict__ h_T, int64_t seq_len,
-    int32_t H, int32_t DV, int64_t num_chains) {
-    __shared__ StateSmem<DK, BV> sm;
+    int32_t H, int64_t num_chains) {
+    __shared__ StateSmem<DK, DV, BV> sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t wg = blockIdx.x;
@@ -840,12 +986,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(
         cr.c0 = cr.n * ((seq_len + kC - 1) / kC);
     }
     if (w < 4)
-        state_role_loop<DK, BV, IO, GT>(sm, cr, q, k, v, log_alpha, beta, h0, recs, o, h_T, H, DV, w, tid);
+        state_role_loop<DK, DV, BV, IO, GT>(sm, cr, q, k, v, log_alpha, beta, h0, o, h_T, H, w, tid);
+    else if (w < 8)
+        output_role_loop<DK, DV, BV, IO>(sm, cr, o, H, w - 4, tid);
     else
-        output_role_loop<DK, BV, IO>(sm, cr, v, recs, o, H, DV, w - 4, tid);
+        loader_role_loop<DK, DV, BV>(sm, cr, recs, H, tid - 512);
 }
 
-template <int DK, typename IO, typename GT>
+template <int DK, int DV, typename IO, typename GT>
 hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
     uint8_t *ws = reinterpret_cast<uint8_t *>(a.workspace);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + kHeaderBytes);
@@ -854,37 +1002,52 @@ hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
     const int64_t nprep = max_chunks(a) * a.H;
     if (nprep > 0)
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, IO, GT>), dim3((unsigned)nprep), dim3(kThreads), 0, st,
-                           (const IO *)a.q, (const IO *)a.k, (const GT *)a.log_alpha, (const GT *)a.beta,
-                           a.cu_seqlens, (const int32_t *)chunk_off, recs, a.num_seqs, a.seq_len, a.H);
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, DV, IO, GT>), dim3((unsigned)nprep), dim3(kThreads), 0, st,
+                           (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
+                           (const GT *)a.beta, a.cu_seqlens, (const int32_t *)chunk_off, recs, a.num_seqs, a.seq_len,
+                           a.H);
     const int64_t chains = a.num_seqs * (int64_t)a.H;
-    if (bv == 32)
-        hipLaunchKernelGGL((chunk_state_kernel<DK, 32, IO, GT>), dim3((unsigned)(chains * (a.d_v / 32))),
-                           dim3(kThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+    // 32 value columns per workgroup only at d_k = 64: at d_k = 128 the loader
+    // buffers and the 32-column state tiles do not fit the 16-wave register budget
+    if constexpr (DK == 64) {
+        if (bv == 32) {
+            hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 32, IO, GT>), dim3((unsigned)(chains * (DV / 32))),
+                               dim3(kStateThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+                               (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
+                               (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT>), dim3((unsigned)(chains * (DV / 16))),
+                           dim3(kStateThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
                            (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
-                           (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains);
-    else
-        hipLaunchKernelGGL((chunk_state_kernel<DK, 16, IO, GT>), dim3((unsigned)(chains * (a.d_v / 16))),
-                           dim3(kThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
-                           (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
-                           (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains);
+                           (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains);
     return hipGetLastError();
+}
+
+template <typename GT>
+hipError_t launch_two_kernel_dims(const ChunkArgs &a, int bv, hipStream_t st) {
+    if (a.d_k == 128)
+        return a.d_v == 128 ? launch_two_kernel<128, 128, bf16_t, GT>(a, bv, st)
+                            : launch_two_kernel<128, 64, bf16_t, GT>(a, bv, st);
+    return a.d_v == 128 ? launch_two_kernel<64, 128, bf16_t, GT>(a, bv, st)
+                        : launch_two_kernel<64, 64, bf16_t, GT>(a, bv, st);
+}
+
+size_t record_bytes(int d_k, int d_v) {
+    if (d_k == 128) return d_v == 128 ? Rec<128, 128>::BYTES : Rec<128, 64>::BYTES;
+    return d_v == 128 ? Rec<64, 128>::BYTES : Rec<64, 64>::BYTES;
 }
 
 }  // namespace
 
 size_t two_kernel_workspace_bytes(const ChunkArgs &a) {
     if (a.total_tokens <= 0) return 0;
-    const size_t rec = a.d_k == 128 ? Rec<128>::BYTES : Rec<64>::BYTES;
-    return kHeaderBytes + plan_bytes(a.num_seqs) + (size_t)max_chunks(a) * a.H * rec;
+    return kHeaderBytes + plan_bytes(a.num_seqs) + (size_t)max_chunks(a) * a.H * record_bytes(a.d_k, a.d_v);
 }
 
 hipError_t launch_chunk_fwd_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
-    if (a.d_k == 128)
-        return a.gate_bf16 ? launch_two_kernel<128, bf16_t, bf16_t>(a, bv, st)
-                           : launch_two_kernel<128, bf16_t, float>(a, bv, st);
-    return a.gate_bf16 ? launch_two_kernel<64, bf16_t, bf16_t>(a, bv, st)
-                       : launch_two_kernel<64, bf16_t, float>(a, bv, st);
+    return a.gate_bf16 ? launch_two_kernel_dims<bf16_t>(a, bv, st) : launch_two_kernel_dims<float>(a, bv, st);
 }
 
 }  // namespace kda
