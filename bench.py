@@ -49,17 +49,22 @@ def decode_alg_bytes(B, H, dk, dv, io_b=2, gate_b=2):
     return B * H * per_state
 
 
-def source_digest():
+CHUNK_SOURCES = ("kda_chunk.hip", "kda_chunk2.hip", "kda_chunk_common.h", "kda_device.h")
+DECODE_SOURCES = ("kda_decode.hip", "kda_device.h")
+
+
+def source_digest(files):
+    """Digest of the kernel sources a counter profile was taken with."""
     h = hashlib.sha256()
-    for f in ("kda_chunk.hip", "kda_device.h"):
+    for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_chunkwise_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(name, digest):
-    """Counter-measured HBM bytes per launch, from a committed rocprofv3 summary;
-    None when absent or when the kernel source changed since it was taken."""
+    """Counter-measured HBM bytes per call, from a committed rocprofv3 summary;
+    None when absent or when the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
@@ -68,7 +73,21 @@ def load_traffic(name, digest):
         return None
     if rec.get("source_digest") != digest:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_call")
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters to bytes: 1 GiB read + 1 GiB written per launch, three launches."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                                           "launches": 3}}), flush=True)
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -117,6 +136,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -125,6 +146,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import gated_delta_rule_chunkwise_amd as kda
     from gated_delta_rule_chunkwise_amd import inputs as I
@@ -147,11 +171,14 @@ def main():
     tok_heads = T * H
     alg_b = chunk_alg_bytes(tok_heads, H, dk, dv)
     alg_f = chunk_alg_flops(tok_heads, dk, dv)
-    digest = source_digest()
-    traffic = load_traffic("chunk_fwd_kernel_c3_traffic.json", digest)
+    digest = source_digest(CHUNK_SOURCES)
+    traffic = load_traffic("chunk_fwd_prefill_h32_t65536_traffic.json", digest)
+    # one kda_chunk_fwd call = chunk_prep_kernel + chunk_state_kernel on one stream
     roof = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "chunk_fwd_kernel<128,16,bf16,bf16>", "alg_bytes_per_launch": alg_b}
+            "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,128,bf16,bf16> + "
+                      "chunk_state_kernel<128,128,16,bf16,bf16>",
+            "alg_bytes_per_launch": alg_b}
     mfma = {"alg_flops_per_launch": alg_f, "achieved_tflops": alg_f / (ms * 1e-3) / 1e12,
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
             "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
@@ -190,8 +217,8 @@ def main():
                          "ms_per_step": dms, "tokens_per_s": dcfg.B / (dms * 1e-3),
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                       "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                                      "traffic": load_traffic("decode_step_kernel_c4_traffic.json",
-                                                              digest),
+                                      "traffic": load_traffic("decode_step_b256_h32_traffic.json",
+                                                              source_digest(DECODE_SOURCES)),
                                       "alg_bytes_per_launch": db}}
         del xs, S
 
