@@ -524,21 +524,29 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
     }
     lds_barrier();
 
-    // ---- W = Tb KA (stored negated, bf16, to LDS) and U0 = Tb V (fp32, record)
+    // ---- W = Tb KA (stored negated, bf16, to LDS) and U0 = Tb V (fp32, record):
+    // waves 0-3 the W tiles, waves 4-7 the U0 tiles, of row block w % 4
     {
-        constexpr int NW = 4 * (DK / 16), NU = 4 * (DV / 16);
-        for (int t = w; t < NW + NU; t += kWaves) {
-            const bool isW = t < NW;
-            const int tt = isW ? t : t - NW;
-            const int rb = tt & 3, ct = tt >> 2;
+        const int rb = w & 3;
+        const bool isW = w < 4;
+        bf16x8_t th[2], tlo[2];   // this row block of Tb, hi and lo, read once
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks <= (rb >> 1)) {   // Tb is lower triangular
+                th[ks] = lds_ld8(&sm.t.T[0][16 * rb + lr][32 * ks + 8 * lg]);
+                tlo[ks] = lds_ld8(&sm.t.T[1][16 * rb + lr][32 * ks + 8 * lg]);
+            }
+        }
+        const int ncol = isW ? DK / 16 : DV / 16;
+        for (int ct = 0; ct < ncol; ++ct) {
             const bf16_t *bsrc = isW ? &sm.KAt[16 * ct + lr][8 * lg] : &sm.Vt[16 * ct + lr][8 * lg];
             f32x4_t acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if (ks <= (rb >> 1)) {   // Tb is lower triangular
+                if (ks <= (rb >> 1)) {
                     const bf16x8_t b = lds_ld8(bsrc + 32 * ks);
-                    acc = mfma16(lds_ld8(&sm.t.T[0][16 * rb + lr][32 * ks + 8 * lg]), b, acc);
-                    acc = mfma16(lds_ld8(&sm.t.T[1][16 * rb + lr][32 * ks + 8 * lg]), b, acc);
+                    acc = mfma16(th[ks], b, acc);
+                    acc = mfma16(tlo[ks], b, acc);
                 }
             }
             if (isW) {
