@@ -132,6 +132,23 @@ def test_strong_decay_takes_exact_path(kda):
     check_against_oracle(kda, d, "f32", what="strong decay")
 
 
+@pytest.mark.parametrize("gate_io", ["bf16", "f32"])
+def test_strong_decay_bf16_two_pass(kda, gate_io):
+    """bf16 I/O (prep + state kernels) with chunks whose decay exceeds the
+    matrix-core range mixed with ordinary ones, across packed sequences: the
+    flagged chunks run token by token in the state kernel."""
+    cfg = I.ChunkConfig("strong16", "bf16", gate_io, H=3, dk=128, dv=128, h0=True, seed=18)
+    lens = [300, 64, 130, 1, 200]
+    d = I.make_chunk_inputs(cfg, lengths=lens)
+    la = d["log_alpha"].clone()
+    la[10] = -30.0                 # a reset inside the first chunk of sequence 0
+    la[70:75] = -28.0              # second chunk of sequence 0
+    la[300:364, 1, :3] = -2.0      # the whole of sequence 1 for head 1 (sum -128 on 3 channels)
+    la[400:430, :, 7] = -4.0       # partial chunk of sequence 2
+    d["log_alpha"] = la.to(d["log_alpha"].dtype)
+    check_against_oracle(kda, d, "bf16", what="strong decay bf16 gates=%s" % gate_io)
+
+
 def test_beta_negative_eigenvalue_range(kda):
     cfg = I.ChunkConfig("beta2", "f32", "f32", H=2, dk=128, dv=128, T=257, seed=14)
     d = I.make_chunk_inputs(cfg)
