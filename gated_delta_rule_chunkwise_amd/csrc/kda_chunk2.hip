@@ -858,11 +858,17 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
             for (int nt = 0; nt < NT; ++nt) {
                 const bf16_t *uh = &sm.U[0][nt * 16 + lr][4 * lg];
                 const bf16_t *ul = &sm.U[1][nt * 16 + lr][4 * lg];
-                f32x4_t acc = accZ[nt];
+                // two accumulators (even and odd column blocks) halve the dependent chain
+                f32x4_t acc = accZ[nt], acc1 = zero4();
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
-                    if (I <= rb) acc = mma4(acc, lds_ld4(uh + 16 * I), lds_ld4(ul + 16 * I), R.ph[I], R.pl[I]);
+                    if (I <= rb) {
+                        if (I & 1) acc1 = mma4(acc1, lds_ld4(uh + 16 * I), lds_ld4(ul + 16 * I), R.ph[I], R.pl[I]);
+                        else acc = mma4(acc, lds_ld4(uh + 16 * I), lds_ld4(ul + 16 * I), R.ph[I], R.pl[I]);
+                    }
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += acc1[e];
                 const int r = 16 * rb + lr;
                 if (r < nv) {
                     bf16x4_t ov;
