@@ -580,21 +580,23 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
 //   loader role (waves 8-15): stream this workgroup's part of each chunk record
 //                             from global memory into a two-slot LDS ring, two
 //                             records ahead.
+// Two barriers per chunk: B1 (S' written) and B2 (U written); everything else
+// is ordered by them.  The state waves write S'(j+1) after B2(j), when the reads
+// of S'(j) are complete; U(j+1) is written after B1(j+1), after every read of
+// U(j).  So the output waves' O(j) overlaps the state waves' update of chunk j
+// and their S'(j+1).
 // The loaders absorb the stalls of the global-load pipe, spreading the fetch of
-// each record over the three phases of a chunk so that the pipe stays busy.
-// Slot j%2 receives record j during chunk j-1 (it held record j-2, whose last
-// reads were in chunk j-2): the part read first (e^m, -W, QA, U0) right after
-// B0, complete at B2, and the rest (P, KI^T) right after B2, complete at B0 of
-// chunk j.  The other roles read the first part right after B2 of chunk j-1 and
-// the rest right after B0 of chunk j, each read issued ahead of compute that
-// hides its latency.
+// each record over the phases of a chunk so that the pipe stays busy.  Record j
+// goes to ring slot j%2 right after B2 of chunk j-2 (i.e. at the start of chunk
+// j-1; the slot held record j-2, whose last reads were before B1 of chunk j-2)
+// and is complete at B2 of chunk j-1, after which the other roles read it into
+// registers, ahead of compute that hides the LDS latency.
 constexpr int kStateWaves = 16;
 constexpr int kStateThreads = 64 * kStateWaves;
 constexpr int kLoaderLanes = 512;
 
-// This workgroup's part of a record, in LDS, ordered by when it is first read:
-// -W and QA, the U0 tiles of its value columns and the column scales and flags
-// (read after B2 of the chunk before), then KI^T and P (read after B0).
+// This workgroup's part of a record, in LDS: -W and QA as in the record, the U0
+// tiles of its value columns, the column scales and flags, then KI^T and P.
 template <int DK, int DV, int BV> struct Slot {
     typedef Rec<DK, DV> RL;
     static constexpr int NT = BV / 16;
@@ -609,12 +611,9 @@ template <int DK, int DV, int BV> struct Slot {
     static constexpr size_t PT = KIT + (RL::PT - RL::KIT);
     static constexpr size_t BYTES = (size_t)NP * 16;
     static constexpr int ITERS = (NP + kLoaderLanes - 1) / kLoaderLanes;
-    // loader schedule per chunk, in units of ITERS: the first W_EARLY are written
-    // after B0, the rest after B2; fetches of the record two chunks ahead are
-    // spread over the three phases, each after the write of the same registers
-    static constexpr int W_EARLY = (P_C + kLoaderLanes - 1) / kLoaderLanes;
-    static constexpr int F1 = ITERS / 4;
-    static constexpr int F2 = (ITERS / 2 < W_EARLY) ? ITERS / 2 : W_EARLY;
+    // loader schedule per chunk, in units of ITERS: the ring write and the fetch
+    // of the record two chunks ahead are split at B1
+    static constexpr int F1 = (ITERS + 1) / 2;
     // 16-byte piece p: its offset in the global record and in the slot
     __device__ __forceinline__ static void piece(int p, int nt0, size_t &g, size_t &s) {
         if (p < P_WQ) {
@@ -746,16 +745,17 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
     const int nch = chunk_count(cr);
     lds_barrier();  // ring slot 0 holds record 0
     StateRole<DK, DV, BV> R;
-    if (nch > 0) R.load_cm(sm.ring[0], w, lg0);
+    if (nch > 0) {
+        R.load_cm(sm.ring[0], w, lg0);
+        R.load_kit(sm.ring[0], w, tid & 63, lg0);
+    }
     for (int j = 0; j < nch; ++j) {
         int tl_;
         asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
         const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
         const int64_t tbase = cr.bos + (int64_t)j * kC;
         const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-        lds_barrier();  // B0
         const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
-        R.load_kit(sm.ring[j & 1], w, tl_ & 63, lg);
         if (slow) {
             for (int r = 0; r < nv; ++r)
                 token_update<DK, BV, IO, GT>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h, DV, col0,
@@ -773,7 +773,6 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
         }
         lds_barrier();  // B1: S' visible
         lds_barrier();  // B2: U visible; slot (j+1)%2 holds record j+1
-        R.load_cm(sm.ring[(j + 1) & 1], w, lg);
         if (!slow) {
             // S <- Diag(e^{g_n}) S + Diag(e^{g_n - m}) KI^T U
 #pragma unroll
@@ -791,6 +790,8 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
                 for (int e = 0; e < 4; ++e) Sacc[i][e] = R.cg[i][e] * Sacc[i][e] + R.cgm[i][e] * acc[e];
             }
         }
+        R.load_cm(sm.ring[(j + 1) & 1], w, lg);
+        R.load_kit(sm.ring[(j + 1) & 1], w, tl_ & 63, lg);
     }
     if (h_T) {
 #pragma unroll
@@ -814,7 +815,10 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
     const int nch = chunk_count(cr);
     lds_barrier();  // ring slot 0 holds record 0
     OutRole<DK, DV, BV> R;
-    if (nch > 0) R.load_wq(sm.ring[0], rb, tid & 63);
+    if (nch > 0) {
+        R.load_wq(sm.ring[0], rb, tid & 63);
+        R.load_p(sm.ring[0], rb, tid & 63);
+    }
     f32x4_t accZ[NT];
     for (int j = 0; j < nch; ++j) {
         int tl_;
@@ -822,9 +826,7 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
         const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
         const int64_t tbase = cr.bos + (int64_t)j * kC;
         const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-        lds_barrier();  // B0
         const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
-        R.load_p(sm.ring[j & 1], rb, tl_ & 63);
         if (slow) {
             // the state role runs the chunk token by token: two barriers per token
             for (int r = 0; r < nv; ++r) {
@@ -878,6 +880,7 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
                 }
             }
         }
+        R.load_p(sm.ring[(j + 1) & 1], rb, tl_ & 63);
     }
 }
 
@@ -921,12 +924,13 @@ template <int DK, int DV, int BV, int N>
 __device__ __forceinline__ void loader_chunk(StateSmem<DK, DV, BV> &sm, u32x4_t (&buf)[N], const uint8_t *rec3,
                                              int jj, int nv, int nt0, int lid) {
     typedef Slot<DK, DV, BV> SL;
-    lds_barrier();  // B0
     const bool slow = __builtin_amdgcn_readfirstlane(slot_flag(sm.ring[jj & 1], SL::FLAG)) != 0;
     uint8_t *dst = sm.ring[(jj + 1) & 1];
-    loader_store<DK, DV, BV, 0, SL::W_EARLY>(buf, dst, nt0, lid);
+    // record jj+1 to its slot in two halves, at the start of the chunk and after
+    // B1 (complete at B2), each followed by the fetch of the same half of record
+    // jj+3 into the registers it frees
+    loader_store<DK, DV, BV, 0, SL::F1>(buf, dst, nt0, lid);
     loader_fetch<DK, DV, BV, 0, SL::F1>(buf, rec3, nt0, lid);
-    // the early writes need to be complete only at B2, the late ones at B0
     if (slow) {
         for (int r = 0; r < nv; ++r) {
             plain_barrier();
@@ -934,10 +938,9 @@ __device__ __forceinline__ void loader_chunk(StateSmem<DK, DV, BV> &sm, u32x4_t 
         }
     }
     plain_barrier();  // B1
-    loader_fetch<DK, DV, BV, SL::F1, SL::F2>(buf, rec3, nt0, lid);
-    lds_barrier();    // B2
-    loader_store<DK, DV, BV, SL::W_EARLY, SL::ITERS>(buf, dst, nt0, lid);
-    loader_fetch<DK, DV, BV, SL::F2, SL::ITERS>(buf, rec3, nt0, lid);
+    loader_store<DK, DV, BV, SL::F1, SL::ITERS>(buf, dst, nt0, lid);
+    loader_fetch<DK, DV, BV, SL::F1, SL::ITERS>(buf, rec3, nt0, lid);
+    lds_barrier();    // B2: the ring writes are complete
 }
 
 template <int DK, int DV, int BV>
