@@ -849,13 +849,21 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
                     accZ[nt] = mfma16(sb, R.qa[ks], accZ[nt]);   // Z^T[j][r]
                 }
                 const int jl = nt * 16 + lr;
-                store_split4(&sm.U[0][jl][16 * rb + 4 * lg], &sm.U[1][jl][16 * rb + 4 * lg], accU);
+                bf16x4_t uh, ul;
+                split4(accU, uh, ul);
+                *reinterpret_cast<bf16x4_t *>(&sm.U[0][jl][16 * rb + 4 * lg]) = uh;
+                *reinterpret_cast<bf16x4_t *>(&sm.U[1][jl][16 * rb + 4 * lg]) = ul;
+                // the diagonal block of P U needs only this wave's own U tile, whose
+                // accumulator layout is the 16x16x16 A-operand layout of U^T: add it now
+#pragma unroll
+                for (int I = 0; I < 4; ++I)   // I == rb, with a compile-time register index
+                    if (I == rb) accZ[nt] = mma4(accZ[nt], uh, ul, R.ph[I], R.pl[I]);
             }
         }
         lds_barrier();  // B2: U visible; slot (j+1)%2 holds record j+1
         R.load_wq(sm.ring[(j + 1) & 1], rb, tl_ & 63);
         if (!slow) {
-            // O^T = Z^T + U^T P^T: lane holds O[16rb + lr][16nt + 4lg + e]
+            // O^T = Z^T + U^T P^T (blocks left of the diagonal): lane holds O[16rb + lr][16nt + 4lg + e]
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const bf16_t *uh = &sm.U[0][nt * 16 + lr][4 * lg];
@@ -863,8 +871,8 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
                 // two accumulators (even and odd column blocks) halve the dependent chain
                 f32x4_t acc = accZ[nt], acc1 = zero4();
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    if (I <= rb) {
+                for (int I = 0; I < 3; ++I) {
+                    if (I < rb) {   // the diagonal block I = rb is already in Z
                         if (I & 1) acc1 = mma4(acc1, lds_ld4(uh + 16 * I), lds_ld4(ul + 16 * I), R.ph[I], R.pl[I]);
                         else acc = mma4(acc, lds_ld4(uh + 16 * I), lds_ld4(ul + 16 * I), R.ph[I], R.pl[I]);
                     }
