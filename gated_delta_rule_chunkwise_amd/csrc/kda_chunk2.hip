@@ -773,6 +773,7 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
         }
         lds_barrier();  // B1: S' visible
         lds_barrier();  // B2: U visible; slot (j+1)%2 holds record j+1
+        R.load_cm(sm.ring[(j + 1) & 1], w, lg);   // e^m of chunk j+1, read during the update
         if (!slow) {
             // S <- Diag(e^{g_n}) S + Diag(e^{g_n - m}) KI^T U
 #pragma unroll
@@ -790,7 +791,6 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
                 for (int e = 0; e < 4; ++e) Sacc[i][e] = R.cg[i][e] * Sacc[i][e] + R.cgm[i][e] * acc[e];
             }
         }
-        R.load_cm(sm.ring[(j + 1) & 1], w, lg);
         R.load_kit(sm.ring[(j + 1) & 1], w, tl_ & 63, lg);
     }
     if (h_T) {
