@@ -134,8 +134,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
