@@ -61,10 +61,12 @@ const char *kda_last_hip_error(void);
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none).
  * Arguments as for kda_chunk_fwd; num_seqs is the number of sequences (B when
  * no cu_seqlens is given).  With bf16 I/O the forward runs in two passes and
- * the workspace holds, per (chunk, head), the chunk's decayed operands, its
- * UT-transform matrix and intra-chunk score block (about 72 KiB at d_k = 128,
- * i.e. about 1.1 KiB per token-head); fp32 I/O needs none.  The size depends
- * only on the arguments, never on tensor contents.
+ * the workspace holds, per (chunk, head), the chunk's state-independent
+ * operands: W and U0 (the UT transform already applied to the decayed keys and
+ * to the values), the decayed queries and keys, the intra-chunk score block
+ * and the per-channel decay scales -- about 92 KiB at d_k = d_v = 128, i.e.
+ * about 1.4 KiB per token-head.  fp32 I/O needs none.  The size depends only
+ * on the arguments, never on tensor contents.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                     int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
