@@ -56,6 +56,9 @@ def _load():
         lib.kda_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, dp,
                                           ctypes.c_int]
         lib.kda_oracle_decode.restype = ctypes.c_int
+        lib.kda_oracle_prologue.argtypes = [dp, dp, dp, dp, i64, i64, ctypes.c_double,
+                                             ctypes.c_double, dp, dp, dp, dp]
+        lib.kda_oracle_prologue.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -166,3 +169,45 @@ def decode(q, k, v, log_alpha, beta, S, nthreads=None):
     if rc != 0:
         raise RuntimeError("kda_oracle_decode failed with code %d" % rc)
     return o, S_new
+
+
+# Default eps of the L2 normalisation (the GPU entry points use the same value).
+PROLOGUE_EPS = 1e-6
+
+
+def prologue(q_raw, k_raw, gate_pre, beta_pre, log_alpha_min, eps=PROLOGUE_EPS):
+    """Input prologue (see ``kda_oracle_prologue`` in kda_oracle.c): per row,
+    q / max(||q||, eps), k / max(||k||, eps), max(-softplus(gate_pre), log_alpha_min)
+    and sigmoid(beta_pre).  q_raw, k_raw, gate_pre: [..., dk]; beta_pre: [...].
+    Returns (q_hat, k_hat, log_alpha, beta) in fp64 with the input shapes."""
+    q = _f64(q_raw)
+    dk = q.shape[-1]
+    lead = q.shape[:-1]
+    k = _f64(k_raw, q.shape)
+    a = _f64(gate_pre, q.shape)
+    b = _f64(beta_pre, lead)
+    rows = int(np.prod(lead)) if lead else 1
+    qh = np.zeros_like(q)
+    kh = np.zeros_like(k)
+    la = np.zeros_like(a)
+    be = np.zeros_like(b)
+    rc = _load().kda_oracle_prologue(_ptr(q), _ptr(k), _ptr(a), _ptr(b), rows, dk,
+                                     float(log_alpha_min), float(eps), _ptr(qh), _ptr(kh),
+                                     _ptr(la), _ptr(be))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_prologue failed with code %d" % rc)
+    return qh, kh, la, be
+
+
+def fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h0=None,
+                 cu_seqlens=None, nthreads=None, eps=PROLOGUE_EPS):
+    """KDA forward on raw projections: ``prologue`` then ``fwd``."""
+    qh, kh, la, be = prologue(q_raw, k_raw, gate_pre, beta_pre, log_alpha_min, eps)
+    return fwd(qh, kh, v, la, be, h0=h0, cu_seqlens=cu_seqlens, nthreads=nthreads)
+
+
+def decode_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, nthreads=None,
+                    eps=PROLOGUE_EPS):
+    """One decode step on raw projections: ``prologue`` then ``decode``."""
+    qh, kh, la, be = prologue(q_raw, k_raw, gate_pre, beta_pre, log_alpha_min, eps)
+    return decode(qh, kh, v, la, be, S, nthreads=nthreads)

@@ -204,4 +204,50 @@ int kda_oracle_decode(const double *q, const double *k, const double *v,
     return rc;
 }
 
-int kda_oracle_version(void) { return 1; }
+/* Input prologue, for the entry points that take raw projections.
+ *
+ * KimiLinear article (intl.cloud.baidu.com), section 3.2 "Balancing Numerical
+ * Stability and Computational Efficiency": the chunkwise KDA keeps the state's
+ * scale under control by normalising its inputs and by constraining and
+ * reparameterising the gate values; the section gives no formulas.  The reading
+ * taken is the set of maps the workloads draw their inputs through, with the
+ * gate constraint as a caller-given floor:
+ *     q_hat = q / max(||q||_2, eps),   k_hat = k / max(||k||_2, eps)
+ *                                          (per token and head, over d_k)
+ *     log_alpha = max(-softplus(a), lo),   softplus(a) = log(1 + e^a)
+ *                                          (per token, head and key channel)
+ *     beta = sigmoid(b) = 1 / (1 + e^-b)   (per token and head)
+ * Layouts: q, k, a, q_hat, k_hat, log_alpha: [rows, dk]; b, beta: [rows], with
+ * rows = tokens x heads.  softplus and sigmoid are evaluated in the forms that
+ * cannot overflow: softplus(a) = max(a, 0) + log1p(e^-|a|), and sigmoid from
+ * e^-|b|. */
+int kda_oracle_prologue(const double *q, const double *k, const double *a, const double *b,
+                        int64_t rows, int64_t dk, double lo, double eps,
+                        double *q_hat, double *k_hat, double *log_alpha, double *beta)
+{
+    if (rows < 0 || dk <= 0 || !(eps > 0.0)) return -2;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *qr = q + r * dk, *kr = k + r * dk, *ar = a + r * dk;
+        double nq = 0.0, nk = 0.0;
+        for (int64_t c = 0; c < dk; ++c) {
+            nq += qr[c] * qr[c];
+            nk += kr[c] * kr[c];
+        }
+        nq = sqrt(nq);
+        nk = sqrt(nk);
+        const double dq = nq > eps ? nq : eps, dkn = nk > eps ? nk : eps;
+        for (int64_t c = 0; c < dk; ++c) {
+            q_hat[r * dk + c] = qr[c] / dq;
+            k_hat[r * dk + c] = kr[c] / dkn;
+            const double x = ar[c];
+            const double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+            const double la = -sp;
+            log_alpha[r * dk + c] = la > lo ? la : lo;
+        }
+        const double e = exp(-fabs(b[r]));
+        beta[r] = b[r] >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
+    }
+    return 0;
+}
+
+int kda_oracle_version(void) { return 2; }

@@ -363,3 +363,113 @@ def test_bad_arguments_raise(oracle_mod):
         oracle_mod.fwd(q, k, v, la, b, cu_seqlens=[0, 3])      # does not end at T
     with pytest.raises(ValueError):
         oracle_mod.fwd(q, k, v, la, b, cu_seqlens=[0, 3, 2, 4])  # decreasing
+
+
+# ---------------------------------------------------------------- input prologue
+# KimiLinear article, section 3.2: inputs normalised, gate values constrained and
+# reparameterised (reading: L2 norm, max(-softplus, floor), sigmoid).  Each map is
+# pinned by closed forms, library routines and invariances, and the composition
+# by a hand-worked example.
+def test_prologue_golden_example(oracle_mod):
+    with open(os.path.join(HERE, "golden", "prologue_examples.json")) as f:
+        gold = json.load(f)
+    for ex in gold["examples"]:
+        T, dk = len(ex["q_raw"]), ex["dk"]
+        sh = lambda a: np.asarray(a, dtype=np.float64).reshape(T, 1, -1)
+        qh, kh, la, be = oracle_mod.prologue(sh(ex["q_raw"]), sh(ex["k_raw"]), sh(ex["gate_pre"]),
+                                             np.asarray(ex["beta_pre"]).reshape(T, 1), ex["lo"])
+        np.testing.assert_allclose(qh[:, 0], ex["q_hat"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(kh[:, 0], ex["k_hat"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(la[:, 0], ex["log_alpha"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(be[:, 0], ex["beta"], rtol=0, atol=1e-15)
+        o, hT = oracle_mod.fwd_prologue(sh(ex["q_raw"]), sh(ex["k_raw"]), sh(ex["v"]), sh(ex["gate_pre"]),
+                                        np.asarray(ex["beta_pre"]).reshape(T, 1), ex["lo"])
+        np.testing.assert_allclose(o[:, 0], ex["o"], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(hT[0, 0], ex["hT"], rtol=0, atol=1e-14)
+
+
+def test_prologue_normalisation(oracle_mod):
+    r = rng0(71)
+    q = r.standard_normal((9, 3, 16)) * r.uniform(0.01, 50.0, (9, 3, 1))
+    k = r.standard_normal((9, 3, 16))
+    a = r.standard_normal((9, 3, 16))
+    b = r.standard_normal((9, 3))
+    qh, kh, _, _ = oracle_mod.prologue(q, k, a, b, -30.0)
+    np.testing.assert_allclose(np.linalg.norm(qh, axis=-1), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(np.linalg.norm(kh, axis=-1), 1.0, rtol=1e-15)
+    # same direction: the cosine with the raw vector is 1
+    cos = np.sum(qh * q, axis=-1) / np.linalg.norm(q, axis=-1)
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-14)
+    # scale invariance per row (positive scales)
+    qh2, kh2, _, _ = oracle_mod.prologue(q * 7.25, k * 1e-3, a, b, -30.0)
+    np.testing.assert_allclose(qh2, qh, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(kh2, kh, rtol=0, atol=1e-15)
+    # eps: a zero row stays zero; a row shorter than eps is divided by eps
+    z = np.zeros((1, 1, 4))
+    tiny = np.array([[[1e-9, 0.0, 0.0, 0.0]]])
+    qz, kt, _, _ = oracle_mod.prologue(z, tiny, np.zeros((1, 1, 4)), np.zeros((1, 1)), -30.0, eps=1e-6)
+    assert np.all(qz == 0.0)
+    np.testing.assert_allclose(kt[0, 0], [1e-3, 0.0, 0.0, 0.0], rtol=1e-15)
+
+
+def test_prologue_gate_softplus_and_floor(oracle_mod):
+    a = np.array([0.0, np.log(np.e - 1.0), -50.0, 50.0, 3.0, -3.0])
+    x = a.reshape(1, 1, -1)
+    one = np.ones_like(x)
+    _, _, la, _ = oracle_mod.prologue(one, one, x, np.zeros((1, 1)), -100.0)
+    la = la[0, 0]
+    assert la[0] == pytest.approx(-np.log(2.0), rel=1e-15)        # softplus(0) = ln 2
+    assert la[1] == pytest.approx(-1.0, rel=1e-15)                # softplus(ln(e-1)) = 1
+    assert la[2] == pytest.approx(-np.exp(-50.0), rel=1e-12)      # alpha -> 1
+    assert la[3] == pytest.approx(-50.0, rel=1e-15)               # softplus(a) -> a
+    # softplus(a) - softplus(-a) = a, and the library's log(1 + e^a)
+    r = rng0(72)
+    aa = r.uniform(-40, 40, (1, 1, 64))
+    ones = np.ones_like(aa)
+    _, _, lp, _ = oracle_mod.prologue(ones, ones, aa, np.zeros((1, 1)), -1e3)
+    _, _, lm, _ = oracle_mod.prologue(ones, ones, -aa, np.zeros((1, 1)), -1e3)
+    np.testing.assert_allclose(-lp + lm, aa, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(-lp, np.logaddexp(0.0, aa), rtol=1e-15, atol=0)
+    # the floor: exactly lo where -softplus falls below it, untouched elsewhere
+    lo = -0.75
+    _, _, lf, _ = oracle_mod.prologue(ones, ones, aa, np.zeros((1, 1)), lo)
+    below = -np.logaddexp(0.0, aa) < lo
+    assert below.any() and (~below).any()
+    assert np.all(lf[below] == lo)
+    np.testing.assert_allclose(lf[~below], lp[~below], rtol=0, atol=0)
+
+
+def test_prologue_beta_sigmoid(oracle_mod):
+    from scipy.special import expit
+    r = rng0(73)
+    b = np.concatenate([[0.0, 40.0, -40.0, 1e-9], r.uniform(-30, 30, 60)]).reshape(64, 1)
+    one = np.ones((64, 1, 2))
+    _, _, _, bp = oracle_mod.prologue(one, one, one, b, -30.0)
+    _, _, _, bm = oracle_mod.prologue(one, one, one, -b, -30.0)
+    assert bp[0, 0] == 0.5
+    np.testing.assert_allclose(bp + bm, 1.0, rtol=0, atol=1e-15)   # sigmoid(b) + sigmoid(-b) = 1
+    np.testing.assert_allclose(bp, expit(b), rtol=1e-15, atol=0)
+    assert bp[2, 0] == pytest.approx(np.exp(-40.0), rel=1e-12)
+
+
+def test_prologue_forward_scale_invariance(oracle_mod):
+    # o and h_T depend on q and k only through their directions
+    r = rng0(74)
+    T, H, dk, dv = 40, 2, 8, 5
+    q = r.standard_normal((T, H, dk))
+    k = r.standard_normal((T, H, dk))
+    v = r.standard_normal((T, H, dv))
+    a = r.standard_normal((T, H, dk))
+    b = r.standard_normal((T, H))
+    o1, h1 = oracle_mod.fwd_prologue(q, k, v, a, b, -20.0)
+    s = r.uniform(0.1, 10.0, (T, H, 1))
+    o2, h2 = oracle_mod.fwd_prologue(q * s, k / s, v, a, b, -20.0)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(h2, h1, rtol=0, atol=1e-12)
+    # and decode on raw inputs equals one forward step
+    S0 = r.standard_normal((T, H, dk, dv)) * 0.1
+    od, Sd = oracle_mod.decode_prologue(q, k, v, a, b, -20.0, S0)
+    cu = np.arange(T + 1)
+    of, hf = oracle_mod.fwd_prologue(q, k, v, a, b, -20.0, h0=S0, cu_seqlens=cu)
+    np.testing.assert_allclose(od, of, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(Sd, hf, rtol=0, atol=1e-15)
