@@ -5,7 +5,9 @@ One "step" is one kda_chunk_fwd call over the long-context prefill workload
 (bf16, B=1, H=32, T=65536, d_k=d_v=128, chunk 64, per-channel decay in
 [0.5, 0.9999]); inputs are seeded, synthetic and resident in HBM before timing.
 The decode step (B=256 resident fp32 states, H=32, d=128, 1000 steps with fresh
-inputs) is timed in the same run and reported under "decode".
+inputs) is timed in the same run and reported under "decode", and the same
+prefill on raw projections through the fused input prologue
+(kda_chunk_fwd_prologue) under "prologue".
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -133,6 +135,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -191,6 +194,29 @@ def main():
                       "B": 1, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": 64,
                       "parallelism": "single GPU"},
            "roofline": roof, "mfma": mfma, "source_digest": digest}
+
+    # ---------------- the same prefill on raw projections (fused input prologue)
+    if not args.no_prologue:
+        dr = I.make_chunk_raw_inputs(cfg, device=dev, gate="uniform")
+        args_p = (dr["q_raw"], dr["k_raw"], dr["v"], dr["gate_pre"], dr["beta_pre"])
+        lo = -30.0
+        fnp = lambda: kda.kda_chunk_fwd_prologue(*args_p, lo, o=o, h_T=hT)
+        per_p, _ = time_launches(fnp, args.steps, args.warmup, stream)
+        pms = float(np.mean(per_p))
+        # a separate prologue pass would read q, k, the gate and beta raw and write
+        # them back mapped: twice their bytes per token-head
+        sep_b = tok_heads * 2 * (2 * dk * 2 + dk * 2 + 2)
+        out["prologue"] = {
+            "workload": "kda_chunk_fwd_prologue bf16 B=1 H=32 T=65536 d_k=d_v=128 chunk=64 on raw "
+                        "projections (q, k ~ N(0,1) unnormalised; beta_pre ~ N(0,1); gate_pre ~ "
+                        "U(%.3f, 0), i.e. decay in [0.5, 0.9999]; floor -30)" % I.RAW_GATE_LO,
+            "ms_per_step": pms, "tokens_per_s": T / (pms * 1e-3), "vs_plain_ms": pms / ms,
+            "roofline": {"bound": "hbm", "achieved": alg_b / (pms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": alg_b / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": None, "alg_bytes_per_launch": alg_b},
+            "separate_pass_alg_bytes": sep_b,
+            "separate_pass_floor_ms": sep_b / (HBM_PEAK_GBS * 1e9) * 1e3}
+        del dr, args_p
 
     # ---------------- decode step
     if not args.no_decode:

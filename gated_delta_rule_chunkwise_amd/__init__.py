@@ -9,6 +9,8 @@ point raises.
 Entry points (same names as the C ABI):
     kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, ...)
     kda_decode_step(q, k, v, log_alpha, beta, S, o=None)
+    kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, ...)
+    kda_decode_step_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, o=None)
     kda_chunk_fwd_workspace_size(...), kda_status_string(code), kda_abi_version()
 """
 from __future__ import annotations
@@ -22,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
-                    "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step")
+                    "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step",
+                    "kda_chunk_fwd_prologue", "kda_decode_step_prologue")
 
 _lib = None
 
@@ -60,6 +63,12 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                     ctypes.c_int, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i32, vp, vp, i32,
+                                           i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    lib.kda_chunk_fwd_prologue.restype = ctypes.c_int
+    lib.kda_decode_step_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i32, i32, i32,
+                                             i32, ctypes.c_int, ctypes.c_int, vp]
+    lib.kda_decode_step_prologue.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -114,6 +123,22 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
     on the device (B must be 1) or None.  Returns (o, h_T) with h_T None when
     output_final_state is False.  Runs asynchronously on the current stream.
     """
+    return _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_state, workspace,
+                      None)
+
+
+def kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h0=None,
+                           cu_seqlens=None, *, o=None, h_T=None, output_final_state=True,
+                           workspace=None):
+    """kda_chunk_fwd on raw projections: the kernels apply q/|q|, k/|k|,
+    log_alpha = max(-softplus(gate_pre), log_alpha_min) and beta = sigmoid(beta_pre)
+    as they read the inputs.  Shapes and dtypes as for kda_chunk_fwd."""
+    return _chunk_fwd(q_raw, k_raw, v, gate_pre, beta_pre, h0, cu_seqlens, o, h_T, output_final_state,
+                      workspace, float(log_alpha_min))
+
+
+def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_state, workspace,
+               log_alpha_min):
     import torch
     lib = load_library()
     squeeze = q.dim() == 3
@@ -148,13 +173,21 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
     ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, N if cu_seqlens is not None else 0, io)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
-                           _ptr(cu_seqlens), N if cu_seqlens is not None else 0, _ptr(o), _ptr(h_T),
-                           B, T, H, dk, dv, io, gt, _ptr(workspace),
-                           0 if workspace is None else workspace.numel() * workspace.element_size(),
-                           _stream_of(q))
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nseq = N if cu_seqlens is not None else 0
+    if log_alpha_min is None:
+        name = "kda_chunk_fwd"
+        rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                               _ptr(cu_seqlens), nseq, _ptr(o), _ptr(h_T), B, T, H, dk, dv, io, gt,
+                               _ptr(workspace), ws_len, _stream_of(q))
+    else:
+        name = "kda_chunk_fwd_prologue"
+        rc = lib.kda_chunk_fwd_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                        log_alpha_min, _ptr(h0), _ptr(cu_seqlens), nseq, _ptr(o),
+                                        _ptr(h_T), B, T, H, dk, dv, io, gt, _ptr(workspace), ws_len,
+                                        _stream_of(q))
     if rc != KDA_OK:
-        raise KDAError(rc, "kda_chunk_fwd", kda_last_hip_error())
+        raise KDAError(rc, name, kda_last_hip_error())
     if squeeze:
         o = o.squeeze(0)
     return o, h_T
@@ -163,6 +196,15 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
 def kda_decode_step(q, k, v, log_alpha, beta, S, o=None):
     """One decode step.  q, k, log_alpha: [B, H, d_k]; v: [B, H, d_v];
     beta: [B, H]; S: [B, H, d_k, d_v] fp32, updated in place.  Returns o."""
+    return _decode_step(q, k, v, log_alpha, beta, S, o, None)
+
+
+def kda_decode_step_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, o=None):
+    """kda_decode_step on raw projections (the maps of kda_chunk_fwd_prologue)."""
+    return _decode_step(q_raw, k_raw, v, gate_pre, beta_pre, S, o, float(log_alpha_min))
+
+
+def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min):
     import torch
     lib = load_library()
     B, H, dk = q.shape
@@ -175,13 +217,22 @@ def kda_decode_step(q, k, v, log_alpha, beta, S, o=None):
         raise ValueError("S must be fp32 [B, H, d_k, d_v]")
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
-    rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
-                             _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha),
-                             _stream_of(q))
+    if log_alpha_min is None:
+        name = "kda_decode_step"
+        rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                 _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha),
+                                 _stream_of(q))
+    else:
+        name = "kda_decode_step_prologue"
+        rc = lib.kda_decode_step_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                          log_alpha_min, _ptr(S), _ptr(o), B, H, dk, dv,
+                                          _dtype_code(q), _dtype_code(log_alpha), _stream_of(q))
     if rc != KDA_OK:
-        raise KDAError(rc, "kda_decode_step", kda_last_hip_error())
+        raise KDAError(rc, name, kda_last_hip_error())
     return o
 
 
 chunk_fwd = kda_chunk_fwd
 decode_step = kda_decode_step
+chunk_fwd_prologue = kda_chunk_fwd_prologue
+decode_step_prologue = kda_decode_step_prologue

@@ -3,6 +3,7 @@
 // so invalid arguments never reach the device.
 #include "kda.h"
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -26,6 +27,19 @@ bool sizes_fit(int64_t a, int64_t b, int64_t c) {
     if (a * b != 0 && c > lim / (a * b)) return false;
     return true;
 }
+
+// The floor of log alpha under the input prologue: finite and <= 0.
+bool valid_floor(float lo) { return isfinite(lo) && lo <= 0.f; }
+
+kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const void *log_alpha,
+                            const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                            void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                            kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream, bool prologue, float lo);
+kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
+                              const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
+                              int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
+                              bool prologue, float lo);
 
 }  // namespace
 
@@ -67,6 +81,47 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
                            kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
+                          io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f);
+}
+
+kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v,
+                                    const void *gate_pre, const void *beta_pre, float log_alpha_min,
+                                    const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                                    void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                    int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
+    return chunk_fwd_impl(q_raw, k_raw, v, gate_pre, beta_pre, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k,
+                          d_v, io_dtype, gate_dtype, workspace, workspace_bytes, stream, true, log_alpha_min);
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
+                             const void *beta, float *S, void *o, int32_t B, int32_t H,
+                             int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                             kda_dtype_t gate_dtype, void *stream) {
+    return decode_step_impl(q, k, v, log_alpha, beta, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
+                            0.f);
+}
+
+kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v,
+                                      const void *gate_pre, const void *beta_pre, float log_alpha_min,
+                                      float *S, void *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                                      kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream) {
+    if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
+    return decode_step_impl(q_raw, k_raw, v, gate_pre, beta_pre, S, o, B, H, d_k, d_v, io_dtype, gate_dtype,
+                            stream, true, log_alpha_min);
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const void *log_alpha,
+                            const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                            void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                            kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream, bool prologue, float lo) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -103,16 +158,17 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.prologue = prologue; a.log_alpha_min = lo;
     g_hip_error[0] = '\0';
     if (kda::launch_chunk_fwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
         return KDA_ERR_HIP;
     return KDA_OK;
 }
 
-kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
-                             const void *beta, float *S, void *o, int32_t B, int32_t H,
-                             int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                             kda_dtype_t gate_dtype, void *stream) {
+kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
+                              const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
+                              int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
+                              bool prologue, float lo) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -126,10 +182,11 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S; a.o = o;
     a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
+    a.prologue = prologue; a.log_alpha_min = lo;
     g_hip_error[0] = '\0';
     if (kda::launch_decode_step(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
         return KDA_ERR_HIP;
     return KDA_OK;
 }
 
-}  // extern "C"
+}  // namespace

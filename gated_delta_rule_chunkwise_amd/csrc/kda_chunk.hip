@@ -77,22 +77,24 @@ struct alignas(16) ChunkSmem {
     float colGn[DK];                           // e^{g_n}
     float colGnM[DK];                          // e^{g_n - m}
     float tot[DK][kWaves];                     // per-8-row sums of log2(alpha)
-    float red[4][2 * BV + 1];                  // token path: cross-wave partial sums
+    float red[4][TokenRed<BV>::N];             // token path: cross-wave partial sums
     float T8[4][2][8][8];                      // 8x8 diagonal inverses, per wave
     float W8[4][8][8];                         // 8x8 merge scratch, per wave
 };
 
 template <int BV>
 struct alignas(16) ExactSmem {
-    float red[4][2 * BV + 1];
+    float red[4][TokenRed<BV>::N];
 };
 
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT>
+// PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
+// (input prologue; lo is the floor of log alpha).
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
     const int32_t *__restrict__ cu_seqlens, IO *__restrict__ o, float *__restrict__ h_T,
-    int64_t seq_len, int32_t H, int32_t DV, int64_t num_chains) {
+    int64_t seq_len, int32_t H, int32_t DV, int64_t num_chains, float lo) {
     constexpr int CPL = DK / 64;    // key channels per lane in the load phase
     constexpr int NKS = DK / 32;    // 32-wide k-steps over d_k
     constexpr int NT = BV / 16;     // 16-column tiles per block
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 
     if constexpr (EXACT) {
         for (int64_t tk = bos; tk < eos; ++tk)
-            token_update<DK, BV, IO, GT>(Sacc, smem.red, q, k, v, log_alpha, beta, o, tk, H, h, DV, col0, w,
-                                         lg, lr);
+            token_update<DK, BV, IO, GT, PRO>(Sacc, smem.red, q, k, v, log_alpha, beta, o, tk, H, h, DV, col0, w,
+                                              lg, lr, lo);
     } else {
         Sm &sm = smem;
         // Upper blocks of T and P are never written: zero them once.
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             (&sm.T[0][0][0])[idx] = (bf16_t)0.f;
             (&sm.P[0][0][0])[idx] = (bf16_t)0.f;
         }
-        ChunkRegs<DK, BV, IO, GT> in;
+        ChunkRegs<DK, BV, IO, GT, PRO> in;
         if (bos < eos) {
             const int nv0 = (int)((eos - bos) < kC ? (eos - bos) : kC);
             in.load(q, k, v, log_alpha, beta, bos, nv0, H, h, DV, col0, w, l, lg, lr);
@@ -165,13 +167,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             lds_barrier();
 
             // ======== phase L: log2-decay cumsum, anchors, decayed operands ========
+            in.prepare(w, lo);
             const bool partial = nv < kC;
             float csum[8][CPL];
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    float x = vget(in.la[i], cc) * kLog2e;
+                    float x = in.gate(i, cc, lo) * kLog2e;
                     if (partial && 8 * w + i >= nv) x = 0.f;
                     csum[i][cc] = i ? csum[i - 1][cc] + x : x;
                 }
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                     float al[8];
 #pragma unroll
                     for (int i = 1; i < 8; ++i) {
-                        float x = vget(in.la[i], cc) * kLog2e;
+                        float x = in.gate(i, cc, lo) * kLog2e;
                         if (partial && 8 * w + i >= nv) x = 0.f;
                         al[i] = kexp2<SPLIT>(x);
                     }
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                     float ka[CPL], qa[CPL], ki[CPL];
 #pragma unroll
                     for (int cc = 0; cc < CPL; ++cc) {
-                        const float kv = vget(in.kk[i], cc), qv = vget(in.qq[i], cc);
+                        const float kv = in.kval(i, cc), qv = in.qval(i, cc);
                         ka[cc] = kv * e1[i][cc];
                         qa[cc] = qv * e1[i][cc];
                         ki[cc] = kv * e2[i][cc];
@@ -293,8 +296,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             if (slow) {
                 // exact token-by-token path for a chunk with a huge in-chunk decay
                 for (int r = 0; r < nv; ++r)
-                    token_update<DK, BV, IO, GT>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h,
-                                                 DV, col0, w, lg, lr);
+                    token_update<DK, BV, IO, GT, PRO>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h,
+                                                      DV, col0, w, lg, lr, lo);
                 continue;
             }
 
@@ -588,26 +591,32 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     }
 }
 
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT>
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t st) {
     const int64_t chains = a.num_seqs * (int64_t)a.H;
     const int64_t nwg = chains * (a.d_v / BV);
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, EXACT>), dim3((unsigned)nwg), dim3(kThreads), 0,
-                       st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
-                       (const GT *)a.beta, a.h0, a.cu_seqlens, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains);
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, EXACT, PRO>), dim3((unsigned)nwg), dim3(kThreads),
+                       0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
+                       (const GT *)a.beta, a.h0, a.cu_seqlens, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains,
+                       a.log_alpha_min);
     return hipGetLastError();
 }
 
 // bf16 I/O: single-bf16 decayed operands.  fp32 I/O: split operands (d_k = 64)
 // or the exact token path (d_k = 128).
-template <int DK, int BV>
+template <int DK, int BV, bool PRO>
 hipError_t launch_types(const ChunkArgs &a, hipStream_t st) {
     if (a.io_bf16)
-        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, false>(a, st)
-                           : launch_t<DK, BV, bf16_t, float, false, false>(a, st);
+        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, false, PRO>(a, st)
+                           : launch_t<DK, BV, bf16_t, float, false, false, PRO>(a, st);
     constexpr bool EX = DK == 128;
-    return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, !EX, EX>(a, st)
-                       : launch_t<DK, BV, float, float, !EX, EX>(a, st);
+    return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, !EX, EX, PRO>(a, st)
+                       : launch_t<DK, BV, float, float, !EX, EX, PRO>(a, st);
+}
+
+template <int DK, int BV>
+hipError_t launch_types_pro(const ChunkArgs &a, hipStream_t st) {
+    return a.prologue ? launch_types<DK, BV, true>(a, st) : launch_types<DK, BV, false>(a, st);
 }
 
 // Value-column block width: 32 when that still gives at least two workgroups
@@ -657,9 +666,9 @@ int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len
         }
         e = launch_chunk_fwd_two_kernel(a, bv, st);
     } else if (a.d_k == 128)
-        e = bv == 32 ? launch_types<128, 32>(a, st) : launch_types<128, 16>(a, st);
+        e = bv == 32 ? launch_types_pro<128, 32>(a, st) : launch_types_pro<128, 16>(a, st);
     else
-        e = bv == 32 ? launch_types<64, 32>(a, st) : launch_types<64, 16>(a, st);
+        e = bv == 32 ? launch_types_pro<64, 32>(a, st) : launch_types_pro<64, 16>(a, st);
     if (e != hipSuccess) {
         snprintf(err, err_len, "%s", hipGetErrorString(e));
         return -1;

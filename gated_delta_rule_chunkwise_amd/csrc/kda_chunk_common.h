@@ -145,17 +145,25 @@ template <int DK, int BV> struct StateTiles {
 // One exact token update of this workgroup's state block (the per-token rule of
 // the KimiLinear article, section 2.3, with the read-out o = S^T q).  Waves 0-3
 // hold the state; all waves take part in the two barriers.
-template <int DK, int BV, typename IO, typename GT>
-__device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 16) / 4], float (*red)[2 * BV + 1],
-                                             const IO *__restrict__ q, const IO *__restrict__ k,
-                                             const IO *__restrict__ v, const GT *__restrict__ log_alpha,
-                                             const GT *__restrict__ beta, IO *__restrict__ o, int64_t tk,
-                                             int H, int h, int DV, int col0, int w, int lg, int lr) {
+// Token-path reduction slots per wave: a (BV), b (BV), q.k, and with the input
+// prologue also |q|^2 and |k|^2.
+template <int BV> struct TokenRed { static constexpr int N = 2 * BV + 3; };
+
+// With PRO (raw projections in), the gate and beta are mapped as they are read
+// and the raw q and k enter through their squared norms: a = k^T S and b = q^T S
+// are taken with the raw vectors and rescaled once the norms are reduced.
+template <int DK, int BV, typename IO, typename GT, bool PRO = false>
+__device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 16) / 4],
+                                             float (*red)[TokenRed<BV>::N], const IO *__restrict__ q,
+                                             const IO *__restrict__ k, const IO *__restrict__ v,
+                                             const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
+                                             IO *__restrict__ o, int64_t tk, int H, int h, int DV, int col0, int w,
+                                             int lg, int lr, float lo = 0.f) {
     constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
     float kc[STW][4];
     if (w < 4) {
         const int64_t kb = (tk * H + h) * (int64_t)DK;
-        float pa[NT], pb[NT], pqk = 0.f;
+        float pa[NT], pb[NT], pqk = 0.f, pqq = 0.f, pkk = 0.f;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) pa[nt] = pb[nt] = 0.f;
 #pragma unroll
@@ -165,12 +173,19 @@ __device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 1
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * mt + 4 * lg + e;
                 const float kv = to_f32(k[kb + c]), qv = to_f32(q[kb + c]);
-                const float av = expf(to_f32(log_alpha[kb + c]));
+                const float la = to_f32(log_alpha[kb + c]);
+                const float av = expf(PRO ? pro_log_alpha(la, lo) : la);
                 kc[i][e] = kv;
                 Sacc[i][e] *= av;
                 pa[nt] += kv * Sacc[i][e];
                 pb[nt] += qv * Sacc[i][e];
-                if (nt == 0) pqk += qv * kv;
+                if (nt == 0) {   // each key channel once per wave
+                    pqk += qv * kv;
+                    if (PRO) {
+                        pqq += qv * qv;
+                        pkk += kv * kv;
+                    }
+                }
             }
         }
 #pragma unroll
@@ -182,27 +197,51 @@ __device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 1
         }
         pqk += __shfl_xor(pqk, 16);
         pqk += __shfl_xor(pqk, 32);
+        if (PRO) {
+            pqq += __shfl_xor(pqq, 16);
+            pqq += __shfl_xor(pqq, 32);
+            pkk += __shfl_xor(pkk, 16);
+            pkk += __shfl_xor(pkk, 32);
+        }
         if (lg == 0) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 red[w][nt * 16 + lr] = pa[nt];
                 red[w][BV + nt * 16 + lr] = pb[nt];
             }
-            if (lr == 0) red[w][2 * BV] = pqk;
+            if (lr == 0) {
+                red[w][2 * BV] = pqk;
+                if (PRO) {
+                    red[w][2 * BV + 1] = pqq;
+                    red[w][2 * BV + 2] = pkk;
+                }
+            }
         }
     }
     lds_barrier();
     if (w < 4) {
-        const float qk = red[0][2 * BV] + red[1][2 * BV] + red[2][2 * BV] + red[3][2 * BV];
-        const float bt = to_f32(beta[tk * H + h]);
+        float qk = red[0][2 * BV] + red[1][2 * BV] + red[2][2 * BV] + red[3][2 * BV];
+        float bt = to_f32(beta[tk * H + h]);
+        float iq = 1.f, ik = 1.f;
+        if (PRO) {
+            iq = pro_inv_norm(red[0][2 * BV + 1] + red[1][2 * BV + 1] + red[2][2 * BV + 1] + red[3][2 * BV + 1]);
+            ik = pro_inv_norm(red[0][2 * BV + 2] + red[1][2 * BV + 2] + red[2][2 * BV + 2] + red[3][2 * BV + 2]);
+            qk *= iq * ik;
+            bt = pro_beta(bt);
+        }
         float u[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int jl = nt * 16 + lr;
-            const float a = red[0][jl] + red[1][jl] + red[2][jl] + red[3][jl];
-            const float b = red[0][BV + jl] + red[1][BV + jl] + red[2][BV + jl] + red[3][BV + jl];
+            float a = red[0][jl] + red[1][jl] + red[2][jl] + red[3][jl];
+            float b = red[0][BV + jl] + red[1][BV + jl] + red[2][BV + jl] + red[3][BV + jl];
+            if (PRO) {
+                a *= ik;
+                b *= iq;
+            }
             u[nt] = bt * (to_f32(v[(tk * H + h) * (int64_t)DV + col0 + jl]) - a);
             if (w == 0 && lg == 0) o[(tk * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(b + u[nt] * qk);
+            if (PRO) u[nt] *= ik;   // the state takes k_hat = k / |k|
         }
 #pragma unroll
         for (int i = 0; i < STW; ++i) {
@@ -227,7 +266,11 @@ template <> __device__ __forceinline__ float vget<float>(const float &x, int) { 
 template <> __device__ __forceinline__ float vget<bf16x2_t>(const bf16x2_t &x, int i) { return (float)x[i]; }
 template <> __device__ __forceinline__ float vget<float2>(const float2 &x, int i) { return i ? x.y : x.x; }
 
-template <int DK, int BV, typename IO, typename GT>
+// With PRO (raw projections in) the accessors return the mapped inputs: gate()
+// the floored -softplus (mapped once, at load), kval()/qval() the raw value
+// times the per-token inverse norm (reduced over the wave, which holds whole
+// rows), and bt is sigmoid(b).
+template <int DK, int BV, typename IO, typename GT, bool PRO = false>
 struct ChunkRegs {
     static constexpr int CPL = DK / 64, NT = BV / 16;
     typedef typename VecT<GT, CPL>::type GV;
@@ -236,6 +279,21 @@ struct ChunkRegs {
     IV kk[8], qq[8];
     float vv[NT][4];
     float bt;
+    float qs[PRO ? 8 : 1], ks[PRO ? 8 : 1];
+    float lf[PRO ? 8 : 1][CPL];
+
+    __device__ __forceinline__ float gate(int i, int cc, float) const {
+        if constexpr (PRO) return lf[i][cc];
+        else return vget(la[i], cc);
+    }
+    __device__ __forceinline__ float kval(int i, int cc) const {
+        if constexpr (PRO) return vget(kk[i], cc) * ks[i];
+        else return vget(kk[i], cc);
+    }
+    __device__ __forceinline__ float qval(int i, int cc) const {
+        if constexpr (PRO) return vget(qq[i], cc) * qs[i];
+        else return vget(qq[i], cc);
+    }
 
     __device__ __forceinline__ void load(const IO *__restrict__ q, const IO *__restrict__ k,
                                          const IO *__restrict__ v, const GT *__restrict__ log_alpha,
@@ -261,6 +319,29 @@ struct ChunkRegs {
                 }
         }
         if (w == 0) bt = to_f32(beta[(tbase + (l < nv ? l : nv - 1)) * H + h]);
+    }
+
+    // The prologue maps of the loaded chunk (nothing without PRO); called once
+    // per load, where the inputs are first used, so that a load issued ahead is
+    // not waited for early.
+    __device__ __forceinline__ void prepare(int w, float lo) {
+        if constexpr (PRO) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const float a = vget(qq[i], cc), b = vget(kk[i], cc);
+                    sq += a * a;
+                    sk += b * b;
+                }
+                qs[i] = pro_inv_norm(wave_sum(sq));
+                ks[i] = pro_inv_norm(wave_sum(sk));
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) lf[i][cc] = pro_log_alpha(vget(la[i], cc), lo);
+            }
+            if (w == 0) bt = pro_beta(bt);
+        }
     }
 };
 

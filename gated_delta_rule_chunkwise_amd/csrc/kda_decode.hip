@@ -19,18 +19,21 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
-template <int DK, int DV, typename IO, typename GT>
+// PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
+// (input prologue; lo is the floor of log alpha).  The reductions then run on
+// the raw q and k and are rescaled by the inverse norms, reduced alongside.
+template <int DK, int DV, typename IO, typename GT, bool PRO>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, float *__restrict__ S,
-    IO *__restrict__ o) {
+    IO *__restrict__ o, float lo) {
     constexpr int NCG = DV / 4;                 // groups of 4 value columns
     constexpr int NRG = kDecodeThreads / NCG;   // row groups
     constexpr int RPT = DK / NRG;               // key rows per thread
     static_assert(RPT >= 1 && RPT * NRG == DK, "bad decode tiling");
 
     __shared__ float red[NRG][NCG][8];
-    __shared__ float red_qk[NRG];
+    __shared__ float red_qk[NRG][PRO ? 3 : 1];
 
     const int64_t bh = blockIdx.x;
     const int t = threadIdx.x;
@@ -47,26 +50,37 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     for (int i = 0; i < RPT; ++i) {
         kk[i] = to_f32(k[bh * DK + row0 + i]);
         qq[i] = to_f32(q[bh * DK + row0 + i]);
-        al[i] = __expf(to_f32(log_alpha[bh * DK + row0 + i]));
+        const float la = to_f32(log_alpha[bh * DK + row0 + i]);
+        al[i] = __expf(PRO ? pro_log_alpha(la, lo) : la);
     }
 
-    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f}, pqk = 0.f;
+    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f}, pqk = 0.f, pqq = 0.f, pkk = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         s[i].x *= al[i]; s[i].y *= al[i]; s[i].z *= al[i]; s[i].w *= al[i];
         pa[0] += kk[i] * s[i].x; pa[1] += kk[i] * s[i].y; pa[2] += kk[i] * s[i].z; pa[3] += kk[i] * s[i].w;
         pb[0] += qq[i] * s[i].x; pb[1] += qq[i] * s[i].y; pb[2] += qq[i] * s[i].z; pb[3] += qq[i] * s[i].w;
         pqk += qq[i] * kk[i];
+        if (PRO) {
+            pqq += qq[i] * qq[i];
+            pkk += kk[i] * kk[i];
+        }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         red[rg][cg][j] = pa[j];
         red[rg][cg][4 + j] = pb[j];
     }
-    if (cg == 0) red_qk[rg] = pqk;
+    if (cg == 0) {
+        red_qk[rg][0] = pqk;
+        if (PRO) {
+            red_qk[rg][1] = pqq;
+            red_qk[rg][2] = pkk;
+        }
+    }
     __syncthreads();
 
-    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f, nq = 0.f, nk = 0.f;
 #pragma unroll
     for (int r = 0; r < NRG; ++r) {
 #pragma unroll
@@ -74,9 +88,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
             a[j] += red[r][cg][j];
             b[j] += red[r][cg][4 + j];
         }
-        qk += red_qk[r];
+        qk += red_qk[r][0];
+        if (PRO) {
+            nq += red_qk[r][1];
+            nk += red_qk[r][2];
+        }
     }
-    const float bt = to_f32(beta[bh]);
+    float bt = to_f32(beta[bh]);
+    float ik = 1.f;
+    if (PRO) {
+        const float iq = pro_inv_norm(nq);
+        ik = pro_inv_norm(nk);
+        qk *= iq * ik;
+        bt = pro_beta(bt);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[j] *= ik;
+            b[j] *= iq;
+        }
+    }
     float u[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) u[j] = bt * (to_f32(v[bh * DV + 4 * cg + j]) - a[j]);
@@ -86,11 +116,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     // from competing with the state still being read (measured: 5.2 -> 6.9 TB/s).
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
+        const float kh = PRO ? kk[i] * ik : kk[i];   // the state takes k / |k|
         f32x4_t r;
-        r[0] = s[i].x + kk[i] * u[0];
-        r[1] = s[i].y + kk[i] * u[1];
-        r[2] = s[i].z + kk[i] * u[2];
-        r[3] = s[i].w + kk[i] * u[3];
+        r[0] = s[i].x + kh * u[0];
+        r[1] = s[i].y + kh * u[1];
+        r[2] = s[i].z + kh * u[2];
+        r[3] = s[i].w + kh * u[3];
         __builtin_nontemporal_store(r, reinterpret_cast<f32x4_t *>(Sp + (row0 + i) * DV));
     }
     if (rg == 0) {
@@ -102,9 +133,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
 template <int DK, int DV, typename IO, typename GT>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
     const int64_t nb = a.B * (int64_t)a.H;
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT>), dim3((unsigned)nb), dim3(kDecodeThreads),
-                       0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
-                       (const GT *)a.log_alpha, (const GT *)a.beta, a.S, (IO *)a.o);
+    if (a.prologue)
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT, true>), dim3((unsigned)nb), dim3(kDecodeThreads),
+                           0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+                           (const GT *)a.log_alpha, (const GT *)a.beta, a.S, (IO *)a.o, a.log_alpha_min);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT, false>), dim3((unsigned)nb), dim3(kDecodeThreads),
+                           0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+                           (const GT *)a.log_alpha, (const GT *)a.beta, a.S, (IO *)a.o, 0.f);
     return hipGetLastError();
 }
 

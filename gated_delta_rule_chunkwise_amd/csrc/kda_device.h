@@ -46,4 +46,54 @@ __device__ __forceinline__ f32x4_t zero4() {
     return z;
 }
 
+// ---- input prologue ---------------------------------------------------------------
+// The entry points on raw projections map their inputs as the kernels read them
+// (reading of the KimiLinear article, section 3.2: normalised inputs,
+// constrained and reparameterised gate values):
+//     log alpha = max(-softplus(a), lo),   beta = sigmoid(b),
+//     q, k scaled per (token, head) by 1 / max(||x||_2, eps).
+// softplus(a) = max(a, 0) + log1p(e^-|a|) cannot overflow.  log1p(t) for t in
+// (0, 1] uses the correction of Goldberg, "What Every Computer Scientist Should
+// Know About Floating-Point Arithmetic", theorem 4: with u = 1 + t rounded,
+// log1p(t) = log(u) * t / (u - 1) (or t when u == 1), which keeps the hardware
+// logarithm's relative accuracy for small t.
+constexpr float kPrologueEps = 1e-6f;
+
+__device__ __forceinline__ float pro_log1p_unit(float t) {
+    const float u = 1.f + t;
+    return u == 1.f ? t : __logf(u) * (t * __builtin_amdgcn_rcpf(u - 1.f));
+}
+__device__ __forceinline__ float pro_log_alpha(float a, float lo) {
+    const float sp = fmaxf(a, 0.f) + pro_log1p_unit(__expf(-fabsf(a)));
+    return fmaxf(-sp, lo);
+}
+__device__ __forceinline__ float pro_beta(float b) {
+    const float e = __expf(-fabsf(b));
+    const float r = __builtin_amdgcn_rcpf(1.f + e);
+    return b >= 0.f ? r : e * r;
+}
+// 1 / max(sqrt(s), eps) = rsqrt(max(s, eps^2)), from the hardware reciprocal
+// square root (about 1 ulp).
+__device__ __forceinline__ float pro_inv_norm(float sumsq) {
+    return __builtin_amdgcn_rsqf(fmaxf(sumsq, kPrologueEps * kPrologueEps));
+}
+
+// Sum of x over the 64 lanes of a wave, returned wave-uniform: data-parallel
+// moves within rows of 16 lanes (quad swaps, then half-row and row mirrors, each
+// pairing a lane with one in the other half), then the four row sums.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 }  // namespace kda

@@ -18,6 +18,8 @@ struct ChunkArgs {
     int32_t H, d_k, d_v;
     int32_t io_bf16, gate_bf16; // 1 = bf16, 0 = fp32
     int32_t varlen;             // cu_seqlens given (sequences packed along T)
+    int32_t prologue;           // q, k, log_alpha, beta are raw projections
+    float log_alpha_min;        // floor of log alpha under the prologue
     void *workspace;
     size_t workspace_bytes;
 };
@@ -29,6 +31,8 @@ struct DecodeArgs {
     int64_t B;
     int32_t H, d_k, d_v;
     int32_t io_bf16, gate_bf16;
+    int32_t prologue;           // q, k, log_alpha, beta are raw projections
+    float log_alpha_min;        // floor of log alpha under the prologue
 };
 
 // Both return 0 when the launch was enqueued, or -1 after a HIP error whose

@@ -15,10 +15,18 @@ Recipe (per token and head unless stated):
   * h0 = N(0, 0.1^2) per sequence when requested, else absent (zeros);
   * varlen lengths are integers drawn uniformly from [lo, hi] inclusive.
 Draw order for one call: lengths, q, k, v, beta, log_alpha, h0.
+
+Raw projections (for the entry points with the input prologue) are the same
+draws before those maps: q_raw, k_raw ~ N(0, 1) (not normalised), beta_pre ~
+N(0, 1), gate_pre ~ N(0, gate_scale^2), rounded to their dtypes; with the same
+seed they are the pre-images of the recipe above ("softplus" gate).  The
+"uniform" raw gate draws gate_pre ~ U(a_lo, 0), the interval that -softplus maps
+onto decays between 0.5 and 0.9999.
 """
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Optional
 
 import torch
@@ -152,4 +160,61 @@ def make_decode_step_inputs(cfg: DecodeConfig, step: int, device="cpu", steps: i
         out["v"].append(_randn((B, H, dv), g, device).to(io))
         out["beta"].append(torch.sigmoid(_randn((B, H), g, device)).to(gio))
         out["log_alpha"].append(draw_gate((B, H, dk), "softplus", g, device).to(gio))
+    return {n: torch.stack(xs).contiguous() for n, xs in out.items()}
+
+
+# gate pre-activation interval whose -softplus image is log alpha in
+# [log 0.5, log 0.9999]: softplus(a) = -log(alpha)  <=>  a = log(expm1(-log(alpha)))
+RAW_GATE_LO = math.log(math.expm1(-math.log(0.9999)))
+RAW_GATE_HI = math.log(math.expm1(-math.log(0.5)))
+
+
+def make_chunk_raw_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None,
+                          lengths: Optional[list] = None, h0: Optional[bool] = None,
+                          gate_scale: float = 1.0, gate: str = "softplus"):
+    """Raw projections for kda_chunk_fwd_prologue: q_raw, k_raw, v, gate_pre,
+    beta_pre, h0 (or None), cu_seqlens, lengths (same draw order as
+    make_chunk_inputs)."""
+    seed = cfg.seed if seed is None else seed
+    g = _gen(seed, device)
+    if lengths is None:
+        lengths = seq_lengths(cfg, g, device)
+    want_h0 = cfg.h0 if h0 is None else h0
+    T = int(sum(lengths))
+    H, dk, dv = cfg.H, cfg.dk, cfg.dv
+    io, gio = _DT[cfg.io], _DT[cfg.gate_io]
+    q = _randn((T, H, dk), g, device).to(io)
+    k = _randn((T, H, dk), g, device).to(io)
+    v = _randn((T, H, dv), g, device).to(io)
+    beta_pre = _randn((T, H), g, device).to(gio)
+    if gate == "uniform":
+        u = torch.rand((T, H, dk), generator=g, device=device, dtype=torch.float32)
+        gate_pre = (RAW_GATE_LO + u * (RAW_GATE_HI - RAW_GATE_LO)).to(gio)
+    elif gate == "softplus":
+        gate_pre = (gate_scale * _randn((T, H, dk), g, device)).to(gio)
+    else:
+        raise ValueError("unknown raw gate " + gate)
+    h0_t = None
+    if want_h0:
+        h0_t = (0.1 * _randn((len(lengths), H, dk, dv), g, device)).contiguous()
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
+    return dict(q_raw=q, k_raw=k, v=v, gate_pre=gate_pre, beta_pre=beta_pre, h0=h0_t,
+                cu_seqlens=cu.to(torch.int32).to(device), lengths=list(lengths))
+
+
+def make_decode_raw_step_inputs(cfg: DecodeConfig, step: int, device="cpu", steps: int = 1):
+    """Raw projections of `steps` decode steps from `step` (same seeds and draw
+    order as make_decode_step_inputs): q_raw, k_raw, gate_pre [steps, B, H, dk];
+    v [steps, B, H, dv]; beta_pre [steps, B, H]."""
+    io, gio = _DT[cfg.io], _DT[cfg.gate_io]
+    B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
+    out = {n: [] for n in ("q_raw", "k_raw", "v", "beta_pre", "gate_pre")}
+    for s in range(step, step + steps):
+        g = _gen(cfg.seed + 1 + s, device)
+        out["q_raw"].append(_randn((B, H, dk), g, device).to(io))
+        out["k_raw"].append(_randn((B, H, dk), g, device).to(io))
+        out["v"].append(_randn((B, H, dv), g, device).to(io))
+        out["beta_pre"].append(_randn((B, H), g, device).to(gio))
+        out["gate_pre"].append(_randn((B, H, dk), g, device).to(gio))
     return {n: torch.stack(xs).contiguous() for n, xs in out.items()}

@@ -140,6 +140,47 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
                              int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
                              kda_dtype_t gate_dtype, void *stream);
 
+/*
+ * kda_chunk_fwd_prologue -- kda_chunk_fwd on raw projections (fused input
+ * prologue).
+ *
+ * The KimiLinear article, section 3.2, keeps the chunkwise computation stable by
+ * normalising the inputs and by constraining and reparameterising the gate
+ * values.  This entry point takes the inputs before those maps and applies them
+ * inside the kernels as the inputs are read, so no separate pass over q, k and
+ * the gates is needed.  Per token and head:
+ *
+ *   q = q_raw / max(||q_raw||_2, 1e-6),   k likewise          (over d_k)
+ *   log_alpha = max(-softplus(gate_pre), log_alpha_min)      (per channel)
+ *   beta = sigmoid(beta_pre)
+ *
+ * then exactly the computation of kda_chunk_fwd.  Arguments, layouts, the
+ * workspace (kda_chunk_fwd_workspace_size), ownership and errors are those of
+ * kda_chunk_fwd, with q_raw, k_raw in place of q, k (io_dtype), gate_pre in
+ * place of log_alpha and beta_pre in place of beta (gate_dtype; any finite
+ * values).  log_alpha_min must be finite and <= 0, else
+ * KDA_ERR_INVALID_ARGUMENT; the accuracy statement of kda_chunk_fwd applies
+ * for log_alpha_min >= -30.
+ */
+kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v,
+                                    const void *gate_pre, const void *beta_pre, float log_alpha_min,
+                                    const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                                    void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                    int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step_prologue -- kda_decode_step on raw projections: the maps of
+ * kda_chunk_fwd_prologue applied to q_raw, k_raw [B, H, d_k], gate_pre
+ * [B, H, d_k] and beta_pre [B, H], then exactly one kda_decode_step.  Same
+ * arguments and errors as kda_decode_step; log_alpha_min as for
+ * kda_chunk_fwd_prologue.
+ */
+kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v,
+                                      const void *gate_pre, const void *beta_pre, float log_alpha_min,
+                                      float *S, void *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                                      kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

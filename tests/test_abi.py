@@ -120,3 +120,49 @@ def test_binding_raises_without_gpu_tensors(kda):
     x = torch.zeros(1, 64, 2, 64)
     with pytest.raises(ValueError):
         kda.kda_chunk_fwd(x, x, x, x, torch.zeros(1, 64, 2))
+
+
+def chunk_pro(lib, lo=-20.0, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+             dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_prologue(a["q"], a["k"], a["v"], a["la"], a["beta"], lo, a["h0"], a["cu"],
+                                      a["N"], a["o"], a["hT"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                      a["io"], a["gt"], a["ws"], a["wsb"], None)
+
+
+def decode_pro(lib, lo=-20.0, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, S=P, o=P, B=4, H=2, dk=128, dv=128, io=1, gt=1)
+    a.update(kw)
+    return lib.kda_decode_step_prologue(a["q"], a["k"], a["v"], a["la"], a["beta"], lo, a["S"], a["o"],
+                                        a["B"], a["H"], a["dk"], a["dv"], a["io"], a["gt"], None)
+
+
+@pytest.mark.parametrize("lo", [float("nan"), float("inf"), float("-inf"), 0.5, 1e-30])
+def test_prologue_rejects_bad_floor(kda, lo):
+    lib = kda.load_library()
+    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    assert chunk_pro(lib, lo=lo, ws=P, wsb=need) == 1
+    assert decode_pro(lib, lo=lo) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), 2), (dict(io=5), 2), (dict(B=0), 1), (dict(q=None), 1), (dict(la=None), 1),
+    (dict(beta=P + 1), 1), (dict(cu=P, N=2, B=2), 1), (dict(ws=None, wsb=0), 3),
+])
+def test_chunk_fwd_prologue_validates_like_chunk_fwd(kda, kw, code):
+    lib = kda.load_library()
+    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    a = dict(ws=P, wsb=need)
+    a.update(kw)
+    assert chunk_pro(lib, lo=0.0, **a) == code
+    assert chunk(lib, **a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=32), 2), (dict(B=0), 1), (dict(S=None), 1), (dict(k=P + 2), 1),
+])
+def test_decode_prologue_validates_like_decode(kda, kw, code):
+    lib = kda.load_library()
+    assert decode_pro(lib, **kw) == code
+    assert decode(lib, **kw) == code

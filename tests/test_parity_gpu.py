@@ -255,3 +255,102 @@ def test_decode_steps_equal_chunk_fwd(kda):
     torch.cuda.synchronize()
     assert_close(torch.stack(outs, 1), o, "f32", "decode vs fwd o")
     assert_close(S, hT, "f32", "decode vs fwd state")
+
+
+# ------------------------------------------------------------------ input prologue
+# kda_chunk_fwd_prologue / kda_decode_step_prologue on raw projections against
+# the oracle's prologue (q/|q|, k/|k|, max(-softplus(a), lo), sigmoid(b)) followed
+# by the recurrence.
+def _raw_as_plain(d):
+    return dict(q=d["q_raw"], k=d["k_raw"], v=d["v"], log_alpha=d["gate_pre"], beta=d["beta_pre"],
+                h0=d["h0"], lengths=d["lengths"], cu_seqlens=d["cu_seqlens"])
+
+
+def check_prologue_against_oracle(kda, d, io, lo, seqs=None, heads=None, what=""):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    o, hT = kda.kda_chunk_fwd_prologue(dev["q_raw"], dev["k_raw"], dev["v"], dev["gate_pre"],
+                                       dev["beta_pre"], lo, h0=dev["h0"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    o, hT = o.cpu(), hT.cpu()
+    ref = to_oracle(_raw_as_plain(d), seqs, heads)
+    ro, rh = oracle.fwd_prologue(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], lo,
+                                 h0=ref["h0"], cu_seqlens=ref["cu_seqlens"])
+    hs = slice(None) if heads is None else list(heads)
+    rows = torch.from_numpy(ref["rows"])
+    go = o.reshape(-1, *o.shape[-2:])[rows][:, hs]
+    sq = list(range(len(d["lengths"]))) if seqs is None else list(seqs)
+    eo = assert_close(go, ro, io, what + " o")
+    eh = assert_close(hT[sq][:, hs], rh, io, what + " h_T")
+    log(what, "o", eo, "h_T", eh)
+    return eo, eh
+
+
+def test_prologue_c3_sampled_heads(kda):
+    """The benchmarked prologue call: c3's full size (T = 65536, H = 32) on raw
+    projections, gate pre-activations spanning decays 0.5-0.9999, floor -30;
+    the oracle checks 2 whole heads end to end."""
+    d = I.make_chunk_raw_inputs(I.C3, gate="uniform")
+    check_prologue_against_oracle(kda, d, "bf16", -30.0, heads=[0, 31], what="prologue c3 heads 0,31")
+
+
+def test_prologue_c1_shape_bf16(kda):
+    """c1's shape (bf16, H=16, T=4096, d=128) on raw projections; gate
+    pre-activations N(0, 2^2) with floor -3, so about 7% of gates sit on it."""
+    d = I.make_chunk_raw_inputs(I.C1, gate_scale=2.0)
+    check_prologue_against_oracle(kda, d, "bf16", -3.0, what="prologue c1")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_prologue_ragged_varlen(kda, dk, dv, io):
+    """Ragged packed sequences with h0, zero-norm rows (the eps branch) and gates
+    driven to the floor -20 over whole chunks (decay beyond the matrix-core
+    range: those chunks run token by token, also under the prologue)."""
+    cfg = I.ChunkConfig("pro-ragged", io, io, H=3, dk=dk, dv=dv, h0=True, seed=31)
+    lens = [300, 64, 130, 1, 200]
+    d = I.make_chunk_raw_inputs(cfg, lengths=lens, gate_scale=2.0)
+    q, k, a = d["q_raw"].clone(), d["k_raw"].clone(), d["gate_pre"].clone()
+    q[5] = 0.0                    # zero query: no read-out from the state
+    k[7, 1] = 0.0                 # zero key: no erase or write for head 1
+    a[10] = 60.0                  # -softplus(60) = -60, floored to -20 on every channel
+    a[70:75] = 40.0
+    a[300:364, 1, :3] = 25.0      # sequence 1, head 1: a whole chunk on the floor
+    d["q_raw"], d["k_raw"], d["gate_pre"] = q, k, a.to(d["gate_pre"].dtype)
+    check_prologue_against_oracle(kda, d, io, -20.0, what="prologue ragged dk=%d dv=%d %s" % (dk, dv, io))
+
+
+def test_prologue_decode_c4_shape(kda):
+    cfg = I.C4
+    S = I.make_decode_state(cfg)
+    Sg, Sref = S.to(DEV), f64(S)
+    steps = I.make_decode_raw_step_inputs(cfg, 0, steps=2)
+    names = ("q_raw", "k_raw", "v", "gate_pre", "beta_pre")
+    for s in range(2):
+        x = {n: t[s] for n, t in steps.items()}
+        o = kda.kda_decode_step_prologue(*(x[n].to(DEV) for n in names[:5]), -6.0, Sg)
+        ro, Sref = oracle.decode_prologue(*(f64(x[n]) for n in names), -6.0, Sref)
+        torch.cuda.synchronize()
+        log("prologue decode step", s, assert_close(o.cpu(), ro, "bf16", "prologue decode o"))
+    eS = errors(Sg.cpu(), Sref)
+    assert eS["rel_fro"] < 1e-5, eS
+    log("prologue decode S", eS)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_prologue_decode_dims_fp32(kda, dk, dv):
+    cfg = I.DecodeConfig("dp", "f32", "f32", B=5, H=3, dk=dk, dv=dv, steps=3, seed=2200)
+    S = I.make_decode_state(cfg)
+    Sg, Sref = S.to(DEV), f64(S)
+    steps = I.make_decode_raw_step_inputs(cfg, 0, steps=3)
+    names = ("q_raw", "k_raw", "v", "gate_pre", "beta_pre")
+    for s in range(3):
+        x = {n: t[s] for n, t in steps.items()}
+        if s == 1:
+            x["q_raw"] = x["q_raw"].clone()
+            x["q_raw"][0, 0] = 0.0
+            x["gate_pre"] = x["gate_pre"] * 8.0
+        o = kda.kda_decode_step_prologue(*(x[n].to(DEV) for n in names), -2.5, Sg)
+        ro, Sref = oracle.decode_prologue(*(f64(x[n]) for n in names), -2.5, Sref)
+        assert_close(o.cpu(), ro, "f32", "prologue decode o")
+    assert_close(Sg.cpu(), Sref, "f32", "prologue decode S")
