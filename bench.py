@@ -179,8 +179,8 @@ def main():
     # one kda_chunk_fwd call = chunk_prep_kernel + chunk_state_kernel on one stream
     roof = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,128,bf16,bf16> + "
-                      "chunk_state_kernel<128,128,16,bf16,bf16>",
+            "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,128,bf16,bf16,false> + "
+                      "chunk_state_kernel<128,128,16,bf16,bf16,false>",
             "alg_bytes_per_launch": alg_b}
     mfma = {"alg_flops_per_launch": alg_f, "achieved_tflops": alg_f / (ms * 1e-3) / 1e12,
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
@@ -213,7 +213,10 @@ def main():
             "ms_per_step": pms, "tokens_per_s": T / (pms * 1e-3), "vs_plain_ms": pms / ms,
             "roofline": {"bound": "hbm", "achieved": alg_b / (pms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": alg_b / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": None, "alg_bytes_per_launch": alg_b},
+                         "traffic": load_traffic("chunk_fwd_prologue_prefill_h32_t65536_traffic.json", digest),
+                         "kernel": "kda_chunk_fwd_prologue = chunk_prep_kernel<128,128,bf16,bf16,true> + "
+                                   "chunk_state_kernel<128,128,16,bf16,bf16,true>",
+                         "alg_bytes_per_launch": alg_b},
             "separate_pass_alg_bytes": sep_b,
             "separate_pass_floor_ms": sep_b / (HBM_PEAK_GBS * 1e9) * 1e3}
         del dr, args_p
