@@ -5,9 +5,10 @@ One "step" is one kda_chunk_fwd call over the long-context prefill workload
 (bf16, B=1, H=32, T=65536, d_k=d_v=128, chunk 64, per-channel decay in
 [0.5, 0.9999]); inputs are seeded, synthetic and resident in HBM before timing.
 The decode step (B=256 resident fp32 states, H=32, d=128, 1000 steps with fresh
-inputs) is timed in the same run and reported under "decode", and the same
-prefill on raw projections through the fused input prologue
-(kda_chunk_fwd_prologue) under "prologue".
+inputs) is timed in the same run and reported under "decode"; the same prefill
+on raw projections through the fused input prologue (kda_chunk_fwd_prologue)
+under "prologue"; and the same shape with one decay per token and head (Gated
+DeltaNet) and with none (DeltaNet), through kda_gdn_chunk_fwd, under "gdn".
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -31,10 +32,12 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix peak, published
 METRIC = "KDA chunk_fwd tokens/s + % MFMA peak; decode step HBM GB/s (1×MI355X)"
 
 
-def chunk_alg_bytes(tok_heads, n_states, dk, dv, io_b=2, gate_b=2):
-    """Algorithmic HBM bytes of one chunk_fwd launch: q, k, log_alpha (d_k each),
-    v and o (d_v each), beta (1) per token-head, plus h_T (and h0) per state."""
-    per = 2 * dk * io_b + dk * gate_b + 2 * dv * io_b + gate_b
+def chunk_alg_bytes(tok_heads, n_states, dk, dv, io_b=2, gate_b=2, gate_per_th=None):
+    """Algorithmic HBM bytes of one chunk_fwd launch: q, k, log_alpha (d_k each,
+    or gate_per_th values for the scalar-gate forms), v and o (d_v each), beta
+    (1) per token-head, plus h_T (and h0) per state."""
+    ng = dk if gate_per_th is None else gate_per_th
+    per = 2 * dk * io_b + ng * gate_b + 2 * dv * io_b + gate_b
     return tok_heads * per + n_states * dk * dv * 4
 
 
@@ -136,6 +139,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -179,8 +183,8 @@ def main():
     # one kda_chunk_fwd call = chunk_prep_kernel + chunk_state_kernel on one stream
     roof = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,128,bf16,bf16,false> + "
-                      "chunk_state_kernel<128,128,16,bf16,bf16,false>",
+            "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,128,bf16,bf16,false,0> + "
+                      "chunk_state_kernel<128,128,16,bf16,bf16,false,0>",
             "alg_bytes_per_launch": alg_b}
     mfma = {"alg_flops_per_launch": alg_f, "achieved_tflops": alg_f / (ms * 1e-3) / 1e12,
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
@@ -214,12 +218,32 @@ def main():
             "roofline": {"bound": "hbm", "achieved": alg_b / (pms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": alg_b / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": load_traffic("chunk_fwd_prologue_prefill_h32_t65536_traffic.json", digest),
-                         "kernel": "kda_chunk_fwd_prologue = chunk_prep_kernel<128,128,bf16,bf16,true> + "
-                                   "chunk_state_kernel<128,128,16,bf16,bf16,true>",
+                         "kernel": "kda_chunk_fwd_prologue = chunk_prep_kernel<128,128,bf16,bf16,true,0> + "
+                                   "chunk_state_kernel<128,128,16,bf16,bf16,true,0>",
                          "alg_bytes_per_launch": alg_b},
             "separate_pass_alg_bytes": sep_b,
             "separate_pass_floor_ms": sep_b / (HBM_PEAK_GBS * 1e9) * 1e3}
         del dr, args_p
+
+    # ---------------- scalar gates: Gated DeltaNet and DeltaNet on the same shape
+    if not args.no_gdn:
+        g = d["log_alpha"][:, :, 0].contiguous()   # c3's draw, one decay per (token, head)
+        gdn = {"workload": "kda_gdn_chunk_fwd bf16 B=1 H=32 T=65536 d_k=d_v=128 chunk=64, log_alpha "
+                           "[T, H] = the first channel of the same per-channel draw; and with "
+                           "log_alpha = NULL (DeltaNet)"}
+        for key, gate, ng in (("gated", g, 1), ("deltanet", None, 0)):
+            fng = lambda: kda.kda_gdn_chunk_fwd(d["q"], d["k"], d["v"], gate, d["beta"], o=o, h_T=hT)
+            per_g, _ = time_launches(fng, args.steps, args.warmup, stream)
+            gms = float(np.mean(per_g))
+            gb = chunk_alg_bytes(tok_heads, H, dk, dv, gate_per_th=ng)
+            gdn[key] = {"ms_per_step": gms, "tokens_per_s": T / (gms * 1e-3), "vs_plain_ms": gms / ms,
+                        "roofline": {"bound": "hbm", "achieved": gb / (gms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": gb / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                     "traffic": load_traffic("chunk_gdn_%s_prefill_h32_t65536_traffic.json" % key,
+                                                             digest),
+                                     "alg_bytes_per_launch": gb}}
+        out["gdn"] = gdn
+        del g
 
     # ---------------- decode step
     if not args.no_decode:

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
     kda_decode_step(q, k, v, log_alpha, beta, S, o=None)
     kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, ...)
     kda_decode_step_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, o=None)
+    kda_gdn_chunk_fwd(q, k, v, log_alpha_or_None, beta, ...)   (scalar gate [.., H], or none)
+    kda_gdn_decode_step(q, k, v, log_alpha_or_None, beta, S, o=None)
     kda_chunk_fwd_workspace_size(...), kda_status_string(code), kda_abi_version()
 """
 from __future__ import annotations
@@ -25,7 +27,8 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ER
 KDA_F32, KDA_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
                     "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step",
-                    "kda_chunk_fwd_prologue", "kda_decode_step_prologue")
+                    "kda_chunk_fwd_prologue", "kda_decode_step_prologue", "kda_gdn_chunk_fwd",
+                    "kda_gdn_decode_step")
 
 _lib = None
 
@@ -69,6 +72,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i32, i32, i32,
                                              i32, ctypes.c_int, ctypes.c_int, vp]
     lib.kda_decode_step_prologue.restype = ctypes.c_int
+    lib.kda_gdn_chunk_fwd.argtypes = list(lib.kda_chunk_fwd.argtypes)
+    lib.kda_gdn_chunk_fwd.restype = ctypes.c_int
+    lib.kda_gdn_decode_step.argtypes = list(lib.kda_decode_step.argtypes)
+    lib.kda_gdn_decode_step.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -127,6 +134,15 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
                       None)
 
 
+def kda_gdn_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None, h_T=None,
+                      output_final_state=True, workspace=None):
+    """Gated DeltaNet (log_alpha [B, T, H], one decay per token and head) or
+    DeltaNet (log_alpha None) through the chunkwise path; otherwise as
+    kda_chunk_fwd."""
+    return _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_state, workspace,
+                      None, gdn=True)
+
+
 def kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h0=None,
                            cu_seqlens=None, *, o=None, h_T=None, output_final_state=True,
                            workspace=None):
@@ -138,21 +154,25 @@ def kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h
 
 
 def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_state, workspace,
-               log_alpha_min):
+               log_alpha_min, gdn=False):
     import torch
     lib = load_library()
     squeeze = q.dim() == 3
     if squeeze:
-        q, k, v, log_alpha, beta = (x.unsqueeze(0) for x in (q, k, v, log_alpha, beta))
+        q, k, v, beta = (x.unsqueeze(0) for x in (q, k, v, beta))
+        if log_alpha is not None:
+            log_alpha = log_alpha.unsqueeze(0)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
-        _check_dev(name, t, dev)
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:3] != (B, T, H) \
-            or beta.shape != (B, T, H):
+        if t is not None or not gdn:
+            _check_dev(name, t, dev)
+    gshape = (B, T, H) if gdn else q.shape
+    if k.shape != q.shape or (log_alpha is not None and log_alpha.shape != gshape) \
+            or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
         raise ValueError("shape mismatch among q, k, v, log_alpha, beta")
-    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != log_alpha.dtype:
+    if k.dtype != q.dtype or v.dtype != q.dtype or (log_alpha is not None and beta.dtype != log_alpha.dtype):
         raise TypeError("q, k, v share one dtype; log_alpha and beta share one dtype")
     if cu_seqlens is not None:
         _check_dev("cu_seqlens", cu_seqlens, dev)
@@ -169,13 +189,18 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
     if h_T is None and output_final_state:
         h_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    io, gt = _dtype_code(q), _dtype_code(log_alpha)
+    io, gt = _dtype_code(q), _dtype_code(beta)
     ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, N if cu_seqlens is not None else 0, io)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     nseq = N if cu_seqlens is not None else 0
-    if log_alpha_min is None:
+    if gdn:
+        name = "kda_gdn_chunk_fwd"
+        rc = lib.kda_gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                   _ptr(cu_seqlens), nseq, _ptr(o), _ptr(h_T), B, T, H, dk, dv, io, gt,
+                                   _ptr(workspace), ws_len, _stream_of(q))
+    elif log_alpha_min is None:
         name = "kda_chunk_fwd"
         rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
                                _ptr(cu_seqlens), nseq, _ptr(o), _ptr(h_T), B, T, H, dk, dv, io, gt,
@@ -199,12 +224,17 @@ def kda_decode_step(q, k, v, log_alpha, beta, S, o=None):
     return _decode_step(q, k, v, log_alpha, beta, S, o, None)
 
 
+def kda_gdn_decode_step(q, k, v, log_alpha, beta, S, o=None):
+    """Decode step with a scalar gate: log_alpha [B, H] or None (no decay)."""
+    return _decode_step(q, k, v, log_alpha, beta, S, o, None, gdn=True)
+
+
 def kda_decode_step_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, o=None):
     """kda_decode_step on raw projections (the maps of kda_chunk_fwd_prologue)."""
     return _decode_step(q_raw, k_raw, v, gate_pre, beta_pre, S, o, float(log_alpha_min))
 
 
-def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min):
+def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min, gdn=False):
     import torch
     lib = load_library()
     B, H, dk = q.shape
@@ -212,12 +242,20 @@ def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min):
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
                     ("S", S)):
-        _check_dev(name, t, dev)
+        if t is not None or not gdn:
+            _check_dev(name, t, dev)
+    if log_alpha is not None and tuple(log_alpha.shape) != ((B, H) if gdn else (B, H, dk)):
+        raise ValueError("log_alpha has the wrong shape")
     if S.dtype != torch.float32 or tuple(S.shape) != (B, H, dk, dv):
         raise ValueError("S must be fp32 [B, H, d_k, d_v]")
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
-    if log_alpha_min is None:
+    if gdn:
+        name = "kda_gdn_decode_step"
+        rc = lib.kda_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                     _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(beta),
+                                     _stream_of(q))
+    elif log_alpha_min is None:
         name = "kda_decode_step"
         rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
                                  _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(log_alpha),
@@ -236,3 +274,5 @@ chunk_fwd = kda_chunk_fwd
 decode_step = kda_decode_step
 chunk_fwd_prologue = kda_chunk_fwd_prologue
 decode_step_prologue = kda_decode_step_prologue
+gdn_chunk_fwd = kda_gdn_chunk_fwd
+gdn_decode_step = kda_gdn_decode_step

@@ -35,11 +35,11 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
                             const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                             kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
-                            size_t workspace_bytes, void *stream, bool prologue, float lo);
+                            size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode);
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
                               const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
                               int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
-                              bool prologue, float lo);
+                              bool prologue, float lo, int gate_mode);
 
 }  // namespace
 
@@ -82,7 +82,7 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
-                          io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f);
+                          io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f, 0);
 }
 
 kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v,
@@ -93,7 +93,7 @@ kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const 
                                     void *workspace, size_t workspace_bytes, void *stream) {
     if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
     return chunk_fwd_impl(q_raw, k_raw, v, gate_pre, beta_pre, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k,
-                          d_v, io_dtype, gate_dtype, workspace, workspace_bytes, stream, true, log_alpha_min);
+                          d_v, io_dtype, gate_dtype, workspace, workspace_bytes, stream, true, log_alpha_min, 0);
 }
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
@@ -101,7 +101,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
                              int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
                              kda_dtype_t gate_dtype, void *stream) {
     return decode_step_impl(q, k, v, log_alpha, beta, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
-                            0.f);
+                            0.f, 0);
 }
 
 kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v,
@@ -110,7 +110,24 @@ kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, cons
                                       kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream) {
     if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
     return decode_step_impl(q_raw, k_raw, v, gate_pre, beta_pre, S, o, B, H, d_k, d_v, io_dtype, gate_dtype,
-                            stream, true, log_alpha_min);
+                            stream, true, log_alpha_min, 0);
+}
+
+kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                               const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                               void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                               kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
+                          io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f,
+                          log_alpha ? 1 : 2);
+}
+
+kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
+                                 const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
+                                 int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream) {
+    return decode_step_impl(q, k, v, log_alpha, beta, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
+                            0.f, log_alpha ? 1 : 2);
 }
 
 }  // extern "C"
@@ -121,7 +138,7 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
                             const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                             kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
-                            size_t workspace_bytes, void *stream, bool prologue, float lo) {
+                            size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -138,11 +155,11 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
     if (!sizes_fit(N, H, (int64_t)d_k * d_v)) return KDA_ERR_INVALID_ARGUMENT;
     const bool have_tokens = (int64_t)B * T > 0;
     if (have_tokens) {
-        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
-            !aligned16(o))
-            return KDA_ERR_INVALID_ARGUMENT;
+        if (!q || !k || !v || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KDA_ERR_INVALID_ARGUMENT;
         if (!aligned_to(beta, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
+        if (gate_mode == 0 && (!log_alpha || !aligned16(log_alpha))) return KDA_ERR_INVALID_ARGUMENT;
+        if (gate_mode == 1 && !aligned_to(log_alpha, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
     }
     if ((h0 && !aligned16(h0)) || (h_T && !aligned16(h_T))) return KDA_ERR_INVALID_ARGUMENT;
     kda::ChunkArgs a = {};
@@ -158,7 +175,7 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    a.prologue = prologue; a.log_alpha_min = lo;
+    a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;
     g_hip_error[0] = '\0';
     if (kda::launch_chunk_fwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
         return KDA_ERR_HIP;
@@ -168,21 +185,22 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
                               const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
                               int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
-                              bool prologue, float lo) {
+                              bool prologue, float lo, int gate_mode) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
     if (!sizes_fit(B, H, (int64_t)d_k * d_v)) return KDA_ERR_INVALID_ARGUMENT;
-    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
-        !aligned16(S) || !aligned16(o))
+    if (!q || !k || !v || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(o))
         return KDA_ERR_INVALID_ARGUMENT;
     if (!aligned_to(beta, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
+    if (gate_mode == 0 && (!log_alpha || !aligned16(log_alpha))) return KDA_ERR_INVALID_ARGUMENT;
+    if (gate_mode == 1 && !aligned_to(log_alpha, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S; a.o = o;
     a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
-    a.prologue = prologue; a.log_alpha_min = lo;
+    a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;
     g_hip_error[0] = '\0';
     if (kda::launch_decode_step(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
         return KDA_ERR_HIP;

@@ -89,7 +89,7 @@ struct alignas(16) ExactSmem {
 
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
 // (input prologue; lo is the floor of log alpha).
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO>
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 
     if constexpr (EXACT) {
         for (int64_t tk = bos; tk < eos; ++tk)
-            token_update<DK, BV, IO, GT, PRO>(Sacc, smem.red, q, k, v, log_alpha, beta, o, tk, H, h, DV, col0, w,
-                                              lg, lr, lo);
+            token_update<DK, BV, IO, GT, PRO, GM>(Sacc, smem.red, q, k, v, log_alpha, beta, o, tk, H, h, DV, col0,
+                                                  w, lg, lr, lo);
     } else {
         Sm &sm = smem;
         // Upper blocks of T and P are never written: zero them once.
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             (&sm.T[0][0][0])[idx] = (bf16_t)0.f;
             (&sm.P[0][0][0])[idx] = (bf16_t)0.f;
         }
-        ChunkRegs<DK, BV, IO, GT, PRO> in;
+        ChunkRegs<DK, BV, IO, GT, PRO, GM> in;
         if (bos < eos) {
             const int nv0 = (int)((eos - bos) < kC ? (eos - bos) : kC);
             in.load(q, k, v, log_alpha, beta, bos, nv0, H, h, DV, col0, w, l, lg, lr);
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             for (int cc = 0; cc < CPL; ++cc) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    float x = in.gate(i, cc, lo) * kLog2e;
+                    float x = in.gate(i, cc) * kLog2e;
                     if (partial && 8 * w + i >= nv) x = 0.f;
                     csum[i][cc] = i ? csum[i - 1][cc] + x : x;
                 }
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                     float al[8];
 #pragma unroll
                     for (int i = 1; i < 8; ++i) {
-                        float x = in.gate(i, cc, lo) * kLog2e;
+                        float x = in.gate(i, cc) * kLog2e;
                         if (partial && 8 * w + i >= nv) x = 0.f;
                         al[i] = kexp2<SPLIT>(x);
                     }
@@ -296,8 +296,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             if (slow) {
                 // exact token-by-token path for a chunk with a huge in-chunk decay
                 for (int r = 0; r < nv; ++r)
-                    token_update<DK, BV, IO, GT, PRO>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h,
-                                                      DV, col0, w, lg, lr, lo);
+                    token_update<DK, BV, IO, GT, PRO, GM>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H,
+                                                          h, DV, col0, w, lg, lr, lo);
                 continue;
             }
 
@@ -591,11 +591,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     }
 }
 
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO>
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t st) {
     const int64_t chains = a.num_seqs * (int64_t)a.H;
     const int64_t nwg = chains * (a.d_v / BV);
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, EXACT, PRO>), dim3((unsigned)nwg), dim3(kThreads),
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, EXACT, PRO, GM>), dim3((unsigned)nwg), dim3(kThreads),
                        0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
                        (const GT *)a.beta, a.h0, a.cu_seqlens, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains,
                        a.log_alpha_min);
@@ -604,19 +604,24 @@ hipError_t launch_t(const ChunkArgs &a, hipStream_t st) {
 
 // bf16 I/O: single-bf16 decayed operands.  fp32 I/O: split operands (d_k = 64)
 // or the exact token path (d_k = 128).
-template <int DK, int BV, bool PRO>
+template <int DK, int BV, bool PRO, int GM>
 hipError_t launch_types(const ChunkArgs &a, hipStream_t st) {
     if (a.io_bf16)
-        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, false, PRO>(a, st)
-                           : launch_t<DK, BV, bf16_t, float, false, false, PRO>(a, st);
+        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, false, PRO, GM>(a, st)
+                           : launch_t<DK, BV, bf16_t, float, false, false, PRO, GM>(a, st);
     constexpr bool EX = DK == 128;
-    return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, !EX, EX, PRO>(a, st)
-                       : launch_t<DK, BV, float, float, !EX, EX, PRO>(a, st);
+    return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, !EX, EX, PRO, GM>(a, st)
+                       : launch_t<DK, BV, float, float, !EX, EX, PRO, GM>(a, st);
 }
 
+// The input variants that exist: per-channel gates with or without the prologue,
+// and the scalar-gate forms without it.
 template <int DK, int BV>
 hipError_t launch_types_pro(const ChunkArgs &a, hipStream_t st) {
-    return a.prologue ? launch_types<DK, BV, true>(a, st) : launch_types<DK, BV, false>(a, st);
+    if (a.gate_mode == kGatePerHead) return launch_types<DK, BV, false, kGatePerHead>(a, st);
+    if (a.gate_mode == kGateNone) return launch_types<DK, BV, false, kGateNone>(a, st);
+    return a.prologue ? launch_types<DK, BV, true, kGatePerChannel>(a, st)
+                      : launch_types<DK, BV, false, kGatePerChannel>(a, st);
 }
 
 // Value-column block width: 32 when that still gives at least two workgroups

@@ -164,7 +164,7 @@ struct alignas(16) PrepSmem {
 // Prep: one workgroup (8 waves) per (chunk, head).
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
 // (input prologue; lo is the floor of log alpha).
-template <int DK, int DV, typename IO, typename GT, bool PRO>
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const int32_t *__restrict__ cu,
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
 
     // ---- load this chunk (rows past the end read the last row; their gates,
     // keys and beta are zeroed below, so they contribute nothing)
-    ChunkRegs<DK, 16, IO, GT, PRO> in;
+    ChunkRegs<DK, 16, IO, GT, PRO, GM> in;
     in.load(q, k, q, log_alpha, beta, t0, nv, H, h, 0, 0, w, l, lg, lr, false);
     in.prepare(w, lo);
     typedef typename VecT<IO, CPV>::type VV;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
     for (int cc = 0; cc < CPL; ++cc) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float x = in.gate(i, cc, lo) * kLog2e;
+            float x = in.gate(i, cc) * kLog2e;
             if (partial && 8 * w + i >= nv) x = 0.f;
             csum[i][cc] = i ? csum[i - 1][cc] + x : x;
         }
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
             al[0] = 1.f;
 #pragma unroll
             for (int i = 1; i < 8; ++i) {
-                float x = in.gate(i, cc, lo) * kLog2e;
+                float x = in.gate(i, cc) * kLog2e;
                 if (partial && 8 * w + i >= nv) x = 0.f;
                 al[i] = kexp2<false>(x);
             }
@@ -727,7 +727,7 @@ struct ChainRange {
 
 __device__ __forceinline__ int chunk_count(const ChainRange &cr) { return (int)((cr.eos - cr.bos + kC - 1) / kC); }
 
-template <int DK, int DV, int BV, typename IO, typename GT, bool PRO>
+template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM>
 __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const ChainRange &cr,
                                                 const IO *__restrict__ q, const IO *__restrict__ k,
                                                 const IO *__restrict__ v, const GT *__restrict__ log_alpha,
@@ -763,8 +763,8 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
         const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
         if (slow) {
             for (int r = 0; r < nv; ++r)
-                token_update<DK, BV, IO, GT, PRO>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h, DV,
-                                                  col0, w, lg, lr, lo);
+                token_update<DK, BV, IO, GT, PRO, GM>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h,
+                                                      DV, col0, w, lg, lr, lo);
         } else {
             // S' = Diag(e^m) S, transposed, to LDS
 #pragma unroll
@@ -990,7 +990,7 @@ __device__ __forceinline__ void loader_role_loop(StateSmem<DK, DV, BV> &sm, cons
     }
 }
 
-template <int DK, int DV, int BV, typename IO, typename GT, bool PRO>
+template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
@@ -1016,14 +1016,14 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
         cr.c0 = cr.n * ((seq_len + kC - 1) / kC);
     }
     if (w < 4)
-        state_role_loop<DK, DV, BV, IO, GT, PRO>(sm, cr, q, k, v, log_alpha, beta, h0, o, h_T, H, w, tid, lo);
+        state_role_loop<DK, DV, BV, IO, GT, PRO, GM>(sm, cr, q, k, v, log_alpha, beta, h0, o, h_T, H, w, tid, lo);
     else if (w < 8)
         output_role_loop<DK, DV, BV, IO>(sm, cr, o, H, w - 4, tid);
     else
         loader_role_loop<DK, DV, BV>(sm, cr, recs, H, tid - 512);
 }
 
-template <int DK, int DV, typename IO, typename GT, bool PRO>
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
 hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
     uint8_t *ws = reinterpret_cast<uint8_t *>(a.workspace);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + kHeaderBytes);
@@ -1032,7 +1032,7 @@ hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
     const int64_t nprep = max_chunks(a) * a.H;
     if (nprep > 0)
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, DV, IO, GT, PRO>), dim3((unsigned)nprep), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, DV, IO, GT, PRO, GM>), dim3((unsigned)nprep), dim3(kThreads), 0, st,
                            (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
                            (const GT *)a.beta, a.cu_seqlens, (const int32_t *)chunk_off, recs, a.num_seqs, a.seq_len,
                            a.H, a.log_alpha_min);
@@ -1041,7 +1041,7 @@ hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
     // buffers and the 32-column state tiles do not fit the 16-wave register budget
     if constexpr (DK == 64) {
         if (bv == 32) {
-            hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 32, IO, GT, PRO>), dim3((unsigned)(chains * (DV / 32))),
+            hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 32, IO, GT, PRO, GM>), dim3((unsigned)(chains * (DV / 32))),
                                dim3(kStateThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
                                (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
                                (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains,
@@ -1049,7 +1049,7 @@ hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT, PRO>), dim3((unsigned)(chains * (DV / 16))),
+    hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT, PRO, GM>), dim3((unsigned)(chains * (DV / 16))),
                            dim3(kStateThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
                            (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
                            (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains,
@@ -1057,13 +1057,23 @@ hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename GT, bool PRO>
+template <typename GT, bool PRO, int GM>
 hipError_t launch_two_kernel_dims(const ChunkArgs &a, int bv, hipStream_t st) {
     if (a.d_k == 128)
-        return a.d_v == 128 ? launch_two_kernel<128, 128, bf16_t, GT, PRO>(a, bv, st)
-                            : launch_two_kernel<128, 64, bf16_t, GT, PRO>(a, bv, st);
-    return a.d_v == 128 ? launch_two_kernel<64, 128, bf16_t, GT, PRO>(a, bv, st)
-                        : launch_two_kernel<64, 64, bf16_t, GT, PRO>(a, bv, st);
+        return a.d_v == 128 ? launch_two_kernel<128, 128, bf16_t, GT, PRO, GM>(a, bv, st)
+                            : launch_two_kernel<128, 64, bf16_t, GT, PRO, GM>(a, bv, st);
+    return a.d_v == 128 ? launch_two_kernel<64, 128, bf16_t, GT, PRO, GM>(a, bv, st)
+                        : launch_two_kernel<64, 64, bf16_t, GT, PRO, GM>(a, bv, st);
+}
+
+// The input variants that exist: per-channel gates with or without the prologue,
+// and the scalar-gate forms without it.
+template <typename GT>
+hipError_t launch_two_kernel_variant(const ChunkArgs &a, int bv, hipStream_t st) {
+    if (a.gate_mode == kGatePerHead) return launch_two_kernel_dims<GT, false, kGatePerHead>(a, bv, st);
+    if (a.gate_mode == kGateNone) return launch_two_kernel_dims<GT, false, kGateNone>(a, bv, st);
+    if (a.prologue) return launch_two_kernel_dims<GT, true, kGatePerChannel>(a, bv, st);
+    return launch_two_kernel_dims<GT, false, kGatePerChannel>(a, bv, st);
 }
 
 size_t record_bytes(int d_k, int d_v) {
@@ -1079,11 +1089,7 @@ size_t two_kernel_workspace_bytes(const ChunkArgs &a) {
 }
 
 hipError_t launch_chunk_fwd_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
-    if (a.prologue)
-        return a.gate_bf16 ? launch_two_kernel_dims<bf16_t, true>(a, bv, st)
-                           : launch_two_kernel_dims<float, true>(a, bv, st);
-    return a.gate_bf16 ? launch_two_kernel_dims<bf16_t, false>(a, bv, st)
-                       : launch_two_kernel_dims<float, false>(a, bv, st);
+    return a.gate_bf16 ? launch_two_kernel_variant<bf16_t>(a, bv, st) : launch_two_kernel_variant<float>(a, bv, st);
 }
 
 }  // namespace kda

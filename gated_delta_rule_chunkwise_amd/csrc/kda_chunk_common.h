@@ -152,13 +152,13 @@ template <int BV> struct TokenRed { static constexpr int N = 2 * BV + 3; };
 // With PRO (raw projections in), the gate and beta are mapped as they are read
 // and the raw q and k enter through their squared norms: a = k^T S and b = q^T S
 // are taken with the raw vectors and rescaled once the norms are reduced.
-template <int DK, int BV, typename IO, typename GT, bool PRO = false>
+template <int DK, int BV, typename IO, typename GT, bool PRO, int GM>
 __device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 16) / 4],
                                              float (*red)[TokenRed<BV>::N], const IO *__restrict__ q,
                                              const IO *__restrict__ k, const IO *__restrict__ v,
                                              const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
                                              IO *__restrict__ o, int64_t tk, int H, int h, int DV, int col0, int w,
-                                             int lg, int lr, float lo = 0.f) {
+                                             int lg, int lr, float lo) {
     constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
     float kc[STW][4];
     if (w < 4) {
@@ -173,8 +173,9 @@ __device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 1
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * mt + 4 * lg + e;
                 const float kv = to_f32(k[kb + c]), qv = to_f32(q[kb + c]);
-                const float la = to_f32(log_alpha[kb + c]);
-                const float av = expf(PRO ? pro_log_alpha(la, lo) : la);
+                const float la = GM == kGatePerChannel ? to_f32(log_alpha[kb + c])
+                                                       : gate_at<GM>(log_alpha, tk * H + h, DK, c);
+                const float av = expf(log_decay<PRO, GM>(la, lo));
                 kc[i][e] = kv;
                 Sacc[i][e] *= av;
                 pa[nt] += kv * Sacc[i][e];
@@ -265,12 +266,22 @@ template <> __device__ __forceinline__ float vget<bf16_t>(const bf16_t &x, int) 
 template <> __device__ __forceinline__ float vget<float>(const float &x, int) { return x; }
 template <> __device__ __forceinline__ float vget<bf16x2_t>(const bf16x2_t &x, int i) { return (float)x[i]; }
 template <> __device__ __forceinline__ float vget<float2>(const float2 &x, int i) { return i ? x.y : x.x; }
+template <typename V, typename S> __device__ __forceinline__ V vsplat(S x);
+template <> __device__ __forceinline__ bf16_t vsplat<bf16_t, bf16_t>(bf16_t x) { return x; }
+template <> __device__ __forceinline__ float vsplat<float, float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16x2_t vsplat<bf16x2_t, bf16_t>(bf16_t x) {
+    bf16x2_t r;
+    r[0] = x;
+    r[1] = x;
+    return r;
+}
+template <> __device__ __forceinline__ float2 vsplat<float2, float>(float x) { return make_float2(x, x); }
 
 // With PRO (raw projections in) the accessors return the mapped inputs: gate()
 // the floored -softplus (mapped once, at load), kval()/qval() the raw value
 // times the per-token inverse norm (reduced over the wave, which holds whole
 // rows), and bt is sigmoid(b).
-template <int DK, int BV, typename IO, typename GT, bool PRO = false>
+template <int DK, int BV, typename IO, typename GT, bool PRO, int GM>
 struct ChunkRegs {
     static constexpr int CPL = DK / 64, NT = BV / 16;
     typedef typename VecT<GT, CPL>::type GV;
@@ -282,7 +293,7 @@ struct ChunkRegs {
     float qs[PRO ? 8 : 1], ks[PRO ? 8 : 1];
     float lf[PRO ? 8 : 1][CPL];
 
-    __device__ __forceinline__ float gate(int i, int cc, float) const {
+    __device__ __forceinline__ float gate(int i, int cc) const {
         if constexpr (PRO) return lf[i][cc];
         else return vget(la[i], cc);
     }
@@ -304,7 +315,12 @@ struct ChunkRegs {
             const int r = 8 * w + i;
             const int rr = r < nv ? r : nv - 1;
             const int64_t base = ((tbase + rr) * H + h) * (int64_t)DK + l * CPL;
-            la[i] = *reinterpret_cast<const GV *>(log_alpha + base);
+            if constexpr (GM == kGatePerChannel) {
+                la[i] = *reinterpret_cast<const GV *>(log_alpha + base);
+            } else {   // one gate per (token, head), or none: the same value on every channel
+                const GT g = GM == kGatePerHead ? log_alpha[(tbase + rr) * H + h] : (GT)0.f;
+                la[i] = vsplat<GV>(g);
+            }
             kk[i] = *reinterpret_cast<const IV *>(k + base);
             qq[i] = *reinterpret_cast<const IV *>(q + base);
         }
@@ -338,7 +354,7 @@ struct ChunkRegs {
                 qs[i] = pro_inv_norm(wave_sum(sq));
                 ks[i] = pro_inv_norm(wave_sum(sk));
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) lf[i][cc] = pro_log_alpha(vget(la[i], cc), lo);
+                for (int cc = 0; cc < CPL; ++cc) lf[i][cc] = log_decay<PRO, GM>(vget(la[i], cc), lo);
             }
             if (w == 0) bt = pro_beta(bt);
         }

@@ -22,7 +22,7 @@ constexpr int kDecodeThreads = 256;
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
 // (input prologue; lo is the floor of log alpha).  The reductions then run on
 // the raw q and k and are rescaled by the inverse norms, reduced alongside.
-template <int DK, int DV, typename IO, typename GT, bool PRO>
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, float *__restrict__ S,
@@ -50,8 +50,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     for (int i = 0; i < RPT; ++i) {
         kk[i] = to_f32(k[bh * DK + row0 + i]);
         qq[i] = to_f32(q[bh * DK + row0 + i]);
-        const float la = to_f32(log_alpha[bh * DK + row0 + i]);
-        al[i] = __expf(PRO ? pro_log_alpha(la, lo) : la);
+        al[i] = __expf(log_decay<PRO, GM>(gate_at<GM>(log_alpha, bh, DK, row0 + i), lo));
     }
 
     float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f}, pqk = 0.f, pqq = 0.f, pkk = 0.f;
@@ -130,18 +129,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     }
 }
 
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
+hipError_t launch_v(const DecodeArgs &a, hipStream_t st) {
+    const int64_t nb = a.B * (int64_t)a.H;
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT, PRO, GM>), dim3((unsigned)nb), dim3(kDecodeThreads), 0,
+                       st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
+                       (const GT *)a.beta, a.S, (IO *)a.o, a.log_alpha_min);
+    return hipGetLastError();
+}
+
+// The input variants that exist: per-channel gates with or without the prologue,
+// and the scalar-gate forms without it.
 template <int DK, int DV, typename IO, typename GT>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
-    const int64_t nb = a.B * (int64_t)a.H;
-    if (a.prologue)
-        hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT, true>), dim3((unsigned)nb), dim3(kDecodeThreads),
-                           0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
-                           (const GT *)a.log_alpha, (const GT *)a.beta, a.S, (IO *)a.o, a.log_alpha_min);
-    else
-        hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT, false>), dim3((unsigned)nb), dim3(kDecodeThreads),
-                           0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
-                           (const GT *)a.log_alpha, (const GT *)a.beta, a.S, (IO *)a.o, 0.f);
-    return hipGetLastError();
+    if (a.gate_mode == kGatePerHead) return launch_v<DK, DV, IO, GT, false, kGatePerHead>(a, st);
+    if (a.gate_mode == kGateNone) return launch_v<DK, DV, IO, GT, false, kGateNone>(a, st);
+    return a.prologue ? launch_v<DK, DV, IO, GT, true, kGatePerChannel>(a, st)
+                      : launch_v<DK, DV, IO, GT, false, kGatePerChannel>(a, st);
 }
 
 template <int DK, int DV>

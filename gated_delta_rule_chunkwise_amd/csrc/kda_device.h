@@ -78,6 +78,25 @@ __device__ __forceinline__ float pro_inv_norm(float sumsq) {
     return __builtin_amdgcn_rsqf(fmaxf(sumsq, kPrologueEps * kPrologueEps));
 }
 
+// Gate layouts (a compile-time parameter GM of the kernels): one log decay per
+// key channel (KDA), one per (token, head) broadcast over the channels (Gated
+// DeltaNet), or none, i.e. log alpha = 0 (DeltaNet).
+enum GateMode : int { kGatePerChannel = 0, kGatePerHead = 1, kGateNone = 2 };
+
+// Gate of (token-head th, key channel c) in layout GM.
+template <int GM, typename GT>
+__device__ __forceinline__ float gate_at(const GT *__restrict__ g, int64_t th, int DK, int c) {
+    if constexpr (GM == kGatePerChannel) return to_f32(g[th * DK + c]);
+    else if constexpr (GM == kGatePerHead) return to_f32(g[th]);
+    else return 0.f;
+}
+// log alpha as the recurrence uses it: the gate value itself, or with the
+// prologue its floored -softplus (no gate stays log alpha = 0).
+template <bool PRO, int GM> __device__ __forceinline__ float log_decay(float x, float lo) {
+    if constexpr (PRO && GM != kGateNone) return pro_log_alpha(x, lo);
+    else return x;
+}
+
 // Sum of x over the 64 lanes of a wave, returned wave-uniform: data-parallel
 // moves within rows of 16 lanes (quad swaps, then half-row and row mirrors, each
 // pairing a lane with one in the other half), then the four row sums.

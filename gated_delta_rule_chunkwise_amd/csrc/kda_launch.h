@@ -20,6 +20,7 @@ struct ChunkArgs {
     int32_t varlen;             // cu_seqlens given (sequences packed along T)
     int32_t prologue;           // q, k, log_alpha, beta are raw projections
     float log_alpha_min;        // floor of log alpha under the prologue
+    int32_t gate_mode;          // 0: log_alpha [.., d_k]; 1: [..] per (token, head); 2: none
     void *workspace;
     size_t workspace_bytes;
 };
@@ -33,6 +34,7 @@ struct DecodeArgs {
     int32_t io_bf16, gate_bf16;
     int32_t prologue;           // q, k, log_alpha, beta are raw projections
     float log_alpha_min;        // floor of log alpha under the prologue
+    int32_t gate_mode;          // 0: log_alpha [B, H, d_k]; 1: [B, H]; 2: none
 };
 
 // Both return 0 when the launch was enqueued, or -1 after a HIP error whose

@@ -181,6 +181,33 @@ kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, cons
                                       float *S, void *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                                       kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream);
 
+/*
+ * kda_gdn_chunk_fwd -- the scalar-gate members of the family through the same
+ * path: Gated DeltaNet, one decay per token and head (KimiLinear article,
+ * section 2.2), and DeltaNet, no decay (section 2.1), when log_alpha is NULL.
+ * Computes exactly kda_chunk_fwd with every key channel's log_alpha[t, h, c]
+ * equal to log_alpha[t, h] (or to 0); the gate is read once per token and head
+ * instead of once per channel.  Arguments, workspace and errors as for
+ * kda_chunk_fwd except:
+ *
+ *   log_alpha   [B, T, H] gate_dtype, aligned to its element size; finite and
+ *               <= 0; or NULL for no decay
+ */
+kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                               const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                               void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                               kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * kda_gdn_decode_step -- kda_decode_step with a scalar gate: log_alpha is
+ * [B, H] (aligned to its element size) or NULL for no decay; every key channel
+ * of a state decays by the same factor.  Otherwise as kda_decode_step.
+ */
+kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
+                                 const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
+                                 int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

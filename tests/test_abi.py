@@ -166,3 +166,49 @@ def test_decode_prologue_validates_like_decode(kda, kw, code):
     lib = kda.load_library()
     assert decode_pro(lib, **kw) == code
     assert decode(lib, **kw) == code
+
+
+def chunk_gdn(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+             dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kda_gdn_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"], a["N"],
+                                 a["o"], a["hT"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"],
+                                 a["gt"], a["ws"], a["wsb"], None)
+
+
+def decode_gdn(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, S=P, o=P, B=4, H=2, dk=128, dv=128, io=1, gt=1)
+    a.update(kw)
+    return lib.kda_gdn_decode_step(a["q"], a["k"], a["v"], a["la"], a["beta"], a["S"], a["o"], a["B"],
+                                   a["H"], a["dk"], a["dv"], a["io"], a["gt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), 2), (dict(B=0), 1), (dict(q=None), 1), (dict(beta=None), 1),
+    (dict(la=P + 1), 1), (dict(la=P + 2, gt=0), 1), (dict(cu=P, N=2, B=2), 1), (dict(ws=None, wsb=0), 3),
+])
+def test_gdn_chunk_fwd_validates(kda, kw, code):
+    lib = kda.load_library()
+    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    a = dict(ws=P, wsb=need)
+    a.update(kw)
+    assert chunk_gdn(lib, **a) == code
+
+
+def test_gdn_gate_alignment_is_element_size(kda):
+    # a scalar gate is [B, T, H]: aligned to its element, not to 16 bytes; the
+    # per-channel entry point still needs 16 bytes
+    lib = kda.load_library()
+    assert decode_gdn(lib, la=P + 2, S=None) == 1      # rejected for the missing state only
+    assert decode_gdn(lib, la=P + 1, gt=1) == 1
+    assert decode_gdn(lib, la=P + 2, gt=0) == 1
+    assert decode(lib, la=P + 2, S=None) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=32), 2), (dict(B=0), 1), (dict(S=None), 1), (dict(k=P + 2), 1), (dict(beta=P + 1), 1),
+])
+def test_gdn_decode_validates(kda, kw, code):
+    lib = kda.load_library()
+    assert decode_gdn(lib, **kw) == code

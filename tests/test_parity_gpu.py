@@ -354,3 +354,79 @@ def test_prologue_decode_dims_fp32(kda, dk, dv):
         ro, Sref = oracle.decode_prologue(*(f64(x[n]) for n in names), -2.5, Sref)
         assert_close(o.cpu(), ro, "f32", "prologue decode o")
     assert_close(Sg.cpu(), Sref, "f32", "prologue decode S")
+
+
+# ------------------------------------------------------------------ scalar gates
+# kda_gdn_chunk_fwd / kda_gdn_decode_step: one log decay per (token, head)
+# (Gated DeltaNet) or none (DeltaNet), against the oracle with that value on
+# every key channel (the oracle's channel-constant case is pinned to a scalar
+# Gated DeltaNet recurrence).
+def _gdn_check(kda, d, g, io, what, seqs=None, heads=None):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    o, hT = kda.kda_gdn_chunk_fwd(dev["q"], dev["k"], dev["v"], None if g is None else g.to(DEV), dev["beta"],
+                                  h0=dev["h0"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    o, hT = o.cpu(), hT.cpu()
+    T, H, dk = d["q"].shape
+    la_full = torch.zeros((T, H, dk), dtype=torch.float64) if g is None else \
+        g.to(torch.float64)[:, :, None].expand(T, H, dk).contiguous()
+    dd = dict(d)
+    dd["log_alpha"] = la_full
+    ref = to_oracle(dd, seqs, heads)
+    ro, rh = oracle.fwd(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], h0=ref["h0"],
+                        cu_seqlens=ref["cu_seqlens"])
+    hs = slice(None) if heads is None else list(heads)
+    rows = torch.from_numpy(ref["rows"])
+    go = o.reshape(-1, *o.shape[-2:])[rows][:, hs]
+    sq = list(range(len(d["lengths"]))) if seqs is None else list(seqs)
+    eo = assert_close(go, ro, io, what + " o")
+    eh = assert_close(hT[sq][:, hs], rh, io, what + " h_T")
+    log(what, "o", eo, "h_T", eh)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+@pytest.mark.parametrize("io,dk,dv", [("bf16", 128, 128), ("bf16", 64, 128), ("f32", 128, 64), ("f32", 64, 64)])
+def test_gdn_ragged_varlen(kda, gate, io, dk, dv):
+    """Ragged packed sequences with h0; the scalar gate includes near-resets and
+    a chunk whose decay exceeds the matrix-core range (token path)."""
+    cfg = I.ChunkConfig("gdn", io, io, H=3, dk=dk, dv=dv, h0=True, seed=41)
+    d = I.make_chunk_inputs(cfg, lengths=[300, 64, 130, 1, 200])
+    g = None
+    if gate == "none":
+        # With no decay the state keeps growing (|o| reaches ~2.7 here), and a
+        # bf16 output in [2, 4) alone rounds by up to 7.8e-3, above the 5e-3
+        # max-abs bound.  o is linear in (v, h0): scale both so |o| stays below 1.
+        d["v"] = (d["v"].float() * 0.35).to(d["v"].dtype)
+        d["h0"] = d["h0"] * 0.35
+    if gate == "scalar":
+        g = d["log_alpha"][:, :, 0].float().clone()
+        g[10] = -30.0
+        g[300:364, 1] = -2.0          # sequence 1, head 1: -128 over one chunk
+        g = g.to(d["log_alpha"].dtype).contiguous()
+    _gdn_check(kda, d, g, io, "gdn %s %s dk=%d dv=%d" % (gate, io, dk, dv))
+
+
+def test_gdn_c3_sampled_heads(kda):
+    """c3's full size with one decay per token and head (c3's per-channel draw,
+    first channel); the oracle checks 2 whole heads."""
+    d = I.make_chunk_inputs(I.C3)
+    g = d["log_alpha"][:, :, 0].contiguous()
+    _gdn_check(kda, d, g, "bf16", "gdn c3 heads 0,31", heads=[0, 31])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+def test_gdn_decode(kda, gate):
+    cfg = I.DecodeConfig("gdn-dec", "f32", "f32", B=5, H=3, dk=128, dv=64, steps=3, seed=2300)
+    S = I.make_decode_state(cfg)
+    Sg, Sref = S.to(DEV), f64(S)
+    steps = I.make_decode_step_inputs(cfg, 0, steps=3)
+    for s in range(3):
+        x = {n: t[s] for n, t in steps.items()}
+        g = x["log_alpha"][:, :, 0].contiguous() if gate == "scalar" else None
+        o = kda.kda_gdn_decode_step(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV),
+                                    None if g is None else g.to(DEV), x["beta"].to(DEV), Sg)
+        la = np.zeros(tuple(x["q"].shape)) if g is None else np.repeat(f64(g)[:, :, None], 128, axis=2)
+        ro, Sref = oracle.decode(f64(x["q"]), f64(x["k"]), f64(x["v"]), la, f64(x["beta"]), Sref)
+        assert_close(o.cpu(), ro, "f32", "gdn decode o")
+    assert_close(Sg.cpu(), Sref, "f32", "gdn decode S")
