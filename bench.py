@@ -7,8 +7,10 @@ One "step" is one kda_chunk_fwd call over the long-context prefill workload
 The decode step (B=256 resident fp32 states, H=32, d=128, 1000 steps with fresh
 inputs) is timed in the same run and reported under "decode"; the same prefill
 on raw projections through the fused input prologue (kda_chunk_fwd_prologue)
-under "prologue"; and the same shape with one decay per token and head (Gated
-DeltaNet) and with none (DeltaNet), through kda_gdn_chunk_fwd, under "gdn".
+under "prologue"; the same shape with one decay per token and head (Gated
+DeltaNet) and with none (DeltaNet), through kda_gdn_chunk_fwd, under "gdn"; and
+with separate erase and write strengths (kda_chunk_fwd_decoupled) under
+"decoupled".
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -140,6 +142,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
+    ap.add_argument("--no-decoupled", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -244,6 +247,24 @@ def main():
                                      "alg_bytes_per_launch": gb}}
         out["gdn"] = gdn
         del g
+
+    # ---------------- separate erase and write strengths on the same inputs
+    if not args.no_decoupled:
+        wv = I.draw_strength(d["beta"].shape, 5200, d["beta"].dtype, device=dev)
+        fnd = lambda: kda.kda_chunk_fwd_decoupled(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], wv,
+                                                  o=o, h_T=hT)
+        per_d, _ = time_launches(fnd, args.steps, args.warmup, stream)
+        dms_ = float(np.mean(per_d))
+        db_ = alg_b + tok_heads * 2       # plus the write strength, 2 B per token-head
+        out["decoupled"] = {
+            "workload": "kda_chunk_fwd_decoupled on the same inputs, beta as the erase strength and a "
+                        "write strength drawn like beta from its own seed",
+            "ms_per_step": dms_, "tokens_per_s": T / (dms_ * 1e-3), "vs_plain_ms": dms_ / ms,
+            "roofline": {"bound": "hbm", "achieved": db_ / (dms_ * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": db_ / (dms_ * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": load_traffic("chunk_fwd_decoupled_prefill_h32_t65536_traffic.json", digest),
+                         "alg_bytes_per_launch": db_}}
+        del wv
 
     # ---------------- decode step
     if not args.no_decode:

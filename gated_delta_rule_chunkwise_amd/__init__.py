@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
     kda_decode_step_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, o=None)
     kda_gdn_chunk_fwd(q, k, v, log_alpha_or_None, beta, ...)   (scalar gate [.., H], or none)
     kda_gdn_decode_step(q, k, v, log_alpha_or_None, beta, S, o=None)
+    kda_chunk_fwd_decoupled(q, k, v, log_alpha, b_erase, w_write, ...)
+    kda_decode_step_decoupled(q, k, v, log_alpha, b_erase, w_write, S, o=None)
     kda_chunk_fwd_workspace_size(...), kda_status_string(code), kda_abi_version()
 """
 from __future__ import annotations
@@ -28,7 +30,7 @@ KDA_F32, KDA_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
                     "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step",
                     "kda_chunk_fwd_prologue", "kda_decode_step_prologue", "kda_gdn_chunk_fwd",
-                    "kda_gdn_decode_step")
+                    "kda_gdn_decode_step", "kda_chunk_fwd_decoupled", "kda_decode_step_decoupled")
 
 _lib = None
 
@@ -76,6 +78,12 @@ def load_library(path: str = LIB_PATH):
     lib.kda_gdn_chunk_fwd.restype = ctypes.c_int
     lib.kda_gdn_decode_step.argtypes = list(lib.kda_decode_step.argtypes)
     lib.kda_gdn_decode_step.restype = ctypes.c_int
+    lib.kda_chunk_fwd_decoupled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                            ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    lib.kda_chunk_fwd_decoupled.restype = ctypes.c_int
+    lib.kda_decode_step_decoupled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                              ctypes.c_int, vp]
+    lib.kda_decode_step_decoupled.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -143,6 +151,14 @@ def kda_gdn_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=N
                       None, gdn=True)
 
 
+def kda_chunk_fwd_decoupled(q, k, v, log_alpha, b_erase, w_write, h0=None, cu_seqlens=None, *, o=None,
+                            h_T=None, output_final_state=True, workspace=None):
+    """KDA with separate erase (b_erase) and write (w_write) strengths, both
+    [B, T, H] in log_alpha's dtype; otherwise as kda_chunk_fwd."""
+    return _chunk_fwd(q, k, v, log_alpha, b_erase, h0, cu_seqlens, o, h_T, output_final_state, workspace,
+                      None, w_write=w_write)
+
+
 def kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h0=None,
                            cu_seqlens=None, *, o=None, h_T=None, output_final_state=True,
                            workspace=None):
@@ -154,12 +170,14 @@ def kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h
 
 
 def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_state, workspace,
-               log_alpha_min, gdn=False):
+               log_alpha_min, gdn=False, w_write=None):
     import torch
     lib = load_library()
     squeeze = q.dim() == 3
     if squeeze:
         q, k, v, beta = (x.unsqueeze(0) for x in (q, k, v, beta))
+        if w_write is not None:
+            w_write = w_write.unsqueeze(0)
         if log_alpha is not None:
             log_alpha = log_alpha.unsqueeze(0)
     B, T, H, dk = q.shape
@@ -174,6 +192,10 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
         raise ValueError("shape mismatch among q, k, v, log_alpha, beta")
     if k.dtype != q.dtype or v.dtype != q.dtype or (log_alpha is not None and beta.dtype != log_alpha.dtype):
         raise TypeError("q, k, v share one dtype; log_alpha and beta share one dtype")
+    if w_write is not None:
+        _check_dev("w_write", w_write, dev)
+        if w_write.shape != beta.shape or w_write.dtype != beta.dtype:
+            raise ValueError("w_write must match beta in shape and dtype")
     if cu_seqlens is not None:
         _check_dev("cu_seqlens", cu_seqlens, dev)
         if cu_seqlens.dtype != torch.int32:
@@ -195,7 +217,12 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     nseq = N if cu_seqlens is not None else 0
-    if gdn:
+    if w_write is not None:
+        name = "kda_chunk_fwd_decoupled"
+        rc = lib.kda_chunk_fwd_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(w_write),
+                                         _ptr(h0), _ptr(cu_seqlens), nseq, _ptr(o), _ptr(h_T), B, T, H, dk, dv,
+                                         io, gt, _ptr(workspace), ws_len, _stream_of(q))
+    elif gdn:
         name = "kda_gdn_chunk_fwd"
         rc = lib.kda_gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
                                    _ptr(cu_seqlens), nseq, _ptr(o), _ptr(h_T), B, T, H, dk, dv, io, gt,
@@ -229,12 +256,17 @@ def kda_gdn_decode_step(q, k, v, log_alpha, beta, S, o=None):
     return _decode_step(q, k, v, log_alpha, beta, S, o, None, gdn=True)
 
 
+def kda_decode_step_decoupled(q, k, v, log_alpha, b_erase, w_write, S, o=None):
+    """Decode step with separate erase and write strengths ([B, H] each)."""
+    return _decode_step(q, k, v, log_alpha, b_erase, S, o, None, w_write=w_write)
+
+
 def kda_decode_step_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, o=None):
     """kda_decode_step on raw projections (the maps of kda_chunk_fwd_prologue)."""
     return _decode_step(q_raw, k_raw, v, gate_pre, beta_pre, S, o, float(log_alpha_min))
 
 
-def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min, gdn=False):
+def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min, gdn=False, w_write=None):
     import torch
     lib = load_library()
     B, H, dk = q.shape
@@ -246,11 +278,20 @@ def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min, gdn=False):
             _check_dev(name, t, dev)
     if log_alpha is not None and tuple(log_alpha.shape) != ((B, H) if gdn else (B, H, dk)):
         raise ValueError("log_alpha has the wrong shape")
+    if w_write is not None:
+        _check_dev("w_write", w_write, dev)
+        if w_write.shape != beta.shape or w_write.dtype != beta.dtype:
+            raise ValueError("w_write must match beta in shape and dtype")
     if S.dtype != torch.float32 or tuple(S.shape) != (B, H, dk, dv):
         raise ValueError("S must be fp32 [B, H, d_k, d_v]")
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
-    if gdn:
+    if w_write is not None:
+        name = "kda_decode_step_decoupled"
+        rc = lib.kda_decode_step_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                           _ptr(w_write), _ptr(S), _ptr(o), B, H, dk, dv, _dtype_code(q),
+                                           _dtype_code(beta), _stream_of(q))
+    elif gdn:
         name = "kda_gdn_decode_step"
         rc = lib.kda_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
                                      _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(beta),
@@ -276,3 +317,5 @@ chunk_fwd_prologue = kda_chunk_fwd_prologue
 decode_step_prologue = kda_decode_step_prologue
 gdn_chunk_fwd = kda_gdn_chunk_fwd
 gdn_decode_step = kda_gdn_decode_step
+chunk_fwd_decoupled = kda_chunk_fwd_decoupled
+decode_step_decoupled = kda_decode_step_decoupled

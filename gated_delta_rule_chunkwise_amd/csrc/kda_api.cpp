@@ -32,12 +32,13 @@ bool sizes_fit(int64_t a, int64_t b, int64_t c) {
 bool valid_floor(float lo) { return isfinite(lo) && lo <= 0.f; }
 
 kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const void *log_alpha,
-                            const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                            const void *beta, const void *w_write, const float *h0, const int32_t *cu_seqlens,
+                            int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                             kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
                             size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode);
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
-                              const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
+                              const void *beta, const void *w_write, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
                               int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
                               bool prologue, float lo, int gate_mode);
 
@@ -81,7 +82,7 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
                            kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream) {
-    return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
                           io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f, 0);
 }
 
@@ -92,7 +93,7 @@ kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const 
                                     int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
                                     void *workspace, size_t workspace_bytes, void *stream) {
     if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
-    return chunk_fwd_impl(q_raw, k_raw, v, gate_pre, beta_pre, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k,
+    return chunk_fwd_impl(q_raw, k_raw, v, gate_pre, beta_pre, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k,
                           d_v, io_dtype, gate_dtype, workspace, workspace_bytes, stream, true, log_alpha_min, 0);
 }
 
@@ -100,7 +101,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
                              const void *beta, float *S, void *o, int32_t B, int32_t H,
                              int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
                              kda_dtype_t gate_dtype, void *stream) {
-    return decode_step_impl(q, k, v, log_alpha, beta, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
+    return decode_step_impl(q, k, v, log_alpha, beta, nullptr, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
                             0.f, 0);
 }
 
@@ -109,7 +110,7 @@ kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, cons
                                       float *S, void *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                                       kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream) {
     if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
-    return decode_step_impl(q_raw, k_raw, v, gate_pre, beta_pre, S, o, B, H, d_k, d_v, io_dtype, gate_dtype,
+    return decode_step_impl(q_raw, k_raw, v, gate_pre, beta_pre, nullptr, S, o, B, H, d_k, d_v, io_dtype, gate_dtype,
                             stream, true, log_alpha_min, 0);
 }
 
@@ -118,7 +119,7 @@ kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
                                void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
                                size_t workspace_bytes, void *stream) {
-    return chunk_fwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
                           io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f,
                           log_alpha ? 1 : 2);
 }
@@ -126,8 +127,30 @@ kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
 kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
                                  const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
                                  int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream) {
-    return decode_step_impl(q, k, v, log_alpha, beta, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
+    return decode_step_impl(q, k, v, log_alpha, beta, nullptr, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
                             0.f, log_alpha ? 1 : 2);
+}
+
+kda_status_t kda_chunk_fwd_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
+                                     const void *b_erase, const void *w_write, const float *h0,
+                                     const int32_t *cu_seqlens, int32_t num_seqs, void *o, float *h_T, int32_t B,
+                                     int32_t T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                                     kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    if ((int64_t)B * T > 0 && (!w_write || !aligned_to(w_write, dsize(gate_dtype))))
+        return valid_dtype(gate_dtype) ? KDA_ERR_INVALID_ARGUMENT : KDA_ERR_UNSUPPORTED;
+    return chunk_fwd_impl(q, k, v, log_alpha, b_erase, w_write, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k,
+                          d_v, io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f, 0);
+}
+
+kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
+                                       const void *b_erase, const void *w_write, float *S, void *o, int32_t B,
+                                       int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                                       kda_dtype_t gate_dtype, void *stream) {
+    if (!w_write || !aligned_to(w_write, dsize(gate_dtype)))
+        return valid_dtype(gate_dtype) ? KDA_ERR_INVALID_ARGUMENT : KDA_ERR_UNSUPPORTED;
+    return decode_step_impl(q, k, v, log_alpha, b_erase, w_write, S, o, B, H, d_k, d_v, io_dtype, gate_dtype,
+                            stream, false, 0.f, 0);
 }
 
 }  // extern "C"
@@ -135,7 +158,8 @@ kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, co
 namespace {
 
 kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const void *log_alpha,
-                            const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                            const void *beta, const void *w_write, const float *h0, const int32_t *cu_seqlens,
+                            int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                             kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
                             size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode) {
@@ -172,7 +196,7 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
     if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
     if (!have_tokens && !h_T) return KDA_OK;  // nothing to compute or write
 
-    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.w_write = w_write;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;
@@ -183,7 +207,7 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
 }
 
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
-                              const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
+                              const void *beta, const void *w_write, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
                               int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
                               bool prologue, float lo, int gate_mode) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
@@ -197,7 +221,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const
     if (gate_mode == 0 && (!log_alpha || !aligned16(log_alpha))) return KDA_ERR_INVALID_ARGUMENT;
     if (gate_mode == 1 && !aligned_to(log_alpha, dsize(gate_dtype))) return KDA_ERR_INVALID_ARGUMENT;
     kda::DecodeArgs a;
-    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S; a.o = o;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.w_write = w_write; a.S = S; a.o = o;
     a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
     a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;

@@ -73,6 +73,7 @@ struct alignas(16) ChunkSmem {
     bf16_t P[2][kC][TS];                       // hi/lo of P
     bf16_t S[NP][BV][KS];                      // (Diag(e^m) S)^T of this column block
     float beta[kC];
+    float wr[kC];                              // separate write strengths (DEC)
     float colM[DK];                            // e^{m}
     float colGn[DK];                           // e^{g_n}
     float colGnM[DK];                          // e^{g_n - m}
@@ -89,10 +90,11 @@ struct alignas(16) ExactSmem {
 
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
 // (input prologue; lo is the floor of log alpha).
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM>
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
-    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
+    const float *__restrict__ h0,
     const int32_t *__restrict__ cu_seqlens, IO *__restrict__ o, float *__restrict__ h_T,
     int64_t seq_len, int32_t H, int32_t DV, int64_t num_chains, float lo) {
     constexpr int CPL = DK / 64;    // key channels per lane in the load phase
@@ -138,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 
     if constexpr (EXACT) {
         for (int64_t tk = bos; tk < eos; ++tk)
-            token_update<DK, BV, IO, GT, PRO, GM>(Sacc, smem.red, q, k, v, log_alpha, beta, o, tk, H, h, DV, col0,
-                                                  w, lg, lr, lo);
+            token_update<DK, BV, IO, GT, PRO, GM, DEC>(Sacc, smem.red, q, k, v, log_alpha, beta, wr, o, tk, H, h, DV,
+                                                       col0, w, lg, lr, lo);
     } else {
         Sm &sm = smem;
         // Upper blocks of T and P are never written: zero them once.
@@ -147,10 +149,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             (&sm.T[0][0][0])[idx] = (bf16_t)0.f;
             (&sm.P[0][0][0])[idx] = (bf16_t)0.f;
         }
-        ChunkRegs<DK, BV, IO, GT, PRO, GM> in;
+        ChunkRegs<DK, BV, IO, GT, PRO, GM, DEC> in;
         if (bos < eos) {
             const int nv0 = (int)((eos - bos) < kC ? (eos - bos) : kC);
-            in.load(q, k, v, log_alpha, beta, bos, nv0, H, h, DV, col0, w, l, lg, lr);
+            in.load(q, k, v, log_alpha, beta, wr, bos, nv0, H, h, DV, col0, w, l, lg, lr);
         }
         f32x4_t accZ[NT];
 
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vcur[nt][e] = in.vv[nt][e];
             if (w == 0) sm.beta[l] = (l < nv) ? in.bt : 0.f;
+            if (DEC && w == 0) sm.wr[l] = (l < nv) ? in.wt : 0.f;
             lds_barrier();
             float m2[CPL];
             bool big = false;
@@ -290,14 +293,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                         *reinterpret_cast<bf16x8_t *>(&sm.KIt[pl][l * CPL + cc][8 * w]) = kit[pl][cc];
             }
             // the next chunk's inputs go in flight now
-            if (has_next) in.load(q, k, v, log_alpha, beta, tbase + kC, nv_next, H, h, DV, col0, w, l, lg, lr);
+            if (has_next) in.load(q, k, v, log_alpha, beta, wr, tbase + kC, nv_next, H, h, DV, col0, w, l, lg, lr);
             lds_barrier();
 
             if (slow) {
                 // exact token-by-token path for a chunk with a huge in-chunk decay
                 for (int r = 0; r < nv; ++r)
-                    token_update<DK, BV, IO, GT, PRO, GM>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H,
-                                                          h, DV, col0, w, lg, lr, lo);
+                    token_update<DK, BV, IO, GT, PRO, GM, DEC>(Sacc, sm.red, q, k, v, log_alpha, beta, wr, o,
+                                                               tbase + r, H, h, DV, col0, w, lg, lr, lo);
                 continue;
             }
 
@@ -444,7 +447,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * rb + 4 * lg + e;
-                        x[e] = sm.beta[r] * (vcur[nt][e] - accY[e]);
+                        x[e] = DEC ? sm.wr[r] * vcur[nt][e] - sm.beta[r] * accY[e]
+                                   : sm.beta[r] * (vcur[nt][e] - accY[e]);
                     }
                     const int jl = nt * 16 + lr;
                     store_split4(&sm.X[0][jl][16 * rb + 4 * lg], &sm.X[1][jl][16 * rb + 4 * lg], x);
@@ -591,37 +595,38 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     }
 }
 
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM>
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM, bool DEC>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t st) {
     const int64_t chains = a.num_seqs * (int64_t)a.H;
     const int64_t nwg = chains * (a.d_v / BV);
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, EXACT, PRO, GM>), dim3((unsigned)nwg), dim3(kThreads),
-                       0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
-                       (const GT *)a.beta, a.h0, a.cu_seqlens, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains,
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, EXACT, PRO, GM, DEC>), dim3((unsigned)nwg),
+                       dim3(kThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
+                       (const GT *)a.log_alpha, (const GT *)a.beta, (const GT *)a.w_write, a.h0, a.cu_seqlens, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains,
                        a.log_alpha_min);
     return hipGetLastError();
 }
 
 // bf16 I/O: single-bf16 decayed operands.  fp32 I/O: split operands (d_k = 64)
 // or the exact token path (d_k = 128).
-template <int DK, int BV, bool PRO, int GM>
+template <int DK, int BV, bool PRO, int GM, bool DEC>
 hipError_t launch_types(const ChunkArgs &a, hipStream_t st) {
     if (a.io_bf16)
-        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, false, PRO, GM>(a, st)
-                           : launch_t<DK, BV, bf16_t, float, false, false, PRO, GM>(a, st);
+        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, false, PRO, GM, DEC>(a, st)
+                           : launch_t<DK, BV, bf16_t, float, false, false, PRO, GM, DEC>(a, st);
     constexpr bool EX = DK == 128;
-    return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, !EX, EX, PRO, GM>(a, st)
-                       : launch_t<DK, BV, float, float, !EX, EX, PRO, GM>(a, st);
+    return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, !EX, EX, PRO, GM, DEC>(a, st)
+                       : launch_t<DK, BV, float, float, !EX, EX, PRO, GM, DEC>(a, st);
 }
 
-// The input variants that exist: per-channel gates with or without the prologue,
-// and the scalar-gate forms without it.
+// The input variants that exist: per-channel gates with or without the prologue
+// or with decoupled strengths, and the scalar-gate forms.
 template <int DK, int BV>
 hipError_t launch_types_pro(const ChunkArgs &a, hipStream_t st) {
-    if (a.gate_mode == kGatePerHead) return launch_types<DK, BV, false, kGatePerHead>(a, st);
-    if (a.gate_mode == kGateNone) return launch_types<DK, BV, false, kGateNone>(a, st);
-    return a.prologue ? launch_types<DK, BV, true, kGatePerChannel>(a, st)
-                      : launch_types<DK, BV, false, kGatePerChannel>(a, st);
+    if (a.gate_mode == kGatePerHead) return launch_types<DK, BV, false, kGatePerHead, false>(a, st);
+    if (a.gate_mode == kGateNone) return launch_types<DK, BV, false, kGateNone, false>(a, st);
+    if (a.prologue) return launch_types<DK, BV, true, kGatePerChannel, false>(a, st);
+    if (a.w_write) return launch_types<DK, BV, false, kGatePerChannel, true>(a, st);
+    return launch_types<DK, BV, false, kGatePerChannel, false>(a, st);
 }
 
 // Value-column block width: 32 when that still gives at least two workgroups

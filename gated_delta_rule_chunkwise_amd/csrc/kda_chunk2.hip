@@ -158,16 +158,19 @@ struct alignas(16) PrepSmem {
     };
     float tot[DK][kWaves];
     float beta[kC];
+    float wr[kC];                              // separate write strengths (DEC)
 };
 
 // ---------------------------------------------------------------------------------
 // Prep: one workgroup (8 waves) per (chunk, head).
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
-// (input prologue; lo is the floor of log alpha).
-template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
+// (input prologue; lo is the floor of log alpha).  GM: gate layout.  DEC: beta
+// erases and wr writes (decoupled strengths): A and W take beta, U0 takes wr.
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
-    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const int32_t *__restrict__ cu,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
+    const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, uint8_t *__restrict__ recs, int64_t N, int64_t T, int32_t H,
     float lo) {
     constexpr int CPL = DK / 64;
@@ -191,8 +194,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
 
     // ---- load this chunk (rows past the end read the last row; their gates,
     // keys and beta are zeroed below, so they contribute nothing)
-    ChunkRegs<DK, 16, IO, GT, PRO, GM> in;
-    in.load(q, k, q, log_alpha, beta, t0, nv, H, h, 0, 0, w, l, lg, lr, false);
+    ChunkRegs<DK, 16, IO, GT, PRO, GM, DEC> in;
+    in.load(q, k, q, log_alpha, beta, wr, t0, nv, H, h, 0, 0, w, l, lg, lr, false);
     in.prepare(w, lo);
     typedef typename VecT<IO, CPV>::type VV;
     VV vr[8];
@@ -215,6 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
         sm.tot[l * CPL + cc][w] = csum[7][cc];
     }
     if (w == 0) sm.beta[l] = (l < nv) ? in.bt : 0.f;
+    if (DEC && w == 0) sm.wr[l] = (l < nv) ? in.wt : 0.f;
     lds_barrier();
     float m2[CPL];
     bool big = false;
@@ -494,7 +498,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
     }
     lds_barrier();
 
-    // ---- Tb = T diag(beta) in place (hi/lo); KA^T and V^T to LDS
+    // ---- Tb = T diag(beta) in place (hi/lo); KA^T and V^T to LDS.  With DEC, T
+    // stays unscaled here: W and U0 scale their rows of T by beta or wr below.
     {
         const int r = tid >> 3, i0 = 8 * (tid & 7);
         const bf16x8_t hv = lds_ld8(&sm.t.T[0][r][i0]), lv = lds_ld8(&sm.t.T[1][r][i0]);
@@ -503,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
         const bool upper = (i0 >> 4) > (r >> 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = upper ? 0.f : ((float)hv[e] + (float)lv[e]) * sm.beta[i0 + e];
+            const float x = upper ? 0.f : ((float)hv[e] + (float)lv[e]) * (DEC ? 1.f : sm.beta[i0 + e]);
             bf16_t hh, ll;
             split_bf16(x, hh, ll);
             h2[e] = hh;
@@ -539,6 +544,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
             if (ks <= (rb >> 1)) {   // Tb is lower triangular
                 th[ks] = lds_ld8(&sm.t.T[0][16 * rb + lr][32 * ks + 8 * lg]);
                 tlo[ks] = lds_ld8(&sm.t.T[1][16 * rb + lr][32 * ks + 8 * lg]);
+                if constexpr (DEC) {   // T diag(beta) for W, T diag(wr) for U0
+                    const float *sc = isW ? sm.beta : sm.wr;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = ((float)th[ks][e] + (float)tlo[ks][e]) * sc[32 * ks + 8 * lg + e];
+                        bf16_t hh, ll;
+                        split_bf16(x, hh, ll);
+                        th[ks][e] = hh;
+                        tlo[ks][e] = ll;
+                    }
+                }
             }
         }
         const int ncol = isW ? DK / 16 : DV / 16;
@@ -727,11 +743,12 @@ struct ChainRange {
 
 __device__ __forceinline__ int chunk_count(const ChainRange &cr) { return (int)((cr.eos - cr.bos + kC - 1) / kC); }
 
-template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM>
+template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const ChainRange &cr,
                                                 const IO *__restrict__ q, const IO *__restrict__ k,
                                                 const IO *__restrict__ v, const GT *__restrict__ log_alpha,
-                                                const GT *__restrict__ beta, const float *__restrict__ h0,
+                                                const GT *__restrict__ beta, const GT *__restrict__ wr,
+                                                const float *__restrict__ h0,
                                                 IO *__restrict__ o, float *__restrict__ h_T, int H, int w, int tid,
                                                 float lo) {
     constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
@@ -763,8 +780,8 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
         const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
         if (slow) {
             for (int r = 0; r < nv; ++r)
-                token_update<DK, BV, IO, GT, PRO, GM>(Sacc, sm.red, q, k, v, log_alpha, beta, o, tbase + r, H, h,
-                                                      DV, col0, w, lg, lr, lo);
+                token_update<DK, BV, IO, GT, PRO, GM, DEC>(Sacc, sm.red, q, k, v, log_alpha, beta, wr, o, tbase + r,
+                                                           H, h, DV, col0, w, lg, lr, lo);
         } else {
             // S' = Diag(e^m) S, transposed, to LDS
 #pragma unroll
@@ -990,10 +1007,11 @@ __device__ __forceinline__ void loader_role_loop(StateSmem<DK, DV, BV> &sm, cons
     }
 }
 
-template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM>
+template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
-    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const float *__restrict__ h0,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
+    const float *__restrict__ h0,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ chunk_off,
     const uint8_t *__restrict__ recs, IO *__restrict__ o, float *__restrict__ h_T, int64_t seq_len,
     int32_t H, int64_t num_chains, float lo) {
@@ -1016,14 +1034,15 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
         cr.c0 = cr.n * ((seq_len + kC - 1) / kC);
     }
     if (w < 4)
-        state_role_loop<DK, DV, BV, IO, GT, PRO, GM>(sm, cr, q, k, v, log_alpha, beta, h0, o, h_T, H, w, tid, lo);
+        state_role_loop<DK, DV, BV, IO, GT, PRO, GM, DEC>(sm, cr, q, k, v, log_alpha, beta, wr, h0, o, h_T, H, w, tid,
+                                                          lo);
     else if (w < 8)
         output_role_loop<DK, DV, BV, IO>(sm, cr, o, H, w - 4, tid);
     else
         loader_role_loop<DK, DV, BV>(sm, cr, recs, H, tid - 512);
 }
 
-template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
     uint8_t *ws = reinterpret_cast<uint8_t *>(a.workspace);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + kHeaderBytes);
@@ -1032,48 +1051,50 @@ hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
     const int64_t nprep = max_chunks(a) * a.H;
     if (nprep > 0)
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, DV, IO, GT, PRO, GM>), dim3((unsigned)nprep), dim3(kThreads), 0, st,
-                           (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
-                           (const GT *)a.beta, a.cu_seqlens, (const int32_t *)chunk_off, recs, a.num_seqs, a.seq_len,
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, DV, IO, GT, PRO, GM, DEC>), dim3((unsigned)nprep), dim3(kThreads), 0,
+                           st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
+                           (const GT *)a.beta, (const GT *)a.w_write, a.cu_seqlens, (const int32_t *)chunk_off, recs, a.num_seqs, a.seq_len,
                            a.H, a.log_alpha_min);
     const int64_t chains = a.num_seqs * (int64_t)a.H;
     // 32 value columns per workgroup only at d_k = 64: at d_k = 128 the loader
     // buffers and the 32-column state tiles do not fit the 16-wave register budget
     if constexpr (DK == 64) {
         if (bv == 32) {
-            hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 32, IO, GT, PRO, GM>), dim3((unsigned)(chains * (DV / 32))),
-                               dim3(kStateThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
-                               (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
+            hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 32, IO, GT, PRO, GM, DEC>),
+                               dim3((unsigned)(chains * (DV / 32))), dim3(kStateThreads), 0, st, (const IO *)a.q,
+                               (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha, (const GT *)a.beta,
+                               (const GT *)a.w_write, a.h0, a.cu_seqlens,
                                (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains,
                                a.log_alpha_min);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT, PRO, GM>), dim3((unsigned)(chains * (DV / 16))),
+    hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT, PRO, GM, DEC>), dim3((unsigned)(chains * (DV / 16))),
                            dim3(kStateThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
-                           (const GT *)a.log_alpha, (const GT *)a.beta, a.h0, a.cu_seqlens,
+                           (const GT *)a.log_alpha, (const GT *)a.beta, (const GT *)a.w_write, a.h0, a.cu_seqlens,
                            (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains,
                            a.log_alpha_min);
     return hipGetLastError();
 }
 
-template <typename GT, bool PRO, int GM>
+template <typename GT, bool PRO, int GM, bool DEC>
 hipError_t launch_two_kernel_dims(const ChunkArgs &a, int bv, hipStream_t st) {
     if (a.d_k == 128)
-        return a.d_v == 128 ? launch_two_kernel<128, 128, bf16_t, GT, PRO, GM>(a, bv, st)
-                            : launch_two_kernel<128, 64, bf16_t, GT, PRO, GM>(a, bv, st);
-    return a.d_v == 128 ? launch_two_kernel<64, 128, bf16_t, GT, PRO, GM>(a, bv, st)
-                        : launch_two_kernel<64, 64, bf16_t, GT, PRO, GM>(a, bv, st);
+        return a.d_v == 128 ? launch_two_kernel<128, 128, bf16_t, GT, PRO, GM, DEC>(a, bv, st)
+                            : launch_two_kernel<128, 64, bf16_t, GT, PRO, GM, DEC>(a, bv, st);
+    return a.d_v == 128 ? launch_two_kernel<64, 128, bf16_t, GT, PRO, GM, DEC>(a, bv, st)
+                        : launch_two_kernel<64, 64, bf16_t, GT, PRO, GM, DEC>(a, bv, st);
 }
 
-// The input variants that exist: per-channel gates with or without the prologue,
-// and the scalar-gate forms without it.
+// The input variants that exist: per-channel gates with or without the prologue
+// or with decoupled strengths, and the scalar-gate forms.
 template <typename GT>
 hipError_t launch_two_kernel_variant(const ChunkArgs &a, int bv, hipStream_t st) {
-    if (a.gate_mode == kGatePerHead) return launch_two_kernel_dims<GT, false, kGatePerHead>(a, bv, st);
-    if (a.gate_mode == kGateNone) return launch_two_kernel_dims<GT, false, kGateNone>(a, bv, st);
-    if (a.prologue) return launch_two_kernel_dims<GT, true, kGatePerChannel>(a, bv, st);
-    return launch_two_kernel_dims<GT, false, kGatePerChannel>(a, bv, st);
+    if (a.gate_mode == kGatePerHead) return launch_two_kernel_dims<GT, false, kGatePerHead, false>(a, bv, st);
+    if (a.gate_mode == kGateNone) return launch_two_kernel_dims<GT, false, kGateNone, false>(a, bv, st);
+    if (a.prologue) return launch_two_kernel_dims<GT, true, kGatePerChannel, false>(a, bv, st);
+    if (a.w_write) return launch_two_kernel_dims<GT, false, kGatePerChannel, true>(a, bv, st);
+    return launch_two_kernel_dims<GT, false, kGatePerChannel, false>(a, bv, st);
 }
 
 size_t record_bytes(int d_k, int d_v) {

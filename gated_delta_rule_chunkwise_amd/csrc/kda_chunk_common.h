@@ -152,13 +152,15 @@ template <int BV> struct TokenRed { static constexpr int N = 2 * BV + 3; };
 // With PRO (raw projections in), the gate and beta are mapped as they are read
 // and the raw q and k enter through their squared norms: a = k^T S and b = q^T S
 // are taken with the raw vectors and rescaled once the norms are reduced.
-template <int DK, int BV, typename IO, typename GT, bool PRO, int GM>
+// With DEC the erase and write strengths are separate (beta erases, wr writes):
+// the written row is u = wr v - beta a instead of beta (v - a).
+template <int DK, int BV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 16) / 4],
                                              float (*red)[TokenRed<BV>::N], const IO *__restrict__ q,
                                              const IO *__restrict__ k, const IO *__restrict__ v,
                                              const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
-                                             IO *__restrict__ o, int64_t tk, int H, int h, int DV, int col0, int w,
-                                             int lg, int lr, float lo) {
+                                             const GT *__restrict__ wr, IO *__restrict__ o, int64_t tk, int H,
+                                             int h, int DV, int col0, int w, int lg, int lr, float lo) {
     constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
     float kc[STW][4];
     if (w < 4) {
@@ -223,6 +225,7 @@ __device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 1
     if (w < 4) {
         float qk = red[0][2 * BV] + red[1][2 * BV] + red[2][2 * BV] + red[3][2 * BV];
         float bt = to_f32(beta[tk * H + h]);
+        const float wt = DEC ? to_f32(wr[tk * H + h]) : 0.f;
         float iq = 1.f, ik = 1.f;
         if (PRO) {
             iq = pro_inv_norm(red[0][2 * BV + 1] + red[1][2 * BV + 1] + red[2][2 * BV + 1] + red[3][2 * BV + 1]);
@@ -240,7 +243,8 @@ __device__ __forceinline__ void token_update(f32x4_t (&Sacc)[(DK / 16) * (BV / 1
                 a *= ik;
                 b *= iq;
             }
-            u[nt] = bt * (to_f32(v[(tk * H + h) * (int64_t)DV + col0 + jl]) - a);
+            const float vj = to_f32(v[(tk * H + h) * (int64_t)DV + col0 + jl]);
+            u[nt] = DEC ? wt * vj - bt * a : bt * (vj - a);
             if (w == 0 && lg == 0) o[(tk * H + h) * (int64_t)DV + col0 + jl] = from_f32<IO>(b + u[nt] * qk);
             if (PRO) u[nt] *= ik;   // the state takes k_hat = k / |k|
         }
@@ -281,7 +285,7 @@ template <> __device__ __forceinline__ float2 vsplat<float2, float>(float x) { r
 // the floored -softplus (mapped once, at load), kval()/qval() the raw value
 // times the per-token inverse norm (reduced over the wave, which holds whole
 // rows), and bt is sigmoid(b).
-template <int DK, int BV, typename IO, typename GT, bool PRO, int GM>
+template <int DK, int BV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 struct ChunkRegs {
     static constexpr int CPL = DK / 64, NT = BV / 16;
     typedef typename VecT<GT, CPL>::type GV;
@@ -289,7 +293,7 @@ struct ChunkRegs {
     GV la[8];
     IV kk[8], qq[8];
     float vv[NT][4];
-    float bt;
+    float bt, wt;   // wave 0, lane = token: beta and (DEC) the write strength
     float qs[PRO ? 8 : 1], ks[PRO ? 8 : 1];
     float lf[PRO ? 8 : 1][CPL];
 
@@ -308,8 +312,9 @@ struct ChunkRegs {
 
     __device__ __forceinline__ void load(const IO *__restrict__ q, const IO *__restrict__ k,
                                          const IO *__restrict__ v, const GT *__restrict__ log_alpha,
-                                         const GT *__restrict__ beta, int64_t tbase, int nv, int H, int h,
-                                         int DV, int col0, int w, int l, int lg, int lr, bool with_v = true) {
+                                         const GT *__restrict__ beta, const GT *__restrict__ wr, int64_t tbase,
+                                         int nv, int H, int h, int DV, int col0, int w, int l, int lg, int lr,
+                                         bool with_v = true) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * w + i;
@@ -335,6 +340,7 @@ struct ChunkRegs {
                 }
         }
         if (w == 0) bt = to_f32(beta[(tbase + (l < nv ? l : nv - 1)) * H + h]);
+        if (DEC && w == 0) wt = to_f32(wr[(tbase + (l < nv ? l : nv - 1)) * H + h]);
     }
 
     // The prologue maps of the loaded chunk (nothing without PRO); called once

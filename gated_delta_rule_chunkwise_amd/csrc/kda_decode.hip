@@ -22,10 +22,11 @@ constexpr int kDecodeThreads = 256;
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
 // (input prologue; lo is the floor of log alpha).  The reductions then run on
 // the raw q and k and are rescaled by the inverse norms, reduced alongside.
-template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
+// DEC: beta erases and wr writes: u = wr v - beta k^T(alpha S).
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
-    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, float *__restrict__ S,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr, float *__restrict__ S,
     IO *__restrict__ o, float lo) {
     constexpr int NCG = DV / 4;                 // groups of 4 value columns
     constexpr int NRG = kDecodeThreads / NCG;   // row groups
@@ -108,7 +109,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     }
     float u[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = bt * (to_f32(v[bh * DV + 4 * cg + j]) - a[j]);
+    for (int j = 0; j < 4; ++j) {
+        const float vj = to_f32(v[bh * DV + 4 * cg + j]);
+        u[j] = DEC ? to_f32(wr[bh]) * vj - bt * a[j] : bt * (vj - a[j]);
+    }
 
     // The updated state is written with non-temporal stores: it is not read again
     // in this step, and streaming it past the caches keeps the HBM write stream
@@ -129,23 +133,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     }
 }
 
-template <int DK, int DV, typename IO, typename GT, bool PRO, int GM>
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 hipError_t launch_v(const DecodeArgs &a, hipStream_t st) {
     const int64_t nb = a.B * (int64_t)a.H;
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT, PRO, GM>), dim3((unsigned)nb), dim3(kDecodeThreads), 0,
-                       st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
-                       (const GT *)a.beta, a.S, (IO *)a.o, a.log_alpha_min);
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO, GT, PRO, GM, DEC>), dim3((unsigned)nb), dim3(kDecodeThreads),
+                       0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
+                       (const GT *)a.beta, (const GT *)a.w_write, a.S, (IO *)a.o, a.log_alpha_min);
     return hipGetLastError();
 }
 
-// The input variants that exist: per-channel gates with or without the prologue,
-// and the scalar-gate forms without it.
+// The input variants that exist: per-channel gates with or without the prologue
+// or with decoupled strengths, and the scalar-gate forms.
 template <int DK, int DV, typename IO, typename GT>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t st) {
-    if (a.gate_mode == kGatePerHead) return launch_v<DK, DV, IO, GT, false, kGatePerHead>(a, st);
-    if (a.gate_mode == kGateNone) return launch_v<DK, DV, IO, GT, false, kGateNone>(a, st);
-    return a.prologue ? launch_v<DK, DV, IO, GT, true, kGatePerChannel>(a, st)
-                      : launch_v<DK, DV, IO, GT, false, kGatePerChannel>(a, st);
+    if (a.gate_mode == kGatePerHead) return launch_v<DK, DV, IO, GT, false, kGatePerHead, false>(a, st);
+    if (a.gate_mode == kGateNone) return launch_v<DK, DV, IO, GT, false, kGateNone, false>(a, st);
+    if (a.prologue) return launch_v<DK, DV, IO, GT, true, kGatePerChannel, false>(a, st);
+    if (a.w_write) return launch_v<DK, DV, IO, GT, false, kGatePerChannel, true>(a, st);
+    return launch_v<DK, DV, IO, GT, false, kGatePerChannel, false>(a, st);
 }
 
 template <int DK, int DV>

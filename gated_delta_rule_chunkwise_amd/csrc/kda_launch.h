@@ -8,6 +8,7 @@ namespace kda {
 
 struct ChunkArgs {
     const void *q, *k, *v, *log_alpha, *beta;
+    const void *w_write;        // separate write strengths [.., H], or nullptr (beta writes)
     const float *h0;
     const int32_t *cu_seqlens;  // device, or nullptr (equal-length batch)
     void *o;
@@ -27,6 +28,7 @@ struct ChunkArgs {
 
 struct DecodeArgs {
     const void *q, *k, *v, *log_alpha, *beta;
+    const void *w_write;        // separate write strengths [B, H], or nullptr (beta writes)
     float *S;
     void *o;
     int64_t B;

@@ -218,3 +218,10 @@ def make_decode_raw_step_inputs(cfg: DecodeConfig, step: int, device="cpu", step
         out["beta_pre"].append(_randn((B, H), g, device).to(gio))
         out["gate_pre"].append(_randn((B, H, dk), g, device).to(gio))
     return {n: torch.stack(xs).contiguous() for n, xs in out.items()}
+
+
+def draw_strength(shape, seed: int, dtype=torch.bfloat16, device="cpu"):
+    """Update strengths drawn like beta, sigmoid(N(0, 1)), from their own seed
+    (the separate write strength of the decoupled entry points)."""
+    g = _gen(seed, device)
+    return torch.sigmoid(_randn(tuple(shape), g, device)).to(dtype)

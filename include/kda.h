@@ -208,6 +208,38 @@ kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, co
                                  const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
                                  int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream);
 
+/*
+ * kda_chunk_fwd_decoupled -- KDA with the update strength split into an erase
+ * strength b_t and a write strength w_t (per token and head):
+ *
+ *     S <- (I - b_t k_t k_t^T) Diag(alpha_t) S + w_t k_t v_t^T,   o_t = S^T q_t
+ *
+ * b_t = w_t = beta_t is kda_chunk_fwd.  The Kimi Linear CoChat record (section
+ * "Claims other papers make about this one") cites a follow-up that unties the
+ * single beta into erase and write gates; it gives no formula, and this is the
+ * scalar reading of it.  Arguments, workspace and errors as for kda_chunk_fwd,
+ * with b_erase in place of beta and
+ *
+ *   w_write     [B, T, H] gate_dtype, aligned to its element size; required
+ *               (NULL is KDA_ERR_INVALID_ARGUMENT when there are tokens)
+ */
+kda_status_t kda_chunk_fwd_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
+                                     const void *b_erase, const void *w_write, const float *h0,
+                                     const int32_t *cu_seqlens, int32_t num_seqs, void *o, float *h_T, int32_t B,
+                                     int32_t T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                                     kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
+ * kda_decode_step_decoupled -- one decode step of the same update: b_erase and
+ * w_write are [B, H] gate_dtype (w_write required); otherwise as
+ * kda_decode_step.
+ */
+kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
+                                       const void *b_erase, const void *w_write, float *S, void *o, int32_t B,
+                                       int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                                       kda_dtype_t gate_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -212,3 +212,40 @@ def test_gdn_gate_alignment_is_element_size(kda):
 def test_gdn_decode_validates(kda, kw, code):
     lib = kda.load_library()
     assert decode_gdn(lib, **kw) == code
+
+
+def chunk_dec(lib, wwr=P, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+             dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_decoupled(a["q"], a["k"], a["v"], a["la"], a["beta"], wwr, a["h0"], a["cu"],
+                                       a["N"], a["o"], a["hT"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                       a["io"], a["gt"], a["ws"], a["wsb"], None)
+
+
+def decode_dec(lib, wwr=P, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, S=P, o=P, B=4, H=2, dk=128, dv=128, io=1, gt=1)
+    a.update(kw)
+    return lib.kda_decode_step_decoupled(a["q"], a["k"], a["v"], a["la"], a["beta"], wwr, a["S"], a["o"],
+                                         a["B"], a["H"], a["dk"], a["dv"], a["io"], a["gt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wwr=None), 1), (dict(wwr=P + 1), 1), (dict(wwr=P + 2, gt=0), 1),
+    (dict(dk=96), 2), (dict(B=0), 1), (dict(la=None), 1), (dict(la=P + 4), 1), (dict(beta=P + 1), 1),
+    (dict(ws=None, wsb=0), 3),
+])
+def test_decoupled_chunk_fwd_validates(kda, kw, code):
+    lib = kda.load_library()
+    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    a = dict(ws=P, wsb=need)
+    a.update(kw)
+    assert chunk_dec(lib, **a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wwr=None), 1), (dict(wwr=P + 1), 1), (dict(dk=32), 2), (dict(S=None), 1), (dict(la=P + 2), 1),
+])
+def test_decoupled_decode_validates(kda, kw, code):
+    lib = kda.load_library()
+    assert decode_dec(lib, **kw) == code

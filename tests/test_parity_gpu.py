@@ -430,3 +430,74 @@ def test_gdn_decode(kda, gate):
         ro, Sref = oracle.decode(f64(x["q"]), f64(x["k"]), f64(x["v"]), la, f64(x["beta"]), Sref)
         assert_close(o.cpu(), ro, "f32", "gdn decode o")
     assert_close(Sg.cpu(), Sref, "f32", "gdn decode S")
+
+
+# ------------------------------------------------------------------ decoupled strengths
+# kda_chunk_fwd_decoupled / kda_decode_step_decoupled against the oracle's
+# generalised recurrence S <- (I - b k k^T) Diag(alpha) S + w k v^T (pinned: b = w
+# is KDA, b = 0, w = 1, alpha = 1 is linear attention).
+def _dec_check(kda, d, wv, io, what, heads=None):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    o, hT = kda.kda_chunk_fwd_decoupled(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], wv.to(DEV),
+                                        h0=dev["h0"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    o, hT = o.cpu(), hT.cpu()
+    dd = dict(d)
+    dd["w"] = wv
+    ref = to_oracle(dd, None, heads)
+    hs = slice(None) if heads is None else list(heads)
+    wref = f64(wv)[ref["rows"]][:, hs]
+    ro, rh = oracle.gen_fwd(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], wref, h0=ref["h0"],
+                            cu_seqlens=ref["cu_seqlens"])
+    go = o.reshape(-1, *o.shape[-2:])[torch.from_numpy(ref["rows"])][:, hs]
+    eo = assert_close(go, ro, io, what + " o")
+    eh = assert_close(hT[:, hs], rh, io, what + " h_T")
+    log(what, "o", eo, "h_T", eh)
+
+
+@pytest.mark.parametrize("case", ["independent", "erase_only", "write_only"])
+@pytest.mark.parametrize("io,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("f32", 128, 128), ("f32", 64, 128)])
+def test_decoupled_ragged_varlen(kda, case, io, dk, dv):
+    """Ragged packed sequences with h0 and a flagged chunk (token path); write
+    strengths drawn independently of beta, or one of the two strengths zero."""
+    cfg = I.ChunkConfig("dec", io, io, H=3, dk=dk, dv=dv, h0=True, seed=51)
+    d = I.make_chunk_inputs(cfg, lengths=[300, 64, 130, 1, 200])
+    la = d["log_alpha"].clone()
+    la[300:364, 1, :3] = -2.0      # sequence 1, head 1: a chunk beyond the matrix-core range
+    d["log_alpha"] = la
+    wv = I.draw_strength(d["beta"].shape, 5100, d["beta"].dtype)
+    if case == "erase_only":
+        wv = torch.zeros_like(wv)
+    elif case == "write_only":
+        d["beta"] = torch.zeros_like(d["beta"])
+    _dec_check(kda, d, wv, io, "decoupled %s %s dk=%d dv=%d" % (case, io, dk, dv))
+
+
+def test_decoupled_c3_sampled_heads(kda):
+    """c3's full size with the write strength drawn independently of beta; the
+    oracle checks 2 whole heads."""
+    d = I.make_chunk_inputs(I.C3)
+    wv = I.draw_strength(d["beta"].shape, 5200, d["beta"].dtype)
+    _dec_check(kda, d, wv, "bf16", "decoupled c3 heads 0,31", heads=[0, 31])
+
+
+def test_decoupled_decode(kda):
+    cfg = I.DecodeConfig("dec-dec", "f32", "f32", B=5, H=3, dk=128, dv=128, steps=3, seed=2400)
+    S = I.make_decode_state(cfg)
+    Sg, Sref = S.to(DEV), f64(S)
+    steps = I.make_decode_step_inputs(cfg, 0, steps=3)
+    for s in range(3):
+        x = {n: t[s] for n, t in steps.items()}
+        wv = I.draw_strength(x["beta"].shape, 5300 + s, torch.float32)
+        o = kda.kda_decode_step_decoupled(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["log_alpha"].to(DEV),
+                                          x["beta"].to(DEV), wv.to(DEV), Sg)
+        Sn = np.zeros_like(Sref)
+        ro = np.zeros((cfg.B, cfg.H, cfg.dv))
+        # one step per (b, h) chain: the generalised recurrence with h0 = S
+        cu = np.arange(cfg.B + 1)
+        ro, Sn = oracle.gen_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["log_alpha"]), f64(x["beta"]), f64(wv),
+                                h0=Sref, cu_seqlens=cu)
+        Sref = Sn
+        assert_close(o.cpu(), ro, "f32", "decoupled decode o")
+    assert_close(Sg.cpu(), Sref, "f32", "decoupled decode S")
