@@ -78,6 +78,24 @@ int64_t max_chunks(const ChunkArgs &a) {
     return a.num_seqs * ((a.seq_len + kC - 1) / kC);
 }
 
+// A single long sequence (B = 1, no cu_seqlens) runs as consecutive segments of
+// whole chunks, each a prep pass then a state pass.  A segment holds at most
+// kSegRecords chunk-heads of records (about 190 MB), so the records the prep
+// kernel writes are still in the 256 MB last-level cache when the state kernel
+// reads them back; the state crosses each boundary in fp32 through the
+// workspace, so the result is bitwise that of a single pass.
+constexpr int64_t kSegRecords = 2048;
+
+// Chunks per segment, or 0 when the call runs as one pass.
+int64_t segment_chunks(const ChunkArgs &a) {
+    if (a.varlen || a.num_seqs != 1) return 0;
+    const int64_t per = kSegRecords / a.H;
+    const int64_t nch = (a.seq_len + kC - 1) / kC;
+    return (per >= 1 && nch > per) ? per : 0;
+}
+
+size_t carry_bytes(const ChunkArgs &a) { return ((size_t)a.H * a.d_k * a.d_v * 4 + 255) / 256 * 256; }
+
 // chunk_off[n] = number of chunks of sequences 0..n-1 (exclusive prefix sum of
 // ceil(L_n / 64)); chunk_off[N] = total.  One workgroup.
 __global__ __launch_bounds__(256) void chunk_plan_kernel(const int32_t *__restrict__ cu, int64_t N,
@@ -1042,19 +1060,18 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
         loader_role_loop<DK, DV, BV>(sm, cr, recs, H, tid - 512);
 }
 
+// One prep pass and one state pass over the tokens described by a, with the
+// records at recs.
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
-hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
-    uint8_t *ws = reinterpret_cast<uint8_t *>(a.workspace);
-    int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + kHeaderBytes);
-    uint8_t *recs = ws + kHeaderBytes + plan_bytes(a.num_seqs);
+hipError_t launch_pass(const ChunkArgs &a, int bv, int32_t *chunk_off, uint8_t *recs, hipStream_t st) {
     if (a.varlen)
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
     const int64_t nprep = max_chunks(a) * a.H;
     if (nprep > 0)
         hipLaunchKernelGGL((chunk_prep_kernel<DK, DV, IO, GT, PRO, GM, DEC>), dim3((unsigned)nprep), dim3(kThreads), 0,
                            st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha,
-                           (const GT *)a.beta, (const GT *)a.w_write, a.cu_seqlens, (const int32_t *)chunk_off, recs, a.num_seqs, a.seq_len,
-                           a.H, a.log_alpha_min);
+                           (const GT *)a.beta, (const GT *)a.w_write, a.cu_seqlens, (const int32_t *)chunk_off, recs,
+                           a.num_seqs, a.seq_len, a.H, a.log_alpha_min);
     const int64_t chains = a.num_seqs * (int64_t)a.H;
     // 32 value columns per workgroup only at d_k = 64: at d_k = 128 the loader
     // buffers and the 32-column state tiles do not fit the 16-wave register budget
@@ -1075,6 +1092,38 @@ hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
                            (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains,
                            a.log_alpha_min);
     return hipGetLastError();
+}
+
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
+hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
+    uint8_t *ws = reinterpret_cast<uint8_t *>(a.workspace);
+    int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + kHeaderBytes);
+    uint8_t *after_plan = ws + kHeaderBytes + plan_bytes(a.num_seqs);
+    const int64_t segc = segment_chunks(a);
+    if (segc == 0) return launch_pass<DK, DV, IO, GT, PRO, GM, DEC>(a, bv, chunk_off, after_plan, st);
+    // segments of one sequence: the state is carried in the workspace
+    float *carry = reinterpret_cast<float *>(after_plan);
+    uint8_t *recs = after_plan + carry_bytes(a);
+    const int64_t seg = segc * kC, H = a.H;
+    for (int64_t t0 = 0; t0 < a.seq_len; t0 += seg) {
+        const int64_t len = a.seq_len - t0 < seg ? a.seq_len - t0 : seg;
+        ChunkArgs s = a;
+        s.seq_len = len;
+        s.total_tokens = len;
+        s.q = (const IO *)a.q + t0 * H * DK;
+        s.k = (const IO *)a.k + t0 * H * DK;
+        s.v = (const IO *)a.v + t0 * H * DV;
+        s.o = (IO *)a.o + t0 * H * DV;
+        if (GM == kGatePerChannel) s.log_alpha = (const GT *)a.log_alpha + t0 * H * DK;
+        else if (GM == kGatePerHead) s.log_alpha = (const GT *)a.log_alpha + t0 * H;
+        s.beta = (const GT *)a.beta + t0 * H;
+        if (a.w_write) s.w_write = (const GT *)a.w_write + t0 * H;
+        s.h0 = t0 == 0 ? a.h0 : carry;
+        s.h_T = t0 + len >= a.seq_len ? a.h_T : carry;
+        const hipError_t e = launch_pass<DK, DV, IO, GT, PRO, GM, DEC>(s, bv, chunk_off, recs, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename GT, bool PRO, int GM, bool DEC>
@@ -1106,6 +1155,10 @@ size_t record_bytes(int d_k, int d_v) {
 
 size_t two_kernel_workspace_bytes(const ChunkArgs &a) {
     if (a.total_tokens <= 0) return 0;
+    const int64_t segc = segment_chunks(a);
+    if (segc > 0)
+        return kHeaderBytes + plan_bytes(a.num_seqs) + carry_bytes(a) +
+               (size_t)segc * a.H * record_bytes(a.d_k, a.d_v);
     return kHeaderBytes + plan_bytes(a.num_seqs) + (size_t)max_chunks(a) * a.H * record_bytes(a.d_k, a.d_v);
 }
 

@@ -65,8 +65,12 @@ const char *kda_last_hip_error(void);
  * operands: W and U0 (the UT transform already applied to the decayed keys and
  * to the values), the decayed queries and keys, the intra-chunk score block
  * and the per-channel decay scales -- about 92 KiB at d_k = d_v = 128, i.e.
- * about 1.4 KiB per token-head.  fp32 I/O needs none.  The size depends only
- * on the arguments, never on tensor contents.
+ * about 1.4 KiB per token-head.  A single sequence (B = 1, no cu_seqlens)
+ * longer than 2048 / H chunks runs in segments of that many chunks, so the
+ * workspace then holds one segment's records (at most 2048 chunk-heads, about
+ * 190 MB, sized to stay in the last-level cache) plus an fp32 state of
+ * H x d_k x d_v.  fp32 I/O needs none.  The size depends only on the
+ * arguments, never on tensor contents.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                     int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);

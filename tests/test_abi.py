@@ -45,10 +45,18 @@ def test_version_and_status_strings(kda):
 def test_workspace_size(kda):
     # bf16 I/O: one per-chunk record per (chunk, head) plus a small header;
     # fp32 I/O needs none; unsupported sizes report 0.
-    big = kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_BF16)
     # a record holds at least the decayed keys, queries and transposed keys
     # (3 x 64 x 128 bf16) and at most ~96 KiB per chunk-head
-    assert 1024 * 32 * (3 * 64 * 128 * 2) <= big <= 1024 * 32 * 96 * 1024 + 4096
+    two = kda.kda_chunk_fwd_workspace_size(2, 65536, 32, 128, 128, 0, kda.KDA_BF16)
+    assert 2 * 1024 * 32 * (3 * 64 * 128 * 2) <= two <= 2 * 1024 * 32 * 96 * 1024 + 4096
+    # one long sequence runs in segments of at most 2048 chunk-heads of records,
+    # plus the fp32 state carried between them
+    big = kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_BF16)
+    carry = 32 * 128 * 128 * 4
+    assert 2048 * (3 * 64 * 128 * 2) + carry <= big <= 2048 * 96 * 1024 + carry + 4096
+    # a sequence that fits one segment is one pass
+    one = kda.kda_chunk_fwd_workspace_size(1, 4096, 32, 128, 128, 0, kda.KDA_BF16)
+    assert 64 * 32 * (3 * 64 * 128 * 2) <= one <= 64 * 32 * 96 * 1024 + 4096
     assert kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_F32) == 0
     assert kda.kda_chunk_fwd_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
     # varlen: room for one partial chunk per sequence

@@ -501,3 +501,25 @@ def test_decoupled_decode(kda):
         Sref = Sn
         assert_close(o.cpu(), ro, "f32", "decoupled decode o")
     assert_close(Sg.cpu(), Sref, "f32", "decoupled decode S")
+
+
+# ------------------------------------------------------------------ long-sequence segments
+def test_long_sequence_segments(kda):
+    """A single long sequence runs as segments of 64 chunks at H = 32 (records
+    kept in the last-level cache): three segments, the last partial, with h0, a
+    near-reset across the first segment boundary (token path), and h_T aliasing
+    h0 on a second call."""
+    cfg = I.ChunkConfig("seg", "bf16", "bf16", H=32, dk=128, dv=128, T=2 * 4096 + 77, seed=61, h0=True)
+    d = I.make_chunk_inputs(cfg)
+    la = d["log_alpha"].clone()
+    la[4090:4100] = -30.0
+    d["log_alpha"] = la
+    heads = [0, 13, 31]
+    check_against_oracle(kda, d, "bf16", heads=heads, what="segments T=%d" % cfg.T)
+    # h_T written over h0 in place
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    o1, h1 = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=g["h0"])
+    hh = g["h0"].clone()
+    o2, h2 = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=hh, h_T=hh)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2) and h2.data_ptr() == hh.data_ptr()
