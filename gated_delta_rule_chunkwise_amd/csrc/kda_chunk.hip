@@ -1,4 +1,6 @@
 // kda_chunk.hip -- chunkwise KDA forward (prefill), one fused kernel.
+// This kernel serves fp32 I/O; bf16 I/O runs the prep + state kernels of
+// kda_chunk2.hip (LIBKDA_FUSED=1 selects this one for comparison).
 //
 // Method (KimiLinear article, section 3.1: intra-chunk part by matrix products,
 // inter-chunk part carried by the recurrent state; Kimi Linear abstract on the

@@ -27,6 +27,12 @@
 // Chunks whose in-chunk decay exceeds the matrix-core range are flagged by the
 // prep kernel and run token by token in the state kernel.
 //
+// Compile-time input variants of both kernels: PRO (raw projections mapped as
+// they are read), GM (gate per key channel, per token and head, or none) and
+// DEC (separate erase and write strengths); the chunk algebra is shared.  A
+// single long sequence runs as segments whose records stay in the last-level
+// cache between the two kernels (segment_chunks below).
+//
 // Record layout: matrix operands are stored in the order the state kernel's
 // lanes hold them, so that each wave-wide load reads one contiguous 1 KiB (or
 // 512 B) run.  A "fragment" is one 16x32 bf16 operand of the 16x16x32 matrix

@@ -23,6 +23,7 @@ constexpr int kDecodeThreads = 256;
 // (input prologue; lo is the floor of log alpha).  The reductions then run on
 // the raw q and k and are rescaled by the inverse norms, reduced alongside.
 // DEC: beta erases and wr writes: u = wr v - beta k^T(alpha S).
+// GM: alpha per key channel, one alpha per (b, h) for every row, or none (1).
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,

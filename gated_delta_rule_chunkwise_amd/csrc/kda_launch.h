@@ -1,5 +1,5 @@
 // Internal interface between the host-side C ABI (kda_api.cpp) and the HIP
-// launchers (kda_chunk.hip, kda_decode.hip).  Not part of the public ABI.
+// launchers (kda_chunk.hip, kda_chunk2.hip, kda_decode.hip).  Not part of the public ABI.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
