@@ -9,6 +9,11 @@ The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, per-token recurrence of
 the KimiLinear article, section 2.3, with the read-out o_t = S_t^T q_t).  This
 module only marshals numpy arrays into it.
 
+``bwd`` is the gradient of ``fwd`` (reverse-mode differentiation of the same
+recurrence), pinned by central finite differences of ``fwd``, by PyTorch fp64
+autograd through an independently written recurrence, and by the closed form
+of the frozen-state case.
+
 Pins: every function here is pinned by ``tests/test_oracle_pins.py`` against
 special cases that the pages' own equations fix (sections 2.1-2.3 of the
 KimiLinear article), a brute-force product of explicit transition matrices, a
@@ -59,6 +64,9 @@ def _load():
         lib.kda_oracle_prologue.argtypes = [dp, dp, dp, dp, i64, i64, ctypes.c_double,
                                              ctypes.c_double, dp, dp, dp, dp]
         lib.kda_oracle_prologue.restype = ctypes.c_int
+        lib.kda_oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, ip, i64, i64, i64, i64, dp, dp,
+                                       dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -169,6 +177,43 @@ def decode(q, k, v, log_alpha, beta, S, nthreads=None):
     if rc != 0:
         raise RuntimeError("kda_oracle_decode failed with code %d" % rc)
     return o, S_new
+
+
+def bwd(q, k, v, log_alpha, beta, d_o, h0=None, d_hT=None, cu_seqlens=None, nthreads=None):
+    """Gradient of the KDA forward (reverse-mode differentiation of the per-token
+    recurrence; ``kda_oracle_bwd`` in kda_oracle.c) for a loss whose gradients
+    with respect to o and h_T are d_o [T, H, dv] and d_hT [N, H, dk, dv] (None:
+    zero).  Returns (dq, dk, dv, dlog_alpha, dbeta, dh0) in fp64 with the input
+    shapes; dh0 is returned whether or not h0 was given."""
+    q = _f64(q)
+    if q.ndim != 3:
+        raise ValueError("q must be [T, H, dk]")
+    T, H, dk = q.shape
+    k = _f64(k, (T, H, dk))
+    la = _f64(log_alpha, (T, H, dk))
+    v = _f64(v)
+    if v.ndim != 3 or v.shape[:2] != (T, H):
+        raise ValueError("v must be [T, H, dv]")
+    dv = v.shape[2]
+    be = _f64(beta, (T, H))
+    do = _f64(d_o, (T, H, dv))
+    cu = _cu(cu_seqlens, T)
+    N = cu.size - 1
+    h0a = None if h0 is None else _f64(h0, (N, H, dk, dv))
+    dhT = None if d_hT is None else _f64(d_hT, (N, H, dk, dv))
+    dq = np.zeros((T, H, dk))
+    dk_ = np.zeros((T, H, dk))
+    dv_ = np.zeros((T, H, dv))
+    dla = np.zeros((T, H, dk))
+    db = np.zeros((T, H))
+    dh0 = np.zeros((N, H, dk, dv))
+    rc = _load().kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(h0a),
+                                _ptr(cu), N, H, dk, dv, _ptr(do), _ptr(dhT), _ptr(dq), _ptr(dk_),
+                                _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dh0),
+                                int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_bwd failed with code %d" % rc)
+    return dq, dk_, dv_, dla, db, dh0
 
 
 # Default eps of the L2 normalisation (the GPU entry points use the same value).

@@ -250,4 +250,225 @@ int kda_oracle_prologue(const double *q, const double *k, const double *a, const
     return 0;
 }
 
-int kda_oracle_version(void) { return 2; }
+/* Gradient of the KDA forward, for training.
+ *
+ * KimiLinear article (intl.cloud.baidu.com), sections 3 and 4.1: the chunkwise
+ * form exists to make training on long sequences efficient, and section 3.2
+ * notes that only a chunk-sized score block needs to be kept for the backward
+ * pass.  The pages give no backward formulas; the gradient is the plain one,
+ * reverse-mode differentiation of the per-token recurrence above (b = w =
+ * beta), for a scalar loss whose gradients with respect to o and h_T are given
+ * (d_o, d_hT; d_hT may be NULL for zero).
+ *
+ * Forward step t, with a = exp(log_alpha_t):
+ *     Sd = Diag(a) S_{t-1};  r = Sd^T k_t;  u = beta_t (v_t - r);
+ *     S_t = Sd + k_t u^T;    o_t = S_t^T q_t.
+ * Reverse step t, with dS = dL/dS_t accumulated from later tokens:
+ *     dS += q_t do_t^T;            dq_t = S_t do_t;
+ *     du = dS^T k_t;               dk_t = dS u;
+ *     dbeta_t = du . (v_t - r);    dv_t = beta_t du;
+ *     dr = -beta_t du;             dk_t += Sd dr;
+ *     dSd = dS + k_t dr^T;         dlog_alpha_t[c] = sum_j dSd[c,j] Sd[c,j];
+ *     dS = Diag(a) dSd             (= dL/dS_{t-1});
+ * and dh0 = dS once the sequence's first token is done.
+ *
+ * The reverse pass needs S_{t-1} and S_t for every t.  They are recomputed
+ * from checkpoints (the state before every K-th token, K ~ sqrt(length)),
+ * one block of K tokens at a time, by the same forward step in the same
+ * order, so every value is the one a full forward pass gives; this only bounds
+ * the memory.
+ */
+typedef struct {
+    const double *q, *k, *v, *log_alpha, *beta, *h0, *d_o, *d_hT;
+    const int64_t *cu_seqlens;
+    int64_t num_seqs, H, dk, dv;
+    double *dq, *dkk, *dvv, *dla, *dbeta, *dh0;
+    int64_t next_chain;
+    pthread_mutex_t mu;
+    int failed;
+} oracle_bwd_job;
+
+/* S <- state after token t, from S = state before token t (forward step). */
+static void bwd_fwd_step(const oracle_bwd_job *J, int64_t t, int64_t h, double *S, double *r)
+{
+    const int64_t H = J->H, dk = J->dk, dv = J->dv;
+    const double *kt = J->k + (t * H + h) * dk;
+    const double *vt = J->v + (t * H + h) * dv;
+    const double *lat = J->log_alpha + (t * H + h) * dk;
+    const double bt = J->beta[t * H + h];
+    for (int64_t c = 0; c < dk; ++c) {
+        const double a = exp(lat[c]);
+        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] *= a;
+    }
+    for (int64_t j = 0; j < dv; ++j) r[j] = 0.0;
+    for (int64_t c = 0; c < dk; ++c)
+        for (int64_t j = 0; j < dv; ++j) r[j] += kt[c] * S[c * dv + j];
+    for (int64_t c = 0; c < dk; ++c)
+        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += kt[c] * (bt * (vt[j] - r[j]));
+}
+
+static int run_bwd_chain(const oracle_bwd_job *J, int64_t n, int64_t h)
+{
+    const int64_t H = J->H, dk = J->dk, dv = J->dv, M = dk * dv;
+    const int64_t t0 = J->cu_seqlens[n], L = J->cu_seqlens[n + 1] - t0;
+    int64_t K = 1;
+    while (K * K < L) ++K;
+    const int64_t nblk = L > 0 ? (L + K - 1) / K : 0;
+    double *ck = (double *)malloc(sizeof(double) * (size_t)((nblk + 1) * M));  /* checkpoints */
+    double *blk = (double *)malloc(sizeof(double) * (size_t)((K + 1) * M));    /* states of one block */
+    double *dS = (double *)malloc(sizeof(double) * (size_t)M);
+    double *Sd = (double *)malloc(sizeof(double) * (size_t)M);
+    double *r = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *du = (double *)malloc(sizeof(double) * (size_t)dv);
+    int rc = 0;
+    if (!ck || !blk || !dS || !Sd || !r || !u || !du) { rc = -1; goto done; }
+
+    /* forward: checkpoint the state before tokens 0, K, 2K, ... */
+    if (J->h0) memcpy(ck, J->h0 + (n * H + h) * M, sizeof(double) * (size_t)M);
+    else memset(ck, 0, sizeof(double) * (size_t)M);
+    for (int64_t b = 0; b < nblk; ++b) {
+        memcpy(ck + (b + 1) * M, ck + b * M, sizeof(double) * (size_t)M);
+        for (int64_t i = b * K; i < L && i < (b + 1) * K; ++i) bwd_fwd_step(J, t0 + i, h, ck + (b + 1) * M, r);
+    }
+
+    if (J->d_hT) memcpy(dS, J->d_hT + (n * H + h) * M, sizeof(double) * (size_t)M);
+    else memset(dS, 0, sizeof(double) * (size_t)M);
+
+    for (int64_t b = nblk - 1; b >= 0; --b) {
+        const int64_t i0 = b * K, i1 = (b + 1) * K < L ? (b + 1) * K : L;
+        /* blk[i - i0] = state before token i, for i0 <= i <= i1 */
+        memcpy(blk, ck + b * M, sizeof(double) * (size_t)M);
+        for (int64_t i = i0; i < i1; ++i) {
+            memcpy(blk + (i - i0 + 1) * M, blk + (i - i0) * M, sizeof(double) * (size_t)M);
+            bwd_fwd_step(J, t0 + i, h, blk + (i - i0 + 1) * M, r);
+        }
+        for (int64_t i = i1 - 1; i >= i0; --i) {
+            const int64_t t = t0 + i;
+            const double *Sp = blk + (i - i0) * M, *St = blk + (i - i0 + 1) * M;
+            const double *qt = J->q + (t * H + h) * dk;
+            const double *kt = J->k + (t * H + h) * dk;
+            const double *vt = J->v + (t * H + h) * dv;
+            const double *lat = J->log_alpha + (t * H + h) * dk;
+            const double *dot = J->d_o + (t * H + h) * dv;
+            const double bt = J->beta[t * H + h];
+            double *dqt = J->dq + (t * H + h) * dk;
+            double *dkt = J->dkk + (t * H + h) * dk;
+            double *dvt = J->dvv + (t * H + h) * dv;
+            double *dlat = J->dla + (t * H + h) * dk;
+
+            /* recompute Sd, r, u of this step */
+            for (int64_t c = 0; c < dk; ++c) {
+                const double a = exp(lat[c]);
+                for (int64_t j = 0; j < dv; ++j) Sd[c * dv + j] = a * Sp[c * dv + j];
+            }
+            for (int64_t j = 0; j < dv; ++j) r[j] = 0.0;
+            for (int64_t c = 0; c < dk; ++c)
+                for (int64_t j = 0; j < dv; ++j) r[j] += kt[c] * Sd[c * dv + j];
+            for (int64_t j = 0; j < dv; ++j) u[j] = bt * (vt[j] - r[j]);
+
+            /* read-out o_t = S_t^T q_t */
+            for (int64_t c = 0; c < dk; ++c)
+                for (int64_t j = 0; j < dv; ++j) dS[c * dv + j] += qt[c] * dot[j];
+            for (int64_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) acc += St[c * dv + j] * dot[j];
+                dqt[c] = acc;
+            }
+            /* write S_t = Sd + k u^T */
+            for (int64_t j = 0; j < dv; ++j) du[j] = 0.0;
+            for (int64_t c = 0; c < dk; ++c)
+                for (int64_t j = 0; j < dv; ++j) du[j] += dS[c * dv + j] * kt[c];
+            for (int64_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) acc += dS[c * dv + j] * u[j];
+                dkt[c] = acc;
+            }
+            /* u = beta (v - r) */
+            double db = 0.0;
+            for (int64_t j = 0; j < dv; ++j) db += du[j] * (vt[j] - r[j]);
+            J->dbeta[t * H + h] = db;
+            for (int64_t j = 0; j < dv; ++j) dvt[j] = bt * du[j];
+            /* r = Sd^T k: dr = -beta du */
+            for (int64_t j = 0; j < dv; ++j) du[j] = -bt * du[j];
+            for (int64_t c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) acc += Sd[c * dv + j] * du[j];
+                dkt[c] += acc;
+            }
+            /* dSd = dS + k dr^T; Sd = Diag(a) S_{t-1} */
+            for (int64_t c = 0; c < dk; ++c) {
+                const double a = exp(lat[c]);
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    const double g = dS[c * dv + j] + kt[c] * du[j];
+                    acc += g * Sd[c * dv + j];
+                    dS[c * dv + j] = a * g;
+                }
+                dlat[c] = acc;
+            }
+        }
+    }
+    if (J->dh0) memcpy(J->dh0 + (n * H + h) * M, dS, sizeof(double) * (size_t)M);
+done:
+    free(ck); free(blk); free(dS); free(Sd); free(r); free(u); free(du);
+    return rc;
+}
+
+static void *bwd_worker(void *arg)
+{
+    oracle_bwd_job *J = (oracle_bwd_job *)arg;
+    const int64_t total = J->num_seqs * J->H;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        const int64_t id = J->next_chain++;
+        pthread_mutex_unlock(&J->mu);
+        if (id >= total) break;
+        if (run_bwd_chain(J, id / J->H, id % J->H) != 0) {
+            pthread_mutex_lock(&J->mu);
+            J->failed = 1;
+            pthread_mutex_unlock(&J->mu);
+        }
+    }
+    return NULL;
+}
+
+/* Layouts as for kda_oracle_fwd; d_o like o, d_hT and dh0 like h0.  Outputs
+ * dq, dk_out, dlog_alpha: [T_total, H, dk]; dv_out: [T_total, H, dv];
+ * dbeta: [T_total, H]; dh0 may be NULL.  Returns 0, -1 (no memory) or -2. */
+int kda_oracle_bwd(const double *q, const double *k, const double *v,
+                   const double *log_alpha, const double *beta, const double *h0,
+                   const int64_t *cu_seqlens, int64_t num_seqs, int64_t H,
+                   int64_t dk, int64_t dv, const double *d_o, const double *d_hT,
+                   double *dq, double *dk_out, double *dv_out, double *dlog_alpha,
+                   double *dbeta, double *dh0, int nthreads)
+{
+    if (H <= 0 || dk <= 0 || dv <= 0) return -2;
+    if (check_seqlens(cu_seqlens, num_seqs) != 0) return -2;
+    if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !dq ||
+                                     !dk_out || !dv_out || !dlog_alpha || !dbeta))
+        return -2;
+    oracle_bwd_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = beta; J.h0 = h0;
+    J.d_o = d_o; J.d_hT = d_hT; J.cu_seqlens = cu_seqlens; J.num_seqs = num_seqs;
+    J.H = H; J.dk = dk; J.dv = dv;
+    J.dq = dq; J.dkk = dk_out; J.dvv = dv_out; J.dla = dlog_alpha; J.dbeta = dbeta; J.dh0 = dh0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 1024) nthreads = 1024;
+    pthread_mutex_init(&J.mu, NULL);
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid) { pthread_mutex_destroy(&J.mu); return -1; }
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, bwd_worker, &J) != 0) break;
+        ++started;
+    }
+    if (started == 0) bwd_worker(&J);
+    for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+    free(tid);
+    pthread_mutex_destroy(&J.mu);
+    return J.failed ? -1 : 0;
+}
+
+int kda_oracle_version(void) { return 3; }

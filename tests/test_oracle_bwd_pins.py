@@ -1,0 +1,148 @@
+"""Pins of the oracle's backward (``oracle.bwd``) against what does not depend
+on its own reverse-mode code.
+
+The backward is the gradient of the KDA forward (the per-token recurrence of
+the KimiLinear article, section 2.3; the pages motivate the chunkwise form by
+training throughput, sections 3 and 4.1).  It is pinned by
+  * central finite differences of the forward oracle, on every input;
+  * PyTorch fp64 autograd through a separately written recurrence;
+  * closed forms: the frozen state (alpha = 1, beta = 0) and linear attention
+    with orthonormal keys (alpha = 1, beta = 1, h0 = 0, section 2.1).
+A dropped term (the erase path into dk, the decay into dlog_alpha, the write
+into dbeta), a wrong sign or a missing d_hT/dh0 link fails at least one.
+"""
+import numpy as np
+import pytest
+import torch
+
+rng0 = np.random.default_rng
+
+
+def _case(T, H, dk, dv, N, seed, la_scale=1.0):
+    r = rng0(seed)
+    q = r.standard_normal((T, H, dk))
+    k = r.standard_normal((T, H, dk)) / np.sqrt(dk)
+    v = r.standard_normal((T, H, dv))
+    la = -la_scale * r.uniform(0.01, 1.0, (T, H, dk))
+    b = r.uniform(0.0, 1.0, (T, H))
+    h0 = r.standard_normal((N, H, dk, dv))
+    return q, k, v, la, b, h0
+
+
+def test_bwd_matches_central_finite_differences(oracle_mod):
+    """Every gradient, element by element, against (L(x+e) - L(x-e)) / 2e of
+    the forward oracle, with an empty sequence in the batch."""
+    T, H, dk, dv = 9, 2, 3, 2
+    cu = np.array([0, 5, 5, 9])
+    N = 3
+    x = list(_case(T, H, dk, dv, N, 11))
+    r = rng0(12)
+    Wo = r.standard_normal((T, H, dv))
+    Wh = r.standard_normal((N, H, dk, dv))
+
+    def loss(a):
+        o, hT = oracle_mod.fwd(*a[:5], h0=a[5], cu_seqlens=cu)
+        return float((o * Wo).sum() + (hT * Wh).sum())
+
+    g = oracle_mod.bwd(*x[:5], Wo, h0=x[5], d_hT=Wh, cu_seqlens=cu)
+    eps = 1e-6
+    for ai in range(6):
+        fd = np.zeros_like(x[ai])
+        for idx in np.ndindex(x[ai].shape):
+            a = [y.copy() for y in x]
+            a[ai][idx] += eps
+            lp = loss(a)
+            a[ai][idx] -= 2 * eps
+            fd[idx] = (lp - loss(a)) / (2 * eps)
+        np.testing.assert_allclose(g[ai], fd, rtol=1e-6, atol=1e-7, err_msg="input %d" % ai)
+
+
+def _torch_recurrence(q, k, v, la, b, h0, cu):
+    """The forward written again with torch ops, vectorised over heads."""
+    outs, hts = [], []
+    for n in range(len(cu) - 1):
+        S = h0[n]
+        for t in range(int(cu[n]), int(cu[n + 1])):
+            S = torch.exp(la[t]).unsqueeze(-1) * S
+            r = torch.einsum("hc,hcj->hj", k[t], S)
+            u = b[t].unsqueeze(-1) * (v[t] - r)
+            S = S + k[t].unsqueeze(-1) * u.unsqueeze(-2)
+            outs.append(torch.einsum("hc,hcj->hj", q[t], S))
+        hts.append(S)
+    return torch.stack(outs), torch.stack(hts)
+
+
+@pytest.mark.parametrize("la_scale", [1.0, 4.0])
+def test_bwd_matches_torch_autograd(oracle_mod, la_scale):
+    T, H, dk, dv = 40, 2, 8, 6
+    cu = np.array([0, 17, 40])
+    N = 2
+    x = _case(T, H, dk, dv, N, 21, la_scale)
+    r = rng0(22)
+    Wo = r.standard_normal((T, H, dv))
+    Wh = r.standard_normal((N, H, dk, dv))
+    tx = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in x]
+    o, hT = _torch_recurrence(*tx, cu)
+    ((o * torch.tensor(Wo)).sum() + (hT * torch.tensor(Wh)).sum()).backward()
+    g = oracle_mod.bwd(*x[:5], Wo, h0=x[5], d_hT=Wh, cu_seqlens=cu)
+    for ai in range(6):
+        ref = tx[ai].grad.numpy()
+        np.testing.assert_allclose(g[ai], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max(),
+                                   err_msg="input %d" % ai)
+
+
+def test_bwd_frozen_state_closed_form(oracle_mod):
+    """alpha = 1, beta = 0: S_t = h0 for all t and o_t = h0^T q_t.  With
+    G_t = d_hT + sum_{s >= t} q_s do_s^T (the state gradient seen by token t):
+    dq_t = h0 do_t, dk = dv = 0, dh0 = G_0, dlog_alpha_t[c] = sum_j G_t[c,j] h0[c,j],
+    dbeta_t = (G_t^T k_t) . (v_t - h0^T k_t)."""
+    T, H, dk, dv = 12, 2, 5, 4
+    q, k, v, _, _, h0 = _case(T, H, dk, dv, 1, 31)
+    la = np.zeros((T, H, dk))
+    b = np.zeros((T, H))
+    r = rng0(32)
+    do = r.standard_normal((T, H, dv))
+    dhT = r.standard_normal((1, H, dk, dv))
+    dq, dk_, dv_, dla, db, dh0 = oracle_mod.bwd(q, k, v, la, b, do, h0=h0, d_hT=dhT)
+    G = dhT[0].copy()
+    for t in range(T - 1, -1, -1):
+        G = G + np.einsum("hc,hj->hcj", q[t], do[t])
+        np.testing.assert_allclose(dq[t], np.einsum("hcj,hj->hc", h0[0], do[t]), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dla[t], np.einsum("hcj,hcj->hc", G, h0[0]), rtol=1e-12, atol=1e-12)
+        du = np.einsum("hcj,hc->hj", G, k[t])
+        rr = np.einsum("hcj,hc->hj", h0[0], k[t])
+        np.testing.assert_allclose(db[t], np.einsum("hj,hj->h", du, v[t] - rr), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dh0[0], G, rtol=1e-12, atol=1e-12)
+    assert np.all(dk_ == 0.0) and np.all(dv_ == 0.0)
+
+
+def test_bwd_linear_attention_closed_form(oracle_mod):
+    """alpha = 1, beta = 1, orthonormal keys, h0 = 0 (section 2.1's linear
+    attention): o_t = sum_{i <= t} (q_t . k_i) v_i, so
+    dq_t = sum_{i <= t} k_i (v_i . do_t) and dv_i = sum_{t >= i} (q_t . k_i) do_t."""
+    T, H, dk, dv = 8, 2, 8, 5
+    r = rng0(41)
+    k = np.zeros((T, H, dk))
+    for h in range(H):
+        Qm, _ = np.linalg.qr(r.standard_normal((dk, dk)))
+        k[:, h, :] = Qm[:, :T].T
+    q = r.standard_normal((T, H, dk))
+    v = r.standard_normal((T, H, dv))
+    do = r.standard_normal((T, H, dv))
+    dq, _, dv_, _, _, _ = oracle_mod.bwd(q, k, v, np.zeros((T, H, dk)), np.ones((T, H)), do)
+    qk = np.einsum("thc,ihc->hti", q, k)            # [H, t, i] = q_t . k_i
+    mask = np.tril(np.ones((T, T)))
+    ref_dq = np.einsum("ti,ihc,ihj,thj->thc", mask, k, v, do)
+    ref_dv = np.einsum("hti,thj->ihj", qk * mask, do)
+    np.testing.assert_allclose(dq, ref_dq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv_, ref_dv, rtol=1e-10, atol=1e-12)
+
+
+def test_bwd_zero_length_sequence_passes_state_gradient(oracle_mod):
+    """A zero-length sequence has h_T = h0, so dh0 = d_hT."""
+    H, dk, dv = 2, 4, 3
+    x = _case(3, H, dk, dv, 2, 51)
+    dhT = rng0(52).standard_normal((2, H, dk, dv))
+    do = rng0(53).standard_normal((3, H, dv))
+    g = oracle_mod.bwd(*x[:5], do, h0=x[5], d_hT=dhT, cu_seqlens=[0, 0, 3])
+    np.testing.assert_array_equal(g[5][0], dhT[0])
