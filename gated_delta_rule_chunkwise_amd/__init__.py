@@ -15,7 +15,9 @@ Entry points (same names as the C ABI):
     kda_gdn_decode_step(q, k, v, log_alpha_or_None, beta, S, o=None)
     kda_chunk_fwd_decoupled(q, k, v, log_alpha, b_erase, w_write, ...)
     kda_decode_step_decoupled(q, k, v, log_alpha, b_erase, w_write, S, o=None)
-    kda_chunk_fwd_workspace_size(...), kda_status_string(code), kda_abi_version()
+    kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_seqlens=None, ...)
+    kda_chunk_fwd_workspace_size(...), kda_chunk_bwd_workspace_size(...),
+    kda_status_string(code), kda_abi_version()
 """
 from __future__ import annotations
 
@@ -30,7 +32,8 @@ KDA_F32, KDA_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
                     "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step",
                     "kda_chunk_fwd_prologue", "kda_decode_step_prologue", "kda_gdn_chunk_fwd",
-                    "kda_gdn_decode_step", "kda_chunk_fwd_decoupled", "kda_decode_step_decoupled")
+                    "kda_gdn_decode_step", "kda_chunk_fwd_decoupled", "kda_decode_step_decoupled",
+                    "kda_chunk_bwd_workspace_size", "kda_chunk_bwd")
 
 _lib = None
 
@@ -84,6 +87,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step_decoupled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                               ctypes.c_int, vp]
     lib.kda_decode_step_decoupled.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_size.argtypes = list(lib.kda_chunk_fwd_workspace_size.argtypes)
+    lib.kda_chunk_bwd_workspace_size.restype = sz
+    lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -243,6 +251,68 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
     if squeeze:
         o = o.squeeze(0)
     return o, h_T
+
+
+def kda_chunk_bwd_workspace_size(B, T, H, d_k, d_v, num_seqs=0, io_dtype=KDA_BF16) -> int:
+    return int(load_library().kda_chunk_bwd_workspace_size(B, T, H, d_k, d_v, num_seqs, io_dtype))
+
+
+def kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_seqlens=None, *,
+                  want_grad_h0=True, workspace=None):
+    """Gradients of kda_chunk_fwd (see kda_chunk_bwd in include/kda.h).
+
+    Inputs as for kda_chunk_fwd plus grad_o (like o) and grad_hT (like h_T, or
+    None).  Returns (dq, dk, dv, dlog_alpha, dbeta, dh0); dh0 is None when
+    want_grad_h0 is False."""
+    import torch
+    lib = load_library()
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v, log_alpha, beta, grad_o = (x.unsqueeze(0) for x in (q, k, v, log_alpha, beta, grad_o))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("grad_o", grad_o)):
+        _check_dev(name, t, dev)
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:3] != (B, T, H) \
+            or beta.shape != (B, T, H) or grad_o.shape != v.shape:
+        raise ValueError("shape mismatch among q, k, v, log_alpha, beta, grad_o")
+    if k.dtype != q.dtype or v.dtype != q.dtype or grad_o.dtype != q.dtype or beta.dtype != log_alpha.dtype:
+        raise TypeError("q, k, v, grad_o share one dtype; log_alpha and beta share one dtype")
+    if cu_seqlens is not None:
+        _check_dev("cu_seqlens", cu_seqlens, dev)
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (("h0", h0), ("grad_hT", grad_hT)):
+        if t is not None:
+            _check_dev(name, t, dev)
+            if t.dtype != torch.float32 or tuple(t.shape) != (N, H, dk, dv):
+                raise ValueError("%s must be fp32 [N, H, d_k, d_v]" % name)
+    dq = torch.empty_like(q)
+    dk_ = torch.empty_like(k)
+    dv_ = torch.empty_like(v)
+    dla = torch.empty_like(log_alpha)
+    db = torch.empty_like(beta)
+    dh0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_grad_h0 else None
+    io, gt = _dtype_code(q), _dtype_code(beta)
+    nseq = N if cu_seqlens is not None else 0
+    ws_bytes = kda_chunk_bwd_workspace_size(B, T, H, dk, dv, nseq, io)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                           _ptr(cu_seqlens), nseq, _ptr(grad_o), _ptr(grad_hT), _ptr(dq), _ptr(dk_),
+                           _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dh0), B, T, H, dk, dv, io, gt,
+                           _ptr(workspace), ws_len, _stream_of(q))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_bwd", kda_last_hip_error())
+    if squeeze:
+        dq, dk_, dv_, dla, db = (x.squeeze(0) for x in (dq, dk_, dv_, dla, db))
+    return dq, dk_, dv_, dla, db, dh0
 
 
 def kda_decode_step(q, k, v, log_alpha, beta, S, o=None):

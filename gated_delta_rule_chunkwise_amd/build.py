@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk2.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk2.hip", "kda_decode.hip", "kda_bwd.hip"]
 
 # Packed fp32 VALU forms are kept out of the device code (see the build notes in
 # the design document); hipcc's host pass warns that it does not know the feature.

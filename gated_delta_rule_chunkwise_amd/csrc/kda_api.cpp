@@ -153,6 +153,71 @@ kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void 
                             stream, false, 0.f, 0);
 }
 
+size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                    int32_t num_seqs, kda_dtype_t io_dtype) {
+    if (B <= 0 || T < 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
+    if (!valid_dtype(io_dtype)) return 0;
+    if (num_seqs < 0 || (num_seqs > 0 && B != 1)) return 0;
+    kda::BwdArgs a = {};
+    a.varlen = num_seqs > 0;
+    a.num_seqs = num_seqs > 0 ? num_seqs : B;
+    a.seq_len = T;
+    a.total_tokens = (int64_t)B * T;
+    a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.io_bf16 = io_dtype == KDA_BF16;
+    return kda::chunk_bwd_workspace_bytes(a);
+}
+
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                           const void *grad_o, const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
+                           void *grad_log_alpha, void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (!sizes_fit((int64_t)B * T, H, (d_k > d_v ? d_k : d_v))) return KDA_ERR_INVALID_ARGUMENT;
+    int64_t N;
+    if (cu_seqlens) {
+        if (B != 1 || num_seqs <= 0) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned_to(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
+        N = num_seqs;
+    } else {
+        if (num_seqs != 0 && num_seqs != B) return KDA_ERR_INVALID_ARGUMENT;
+        N = B;
+    }
+    if (!sizes_fit(N, H, (int64_t)d_k * d_v)) return KDA_ERR_INVALID_ARGUMENT;
+    const bool have_tokens = (int64_t)B * T > 0;
+    if (have_tokens) {
+        const void *need16[] = {q, k, v, log_alpha, grad_o, grad_q, grad_k, grad_v, grad_log_alpha};
+        for (const void *p : need16)
+            if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARGUMENT;
+        if (!beta || !grad_beta || !aligned_to(beta, dsize(gate_dtype)) || !aligned_to(grad_beta, dsize(gate_dtype)))
+            return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((h0 && !aligned16(h0)) || (grad_hT && !aligned16(grad_hT)) || (grad_h0 && !aligned16(grad_h0)))
+        return KDA_ERR_INVALID_ARGUMENT;
+    kda::BwdArgs a = {};
+    a.varlen = cu_seqlens != nullptr;
+    a.num_seqs = N; a.seq_len = T; a.total_tokens = (int64_t)B * T;
+    a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
+    const size_t need = kda::chunk_bwd_workspace_bytes(a);
+    if (workspace_bytes < need || !workspace) return KDA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!have_tokens && !grad_h0) return KDA_OK;  // nothing to compute or write
+
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0; a.cu_seqlens = cu_seqlens;
+    a.d_o = grad_o; a.d_hT = grad_hT;
+    a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = grad_log_alpha; a.dbeta = grad_beta;
+    a.dh0 = grad_h0;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    g_hip_error[0] = '\0';
+    if (kda::launch_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -1,0 +1,894 @@
+// kda_bwd.hip -- chunkwise KDA backward: gradients with respect to q, k, v,
+// log_alpha, beta and h0, given those of o and h_T.
+//
+// The KimiLinear article motivates the chunkwise form by training throughput
+// (sections 3 and 4.1) and notes that only a chunk-sized score block has to be
+// kept per chunk for the backward pass (section 3.2).  The gradient is that of
+// the forward recurrence (section 2.3); here it is taken through the chunk form
+// of the forward.  Per chunk, with the in-chunk cumsum G of log alpha, its
+// total g_n, the anchor m = g_n / 2 and the decayed operands
+//     QA = Q.e^{G-m},  KA = K.e^{G-m},  KI = K.e^{m-G},
+//     M = strictly-lower(KA KI^T),  A = diag(beta) M,  T = (I + A)^{-1},
+//     P = lower(QA KI^T),  W = T diag(beta) KA,
+// and S' = Diag(e^m) S for the chunk's start state S, the forward is
+//     X = V - KA S',  U = T diag(beta) X,  O = QA S' + P U,
+//     S_next = Diag(e^{g_n}) S + Diag(e^{g_n-m}) KI^T U.
+// Given dO and dS_next, reverse-mode differentiation of these lines gives
+//     dU  = P^T dO + KI Diag(e^{g_n-m}) dS_next
+//     dS  = Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS_next
+//     dY  = T^T dU,  dV = diag(beta) dY,  dA = -strictly-lower(dY U^T)
+//     dP  = lower(dO U^T),  dM = diag(beta) dA
+//     dQA = dO S'^T + dP KI
+//     dKA = -diag(beta) dY S'^T + dM KI
+//     dKI = dP^T QA + dM^T KA + Diag-cols(e^{g_n-m}) (U dS_next^T)
+//     dbeta_r = sum_j dY[r,j] X[r,j] + sum_i dA[r,i] M[r,i]
+//     dQ = dQA.e^{G-m},  dK = dKA.e^{G-m} + dKI.e^{m-G}
+//     dG = dQA.QA + dKA.KA - dKI.KI
+//     dg_n[c] = e^{g_n-m}[c] (sum_j dS_next[c,j] S'[c,j] + sum_r (U dS_next^T)[r,c] KI[r,c])
+//     dlog_alpha[t,c] = sum_{r >= t} dG[r,c] + dg_n[c]
+// (the anchor m cancels from every result, so it is held fixed; g_n enters
+// through e^{g_n} and e^{g_n-m}).
+//
+// Four kernels, all in fp32 on the fp32 matrix cores:
+//   bwd_prep_kernel    per (chunk, head), all in parallel: QA, KI, W, T, P, M
+//                      and the anchor factors into a record per chunk-head;
+//   bwd_fwd_state      per (sequence, head, 16 value columns): replays the
+//                      state recurrence, storing each chunk's start state and U;
+//   bwd_rev_state      same grid, chunks in reverse: the state gradient at each
+//                      chunk's end and dU; dh0 after the first chunk;
+//   bwd_grad_kernel    per (chunk, head), all in parallel: everything else,
+//                      with the d_v contractions accumulated over 16-column
+//                      blocks in registers.
+// The value columns of the state evolve independently, so the two sequential
+// passes split d_v across workgroups; the gradients of q, k, log alpha and
+// beta sum over all columns and are formed per chunk-head in one workgroup,
+// so no cross-workgroup reduction (and no atomic) is needed: results are
+// bitwise deterministic.
+//
+// Range: the anchored factors e^{+-(G-m)} reach e^{D/2}, D = max_c(-g_n[c]).
+// A chunk with D above about 160 (log2 units: kBwdMaxRange2) would overflow
+// fp32; the prep kernel flags it, and every gradient of that sequence and head
+// (dh0 included) comes out NaN: a loud result rather than a wrong one.
+#include "kda_device.h"
+#include "kda_launch.h"
+#include "kda_plan.h"
+
+#include <stdio.h>
+
+namespace kda {
+namespace {
+
+constexpr int kB = kPlanChunk;                    // chunk length, 64
+constexpr float kBL2E = 1.4426950408889634f;
+constexpr float kBwdMaxRange2 = 230.f;            // max in-chunk decay, log2 units
+constexpr int kBV = 16;                           // value columns per block
+
+// D(16x16) += A(16x4) B(4x16), fp32.  Lane l holds A[l%16][l/16],
+// B[l/16][l%16] and D[4*(l/16) + e][l%16], e = 0..3.
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += A B over one 16x16 tile, K a multiple of 4, with
+// A(i, k) = a[i*AI + k*AK] and B(k, j) = b[k*BK + j*BJ].
+template <int K, int AI, int AK, int BK, int BJ>
+__device__ __forceinline__ f32x4_t mm(f32x4_t acc, const float *a, const float *b, int lane) {
+    const float *pa = a + (lane & 15) * AI + (lane >> 4) * AK;
+    const float *pb = b + (lane >> 4) * BK + (lane & 15) * BJ;
+#pragma unroll
+    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * AK], pb[k * BK], acc);
+    return acc;
+}
+
+__device__ __forceinline__ int acc_row(int lane, int e) { return 4 * (lane >> 4) + e; }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
+
+// Lower 16x16 blocks (R, I), I <= R, of a 64x64 chunk matrix, in order
+// (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3).
+__device__ __forceinline__ void low_tile(int idx, int &R, int &I) {
+    R = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
+    I = idx - (R * (R + 1)) / 2;
+}
+
+// Per chunk-head record (fp32, row-major, offsets in floats).
+template <int DK> struct BRec {
+    static constexpr size_t QA = 0;
+    static constexpr size_t KI = QA + (size_t)kB * DK;
+    static constexpr size_t W = KI + (size_t)kB * DK;
+    static constexpr size_t T = W + (size_t)kB * DK;
+    static constexpr size_t P = T + kB * kB;
+    static constexpr size_t M = P + kB * kB;
+    static constexpr size_t EM = M + kB * kB;     // e^m
+    static constexpr size_t EG = EM + DK;         // e^{g_n}
+    static constexpr size_t EGM = EG + DK;        // e^{g_n - m}
+    static constexpr size_t FLAG = EGM + DK;      // nonzero: decay out of range
+    static constexpr size_t FLOATS = (FLAG + 1 + 63) / 64 * 64;
+};
+
+struct BwdLayout {
+    int64_t nch;                 // chunk slots (upper bound over sequences)
+    size_t plan, sflag, rec, sc, uc, dsc, duc, total;
+};
+
+int64_t bwd_max_chunks(const BwdArgs &a) {
+    if (a.varlen) return (a.total_tokens + kB - 1) / kB + a.num_seqs;
+    return a.num_seqs * ((a.seq_len + kB - 1) / kB);
+}
+
+template <int DK> size_t rec_floats() { return BRec<DK>::FLOATS; }
+
+BwdLayout bwd_layout(const BwdArgs &a) {
+    BwdLayout L;
+    L.nch = bwd_max_chunks(a);
+    const size_t ch = (size_t)L.nch * a.H;
+    const size_t recf = a.d_k == 128 ? rec_floats<128>() : rec_floats<64>();
+    L.plan = 0;
+    L.sflag = plan_bytes(a.num_seqs);                        // [N, H] fp32: sequence out of range
+    L.rec = L.sflag + ((size_t)a.num_seqs * a.H * 4 + 255) / 256 * 256;
+    L.sc = L.rec + ch * recf * 4;
+    L.uc = L.sc + ch * a.d_k * a.d_v * 4;
+    L.dsc = L.uc + ch * kB * a.d_v * 4;
+    L.duc = L.dsc + ch * a.d_k * a.d_v * 4;
+    L.total = L.duc + ch * kB * a.d_v * 4;
+    return L;
+}
+
+// Token range [bos, eos) and first chunk slot of sequence n.
+__device__ __forceinline__ void seq_range(int64_t n, const int32_t *__restrict__ cu,
+                                          const int32_t *__restrict__ chunk_off, int64_t T, int64_t &bos,
+                                          int64_t &eos, int64_t &slot0) {
+    if (cu) {
+        bos = cu[n];
+        eos = cu[n + 1];
+        slot0 = chunk_off[n];
+    } else {
+        bos = n * T;
+        eos = bos + T;
+        slot0 = n * ((T + kB - 1) / kB);
+    }
+}
+
+// Copies a rows x COLS fp32 block (dense, row-major) from global memory into an
+// LDS array with row stride LS, 16 bytes per access.
+template <int COLS, int LS, int NT>
+__device__ __forceinline__ void copy_rows(float *dst, const float *__restrict__ src, int rows, int tid) {
+    constexpr int C4 = COLS / 4;
+    for (int i = tid; i < rows * C4; i += NT) {
+        const int r = i / C4, c = (i % C4) * 4;
+        *reinterpret_cast<f32x4_t *>(dst + r * LS + c) = *reinterpret_cast<const f32x4_t *>(src + (size_t)r * COLS + c);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Prep: one workgroup of 4 waves per (chunk, head).
+template <int DK> struct PrepBS {
+    static constexpr int KS = DK + 4;
+    static constexpr int CS = 66;
+    float KA[kB][KS];
+    float KI[kB][KS];
+    union {
+        float QA[kB][KS];                    // Gram phase
+        struct {
+            float A[kB][CS];                 // beta M
+            float T[kB][CS];                 // (I + A)^{-1}
+        } t;
+    };
+    float X[4][16][20];                      // per-wave product tile
+    float beta[kB];
+    int flag;
+};
+
+template <int DK, typename IO, typename GT>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
+                                                       const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
+                                                       const int32_t *__restrict__ cu,
+                                                       const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
+                                                       int H, float *__restrict__ recs) {
+    using R = BRec<DK>;
+    using S = PrepBS<DK>;
+    __shared__ S sm;
+    const int64_t chunk = blockIdx.x;
+    const int h = blockIdx.y;
+    int64_t n, t0;
+    int nv;
+    if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    float *rec = recs + ((size_t)chunk * H + h) * R::FLOATS;
+
+    if (tid == 0) sm.flag = 0;
+    if (tid < kB) sm.beta[tid] = tid < nv ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+    __syncthreads();
+    if (tid < DK) {
+        const int c = tid;
+        float g2 = 0.f;
+        for (int r = 0; r < nv; ++r) g2 += to_f32(log_alpha[((t0 + r) * H + h) * DK + c]) * kBL2E;
+        const float m2 = 0.5f * g2;
+        if (-g2 > kBwdMaxRange2 || !(g2 == g2)) sm.flag = 1;
+        float G = 0.f;
+        for (int r = 0; r < kB; ++r) {
+            float qa = 0.f, ka = 0.f, ki = 0.f;
+            if (r < nv) {
+                const size_t o = ((t0 + r) * H + h) * DK + c;
+                G += to_f32(log_alpha[o]) * kBL2E;
+                const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
+                const float kv = to_f32(k[o]);
+                qa = to_f32(q[o]) * ea;
+                ka = kv * ea;
+                ki = kv * ei;
+            }
+            sm.QA[r][c] = qa;
+            sm.KA[r][c] = ka;
+            sm.KI[r][c] = ki;
+        }
+        rec[R::EM + c] = __builtin_amdgcn_exp2f(m2);
+        rec[R::EG + c] = __builtin_amdgcn_exp2f(g2);
+        rec[R::EGM + c] = __builtin_amdgcn_exp2f(g2 - m2);
+    }
+    __syncthreads();
+    if (tid == 0) rec[R::FLAG] = sm.flag ? 1.f : 0.f;
+    // QA and KI go to the record as they are.
+    for (int i = tid; i < kB * DK / 4; i += 256) {
+        const int r = i / (DK / 4), c = (i % (DK / 4)) * 4;
+        *reinterpret_cast<f32x4_t *>(rec + R::QA + r * DK + c) = *reinterpret_cast<const f32x4_t *>(&sm.QA[r][c]);
+        *reinterpret_cast<f32x4_t *>(rec + R::KI + r * DK + c) = *reinterpret_cast<const f32x4_t *>(&sm.KI[r][c]);
+    }
+    // P = lower(QA KI^T) and M = strictly-lower(KA KI^T): wave w computes the
+    // tiles of block column w, s = 0..3 of P and s = 4..7 of M (block row s & 3).
+    f32x4_t mt[4];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const bool isM = s >= 4;
+        const int Rt = s & 3, It = w;
+        f32x4_t acc = zero4();
+        if (It <= Rt) {
+            const float *a = isM ? &sm.KA[16 * Rt][0] : &sm.QA[16 * Rt][0];
+            acc = mm<DK, S::KS, 1, 1, S::KS>(acc, a, &sm.KI[16 * It][0], lane);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * Rt + acc_row(lane, e), c = 16 * It + acc_col(lane);
+            const bool keep = isM ? r > c : r >= c;
+            acc[e] = keep ? acc[e] : 0.f;
+            rec[(isM ? R::M : R::P) + r * kB + c] = acc[e];
+        }
+        if (isM) mt[s & 3] = acc;
+    }
+    __syncthreads();   // QA no longer read
+    // A = diag(beta) M into the inversion area; KA <- diag(beta) KA for W.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * s + acc_row(lane, e), c = 16 * w + acc_col(lane);
+            sm.t.A[r][c] = sm.beta[r] * mt[s][e];
+        }
+    }
+    for (int i = tid; i < kB * DK; i += 256) {
+        const int r = i / DK, c = i % DK;
+        sm.KA[r][c] *= sm.beta[r];
+    }
+    __syncthreads();
+    // T = (I + A)^{-1}, unit lower triangular.  Diagonal 16x16 blocks by forward
+    // substitution (wave 0, lane 16b + j holds column j of block b); the other
+    // waves clear the blocks above the diagonal.
+    if (w == 0) {
+        const int b = lane >> 4, j = lane & 15;
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) s += sm.t.A[16 * b + i][16 * b + m] * t[m];
+            t[i] = i < j ? 0.f : (i == j ? 1.f : -s);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.t.T[16 * b + i][16 * b + j] = t[i];
+    } else {
+        for (int i = tid - 64; i < kB * kB; i += 192) {
+            const int r = i / kB, c = i % kB;
+            if ((c >> 4) > (r >> 4)) sm.t.T[r][c] = 0.f;
+        }
+    }
+    __syncthreads();
+    // Off-diagonal blocks, block row by block row:
+    //     T_RI = -T_RR sum_{m=I}^{R-1} A_Rm T_mI.
+    for (int Rb = 1; Rb < 4; ++Rb) {
+        if (w < Rb) {
+            const int Ib = w;
+            f32x4_t acc = zero4();
+            for (int m = Ib; m < Rb; ++m)
+                acc = mm<16, S::CS, 1, S::CS, 1>(acc, &sm.t.A[16 * Rb][16 * m], &sm.t.T[16 * m][16 * Ib], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.X[w][acc_row(lane, e)][acc_col(lane)] = acc[e];
+        }
+        __syncthreads();
+        if (w < Rb) {
+            const int Ib = w;
+            f32x4_t acc = zero4();
+            acc = mm<16, S::CS, 1, 20, 1>(acc, &sm.t.T[16 * Rb][16 * Rb], &sm.X[w][0][0], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.t.T[16 * Rb + acc_row(lane, e)][16 * Ib + acc_col(lane)] = -acc[e];
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < kB * kB; i += 256) {
+        const int r = i / kB, c = i % kB;
+        rec[R::T + i] = sm.t.T[r][c];
+    }
+    // W = T diag(beta) KA: 4 x DK/16 tiles.
+    constexpr int NWT = 4 * (DK / 16);
+    for (int idx = w; idx < NWT; idx += 4) {
+        const int Rt = idx / (DK / 16), Ct = idx % (DK / 16);
+        f32x4_t acc = zero4();
+        acc = mm<kB, S::CS, 1, S::KS, 1>(acc, &sm.t.T[16 * Rt][0], &sm.KA[0][16 * Ct], lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rec[R::W + (16 * Rt + acc_row(lane, e)) * DK + 16 * Ct + acc_col(lane)] = acc[e];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Forward state replay: one workgroup of 4 waves per (sequence, head, block of
+// 16 value columns).
+template <int DK> struct FwdBS {
+    static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
+    float W[kB][KS];
+    float KI[kB][KS];
+    float T[kB][CS];
+    float V[kB][VS];                         // diag(beta) V block
+    float U[kB][VS];
+    float S[DK][VS];
+    float Sp[DK][VS];                        // Diag(e^m) S
+    float em[DK], eg[DK], egm[DK];
+};
+
+template <int DK, int DV, typename IO, typename GT>
+__global__ __launch_bounds__(256) void bwd_fwd_state_kernel(const IO *__restrict__ v, const GT *__restrict__ beta,
+                                                            const float *__restrict__ h0, const int32_t *__restrict__ cu,
+                                                            const int32_t *__restrict__ chunk_off, int64_t T, int H,
+                                                            const float *__restrict__ recs, float *__restrict__ Sc,
+                                                            float *__restrict__ Uc, float *__restrict__ sflag) {
+    using R = BRec<DK>;
+    using S = FwdBS<DK>;
+    __shared__ S sm;
+    constexpr int NVB = DV / kBV;
+    const int64_t id = blockIdx.x;
+    const int vb = (int)(id % NVB);
+    const int h = (int)((id / NVB) % H);
+    const int64_t n = id / ((int64_t)NVB * H);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int j0 = vb * kBV;
+    int64_t bos, eos, slot0;
+    seq_range(n, cu, chunk_off, T, bos, eos, slot0);
+
+    for (int i = tid; i < DK * kBV; i += 256) {
+        const int c = i / kBV, j = i % kBV;
+        sm.S[c][j] = h0 ? h0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
+    }
+    const int nchunks = (int)((eos - bos + kB - 1) / kB);
+    float anybad = 0.f;
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int64_t slot = slot0 + ci;
+        const int64_t t0 = bos + (int64_t)kB * ci;
+        const int nv = (int)(eos - t0 < kB ? eos - t0 : kB);
+        const float *rec = recs + ((size_t)slot * H + h) * R::FLOATS;
+        anybad = fmaxf(anybad, rec[R::FLAG]);
+        copy_rows<DK, S::KS, 256>(&sm.W[0][0], rec + R::W, kB, tid);
+        copy_rows<DK, S::KS, 256>(&sm.KI[0][0], rec + R::KI, kB, tid);
+        copy_rows<kB, S::CS, 256>(&sm.T[0][0], rec + R::T, kB, tid);
+        if (tid < DK) {
+            sm.em[tid] = rec[R::EM + tid];
+            sm.eg[tid] = rec[R::EG + tid];
+            sm.egm[tid] = rec[R::EGM + tid];
+        }
+        for (int i = tid; i < kB * kBV; i += 256) {
+            const int r = i / kBV, j = i % kBV;
+            float x = 0.f;
+            if (r < nv) x = to_f32(beta[(t0 + r) * H + h]) * to_f32(v[((t0 + r) * H + h) * DV + j0 + j]);
+            sm.V[r][j] = x;
+        }
+        __syncthreads();
+        float *sc = Sc + ((size_t)slot * H + h) * DK * DV;
+        for (int i = tid; i < DK * kBV; i += 256) {
+            const int c = i / kBV, j = i % kBV;
+            const float s = sm.S[c][j];
+            sc[(size_t)c * DV + j0 + j] = s;
+            sm.Sp[c][j] = sm.em[c] * s;
+        }
+        __syncthreads();
+        {   // U = T diag(beta) V - W S', one row tile per wave
+            f32x4_t a = zero4(), b = zero4();
+            a = mm<kB, S::CS, 1, S::VS, 1>(a, &sm.T[16 * w][0], &sm.V[0][0], lane);
+            b = mm<DK, S::KS, 1, S::VS, 1>(b, &sm.W[16 * w][0], &sm.Sp[0][0], lane);
+            float *uc = Uc + ((size_t)slot * H + h) * kB * DV;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
+                const float u = a[e] - b[e];
+                sm.U[r][j] = u;
+                uc[(size_t)r * DV + j0 + j] = u;
+            }
+        }
+        __syncthreads();
+        // S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) KI^T U
+        for (int ct = w; ct < DK / 16; ct += 4) {
+            f32x4_t a = zero4();
+            a = mm<kB, 1, S::KS, S::VS, 1>(a, &sm.KI[0][16 * ct], &sm.U[0][0], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
+                sm.S[c][j] = sm.eg[c] * sm.S[c][j] + sm.egm[c] * a[e];
+            }
+        }
+        __syncthreads();
+    }
+    // One flag per (sequence, head): any chunk out of range makes every
+    // gradient of the chain NaN (the gradient kernel reads it).
+    if (vb == 0 && tid == 0) sflag[n * H + h] = anybad;
+}
+
+// ----------------------------------------------------------------------------
+// Reverse state-gradient pass: same grid, chunks in reverse order.
+template <int DK> struct RevBS {
+    static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
+    float QA[kB][KS];
+    float KI[kB][KS];
+    float W[kB][KS];
+    float P[kB][CS];
+    float dO[kB][VS];
+    float dU[kB][VS];
+    float dS[DK][VS];                        // dL/dS at the chunk's end
+    float dSs[DK][VS];                       // Diag(e^{g_n-m}) dS
+    float em[DK], eg[DK], egm[DK];
+    float flag;
+};
+
+template <int DK, int DV, typename IO>
+__global__ __launch_bounds__(256) void bwd_rev_state_kernel(const IO *__restrict__ d_o, const float *__restrict__ d_hT,
+                                                            const int32_t *__restrict__ cu,
+                                                            const int32_t *__restrict__ chunk_off, int64_t T, int H,
+                                                            const float *__restrict__ recs, float *__restrict__ dSc,
+                                                            float *__restrict__ dUc, float *__restrict__ dh0) {
+    using R = BRec<DK>;
+    using S = RevBS<DK>;
+    __shared__ S sm;
+    constexpr int NVB = DV / kBV;
+    const int64_t id = blockIdx.x;
+    const int vb = (int)(id % NVB);
+    const int h = (int)((id / NVB) % H);
+    const int64_t n = id / ((int64_t)NVB * H);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int j0 = vb * kBV;
+    int64_t bos, eos, slot0;
+    seq_range(n, cu, chunk_off, T, bos, eos, slot0);
+
+    for (int i = tid; i < DK * kBV; i += 256) {
+        const int c = i / kBV, j = i % kBV;
+        sm.dS[c][j] = d_hT ? d_hT[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
+    }
+    const int nchunks = (int)((eos - bos + kB - 1) / kB);
+    for (int ci = nchunks - 1; ci >= 0; --ci) {
+        const int64_t slot = slot0 + ci;
+        const int64_t t0 = bos + (int64_t)kB * ci;
+        const int nv = (int)(eos - t0 < kB ? eos - t0 : kB);
+        const float *rec = recs + ((size_t)slot * H + h) * R::FLOATS;
+        copy_rows<DK, S::KS, 256>(&sm.QA[0][0], rec + R::QA, kB, tid);
+        copy_rows<DK, S::KS, 256>(&sm.KI[0][0], rec + R::KI, kB, tid);
+        copy_rows<DK, S::KS, 256>(&sm.W[0][0], rec + R::W, kB, tid);
+        copy_rows<kB, S::CS, 256>(&sm.P[0][0], rec + R::P, kB, tid);
+        if (tid < DK) {
+            sm.em[tid] = rec[R::EM + tid];
+            sm.eg[tid] = rec[R::EG + tid];
+            sm.egm[tid] = rec[R::EGM + tid];
+        }
+        if (tid == 0) sm.flag = rec[R::FLAG];
+        for (int i = tid; i < kB * kBV; i += 256) {
+            const int r = i / kBV, j = i % kBV;
+            sm.dO[r][j] = r < nv ? to_f32(d_o[((t0 + r) * H + h) * DV + j0 + j]) : 0.f;
+        }
+        __syncthreads();
+        float *dsc = dSc + ((size_t)slot * H + h) * DK * DV;
+        for (int i = tid; i < DK * kBV; i += 256) {
+            const int c = i / kBV, j = i % kBV;
+            const float s = sm.dS[c][j];
+            dsc[(size_t)c * DV + j0 + j] = s;
+            sm.dSs[c][j] = sm.egm[c] * s;
+        }
+        __syncthreads();
+        {   // dU = P^T dO + KI Diag(e^{g_n-m}) dS, one row tile per wave
+            f32x4_t a = zero4();
+            a = mm<kB, 1, S::CS, S::VS, 1>(a, &sm.P[0][16 * w], &sm.dO[0][0], lane);
+            a = mm<DK, S::KS, 1, S::VS, 1>(a, &sm.KI[16 * w][0], &sm.dSs[0][0], lane);
+            float *duc = dUc + ((size_t)slot * H + h) * kB * DV;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
+                sm.dU[r][j] = a[e];
+                duc[(size_t)r * DV + j0 + j] = a[e];
+            }
+        }
+        __syncthreads();
+        // dS <- Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS
+        const bool bad = sm.flag != 0.f;
+        for (int ct = w; ct < DK / 16; ct += 4) {
+            f32x4_t a = zero4(), b = zero4();
+            a = mm<kB, 1, S::KS, S::VS, 1>(a, &sm.QA[0][16 * ct], &sm.dO[0][0], lane);
+            b = mm<kB, 1, S::KS, S::VS, 1>(b, &sm.W[0][16 * ct], &sm.dU[0][0], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
+                const float x = sm.em[c] * (a[e] - b[e]) + sm.eg[c] * sm.dS[c][j];
+                sm.dS[c][j] = bad ? __builtin_nanf("") : x;
+            }
+        }
+        __syncthreads();
+    }
+    if (dh0) {
+        for (int i = tid; i < DK * kBV; i += 256) {
+            const int c = i / kBV, j = i % kBV;
+            dh0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] = sm.dS[c][j];
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Gradient kernel: one workgroup of 8 waves per (chunk, head).
+template <int DK> struct GradBS {
+    static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
+    float KA[kB][KS];
+    union {
+        struct {
+            float T[kB][CS];                 // loop: (I + A)^{-1}; after: dP
+            float dM[kB][CS];
+        } m;
+        float G2[kB][DK];                    // in-chunk log2-decay cumsum, at the end
+    } r2;
+    union {
+        struct {
+            float dO[kB][VS], U[kB][VS], dU[kB][VS], X[kB][VS], dY[kB][VS];
+            float Sp[DK][VS], dSn[DK][VS];
+        } lp;
+        struct {
+            float QA[kB][KS];                // then dG
+            float KI[kB][KS];                // then (U dS_next^T) . KI
+        } pt;
+    } r3;
+    float beta[kB];
+    float dbr[kB];
+    float dbA[4][kB];
+    float m2[DK], em[DK], eg[DK], egm[DK];
+};
+
+template <int DK, int DV, typename IO, typename GT>
+__global__ __launch_bounds__(512) void bwd_grad_kernel(
+    const IO *__restrict__ k, const IO *__restrict__ v, const GT *__restrict__ log_alpha,
+    const GT *__restrict__ beta, const IO *__restrict__ d_o, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, int64_t N, int64_t T, int H, const float *__restrict__ recs,
+    const float *__restrict__ Sc, const float *__restrict__ Uc, const float *__restrict__ dSc,
+    const float *__restrict__ dUc, const float *__restrict__ sflag, IO *__restrict__ dq, IO *__restrict__ dk,
+    IO *__restrict__ dv, GT *__restrict__ dla, GT *__restrict__ dbeta) {
+    using R = BRec<DK>;
+    using S = GradBS<DK>;
+    __shared__ S sm;
+    const int64_t chunk = blockIdx.x;
+    const int h = blockIdx.y;
+    int64_t n, t0;
+    int nv;
+    if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float *rec = recs + ((size_t)chunk * H + h) * R::FLOATS;
+    const size_t ch = (size_t)chunk * H + h;
+    constexpr int NCT = DK / 16;             // key-column tiles
+    constexpr int NOWN = 4 * NCT / 8;        // (row, key) tiles per wave
+
+    if (tid < kB) {
+        sm.beta[tid] = tid < nv ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+        sm.dbr[tid] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.dbA[i][tid] = 0.f;
+    }
+    float dgn1 = 0.f;                        // thread c < DK: sum_j dS_next[c,j] S'[c,j]
+    if (tid < DK) {
+        const int c = tid;
+        sm.em[c] = rec[R::EM + c];
+        sm.eg[c] = rec[R::EG + c];
+        sm.egm[c] = rec[R::EGM + c];
+        float g2 = 0.f;
+        for (int r = 0; r < nv; ++r) g2 += to_f32(log_alpha[((t0 + r) * H + h) * DK + c]) * kBL2E;
+        const float m2 = 0.5f * g2;
+        sm.m2[c] = m2;
+        float G = 0.f;
+        for (int r = 0; r < kB; ++r) {
+            float ka = 0.f;
+            if (r < nv) {
+                const size_t o = ((t0 + r) * H + h) * DK + c;
+                G += to_f32(log_alpha[o]) * kBL2E;
+                ka = to_f32(k[o]) * __builtin_amdgcn_exp2f(G - m2);
+            }
+            sm.KA[r][c] = ka;
+        }
+    }
+    copy_rows<kB, S::CS, 512>(&sm.r2.m.T[0][0], rec + R::T, kB, tid);
+
+    f32x4_t aQ[NOWN], aK[NOWN], aB[NOWN];    // dQA, dY S'^T, U dS_next^T
+#pragma unroll
+    for (int s = 0; s < NOWN; ++s) aQ[s] = aK[s] = aB[s] = zero4();
+    f32x4_t aL[3];                           // lower tiles: idx < 10 dP, else dY U^T
+#pragma unroll
+    for (int s = 0; s < 3; ++s) aL[s] = zero4();
+    f32x4_t xr = zero4(), dbp = zero4();     // waves 0-3: X tile, dbeta partial
+
+    const float *sc = Sc + ch * DK * DV;
+    const float *uc = Uc + ch * kB * DV;
+    const float *dsc = dSc + ch * DK * DV;
+    const float *duc = dUc + ch * kB * DV;
+    const bool bad = sflag[n * H + h] != 0.f;
+
+    for (int vb = 0; vb < DV / kBV; ++vb) {
+        const int j0 = vb * kBV;
+        __syncthreads();                     // previous block's reads done
+        for (int i = tid; i < kB * kBV; i += 512) {
+            const int r = i / kBV, j = i % kBV;
+            const bool ok = r < nv;
+            const size_t o = ((t0 + r) * H + h) * DV + j0 + j;
+            sm.r3.lp.dO[r][j] = ok ? to_f32(d_o[o]) : 0.f;
+            sm.r3.lp.X[r][j] = ok ? to_f32(v[o]) : 0.f;
+            sm.r3.lp.U[r][j] = uc[(size_t)r * DV + j0 + j];
+            sm.r3.lp.dU[r][j] = duc[(size_t)r * DV + j0 + j];
+        }
+        for (int i = tid; i < DK * kBV; i += 512) {
+            const int c = i / kBV, j = i % kBV;
+            sm.r3.lp.Sp[c][j] = sm.em[c] * sc[(size_t)c * DV + j0 + j];
+            sm.r3.lp.dSn[c][j] = dsc[(size_t)c * DV + j0 + j];
+        }
+        __syncthreads();
+        if (w < 4) {   // X = V - KA S'
+            f32x4_t a = zero4();
+            a = mm<DK, S::KS, 1, S::VS, 1>(a, &sm.KA[16 * w][0], &sm.r3.lp.Sp[0][0], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
+                xr[e] = sm.r3.lp.X[r][j] - a[e];
+            }
+        } else {       // dY = T^T dU; dV = diag(beta) dY
+            const int rt = w - 4;
+            f32x4_t a = zero4();
+            a = mm<kB, 1, S::CS, S::VS, 1>(a, &sm.r2.m.T[0][16 * rt], &sm.r3.lp.dU[0][0], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + acc_row(lane, e), j = acc_col(lane);
+                sm.r3.lp.dY[r][j] = a[e];
+                if (r < nv) {
+                    const float x = bad ? __builtin_nanf("") : sm.beta[r] * a[e];
+                    dv[((t0 + r) * H + h) * DV + j0 + j] = from_f32<IO>(x);
+                }
+            }
+        }
+        __syncthreads();
+        if (w < 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dbp[e] += xr[e] * sm.r3.lp.dY[16 * w + acc_row(lane, e)][acc_col(lane)];
+        }
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const int idx = w + 8 * s;
+            if (idx < 20) {
+                int Rt, It;
+                low_tile(idx % 10, Rt, It);
+                const float *a = idx < 10 ? &sm.r3.lp.dO[16 * Rt][0] : &sm.r3.lp.dY[16 * Rt][0];
+                aL[s] = mm<kBV, S::VS, 1, 1, S::VS>(aL[s], a, &sm.r3.lp.U[16 * It][0], lane);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NOWN; ++s) {
+            const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
+            aQ[s] = mm<kBV, S::VS, 1, 1, S::VS>(aQ[s], &sm.r3.lp.dO[16 * rt][0], &sm.r3.lp.Sp[16 * ct][0], lane);
+            aK[s] = mm<kBV, S::VS, 1, 1, S::VS>(aK[s], &sm.r3.lp.dY[16 * rt][0], &sm.r3.lp.Sp[16 * ct][0], lane);
+            aB[s] = mm<kBV, S::VS, 1, 1, S::VS>(aB[s], &sm.r3.lp.U[16 * rt][0], &sm.r3.lp.dSn[16 * ct][0], lane);
+        }
+        if (tid < DK) {
+#pragma unroll
+            for (int j = 0; j < kBV; ++j) dgn1 += sm.r3.lp.dSn[tid][j] * sm.r3.lp.Sp[tid][j];
+        }
+    }
+    __syncthreads();                         // loop buffers and T free
+
+    // dbeta from X . dY: sum over the 16 columns of each tile row.
+    if (w < 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = dbp[e];
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if ((lane & 15) == 0) sm.dbr[16 * w + acc_row(lane, e)] = x;
+        }
+    }
+    // dP (inclusive lower) and dM = diag(beta) dA, dA = -strictly-lower(dY U^T).
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int idx = w + 8 * s;
+        if (idx < 20) {
+            int Rt, It;
+            low_tile(idx % 10, Rt, It);
+            const bool isA = idx >= 10;
+            float rowsum[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * Rt + acc_row(lane, e), c = 16 * It + acc_col(lane);
+                if (!isA) {
+                    sm.r2.m.T[r][c] = r >= c ? aL[s][e] : 0.f;     // dP
+                    rowsum[e] = 0.f;
+                } else {
+                    const float dA = r > c ? -aL[s][e] : 0.f;
+                    sm.r2.m.dM[r][c] = sm.beta[r] * dA;
+                    rowsum[e] = dA * rec[R::M + r * kB + c];
+                }
+            }
+            if (isA) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = rowsum[e];
+                    x += __shfl_xor(x, 1);
+                    x += __shfl_xor(x, 2);
+                    x += __shfl_xor(x, 4);
+                    x += __shfl_xor(x, 8);
+                    if ((lane & 15) == 0) sm.dbA[It][16 * Rt + acc_row(lane, e)] = x;
+                }
+            }
+        }
+    }
+    // Upper blocks of dP and dM are never written above: clear them.
+    for (int i = tid; i < kB * kB; i += 512) {
+        const int r = i / kB, c = i % kB;
+        if ((c >> 4) > (r >> 4)) {
+            sm.r2.m.T[r][c] = 0.f;
+            sm.r2.m.dM[r][c] = 0.f;
+        }
+    }
+    copy_rows<DK, S::KS, 512>(&sm.r3.pt.QA[0][0], rec + R::QA, kB, tid);
+    copy_rows<DK, S::KS, 512>(&sm.r3.pt.KI[0][0], rec + R::KI, kB, tid);
+    __syncthreads();
+
+    f32x4_t aI[NOWN];                        // dKI
+#pragma unroll
+    for (int s = 0; s < NOWN; ++s) {
+        const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
+        const float *dP = &sm.r2.m.T[0][0];
+        const float *dM = &sm.r2.m.dM[0][0];
+        aQ[s] = mm<kB, S::CS, 1, S::KS, 1>(aQ[s], dP + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
+        f32x4_t t = zero4();
+        t = mm<kB, S::CS, 1, S::KS, 1>(t, dM + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) aK[s][e] = t[e] - sm.beta[16 * rt + acc_row(lane, e)] * aK[s][e];
+        f32x4_t u = zero4();
+        u = mm<kB, 1, S::CS, S::KS, 1>(u, dP + 16 * rt, &sm.r3.pt.QA[0][16 * ct], lane);
+        u = mm<kB, 1, S::CS, S::KS, 1>(u, dM + 16 * rt, &sm.KA[0][16 * ct], lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] += sm.egm[16 * ct + acc_col(lane)] * aB[s][e];
+        aI[s] = u;
+    }
+    __syncthreads();                         // dP, dM, QA, KI reads done
+
+    if (tid < DK) {   // G (log2 units) again, into the freed area
+        const int c = tid;
+        float G = 0.f;
+        for (int r = 0; r < kB; ++r) {
+            if (r < nv) G += to_f32(log_alpha[((t0 + r) * H + h) * DK + c]) * kBL2E;
+            sm.r2.G2[r][c] = G;
+        }
+    }
+    __syncthreads();
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int s = 0; s < NOWN; ++s) {
+        const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + acc_row(lane, e), c = 16 * ct + acc_col(lane);
+            float dG = 0.f, kb = 0.f;
+            if (r < nv) {
+                const float g = sm.r2.G2[r][c] - sm.m2[c];
+                const float ea = __builtin_amdgcn_exp2f(g), ei = __builtin_amdgcn_exp2f(-g);
+                const size_t o = ((t0 + r) * H + h) * DK + c;
+                const float ki = sm.r3.pt.KI[r][c];
+                dq[o] = from_f32<IO>(bad ? qnan : aQ[s][e] * ea);
+                dk[o] = from_f32<IO>(bad ? qnan : aK[s][e] * ea + aI[s][e] * ei);
+                dG = aQ[s][e] * sm.r3.pt.QA[r][c] + aK[s][e] * sm.KA[r][c] - aI[s][e] * ki;
+                kb = aB[s][e] * ki;
+            }
+            sm.r3.pt.QA[r][c] = dG;
+            sm.r3.pt.KI[r][c] = kb;
+        }
+    }
+    __syncthreads();
+    if (tid < DK) {
+        const int c = tid;
+        float kbs = 0.f;
+        for (int r = 0; r < kB; ++r) kbs += sm.r3.pt.KI[r][c];
+        const float dgn = sm.egm[c] * (dgn1 + kbs);
+        float s = 0.f;
+        for (int r = nv - 1; r >= 0; --r) {
+            s += sm.r3.pt.QA[r][c];
+            dla[((t0 + r) * H + h) * DK + c] = from_f32<GT>(bad ? qnan : s + dgn);
+        }
+    } else if (tid >= 256 && tid < 256 + kB) {
+        const int r = tid - 256;
+        if (r < nv) {
+            const float x = sm.dbr[r] + ((sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]));
+            dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
+        }
+    }
+}
+
+template <int DK, int DV, typename IO, typename GT>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
+    const BwdLayout L = bwd_layout(a);
+    uint8_t *ws = static_cast<uint8_t *>(a.workspace);
+    int32_t *chunk_off = a.varlen ? reinterpret_cast<int32_t *>(ws + L.plan) : nullptr;
+    float *recs = reinterpret_cast<float *>(ws + L.rec);
+    float *Sc = reinterpret_cast<float *>(ws + L.sc);
+    float *Uc = reinterpret_cast<float *>(ws + L.uc);
+    float *dSc = reinterpret_cast<float *>(ws + L.dsc);
+    float *dUc = reinterpret_cast<float *>(ws + L.duc);
+    float *sflag = reinterpret_cast<float *>(ws + L.sflag);
+    const IO *q = static_cast<const IO *>(a.q), *k = static_cast<const IO *>(a.k), *v = static_cast<const IO *>(a.v);
+    const GT *la = static_cast<const GT *>(a.log_alpha), *be = static_cast<const GT *>(a.beta);
+    const IO *dO = static_cast<const IO *>(a.d_o);
+    const int64_t T = a.seq_len;
+    if (a.varlen)
+        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
+    if (L.nch > 0 && a.total_tokens > 0)
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st, q, k,
+                           la, be, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, recs);
+    const int64_t chains = a.num_seqs * a.H * (DV / kBV);
+    if (chains > 0) {
+        if (a.total_tokens > 0)
+            hipLaunchKernelGGL((bwd_fwd_state_kernel<DK, DV, IO, GT>), dim3((unsigned)chains), dim3(256), 0, st, v, be,
+                               a.h0, a.cu_seqlens, chunk_off, T, a.H, recs, Sc, Uc, sflag);
+        hipLaunchKernelGGL((bwd_rev_state_kernel<DK, DV, IO>), dim3((unsigned)chains), dim3(256), 0, st, dO, a.d_hT,
+                           a.cu_seqlens, chunk_off, T, a.H, recs, dSc, dUc, a.dh0);
+    }
+    if (L.nch > 0 && a.total_tokens > 0)
+        hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st, k,
+                           v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, recs, Sc, Uc, dSc, dUc,
+                           sflag, static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv),
+                           static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta));
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t st) {
+    if (a.io_bf16)
+        return a.gate_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t>(a, st) : launch_bwd_t<DK, DV, bf16_t, float>(a, st);
+    return a.gate_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a, st) : launch_bwd_t<DK, DV, float, float>(a, st);
+}
+
+}  // namespace
+
+size_t chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total; }
+
+int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const BwdLayout L = bwd_layout(a);
+    if (L.nch > 0x7fffffffLL || a.num_seqs * a.H * (a.d_v / kBV) > 0x7fffffffLL) {
+        snprintf(err, err_len, "chunk_bwd grid too large");
+        return -1;
+    }
+    if (a.workspace_bytes < L.total) {
+        snprintf(err, err_len, "workspace too small");
+        return -1;
+    }
+    hipError_t e;
+    if (a.d_k == 128)
+        e = a.d_v == 128 ? launch_bwd_dims<128, 128>(a, st) : launch_bwd_dims<128, 64>(a, st);
+    else
+        e = a.d_v == 128 ? launch_bwd_dims<64, 128>(a, st) : launch_bwd_dims<64, 64>(a, st);
+    if (e != hipSuccess) {
+        snprintf(err, err_len, "%s", hipGetErrorString(e));
+        return -1;
+    }
+    return 0;
+}
+
+}  // namespace kda

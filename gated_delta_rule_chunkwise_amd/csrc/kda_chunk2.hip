@@ -48,12 +48,15 @@
 // padded to a multiple of 256 bytes.
 #include "kda_chunk_common.h"
 #include "kda_launch.h"
+#include "kda_plan.h"
 
 #include <stdio.h>
 #include <stdlib.h>
 
 namespace kda {
 namespace {
+
+static_assert(kPlanChunk == kC, "the varlen plan and the kernels use one chunk length");
 
 template <int DK, int DV> struct Rec {
     static constexpr int NKS = DK / 32;
@@ -77,8 +80,6 @@ __device__ __forceinline__ int p_tile(int R, int I) { return (R * (R + 1)) / 2 +
 
 constexpr size_t kHeaderBytes = 256;
 
-size_t plan_bytes(int64_t num_seqs) { return ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256; }
-
 int64_t max_chunks(const ChunkArgs &a) {
     if (a.varlen) return (a.total_tokens + kC - 1) / kC + a.num_seqs;
     return a.num_seqs * ((a.seq_len + kC - 1) / kC);
@@ -101,61 +102,6 @@ int64_t segment_chunks(const ChunkArgs &a) {
 }
 
 size_t carry_bytes(const ChunkArgs &a) { return ((size_t)a.H * a.d_k * a.d_v * 4 + 255) / 256 * 256; }
-
-// chunk_off[n] = number of chunks of sequences 0..n-1 (exclusive prefix sum of
-// ceil(L_n / 64)); chunk_off[N] = total.  One workgroup.
-__global__ __launch_bounds__(256) void chunk_plan_kernel(const int32_t *__restrict__ cu, int64_t N,
-                                                         int32_t *__restrict__ chunk_off) {
-    __shared__ int32_t part[256];
-    __shared__ int32_t carry;
-    const int t = threadIdx.x;
-    if (t == 0) carry = 0;
-    __syncthreads();
-    for (int64_t base = 0; base <= N; base += 256) {
-        const int64_t n = base + t;
-        int32_t cnt = 0;
-        if (n < N) cnt = (cu[n + 1] - cu[n] + kC - 1) / kC;
-        part[t] = cnt;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {   // inclusive Hillis-Steele scan
-            const int32_t x = t >= off ? part[t - off] : 0;
-            __syncthreads();
-            part[t] += x;
-            __syncthreads();
-        }
-        if (n <= N) chunk_off[n] = carry + part[t] - cnt;
-        __syncthreads();
-        if (t == 255) carry += part[255];
-        __syncthreads();
-    }
-}
-
-// Finds the sequence and token range of chunk `chunk`; false if past the end.
-__device__ __forceinline__ bool locate_chunk(int64_t chunk, const int32_t *__restrict__ cu,
-                                             const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
-                                             int64_t &n, int64_t &t0, int &nv) {
-    if (cu) {
-        if (chunk >= chunk_off[N]) return false;
-        int64_t lo = 0, hi = N - 1;   // largest n with chunk_off[n] <= chunk (and a non-empty sequence)
-        while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) >> 1;
-            if (chunk_off[mid] <= chunk) lo = mid;
-            else hi = mid - 1;
-        }
-        n = lo;
-        t0 = cu[n] + (int64_t)kC * (chunk - chunk_off[n]);
-        const int64_t rem = cu[n + 1] - t0;
-        nv = (int)(rem < kC ? rem : kC);
-        return true;
-    }
-    const int64_t cps = (T + kC - 1) / kC;
-    n = chunk / cps;
-    const int64_t c = chunk % cps;
-    t0 = n * T + (int64_t)kC * c;
-    const int64_t rem = T - (int64_t)kC * c;
-    nv = (int)(rem < kC ? rem : kC);
-    return true;
-}
 
 template <int DK, int DV>
 struct alignas(16) PrepSmem {

@@ -46,4 +46,23 @@ int launch_decode_step(const DecodeArgs &a, void *stream, char *err, size_t err_
 // Workspace for these arguments (pointers are not read).
 size_t chunk_fwd_workspace_bytes(const ChunkArgs &a);
 
+struct BwdArgs {
+    const void *q, *k, *v, *log_alpha, *beta;
+    const float *h0;            // [N, H, d_k, d_v] or nullptr (zero state)
+    const int32_t *cu_seqlens;  // device, or nullptr (equal-length batch)
+    const void *d_o;            // gradient of o, io dtype
+    const float *d_hT;          // gradient of h_T, or nullptr (zero)
+    void *dq, *dk, *dv;         // io dtype
+    void *dlog_alpha, *dbeta;   // gate dtype
+    float *dh0;                 // or nullptr (not wanted)
+    int64_t num_seqs, seq_len, total_tokens;
+    int32_t H, d_k, d_v;
+    int32_t io_bf16, gate_bf16, varlen;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+size_t chunk_bwd_workspace_bytes(const BwdArgs &a);
+int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len);
+
 }  // namespace kda

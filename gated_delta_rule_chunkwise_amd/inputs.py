@@ -225,3 +225,16 @@ def draw_strength(shape, seed: int, dtype=torch.bfloat16, device="cpu"):
     (the separate write strength of the decoupled entry points)."""
     g = _gen(seed, device)
     return torch.sigmoid(_randn(tuple(shape), g, device)).to(dtype)
+
+
+def make_upstream_grads(d: dict, seed: int, device="cpu", with_state=True):
+    """Gradients of a training loss with respect to o and h_T, for the backward:
+    grad_o ~ N(0, 1) in the dtype of v, [T_total, H, d_v]; grad_hT ~ N(0, 0.1^2)
+    fp32 [N, H, d_k, d_v] (None when with_state is False).  Own seed."""
+    g = _gen(seed, device)
+    T, H, dv = d["v"].shape
+    dk = d["q"].shape[-1]
+    N = len(d["lengths"])
+    grad_o = _randn((T, H, dv), g, device).to(d["v"].dtype)
+    grad_hT = (0.1 * _randn((N, H, dk, dv), g, device)).contiguous() if with_state else None
+    return grad_o, grad_hT

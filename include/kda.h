@@ -244,6 +244,65 @@ kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void 
                                        int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
                                        kda_dtype_t gate_dtype, void *stream);
 
+/*
+ * Bytes of device workspace kda_chunk_bwd needs for these sizes (arguments as
+ * for kda_chunk_bwd; 0 for invalid arguments).  The backward keeps, per
+ * (chunk, head), in fp32: the chunk's decayed queries and keys, W, the UT
+ * inverse, the intra-chunk score and Gram blocks and the decay scales (about
+ * 130 KiB at d_k = 128), the state at the chunk's start and the state gradient
+ * at its end (d_k x d_v each), and U and dU (64 x d_v each): about 330 KiB per
+ * chunk-head at d_k = d_v = 128, i.e. about 5 KiB per token-head (about 11 GB
+ * for 65,536 tokens x 32 heads, well inside 288 GB of HBM).  The size depends
+ * only on the arguments.
+ */
+size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                    int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+
+/*
+ * kda_chunk_bwd -- gradients of kda_chunk_fwd, for training.
+ *
+ * The KimiLinear article presents the chunkwise form as what makes training on
+ * long sequences efficient (sections 3 and 4.1) and notes that it only keeps a
+ * chunk-sized score block per chunk for the backward pass (section 3.2).  The
+ * gradient itself is that of the per-token recurrence above: for a scalar loss
+ * L whose gradients with respect to o and h_T are grad_o and grad_hT, this
+ * computes dL/dq, dL/dk, dL/dv, dL/dlog_alpha, dL/dbeta and dL/dh0.  It runs in
+ * chunks of 64 tokens: the state-independent chunk operands in parallel, one
+ * forward pass and one reverse pass over the chunks for the states and state
+ * gradients at chunk boundaries, then the per-chunk gradients in parallel.
+ *
+ *   q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, B, T, H, d_k, d_v,
+ *   io_dtype, gate_dtype    the forward's inputs, as for kda_chunk_fwd
+ *   grad_o          [B, T, H, d_v]  io_dtype
+ *   grad_hT         [N, H, d_k, d_v] fp32, or NULL (L does not depend on h_T)
+ *   grad_q, grad_k  [B, T, H, d_k]  io_dtype (out)
+ *   grad_v          [B, T, H, d_v]  io_dtype (out)
+ *   grad_log_alpha  [B, T, H, d_k]  gate_dtype (out)
+ *   grad_beta       [B, T, H]       gate_dtype (out)
+ *   grad_h0         [N, H, d_k, d_v] fp32 (out), or NULL (not wanted); given
+ *                   also when h0 is NULL (the gradient at a zero state).  A
+ *                   zero-length sequence gives grad_h0 = grad_hT (or zeros).
+ *   workspace       at least kda_chunk_bwd_workspace_size() bytes, 16-byte
+ *                   aligned, caller-owned; contents on entry do not matter.
+ *
+ * Outputs must not alias inputs or one another.  Numerics: every product and
+ * accumulation is fp32 (fp32 matrix cores); outputs are rounded to their dtype
+ * with round-to-nearest-even.  Range: a chunk in which some key channel decays
+ * by more than about e^-160 in total (sum of log_alpha over the chunk below
+ * about -160) is outside the fp32 range of the chunk factors; every gradient
+ * of that sequence and head, grad_h0 included, is then NaN (never a silently
+ * wrong value).  Deterministic: no atomics; the same inputs give
+ * bitwise identical outputs.
+ */
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *beta, const float *h0, const int32_t *cu_seqlens,
+                           int32_t num_seqs, const void *grad_o, const float *grad_hT,
+                           void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
+                           void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                           kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -257,3 +257,51 @@ def test_decoupled_chunk_fwd_validates(kda, kw, code):
 def test_decoupled_decode_validates(kda, kw, code):
     lib = kda.load_library()
     assert decode_dec(lib, **kw) == code
+
+
+def bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, go=P, ghT=None, dq=P, dk=P, dv=P,
+             dla=P, db=P, dh0=P, B=1, T=128, H=2, dk_=128, dv_=128, io=1, gt=1, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"], a["N"],
+                             a["go"], a["ghT"], a["dq"], a["dk"], a["dv"], a["dla"], a["db"], a["dh0"],
+                             a["B"], a["T"], a["H"], a["dk_"], a["dv_"], a["io"], a["gt"], a["ws"],
+                             a["wsb"], None)
+
+
+def test_bwd_workspace_size(kda):
+    # per chunk-head: the fp32 record (3 x 64 x d_k + 3 x 64 x 64 + 3 x d_k floats),
+    # the state and state gradient (2 x d_k x d_v) and U, dU (2 x 64 x d_v), fp32
+    per = 4 * (3 * 64 * 128 + 3 * 64 * 64 + 3 * 128 + 2 * 128 * 128 + 2 * 64 * 128)
+    w = kda.kda_chunk_bwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_BF16)
+    assert 1024 * 32 * per <= w <= 1024 * 32 * (per + 1024) + 65536
+    assert kda.kda_chunk_bwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_F32) == w
+    assert kda.kda_chunk_bwd_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
+    assert kda.kda_chunk_bwd_workspace_size(2, 100, 2, 64, 64, 3, kda.KDA_BF16) == 0
+    v1 = kda.kda_chunk_bwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
+    v0 = kda.kda_chunk_bwd_workspace_size(1, 1000, 2, 64, 64, 0, kda.KDA_BF16)
+    assert v1 > v0 > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk_=96), 2), (dict(dv_=32), 2), (dict(io=4), 2), (dict(gt=9), 2),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1),
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(la=None), 1), (dict(beta=None), 1),
+    (dict(go=None), 1), (dict(dq=None), 1), (dict(dk=None), 1), (dict(dv=None), 1), (dict(dla=None), 1),
+    (dict(db=None), 1),
+    (dict(q=P + 4), 1), (dict(go=P + 8), 1), (dict(dv=P + 2), 1), (dict(dla=P + 4), 1),
+    (dict(h0=P + 4), 1), (dict(ghT=P + 8), 1), (dict(dh0=P + 2), 1), (dict(beta=P + 1), 1),
+    (dict(db=P + 2, gt=0), 1),
+    (dict(cu=P, N=2, B=2), 1), (dict(cu=P, N=0), 1), (dict(cu=P + 2, N=2), 1), (dict(N=3), 1),
+    (dict(ws=None), 3), (dict(wsb=0), 3), (dict(ws=P + 8), 1),
+    (dict(T=1 << 30, H=1 << 20), 1),
+])
+def test_bwd_rejects(kda, kw, code):
+    lib = kda.load_library()
+    assert bwd(lib, **kw) == code
+
+
+def test_bwd_empty_without_state_is_noop(kda):
+    lib = kda.load_library()
+    assert bwd(lib, T=0, q=None, k=None, v=None, la=None, beta=None, go=None, dq=None, dk=None, dv=None,
+               dla=None, db=None, dh0=None) == 0

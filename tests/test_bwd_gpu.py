@@ -1,0 +1,183 @@
+"""GPU parity of kda_chunk_bwd (through the C ABI) against the fp64 oracle's
+backward (oracle.bwd) on the same seeded inputs and upstream gradients.
+
+Tolerance, derived from the arithmetic: the backward computes every product
+and accumulation in fp32, and rounds each output once to its dtype.  A bf16
+output is then off by at most 2^-9 of its own size plus the fp32 error, so bf16
+outputs must meet max|d| <= 2^-8 max|ref| and ||d||_F <= 2^-8 ||ref||_F (twice
+the rounding bound); fp32 outputs (everything with fp32 I/O, and grad_h0 always)
+must meet 1e-4 relative in both norms, the forward's fp32 bound.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kda_testutil import errors, f64, to_oracle
+
+from gated_delta_rule_chunkwise_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16_REL = 2.0 ** -8
+F32_REL = 1e-4
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0")
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_chunkwise_amd as kda
+    kda.load_library()
+    return kda
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_bwd(kda, d, go, ghT, with_h0=True, want_dh0=True):
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = g["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    out = kda.kda_chunk_bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], go.to(DEV),
+                            h0=g["h0"] if with_h0 else None,
+                            grad_hT=None if ghT is None else ghT.to(DEV), cu_seqlens=cu,
+                            want_grad_h0=want_dh0)
+    torch.cuda.synchronize()
+    return [None if x is None else x.cpu() for x in out]
+
+
+def oracle_bwd(d, go, ghT, seqs=None, heads=None, with_h0=True):
+    ref = to_oracle(d, seqs, heads)
+    hs = slice(None) if heads is None else list(heads)
+    sq = list(range(len(d["lengths"]))) if seqs is None else list(seqs)
+    rows = torch.from_numpy(ref["rows"])
+    dO = f64(go[rows][:, hs])
+    dhT = None if ghT is None else f64(ghT[sq][:, hs])
+    res = oracle.bwd(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], dO,
+                     h0=ref["h0"] if with_h0 else None, d_hT=dhT, cu_seqlens=ref["cu_seqlens"])
+    return res, rows, hs, sq
+
+
+def check(kda, d, io, go, ghT, seqs=None, heads=None, with_h0=True, what=""):
+    out = run_bwd(kda, d, go, ghT, with_h0=with_h0)
+    ref, rows, hs, sq = oracle_bwd(d, go, ghT, seqs, heads, with_h0)
+    errs = {}
+    for name, g, r in zip(NAMES, out, ref):
+        g = g[sq][:, hs] if name == "dh0" else g[rows][:, hs]
+        e = errors(g, r)
+        tol = F32_REL if (io == "f32" or name == "dh0") else BF16_REL
+        assert e["rel_max"] <= tol and e["rel_fro"] <= tol, "%s %s: %s (tol %g)" % (what, name, e, tol)
+        errs[name] = "%.1e/%.1e" % (e["rel_max"], e["rel_fro"])
+    log(what, errs)
+    return out
+
+
+def test_bwd_c0_shape_fp32(kda):
+    d = I.make_chunk_inputs(I.C0, h0=True)
+    go, ghT = I.make_upstream_grads(d, 3000)
+    check(kda, d, "f32", go, ghT, what="c0")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_bwd_ragged_varlen_dims(kda, io, dk, dv):
+    """Lengths span partial, exact and multi-chunk sequences and an empty one."""
+    cfg = I.ChunkConfig("ragged", io, io, H=3, dk=dk, dv=dv, h0=True, seed=3100 + dk + dv)
+    d = I.make_chunk_inputs(cfg, lengths=[1, 63, 64, 65, 200, 0, 130])
+    go, ghT = I.make_upstream_grads(d, 3101)
+    check(kda, d, io, go, ghT, what="ragged %s %dx%d" % (io, dk, dv))
+
+
+def test_bwd_bf16_io_fp32_gates(kda):
+    cfg = I.ChunkConfig("mixed", "bf16", "f32", H=2, dk=128, dv=128, h0=True, seed=3200)
+    d = I.make_chunk_inputs(cfg, lengths=[300, 77])
+    go, ghT = I.make_upstream_grads(d, 3201)
+    check(kda, d, "bf16", go, ghT, what="bf16 io, f32 gates")
+
+
+def test_bwd_c1_shape_bf16(kda):
+    d = I.make_chunk_inputs(I.C1)
+    go, ghT = I.make_upstream_grads(d, 3300)
+    check(kda, d, "bf16", go, ghT, what="c1")
+
+
+def test_bwd_c3_sampled_heads(kda):
+    """Full long-context shape (T = 65,536, H = 32) in the launch the benchmark
+    times; the oracle checks two whole heads."""
+    d = I.make_chunk_inputs(I.C3)
+    go, ghT = I.make_upstream_grads(d, 3400, with_state=False)
+    check(kda, d, "bf16", go, None, heads=[0, 21], what="c3 heads 0,21")
+
+
+def test_bwd_without_state_inputs(kda):
+    """h0 = NULL, grad_hT = NULL; grad_h0 not requested, then requested."""
+    cfg = I.ChunkConfig("nostate", "bf16", "bf16", H=2, dk=128, dv=64, h0=False, seed=3500)
+    d = I.make_chunk_inputs(cfg, lengths=[150, 40])
+    go, _ = I.make_upstream_grads(d, 3501, with_state=False)
+    out = run_bwd(kda, d, go, None, with_h0=False, want_dh0=False)
+    assert out[5] is None
+    check(kda, d, "bf16", go, None, with_h0=False, what="no h0, no grad_hT")
+
+
+def test_bwd_bitwise_determinism(kda):
+    cfg = I.ChunkConfig("det", "bf16", "bf16", H=4, dk=128, dv=128, h0=True, seed=3600)
+    d = I.make_chunk_inputs(cfg, lengths=[500, 129])
+    go, ghT = I.make_upstream_grads(d, 3601)
+    a = run_bwd(kda, d, go, ghT)
+    b = run_bwd(kda, d, go, ghT)
+    for name, x, y in zip(NAMES, a, b):
+        assert torch.equal(x, y), name
+
+
+def test_bwd_out_of_range_chunk_is_nan(kda):
+    """A chunk whose key channel 0 decays by e^-192 (log_alpha = -3 on 64 tokens)
+    is outside the backward's fp32 range: every gradient of that sequence and
+    head is NaN; the other sequence is unaffected and matches the oracle."""
+    cfg = I.ChunkConfig("reset", "bf16", "bf16", H=2, dk=64, dv=64, h0=True, seed=3700)
+    d = I.make_chunk_inputs(cfg, lengths=[192, 100])
+    la = d["log_alpha"].clone()
+    la[64:128, 0, 0] = -3.0
+    d["log_alpha"] = la
+    go, ghT = I.make_upstream_grads(d, 3701)
+    out = run_bwd(kda, d, go, ghT)
+    for name, g in zip(NAMES, out):
+        bad = g[0, 0] if name == "dh0" else g[:192, 0]
+        assert torch.isnan(bad.float()).all(), name
+        ok = g[0, 1] if name == "dh0" else g[:192, 1]
+        assert torch.isfinite(ok.float()).all(), name
+    check(kda, d, "bf16", go, ghT, seqs=[1], what="other sequence")
+
+
+def test_bwd_matches_forward_directional_derivative(kda):
+    """Cross-check of the two GPU paths: for a random direction x' of all
+    inputs, <grad, x'> from kda_chunk_bwd equals the central difference of
+    <grad_o, o> + <grad_hT, h_T> computed with kda_chunk_fwd (fp32 I/O)."""
+    cfg = I.ChunkConfig("dir", "f32", "f32", H=2, dk=64, dv=64, h0=True, seed=3800)
+    d = I.make_chunk_inputs(cfg, lengths=[130, 70])
+    go, ghT = I.make_upstream_grads(d, 3801)
+    grads = run_bwd(kda, d, go, ghT)
+    gen = torch.Generator().manual_seed(3802)
+    keys = ("q", "k", "v", "log_alpha", "beta", "h0")
+    dirs = {k: torch.randn(d[k].shape, generator=gen, dtype=torch.float64) for k in keys}
+    dirs["log_alpha"] *= 0.1
+    cu = d["cu_seqlens"].to(DEV)
+
+    def loss(eps):
+        x = {k: (d[k].double() + eps * dirs[k]).float().to(DEV) for k in keys}
+        o, hT = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], h0=x["h0"],
+                                  cu_seqlens=cu)
+        return float((o.double().cpu() * go.double()).sum() + (hT.double().cpu() * ghT.double()).sum())
+
+    # The forward's own rounding (about 1e-5 relative per output) over ~3e4
+    # outputs puts about 2e-3 of noise on each loss; divided by 2 eps = 2e-2 that
+    # is about 0.1 on the difference quotient, against |<grad, x'>| ~ 1e2.
+    eps = 1e-2
+    fd = (loss(eps) - loss(-eps)) / (2 * eps)
+    an = sum(float((g.double() * dirs[k]).sum()) for g, k in zip(grads, keys))
+    log("directional derivative: fd %.6f analytic %.6f" % (fd, an))
+    assert abs(fd - an) <= 1e-2 * max(1.0, abs(an))
