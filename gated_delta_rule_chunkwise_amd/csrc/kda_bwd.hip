@@ -90,19 +90,22 @@ __device__ __forceinline__ void low_tile(int idx, int &R, int &I) {
     I = idx - (R * (R + 1)) / 2;
 }
 
-// Per chunk-head record (fp32, row-major, offsets in floats).
+// Per chunk-head record (fp32, row-major, offsets in floats).  The forward
+// replay reads [T, QA) and the reverse pass [KI, M), each one contiguous span.
+// Records, like every per-chunk array of the workspace, are indexed
+// [head][chunk slot], so that a chain walks through contiguous memory.
 template <int DK> struct BRec {
-    static constexpr size_t QA = 0;
-    static constexpr size_t KI = QA + (size_t)kB * DK;
+    static constexpr size_t T = 0;
+    static constexpr size_t KI = T + kB * kB;
     static constexpr size_t W = KI + (size_t)kB * DK;
-    static constexpr size_t T = W + (size_t)kB * DK;
-    static constexpr size_t P = T + kB * kB;
+    static constexpr size_t QA = W + (size_t)kB * DK;
+    static constexpr size_t P = QA + (size_t)kB * DK;
     static constexpr size_t M = P + kB * kB;
     static constexpr size_t EM = M + kB * kB;     // e^m
     static constexpr size_t EG = EM + DK;         // e^{g_n}
     static constexpr size_t EGM = EG + DK;        // e^{g_n - m}
     static constexpr size_t FLAG = EGM + DK;      // nonzero: decay out of range
-    static constexpr size_t FLOATS = (FLAG + 1 + 63) / 64 * 64;
+    static constexpr size_t FLOATS = (FLAG + 4 + 63) / 64 * 64;
 };
 
 struct BwdLayout {
@@ -148,16 +151,60 @@ __device__ __forceinline__ void seq_range(int64_t n, const int32_t *__restrict__
     }
 }
 
-// Copies a rows x COLS fp32 block (dense, row-major) from global memory into an
-// LDS array with row stride LS, 16 bytes per access.
-template <int COLS, int LS, int NT>
-__device__ __forceinline__ void copy_rows(float *dst, const float *__restrict__ src, int rows, int tid) {
-    constexpr int C4 = COLS / 4;
-    for (int i = tid; i < rows * C4; i += NT) {
-        const int r = i / C4, c = (i % C4) * 4;
-        *reinterpret_cast<f32x4_t *>(dst + r * LS + c) = *reinterpret_cast<const f32x4_t *>(src + (size_t)r * COLS + c);
+// 16-byte vectors of X, converted to fp32 on the way into LDS.
+template <typename X> struct Vec16;
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    typedef f32x4_t raw;
+};
+template <> struct Vec16<bf16_t> {
+    static constexpr int N = 8;
+    typedef bf16x8_t raw;
+};
+
+template <typename X>
+__device__ __forceinline__ void put_f32(float *dst, const typename Vec16<X>::raw &v, float scale) {
+    if constexpr (Vec16<X>::N == 4) {
+        *reinterpret_cast<f32x4_t *>(dst) = v * scale;
+    } else {
+        f32x4_t a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (float)v[e] * scale;
+            b[e] = (float)v[e + 4] * scale;
+        }
+        *reinterpret_cast<f32x4_t *>(dst) = a;
+        *reinterpret_cast<f32x4_t *>(dst + 4) = b;
     }
 }
+
+// A ROWS x COLS block of X (row r at src + r * pitch, rows >= nv read as zero)
+// moved into an fp32 LDS array with row stride LS by NT threads: load() issues
+// every 16-byte load into registers, store() writes them out (optionally scaled
+// per row), so that the loads can be in flight during unrelated work.
+template <int ROWS, int COLS, int NT, typename X> struct Stage {
+    static constexpr int VE = Vec16<X>::N, PER = COLS / VE, TOT = ROWS * PER, IT = (TOT + NT - 1) / NT;
+    static_assert(COLS % VE == 0, "row length must be a whole number of 16-byte vectors");
+    typename Vec16<X>::raw buf[IT];
+    __device__ __forceinline__ void load(const X *__restrict__ src, size_t pitch, int nv, int tid) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int i = tid + NT * it, r = i / PER;
+            typename Vec16<X>::raw z = {};
+            buf[it] = z;
+            if (i < TOT && r < nv)
+                buf[it] = *reinterpret_cast<const typename Vec16<X>::raw *>(src + (size_t)r * pitch + (i % PER) * VE);
+        }
+    }
+    template <int LS>
+    __device__ __forceinline__ void store(float *dst, int tid, const float *rscale = nullptr) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int i = tid + NT * it, r = i / PER;
+            if (i < TOT) put_f32<X>(dst + r * LS + (i % PER) * VE, buf[it], rscale ? rscale[r] : 1.f);
+        }
+    }
+};
 
 // ----------------------------------------------------------------------------
 // Prep: one workgroup of 4 waves per (chunk, head).
@@ -183,7 +230,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
                                                        const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
                                                        const int32_t *__restrict__ cu,
                                                        const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
-                                                       int H, float *__restrict__ recs) {
+                                                       int H, int64_t nch, float *__restrict__ recs) {
     using R = BRec<DK>;
     using S = PrepBS<DK>;
     __shared__ S sm;
@@ -193,32 +240,36 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
     int nv;
     if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    float *rec = recs + ((size_t)chunk * H + h) * R::FLOATS;
+    float *rec = recs + ((size_t)h * nch + chunk) * R::FLOATS;
 
     if (tid == 0) sm.flag = 0;
     if (tid < kB) sm.beta[tid] = tid < nv ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+    {   // q -> QA, k -> KA, log alpha -> KI, as fp32 (rows >= nv zero)
+        const size_t base = ((size_t)t0 * H + h) * DK, pitch = (size_t)H * DK;
+        Stage<kB, DK, 256, IO> sq, sk;
+        Stage<kB, DK, 256, GT> sl;
+        sq.load(q + base, pitch, nv, tid);
+        sk.load(k + base, pitch, nv, tid);
+        sl.load(log_alpha + base, pitch, nv, tid);
+        sq.template store<S::KS>(&sm.QA[0][0], tid);
+        sk.template store<S::KS>(&sm.KA[0][0], tid);
+        sl.template store<S::KS>(&sm.KI[0][0], tid);
+    }
     __syncthreads();
-    if (tid < DK) {
+    if (tid < DK) {   // column c: G (log2 units), then the decayed operands in place
         const int c = tid;
         float g2 = 0.f;
-        for (int r = 0; r < nv; ++r) g2 += to_f32(log_alpha[((t0 + r) * H + h) * DK + c]) * kBL2E;
+        for (int r = 0; r < nv; ++r) g2 += sm.KI[r][c] * kBL2E;
         const float m2 = 0.5f * g2;
         if (-g2 > kBwdMaxRange2 || !(g2 == g2)) sm.flag = 1;
         float G = 0.f;
-        for (int r = 0; r < kB; ++r) {
-            float qa = 0.f, ka = 0.f, ki = 0.f;
-            if (r < nv) {
-                const size_t o = ((t0 + r) * H + h) * DK + c;
-                G += to_f32(log_alpha[o]) * kBL2E;
-                const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
-                const float kv = to_f32(k[o]);
-                qa = to_f32(q[o]) * ea;
-                ka = kv * ea;
-                ki = kv * ei;
-            }
-            sm.QA[r][c] = qa;
-            sm.KA[r][c] = ka;
-            sm.KI[r][c] = ki;
+        for (int r = 0; r < nv; ++r) {
+            G += sm.KI[r][c] * kBL2E;
+            const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
+            const float kv = sm.KA[r][c];
+            sm.QA[r][c] *= ea;
+            sm.KA[r][c] = kv * ea;
+            sm.KI[r][c] = kv * ei;
         }
         rec[R::EM + c] = __builtin_amdgcn_exp2f(m2);
         rec[R::EG + c] = __builtin_amdgcn_exp2f(g2);
@@ -327,79 +378,149 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
 }
 
 // ----------------------------------------------------------------------------
-// Forward state replay: one workgroup of 4 waves per (sequence, head, block of
-// 16 value columns).
+// The two sequential passes: one workgroup of 8 waves per (sequence, head,
+// block of 16 value columns), walking the sequence's chunks.  The record span a
+// chunk needs is prefetched into registers (slot s of thread t holds float4
+// number t + 512 s of the span) while the previous chunk is computed.
+constexpr int kSP = 512;
+constexpr int kXCD = 8;
+
+// Block id -> (chain = sequence * H + head, column block).  Workgroups go to the
+// 8 XCDs round-robin by block id, so the NVB column blocks of one chain get ids
+// that are equal modulo 8: they run on one XCD and the chunk records they all
+// read are fetched once into that XCD's L2.  Ids past the last chain return.
+template <int NVB>
+__device__ __forceinline__ bool chain_of(int64_t id, int64_t chains, int64_t &chain, int &vb) {
+    const int64_t q = id / kXCD;
+    vb = (int)(q % NVB);
+    chain = id % kXCD + kXCD * (q / NVB);
+    return chain < chains;
+}
+
+int64_t chain_grid(int64_t chains, int nvb) { return (chains + kXCD - 1) / kXCD * kXCD * nvb; }
+
+template <int NS> struct SpanRegs {
+    f32x4_t r[NS];
+    __device__ __forceinline__ void load(const float *__restrict__ span, int tid) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) r[s] = *reinterpret_cast<const f32x4_t *>(span + 4 * (tid + kSP * s));
+    }
+};
+
+// Writes float4 number fl of a [rows][COLS] block into an LDS array of row stride LS.
+template <int COLS, int LS>
+__device__ __forceinline__ void put4(float *dst, int fl, const f32x4_t &x) {
+    *reinterpret_cast<f32x4_t *>(dst + (fl / (COLS / 4)) * LS + (fl % (COLS / 4)) * 4) = x;
+}
+
+// The per-channel factors and the flag: floats [EM, EM + 3 DK + 4) of a record.
+template <int DK> struct ColRegs {
+    f32x4_t r;
+    __device__ __forceinline__ void load(const float *__restrict__ rec, int tid) {
+        if (tid < 3 * DK / 4 + 1) r = *reinterpret_cast<const f32x4_t *>(rec + BRec<DK>::EM + 4 * tid);
+    }
+    __device__ __forceinline__ void store(float *cv, int tid) const {
+        if (tid < 3 * DK / 4 + 1) *reinterpret_cast<f32x4_t *>(cv + 4 * tid) = r;
+    }
+};
+
 template <int DK> struct FwdBS {
     static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
-    float W[kB][KS];
-    float KI[kB][KS];
     float T[kB][CS];
-    float V[kB][VS];                         // diag(beta) V block
+    float KI[kB][KS];
+    float W[kB][KS];
+    float V[kB][VS];
+    float beta[kB];
     float U[kB][VS];
     float S[DK][VS];
     float Sp[DK][VS];                        // Diag(e^m) S
-    float em[DK], eg[DK], egm[DK];
+    float cv[3 * DK + 4];                    // e^m, e^{g_n}, e^{g_n-m}, flag
 };
 
+// acc += A diag(bs) B over one 16x16 tile (B's rows scaled by bs).
+template <int K, int AI, int AK, int BK, int BJ>
+__device__ __forceinline__ f32x4_t mm_bs(f32x4_t acc, const float *a, const float *b, const float *bs, int lane) {
+    const float *pa = a + (lane & 15) * AI + (lane >> 4) * AK;
+    const float *pb = b + (lane >> 4) * BK + (lane & 15) * BJ;
+    const float *ps = bs + (lane >> 4);
+#pragma unroll
+    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * AK], pb[k * BK] * ps[k], acc);
+    return acc;
+}
+
 template <int DK, int DV, typename IO, typename GT>
-__global__ __launch_bounds__(256) void bwd_fwd_state_kernel(const IO *__restrict__ v, const GT *__restrict__ beta,
+__global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict__ v, const GT *__restrict__ beta,
                                                             const float *__restrict__ h0, const int32_t *__restrict__ cu,
-                                                            const int32_t *__restrict__ chunk_off, int64_t T, int H,
+                                                            const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
+                                                            int H, int64_t nch,
                                                             const float *__restrict__ recs, float *__restrict__ Sc,
                                                             float *__restrict__ Uc, float *__restrict__ sflag) {
     using R = BRec<DK>;
     using S = FwdBS<DK>;
     __shared__ S sm;
     constexpr int NVB = DV / kBV;
-    const int64_t id = blockIdx.x;
-    const int vb = (int)(id % NVB);
-    const int h = (int)((id / NVB) % H);
-    const int64_t n = id / ((int64_t)NVB * H);
+    constexpr int ST = kB * kB / 4 / kSP, SK = kB * DK / 4 / kSP, NS = ST + 2 * SK;
+    static_assert(ST * kSP * 4 == kB * kB && SK * kSP * 4 == kB * DK, "span slots");
+    int64_t chain;
+    int vb;
+    if (!chain_of<NVB>(blockIdx.x, (int64_t)N * H, chain, vb)) return;
+    const int h = (int)(chain % H);
+    const int64_t n = chain / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int j0 = vb * kBV;
     int64_t bos, eos, slot0;
     seq_range(n, cu, chunk_off, T, bos, eos, slot0);
+    const int nchunks = (int)((eos - bos + kB - 1) / kB);
 
-    for (int i = tid; i < DK * kBV; i += 256) {
+    for (int i = tid; i < DK * kBV; i += kSP) {
         const int c = i / kBV, j = i % kBV;
         sm.S[c][j] = h0 ? h0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
     }
-    const int nchunks = (int)((eos - bos + kB - 1) / kB);
+    SpanRegs<NS> pf;
+    ColRegs<DK> pc;
+    Stage<kB, kBV, kSP, IO> pv;
+    float pb = 0.f;
+    auto fetch = [&](int ci) {
+        const int64_t t0 = bos + (int64_t)kB * ci;
+        const int nv = (int)(eos - t0 < kB ? eos - t0 : kB);
+        const float *rec = recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS;
+        pf.load(rec + R::T, tid);
+        pc.load(rec, tid);
+        pv.load(v + ((size_t)t0 * H + h) * DV + j0, (size_t)H * DV, nv, tid);
+        const int r = tid - (kSP - kB);
+        if (r >= 0) pb = r < nv ? to_f32(beta[(t0 + r) * H + h]) : 0.f;
+    };
+    if (nchunks > 0) fetch(0);
     float anybad = 0.f;
     for (int ci = 0; ci < nchunks; ++ci) {
         const int64_t slot = slot0 + ci;
-        const int64_t t0 = bos + (int64_t)kB * ci;
-        const int nv = (int)(eos - t0 < kB ? eos - t0 : kB);
-        const float *rec = recs + ((size_t)slot * H + h) * R::FLOATS;
-        anybad = fmaxf(anybad, rec[R::FLAG]);
-        copy_rows<DK, S::KS, 256>(&sm.W[0][0], rec + R::W, kB, tid);
-        copy_rows<DK, S::KS, 256>(&sm.KI[0][0], rec + R::KI, kB, tid);
-        copy_rows<kB, S::CS, 256>(&sm.T[0][0], rec + R::T, kB, tid);
-        if (tid < DK) {
-            sm.em[tid] = rec[R::EM + tid];
-            sm.eg[tid] = rec[R::EG + tid];
-            sm.egm[tid] = rec[R::EGM + tid];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int f = tid + kSP * s;
+            if (s < ST) put4<kB, S::CS>(&sm.T[0][0], f, pf.r[s]);
+            else if (s < ST + SK) put4<DK, S::KS>(&sm.KI[0][0], f - ST * kSP, pf.r[s]);
+            else put4<DK, S::KS>(&sm.W[0][0], f - (ST + SK) * kSP, pf.r[s]);
         }
-        for (int i = tid; i < kB * kBV; i += 256) {
-            const int r = i / kBV, j = i % kBV;
-            float x = 0.f;
-            if (r < nv) x = to_f32(beta[(t0 + r) * H + h]) * to_f32(v[((t0 + r) * H + h) * DV + j0 + j]);
-            sm.V[r][j] = x;
-        }
+        pc.store(sm.cv, tid);
+        pv.template store<S::VS>(&sm.V[0][0], tid);
+        if (tid >= kSP - kB) sm.beta[tid - (kSP - kB)] = pb;
         __syncthreads();
-        float *sc = Sc + ((size_t)slot * H + h) * DK * DV;
-        for (int i = tid; i < DK * kBV; i += 256) {
+        if (ci + 1 < nchunks) fetch(ci + 1);
+        const float *em = sm.cv, *eg = sm.cv + DK, *egm = sm.cv + 2 * DK;
+        anybad = fmaxf(anybad, sm.cv[3 * DK]);
+        float *sc = Sc + ((size_t)h * nch + slot) * DK * DV;
+        for (int i = tid; i < DK * kBV; i += kSP) {
             const int c = i / kBV, j = i % kBV;
-            const float s = sm.S[c][j];
-            sc[(size_t)c * DV + j0 + j] = s;
-            sm.Sp[c][j] = sm.em[c] * s;
+            const float x = sm.S[c][j];
+            sc[(size_t)c * DV + j0 + j] = x;
+            sm.Sp[c][j] = em[c] * x;
         }
         __syncthreads();
-        {   // U = T diag(beta) V - W S', one row tile per wave
+        if (w < 4) {   // U = T diag(beta) V - W S', one row tile per wave
             f32x4_t a = zero4(), b = zero4();
-            a = mm<kB, S::CS, 1, S::VS, 1>(a, &sm.T[16 * w][0], &sm.V[0][0], lane);
+            a = mm_bs<kB, S::CS, 1, S::VS, 1>(a, &sm.T[16 * w][0], &sm.V[0][0], sm.beta, lane);
             b = mm<DK, S::KS, 1, S::VS, 1>(b, &sm.W[16 * w][0], &sm.Sp[0][0], lane);
-            float *uc = Uc + ((size_t)slot * H + h) * kB * DV;
+            float *uc = Uc + ((size_t)h * nch + slot) * kB * DV;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
@@ -409,14 +530,14 @@ __global__ __launch_bounds__(256) void bwd_fwd_state_kernel(const IO *__restrict
             }
         }
         __syncthreads();
-        // S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) KI^T U
-        for (int ct = w; ct < DK / 16; ct += 4) {
+        if (w < DK / 16) {   // S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) KI^T U
+            const int ct = w;
             f32x4_t a = zero4();
             a = mm<kB, 1, S::KS, S::VS, 1>(a, &sm.KI[0][16 * ct], &sm.U[0][0], lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
-                sm.S[c][j] = sm.eg[c] * sm.S[c][j] + sm.egm[c] * a[e];
+                sm.S[c][j] = eg[c] * sm.S[c][j] + egm[c] * a[e];
             }
         }
         __syncthreads();
@@ -426,104 +547,114 @@ __global__ __launch_bounds__(256) void bwd_fwd_state_kernel(const IO *__restrict
     if (vb == 0 && tid == 0) sflag[n * H + h] = anybad;
 }
 
-// ----------------------------------------------------------------------------
 // Reverse state-gradient pass: same grid, chunks in reverse order.
 template <int DK> struct RevBS {
     static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
-    float QA[kB][KS];
     float KI[kB][KS];
     float W[kB][KS];
+    float QA[kB][KS];
     float P[kB][CS];
     float dO[kB][VS];
     float dU[kB][VS];
     float dS[DK][VS];                        // dL/dS at the chunk's end
     float dSs[DK][VS];                       // Diag(e^{g_n-m}) dS
-    float em[DK], eg[DK], egm[DK];
-    float flag;
+    float cv[3 * DK + 4];                    // e^m, e^{g_n}, e^{g_n-m}, flag
 };
 
 template <int DK, int DV, typename IO>
-__global__ __launch_bounds__(256) void bwd_rev_state_kernel(const IO *__restrict__ d_o, const float *__restrict__ d_hT,
+__global__ __launch_bounds__(kSP) void bwd_rev_state_kernel(const IO *__restrict__ d_o, const float *__restrict__ d_hT,
                                                             const int32_t *__restrict__ cu,
-                                                            const int32_t *__restrict__ chunk_off, int64_t T, int H,
-                                                            const float *__restrict__ recs, float *__restrict__ dSc,
+                                                            const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
+                                                            int H, int64_t nch, const float *__restrict__ recs,
+                                                            float *__restrict__ dSc,
                                                             float *__restrict__ dUc, float *__restrict__ dh0) {
     using R = BRec<DK>;
     using S = RevBS<DK>;
     __shared__ S sm;
     constexpr int NVB = DV / kBV;
-    const int64_t id = blockIdx.x;
-    const int vb = (int)(id % NVB);
-    const int h = (int)((id / NVB) % H);
-    const int64_t n = id / ((int64_t)NVB * H);
+    constexpr int ST = kB * kB / 4 / kSP, SK = kB * DK / 4 / kSP, NS = 3 * SK + ST;
+    static_assert(ST * kSP * 4 == kB * kB && SK * kSP * 4 == kB * DK, "span slots");
+    int64_t chain;
+    int vb;
+    if (!chain_of<NVB>(blockIdx.x, (int64_t)N * H, chain, vb)) return;
+    const int h = (int)(chain % H);
+    const int64_t n = chain / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int j0 = vb * kBV;
     int64_t bos, eos, slot0;
     seq_range(n, cu, chunk_off, T, bos, eos, slot0);
+    const int nchunks = (int)((eos - bos + kB - 1) / kB);
 
-    for (int i = tid; i < DK * kBV; i += 256) {
+    for (int i = tid; i < DK * kBV; i += kSP) {
         const int c = i / kBV, j = i % kBV;
         sm.dS[c][j] = d_hT ? d_hT[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
     }
-    const int nchunks = (int)((eos - bos + kB - 1) / kB);
-    for (int ci = nchunks - 1; ci >= 0; --ci) {
-        const int64_t slot = slot0 + ci;
+    SpanRegs<NS> pf;
+    ColRegs<DK> pc;
+    Stage<kB, kBV, kSP, IO> po;
+    auto fetch = [&](int ci) {
         const int64_t t0 = bos + (int64_t)kB * ci;
         const int nv = (int)(eos - t0 < kB ? eos - t0 : kB);
-        const float *rec = recs + ((size_t)slot * H + h) * R::FLOATS;
-        copy_rows<DK, S::KS, 256>(&sm.QA[0][0], rec + R::QA, kB, tid);
-        copy_rows<DK, S::KS, 256>(&sm.KI[0][0], rec + R::KI, kB, tid);
-        copy_rows<DK, S::KS, 256>(&sm.W[0][0], rec + R::W, kB, tid);
-        copy_rows<kB, S::CS, 256>(&sm.P[0][0], rec + R::P, kB, tid);
-        if (tid < DK) {
-            sm.em[tid] = rec[R::EM + tid];
-            sm.eg[tid] = rec[R::EG + tid];
-            sm.egm[tid] = rec[R::EGM + tid];
+        const float *rec = recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS;
+        pf.load(rec + R::KI, tid);
+        pc.load(rec, tid);
+        po.load(d_o + ((size_t)t0 * H + h) * DV + j0, (size_t)H * DV, nv, tid);
+    };
+    if (nchunks > 0) fetch(nchunks - 1);
+    for (int ci = nchunks - 1; ci >= 0; --ci) {
+        const int64_t slot = slot0 + ci;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int f = tid + kSP * s;
+            if (s < SK) put4<DK, S::KS>(&sm.KI[0][0], f, pf.r[s]);
+            else if (s < 2 * SK) put4<DK, S::KS>(&sm.W[0][0], f - SK * kSP, pf.r[s]);
+            else if (s < 3 * SK) put4<DK, S::KS>(&sm.QA[0][0], f - 2 * SK * kSP, pf.r[s]);
+            else put4<kB, S::CS>(&sm.P[0][0], f - 3 * SK * kSP, pf.r[s]);
         }
-        if (tid == 0) sm.flag = rec[R::FLAG];
-        for (int i = tid; i < kB * kBV; i += 256) {
-            const int r = i / kBV, j = i % kBV;
-            sm.dO[r][j] = r < nv ? to_f32(d_o[((t0 + r) * H + h) * DV + j0 + j]) : 0.f;
-        }
+        pc.store(sm.cv, tid);
+        po.template store<S::VS>(&sm.dO[0][0], tid);
         __syncthreads();
-        float *dsc = dSc + ((size_t)slot * H + h) * DK * DV;
-        for (int i = tid; i < DK * kBV; i += 256) {
+        if (ci > 0) fetch(ci - 1);
+        const float *em = sm.cv, *eg = sm.cv + DK, *egm = sm.cv + 2 * DK;
+        const bool bad = sm.cv[3 * DK] != 0.f;
+        float *dsc = dSc + ((size_t)h * nch + slot) * DK * DV;
+        for (int i = tid; i < DK * kBV; i += kSP) {
             const int c = i / kBV, j = i % kBV;
-            const float s = sm.dS[c][j];
-            dsc[(size_t)c * DV + j0 + j] = s;
-            sm.dSs[c][j] = sm.egm[c] * s;
+            const float x = sm.dS[c][j];
+            dsc[(size_t)c * DV + j0 + j] = x;
+            sm.dSs[c][j] = egm[c] * x;
         }
         __syncthreads();
-        {   // dU = P^T dO + KI Diag(e^{g_n-m}) dS, one row tile per wave
-            f32x4_t a = zero4();
+        if (w < 4) {   // dU = P^T dO + KI Diag(e^{g_n-m}) dS, one row tile per wave
+            f32x4_t a = zero4(), b = zero4();
             a = mm<kB, 1, S::CS, S::VS, 1>(a, &sm.P[0][16 * w], &sm.dO[0][0], lane);
-            a = mm<DK, S::KS, 1, S::VS, 1>(a, &sm.KI[16 * w][0], &sm.dSs[0][0], lane);
-            float *duc = dUc + ((size_t)slot * H + h) * kB * DV;
+            b = mm<DK, S::KS, 1, S::VS, 1>(b, &sm.KI[16 * w][0], &sm.dSs[0][0], lane);
+            float *duc = dUc + ((size_t)h * nch + slot) * kB * DV;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
-                sm.dU[r][j] = a[e];
-                duc[(size_t)r * DV + j0 + j] = a[e];
+                const float x = a[e] + b[e];
+                sm.dU[r][j] = x;
+                duc[(size_t)r * DV + j0 + j] = x;
             }
         }
         __syncthreads();
-        // dS <- Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS
-        const bool bad = sm.flag != 0.f;
-        for (int ct = w; ct < DK / 16; ct += 4) {
+        if (w < DK / 16) {   // dS <- Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS
+            const int ct = w;
             f32x4_t a = zero4(), b = zero4();
             a = mm<kB, 1, S::KS, S::VS, 1>(a, &sm.QA[0][16 * ct], &sm.dO[0][0], lane);
             b = mm<kB, 1, S::KS, S::VS, 1>(b, &sm.W[0][16 * ct], &sm.dU[0][0], lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
-                const float x = sm.em[c] * (a[e] - b[e]) + sm.eg[c] * sm.dS[c][j];
+                const float x = em[c] * (a[e] - b[e]) + eg[c] * sm.dS[c][j];
                 sm.dS[c][j] = bad ? __builtin_nanf("") : x;
             }
         }
         __syncthreads();
     }
     if (dh0) {
-        for (int i = tid; i < DK * kBV; i += 256) {
+        for (int i = tid; i < DK * kBV; i += kSP) {
             const int c = i / kBV, j = i % kBV;
             dh0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] = sm.dS[c][j];
         }
@@ -562,7 +693,7 @@ template <int DK, int DV, typename IO, typename GT>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const IO *__restrict__ k, const IO *__restrict__ v, const GT *__restrict__ log_alpha,
     const GT *__restrict__ beta, const IO *__restrict__ d_o, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, int64_t N, int64_t T, int H, const float *__restrict__ recs,
+    const int32_t *__restrict__ chunk_off, int64_t N, int64_t T, int H, int64_t nch, const float *__restrict__ recs,
     const float *__restrict__ Sc, const float *__restrict__ Uc, const float *__restrict__ dSc,
     const float *__restrict__ dUc, const float *__restrict__ sflag, IO *__restrict__ dq, IO *__restrict__ dk,
     IO *__restrict__ dv, GT *__restrict__ dla, GT *__restrict__ dbeta) {
@@ -575,8 +706,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     int nv;
     if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const float *rec = recs + ((size_t)chunk * H + h) * R::FLOATS;
-    const size_t ch = (size_t)chunk * H + h;
+    const float *rec = recs + ((size_t)h * nch + chunk) * R::FLOATS;
+    const size_t ch = (size_t)h * nch + chunk;
     constexpr int NCT = DK / 16;             // key-column tiles
     constexpr int NOWN = 4 * NCT / 8;        // (row, key) tiles per wave
 
@@ -587,27 +718,38 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int i = 0; i < 4; ++i) sm.dbA[i][tid] = 0.f;
     }
     float dgn1 = 0.f;                        // thread c < DK: sum_j dS_next[c,j] S'[c,j]
+    {   // k and log alpha staged through the (still free) loop area; T from the record
+        const size_t base = ((size_t)t0 * H + h) * DK, pitch = (size_t)H * DK;
+        Stage<kB, DK, 512, IO> sk;
+        Stage<kB, DK, 512, GT> sl;
+        Stage<kB, kB, 512, float> st;
+        sk.load(k + base, pitch, nv, tid);
+        sl.load(log_alpha + base, pitch, nv, tid);
+        st.load(rec + R::T, kB, kB, tid);
+        sk.template store<S::KS>(&sm.r3.pt.QA[0][0], tid);
+        sl.template store<S::KS>(&sm.r3.pt.KI[0][0], tid);
+        st.template store<S::CS>(&sm.r2.m.T[0][0], tid);
+    }
+    __syncthreads();
     if (tid < DK) {
         const int c = tid;
         sm.em[c] = rec[R::EM + c];
         sm.eg[c] = rec[R::EG + c];
         sm.egm[c] = rec[R::EGM + c];
         float g2 = 0.f;
-        for (int r = 0; r < nv; ++r) g2 += to_f32(log_alpha[((t0 + r) * H + h) * DK + c]) * kBL2E;
+        for (int r = 0; r < nv; ++r) g2 += sm.r3.pt.KI[r][c] * kBL2E;
         const float m2 = 0.5f * g2;
         sm.m2[c] = m2;
         float G = 0.f;
         for (int r = 0; r < kB; ++r) {
             float ka = 0.f;
             if (r < nv) {
-                const size_t o = ((t0 + r) * H + h) * DK + c;
-                G += to_f32(log_alpha[o]) * kBL2E;
-                ka = to_f32(k[o]) * __builtin_amdgcn_exp2f(G - m2);
+                G += sm.r3.pt.KI[r][c] * kBL2E;
+                ka = sm.r3.pt.QA[r][c] * __builtin_amdgcn_exp2f(G - m2);
             }
             sm.KA[r][c] = ka;
         }
     }
-    copy_rows<kB, S::CS, 512>(&sm.r2.m.T[0][0], rec + R::T, kB, tid);
 
     f32x4_t aQ[NOWN], aK[NOWN], aB[NOWN];    // dQA, dY S'^T, U dS_next^T
 #pragma unroll
@@ -623,24 +765,33 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const float *duc = dUc + ch * kB * DV;
     const bool bad = sflag[n * H + h] != 0.f;
 
+    // The next 16-column block's operands are loaded into registers while the
+    // current one is processed.
+    Stage<kB, kBV, 512, IO> pO, pV;
+    Stage<kB, kBV, 512, float> pU, pdU;
+    Stage<DK, kBV, 512, float> pS, pdS;
+    auto fetch = [&](int vb) {
+        const int j0 = vb * kBV;
+        const size_t tb = ((size_t)t0 * H + h) * DV + j0, tp = (size_t)H * DV;
+        pO.load(d_o + tb, tp, nv, tid);
+        pV.load(v + tb, tp, nv, tid);
+        pU.load(uc + j0, DV, kB, tid);
+        pdU.load(duc + j0, DV, kB, tid);
+        pS.load(sc + j0, DV, DK, tid);
+        pdS.load(dsc + j0, DV, DK, tid);
+    };
+    fetch(0);
     for (int vb = 0; vb < DV / kBV; ++vb) {
         const int j0 = vb * kBV;
         __syncthreads();                     // previous block's reads done
-        for (int i = tid; i < kB * kBV; i += 512) {
-            const int r = i / kBV, j = i % kBV;
-            const bool ok = r < nv;
-            const size_t o = ((t0 + r) * H + h) * DV + j0 + j;
-            sm.r3.lp.dO[r][j] = ok ? to_f32(d_o[o]) : 0.f;
-            sm.r3.lp.X[r][j] = ok ? to_f32(v[o]) : 0.f;
-            sm.r3.lp.U[r][j] = uc[(size_t)r * DV + j0 + j];
-            sm.r3.lp.dU[r][j] = duc[(size_t)r * DV + j0 + j];
-        }
-        for (int i = tid; i < DK * kBV; i += 512) {
-            const int c = i / kBV, j = i % kBV;
-            sm.r3.lp.Sp[c][j] = sm.em[c] * sc[(size_t)c * DV + j0 + j];
-            sm.r3.lp.dSn[c][j] = dsc[(size_t)c * DV + j0 + j];
-        }
+        pO.template store<S::VS>(&sm.r3.lp.dO[0][0], tid);
+        pV.template store<S::VS>(&sm.r3.lp.X[0][0], tid);
+        pU.template store<S::VS>(&sm.r3.lp.U[0][0], tid);
+        pdU.template store<S::VS>(&sm.r3.lp.dU[0][0], tid);
+        pS.template store<S::VS>(&sm.r3.lp.Sp[0][0], tid, sm.em);
+        pdS.template store<S::VS>(&sm.r3.lp.dSn[0][0], tid);
         __syncthreads();
+        if (vb + 1 < DV / kBV) fetch(vb + 1);
         if (w < 4) {   // X = V - KA S'
             f32x4_t a = zero4();
             a = mm<DK, S::KS, 1, S::VS, 1>(a, &sm.KA[16 * w][0], &sm.r3.lp.Sp[0][0], lane);
@@ -746,8 +897,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             sm.r2.m.dM[r][c] = 0.f;
         }
     }
-    copy_rows<DK, S::KS, 512>(&sm.r3.pt.QA[0][0], rec + R::QA, kB, tid);
-    copy_rows<DK, S::KS, 512>(&sm.r3.pt.KI[0][0], rec + R::KI, kB, tid);
+    {
+        Stage<kB, DK, 512, float> sq, si;
+        sq.load(rec + R::QA, DK, kB, tid);
+        si.load(rec + R::KI, DK, kB, tid);
+        sq.template store<S::KS>(&sm.r3.pt.QA[0][0], tid);
+        si.template store<S::KS>(&sm.r3.pt.KI[0][0], tid);
+    }
     __syncthreads();
 
     f32x4_t aI[NOWN];                        // dKI
@@ -770,11 +926,17 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     }
     __syncthreads();                         // dP, dM, QA, KI reads done
 
-    if (tid < DK) {   // G (log2 units) again, into the freed area
+    {   // G (log2 units) again, into the freed area
+        Stage<kB, DK, 512, GT> sl;
+        sl.load(log_alpha + ((size_t)t0 * H + h) * DK, (size_t)H * DK, nv, tid);
+        sl.template store<DK>(&sm.r2.G2[0][0], tid);
+    }
+    __syncthreads();
+    if (tid < DK) {
         const int c = tid;
         float G = 0.f;
-        for (int r = 0; r < kB; ++r) {
-            if (r < nv) G += to_f32(log_alpha[((t0 + r) * H + h) * DK + c]) * kBL2E;
+        for (int r = 0; r < nv; ++r) {
+            G += sm.r2.G2[r][c] * kBL2E;
             sm.r2.G2[r][c] = G;
         }
     }
@@ -840,18 +1002,18 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
     if (L.nch > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((bwd_prep_kernel<DK, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st, q, k,
-                           la, be, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, recs);
-    const int64_t chains = a.num_seqs * a.H * (DV / kBV);
-    if (chains > 0) {
+                           la, be, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs);
+    const int64_t grid = chain_grid(a.num_seqs * a.H, DV / kBV);
+    if (grid > 0) {
         if (a.total_tokens > 0)
-            hipLaunchKernelGGL((bwd_fwd_state_kernel<DK, DV, IO, GT>), dim3((unsigned)chains), dim3(256), 0, st, v, be,
-                               a.h0, a.cu_seqlens, chunk_off, T, a.H, recs, Sc, Uc, sflag);
-        hipLaunchKernelGGL((bwd_rev_state_kernel<DK, DV, IO>), dim3((unsigned)chains), dim3(256), 0, st, dO, a.d_hT,
-                           a.cu_seqlens, chunk_off, T, a.H, recs, dSc, dUc, a.dh0);
+            hipLaunchKernelGGL((bwd_fwd_state_kernel<DK, DV, IO, GT>), dim3((unsigned)grid), dim3(kSP), 0, st, v, be,
+                               a.h0, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, sflag);
+        hipLaunchKernelGGL((bwd_rev_state_kernel<DK, DV, IO>), dim3((unsigned)grid), dim3(kSP), 0, st, dO, a.d_hT,
+                           a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, dSc, dUc, a.dh0);
     }
     if (L.nch > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st, k,
-                           v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, recs, Sc, Uc, dSc, dUc,
+                           v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, dSc, dUc,
                            sflag, static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv),
                            static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta));
     return hipGetLastError();
@@ -871,7 +1033,7 @@ size_t chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total;
 int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const BwdLayout L = bwd_layout(a);
-    if (L.nch > 0x7fffffffLL || a.num_seqs * a.H * (a.d_v / kBV) > 0x7fffffffLL) {
+    if (L.nch > 0x7fffffffLL || chain_grid(a.num_seqs * a.H, a.d_v / kBV) > 0x7fffffffLL) {
         snprintf(err, err_len, "chunk_bwd grid too large");
         return -1;
     }
