@@ -69,14 +69,41 @@ __device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// acc += A B over one 16x16 tile, K a multiple of 4, with
-// A(i, k) = a[i*AI + k*AK] and B(k, j) = b[k*BK + j*BJ].
+// Four consecutive-k values of an operand for one lane: one 16-byte LDS read
+// when the operand is contiguous along k (stride 1), else four reads.
+template <int STRIDE>
+__device__ __forceinline__ f32x4_t k4(const float *p) {
+    if constexpr (STRIDE == 1) {
+        return *reinterpret_cast<const f32x4_t *>(p);
+    } else {
+        f32x4_t v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = p[u * STRIDE];
+        return v;
+    }
+}
+
+// acc += A B over one 16x16 tile, K a multiple of 16, with
+// A(i, k) = a[i*AI + k*AK] and B(k, j) = b[k*BK + j*BJ].  Within each group of
+// 16 k values, lane group kq = lane/16 takes k = 16g + 4kq + u at step u, so an
+// operand with unit stride along k is read 4 values at a time.  (The matrix
+// instruction only requires A and B to agree on which k each lane supplies.)
 template <int K, int AI, int AK, int BK, int BJ>
 __device__ __forceinline__ f32x4_t mm(f32x4_t acc, const float *a, const float *b, int lane) {
-    const float *pa = a + (lane & 15) * AI + (lane >> 4) * AK;
-    const float *pb = b + (lane >> 4) * BK + (lane & 15) * BJ;
+    static_assert(K % 16 == 0, "K must be a multiple of 16");
+    constexpr int NG = K / 16;
+    const float *pa = a + (lane & 15) * AI + 4 * (lane >> 4) * AK;
+    const float *pb = b + 4 * (lane >> 4) * BK + (lane & 15) * BJ;
+    f32x4_t av[NG], bv[NG];                  // every operand read is issued first
 #pragma unroll
-    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * AK], pb[k * BK], acc);
+    for (int g = 0; g < NG; ++g) {
+        av[g] = k4<AK>(pa + 16 * g * AK);
+        bv[g] = k4<BK>(pb + 16 * g * BK);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = mfma4(av[g][u], bv[g][u], acc);
     return acc;
 }
 
@@ -196,6 +223,18 @@ template <int ROWS, int COLS, int NT, typename X> struct Stage {
                 buf[it] = *reinterpret_cast<const typename Vec16<X>::raw *>(src + (size_t)r * pitch + (i % PER) * VE);
         }
     }
+    // Transposed: element (r, c) goes to dst[c * LS + r].
+    template <int LS>
+    __device__ __forceinline__ void store_t(float *dst, int tid) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int i = tid + NT * it, r = i / PER, c = (i % PER) * VE;
+            if (i < TOT) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) dst[(c + e) * LS + r] = (float)buf[it][e];
+            }
+        }
+    }
     template <int LS>
     __device__ __forceinline__ void store(float *dst, int tid, const float *rscale = nullptr) const {
 #pragma unroll
@@ -208,9 +247,9 @@ template <int ROWS, int COLS, int NT, typename X> struct Stage {
 
 // ----------------------------------------------------------------------------
 // Prep: one workgroup of 4 waves per (chunk, head).
-template <int DK> struct PrepBS {
+template <int DK> struct alignas(16) PrepBS {
     static constexpr int KS = DK + 4;
-    static constexpr int CS = 66;
+    static constexpr int CS = kB + 4;
     float KA[kB][KS];
     float KI[kB][KS];
     union {
@@ -379,10 +418,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
 
 // ----------------------------------------------------------------------------
 // The two sequential passes: one workgroup of 8 waves per (sequence, head,
-// block of 16 value columns), walking the sequence's chunks.  The record span a
-// chunk needs is prefetched into registers (slot s of thread t holds float4
-// number t + 512 s of the span) while the previous chunk is computed.
-constexpr int kSP = 512;
+// block of 16 value columns), walking the sequence's chunks.  Waves 0-3 compute;
+// waves 4-7 only move data: they hold the next chunk's record span in registers
+// (slot s of loader thread t: float4 number t + 256 s of the span), write it
+// into LDS at the chunk boundary, issue the following chunk's loads while the
+// compute waves work, and store the per-chunk results.  The CU's vector-memory
+// pipe then never sits in front of the matrix products.
+constexpr int kSP = 512;                     // threads per workgroup
+constexpr int kLT = 256;                     // loader threads (waves 4-7)
 constexpr int kXCD = 8;
 
 // Block id -> (chain = sequence * H + head, column block).  Workgroups go to the
@@ -401,9 +444,9 @@ int64_t chain_grid(int64_t chains, int nvb) { return (chains + kXCD - 1) / kXCD 
 
 template <int NS> struct SpanRegs {
     f32x4_t r[NS];
-    __device__ __forceinline__ void load(const float *__restrict__ span, int tid) {
+    __device__ __forceinline__ void load(const float *__restrict__ span, int lt) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) r[s] = *reinterpret_cast<const f32x4_t *>(span + 4 * (tid + kSP * s));
+        for (int s = 0; s < NS; ++s) r[s] = *reinterpret_cast<const f32x4_t *>(span + 4 * (lt + kLT * s));
     }
 };
 
@@ -416,37 +459,62 @@ __device__ __forceinline__ void put4(float *dst, int fl, const f32x4_t &x) {
 // The per-channel factors and the flag: floats [EM, EM + 3 DK + 4) of a record.
 template <int DK> struct ColRegs {
     f32x4_t r;
-    __device__ __forceinline__ void load(const float *__restrict__ rec, int tid) {
-        if (tid < 3 * DK / 4 + 1) r = *reinterpret_cast<const f32x4_t *>(rec + BRec<DK>::EM + 4 * tid);
+    __device__ __forceinline__ void load(const float *__restrict__ rec, int lt) {
+        if (lt < 3 * DK / 4 + 1) r = *reinterpret_cast<const f32x4_t *>(rec + BRec<DK>::EM + 4 * lt);
     }
-    __device__ __forceinline__ void store(float *cv, int tid) const {
-        if (tid < 3 * DK / 4 + 1) *reinterpret_cast<f32x4_t *>(cv + 4 * tid) = r;
+    __device__ __forceinline__ void store(float *cv, int lt) const {
+        if (lt < 3 * DK / 4 + 1) *reinterpret_cast<f32x4_t *>(cv + 4 * lt) = r;
     }
 };
 
-template <int DK> struct FwdBS {
-    static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
+// acc += A diag(bs) B over one 16x16 tile (B's rows scaled by bs), k mapped as in mm.
+template <int K, int AI, int AK, int BK, int BJ>
+__device__ __forceinline__ f32x4_t mm_bs(f32x4_t acc, const float *a, const float *b, const float *bs, int lane) {
+    static_assert(K % 16 == 0, "K must be a multiple of 16");
+    constexpr int NG = K / 16;
+    const float *pa = a + (lane & 15) * AI + 4 * (lane >> 4) * AK;
+    const float *pb = b + 4 * (lane >> 4) * BK + (lane & 15) * BJ;
+    const float *ps = bs + 4 * (lane >> 4);
+    f32x4_t av[NG], bv[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        av[g] = k4<AK>(pa + 16 * g * AK);
+        bv[g] = k4<BK>(pb + 16 * g * BK) * k4<1>(ps + 16 * g);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = mfma4(av[g][u], bv[g][u], acc);
+    return acc;
+}
+
+// Stores a [ROWS][16] block held transposed in LDS (element (r, c) at
+// src[c * LS + r]) to global rows of the given pitch, with NT threads.
+template <int ROWS, int LS, int NT>
+__device__ __forceinline__ void block_out_t(float *__restrict__ dst, size_t pitch, const float *src, int t) {
+#pragma unroll
+    for (int i = t; i < ROWS * kBV / 4; i += NT) {
+        const int r = i / (kBV / 4), c = (i % (kBV / 4)) * 4;
+        f32x4_t x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = src[(c + e) * LS + r];
+        *reinterpret_cast<f32x4_t *>(dst + (size_t)r * pitch + c) = x;
+    }
+}
+
+// Blocks with the 16 value columns as rows (Vt, Ut, St) are kept transposed, so
+// that they are contiguous along the contraction index as B operands.
+template <int DK> struct alignas(16) FwdBS {
+    static constexpr int KS = DK + 4, CS = kB + 4;
     float T[kB][CS];
     float KI[kB][KS];
     float W[kB][KS];
-    float V[kB][VS];
+    float Vt[kBV][CS];                       // V^T block
     float beta[kB];
-    float U[kB][VS];
-    float S[DK][VS];
-    float Sp[DK][VS];                        // Diag(e^m) S
+    float Ut[kBV][CS];
+    float St[kBV][KS];                       // S^T block
     float cv[3 * DK + 4];                    // e^m, e^{g_n}, e^{g_n-m}, flag
 };
-
-// acc += A diag(bs) B over one 16x16 tile (B's rows scaled by bs).
-template <int K, int AI, int AK, int BK, int BJ>
-__device__ __forceinline__ f32x4_t mm_bs(f32x4_t acc, const float *a, const float *b, const float *bs, int lane) {
-    const float *pa = a + (lane & 15) * AI + (lane >> 4) * AK;
-    const float *pb = b + (lane >> 4) * BK + (lane & 15) * BJ;
-    const float *ps = bs + (lane >> 4);
-#pragma unroll
-    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * AK], pb[k * BK] * ps[k], acc);
-    return acc;
-}
 
 template <int DK, int DV, typename IO, typename GT>
 __global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict__ v, const GT *__restrict__ beta,
@@ -459,14 +527,16 @@ __global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict
     using S = FwdBS<DK>;
     __shared__ S sm;
     constexpr int NVB = DV / kBV;
-    constexpr int ST = kB * kB / 4 / kSP, SK = kB * DK / 4 / kSP, NS = ST + 2 * SK;
-    static_assert(ST * kSP * 4 == kB * kB && SK * kSP * 4 == kB * DK, "span slots");
+    constexpr int ST = kB * kB / 4 / kLT, SK = kB * DK / 4 / kLT;
+    static_assert(ST * kLT * 4 == kB * kB && SK * kLT * 4 == kB * DK, "span slots");
     int64_t chain;
     int vb;
     if (!chain_of<NVB>(blockIdx.x, (int64_t)N * H, chain, vb)) return;
     const int h = (int)(chain % H);
     const int64_t n = chain / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool loader = tid >= kSP - kLT;
+    const int lt = tid - (kSP - kLT);
     const int j0 = vb * kBV;
     int64_t bos, eos, slot0;
     seq_range(n, cu, chunk_off, T, bos, eos, slot0);
@@ -474,70 +544,75 @@ __global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict
 
     for (int i = tid; i < DK * kBV; i += kSP) {
         const int c = i / kBV, j = i % kBV;
-        sm.S[c][j] = h0 ? h0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
+        sm.St[j][c] = h0 ? h0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
     }
-    SpanRegs<NS> pf;
+    // Loader schedule per chunk: at the boundary, T, W, the factors, V and beta
+    // go into LDS; during the U products KI goes in (it is first read by the
+    // state update), the next chunk's T, W, V, beta and factors are requested and
+    // the start state is stored; during the state update the next KI is
+    // requested and U is stored.
+    SpanRegs<ST> pT;
+    SpanRegs<SK> pW, pK;
     ColRegs<DK> pc;
-    Stage<kB, kBV, kSP, IO> pv;
+    Stage<kB, kBV, kLT, IO> pv;
     float pb = 0.f;
-    auto fetch = [&](int ci) {
+    auto rec_of = [&](int ci) { return recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS; };
+    auto fetch_a = [&](int ci) {
         const int64_t t0 = bos + (int64_t)kB * ci;
         const int nv = (int)(eos - t0 < kB ? eos - t0 : kB);
-        const float *rec = recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS;
-        pf.load(rec + R::T, tid);
-        pc.load(rec, tid);
-        pv.load(v + ((size_t)t0 * H + h) * DV + j0, (size_t)H * DV, nv, tid);
-        const int r = tid - (kSP - kB);
+        const float *rec = rec_of(ci);
+        pT.load(rec + R::T, lt);
+        pW.load(rec + R::W, lt);
+        pc.load(rec, lt);
+        pv.load(v + ((size_t)t0 * H + h) * DV + j0, (size_t)H * DV, nv, lt);
+        const int r = lt - (kLT - kB);
         if (r >= 0) pb = r < nv ? to_f32(beta[(t0 + r) * H + h]) : 0.f;
     };
-    if (nchunks > 0) fetch(0);
+    if (loader && nchunks > 0) {
+        fetch_a(0);
+        pK.load(rec_of(0) + R::KI, lt);
+    }
     float anybad = 0.f;
     for (int ci = 0; ci < nchunks; ++ci) {
         const int64_t slot = slot0 + ci;
+        if (loader) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int f = tid + kSP * s;
-            if (s < ST) put4<kB, S::CS>(&sm.T[0][0], f, pf.r[s]);
-            else if (s < ST + SK) put4<DK, S::KS>(&sm.KI[0][0], f - ST * kSP, pf.r[s]);
-            else put4<DK, S::KS>(&sm.W[0][0], f - (ST + SK) * kSP, pf.r[s]);
+            for (int s = 0; s < ST; ++s) put4<kB, S::CS>(&sm.T[0][0], lt + kLT * s, pT.r[s]);
+#pragma unroll
+            for (int s = 0; s < SK; ++s) put4<DK, S::KS>(&sm.W[0][0], lt + kLT * s, pW.r[s]);
+            pc.store(sm.cv, lt);
+            pv.template store_t<S::CS>(&sm.Vt[0][0], lt);
+            if (lt >= kLT - kB) sm.beta[lt - (kLT - kB)] = pb;
         }
-        pc.store(sm.cv, tid);
-        pv.template store<S::VS>(&sm.V[0][0], tid);
-        if (tid >= kSP - kB) sm.beta[tid - (kSP - kB)] = pb;
         __syncthreads();
-        if (ci + 1 < nchunks) fetch(ci + 1);
         const float *em = sm.cv, *eg = sm.cv + DK, *egm = sm.cv + 2 * DK;
-        anybad = fmaxf(anybad, sm.cv[3 * DK]);
-        float *sc = Sc + ((size_t)h * nch + slot) * DK * DV;
-        for (int i = tid; i < DK * kBV; i += kSP) {
-            const int c = i / kBV, j = i % kBV;
-            const float x = sm.S[c][j];
-            sc[(size_t)c * DV + j0 + j] = x;
-            sm.Sp[c][j] = em[c] * x;
-        }
-        __syncthreads();
-        if (w < 4) {   // U = T diag(beta) V - W S', one row tile per wave
+        if (tid == 0) anybad = fmaxf(anybad, sm.cv[3 * DK]);
+        if (loader) {
+#pragma unroll
+            for (int s = 0; s < SK; ++s) put4<DK, S::KS>(&sm.KI[0][0], lt + kLT * s, pK.r[s]);
+            if (ci + 1 < nchunks) fetch_a(ci + 1);
+            block_out_t<DK, S::KS, kLT>(Sc + ((size_t)h * nch + slot) * DK * DV + j0, DV, &sm.St[0][0], lt);
+        } else {   // U = T diag(beta) V - W Diag(e^m) S, one row tile per wave
             f32x4_t a = zero4(), b = zero4();
-            a = mm_bs<kB, S::CS, 1, S::VS, 1>(a, &sm.T[16 * w][0], &sm.V[0][0], sm.beta, lane);
-            b = mm<DK, S::KS, 1, S::VS, 1>(b, &sm.W[16 * w][0], &sm.Sp[0][0], lane);
-            float *uc = Uc + ((size_t)h * nch + slot) * kB * DV;
+            a = mm_bs<kB, S::CS, 1, 1, S::CS>(a, &sm.T[16 * w][0], &sm.Vt[0][0], sm.beta, lane);
+            b = mm_bs<DK, S::KS, 1, 1, S::KS>(b, &sm.W[16 * w][0], &sm.St[0][0], em, lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
-                const float u = a[e] - b[e];
-                sm.U[r][j] = u;
-                uc[(size_t)r * DV + j0 + j] = u;
-            }
+            for (int e = 0; e < 4; ++e) sm.Ut[acc_col(lane)][16 * w + acc_row(lane, e)] = a[e] - b[e];
         }
         __syncthreads();
-        if (w < DK / 16) {   // S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) KI^T U
-            const int ct = w;
-            f32x4_t a = zero4();
-            a = mm<kB, 1, S::KS, S::VS, 1>(a, &sm.KI[0][16 * ct], &sm.U[0][0], lane);
+        if (loader) {
+            if (ci + 1 < nchunks) pK.load(rec_of(ci + 1) + R::KI, lt);
+            block_out_t<kB, S::CS, kLT>(Uc + ((size_t)h * nch + slot) * kB * DV + j0, DV, &sm.Ut[0][0], lt);
+        } else {   // S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) KI^T U
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
-                sm.S[c][j] = eg[c] * sm.S[c][j] + egm[c] * a[e];
+            for (int ct = w; ct < DK / 16; ct += 4) {
+                f32x4_t a = zero4();
+                a = mm<kB, 1, S::KS, 1, S::CS>(a, &sm.KI[0][16 * ct], &sm.Ut[0][0], lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
+                    sm.St[j][c] = eg[c] * sm.St[j][c] + egm[c] * a[e];
+                }
             }
         }
         __syncthreads();
@@ -547,17 +622,16 @@ __global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict
     if (vb == 0 && tid == 0) sflag[n * H + h] = anybad;
 }
 
-// Reverse state-gradient pass: same grid, chunks in reverse order.
-template <int DK> struct RevBS {
-    static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
+// Reverse state-gradient pass: same grid and roles, chunks in reverse order.
+template <int DK> struct alignas(16) RevBS {
+    static constexpr int KS = DK + 4, CS = kB + 4;
     float KI[kB][KS];
     float W[kB][KS];
     float QA[kB][KS];
     float P[kB][CS];
-    float dO[kB][VS];
-    float dU[kB][VS];
-    float dS[DK][VS];                        // dL/dS at the chunk's end
-    float dSs[DK][VS];                       // Diag(e^{g_n-m}) dS
+    float dOt[kBV][CS];                      // dO^T block
+    float dUt[kBV][CS];
+    float dSt[kBV][KS];                      // (dL/dS at the chunk's end)^T
     float cv[3 * DK + 4];                    // e^m, e^{g_n}, e^{g_n-m}, flag
 };
 
@@ -572,14 +646,16 @@ __global__ __launch_bounds__(kSP) void bwd_rev_state_kernel(const IO *__restrict
     using S = RevBS<DK>;
     __shared__ S sm;
     constexpr int NVB = DV / kBV;
-    constexpr int ST = kB * kB / 4 / kSP, SK = kB * DK / 4 / kSP, NS = 3 * SK + ST;
-    static_assert(ST * kSP * 4 == kB * kB && SK * kSP * 4 == kB * DK, "span slots");
+    constexpr int ST = kB * kB / 4 / kLT, SK = kB * DK / 4 / kLT;
+    static_assert(ST * kLT * 4 == kB * kB && SK * kLT * 4 == kB * DK, "span slots");
     int64_t chain;
     int vb;
     if (!chain_of<NVB>(blockIdx.x, (int64_t)N * H, chain, vb)) return;
     const int h = (int)(chain % H);
     const int64_t n = chain / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool loader = tid >= kSP - kLT;
+    const int lt = tid - (kSP - kLT);
     const int j0 = vb * kBV;
     int64_t bos, eos, slot0;
     seq_range(n, cu, chunk_off, T, bos, eos, slot0);
@@ -587,68 +663,76 @@ __global__ __launch_bounds__(kSP) void bwd_rev_state_kernel(const IO *__restrict
 
     for (int i = tid; i < DK * kBV; i += kSP) {
         const int c = i / kBV, j = i % kBV;
-        sm.dS[c][j] = d_hT ? d_hT[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
+        sm.dSt[j][c] = d_hT ? d_hT[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
     }
-    SpanRegs<NS> pf;
+    // Loader schedule per chunk: at the boundary, KI, P, the factors and dO go
+    // into LDS; during the dU products QA and W go in (first read by the
+    // state-gradient update), the previous chunk's KI, P, factors and dO are
+    // requested and the state gradient is stored; during the update the previous
+    // QA and W are requested and dU is stored.
+    SpanRegs<SK> pK;
+    SpanRegs<ST> pP;
+    SpanRegs<2 * SK> pWQ;                    // W and QA are adjacent in the record
     ColRegs<DK> pc;
-    Stage<kB, kBV, kSP, IO> po;
-    auto fetch = [&](int ci) {
+    Stage<kB, kBV, kLT, IO> po;
+    auto rec_of = [&](int ci) { return recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS; };
+    auto fetch_a = [&](int ci) {
         const int64_t t0 = bos + (int64_t)kB * ci;
         const int nv = (int)(eos - t0 < kB ? eos - t0 : kB);
-        const float *rec = recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS;
-        pf.load(rec + R::KI, tid);
-        pc.load(rec, tid);
-        po.load(d_o + ((size_t)t0 * H + h) * DV + j0, (size_t)H * DV, nv, tid);
+        const float *rec = rec_of(ci);
+        pK.load(rec + R::KI, lt);
+        pP.load(rec + R::P, lt);
+        pc.load(rec, lt);
+        po.load(d_o + ((size_t)t0 * H + h) * DV + j0, (size_t)H * DV, nv, lt);
     };
-    if (nchunks > 0) fetch(nchunks - 1);
+    if (loader && nchunks > 0) {
+        fetch_a(nchunks - 1);
+        pWQ.load(rec_of(nchunks - 1) + R::W, lt);
+    }
     for (int ci = nchunks - 1; ci >= 0; --ci) {
         const int64_t slot = slot0 + ci;
+        if (loader) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int f = tid + kSP * s;
-            if (s < SK) put4<DK, S::KS>(&sm.KI[0][0], f, pf.r[s]);
-            else if (s < 2 * SK) put4<DK, S::KS>(&sm.W[0][0], f - SK * kSP, pf.r[s]);
-            else if (s < 3 * SK) put4<DK, S::KS>(&sm.QA[0][0], f - 2 * SK * kSP, pf.r[s]);
-            else put4<kB, S::CS>(&sm.P[0][0], f - 3 * SK * kSP, pf.r[s]);
+            for (int s = 0; s < SK; ++s) put4<DK, S::KS>(&sm.KI[0][0], lt + kLT * s, pK.r[s]);
+#pragma unroll
+            for (int s = 0; s < ST; ++s) put4<kB, S::CS>(&sm.P[0][0], lt + kLT * s, pP.r[s]);
+            pc.store(sm.cv, lt);
+            po.template store_t<S::CS>(&sm.dOt[0][0], lt);
         }
-        pc.store(sm.cv, tid);
-        po.template store<S::VS>(&sm.dO[0][0], tid);
         __syncthreads();
-        if (ci > 0) fetch(ci - 1);
         const float *em = sm.cv, *eg = sm.cv + DK, *egm = sm.cv + 2 * DK;
-        const bool bad = sm.cv[3 * DK] != 0.f;
-        float *dsc = dSc + ((size_t)h * nch + slot) * DK * DV;
-        for (int i = tid; i < DK * kBV; i += kSP) {
-            const int c = i / kBV, j = i % kBV;
-            const float x = sm.dS[c][j];
-            dsc[(size_t)c * DV + j0 + j] = x;
-            sm.dSs[c][j] = egm[c] * x;
-        }
-        __syncthreads();
-        if (w < 4) {   // dU = P^T dO + KI Diag(e^{g_n-m}) dS, one row tile per wave
-            f32x4_t a = zero4(), b = zero4();
-            a = mm<kB, 1, S::CS, S::VS, 1>(a, &sm.P[0][16 * w], &sm.dO[0][0], lane);
-            b = mm<DK, S::KS, 1, S::VS, 1>(b, &sm.KI[16 * w][0], &sm.dSs[0][0], lane);
-            float *duc = dUc + ((size_t)h * nch + slot) * kB * DV;
+        if (loader) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
-                const float x = a[e] + b[e];
-                sm.dU[r][j] = x;
-                duc[(size_t)r * DV + j0 + j] = x;
+            for (int s = 0; s < 2 * SK; ++s) {
+                if (s < SK) put4<DK, S::KS>(&sm.W[0][0], lt + kLT * s, pWQ.r[s]);
+                else put4<DK, S::KS>(&sm.QA[0][0], lt + kLT * (s - SK), pWQ.r[s]);
             }
+            if (ci > 0) fetch_a(ci - 1);
+            block_out_t<DK, S::KS, kLT>(dSc + ((size_t)h * nch + slot) * DK * DV + j0, DV, &sm.dSt[0][0], lt);
+        } else {   // dU = P^T dO + KI Diag(e^{g_n-m}) dS, one row tile per wave
+            f32x4_t a = zero4(), b = zero4();
+            a = mm<kB, 1, S::CS, 1, S::CS>(a, &sm.P[0][16 * w], &sm.dOt[0][0], lane);
+            b = mm_bs<DK, S::KS, 1, 1, S::KS>(b, &sm.KI[16 * w][0], &sm.dSt[0][0], egm, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.dUt[acc_col(lane)][16 * w + acc_row(lane, e)] = a[e] + b[e];
         }
         __syncthreads();
-        if (w < DK / 16) {   // dS <- Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS
-            const int ct = w;
-            f32x4_t a = zero4(), b = zero4();
-            a = mm<kB, 1, S::KS, S::VS, 1>(a, &sm.QA[0][16 * ct], &sm.dO[0][0], lane);
-            b = mm<kB, 1, S::KS, S::VS, 1>(b, &sm.W[0][16 * ct], &sm.dU[0][0], lane);
+        if (loader) {
+            if (ci > 0) pWQ.load(rec_of(ci - 1) + R::W, lt);
+            block_out_t<kB, S::CS, kLT>(dUc + ((size_t)h * nch + slot) * kB * DV + j0, DV, &sm.dUt[0][0], lt);
+        } else {   // dS <- Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS
+            const bool bad = sm.cv[3 * DK] != 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
-                const float x = em[c] * (a[e] - b[e]) + eg[c] * sm.dS[c][j];
-                sm.dS[c][j] = bad ? __builtin_nanf("") : x;
+            for (int ct = w; ct < DK / 16; ct += 4) {
+                f32x4_t a = zero4(), b = zero4();
+                a = mm<kB, 1, S::KS, 1, S::CS>(a, &sm.QA[0][16 * ct], &sm.dOt[0][0], lane);
+                b = mm<kB, 1, S::KS, 1, S::CS>(b, &sm.W[0][16 * ct], &sm.dUt[0][0], lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
+                    const float x = em[c] * (a[e] - b[e]) + eg[c] * sm.dSt[j][c];
+                    sm.dSt[j][c] = bad ? __builtin_nanf("") : x;
+                }
             }
         }
         __syncthreads();
@@ -656,14 +740,14 @@ __global__ __launch_bounds__(kSP) void bwd_rev_state_kernel(const IO *__restrict
     if (dh0) {
         for (int i = tid; i < DK * kBV; i += kSP) {
             const int c = i / kBV, j = i % kBV;
-            dh0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] = sm.dS[c][j];
+            dh0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] = sm.dSt[j][c];
         }
     }
 }
 
 // ----------------------------------------------------------------------------
 // Gradient kernel: one workgroup of 8 waves per (chunk, head).
-template <int DK> struct GradBS {
+template <int DK> struct alignas(16) GradBS {
     static constexpr int KS = DK + 4, CS = kB + 4, VS = kBV + 4;
     float KA[kB][KS];
     union {
