@@ -10,7 +10,8 @@ on raw projections through the fused input prologue (kda_chunk_fwd_prologue)
 under "prologue"; the same shape with one decay per token and head (Gated
 DeltaNet) and with none (DeltaNet), through kda_gdn_chunk_fwd, under "gdn"; and
 with separate erase and write strengths (kda_chunk_fwd_decoupled) under
-"decoupled".
+"decoupled"; the gradients of the same prefill (kda_chunk_bwd) under
+"backward".
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -31,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix peak, published
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak, published
 METRIC = "KDA chunk_fwd tokens/s + % MFMA peak; decode step HBM GB/s (1×MI355X)"
 
 
@@ -51,6 +53,27 @@ def chunk_alg_flops(tok_heads, dk, dv, C=64):
     return tok_heads * per
 
 
+def bwd_alg_flops(tok_heads, dk, dv, C=64):
+    """Algorithmic flops per token-head of the chunkwise backward (triangles as
+    triangles): the prep (the two Gram blocks, the UT transform, W), the state
+    replay (U, the state update), the reverse pass (dU, the state gradient) and
+    the per-chunk gradients (X, dY, dP, dA, dQA, dKA, dKB, dKI)."""
+    prep = C * dk + C * C / 6 + (C - 1) / 2 * dk
+    replay = (C - 1) / 2 * dv + 2 * dk * dv
+    reverse = (C + 1) / 2 * dv + 3 * dk * dv
+    grads = 4 * dk * dv + 3 * C / 2 * dv + C * dk + C * dk
+    return tok_heads * 2 * (prep + replay + reverse + grads)
+
+
+def bwd_alg_bytes(tok_heads, dk, dv, io_b=2, gate_b=2):
+    """Algorithmic HBM bytes of one backward call: q, k, v, log_alpha, beta and
+    grad_o read, grad_q, grad_k, grad_v, grad_log_alpha and grad_beta written,
+    per token-head."""
+    reads = (2 * dk + 2 * dv) * io_b + dk * gate_b + gate_b
+    writes = (2 * dk + dv) * io_b + dk * gate_b + gate_b
+    return tok_heads * (reads + writes)
+
+
 def decode_alg_bytes(B, H, dk, dv, io_b=2, gate_b=2):
     per_state = 2 * dk * dv * 4 + (2 * dk + 2 * dv) * io_b + dk * gate_b + gate_b
     return B * H * per_state
@@ -58,6 +81,7 @@ def decode_alg_bytes(B, H, dk, dv, io_b=2, gate_b=2):
 
 CHUNK_SOURCES = ("kda_chunk.hip", "kda_chunk2.hip", "kda_chunk_common.h", "kda_device.h")
 DECODE_SOURCES = ("kda_decode.hip", "kda_device.h")
+BWD_SOURCES = ("kda_bwd.hip", "kda_plan.h", "kda_device.h")
 
 
 def source_digest(files):
@@ -133,6 +157,24 @@ def cpu_baseline_chunk(d, heads, T_sample, H_total):
                       % (heads, T_sample, tok_heads, dt, H_total)}
 
 
+def cpu_baseline_bwd(d, go, heads, T_sample, H_total):
+    """Times the oracle's backward (as it stands) on a bounded sample: `heads`
+    whole chains over the first T_sample tokens of the same inputs."""
+    import oracle
+    oracle.build(force=False)
+    sl = slice(0, T_sample)
+    f = lambda x: np.ascontiguousarray(x[sl][:, :heads].to("cpu", torch.float64).numpy())
+    q, k, v, la, be, do = (f(x) for x in (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], go))
+    nthreads = min(heads, oracle.default_threads())
+    t0 = time.perf_counter()
+    oracle.bwd(q, k, v, la, be, do, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    tok_heads = heads * T_sample
+    return {"value": tok_heads / H_total / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": "fp64 reverse-mode per-token recurrence, %d heads x first %d tokens (%d token-heads, "
+                      "%.1f s); tokens/s = token-heads/s / %d heads" % (heads, T_sample, tok_heads, dt, H_total)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +185,7 @@ def main():
     ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--no-decoupled", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -265,6 +308,35 @@ def main():
                          "traffic": load_traffic("chunk_fwd_decoupled_prefill_h32_t65536_traffic.json", digest),
                          "alg_bytes_per_launch": db_}}
         del wv
+
+    # ---------------- backward of the same prefill
+    if not args.no_backward:
+        go, _ = I.make_upstream_grads(d, 3400, device=dev, with_state=False)
+        ws = torch.empty(kda.kda_chunk_bwd_workspace_size(1, T, H, dk, dv, 0, kda.KDA_BF16),
+                         dtype=torch.uint8, device=dev)
+        a4 = [x.unsqueeze(0) for x in args_c]
+        fnb = lambda: kda.kda_chunk_bwd(*a4, go.unsqueeze(0), want_grad_h0=False, workspace=ws)
+        per_b, _ = time_launches(fnb, args.steps, args.warmup, stream)
+        bms = float(np.mean(per_b))
+        bf = bwd_alg_flops(tok_heads, dk, dv)
+        bb = bwd_alg_bytes(tok_heads, dk, dv)
+        out["backward"] = {
+            "workload": "kda_chunk_bwd on the same inputs, grad_o ~ N(0,1) bf16 (seed 3400), no grad_hT, "
+                        "no h0; fp32 arithmetic on the fp32 matrix cores",
+            "ms_per_step": bms, "tokens_per_s": T / (bms * 1e-3), "vs_forward_ms": bms / ms,
+            "roofline": {"bound": "mfma", "achieved": bf / (bms * 1e-3) / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": bf / (bms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+                         "traffic": load_traffic("chunk_bwd_prefill_h32_t65536_traffic.json",
+                                                 source_digest(BWD_SOURCES)),
+                         "kernel": "kda_chunk_bwd = bwd_prep_kernel + bwd_fwd_state_kernel + "
+                                   "bwd_rev_state_kernel + bwd_grad_kernel <128,128,bf16,bf16>",
+                         "alg_flops_per_launch": bf},
+            "hbm": {"alg_bytes_per_launch": bb, "achieved_gbs": bb / (bms * 1e-3) / 1e9,
+                    "frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "workspace_bytes": ws.numel()}
+        if not args.no_cpu_baseline:
+            out["backward"]["cpu_baseline"] = cpu_baseline_bwd(d, go, 2, 16384, H)
+        del go, ws, a4
 
     # ---------------- decode step
     if not args.no_decode:
