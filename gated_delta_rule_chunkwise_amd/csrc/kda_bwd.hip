@@ -62,6 +62,13 @@ constexpr int kB = kPlanChunk;                    // chunk length, 64
 constexpr float kBL2E = 1.4426950408889634f;
 constexpr float kBwdMaxRange2 = 230.f;            // max in-chunk decay, log2 units
 constexpr int kBV = 16;                           // value columns per block
+// Column scans over a chunk (the in-chunk cumsum of log alpha and the reverse
+// cumsum of its gradient) run as kSeg segments of kSegRows rows per key
+// channel, in parallel: G_r = (sum of the earlier segments' totals) + (running
+// sum within r's segment).  The chunk total, summed from the same segment
+// totals in the same order, then equals G at the last row bitwise, and every
+// kernel that forms G forms it identically.
+constexpr int kSeg = 4, kSegRows = kB / kSeg;
 
 // D(16x16) += A(16x4) B(4x16), fp32.  Lane l holds A[l%16][l/16],
 // B[l/16][l%16] and D[4*(l/16) + e][l%16], e = 0..3.
@@ -261,6 +268,7 @@ template <int DK> struct alignas(16) PrepBS {
     };
     float X[4][16][20];                      // per-wave product tile
     float beta[kB];
+    float part[kSeg][DK];                    // segment totals of the column scan
     int flag;
 };
 
@@ -295,24 +303,45 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
         sl.template store<S::KS>(&sm.KI[0][0], tid);
     }
     __syncthreads();
-    if (tid < DK) {   // column c: G (log2 units), then the decayed operands in place
-        const int c = tid;
-        float g2 = 0.f;
-        for (int r = 0; r < nv; ++r) g2 += sm.KI[r][c] * kBL2E;
-        const float m2 = 0.5f * g2;
-        if (-g2 > kBwdMaxRange2 || !(g2 == g2)) sm.flag = 1;
-        float G = 0.f;
-        for (int r = 0; r < nv; ++r) {
-            G += sm.KI[r][c] * kBL2E;
-            const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
-            const float kv = sm.KA[r][c];
-            sm.QA[r][c] *= ea;
-            sm.KA[r][c] = kv * ea;
-            sm.KI[r][c] = kv * ei;
+    {   // G (log2 units) per key channel, segment totals first
+        constexpr int PT = 256 / DK;
+        const int c = tid % DK, p = tid / DK;
+        for (int sg = p; sg < kSeg; sg += PT) {
+            const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
+            float l = 0.f;
+            for (int r = r0; r < r1; ++r) l += sm.KI[r][c] * kBL2E;
+            sm.part[sg][c] = l;
         }
-        rec[R::EM + c] = __builtin_amdgcn_exp2f(m2);
-        rec[R::EG + c] = __builtin_amdgcn_exp2f(g2);
-        rec[R::EGM + c] = __builtin_amdgcn_exp2f(g2 - m2);
+    }
+    __syncthreads();
+    {   // then the decayed operands in place
+        constexpr int PT = 256 / DK;
+        const int c = tid % DK, p = tid / DK;
+        float g2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSeg; ++i) g2 += sm.part[i][c];
+        const float m2 = 0.5f * g2;
+        for (int sg = p; sg < kSeg; sg += PT) {
+            float pre = 0.f;
+            for (int i = 0; i < sg; ++i) pre += sm.part[i][c];
+            const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
+            float l = 0.f;
+            for (int r = r0; r < r1; ++r) {
+                l += sm.KI[r][c] * kBL2E;
+                const float G = pre + l;
+                const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
+                const float kv = sm.KA[r][c];
+                sm.QA[r][c] *= ea;
+                sm.KA[r][c] = kv * ea;
+                sm.KI[r][c] = kv * ei;
+            }
+        }
+        if (p == 0) {
+            if (-g2 > kBwdMaxRange2 || !(g2 == g2)) sm.flag = 1;
+            rec[R::EM + c] = __builtin_amdgcn_exp2f(m2);
+            rec[R::EG + c] = __builtin_amdgcn_exp2f(g2);
+            rec[R::EGM + c] = __builtin_amdgcn_exp2f(g2 - m2);
+        }
     }
     __syncthreads();
     if (tid == 0) rec[R::FLAG] = sm.flag ? 1.f : 0.f;
@@ -771,6 +800,8 @@ template <int DK> struct alignas(16) GradBS {
     float dbr[kB];
     float dbA[4][kB];
     float m2[DK], em[DK], eg[DK], egm[DK];
+    float part[kSeg][DK], partk[kSeg][DK];   // segment totals of the column scans
+    float dgn1[DK];
 };
 
 template <int DK, int DV, typename IO, typename GT>
@@ -815,21 +846,36 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         st.template store<S::CS>(&sm.r2.m.T[0][0], tid);
     }
     __syncthreads();
+    const int sc_c = tid % DK, sc_p = tid / DK;   // column-scan roles: channel, segment
     if (tid < DK) {
-        const int c = tid;
-        sm.em[c] = rec[R::EM + c];
-        sm.eg[c] = rec[R::EG + c];
-        sm.egm[c] = rec[R::EGM + c];
-        float g2 = 0.f;
-        for (int r = 0; r < nv; ++r) g2 += sm.r3.pt.KI[r][c] * kBL2E;
+        sm.em[tid] = rec[R::EM + tid];
+        sm.eg[tid] = rec[R::EG + tid];
+        sm.egm[tid] = rec[R::EGM + tid];
+    }
+    if (sc_p < kSeg) {   // G (log2 units), as the prep kernel forms it: segment totals
+        const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
+        float l = 0.f;
+        for (int r = r0; r < r1; ++r) l += sm.r3.pt.KI[r][sc_c] * kBL2E;
+        sm.part[sc_p][sc_c] = l;
+    }
+    __syncthreads();
+    if (sc_p < kSeg) {   // then KA = K e^{G - m} per segment
+        const int c = sc_c;
+        float g2 = 0.f, pre = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSeg; ++i) {
+            g2 += sm.part[i][c];
+            if (i < sc_p) pre += sm.part[i][c];
+        }
         const float m2 = 0.5f * g2;
-        sm.m2[c] = m2;
-        float G = 0.f;
-        for (int r = 0; r < kB; ++r) {
+        if (sc_p == 0) sm.m2[c] = m2;
+        const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
+        float l = 0.f;
+        for (int r = r0; r < kSegRows + r0; ++r) {
             float ka = 0.f;
-            if (r < nv) {
-                G += sm.r3.pt.KI[r][c] * kBL2E;
-                ka = sm.r3.pt.QA[r][c] * __builtin_amdgcn_exp2f(G - m2);
+            if (r < r1) {
+                l += sm.r3.pt.KI[r][c] * kBL2E;
+                ka = sm.r3.pt.QA[r][c] * __builtin_amdgcn_exp2f((pre + l) - m2);
             }
             sm.KA[r][c] = ka;
         }
@@ -1016,12 +1062,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         sl.template store<DK>(&sm.r2.G2[0][0], tid);
     }
     __syncthreads();
-    if (tid < DK) {
-        const int c = tid;
-        float G = 0.f;
-        for (int r = 0; r < nv; ++r) {
-            G += sm.r2.G2[r][c] * kBL2E;
-            sm.r2.G2[r][c] = G;
+    if (sc_p < kSeg) {   // segment totals, then G in place (as above)
+        const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
+        float l = 0.f;
+        for (int r = r0; r < r1; ++r) l += sm.r2.G2[r][sc_c] * kBL2E;
+        sm.part[sc_p][sc_c] = l;
+    }
+    __syncthreads();
+    if (sc_p < kSeg) {
+        float pre = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSeg; ++i)
+            if (i < sc_p) pre += sm.part[i][sc_c];
+        const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
+        float l = 0.f;
+        for (int r = r0; r < r1; ++r) {
+            l += sm.r2.G2[r][sc_c] * kBL2E;
+            sm.r2.G2[r][sc_c] = pre + l;
         }
     }
     __syncthreads();
@@ -1048,21 +1105,37 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         }
     }
     __syncthreads();
-    if (tid < DK) {
-        const int c = tid;
-        float kbs = 0.f;
-        for (int r = 0; r < kB; ++r) kbs += sm.r3.pt.KI[r][c];
-        const float dgn = sm.egm[c] * (dgn1 + kbs);
-        float s = 0.f;
-        for (int r = nv - 1; r >= 0; --r) {
-            s += sm.r3.pt.QA[r][c];
-            dla[((t0 + r) * H + h) * DK + c] = from_f32<GT>(bad ? qnan : s + dgn);
+    if (sc_p < kSeg) {   // segment totals of dG and of the KI-weighted U dS_next^T
+        const int r0 = sc_p * kSegRows;
+        float d = 0.f, kb = 0.f;
+        for (int r = r0; r < r0 + kSegRows; ++r) {
+            d += sm.r3.pt.QA[r][sc_c];
+            kb += sm.r3.pt.KI[r][sc_c];
         }
-    } else if (tid >= 256 && tid < 256 + kB) {
-        const int r = tid - 256;
-        if (r < nv) {
-            const float x = sm.dbr[r] + ((sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]));
-            dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
+        sm.part[sc_p][sc_c] = d;
+        sm.partk[sc_p][sc_c] = kb;
+    }
+    if (tid < DK) sm.dgn1[tid] = dgn1;
+    if (tid < kB && tid < nv) {
+        const int r = tid;
+        const float x = sm.dbr[r] + ((sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]));
+        dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
+    }
+    __syncthreads();
+    if (sc_p < kSeg) {   // dlog alpha: reverse cumsum of dG plus dg_n
+        const int c = sc_c;
+        float kbs = 0.f, suf = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSeg; ++i) {
+            kbs += sm.partk[i][c];
+            if (i > sc_p) suf += sm.part[i][c];
+        }
+        const float dgn = sm.egm[c] * (sm.dgn1[c] + kbs);
+        const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
+        float sacc = suf;
+        for (int r = r1 - 1; r >= r0; --r) {
+            sacc += sm.r3.pt.QA[r][c];
+            dla[((t0 + r) * H + h) * DK + c] = from_f32<GT>(bad ? qnan : sacc + dgn);
         }
     }
 }
