@@ -114,6 +114,17 @@ def test_bwd_c3_sampled_heads(kda):
     check(kda, d, "bf16", go, None, heads=[0, 21], what="c3 heads 0,21")
 
 
+def test_bwd_c2_varlen_sampled(kda):
+    """Full-size packed batch (32 sequences of 512-8192 tokens, h0 != 0, with
+    grad_hT) in one call; the oracle checks three whole sequences, including the
+    longest and the shortest."""
+    d = I.make_chunk_inputs(I.C2)
+    go, ghT = I.make_upstream_grads(d, 3450)
+    lens = d["lengths"]
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7})
+    check(kda, d, "bf16", go, ghT, seqs=seqs, what="c2 seqs %s" % seqs)
+
+
 def test_bwd_without_state_inputs(kda):
     """h0 = NULL, grad_hT = NULL; grad_h0 not requested, then requested."""
     cfg = I.ChunkConfig("nostate", "bf16", "bf16", H=2, dk=128, dv=64, h0=False, seed=3500)
