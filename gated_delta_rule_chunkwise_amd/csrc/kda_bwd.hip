@@ -22,6 +22,7 @@
 //     dKA = -diag(beta) dY S'^T + dM KI
 //     dKI = dP^T QA + dM^T KA + Diag-cols(e^{g_n-m}) (U dS_next^T)
 //     dbeta_r = sum_j dY[r,j] X[r,j] + sum_i dA[r,i] M[r,i]
+//             (sum_j dY X taken as sum_j dY V - sum_c KA (dY S'^T), so X is never formed)
 //     dQ = dQA.e^{G-m},  dK = dKA.e^{G-m} + dKI.e^{m-G}
 //     dG = dQA.QA + dKA.KA - dKI.KI
 //     dg_n[c] = e^{g_n-m}[c] (sum_j dS_next[c,j] S'[c,j] + sum_r (U dS_next^T)[r,c] KI[r,c])
@@ -788,7 +789,7 @@ template <int DK> struct alignas(16) GradBS {
     } r2;
     union {
         struct {
-            float dO[kB][VS], U[kB][VS], dU[kB][VS], X[kB][VS], dY[kB][VS];
+            float dO[kB][VS], U[kB][VS], dU[kB][VS], V[kB][VS], dY[kB][VS];
             float Sp[DK][VS], dSn[DK][VS];
         } lp;
         struct {
@@ -802,6 +803,7 @@ template <int DK> struct alignas(16) GradBS {
     float m2[DK], em[DK], eg[DK], egm[DK];
     float part[kSeg][DK], partk[kSeg][DK];   // segment totals of the column scans
     float dgn1[DK];
+    float dbK[DK / 16][kB];                  // per key tile: sum_c KA (dY S'^T) of a row
 };
 
 template <int DK, int DV, typename IO, typename GT>
@@ -887,7 +889,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     f32x4_t aL[3];                           // lower tiles: idx < 10 dP, else dY U^T
 #pragma unroll
     for (int s = 0; s < 3; ++s) aL[s] = zero4();
-    f32x4_t xr = zero4(), dbp = zero4();     // waves 0-3: X tile, dbeta partial
+    f32x4_t dbp = zero4();                   // waves 4-7: the dY.V part of dbeta
 
     const float *sc = Sc + ch * DK * DV;
     const float *uc = Uc + ch * kB * DV;
@@ -915,22 +917,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         const int j0 = vb * kBV;
         __syncthreads();                     // previous block's reads done
         pO.template store<S::VS>(&sm.r3.lp.dO[0][0], tid);
-        pV.template store<S::VS>(&sm.r3.lp.X[0][0], tid);
+        pV.template store<S::VS>(&sm.r3.lp.V[0][0], tid);
         pU.template store<S::VS>(&sm.r3.lp.U[0][0], tid);
         pdU.template store<S::VS>(&sm.r3.lp.dU[0][0], tid);
         pS.template store<S::VS>(&sm.r3.lp.Sp[0][0], tid, sm.em);
         pdS.template store<S::VS>(&sm.r3.lp.dSn[0][0], tid);
         __syncthreads();
         if (vb + 1 < DV / kBV) fetch(vb + 1);
-        if (w < 4) {   // X = V - KA S'
-            f32x4_t a = zero4();
-            a = mm<DK, S::KS, 1, S::VS, 1>(a, &sm.KA[16 * w][0], &sm.r3.lp.Sp[0][0], lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * w + acc_row(lane, e), j = acc_col(lane);
-                xr[e] = sm.r3.lp.X[r][j] - a[e];
-            }
-        } else {       // dY = T^T dU; dV = diag(beta) dY
+        if (w >= 4) {   // dY = T^T dU; dV = diag(beta) dY; the dY.V part of dbeta
             const int rt = w - 4;
             f32x4_t a = zero4();
             a = mm<kB, 1, S::CS, S::VS, 1>(a, &sm.r2.m.T[0][16 * rt], &sm.r3.lp.dU[0][0], lane);
@@ -938,6 +932,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rt + acc_row(lane, e), j = acc_col(lane);
                 sm.r3.lp.dY[r][j] = a[e];
+                dbp[e] += a[e] * sm.r3.lp.V[r][j];
                 if (r < nv) {
                     const float x = bad ? __builtin_nanf("") : sm.beta[r] * a[e];
                     dv[((t0 + r) * H + h) * DV + j0 + j] = from_f32<IO>(x);
@@ -945,10 +940,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             }
         }
         __syncthreads();
-        if (w < 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dbp[e] += xr[e] * sm.r3.lp.dY[16 * w + acc_row(lane, e)][acc_col(lane)];
-        }
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
             const int idx = w + 8 * s;
@@ -973,8 +964,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     }
     __syncthreads();                         // loop buffers and T free
 
-    // dbeta from X . dY: sum over the 16 columns of each tile row.
-    if (w < 4) {
+    // dbeta_r = sum_j dY[r,j] X[r,j] with X = V - KA S', taken as
+    // sum_j dY[r,j] V[r,j] - sum_c KA[r,c] (dY S'^T)[r,c]: the first part here
+    // (a sum over the 16 columns of each tile row), the second below.
+    if (w >= 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float x = dbp[e];
@@ -982,7 +975,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             x += __shfl_xor(x, 2);
             x += __shfl_xor(x, 4);
             x += __shfl_xor(x, 8);
-            if ((lane & 15) == 0) sm.dbr[16 * w + acc_row(lane, e)] = x;
+            if ((lane & 15) == 0) sm.dbr[16 * (w - 4) + acc_row(lane, e)] = x;
         }
     }
     // dP (inclusive lower) and dM = diag(beta) dA, dA = -strictly-lower(dY U^T).
@@ -1043,6 +1036,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         const float *dP = &sm.r2.m.T[0][0];
         const float *dM = &sm.r2.m.dM[0][0];
         aQ[s] = mm<kB, S::CS, 1, S::KS, 1>(aQ[s], dP + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {   // sum_c KA[r,c] (dY S'^T)[r,c] over this tile's 16 columns
+            float x = sm.KA[16 * rt + acc_row(lane, e)][16 * ct + acc_col(lane)] * aK[s][e];
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if ((lane & 15) == 0) sm.dbK[ct][16 * rt + acc_row(lane, e)] = x;
+        }
         f32x4_t t = zero4();
         t = mm<kB, S::CS, 1, S::KS, 1>(t, dM + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
 #pragma unroll
@@ -1118,7 +1120,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     if (tid < DK) sm.dgn1[tid] = dgn1;
     if (tid < kB && tid < nv) {
         const int r = tid;
-        const float x = sm.dbr[r] + ((sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]));
+        float kx = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK / 16; ++i) kx += sm.dbK[i][r];
+        const float x = (sm.dbr[r] - kx) + ((sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]));
         dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
     }
     __syncthreads();
