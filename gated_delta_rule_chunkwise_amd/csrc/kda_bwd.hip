@@ -215,8 +215,8 @@ __device__ __forceinline__ void put_f32(float *dst, const typename Vec16<X>::raw
 
 // A ROWS x COLS block of X (row r at src + r * pitch, rows >= nv read as zero)
 // moved into an fp32 LDS array with row stride LS by NT threads: load() issues
-// every 16-byte load into registers, store() writes them out (optionally scaled
-// per row), so that the loads can be in flight during unrelated work.
+// the 16-byte loads into registers, store() writes them out later (optionally
+// scaled per row).
 template <int ROWS, int COLS, int NT, typename X> struct Stage {
     static constexpr int VE = Vec16<X>::N, PER = COLS / VE, TOT = ROWS * PER, IT = (TOT + NT - 1) / NT;
     static_assert(COLS % VE == 0, "row length must be a whole number of 16-byte vectors");
@@ -452,16 +452,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
 // waves 4-7 only move data: they hold the next chunk's record span in registers
 // (slot s of loader thread t: float4 number t + 256 s of the span), write it
 // into LDS at the chunk boundary, issue the following chunk's loads while the
-// compute waves work, and store the per-chunk results.  The CU's vector-memory
-// pipe then never sits in front of the matrix products.
+// compute waves work, and store the per-chunk results, so that the compute
+// waves issue no global memory instruction.
 constexpr int kSP = 512;                     // threads per workgroup
 constexpr int kLT = 256;                     // loader threads (waves 4-7)
 constexpr int kXCD = 8;
 
 // Block id -> (chain = sequence * H + head, column block).  Workgroups go to the
 // 8 XCDs round-robin by block id, so the NVB column blocks of one chain get ids
-// that are equal modulo 8: they run on one XCD and the chunk records they all
-// read are fetched once into that XCD's L2.  Ids past the last chain return.
+// that are equal modulo 8: they run on one XCD, where the chunk records they
+// all read can be served from that XCD's L2.  Ids past the last chain return.
 template <int NVB>
 __device__ __forceinline__ bool chain_of(int64_t id, int64_t chains, int64_t &chain, int &vb) {
     const int64_t q = id / kXCD;
@@ -897,8 +897,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const float *duc = dUc + ch * kB * DV;
     const bool bad = sflag[n * H + h] != 0.f;
 
-    // The next 16-column block's operands are loaded into registers while the
-    // current one is processed.
+    // The next 16-column block's operands are requested (into registers) before
+    // the current block's products.
     Stage<kB, kBV, 512, IO> pO, pV;
     Stage<kB, kBV, 512, float> pU, pdU;
     Stage<DK, kBV, 512, float> pS, pdS;
