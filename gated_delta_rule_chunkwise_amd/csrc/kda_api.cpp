@@ -155,7 +155,7 @@ kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void 
 
 size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                     int32_t num_seqs, kda_dtype_t io_dtype) {
-    if (B <= 0 || T < 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
+    if (B <= 0 || T < 0 || H <= 0 || H > 65535 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
     if (!valid_dtype(io_dtype)) return 0;
     if (num_seqs < 0 || (num_seqs > 0 && B != 1)) return 0;
     kda::BwdArgs a = {};
@@ -177,6 +177,7 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (H > 65535) return KDA_ERR_UNSUPPORTED;   // heads are a grid dimension of the per-chunk kernels
     if (!sizes_fit((int64_t)B * T, H, (d_k > d_v ? d_k : d_v))) return KDA_ERR_INVALID_ARGUMENT;
     int64_t N;
     if (cu_seqlens) {

@@ -273,6 +273,7 @@ size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
  *
  *   q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, B, T, H, d_k, d_v,
  *   io_dtype, gate_dtype    the forward's inputs, as for kda_chunk_fwd
+ *   H               at most 65,535 (KDA_ERR_UNSUPPORTED above)
  *   grad_o          [B, T, H, d_v]  io_dtype
  *   grad_hT         [N, H, d_k, d_v] fp32, or NULL (L does not depend on h_T)
  *   grad_q, grad_k  [B, T, H, d_k]  io_dtype (out)

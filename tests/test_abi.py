@@ -294,7 +294,7 @@ def test_bwd_workspace_size(kda):
     (dict(db=P + 2, gt=0), 1),
     (dict(cu=P, N=2, B=2), 1), (dict(cu=P, N=0), 1), (dict(cu=P + 2, N=2), 1), (dict(N=3), 1),
     (dict(ws=None), 3), (dict(wsb=0), 3), (dict(ws=P + 8), 1),
-    (dict(T=1 << 30, H=1 << 20), 1),
+    (dict(T=1 << 30, H=1 << 20), 2), (dict(H=65536, T=1), 2),
 ])
 def test_bwd_rejects(kda, kw, code):
     lib = kda.load_library()
