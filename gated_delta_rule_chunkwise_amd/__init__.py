@@ -16,7 +16,9 @@ Entry points (same names as the C ABI):
     kda_chunk_fwd_decoupled(q, k, v, log_alpha, b_erase, w_write, ...)
     kda_decode_step_decoupled(q, k, v, log_alpha, b_erase, w_write, S, o=None)
     kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_seqlens=None, ...)
+    kda_gdn_chunk_bwd(q, k, v, log_alpha_or_None, beta, grad_o, ...)
     kda_chunk_fwd_workspace_size(...), kda_chunk_bwd_workspace_size(...),
+    kda_gdn_chunk_bwd_workspace_size(...),
     kda_status_string(code), kda_abi_version()
 """
 from __future__ import annotations
@@ -33,7 +35,8 @@ EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error"
                     "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step",
                     "kda_chunk_fwd_prologue", "kda_decode_step_prologue", "kda_gdn_chunk_fwd",
                     "kda_gdn_decode_step", "kda_chunk_fwd_decoupled", "kda_decode_step_decoupled",
-                    "kda_chunk_bwd_workspace_size", "kda_chunk_bwd")
+                    "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
+                    "kda_gdn_chunk_bwd_workspace_size", "kda_gdn_chunk_bwd")
 
 _lib = None
 
@@ -92,6 +95,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                   i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
     lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_gdn_chunk_bwd_workspace_size.argtypes = list(lib.kda_chunk_fwd_workspace_size.argtypes)
+    lib.kda_gdn_chunk_bwd_workspace_size.restype = sz
+    lib.kda_gdn_chunk_bwd.argtypes = list(lib.kda_chunk_bwd.argtypes)
+    lib.kda_gdn_chunk_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -257,6 +264,10 @@ def kda_chunk_bwd_workspace_size(B, T, H, d_k, d_v, num_seqs=0, io_dtype=KDA_BF1
     return int(load_library().kda_chunk_bwd_workspace_size(B, T, H, d_k, d_v, num_seqs, io_dtype))
 
 
+def kda_gdn_chunk_bwd_workspace_size(B, T, H, d_k, d_v, num_seqs=0, io_dtype=KDA_BF16) -> int:
+    return int(load_library().kda_gdn_chunk_bwd_workspace_size(B, T, H, d_k, d_v, num_seqs, io_dtype))
+
+
 def kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_seqlens=None, *,
                   want_grad_h0=True, workspace=None):
     """Gradients of kda_chunk_fwd (see kda_chunk_bwd in include/kda.h).
@@ -264,21 +275,42 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_se
     Inputs as for kda_chunk_fwd plus grad_o (like o) and grad_hT (like h_T, or
     None).  Returns (dq, dk, dv, dlog_alpha, dbeta, dh0); dh0 is None when
     want_grad_h0 is False."""
+    return _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0, workspace,
+                      gdn=False)
+
+
+def kda_gdn_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_seqlens=None, *,
+                      want_grad_h0=True, workspace=None):
+    """Gradients of kda_gdn_chunk_fwd: log_alpha is [B, T, H] or None (no
+    decay).  Returns (dq, dk, dv, dlog_alpha, dbeta, dh0); dlog_alpha is None
+    when log_alpha is None, dh0 when want_grad_h0 is False."""
+    return _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0, workspace,
+                      gdn=True)
+
+
+def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0, workspace, gdn):
     import torch
     lib = load_library()
     squeeze = q.dim() == 3
     if squeeze:
-        q, k, v, log_alpha, beta, grad_o = (x.unsqueeze(0) for x in (q, k, v, log_alpha, beta, grad_o))
+        q, k, v, beta, grad_o = (x.unsqueeze(0) for x in (q, k, v, beta, grad_o))
+        if log_alpha is not None:
+            log_alpha = log_alpha.unsqueeze(0)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
+    if log_alpha is None and not gdn:
+        raise ValueError("log_alpha is required")
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
                     ("grad_o", grad_o)):
-        _check_dev(name, t, dev)
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:3] != (B, T, H) \
-            or beta.shape != (B, T, H) or grad_o.shape != v.shape:
+        if t is not None:
+            _check_dev(name, t, dev)
+    gshape = (B, T, H) if gdn else q.shape
+    if k.shape != q.shape or (log_alpha is not None and log_alpha.shape != gshape) \
+            or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H) or grad_o.shape != v.shape:
         raise ValueError("shape mismatch among q, k, v, log_alpha, beta, grad_o")
-    if k.dtype != q.dtype or v.dtype != q.dtype or grad_o.dtype != q.dtype or beta.dtype != log_alpha.dtype:
+    if k.dtype != q.dtype or v.dtype != q.dtype or grad_o.dtype != q.dtype \
+            or (log_alpha is not None and beta.dtype != log_alpha.dtype):
         raise TypeError("q, k, v, grad_o share one dtype; log_alpha and beta share one dtype")
     if cu_seqlens is not None:
         _check_dev("cu_seqlens", cu_seqlens, dev)
@@ -295,23 +327,27 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_se
     dq = torch.empty_like(q)
     dk_ = torch.empty_like(k)
     dv_ = torch.empty_like(v)
-    dla = torch.empty_like(log_alpha)
+    dla = torch.empty_like(log_alpha) if log_alpha is not None else None
     db = torch.empty_like(beta)
     dh0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_grad_h0 else None
     io, gt = _dtype_code(q), _dtype_code(beta)
     nseq = N if cu_seqlens is not None else 0
-    ws_bytes = kda_chunk_bwd_workspace_size(B, T, H, dk, dv, nseq, io)
+    size_fn = kda_gdn_chunk_bwd_workspace_size if gdn else kda_chunk_bwd_workspace_size
+    ws_bytes = size_fn(B, T, H, dk, dv, nseq, io)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() * workspace.element_size()
-    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
-                           _ptr(cu_seqlens), nseq, _ptr(grad_o), _ptr(grad_hT), _ptr(dq), _ptr(dk_),
-                           _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dh0), B, T, H, dk, dv, io, gt,
-                           _ptr(workspace), ws_len, _stream_of(q))
+    name = "kda_gdn_chunk_bwd" if gdn else "kda_chunk_bwd"
+    rc = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                            _ptr(cu_seqlens), nseq, _ptr(grad_o), _ptr(grad_hT), _ptr(dq), _ptr(dk_),
+                            _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dh0), B, T, H, dk, dv, io, gt,
+                            _ptr(workspace), ws_len, _stream_of(q))
     if rc != KDA_OK:
-        raise KDAError(rc, "kda_chunk_bwd", kda_last_hip_error())
+        raise KDAError(rc, name, kda_last_hip_error())
     if squeeze:
-        dq, dk_, dv_, dla, db = (x.squeeze(0) for x in (dq, dk_, dv_, dla, db))
+        dq, dk_, dv_, db = (x.squeeze(0) for x in (dq, dk_, dv_, db))
+        if dla is not None:
+            dla = dla.squeeze(0)
     return dq, dk_, dv_, dla, db, dh0
 
 

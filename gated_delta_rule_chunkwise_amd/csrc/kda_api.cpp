@@ -153,11 +153,8 @@ kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void 
                             stream, false, 0.f, 0);
 }
 
-size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                    int32_t num_seqs, kda_dtype_t io_dtype) {
-    if (B <= 0 || T < 0 || H <= 0 || H > 65535 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
-    if (!valid_dtype(io_dtype)) return 0;
-    if (num_seqs < 0 || (num_seqs > 0 && B != 1)) return 0;
+static kda::BwdArgs bwd_sizes(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t num_seqs,
+                              kda_dtype_t io_dtype) {
     kda::BwdArgs a = {};
     a.varlen = num_seqs > 0;
     a.num_seqs = num_seqs > 0 ? num_seqs : B;
@@ -165,15 +162,39 @@ size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
     a.total_tokens = (int64_t)B * T;
     a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.io_bf16 = io_dtype == KDA_BF16;
-    return kda::chunk_bwd_workspace_bytes(a);
+    return a;
 }
 
-kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
-                           const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
-                           const void *grad_o, const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
-                           void *grad_log_alpha, void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
-                           int32_t d_k, int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+static bool bwd_sizes_ok(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t num_seqs,
+                         kda_dtype_t io_dtype) {
+    if (B <= 0 || T < 0 || H <= 0 || H > 65535 || !supported_dim(d_k) || !supported_dim(d_v)) return false;
+    if (!valid_dtype(io_dtype)) return false;
+    return !(num_seqs < 0 || (num_seqs > 0 && B != 1));
+}
+
+size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                    int32_t num_seqs, kda_dtype_t io_dtype) {
+    if (!bwd_sizes_ok(B, T, H, d_k, d_v, num_seqs, io_dtype)) return 0;
+    return kda::chunk_bwd_workspace_bytes(bwd_sizes(B, T, H, d_k, d_v, num_seqs, io_dtype));
+}
+
+size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                        int32_t num_seqs, kda_dtype_t io_dtype) {
+    if (!bwd_sizes_ok(B, T, H, d_k, d_v, num_seqs, io_dtype)) return 0;
+    return kda::gdn_chunk_bwd_workspace_bytes(bwd_sizes(B, T, H, d_k, d_v, num_seqs, io_dtype));
+}
+
+}  // extern "C"
+
+namespace {
+
+// gate_mode 0: log_alpha [.., d_k] (KDA); 1: [..] per (token, head); 2: none.
+kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const void *log_alpha, const void *beta,
+                            const float *h0, const int32_t *cu_seqlens, int32_t num_seqs, const void *grad_o,
+                            const float *grad_hT, void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
+                            void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                            int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream, int gate_mode) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -191,32 +212,62 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     if (!sizes_fit(N, H, (int64_t)d_k * d_v)) return KDA_ERR_INVALID_ARGUMENT;
     const bool have_tokens = (int64_t)B * T > 0;
     if (have_tokens) {
-        const void *need16[] = {q, k, v, log_alpha, grad_o, grad_q, grad_k, grad_v, grad_log_alpha};
+        const void *need16[] = {q, k, v, grad_o, grad_q, grad_k, grad_v};
         for (const void *p : need16)
             if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARGUMENT;
-        if (!beta || !grad_beta || !aligned_to(beta, dsize(gate_dtype)) || !aligned_to(grad_beta, dsize(gate_dtype)))
+        const uintptr_t gsz = dsize(gate_dtype);
+        if (!beta || !grad_beta || !aligned_to(beta, gsz) || !aligned_to(grad_beta, gsz))
+            return KDA_ERR_INVALID_ARGUMENT;
+        if (gate_mode == 0 && (!log_alpha || !aligned16(log_alpha) || !grad_log_alpha || !aligned16(grad_log_alpha)))
+            return KDA_ERR_INVALID_ARGUMENT;
+        if (gate_mode == 1 && (!grad_log_alpha || !aligned_to(log_alpha, gsz) || !aligned_to(grad_log_alpha, gsz)))
             return KDA_ERR_INVALID_ARGUMENT;
     }
     if ((h0 && !aligned16(h0)) || (grad_hT && !aligned16(grad_hT)) || (grad_h0 && !aligned16(grad_h0)))
         return KDA_ERR_INVALID_ARGUMENT;
-    kda::BwdArgs a = {};
-    a.varlen = cu_seqlens != nullptr;
-    a.num_seqs = N; a.seq_len = T; a.total_tokens = (int64_t)B * T;
-    a.H = H; a.d_k = d_k; a.d_v = d_v;
-    a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
-    const size_t need = kda::chunk_bwd_workspace_bytes(a);
+    kda::BwdArgs a = bwd_sizes(B, T, H, d_k, d_v, cu_seqlens ? num_seqs : 0, io_dtype);
+    a.gate_bf16 = gate_dtype == KDA_BF16;
+    const size_t need = gate_mode == 0 ? kda::chunk_bwd_workspace_bytes(a) : kda::gdn_chunk_bwd_workspace_bytes(a);
     if (workspace_bytes < need || !workspace) return KDA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
     if (!have_tokens && !grad_h0) return KDA_OK;  // nothing to compute or write
 
-    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0; a.cu_seqlens = cu_seqlens;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = gate_mode == 2 ? nullptr : log_alpha; a.beta = beta; a.h0 = h0;
+    a.cu_seqlens = cu_seqlens;
     a.d_o = grad_o; a.d_hT = grad_hT;
-    a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = grad_log_alpha; a.dbeta = grad_beta;
-    a.dh0 = grad_h0;
+    a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = gate_mode == 2 ? nullptr : grad_log_alpha;
+    a.dbeta = grad_beta; a.dh0 = grad_h0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     g_hip_error[0] = '\0';
-    if (kda::launch_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0) return KDA_ERR_HIP;
-    return KDA_OK;
+    const int rc = gate_mode == 0 ? kda::launch_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error))
+                                  : kda::launch_gdn_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error));
+    return rc != 0 ? KDA_ERR_HIP : KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                           const void *grad_o, const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
+                           void *grad_log_alpha, void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k, grad_v,
+                          grad_log_alpha, grad_beta, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype, workspace,
+                          workspace_bytes, stream, 0);
+}
+
+kda_status_t kda_gdn_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                               const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                               const void *grad_o, const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
+                               void *grad_log_alpha, void *grad_beta, float *grad_h0, int32_t B, int32_t T,
+                               int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k, grad_v,
+                          grad_log_alpha, grad_beta, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype, workspace,
+                          workspace_bytes, stream, log_alpha ? 1 : 2);
 }
 
 }  // extern "C"

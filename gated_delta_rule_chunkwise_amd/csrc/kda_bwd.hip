@@ -1188,9 +1188,108 @@ hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t st) {
     return a.gate_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a, st) : launch_bwd_t<DK, DV, float, float>(a, st);
 }
 
+// ----------------------------------------------------------------------------
+// Scalar gates (Gated DeltaNet: one log alpha per token and head; DeltaNet: none)
+// through the same kernels: the gate is broadcast over the key channels into an
+// fp32 buffer, beta converted to fp32, the backward run with fp32 gates, and
+// the channel gradients of log alpha summed per (token, head) in a fixed order.
+// This is exact by the chain rule: every channel's log alpha is the one value.
+
+// la_full[th][c] = log_alpha[th] (0 without a gate), beta32[th] = beta[th].
+template <typename GT>
+__global__ __launch_bounds__(256) void gdn_expand_kernel(const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
+                                                         int64_t rows, int dk, float *__restrict__ la_full,
+                                                         float *__restrict__ beta32) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one element of la_full
+    if (i >= rows * dk) return;
+    const int64_t th = i / dk;
+    la_full[i] = log_alpha ? to_f32(log_alpha[th]) : 0.f;
+    if (i % dk == 0) beta32[th] = to_f32(beta[th]);
+}
+
+// grad_log_alpha[th] = sum_c dla32[th][c] (fixed order), grad_beta[th] = dbeta32[th].
+template <typename GT>
+__global__ __launch_bounds__(256) void gdn_finish_kernel(const float *__restrict__ dla32,
+                                                         const float *__restrict__ dbeta32, int64_t rows, int dk,
+                                                         GT *__restrict__ grad_log_alpha, GT *__restrict__ grad_beta) {
+    const int64_t th = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (th >= rows) return;
+    if (grad_log_alpha) {
+        const float *x = dla32 + th * dk;
+        float acc = 0.f;
+        for (int c = 0; c < dk; ++c) acc += x[c];
+        grad_log_alpha[th] = from_f32<GT>(acc);
+    }
+    grad_beta[th] = from_f32<GT>(dbeta32[th]);
+}
+
+size_t gdn_extra_bytes(const BwdArgs &a) {
+    const size_t rows = (size_t)a.total_tokens * a.H;
+    return (2 * rows * a.d_k * 4 + 255) / 256 * 256 + 2 * ((rows * 4 + 255) / 256 * 256);
+}
+
 }  // namespace
 
 size_t chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total; }
+
+size_t gdn_chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total + gdn_extra_bytes(a); }
+
+int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t base = bwd_layout(a).total;
+    if (a.workspace_bytes < base + gdn_extra_bytes(a)) {
+        snprintf(err, err_len, "workspace too small");
+        return -1;
+    }
+    const int64_t rows = a.total_tokens * a.H;
+    uint8_t *x = static_cast<uint8_t *>(a.workspace) + base;
+    const size_t full = (size_t)rows * a.d_k * 4;
+    float *la_full = reinterpret_cast<float *>(x);
+    float *dla32 = reinterpret_cast<float *>(x + full);
+    float *beta32 = reinterpret_cast<float *>(x + (2 * full + 255) / 256 * 256);
+    float *dbeta32 = reinterpret_cast<float *>(x + (2 * full + 255) / 256 * 256 + ((size_t)rows * 4 + 255) / 256 * 256);
+    if ((rows * a.d_k + 255) / 256 > 0x7fffffffLL) {
+        snprintf(err, err_len, "gdn_chunk_bwd grid too large");
+        return -1;
+    }
+    if (rows > 0) {
+        const int64_t nblk = (rows * a.d_k + 255) / 256;
+        if (a.gate_bf16)
+            hipLaunchKernelGGL(gdn_expand_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
+                               static_cast<const bf16_t *>(a.log_alpha), static_cast<const bf16_t *>(a.beta), rows,
+                               a.d_k, la_full, beta32);
+        else
+            hipLaunchKernelGGL(gdn_expand_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
+                               static_cast<const float *>(a.log_alpha), static_cast<const float *>(a.beta), rows,
+                               a.d_k, la_full, beta32);
+    }
+    BwdArgs b = a;
+    b.log_alpha = la_full;
+    b.beta = beta32;
+    b.gate_bf16 = 0;
+    b.dlog_alpha = dla32;
+    b.dbeta = dbeta32;
+    b.workspace_bytes = base;
+    if (launch_chunk_bwd(b, stream, err, err_len) != 0) return -1;
+    if (rows > 0) {
+        const int64_t nblk = (rows + 255) / 256;
+        const float *src_la = a.dlog_alpha ? dla32 : nullptr;
+        if (a.gate_bf16)
+            hipLaunchKernelGGL(gdn_finish_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st, dla32, dbeta32, rows,
+                               a.d_k, src_la ? static_cast<bf16_t *>(a.dlog_alpha) : nullptr,
+                               static_cast<bf16_t *>(a.dbeta));
+        else
+            hipLaunchKernelGGL(gdn_finish_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st, dla32, dbeta32, rows,
+                               a.d_k, src_la ? static_cast<float *>(a.dlog_alpha) : nullptr,
+                               static_cast<float *>(a.dbeta));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            snprintf(err, err_len, "%s", hipGetErrorString(e));
+            return -1;
+        }
+    }
+    return 0;
+}
 
 int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -64,5 +64,8 @@ struct BwdArgs {
 
 size_t chunk_bwd_workspace_bytes(const BwdArgs &a);
 int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len);
+// Scalar-gate form: log_alpha [.., H] (or nullptr: no decay), dlog_alpha likewise.
+size_t gdn_chunk_bwd_workspace_bytes(const BwdArgs &a);
+int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len);
 
 }  // namespace kda

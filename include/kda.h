@@ -304,6 +304,41 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/*
+ * Bytes of device workspace kda_gdn_chunk_bwd needs (arguments as for
+ * kda_chunk_bwd_workspace_size; 0 for invalid arguments): that of
+ * kda_chunk_bwd plus two fp32 [B*T*H, d_k] buffers and two fp32 [B*T*H]
+ * buffers (about 1 KiB more per token-head at d_k = 128).
+ */
+size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                        int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+
+/*
+ * kda_gdn_chunk_bwd -- gradients of kda_gdn_chunk_fwd: Gated DeltaNet (one
+ * decay per token and head, KimiLinear article section 2.2) or DeltaNet (no
+ * decay, section 2.1) when log_alpha is NULL.  The scalar gate is the
+ * per-channel gate of kda_chunk_bwd with every channel equal to it, so by the
+ * chain rule its gradient is the sum over the key channels of the per-channel
+ * gradient; the library broadcasts the gate into the workspace, runs the
+ * kernels of kda_chunk_bwd, and sums those channel gradients per (token, head)
+ * in a fixed order.  Arguments, workspace, numerics, range and errors as for
+ * kda_chunk_bwd except:
+ *
+ *   log_alpha       [B, T, H] gate_dtype, aligned to its element size; or NULL
+ *                   for no decay
+ *   grad_log_alpha  [B, T, H] gate_dtype (out), aligned to its element size;
+ *                   required when log_alpha is given, ignored when it is NULL
+ *   workspace       at least kda_gdn_chunk_bwd_workspace_size() bytes
+ */
+kda_status_t kda_gdn_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                               const void *beta, const float *h0, const int32_t *cu_seqlens,
+                               int32_t num_seqs, const void *grad_o, const float *grad_hT,
+                               void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
+                               void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
+                               int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                               kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -305,3 +305,48 @@ def test_bwd_empty_without_state_is_noop(kda):
     lib = kda.load_library()
     assert bwd(lib, T=0, q=None, k=None, v=None, la=None, beta=None, go=None, dq=None, dk=None, dv=None,
                dla=None, db=None, dh0=None) == 0
+
+
+def bwd_gdn(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, go=P, ghT=None, dq=P, dk=P, dv=P,
+             dla=P, db=P, dh0=P, B=1, T=128, H=2, dk_=128, dv_=128, io=1, gt=1, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_gdn_chunk_bwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"], a["N"],
+                                 a["go"], a["ghT"], a["dq"], a["dk"], a["dv"], a["dla"], a["db"], a["dh0"],
+                                 a["B"], a["T"], a["H"], a["dk_"], a["dv_"], a["io"], a["gt"], a["ws"],
+                                 a["wsb"], None)
+
+
+def test_gdn_bwd_workspace_size(kda):
+    # the per-channel backward's workspace plus the broadcast gate and its
+    # channel gradient (2 x rows x d_k fp32) and beta, dbeta in fp32 (2 x rows)
+    rows = 1000 * 2
+    for d_k in (64, 128):
+        base = kda.kda_chunk_bwd_workspace_size(1, 1000, 2, d_k, 64, 0, kda.KDA_BF16)
+        w = kda.kda_gdn_chunk_bwd_workspace_size(1, 1000, 2, d_k, 64, 0, kda.KDA_BF16)
+        assert base + 2 * rows * d_k * 4 + 2 * rows * 4 <= w <= base + 2 * rows * d_k * 4 + 2 * rows * 4 + 768
+    assert kda.kda_gdn_chunk_bwd_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
+    assert kda.kda_gdn_chunk_bwd_workspace_size(1, 100, 65536, 64, 64, 0, kda.KDA_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk_=96), 2), (dict(B=0), 1), (dict(H=65536, T=1), 2), (dict(q=None), 1), (dict(go=None), 1),
+    (dict(beta=None), 1), (dict(db=None), 1),
+    (dict(la=P + 1), 1), (dict(la=P + 2, gt=0), 1), (dict(dla=None), 1), (dict(dla=P + 1), 1),
+    (dict(dla=P + 2, gt=0), 1), (dict(cu=P, N=2, B=2), 1), (dict(ws=None), 3),
+])
+def test_gdn_bwd_rejects(kda, kw, code):
+    lib = kda.load_library()
+    assert bwd_gdn(lib, **kw) == code
+
+
+def test_gdn_bwd_gate_alignment_is_element_size(kda):
+    # a [B, T, H] gate and its gradient are accepted at element alignment: with
+    # both at P + 2 (bf16) the call gets as far as the workspace check
+    lib = kda.load_library()
+    need = kda.kda_gdn_chunk_bwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    base = kda.kda_chunk_bwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    assert need > base
+    assert bwd_gdn(lib, la=P + 2, dla=P + 2, wsb=need - 1) == 3
+    assert bwd_gdn(lib, la=P + 4, dla=P + 4, gt=0, wsb=base) == 3
+    assert bwd(lib, la=P + 2, dla=P + 2) == 1          # the per-channel entry point needs 16 bytes

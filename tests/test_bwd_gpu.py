@@ -135,6 +135,28 @@ def test_bwd_without_state_inputs(kda):
     check(kda, d, "bf16", go, None, with_h0=False, what="no h0, no grad_hT")
 
 
+@pytest.mark.parametrize("lengths", [[1], [1, 2, 3, 1, 64, 65, 1], [127, 0, 0, 129]])
+def test_bwd_tiny_and_empty_sequences(kda, lengths):
+    """Single tokens, runs of one-token sequences, and empty sequences between
+    others (grad_h0 of an empty sequence is grad_hT)."""
+    cfg = I.ChunkConfig("tiny", "bf16", "bf16", H=2, dk=64, dv=128, h0=True, seed=3900 + len(lengths))
+    d = I.make_chunk_inputs(cfg, lengths=lengths)
+    go, ghT = I.make_upstream_grads(d, 3901)
+    check(kda, d, "bf16", go, ghT, what="lengths %s" % lengths)
+
+
+def test_bwd_empty_batch_passes_state_gradient(kda):
+    """T = 0: only grad_h0 = grad_hT is written."""
+    dev = DEV
+    H, dk, dv = 2, 64, 64
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=dev)
+    ghT = torch.randn((1, H, dk, dv), generator=torch.Generator().manual_seed(3950)).to(dev)
+    out = kda.kda_chunk_bwd(z(1, 0, H, dk), z(1, 0, H, dk), z(1, 0, H, dv), z(1, 0, H, dk), z(1, 0, H),
+                            z(1, 0, H, dv), grad_hT=ghT)
+    torch.cuda.synchronize()
+    assert torch.equal(out[5], ghT)
+
+
 def test_bwd_bitwise_determinism(kda):
     cfg = I.ChunkConfig("det", "bf16", "bf16", H=4, dk=128, dv=128, h0=True, seed=3600)
     d = I.make_chunk_inputs(cfg, lengths=[500, 129])
@@ -192,3 +214,68 @@ def test_bwd_matches_forward_directional_derivative(kda):
     an = sum(float((g.double() * dirs[k]).sum()) for g, k in zip(grads, keys))
     log("directional derivative: fd %.6f analytic %.6f" % (fd, an))
     assert abs(fd - an) <= 1e-2 * max(1.0, abs(an))
+
+
+# ------------------------------------------------------------------ scalar gates
+# kda_gdn_chunk_bwd: Gated DeltaNet (one log decay per token and head) or
+# DeltaNet (none), against the oracle's backward with that value on every key
+# channel; the scalar gate's gradient is the oracle's channel gradients summed
+# (the chain rule, pinned on the CPU by finite differences of a scalar-gate
+# recurrence).
+def gdn_check(kda, d, g, io, go, ghT, seqs=None, heads=None, what=""):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    out = kda.kda_gdn_chunk_bwd(dev["q"], dev["k"], dev["v"], None if g is None else g.to(DEV), dev["beta"],
+                                go.to(DEV), h0=dev["h0"], grad_hT=None if ghT is None else ghT.to(DEV),
+                                cu_seqlens=cu)
+    torch.cuda.synchronize()
+    out = [None if x is None else x.cpu() for x in out]
+    assert (out[3] is None) == (g is None)
+    T, H, dk = d["q"].shape
+    dd = dict(d)
+    dd["log_alpha"] = torch.zeros((T, H, dk), dtype=torch.float64) if g is None else \
+        g.to(torch.float64)[:, :, None].expand(T, H, dk).contiguous()
+    ref, rows, hs, sq = oracle_bwd(dd, go, ghT, seqs, heads)
+    ref = list(ref)
+    ref[3] = ref[3].sum(-1)
+    errs = {}
+    for name, x, r in zip(NAMES, out, ref):
+        if x is None:
+            continue
+        x = x[sq][:, hs] if name == "dh0" else x[rows][:, hs]
+        e = errors(x, r)
+        tol = F32_REL if (io == "f32" or name == "dh0") else BF16_REL
+        assert e["rel_max"] <= tol and e["rel_fro"] <= tol, "%s %s: %s (tol %g)" % (what, name, e, tol)
+        errs[name] = "%.1e/%.1e" % (e["rel_max"], e["rel_fro"])
+    log(what, errs)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+@pytest.mark.parametrize("io,dk,dv", [("bf16", 128, 128), ("bf16", 64, 128), ("f32", 128, 64), ("f32", 64, 64)])
+def test_gdn_bwd_ragged_varlen(kda, gate, io, dk, dv):
+    """Ragged packed sequences with h0 and grad_hT; the scalar gate includes a
+    near-reset (log a = -30) and a chunk that decays by e^-128 in total."""
+    cfg = I.ChunkConfig("gdn-bwd", io, io, H=3, dk=dk, dv=dv, h0=True, seed=4000 + dk + dv)
+    d = I.make_chunk_inputs(cfg, lengths=[300, 64, 130, 1, 200, 0])
+    g = None
+    if gate == "none":
+        # no decay: keep the growing state's outputs, and so the gradients,
+        # of order one (they are linear in v and h0)
+        d["v"] = (d["v"].float() * 0.35).to(d["v"].dtype)
+        d["h0"] = d["h0"] * 0.35
+    else:
+        g = d["log_alpha"][:, :, 0].float().clone()
+        g[10] = -30.0
+        g[300:364, 1] = -2.0
+        g = g.to(d["log_alpha"].dtype).contiguous()
+    go, ghT = I.make_upstream_grads(d, 4001)
+    gdn_check(kda, d, g, io, go, ghT, what="gdn bwd %s %s %dx%d" % (gate, io, dk, dv))
+
+
+def test_gdn_bwd_c3_sampled_heads(kda):
+    """Full long-context size (T = 65,536, H = 32) with one decay per token
+    and head; the oracle checks two whole heads."""
+    d = I.make_chunk_inputs(I.C3)
+    g = d["log_alpha"][:, :, 0].contiguous()
+    go, _ = I.make_upstream_grads(d, 4100, with_state=False)
+    gdn_check(kda, d, g, "bf16", go, None, heads=[0, 31], what="gdn bwd c3 heads 0,31")

@@ -170,3 +170,44 @@ def test_bwd_chunkwise_algebra_agrees(oracle_mod, T, chunk):
     for name, g, rr in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"), got, ref):
         rr = rr.reshape(g.shape)
         assert np.abs(g - rr).max() <= 1e-11 * max(1.0, np.abs(rr).max()), name
+
+
+def test_bwd_scalar_gate_is_channel_sum(oracle_mod):
+    """Gated DeltaNet (section 2.2: one decay a_t per token and head) is KDA
+    with every key channel's log_alpha equal to log a_t, so dL/dlog a_t is the
+    sum over channels of the oracle's dlog_alpha.  Pinned by central finite
+    differences of a separately written scalar-gate recurrence in log a_t; the
+    other gradients against the same differences on beta."""
+    T, H, dk, dv = 11, 2, 4, 3
+    r = rng0(71)
+    q = r.standard_normal((T, H, dk))
+    k = r.standard_normal((T, H, dk)) / np.sqrt(dk)
+    v = r.standard_normal((T, H, dv))
+    g = np.log(r.uniform(0.4, 1.0, (T, H)))
+    b = r.uniform(0.0, 1.0, (T, H))
+    h0 = r.standard_normal((H, dk, dv))
+    Wo = r.standard_normal((T, H, dv))
+    Wh = r.standard_normal((H, dk, dv))
+
+    def loss(gg, bb):
+        o = np.zeros((T, H, dv))
+        S = h0.copy()
+        for t in range(T):
+            for h in range(H):
+                kk = k[t, h]
+                S[h] = np.exp(gg[t, h]) * S[h]
+                S[h] = S[h] + bb[t, h] * np.outer(kk, v[t, h] - kk @ S[h])
+                o[t, h] = S[h].T @ q[t, h]
+        return float((o * Wo).sum() + (S * Wh).sum())
+
+    la = np.repeat(g[:, :, None], dk, axis=2)
+    res = oracle_mod.bwd(q, k, v, la, b, Wo, h0=h0[None], d_hT=Wh[None])
+    eps = 1e-6
+    for x, got in ((g, res[3].sum(-1)), (b, res[4])):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            fd[idx] = ((loss(xp, b) - loss(xm, b)) if x is g else (loss(g, xp) - loss(g, xm))) / (2 * eps)
+        np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-7)
