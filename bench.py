@@ -334,6 +334,22 @@ def main():
             "hbm": {"alg_bytes_per_launch": bb, "achieved_gbs": bb / (bms * 1e-3) / 1e9,
                     "frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "workspace_bytes": ws.numel()}
+        if not args.no_gdn:
+            # the scalar-gate backward (Gated DeltaNet) on the same inputs, the
+            # gate being the first channel of the per-channel draw
+            del ws
+            g4 = d["log_alpha"][:, :, 0].contiguous().unsqueeze(0)
+            ws = torch.empty(kda.kda_gdn_chunk_bwd_workspace_size(1, T, H, dk, dv, 0, kda.KDA_BF16),
+                             dtype=torch.uint8, device=dev)
+            fng = lambda: kda.kda_gdn_chunk_bwd(a4[0], a4[1], a4[2], g4, a4[4], go.unsqueeze(0),
+                                                want_grad_h0=False, workspace=ws)
+            per_gb, _ = time_launches(fng, args.steps, args.warmup, stream)
+            gbms = float(np.mean(per_gb))
+            out["backward"]["gdn"] = {
+                "workload": "kda_gdn_chunk_bwd, log_alpha [T, H] = the first channel of the same draw",
+                "ms_per_step": gbms, "tokens_per_s": T / (gbms * 1e-3), "vs_kda_backward_ms": gbms / bms,
+                "workspace_bytes": ws.numel()}
+            del g4
         if not args.no_cpu_baseline:
             out["backward"]["cpu_baseline"] = cpu_baseline_bwd(d, go, 2, 16384, H)
         del go, ws, a4

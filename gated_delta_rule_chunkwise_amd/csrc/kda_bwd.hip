@@ -1195,32 +1195,43 @@ hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t st) {
 // the channel gradients of log alpha summed per (token, head) in a fixed order.
 // This is exact by the chain rule: every channel's log alpha is the one value.
 
-// la_full[th][c] = log_alpha[th] (0 without a gate), beta32[th] = beta[th].
+// la_full[th][c] = log_alpha[th] (0 without a gate), beta32[th] = beta[th];
+// one thread per 4 channels (16-byte stores).
 template <typename GT>
 __global__ __launch_bounds__(256) void gdn_expand_kernel(const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
                                                          int64_t rows, int dk, float *__restrict__ la_full,
                                                          float *__restrict__ beta32) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one element of la_full
-    if (i >= rows * dk) return;
-    const int64_t th = i / dk;
-    la_full[i] = log_alpha ? to_f32(log_alpha[th]) : 0.f;
-    if (i % dk == 0) beta32[th] = to_f32(beta[th]);
+    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 consecutive elements of la_full
+    if (i4 >= rows * (dk / 4)) return;
+    const int64_t th = i4 / (dk / 4);
+    const float x = log_alpha ? to_f32(log_alpha[th]) : 0.f;
+    f32x4_t y;
+    y[0] = y[1] = y[2] = y[3] = x;
+    *reinterpret_cast<f32x4_t *>(la_full + 4 * i4) = y;
+    if (i4 % (dk / 4) == 0) beta32[th] = to_f32(beta[th]);
 }
 
-// grad_log_alpha[th] = sum_c dla32[th][c] (fixed order), grad_beta[th] = dbeta32[th].
+// grad_log_alpha[th] = sum_c dla32[th][c], grad_beta[th] = dbeta32[th].  A row
+// is summed by dk/4 lanes (16-byte loads), then across them by an xor
+// butterfly: a fixed order, so the result is deterministic.
 template <typename GT>
 __global__ __launch_bounds__(256) void gdn_finish_kernel(const float *__restrict__ dla32,
                                                          const float *__restrict__ dbeta32, int64_t rows, int dk,
                                                          GT *__restrict__ grad_log_alpha, GT *__restrict__ grad_beta) {
-    const int64_t th = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (th >= rows) return;
-    if (grad_log_alpha) {
-        const float *x = dla32 + th * dk;
-        float acc = 0.f;
-        for (int c = 0; c < dk; ++c) acc += x[c];
-        grad_log_alpha[th] = from_f32<GT>(acc);
+    const int lpr = dk / 4;                                  // lanes per row: 32 or 16, dividing the wave
+    const int sub = threadIdx.x % lpr;
+    const int64_t th = ((int64_t)blockIdx.x * 256 + threadIdx.x) / lpr;
+    const bool ok = th < rows;
+    float v = 0.f;
+    if (grad_log_alpha && ok) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(dla32 + th * dk + 4 * sub);
+        v = (x[0] + x[1]) + (x[2] + x[3]);
     }
-    grad_beta[th] = from_f32<GT>(dbeta32[th]);
+    for (int off = lpr / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (ok && sub == 0) {
+        if (grad_log_alpha) grad_log_alpha[th] = from_f32<GT>(v);
+        grad_beta[th] = from_f32<GT>(dbeta32[th]);
+    }
 }
 
 size_t gdn_extra_bytes(const BwdArgs &a) {
@@ -1248,12 +1259,12 @@ int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_l
     float *dla32 = reinterpret_cast<float *>(x + full);
     float *beta32 = reinterpret_cast<float *>(x + (2 * full + 255) / 256 * 256);
     float *dbeta32 = reinterpret_cast<float *>(x + (2 * full + 255) / 256 * 256 + ((size_t)rows * 4 + 255) / 256 * 256);
-    if ((rows * a.d_k + 255) / 256 > 0x7fffffffLL) {
+    if ((rows * (a.d_k / 4) + 255) / 256 > 0x7fffffffLL) {
         snprintf(err, err_len, "gdn_chunk_bwd grid too large");
         return -1;
     }
     if (rows > 0) {
-        const int64_t nblk = (rows * a.d_k + 255) / 256;
+        const int64_t nblk = (rows * (a.d_k / 4) + 255) / 256;
         if (a.gate_bf16)
             hipLaunchKernelGGL(gdn_expand_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
                                static_cast<const bf16_t *>(a.log_alpha), static_cast<const bf16_t *>(a.beta), rows,
@@ -1272,7 +1283,7 @@ int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_l
     b.workspace_bytes = base;
     if (launch_chunk_bwd(b, stream, err, err_len) != 0) return -1;
     if (rows > 0) {
-        const int64_t nblk = (rows + 255) / 256;
+        const int64_t nblk = (rows * (a.d_k / 4) + 255) / 256;
         const float *src_la = a.dlog_alpha ? dla32 : nullptr;
         if (a.gate_bf16)
             hipLaunchKernelGGL(gdn_finish_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st, dla32, dbeta32, rows,
