@@ -254,14 +254,20 @@ template <int ROWS, int COLS, int NT, typename X> struct Stage {
 };
 
 // ----------------------------------------------------------------------------
-// Prep: one workgroup of 4 waves per (chunk, head).
+// Prep: one workgroup of 4 waves per (chunk, head).  The key channels are taken
+// 64 at a time (the column scan is per channel and the Gram products are sums
+// over channels, accumulated in registers across the passes in the order of a
+// single pass); only KA is kept for all channels, for W.  This keeps the
+// workgroup within half of the LDS, so that two share a CU.
 template <int DK> struct alignas(16) PrepBS {
-    static constexpr int KS = DK + 4;
-    static constexpr int CS = kB + 4;
-    float KA[kB][KS];
-    float KI[kB][KS];
+    static constexpr int CH = DK < 64 ? DK : 64;   // channels per pass
+    static constexpr int KS = DK + 4, HS = CH + 4, CS = kB + 4;
+    float KA[kB][KS];                        // k, then K e^{G-m}, then diag(beta) KA
     union {
-        float QA[kB][KS];                    // Gram phase
+        struct {
+            float QA[kB][HS];                // this pass's channels: q, then QA
+            float KI[kB][HS];                // log alpha, then K e^{m-G}
+        } g;
         struct {
             float A[kB][CS];                 // beta M
             float T[kB][CS];                 // (I + A)^{-1}
@@ -269,7 +275,7 @@ template <int DK> struct alignas(16) PrepBS {
     };
     float X[4][16][20];                      // per-wave product tile
     float beta[kB];
-    float part[kSeg][DK];                    // segment totals of the column scan
+    float part[kSeg][CH];                    // segment totals of the column scan
     int flag;
 };
 
@@ -292,78 +298,93 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
 
     if (tid == 0) sm.flag = 0;
     if (tid < kB) sm.beta[tid] = tid < nv ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
-    {   // q -> QA, k -> KA, log alpha -> KI, as fp32 (rows >= nv zero)
-        const size_t base = ((size_t)t0 * H + h) * DK, pitch = (size_t)H * DK;
-        Stage<kB, DK, 256, IO> sq, sk;
-        Stage<kB, DK, 256, GT> sl;
-        sq.load(q + base, pitch, nv, tid);
-        sk.load(k + base, pitch, nv, tid);
-        sl.load(log_alpha + base, pitch, nv, tid);
-        sq.template store<S::KS>(&sm.QA[0][0], tid);
-        sk.template store<S::KS>(&sm.KA[0][0], tid);
-        sl.template store<S::KS>(&sm.KI[0][0], tid);
-    }
-    __syncthreads();
-    {   // G (log2 units) per key channel, segment totals first
-        constexpr int PT = 256 / DK;
-        const int c = tid % DK, p = tid / DK;
-        for (int sg = p; sg < kSeg; sg += PT) {
-            const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
-            float l = 0.f;
-            for (int r = r0; r < r1; ++r) l += sm.KI[r][c] * kBL2E;
-            sm.part[sg][c] = l;
-        }
-    }
-    __syncthreads();
-    {   // then the decayed operands in place
-        constexpr int PT = 256 / DK;
-        const int c = tid % DK, p = tid / DK;
-        float g2 = 0.f;
+    // Wave w accumulates tile (s, w) of P = lower(QA KI^T) and of
+    // M = strictly-lower(KA KI^T) for block rows s >= w.
+    constexpr int CH = S::CH, NH = DK / CH;
+    f32x4_t accP[4], accM[4];
 #pragma unroll
-        for (int i = 0; i < kSeg; ++i) g2 += sm.part[i][c];
-        const float m2 = 0.5f * g2;
-        for (int sg = p; sg < kSeg; sg += PT) {
-            float pre = 0.f;
-            for (int i = 0; i < sg; ++i) pre += sm.part[i][c];
-            const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
-            float l = 0.f;
-            for (int r = r0; r < r1; ++r) {
-                l += sm.KI[r][c] * kBL2E;
-                const float G = pre + l;
-                const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
-                const float kv = sm.KA[r][c];
-                sm.QA[r][c] *= ea;
-                sm.KA[r][c] = kv * ea;
-                sm.KI[r][c] = kv * ei;
+    for (int s4 = 0; s4 < 4; ++s4) accP[s4] = accM[s4] = zero4();
+    const size_t base = ((size_t)t0 * H + h) * DK, pitch = (size_t)H * DK;
+    for (int hf = 0; hf < NH; ++hf) {
+        const int c0 = hf * CH;
+        {   // q -> QA, k -> KA, log alpha -> KI, as fp32 (rows >= nv zero)
+            Stage<kB, CH, 256, IO> sq, sk;
+            Stage<kB, CH, 256, GT> sl;
+            sq.load(q + base + c0, pitch, nv, tid);
+            sk.load(k + base + c0, pitch, nv, tid);
+            sl.load(log_alpha + base + c0, pitch, nv, tid);
+            if (hf > 0) __syncthreads();     // the previous pass's reads of QA and KI are done
+            sq.template store<S::HS>(&sm.g.QA[0][0], tid);
+            sk.template store<S::KS>(&sm.KA[0][c0], tid);
+            sl.template store<S::HS>(&sm.g.KI[0][0], tid);
+        }
+        __syncthreads();
+        {   // G (log2 units) per key channel, segment totals first
+            constexpr int PT = 256 / CH;
+            const int c = tid % CH, p = tid / CH;
+            for (int sg = p; sg < kSeg; sg += PT) {
+                const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
+                float l = 0.f;
+                for (int r = r0; r < r1; ++r) l += sm.g.KI[r][c] * kBL2E;
+                sm.part[sg][c] = l;
             }
         }
-        if (p == 0) {
-            if (-g2 > kBwdMaxRange2 || !(g2 == g2)) sm.flag = 1;
-            rec[R::EM + c] = __builtin_amdgcn_exp2f(m2);
-            rec[R::EG + c] = __builtin_amdgcn_exp2f(g2);
-            rec[R::EGM + c] = __builtin_amdgcn_exp2f(g2 - m2);
+        __syncthreads();
+        {   // then the decayed operands in place
+            constexpr int PT = 256 / CH;
+            const int c = tid % CH, p = tid / CH;
+            float g2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < kSeg; ++i) g2 += sm.part[i][c];
+            const float m2 = 0.5f * g2;
+            for (int sg = p; sg < kSeg; sg += PT) {
+                float pre = 0.f;
+                for (int i = 0; i < sg; ++i) pre += sm.part[i][c];
+                const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
+                float l = 0.f;
+                for (int r = r0; r < r1; ++r) {
+                    l += sm.g.KI[r][c] * kBL2E;
+                    const float G = pre + l;
+                    const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
+                    const float kv = sm.KA[r][c0 + c];
+                    sm.g.QA[r][c] *= ea;
+                    sm.KA[r][c0 + c] = kv * ea;
+                    sm.g.KI[r][c] = kv * ei;
+                }
+            }
+            if (p == 0) {
+                if (-g2 > kBwdMaxRange2 || !(g2 == g2)) sm.flag = 1;
+                rec[R::EM + c0 + c] = __builtin_amdgcn_exp2f(m2);
+                rec[R::EG + c0 + c] = __builtin_amdgcn_exp2f(g2);
+                rec[R::EGM + c0 + c] = __builtin_amdgcn_exp2f(g2 - m2);
+            }
+        }
+        __syncthreads();
+        // QA and KI of these channels go to the record as they are.
+        for (int i = tid; i < kB * CH / 4; i += 256) {
+            const int r = i / (CH / 4), c = (i % (CH / 4)) * 4;
+            *reinterpret_cast<f32x4_t *>(rec + R::QA + r * DK + c0 + c) =
+                *reinterpret_cast<const f32x4_t *>(&sm.g.QA[r][c]);
+            *reinterpret_cast<f32x4_t *>(rec + R::KI + r * DK + c0 + c) =
+                *reinterpret_cast<const f32x4_t *>(&sm.g.KI[r][c]);
+        }
+        // the Gram products over these channels
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            if (w <= s4) {
+                accP[s4] = mm<CH, S::HS, 1, 1, S::HS>(accP[s4], &sm.g.QA[16 * s4][0], &sm.g.KI[16 * w][0], lane);
+                accM[s4] = mm<CH, S::KS, 1, 1, S::HS>(accM[s4], &sm.KA[16 * s4][c0], &sm.g.KI[16 * w][0], lane);
+            }
         }
     }
-    __syncthreads();
     if (tid == 0) rec[R::FLAG] = sm.flag ? 1.f : 0.f;
-    // QA and KI go to the record as they are.
-    for (int i = tid; i < kB * DK / 4; i += 256) {
-        const int r = i / (DK / 4), c = (i % (DK / 4)) * 4;
-        *reinterpret_cast<f32x4_t *>(rec + R::QA + r * DK + c) = *reinterpret_cast<const f32x4_t *>(&sm.QA[r][c]);
-        *reinterpret_cast<f32x4_t *>(rec + R::KI + r * DK + c) = *reinterpret_cast<const f32x4_t *>(&sm.KI[r][c]);
-    }
-    // P = lower(QA KI^T) and M = strictly-lower(KA KI^T): wave w computes the
-    // tiles of block column w, s = 0..3 of P and s = 4..7 of M (block row s & 3).
+    // P and M to the record (tiles above the diagonal are zero)
     f32x4_t mt[4];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const bool isM = s >= 4;
         const int Rt = s & 3, It = w;
-        f32x4_t acc = zero4();
-        if (It <= Rt) {
-            const float *a = isM ? &sm.KA[16 * Rt][0] : &sm.QA[16 * Rt][0];
-            acc = mm<DK, S::KS, 1, 1, S::KS>(acc, a, &sm.KI[16 * It][0], lane);
-        }
+        f32x4_t acc = isM ? accM[Rt] : accP[Rt];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * Rt + acc_row(lane, e), c = 16 * It + acc_col(lane);
@@ -373,7 +394,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
         }
         if (isM) mt[s & 3] = acc;
     }
-    __syncthreads();   // QA no longer read
+    __syncthreads();   // QA and KI no longer read
     // A = diag(beta) M into the inversion area; KA <- diag(beta) KA for W.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
