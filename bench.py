@@ -328,8 +328,8 @@ def main():
                          "unit": "TFLOP/s", "frac": bf / (bms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
                          "traffic": load_traffic("chunk_bwd_prefill_h32_t65536_traffic.json",
                                                  source_digest(BWD_SOURCES)),
-                         "kernel": "kda_chunk_bwd = bwd_prep_kernel + bwd_fwd_state_kernel + "
-                                   "bwd_rev_state_kernel + bwd_grad_kernel <128,128,bf16,bf16>",
+                         "kernel": "kda_chunk_bwd = bwd_prep_kernel + bwd_state_kernel (replay and reverse "
+                                   "passes in one launch) + bwd_grad_kernel <128,128,bf16,bf16>",
                          "alg_flops_per_launch": bf},
             "hbm": {"alg_bytes_per_launch": bb, "achieved_gbs": bb / (bms * 1e-3) / 1e9,
                     "frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},

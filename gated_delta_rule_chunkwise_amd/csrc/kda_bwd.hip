@@ -30,13 +30,15 @@
 // (the anchor m cancels from every result, so it is held fixed; g_n enters
 // through e^{g_n} and e^{g_n-m}).
 //
-// Four kernels, all in fp32 on the fp32 matrix cores:
+// Three kernels, all in fp32 on the fp32 matrix cores:
 //   bwd_prep_kernel    per (chunk, head), all in parallel: QA, KI, W, T, P, M
 //                      and the anchor factors into a record per chunk-head;
-//   bwd_fwd_state      per (sequence, head, 16 value columns): replays the
-//                      state recurrence, storing each chunk's start state and U;
-//   bwd_rev_state      same grid, chunks in reverse: the state gradient at each
-//                      chunk's end and dU; dh0 after the first chunk;
+//   bwd_state_kernel   two independent passes side by side in one launch, each
+//                      per (sequence, head, 32 value columns):
+//                        replay: the state recurrence, storing each chunk's
+//                        start state and U;
+//                        reverse: chunks in reverse order, the state gradient
+//                        at each chunk's end and dU; dh0 after the first chunk;
 //   bwd_grad_kernel    per (chunk, head), all in parallel: everything else,
 //                      with the d_v contractions accumulated over 16-column
 //                      blocks in registers.
@@ -62,7 +64,7 @@ namespace {
 constexpr int kB = kPlanChunk;                    // chunk length, 64
 constexpr float kBL2E = 1.4426950408889634f;
 constexpr float kBwdMaxRange2 = 230.f;            // max in-chunk decay, log2 units
-constexpr int kBV = 16;                           // value columns per block
+constexpr int kBV = 16;                           // value columns per block of the gradient kernel
 // Column scans over a chunk (the in-chunk cumsum of log alpha and the reverse
 // cumsum of its gradient) run as kSeg segments of kSegRows rows per key
 // channel, in parallel: G_r = (sum of the earlier segments' totals) + (running
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
 
 // ----------------------------------------------------------------------------
 // The two sequential passes: one workgroup of 8 waves per (sequence, head,
-// block of 16 value columns), walking the sequence's chunks.  Waves 0-3 compute;
+// block of value columns), walking the sequence's chunks.  Waves 0-3 compute;
 // waves 4-7 only move data: they hold the next chunk's record span in registers
 // (slot s of loader thread t: float4 number t + 256 s of the span), write it
 // into LDS at the chunk boundary, issue the following chunk's loads while the
@@ -539,13 +541,13 @@ __device__ __forceinline__ f32x4_t mm_bs(f32x4_t acc, const float *a, const floa
     return acc;
 }
 
-// Stores a [ROWS][16] block held transposed in LDS (element (r, c) at
+// Stores a [ROWS][BV] block held transposed in LDS (element (r, c) at
 // src[c * LS + r]) to global rows of the given pitch, with NT threads.
-template <int ROWS, int LS, int NT>
+template <int ROWS, int BV, int LS, int NT>
 __device__ __forceinline__ void block_out_t(float *__restrict__ dst, size_t pitch, const float *src, int t) {
 #pragma unroll
-    for (int i = t; i < ROWS * kBV / 4; i += NT) {
-        const int r = i / (kBV / 4), c = (i % (kBV / 4)) * 4;
+    for (int i = t; i < ROWS * BV / 4; i += NT) {
+        const int r = i / (BV / 4), c = (i % (BV / 4)) * 4;
         f32x4_t x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = src[(c + e) * LS + r];
@@ -553,48 +555,49 @@ __device__ __forceinline__ void block_out_t(float *__restrict__ dst, size_t pitc
     }
 }
 
-// Blocks with the 16 value columns as rows (Vt, Ut, St) are kept transposed, so
+// Blocks with the BV value columns as rows (Vt, Ut, St) are kept transposed, so
 // that they are contiguous along the contraction index as B operands.
-template <int DK> struct alignas(16) FwdBS {
+template <int DK, int BV> struct alignas(16) FwdBS {
     static constexpr int KS = DK + 4, CS = kB + 4;
     float T[kB][CS];
     float KI[kB][KS];
     float W[kB][KS];
-    float Vt[kBV][CS];                       // V^T block
+    float Vt[BV][CS];                        // V^T block
     float beta[kB];
-    float Ut[kBV][CS];
-    float St[kBV][KS];                       // S^T block
+    float Ut[BV][CS];
+    float St[BV][KS];                        // S^T block
     float cv[3 * DK + 4];                    // e^m, e^{g_n}, e^{g_n-m}, flag
 };
 
-template <int DK, int DV, typename IO, typename GT>
-__global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict__ v, const GT *__restrict__ beta,
-                                                            const float *__restrict__ h0, const int32_t *__restrict__ cu,
-                                                            const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
-                                                            int H, int64_t nch,
-                                                            const float *__restrict__ recs, float *__restrict__ Sc,
-                                                            float *__restrict__ Uc, float *__restrict__ sflag) {
+// Forward replay of one (sequence, head, BV value columns): S at every chunk's
+// start and U, from h0, walking the chunks forwards.
+template <int DK, int DV, int BV, typename IO, typename GT>
+__device__ __forceinline__ void fwd_state_body(FwdBS<DK, BV> &sm, int64_t id, const IO *__restrict__ v,
+                                               const GT *__restrict__ beta, const float *__restrict__ h0,
+                                               const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+                                               int64_t N, int64_t T, int H, int64_t nch,
+                                               const float *__restrict__ recs, float *__restrict__ Sc,
+                                               float *__restrict__ Uc, float *__restrict__ sflag) {
     using R = BRec<DK>;
-    using S = FwdBS<DK>;
-    __shared__ S sm;
-    constexpr int NVB = DV / kBV;
+    using S = FwdBS<DK, BV>;
+    constexpr int NVB = DV / BV;
     constexpr int ST = kB * kB / 4 / kLT, SK = kB * DK / 4 / kLT;
     static_assert(ST * kLT * 4 == kB * kB && SK * kLT * 4 == kB * DK, "span slots");
     int64_t chain;
     int vb;
-    if (!chain_of<NVB>(blockIdx.x, (int64_t)N * H, chain, vb)) return;
+    if (!chain_of<NVB>(id, (int64_t)N * H, chain, vb)) return;
     const int h = (int)(chain % H);
     const int64_t n = chain / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const bool loader = tid >= kSP - kLT;
     const int lt = tid - (kSP - kLT);
-    const int j0 = vb * kBV;
+    const int j0 = vb * BV;
     int64_t bos, eos, slot0;
     seq_range(n, cu, chunk_off, T, bos, eos, slot0);
     const int nchunks = (int)((eos - bos + kB - 1) / kB);
 
-    for (int i = tid; i < DK * kBV; i += kSP) {
-        const int c = i / kBV, j = i % kBV;
+    for (int i = tid; i < DK * BV; i += kSP) {
+        const int c = i / BV, j = i % BV;
         sm.St[j][c] = h0 ? h0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
     }
     // Loader schedule per chunk: at the boundary, T, W, the factors, V and beta
@@ -605,7 +608,7 @@ __global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict
     SpanRegs<ST> pT;
     SpanRegs<SK> pW, pK;
     ColRegs<DK> pc;
-    Stage<kB, kBV, kLT, IO> pv;
+    Stage<kB, BV, kLT, IO> pv;
     float pb = 0.f;
     auto rec_of = [&](int ci) { return recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS; };
     auto fetch_a = [&](int ci) {
@@ -642,27 +645,33 @@ __global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict
 #pragma unroll
             for (int s = 0; s < SK; ++s) put4<DK, S::KS>(&sm.KI[0][0], lt + kLT * s, pK.r[s]);
             if (ci + 1 < nchunks) fetch_a(ci + 1);
-            block_out_t<DK, S::KS, kLT>(Sc + ((size_t)h * nch + slot) * DK * DV + j0, DV, &sm.St[0][0], lt);
-        } else {   // U = T diag(beta) V - W Diag(e^m) S, one row tile per wave
-            f32x4_t a = zero4(), b = zero4();
-            a = mm_bs<kB, S::CS, 1, 1, S::CS>(a, &sm.T[16 * w][0], &sm.Vt[0][0], sm.beta, lane);
-            b = mm_bs<DK, S::KS, 1, 1, S::KS>(b, &sm.W[16 * w][0], &sm.St[0][0], em, lane);
+            block_out_t<DK, BV, S::KS, kLT>(Sc + ((size_t)h * nch + slot) * DK * DV + j0, DV, &sm.St[0][0], lt);
+        } else {   // U = T diag(beta) V - W Diag(e^m) S: one row tile per wave, each 16-column tile
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Ut[acc_col(lane)][16 * w + acc_row(lane, e)] = a[e] - b[e];
+            for (int jt = 0; jt < BV / 16; ++jt) {
+                f32x4_t a = zero4(), b = zero4();
+                a = mm_bs<kB, S::CS, 1, 1, S::CS>(a, &sm.T[16 * w][0], &sm.Vt[16 * jt][0], sm.beta, lane);
+                b = mm_bs<DK, S::KS, 1, 1, S::KS>(b, &sm.W[16 * w][0], &sm.St[16 * jt][0], em, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.Ut[16 * jt + acc_col(lane)][16 * w + acc_row(lane, e)] = a[e] - b[e];
+            }
         }
         __syncthreads();
         if (loader) {
             if (ci + 1 < nchunks) pK.load(rec_of(ci + 1) + R::KI, lt);
-            block_out_t<kB, S::CS, kLT>(Uc + ((size_t)h * nch + slot) * kB * DV + j0, DV, &sm.Ut[0][0], lt);
+            block_out_t<kB, BV, S::CS, kLT>(Uc + ((size_t)h * nch + slot) * kB * DV + j0, DV, &sm.Ut[0][0], lt);
         } else {   // S <- Diag(e^{g_n}) S + Diag(e^{g_n-m}) KI^T U
 #pragma unroll
             for (int ct = w; ct < DK / 16; ct += 4) {
-                f32x4_t a = zero4();
-                a = mm<kB, 1, S::KS, 1, S::CS>(a, &sm.KI[0][16 * ct], &sm.Ut[0][0], lane);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
-                    sm.St[j][c] = eg[c] * sm.St[j][c] + egm[c] * a[e];
+                for (int jt = 0; jt < BV / 16; ++jt) {
+                    f32x4_t a = zero4();
+                    a = mm<kB, 1, S::KS, 1, S::CS>(a, &sm.KI[0][16 * ct], &sm.Ut[16 * jt][0], lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 16 * ct + acc_row(lane, e), j = 16 * jt + acc_col(lane);
+                        sm.St[j][c] = eg[c] * sm.St[j][c] + egm[c] * a[e];
+                    }
                 }
             }
         }
@@ -673,47 +682,45 @@ __global__ __launch_bounds__(kSP) void bwd_fwd_state_kernel(const IO *__restrict
     if (vb == 0 && tid == 0) sflag[n * H + h] = anybad;
 }
 
-// Reverse state-gradient pass: same grid and roles, chunks in reverse order.
-template <int DK> struct alignas(16) RevBS {
+// Reverse state-gradient pass: same roles, chunks in reverse order.
+template <int DK, int BV> struct alignas(16) RevBS {
     static constexpr int KS = DK + 4, CS = kB + 4;
     float KI[kB][KS];
     float W[kB][KS];
     float QA[kB][KS];
     float P[kB][CS];
-    float dOt[kBV][CS];                      // dO^T block
-    float dUt[kBV][CS];
-    float dSt[kBV][KS];                      // (dL/dS at the chunk's end)^T
+    float dOt[BV][CS];                       // dO^T block
+    float dUt[BV][CS];
+    float dSt[BV][KS];                       // (dL/dS at the chunk's end)^T
     float cv[3 * DK + 4];                    // e^m, e^{g_n}, e^{g_n-m}, flag
 };
 
-template <int DK, int DV, typename IO>
-__global__ __launch_bounds__(kSP) void bwd_rev_state_kernel(const IO *__restrict__ d_o, const float *__restrict__ d_hT,
-                                                            const int32_t *__restrict__ cu,
-                                                            const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
-                                                            int H, int64_t nch, const float *__restrict__ recs,
-                                                            float *__restrict__ dSc,
-                                                            float *__restrict__ dUc, float *__restrict__ dh0) {
+template <int DK, int DV, int BV, typename IO>
+__device__ __forceinline__ void rev_state_body(RevBS<DK, BV> &sm, int64_t id, const IO *__restrict__ d_o,
+                                               const float *__restrict__ d_hT, const int32_t *__restrict__ cu,
+                                               const int32_t *__restrict__ chunk_off, int64_t N, int64_t T, int H,
+                                               int64_t nch, const float *__restrict__ recs, float *__restrict__ dSc,
+                                               float *__restrict__ dUc, float *__restrict__ dh0) {
     using R = BRec<DK>;
-    using S = RevBS<DK>;
-    __shared__ S sm;
-    constexpr int NVB = DV / kBV;
+    using S = RevBS<DK, BV>;
+    constexpr int NVB = DV / BV;
     constexpr int ST = kB * kB / 4 / kLT, SK = kB * DK / 4 / kLT;
     static_assert(ST * kLT * 4 == kB * kB && SK * kLT * 4 == kB * DK, "span slots");
     int64_t chain;
     int vb;
-    if (!chain_of<NVB>(blockIdx.x, (int64_t)N * H, chain, vb)) return;
+    if (!chain_of<NVB>(id, (int64_t)N * H, chain, vb)) return;
     const int h = (int)(chain % H);
     const int64_t n = chain / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const bool loader = tid >= kSP - kLT;
     const int lt = tid - (kSP - kLT);
-    const int j0 = vb * kBV;
+    const int j0 = vb * BV;
     int64_t bos, eos, slot0;
     seq_range(n, cu, chunk_off, T, bos, eos, slot0);
     const int nchunks = (int)((eos - bos + kB - 1) / kB);
 
-    for (int i = tid; i < DK * kBV; i += kSP) {
-        const int c = i / kBV, j = i % kBV;
+    for (int i = tid; i < DK * BV; i += kSP) {
+        const int c = i / BV, j = i % BV;
         sm.dSt[j][c] = d_hT ? d_hT[(((size_t)n * H + h) * DK + c) * DV + j0 + j] : 0.f;
     }
     // Loader schedule per chunk: at the boundary, KI, P, the factors and dO go
@@ -725,7 +732,7 @@ __global__ __launch_bounds__(kSP) void bwd_rev_state_kernel(const IO *__restrict
     SpanRegs<ST> pP;
     SpanRegs<2 * SK> pWQ;                    // W and QA are adjacent in the record
     ColRegs<DK> pc;
-    Stage<kB, kBV, kLT, IO> po;
+    Stage<kB, BV, kLT, IO> po;
     auto rec_of = [&](int ci) { return recs + ((size_t)h * nch + slot0 + ci) * R::FLOATS; };
     auto fetch_a = [&](int ci) {
         const int64_t t0 = bos + (int64_t)kB * ci;
@@ -759,41 +766,77 @@ __global__ __launch_bounds__(kSP) void bwd_rev_state_kernel(const IO *__restrict
                 else put4<DK, S::KS>(&sm.QA[0][0], lt + kLT * (s - SK), pWQ.r[s]);
             }
             if (ci > 0) fetch_a(ci - 1);
-            block_out_t<DK, S::KS, kLT>(dSc + ((size_t)h * nch + slot) * DK * DV + j0, DV, &sm.dSt[0][0], lt);
-        } else {   // dU = P^T dO + KI Diag(e^{g_n-m}) dS, one row tile per wave
-            f32x4_t a = zero4(), b = zero4();
-            a = mm<kB, 1, S::CS, 1, S::CS>(a, &sm.P[0][16 * w], &sm.dOt[0][0], lane);
-            b = mm_bs<DK, S::KS, 1, 1, S::KS>(b, &sm.KI[16 * w][0], &sm.dSt[0][0], egm, lane);
+            block_out_t<DK, BV, S::KS, kLT>(dSc + ((size_t)h * nch + slot) * DK * DV + j0, DV, &sm.dSt[0][0], lt);
+        } else {   // dU = P^T dO + KI Diag(e^{g_n-m}) dS: one row tile per wave, each 16-column tile
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.dUt[acc_col(lane)][16 * w + acc_row(lane, e)] = a[e] + b[e];
+            for (int jt = 0; jt < BV / 16; ++jt) {
+                f32x4_t a = zero4(), b = zero4();
+                a = mm<kB, 1, S::CS, 1, S::CS>(a, &sm.P[0][16 * w], &sm.dOt[16 * jt][0], lane);
+                b = mm_bs<DK, S::KS, 1, 1, S::KS>(b, &sm.KI[16 * w][0], &sm.dSt[16 * jt][0], egm, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.dUt[16 * jt + acc_col(lane)][16 * w + acc_row(lane, e)] = a[e] + b[e];
+            }
         }
         __syncthreads();
         if (loader) {
             if (ci > 0) pWQ.load(rec_of(ci - 1) + R::W, lt);
-            block_out_t<kB, S::CS, kLT>(dUc + ((size_t)h * nch + slot) * kB * DV + j0, DV, &sm.dUt[0][0], lt);
+            block_out_t<kB, BV, S::CS, kLT>(dUc + ((size_t)h * nch + slot) * kB * DV + j0, DV, &sm.dUt[0][0], lt);
         } else {   // dS <- Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS
             const bool bad = sm.cv[3 * DK] != 0.f;
 #pragma unroll
             for (int ct = w; ct < DK / 16; ct += 4) {
-                f32x4_t a = zero4(), b = zero4();
-                a = mm<kB, 1, S::KS, 1, S::CS>(a, &sm.QA[0][16 * ct], &sm.dOt[0][0], lane);
-                b = mm<kB, 1, S::KS, 1, S::CS>(b, &sm.W[0][16 * ct], &sm.dUt[0][0], lane);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = 16 * ct + acc_row(lane, e), j = acc_col(lane);
-                    const float x = em[c] * (a[e] - b[e]) + eg[c] * sm.dSt[j][c];
-                    sm.dSt[j][c] = bad ? __builtin_nanf("") : x;
+                for (int jt = 0; jt < BV / 16; ++jt) {
+                    f32x4_t a = zero4(), b = zero4();
+                    a = mm<kB, 1, S::KS, 1, S::CS>(a, &sm.QA[0][16 * ct], &sm.dOt[16 * jt][0], lane);
+                    b = mm<kB, 1, S::KS, 1, S::CS>(b, &sm.W[0][16 * ct], &sm.dUt[16 * jt][0], lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 16 * ct + acc_row(lane, e), j = 16 * jt + acc_col(lane);
+                        const float x = em[c] * (a[e] - b[e]) + eg[c] * sm.dSt[j][c];
+                        sm.dSt[j][c] = bad ? __builtin_nanf("") : x;
+                    }
                 }
             }
         }
         __syncthreads();
     }
     if (dh0) {
-        for (int i = tid; i < DK * kBV; i += kSP) {
-            const int c = i / kBV, j = i % kBV;
+        for (int i = tid; i < DK * BV; i += kSP) {
+            const int c = i / BV, j = i % BV;
             dh0[(((size_t)n * H + h) * DK + c) * DV + j0 + j] = sm.dSt[j][c];
         }
     }
+}
+
+// The two sequential passes read only the prep kernel's records (the reverse
+// pass needs neither S nor U), so they run side by side in one launch: blocks
+// [0, fwd_blocks) replay forwards, the rest walk backwards.  With kSBV value
+// columns per workgroup each pass has half as many workgroups as with 16, and
+// at the long-context shape both fit the chip at once.
+constexpr int kSBV = 32;
+template <int DK, int BV> union StateBS {
+    FwdBS<DK, BV> f;
+    RevBS<DK, BV> r;
+};
+
+template <int DK, int DV, int BV, typename IO, typename GT>
+__global__ __launch_bounds__(kSP) void bwd_state_kernel(const IO *__restrict__ v, const GT *__restrict__ beta,
+                                                        const float *__restrict__ h0, const IO *__restrict__ d_o,
+                                                        const float *__restrict__ d_hT, const int32_t *__restrict__ cu,
+                                                        const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
+                                                        int H, int64_t nch, const float *__restrict__ recs,
+                                                        float *__restrict__ Sc, float *__restrict__ Uc,
+                                                        float *__restrict__ sflag, float *__restrict__ dSc,
+                                                        float *__restrict__ dUc, float *__restrict__ dh0,
+                                                        int64_t fwd_blocks) {
+    __shared__ StateBS<DK, BV> sm;
+    const int64_t id = blockIdx.x;
+    if (id < fwd_blocks)
+        fwd_state_body<DK, DV, BV, IO, GT>(sm.f, id, v, beta, h0, cu, chunk_off, N, T, H, nch, recs, Sc, Uc, sflag);
+    else
+        rev_state_body<DK, DV, BV, IO>(sm.r, id - fwd_blocks, d_o, d_hT, cu, chunk_off, N, T, H, nch, recs, dSc, dUc,
+                                       dh0);
 }
 
 // ----------------------------------------------------------------------------
@@ -1186,13 +1229,12 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     if (L.nch > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((bwd_prep_kernel<DK, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st, q, k,
                            la, be, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs);
-    const int64_t grid = chain_grid(a.num_seqs * a.H, DV / kBV);
+    const int64_t grid = chain_grid(a.num_seqs * a.H, DV / kSBV);   // per pass (a multiple of 8)
     if (grid > 0) {
-        if (a.total_tokens > 0)
-            hipLaunchKernelGGL((bwd_fwd_state_kernel<DK, DV, IO, GT>), dim3((unsigned)grid), dim3(kSP), 0, st, v, be,
-                               a.h0, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, sflag);
-        hipLaunchKernelGGL((bwd_rev_state_kernel<DK, DV, IO>), dim3((unsigned)grid), dim3(kSP), 0, st, dO, a.d_hT,
-                           a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, dSc, dUc, a.dh0);
+        const int64_t fb = a.total_tokens > 0 ? grid : 0;   // no replay without tokens
+        hipLaunchKernelGGL((bwd_state_kernel<DK, DV, kSBV, IO, GT>), dim3((unsigned)(fb + grid)), dim3(kSP), 0, st, v,
+                           be, a.h0, dO, a.d_hT, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc,
+                           sflag, dSc, dUc, a.dh0, fb);
     }
     if (L.nch > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st, k,
@@ -1326,7 +1368,7 @@ int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_l
 int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const BwdLayout L = bwd_layout(a);
-    if (L.nch > 0x7fffffffLL || chain_grid(a.num_seqs * a.H, a.d_v / kBV) > 0x7fffffffLL) {
+    if (L.nch > 0x7fffffffLL || 2 * chain_grid(a.num_seqs * a.H, a.d_v / kSBV) > 0x7fffffffLL) {
         snprintf(err, err_len, "chunk_bwd grid too large");
         return -1;
     }
