@@ -11,7 +11,8 @@ under "prologue"; the same shape with one decay per token and head (Gated
 DeltaNet) and with none (DeltaNet), through kda_gdn_chunk_fwd, under "gdn"; and
 with separate erase and write strengths (kda_chunk_fwd_decoupled) under
 "decoupled"; the gradients of the same prefill (kda_chunk_bwd) under
-"backward".
+"backward"; kda_chunk_fwd on the short (H=16, T=4096) and packed variable-length
+(32 sequences of 512-8192 tokens, h0 given) workloads under "other_workloads".
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -186,6 +187,7 @@ def main():
     ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--no-decoupled", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-other", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -308,6 +310,27 @@ def main():
                          "traffic": load_traffic("chunk_fwd_decoupled_prefill_h32_t65536_traffic.json", digest),
                          "alg_bytes_per_launch": db_}}
         del wv
+
+    # ---------------- the other prefill workloads: short sequence and packed batch
+    if not args.no_other:
+        other = {}
+        for key, cfg in (("c1", I.C1), ("c2", I.C2)):
+            dd = I.make_chunk_inputs(cfg, device=dev)
+            Tt, Hh = dd["q"].shape[0], dd["q"].shape[1]
+            nseq = len(dd["lengths"])
+            cu = dd["cu_seqlens"].to(dev) if nseq > 1 else None
+            h_T = torch.empty((nseq, Hh, dk, dv), dtype=torch.float32, device=dev)
+            o2 = torch.empty_like(dd["v"])
+            fno = lambda: kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], h0=dd["h0"],
+                                            cu_seqlens=cu, o=o2, h_T=h_T)
+            per_o, _ = time_launches(fno, args.steps, args.warmup, stream)
+            oms = float(np.mean(per_o))
+            ob = chunk_alg_bytes(Tt * Hh, nseq * Hh * (2 if dd["h0"] is not None else 1), dk, dv)
+            other[key] = {"workload": "kda_chunk_fwd, " + cfg.name + (" (%d sequences, %d tokens)" % (nseq, Tt)),
+                          "ms_per_step": oms, "tokens_per_s": Tt / (oms * 1e-3),
+                          "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob}
+            del dd, o2, h_T, cu
+        out["other_workloads"] = other
 
     # ---------------- backward of the same prefill
     if not args.no_backward:

@@ -664,7 +664,8 @@ size_t chunk_fwd_workspace_bytes(const ChunkArgs &a) {
 
 int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const int64_t nwg = a.num_seqs * (int64_t)a.H * (a.d_v / 16);
+    // the state kernel pads the chains to a multiple of 8 (one group per XCD)
+    const int64_t nwg = (a.num_seqs * (int64_t)a.H + 7) / 8 * 8 * (a.d_v / 16);
     if (nwg > 0x7fffffffLL) {
         snprintf(err, err_len, "chunk_fwd grid too large");
         return -1;

@@ -977,6 +977,20 @@ __device__ __forceinline__ void loader_role_loop(StateSmem<DK, DV, BV> &sm, cons
     }
 }
 
+// Block id -> (chain = sequence * H + head, value-column block).  Workgroups go
+// to the 8 XCDs round-robin by block id; the nvb column blocks of one chain get
+// ids that are equal modulo 8 and within 8 * nvb of each other, so they run on
+// one XCD at about the same time and read each chunk record from that XCD's L2
+// once, however many chains there are.  Ids past the last chain return.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool state_block(int64_t id, int64_t chains, int nvb, int64_t &chain, int &vb) {
+    const int64_t q = id / kXcds;
+    vb = (int)(q % nvb);
+    chain = id % kXcds + kXcds * (q / nvb);
+    return chain < chains;
+}
+int64_t state_grid(int64_t chains, int nvb) { return (chains + kXcds - 1) / kXcds * kXcds * nvb; }
+
 template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
@@ -988,12 +1002,13 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
     __shared__ StateSmem<DK, DV, BV> sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t wg = blockIdx.x;
-    const int64_t chain = wg % num_chains;
+    int64_t chain;
+    int vb;
+    if (!state_block(blockIdx.x, num_chains, DV / BV, chain, vb)) return;
     ChainRange cr;
     cr.n = chain / H;
     cr.h = (int)(chain % H);
-    cr.col0 = (int)(wg / num_chains) * BV;
+    cr.col0 = vb * BV;
     if (cu_seqlens) {
         cr.bos = cu_seqlens[cr.n];
         cr.eos = cu_seqlens[cr.n + 1];
@@ -1030,7 +1045,7 @@ hipError_t launch_pass(const ChunkArgs &a, int bv, int32_t *chunk_off, uint8_t *
     if constexpr (DK == 64) {
         if (bv == 32) {
             hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 32, IO, GT, PRO, GM, DEC>),
-                               dim3((unsigned)(chains * (DV / 32))), dim3(kStateThreads), 0, st, (const IO *)a.q,
+                               dim3((unsigned)state_grid(chains, DV / 32)), dim3(kStateThreads), 0, st, (const IO *)a.q,
                                (const IO *)a.k, (const IO *)a.v, (const GT *)a.log_alpha, (const GT *)a.beta,
                                (const GT *)a.w_write, a.h0, a.cu_seqlens,
                                (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains,
@@ -1038,7 +1053,7 @@ hipError_t launch_pass(const ChunkArgs &a, int bv, int32_t *chunk_off, uint8_t *
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT, PRO, GM, DEC>), dim3((unsigned)(chains * (DV / 16))),
+    hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT, PRO, GM, DEC>), dim3((unsigned)state_grid(chains, DV / 16)),
                            dim3(kStateThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
                            (const GT *)a.log_alpha, (const GT *)a.beta, (const GT *)a.w_write, a.h0, a.cu_seqlens,
                            (const int32_t *)chunk_off, recs, (IO *)a.o, a.h_T, a.seq_len, a.H, chains,
