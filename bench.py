@@ -108,6 +108,19 @@ def load_traffic(name, digest):
     return rec.get("hbm_bytes_per_call")
 
 
+def load_mfma_counters(name, digest):
+    """Counter-measured matrix-core busy share and matrix flops per call, from the
+    same committed summary; None when absent or stale."""
+    try:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != digest or rec.get("mfma_busy_pct") is None:
+        return None
+    return {"busy_pct": rec["mfma_busy_pct"], "flops_per_call": rec.get("mfma_flops_per_call")}
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
     counters to bytes: 1 GiB read + 1 GiB written per launch, three launches."""
@@ -236,7 +249,8 @@ def main():
             "alg_bytes_per_launch": alg_b}
     mfma = {"alg_flops_per_launch": alg_f, "achieved_tflops": alg_f / (ms * 1e-3) / 1e12,
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
-            "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+            "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "counters": load_mfma_counters("chunk_fwd_prefill_h32_t65536_traffic.json", digest)}
 
     out = {"metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -353,7 +367,9 @@ def main():
                                                  source_digest(BWD_SOURCES)),
                          "kernel": "kda_chunk_bwd = bwd_prep_kernel + bwd_state_kernel (replay and reverse "
                                    "passes in one launch) + bwd_grad_kernel <128,128,bf16,bf16>",
-                         "alg_flops_per_launch": bf},
+                         "alg_flops_per_launch": bf,
+                         "counters": load_mfma_counters("chunk_bwd_prefill_h32_t65536_traffic.json",
+                                                        source_digest(BWD_SOURCES))},
             "hbm": {"alg_bytes_per_launch": bb, "achieved_gbs": bb / (bms * 1e-3) / 1e9,
                     "frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "workspace_bytes": ws.numel()}
