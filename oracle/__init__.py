@@ -67,6 +67,9 @@ def _load():
         lib.kda_oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, ip, i64, i64, i64, i64, dp, dp,
                                        dp, dp, dp, dp, dp, dp, ctypes.c_int]
         lib.kda_oracle_bwd.restype = ctypes.c_int
+        lib.kda_oracle_gen_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, i64, i64, i64, i64, dp, dp,
+                                           dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_gen_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -214,6 +217,43 @@ def bwd(q, k, v, log_alpha, beta, d_o, h0=None, d_hT=None, cu_seqlens=None, nthr
     if rc != 0:
         raise RuntimeError("kda_oracle_bwd failed with code %d" % rc)
     return dq, dk_, dv_, dla, db, dh0
+
+
+def gen_bwd(q, k, v, log_alpha, b_erase, w_write, d_o, h0=None, d_hT=None, cu_seqlens=None, nthreads=None):
+    """Gradient of the generalised recurrence (``gen_fwd``: separate erase and
+    write strengths; ``kda_oracle_gen_bwd`` in kda_oracle.c).  Returns (dq, dk,
+    dv, dlog_alpha, db_erase, dw_write, dh0) in fp64 with the input shapes."""
+    q = _f64(q)
+    if q.ndim != 3:
+        raise ValueError("q must be [T, H, dk]")
+    T, H, dk = q.shape
+    k = _f64(k, (T, H, dk))
+    la = _f64(log_alpha, (T, H, dk))
+    v = _f64(v)
+    if v.ndim != 3 or v.shape[:2] != (T, H):
+        raise ValueError("v must be [T, H, dv]")
+    dv = v.shape[2]
+    be = _f64(b_erase, (T, H))
+    wr = _f64(w_write, (T, H))
+    do = _f64(d_o, (T, H, dv))
+    cu = _cu(cu_seqlens, T)
+    N = cu.size - 1
+    h0a = None if h0 is None else _f64(h0, (N, H, dk, dv))
+    dhT = None if d_hT is None else _f64(d_hT, (N, H, dk, dv))
+    dq = np.zeros((T, H, dk))
+    dk_ = np.zeros((T, H, dk))
+    dv_ = np.zeros((T, H, dv))
+    dla = np.zeros((T, H, dk))
+    db = np.zeros((T, H))
+    dw = np.zeros((T, H))
+    dh0 = np.zeros((N, H, dk, dv))
+    rc = _load().kda_oracle_gen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(wr), _ptr(h0a),
+                                    _ptr(cu), N, H, dk, dv, _ptr(do), _ptr(dhT), _ptr(dq), _ptr(dk_),
+                                    _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dw), _ptr(dh0),
+                                    int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_gen_bwd failed with code %d" % rc)
+    return dq, dk_, dv_, dla, db, dw, dh0
 
 
 # Default eps of the L2 normalisation (the GPU entry points use the same value).

@@ -272,6 +272,11 @@ int kda_oracle_prologue(const double *q, const double *k, const double *a, const
  *     dS = Diag(a) dSd             (= dL/dS_{t-1});
  * and dh0 = dS once the sequence's first token is done.
  *
+ * With separate erase and write strengths (the generalised recurrence, u =
+ * w_t v_t - b_t r), the same reverse step has dw_t = du . v_t,
+ * db_t = -du . r, dv_t = w_t du and dr = -b_t du; with w = b, dw + db is the
+ * dbeta above.
+ *
  * The reverse pass needs S_{t-1} and S_t for every t.  They are recomputed
  * from checkpoints (the state before every K-th token, K ~ sqrt(length)),
  * one block of K tokens at a time, by the same forward step in the same
@@ -280,9 +285,11 @@ int kda_oracle_prologue(const double *q, const double *k, const double *a, const
  */
 typedef struct {
     const double *q, *k, *v, *log_alpha, *beta, *h0, *d_o, *d_hT;
+    const double *wr;             /* write strengths; NULL: tied to beta */
     const int64_t *cu_seqlens;
     int64_t num_seqs, H, dk, dv;
     double *dq, *dkk, *dvv, *dla, *dbeta, *dh0;
+    double *dwr;                  /* gradient of wr (used when wr is given) */
     int64_t next_chain;
     pthread_mutex_t mu;
     int failed;
@@ -303,8 +310,14 @@ static void bwd_fwd_step(const oracle_bwd_job *J, int64_t t, int64_t h, double *
     for (int64_t j = 0; j < dv; ++j) r[j] = 0.0;
     for (int64_t c = 0; c < dk; ++c)
         for (int64_t j = 0; j < dv; ++j) r[j] += kt[c] * S[c * dv + j];
-    for (int64_t c = 0; c < dk; ++c)
-        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += kt[c] * (bt * (vt[j] - r[j]));
+    if (J->wr) {
+        const double wt = J->wr[t * H + h];
+        for (int64_t c = 0; c < dk; ++c)
+            for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += kt[c] * (wt * vt[j] - bt * r[j]);
+    } else {
+        for (int64_t c = 0; c < dk; ++c)
+            for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += kt[c] * (bt * (vt[j] - r[j]));
+    }
 }
 
 static int run_bwd_chain(const oracle_bwd_job *J, int64_t n, int64_t h)
@@ -352,6 +365,7 @@ static int run_bwd_chain(const oracle_bwd_job *J, int64_t n, int64_t h)
             const double *lat = J->log_alpha + (t * H + h) * dk;
             const double *dot = J->d_o + (t * H + h) * dv;
             const double bt = J->beta[t * H + h];
+            const double wt = J->wr ? J->wr[t * H + h] : bt;
             double *dqt = J->dq + (t * H + h) * dk;
             double *dkt = J->dkk + (t * H + h) * dk;
             double *dvt = J->dvv + (t * H + h) * dv;
@@ -365,7 +379,10 @@ static int run_bwd_chain(const oracle_bwd_job *J, int64_t n, int64_t h)
             for (int64_t j = 0; j < dv; ++j) r[j] = 0.0;
             for (int64_t c = 0; c < dk; ++c)
                 for (int64_t j = 0; j < dv; ++j) r[j] += kt[c] * Sd[c * dv + j];
-            for (int64_t j = 0; j < dv; ++j) u[j] = bt * (vt[j] - r[j]);
+            if (J->wr)
+                for (int64_t j = 0; j < dv; ++j) u[j] = wt * vt[j] - bt * r[j];
+            else
+                for (int64_t j = 0; j < dv; ++j) u[j] = bt * (vt[j] - r[j]);
 
             /* read-out o_t = S_t^T q_t */
             for (int64_t c = 0; c < dk; ++c)
@@ -384,11 +401,20 @@ static int run_bwd_chain(const oracle_bwd_job *J, int64_t n, int64_t h)
                 for (int64_t j = 0; j < dv; ++j) acc += dS[c * dv + j] * u[j];
                 dkt[c] = acc;
             }
-            /* u = beta (v - r) */
-            double db = 0.0;
-            for (int64_t j = 0; j < dv; ++j) db += du[j] * (vt[j] - r[j]);
-            J->dbeta[t * H + h] = db;
-            for (int64_t j = 0; j < dv; ++j) dvt[j] = bt * du[j];
+            /* u = beta (v - r), or w v - b r */
+            if (J->wr) {
+                double dw = 0.0, db = 0.0;
+                for (int64_t j = 0; j < dv; ++j) dw += du[j] * vt[j];
+                for (int64_t j = 0; j < dv; ++j) db -= du[j] * r[j];
+                J->dwr[t * H + h] = dw;
+                J->dbeta[t * H + h] = db;
+                for (int64_t j = 0; j < dv; ++j) dvt[j] = wt * du[j];
+            } else {
+                double db = 0.0;
+                for (int64_t j = 0; j < dv; ++j) db += du[j] * (vt[j] - r[j]);
+                J->dbeta[t * H + h] = db;
+                for (int64_t j = 0; j < dv; ++j) dvt[j] = bt * du[j];
+            }
             /* r = Sd^T k: dr = -beta du */
             for (int64_t j = 0; j < dv; ++j) du[j] = -bt * du[j];
             for (int64_t c = 0; c < dk; ++c) {
@@ -433,6 +459,25 @@ static void *bwd_worker(void *arg)
     return NULL;
 }
 
+static int run_bwd_job(oracle_bwd_job *J, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 1024) nthreads = 1024;
+    pthread_mutex_init(&J->mu, NULL);
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid) { pthread_mutex_destroy(&J->mu); return -1; }
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, bwd_worker, J) != 0) break;
+        ++started;
+    }
+    if (started == 0) bwd_worker(J);
+    for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+    free(tid);
+    pthread_mutex_destroy(&J->mu);
+    return J->failed ? -1 : 0;
+}
+
 /* Layouts as for kda_oracle_fwd; d_o like o, d_hT and dh0 like h0.  Outputs
  * dq, dk_out, dlog_alpha: [T_total, H, dk]; dv_out: [T_total, H, dv];
  * dbeta: [T_total, H]; dh0 may be NULL.  Returns 0, -1 (no memory) or -2. */
@@ -454,21 +499,32 @@ int kda_oracle_bwd(const double *q, const double *k, const double *v,
     J.d_o = d_o; J.d_hT = d_hT; J.cu_seqlens = cu_seqlens; J.num_seqs = num_seqs;
     J.H = H; J.dk = dk; J.dv = dv;
     J.dq = dq; J.dkk = dk_out; J.dvv = dv_out; J.dla = dlog_alpha; J.dbeta = dbeta; J.dh0 = dh0;
-    if (nthreads < 1) nthreads = 1;
-    if (nthreads > 1024) nthreads = 1024;
-    pthread_mutex_init(&J.mu, NULL);
-    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
-    if (!tid) { pthread_mutex_destroy(&J.mu); return -1; }
-    int started = 0;
-    for (int i = 0; i < nthreads; ++i) {
-        if (pthread_create(&tid[i], NULL, bwd_worker, &J) != 0) break;
-        ++started;
-    }
-    if (started == 0) bwd_worker(&J);
-    for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
-    free(tid);
-    pthread_mutex_destroy(&J.mu);
-    return J.failed ? -1 : 0;
+    return run_bwd_job(&J, nthreads);
 }
 
-int kda_oracle_version(void) { return 3; }
+/* Gradient of the generalised recurrence (kda_oracle_gen_fwd): as
+ * kda_oracle_bwd with the erase strengths b_erase in place of beta, plus the
+ * write strengths w_write [T_total, H]; d_b and d_w are their gradients. */
+int kda_oracle_gen_bwd(const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *b_erase, const double *w_write,
+                       const double *h0, const int64_t *cu_seqlens, int64_t num_seqs, int64_t H,
+                       int64_t dk, int64_t dv, const double *d_o, const double *d_hT,
+                       double *dq, double *dk_out, double *dv_out, double *dlog_alpha,
+                       double *d_b, double *d_w, double *dh0, int nthreads)
+{
+    if (H <= 0 || dk <= 0 || dv <= 0) return -2;
+    if (check_seqlens(cu_seqlens, num_seqs) != 0) return -2;
+    if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !log_alpha || !b_erase || !w_write || !d_o ||
+                                     !dq || !dk_out || !dv_out || !dlog_alpha || !d_b || !d_w))
+        return -2;
+    oracle_bwd_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = b_erase; J.wr = w_write; J.h0 = h0;
+    J.d_o = d_o; J.d_hT = d_hT; J.cu_seqlens = cu_seqlens; J.num_seqs = num_seqs;
+    J.H = H; J.dk = dk; J.dv = dv;
+    J.dq = dq; J.dkk = dk_out; J.dvv = dv_out; J.dla = dlog_alpha; J.dbeta = d_b; J.dwr = d_w;
+    J.dh0 = dh0;
+    return run_bwd_job(&J, nthreads);
+}
+
+int kda_oracle_version(void) { return 4; }

@@ -211,3 +211,80 @@ def test_bwd_scalar_gate_is_channel_sum(oracle_mod):
             xm[idx] -= eps
             fd[idx] = ((loss(xp, b) - loss(xm, b)) if x is g else (loss(g, xp) - loss(g, xm))) / (2 * eps)
         np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-7)
+
+
+def test_gen_bwd_matches_central_finite_differences(oracle_mod):
+    """Separate erase and write strengths: every element of all seven
+    gradients of the generalised recurrence against central differences of
+    oracle.gen_fwd, with an empty sequence in the batch."""
+    T, H, dk, dv = 8, 2, 3, 2
+    cu = np.array([0, 5, 5, 8])
+    N = 3
+    q, k, v, la, b, h0 = _case(T, H, dk, dv, N, 81)
+    w = rng0(82).uniform(-0.5, 1.5, (T, H))
+    x = [q, k, v, la, b, w, h0]
+    r = rng0(83)
+    Wo = r.standard_normal((T, H, dv))
+    Wh = r.standard_normal((N, H, dk, dv))
+
+    def loss(a):
+        o, hT = oracle_mod.gen_fwd(*a[:6], h0=a[6], cu_seqlens=cu)
+        return float((o * Wo).sum() + (hT * Wh).sum())
+
+    g = oracle_mod.gen_bwd(*x[:6], Wo, h0=x[6], d_hT=Wh, cu_seqlens=cu)
+    order = (0, 1, 2, 3, 4, 5, 6)     # gen_bwd returns dq, dk, dv, dla, db, dw, dh0
+    eps = 1e-6
+    for ai, gi in zip(range(7), order):
+        fd = np.zeros_like(x[ai])
+        for idx in np.ndindex(x[ai].shape):
+            a = [y.copy() for y in x]
+            a[ai][idx] += eps
+            lp = loss(a)
+            a[ai][idx] -= 2 * eps
+            fd[idx] = (lp - loss(a)) / (2 * eps)
+        np.testing.assert_allclose(g[gi], fd, rtol=1e-6, atol=1e-7, err_msg="input %d" % ai)
+
+
+def test_gen_bwd_tied_strengths_is_kda_bwd(oracle_mod):
+    """w = b = beta is KDA: the generalised gradient equals oracle.bwd, with
+    db + dw = dbeta."""
+    T, H, dk, dv = 30, 2, 6, 5
+    cu = np.array([0, 13, 30])
+    x = _case(T, H, dk, dv, 2, 91)
+    do = rng0(92).standard_normal((T, H, dv))
+    dhT = rng0(93).standard_normal((2, H, dk, dv))
+    a = oracle_mod.bwd(*x[:5], do, h0=x[5], d_hT=dhT, cu_seqlens=cu)
+    g = oracle_mod.gen_bwd(*x[:5], x[4], do, h0=x[5], d_hT=dhT, cu_seqlens=cu)
+    for name, u, ref in (("dq", g[0], a[0]), ("dk", g[1], a[1]), ("dv", g[2], a[2]), ("dla", g[3], a[3]),
+                         ("dbeta", g[4] + g[5], a[4]), ("dh0", g[6], a[5])):
+        np.testing.assert_allclose(u, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max(), err_msg=name)
+
+
+def test_gen_bwd_write_only_linear_attention(oracle_mod):
+    """b = 0, w = 1, alpha = 1, h0 = 0: S_t = sum_{i<=t} k_i v_i^T for ANY keys
+    (section 2.1's linear attention), o_t = sum_{i<=t} (q_t . k_i) v_i.  So
+    dq_t = sum_{i<=t} k_i (v_i . do_t), dk_i = sum_{t>=i} q_t (v_i . do_t),
+    dv_i = sum_{t>=i} (q_t . k_i) do_t, dw_i = v_i . dv_i, and
+    db_i = -(sum_{t>=i} (q_t . k_i) do_t) . (sum_{m<i} (k_m . k_i) v_m)."""
+    T, H, dk, dv = 9, 2, 4, 3
+    r = rng0(101)
+    q = r.standard_normal((T, H, dk))
+    k = r.standard_normal((T, H, dk))
+    v = r.standard_normal((T, H, dv))
+    do = r.standard_normal((T, H, dv))
+    la = np.zeros((T, H, dk))
+    g = oracle_mod.gen_bwd(q, k, v, la, np.zeros((T, H)), np.ones((T, H)), do)
+    qk = np.einsum("thc,ihc->hti", q, k)                 # [H, t, i] = q_t . k_i
+    kk = np.einsum("mhc,ihc->hmi", k, k)                 # [H, m, i] = k_m . k_i
+    vd = np.einsum("ihj,thj->hit", v, do)                # [H, i, t] = v_i . do_t
+    low = np.tril(np.ones((T, T)))                       # [t, i]: i <= t
+    ref_dq = np.einsum("ti,hit,ihc->thc", low, vd, k)
+    ref_dk = np.einsum("ti,hit,thc->ihc", low, vd, q)
+    ref_dv = np.einsum("ti,hti,thj->ihj", low, qk, do)
+    ref_dw = np.einsum("ihj,ihj->ih", v, ref_dv)
+    strict = np.tril(np.ones((T, T)), -1)                # [i, m]: m < i
+    rvec = np.einsum("im,hmi,mhj->ihj", strict, kk, v)   # sum_{m<i} (k_m . k_i) v_m
+    ref_db = -np.einsum("ihj,ihj->ih", ref_dv, rvec)
+    for name, u, ref in (("dq", g[0], ref_dq), ("dk", g[1], ref_dk), ("dv", g[2], ref_dv),
+                         ("dw", g[5], ref_dw), ("db", g[4], ref_db)):
+        np.testing.assert_allclose(u, ref, rtol=1e-10, atol=1e-12, err_msg=name)
