@@ -373,6 +373,17 @@ def main():
             "hbm": {"alg_bytes_per_launch": bb, "achieved_gbs": bb / (bms * 1e-3) / 1e9,
                     "frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "workspace_bytes": ws.numel()}
+        if not args.no_decoupled:
+            # separate erase and write strengths: beta erases, a write strength
+            # drawn like beta from its own seed writes
+            wv4 = I.draw_strength(d["beta"].shape, 5200, d["beta"].dtype, device=dev).unsqueeze(0)
+            fnd = lambda: kda.kda_chunk_bwd_decoupled(*a4, wv4, go.unsqueeze(0), want_grad_h0=False, workspace=ws)
+            per_db, _ = time_launches(fnd, args.steps, args.warmup, stream)
+            dbms = float(np.mean(per_db))
+            out["backward"]["decoupled"] = {
+                "workload": "kda_chunk_bwd_decoupled on the same inputs, beta as the erase strength",
+                "ms_per_step": dbms, "tokens_per_s": T / (dbms * 1e-3), "vs_kda_backward_ms": dbms / bms}
+            del wv4
         if not args.no_gdn:
             # the scalar-gate backward (Gated DeltaNet) on the same inputs, the
             # gate being the first channel of the per-channel draw

@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
     kda_decode_step_decoupled(q, k, v, log_alpha, b_erase, w_write, S, o=None)
     kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_seqlens=None, ...)
     kda_gdn_chunk_bwd(q, k, v, log_alpha_or_None, beta, grad_o, ...)
+    kda_chunk_bwd_decoupled(q, k, v, log_alpha, b_erase, w_write, grad_o, ...)
     kda_chunk_fwd_workspace_size(...), kda_chunk_bwd_workspace_size(...),
     kda_gdn_chunk_bwd_workspace_size(...),
     kda_status_string(code), kda_abi_version()
@@ -36,7 +37,7 @@ EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error"
                     "kda_chunk_fwd_prologue", "kda_decode_step_prologue", "kda_gdn_chunk_fwd",
                     "kda_gdn_decode_step", "kda_chunk_fwd_decoupled", "kda_decode_step_decoupled",
                     "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
-                    "kda_gdn_chunk_bwd_workspace_size", "kda_gdn_chunk_bwd")
+                    "kda_gdn_chunk_bwd_workspace_size", "kda_gdn_chunk_bwd", "kda_chunk_bwd_decoupled")
 
 _lib = None
 
@@ -99,6 +100,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_gdn_chunk_bwd_workspace_size.restype = sz
     lib.kda_gdn_chunk_bwd.argtypes = list(lib.kda_chunk_bwd.argtypes)
     lib.kda_gdn_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd_decoupled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    lib.kda_chunk_bwd_decoupled.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -288,7 +292,17 @@ def kda_gdn_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, c
                       gdn=True)
 
 
-def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0, workspace, gdn):
+def kda_chunk_bwd_decoupled(q, k, v, log_alpha, b_erase, w_write, grad_o, h0=None, grad_hT=None, cu_seqlens=None,
+                            *, want_grad_h0=True, workspace=None):
+    """Gradients of kda_chunk_fwd_decoupled: b_erase and w_write [B, T, H] in
+    log_alpha's dtype.  Returns (dq, dk, dv, dlog_alpha, db_erase, dw_write, dh0);
+    dh0 is None when want_grad_h0 is False."""
+    return _chunk_bwd(q, k, v, log_alpha, b_erase, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0, workspace,
+                      gdn=False, w_write=w_write)
+
+
+def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0, workspace, gdn,
+               w_write=None):
     import torch
     lib = load_library()
     squeeze = q.dim() == 3
@@ -296,6 +310,8 @@ def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_g
         q, k, v, beta, grad_o = (x.unsqueeze(0) for x in (q, k, v, beta, grad_o))
         if log_alpha is not None:
             log_alpha = log_alpha.unsqueeze(0)
+        if w_write is not None:
+            w_write = w_write.unsqueeze(0)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -312,6 +328,10 @@ def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_g
     if k.dtype != q.dtype or v.dtype != q.dtype or grad_o.dtype != q.dtype \
             or (log_alpha is not None and beta.dtype != log_alpha.dtype):
         raise TypeError("q, k, v, grad_o share one dtype; log_alpha and beta share one dtype")
+    if w_write is not None:
+        _check_dev("w_write", w_write, dev)
+        if w_write.shape != beta.shape or w_write.dtype != beta.dtype:
+            raise ValueError("w_write must match b_erase in shape and dtype")
     if cu_seqlens is not None:
         _check_dev("cu_seqlens", cu_seqlens, dev)
         if cu_seqlens.dtype != torch.int32:
@@ -337,17 +357,29 @@ def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_g
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() * workspace.element_size()
-    name = "kda_gdn_chunk_bwd" if gdn else "kda_chunk_bwd"
-    rc = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
-                            _ptr(cu_seqlens), nseq, _ptr(grad_o), _ptr(grad_hT), _ptr(dq), _ptr(dk_),
-                            _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dh0), B, T, H, dk, dv, io, gt,
-                            _ptr(workspace), ws_len, _stream_of(q))
+    if w_write is not None:
+        name = "kda_chunk_bwd_decoupled"
+        dw = torch.empty_like(w_write)
+        rc = lib.kda_chunk_bwd_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(w_write),
+                                         _ptr(h0), _ptr(cu_seqlens), nseq, _ptr(grad_o), _ptr(grad_hT), _ptr(dq),
+                                         _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dw), _ptr(dh0), B, T, H,
+                                         dk, dv, io, gt, _ptr(workspace), ws_len, _stream_of(q))
+    else:
+        name = "kda_gdn_chunk_bwd" if gdn else "kda_chunk_bwd"
+        rc = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                _ptr(cu_seqlens), nseq, _ptr(grad_o), _ptr(grad_hT), _ptr(dq), _ptr(dk_),
+                                _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dh0), B, T, H, dk, dv, io, gt,
+                                _ptr(workspace), ws_len, _stream_of(q))
     if rc != KDA_OK:
         raise KDAError(rc, name, kda_last_hip_error())
     if squeeze:
         dq, dk_, dv_, db = (x.squeeze(0) for x in (dq, dk_, dv_, db))
         if dla is not None:
             dla = dla.squeeze(0)
+        if w_write is not None:
+            dw = dw.squeeze(0)
+    if w_write is not None:
+        return dq, dk_, dv_, dla, db, dw, dh0
     return dq, dk_, dv_, dla, db, dh0
 
 

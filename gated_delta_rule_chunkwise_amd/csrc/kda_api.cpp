@@ -194,7 +194,8 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
                             const float *grad_hT, void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
                             void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H, int32_t d_k,
                             int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
-                            size_t workspace_bytes, void *stream, int gate_mode) {
+                            size_t workspace_bytes, void *stream, int gate_mode, bool decoupled = false,
+                            const void *w_write = nullptr, void *grad_w_write = nullptr) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -222,6 +223,8 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
             return KDA_ERR_INVALID_ARGUMENT;
         if (gate_mode == 1 && (!grad_log_alpha || !aligned_to(log_alpha, gsz) || !aligned_to(grad_log_alpha, gsz)))
             return KDA_ERR_INVALID_ARGUMENT;
+        if (decoupled && (!w_write || !grad_w_write || !aligned_to(w_write, gsz) || !aligned_to(grad_w_write, gsz)))
+            return KDA_ERR_INVALID_ARGUMENT;
     }
     if ((h0 && !aligned16(h0)) || (grad_hT && !aligned16(grad_hT)) || (grad_h0 && !aligned16(grad_h0)))
         return KDA_ERR_INVALID_ARGUMENT;
@@ -237,6 +240,8 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
     a.d_o = grad_o; a.d_hT = grad_hT;
     a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = gate_mode == 2 ? nullptr : grad_log_alpha;
     a.dbeta = grad_beta; a.dh0 = grad_h0;
+    a.w_write = decoupled ? w_write : nullptr;
+    a.dw_write = decoupled ? grad_w_write : nullptr;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     g_hip_error[0] = '\0';
     const int rc = gate_mode == 0 ? kda::launch_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error))
@@ -257,6 +262,19 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k, grad_v,
                           grad_log_alpha, grad_beta, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype, workspace,
                           workspace_bytes, stream, 0);
+}
+
+kda_status_t kda_chunk_bwd_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
+                                     const void *b_erase, const void *w_write, const float *h0,
+                                     const int32_t *cu_seqlens, int32_t num_seqs, const void *grad_o,
+                                     const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
+                                     void *grad_log_alpha, void *grad_b_erase, void *grad_w_write, float *grad_h0,
+                                     int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                     kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    return chunk_bwd_impl(q, k, v, log_alpha, b_erase, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k,
+                          grad_v, grad_log_alpha, grad_b_erase, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype,
+                          workspace, workspace_bytes, stream, 0, true, w_write, grad_w_write);
 }
 
 kda_status_t kda_gdn_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,

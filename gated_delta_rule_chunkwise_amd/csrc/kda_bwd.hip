@@ -861,7 +861,8 @@ template <int DK> struct alignas(16) GradBS {
             float KI[kB][KS];                // then (U dS_next^T) . KI
         } pt;
     } r3;
-    float beta[kB];
+    float beta[kB];                          // beta, or the erase strengths b
+    float wv[kB];                            // the write strengths w (separate strengths only)
     float dbr[kB];
     float dbA[4][kB];
     float m2[DK], em[DK], eg[DK], egm[DK];
@@ -877,7 +878,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const int32_t *__restrict__ chunk_off, int64_t N, int64_t T, int H, int64_t nch, const float *__restrict__ recs,
     const float *__restrict__ Sc, const float *__restrict__ Uc, const float *__restrict__ dSc,
     const float *__restrict__ dUc, const float *__restrict__ sflag, IO *__restrict__ dq, IO *__restrict__ dk,
-    IO *__restrict__ dv, GT *__restrict__ dla, GT *__restrict__ dbeta) {
+    IO *__restrict__ dv, GT *__restrict__ dla, GT *__restrict__ dbeta, const GT *__restrict__ wr,
+    GT *__restrict__ dwr) {
     using R = BRec<DK>;
     using S = GradBS<DK>;
     __shared__ S sm;
@@ -894,6 +896,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 
     if (tid < kB) {
         sm.beta[tid] = tid < nv ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+        sm.wv[tid] = (wr && tid < nv) ? to_f32(wr[(t0 + tid) * H + h]) : 0.f;
         sm.dbr[tid] = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.dbA[i][tid] = 0.f;
@@ -998,7 +1001,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 sm.r3.lp.dY[r][j] = a[e];
                 dbp[e] += a[e] * sm.r3.lp.V[r][j];
                 if (r < nv) {
-                    const float x = bad ? __builtin_nanf("") : sm.beta[r] * a[e];
+                    const float x = bad ? __builtin_nanf("") : (wr ? sm.wv[r] : sm.beta[r]) * a[e];
                     dv[((t0 + r) * H + h) * DV + j0 + j] = from_f32<IO>(x);
                 }
             }
@@ -1187,8 +1190,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         float kx = 0.f;
 #pragma unroll
         for (int i = 0; i < DK / 16; ++i) kx += sm.dbK[i][r];
-        const float x = (sm.dbr[r] - kx) + ((sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]));
-        dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
+        const float ma = (sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]);
+        if (wr) {   // separate strengths: the V term is the write strength's, the rest the erase's
+            dwr[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : sm.dbr[r]);
+            dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : ma - kx);
+        } else {
+            const float x = (sm.dbr[r] - kx) + ma;
+            dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
+        }
     }
     __syncthreads();
     if (sc_p < kSeg) {   // dlog alpha: reverse cumsum of dG plus dg_n
@@ -1222,6 +1231,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     float *sflag = reinterpret_cast<float *>(ws + L.sflag);
     const IO *q = static_cast<const IO *>(a.q), *k = static_cast<const IO *>(a.k), *v = static_cast<const IO *>(a.v);
     const GT *la = static_cast<const GT *>(a.log_alpha), *be = static_cast<const GT *>(a.beta);
+    const GT *wr = static_cast<const GT *>(a.w_write);     // separate write strengths, or NULL
     const IO *dO = static_cast<const IO *>(a.d_o);
     const int64_t T = a.seq_len;
     if (a.varlen)
@@ -1232,15 +1242,17 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const int64_t grid = chain_grid(a.num_seqs * a.H, DV / kSBV);   // per pass (a multiple of 8)
     if (grid > 0) {
         const int64_t fb = a.total_tokens > 0 ? grid : 0;   // no replay without tokens
+        // the replay's U takes the write strengths (beta when they are tied)
         hipLaunchKernelGGL((bwd_state_kernel<DK, DV, kSBV, IO, GT>), dim3((unsigned)(fb + grid)), dim3(kSP), 0, st, v,
-                           be, a.h0, dO, a.d_hT, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc,
-                           sflag, dSc, dUc, a.dh0, fb);
+                           wr ? wr : be, a.h0, dO, a.d_hT, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs,
+                           Sc, Uc, sflag, dSc, dUc, a.dh0, fb);
     }
     if (L.nch > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st, k,
                            v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, dSc, dUc,
                            sflag, static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv),
-                           static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta));
+                           static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta), wr,
+                           static_cast<GT *>(a.dw_write));
     return hipGetLastError();
 }
 

@@ -54,6 +54,9 @@ struct BwdArgs {
     const float *d_hT;          // gradient of h_T, or nullptr (zero)
     void *dq, *dk, *dv;         // io dtype
     void *dlog_alpha, *dbeta;   // gate dtype
+    const void *w_write;        // separate write strengths (gate dtype; beta is then the erase
+                                // strength), or nullptr: tied to beta
+    void *dw_write;             // their gradient (with w_write; dbeta is then the erase strength's)
     float *dh0;                 // or nullptr (not wanted)
     int64_t num_seqs, seq_len, total_tokens;
     int32_t H, d_k, d_v;

@@ -305,6 +305,35 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            void *stream);
 
 /*
+ * kda_chunk_bwd_decoupled -- gradients of kda_chunk_fwd_decoupled (separate
+ * erase strength b and write strength w per token and head):
+ *
+ *     S <- (I - b_t k_t k_t^T) Diag(alpha_t) S + w_t k_t v_t^T,   o_t = S^T q_t
+ *
+ * For a scalar loss with gradients grad_o, grad_hT as for kda_chunk_bwd, this
+ * computes dL/dq, dL/dk, dL/dv, dL/dlog_alpha, dL/db, dL/dw and dL/dh0 in the
+ * same kernels: the erase strength enters the triangular system and the
+ * erase term, the write strength the written values.  Arguments, workspace
+ * (kda_chunk_bwd_workspace_size), numerics, range and errors as for
+ * kda_chunk_bwd, with b_erase in place of beta and
+ *
+ *   w_write        [B, T, H] gate_dtype, aligned to its element size; required
+ *   grad_b_erase   [B, T, H] gate_dtype (out), in place of grad_beta
+ *   grad_w_write   [B, T, H] gate_dtype (out), aligned to its element size; required
+ *
+ * With w_write equal to b_erase, grad_b_erase + grad_w_write is kda_chunk_bwd's
+ * grad_beta (each part rounded on its own).
+ */
+kda_status_t kda_chunk_bwd_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
+                                     const void *b_erase, const void *w_write, const float *h0,
+                                     const int32_t *cu_seqlens, int32_t num_seqs, const void *grad_o,
+                                     const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
+                                     void *grad_log_alpha, void *grad_b_erase, void *grad_w_write,
+                                     float *grad_h0, int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                     int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace kda_gdn_chunk_bwd needs (arguments as for
  * kda_chunk_bwd_workspace_size; 0 for invalid arguments): that of
  * kda_chunk_bwd plus two fp32 [B*T*H, d_k] buffers and two fp32 [B*T*H]

@@ -350,3 +350,29 @@ def test_gdn_bwd_gate_alignment_is_element_size(kda):
     assert bwd_gdn(lib, la=P + 2, dla=P + 2, wsb=need - 1) == 3
     assert bwd_gdn(lib, la=P + 4, dla=P + 4, gt=0, wsb=base) == 3
     assert bwd(lib, la=P + 2, dla=P + 2) == 1          # the per-channel entry point needs 16 bytes
+
+
+def bwd_dec(lib, wr=P, dwr=P, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, go=P, ghT=None, dq=P, dk=P, dv=P,
+             dla=P, db=P, dh0=P, B=1, T=128, H=2, dk_=128, dv_=128, io=1, gt=1, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_chunk_bwd_decoupled(a["q"], a["k"], a["v"], a["la"], a["beta"], wr, a["h0"], a["cu"],
+                                       a["N"], a["go"], a["ghT"], a["dq"], a["dk"], a["dv"], a["dla"], a["db"],
+                                       dwr, a["dh0"], a["B"], a["T"], a["H"], a["dk_"], a["dv_"], a["io"],
+                                       a["gt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wr=None), 1), (dict(dwr=None), 1), (dict(wr=P + 1), 1), (dict(dwr=P + 2, gt=0), 1),
+    (dict(dk_=96), 2), (dict(H=65536, T=1), 2), (dict(la=P + 4), 1), (dict(beta=None), 1), (dict(db=None), 1),
+    (dict(ws=None), 3), (dict(wsb=0), 3),
+])
+def test_decoupled_bwd_rejects(kda, kw, code):
+    lib = kda.load_library()
+    assert bwd_dec(lib, **kw) == code
+
+
+def test_decoupled_bwd_empty_without_state_is_noop(kda):
+    lib = kda.load_library()
+    assert bwd_dec(lib, T=0, q=None, k=None, v=None, la=None, beta=None, wr=None, dwr=None, go=None, dq=None,
+                   dk=None, dv=None, dla=None, db=None, dh0=None) == 0

@@ -279,3 +279,70 @@ def test_gdn_bwd_c3_sampled_heads(kda):
     g = d["log_alpha"][:, :, 0].contiguous()
     go, _ = I.make_upstream_grads(d, 4100, with_state=False)
     gdn_check(kda, d, g, "bf16", go, None, heads=[0, 31], what="gdn bwd c3 heads 0,31")
+
+
+# ------------------------------------------------------------------ separate strengths
+# kda_chunk_bwd_decoupled: erase strength b and write strength w, against the
+# oracle's generalised backward (oracle.gen_bwd).
+NAMES_DEC = ("dq", "dk", "dv", "dlog_alpha", "db_erase", "dw_write", "dh0")
+
+
+def dec_check(kda, d, w, io, go, ghT, seqs=None, heads=None, what=""):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    out = kda.kda_chunk_bwd_decoupled(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], w.to(DEV),
+                                      go.to(DEV), h0=dev["h0"], grad_hT=None if ghT is None else ghT.to(DEV),
+                                      cu_seqlens=cu)
+    torch.cuda.synchronize()
+    out = [x.cpu() for x in out]
+    ref = to_oracle(d, seqs, heads)
+    hs = slice(None) if heads is None else list(heads)
+    sq = list(range(len(d["lengths"]))) if seqs is None else list(seqs)
+    rows = torch.from_numpy(ref["rows"])
+    res = oracle.gen_bwd(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], f64(w[rows][:, hs]),
+                         f64(go[rows][:, hs]), h0=ref["h0"], d_hT=None if ghT is None else f64(ghT[sq][:, hs]),
+                         cu_seqlens=ref["cu_seqlens"])
+    errs = {}
+    for name, x, r in zip(NAMES_DEC, out, res):
+        x = x[sq][:, hs] if name == "dh0" else x[rows][:, hs]
+        e = errors(x, r)
+        tol = F32_REL if (io == "f32" or name == "dh0") else BF16_REL
+        assert e["rel_max"] <= tol and e["rel_fro"] <= tol, "%s %s: %s (tol %g)" % (what, name, e, tol)
+        errs[name] = "%.1e/%.1e" % (e["rel_max"], e["rel_fro"])
+    log(what, errs)
+    return out
+
+
+@pytest.mark.parametrize("io,dk,dv", [("bf16", 128, 128), ("bf16", 64, 128), ("f32", 128, 64), ("f32", 64, 64)])
+def test_decoupled_bwd_ragged(kda, io, dk, dv):
+    cfg = I.ChunkConfig("dec-bwd", io, io, H=3, dk=dk, dv=dv, h0=True, seed=4200 + dk + dv)
+    d = I.make_chunk_inputs(cfg, lengths=[300, 64, 1, 0, 130])
+    w = I.draw_strength(d["beta"].shape, 4201, d["beta"].dtype)
+    go, ghT = I.make_upstream_grads(d, 4202)
+    dec_check(kda, d, w, io, go, ghT, what="decoupled bwd %s %dx%d" % (io, dk, dv))
+
+
+def test_decoupled_bwd_tied_is_kda_bwd(kda):
+    """w = b: the same gradients as kda_chunk_bwd, and db + dw = dbeta (each part
+    rounded on its own)."""
+    cfg = I.ChunkConfig("dec-tied", "f32", "f32", H=2, dk=128, dv=128, h0=True, seed=4300)
+    d = I.make_chunk_inputs(cfg, lengths=[200, 77])
+    go, ghT = I.make_upstream_grads(d, 4301)
+    a = run_bwd(kda, d, go, ghT)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    b = kda.kda_chunk_bwd_decoupled(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["beta"], go.to(DEV),
+                                    h0=g["h0"], grad_hT=ghT.to(DEV), cu_seqlens=g["cu_seqlens"])
+    torch.cuda.synchronize()
+    b = [x.cpu() for x in b]
+    for i, name in ((0, "dq"), (1, "dk"), (2, "dv"), (3, "dlog_alpha")):
+        assert torch.equal(a[i], b[i]), name
+    assert torch.equal(a[5], b[6]), "dh0"
+    e = errors(b[4] + b[5], f64(a[4]))
+    assert e["rel_max"] <= 1e-5, e
+
+
+def test_decoupled_bwd_c1_shape(kda):
+    d = I.make_chunk_inputs(I.C1)
+    w = I.draw_strength(d["beta"].shape, 4400, d["beta"].dtype)
+    go, ghT = I.make_upstream_grads(d, 4401)
+    dec_check(kda, d, w, "bf16", go, ghT, what="decoupled bwd c1")
