@@ -29,6 +29,9 @@
 //     dlog_alpha[t,c] = sum_{r >= t} dG[r,c] + dg_n[c]
 // (the anchor m cancels from every result, so it is held fixed; g_n enters
 // through e^{g_n} and e^{g_n-m}).
+// With separate erase and write strengths (b, w) beta above is b, except in
+// U's V term: U = T (diag(w) V - diag(b) KA S').  Then dV = diag(w) dY, and
+// dbeta splits into dw_r = sum_j dY[r,j] V[r,j] and db_r = the other two terms.
 //
 // Three kernels, all in fp32 on the fp32 matrix cores:
 //   bwd_prep_kernel    per (chunk, head), all in parallel: QA, KI, W, T, P, M
