@@ -70,6 +70,9 @@ def _load():
         lib.kda_oracle_gen_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, i64, i64, i64, i64, dp, dp,
                                            dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
         lib.kda_oracle_gen_bwd.restype = ctypes.c_int
+        lib.kda_oracle_prologue_bwd.argtypes = [dp, dp, dp, dp, i64, i64, ctypes.c_double, ctypes.c_double,
+                                                dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.kda_oracle_prologue_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -289,6 +292,30 @@ def fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h0=None,
     """KDA forward on raw projections: ``prologue`` then ``fwd``."""
     qh, kh, la, be = prologue(q_raw, k_raw, gate_pre, beta_pre, log_alpha_min, eps)
     return fwd(qh, kh, v, la, be, h0=h0, cu_seqlens=cu_seqlens, nthreads=nthreads)
+
+
+def bwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, d_o, h0=None, d_hT=None,
+                 cu_seqlens=None, nthreads=None, eps=PROLOGUE_EPS):
+    """Gradient of ``fwd_prologue``: ``bwd`` at the mapped inputs, then the chain
+    rule through the prologue maps (``kda_oracle_prologue_bwd`` in kda_oracle.c).
+    Returns (dq_raw, dk_raw, dv, dgate_pre, dbeta_pre, dh0) in fp64."""
+    qh, kh, la, be = prologue(q_raw, k_raw, gate_pre, beta_pre, log_alpha_min, eps)
+    dqh, dkh, dv, dla, dbe, dh0 = bwd(qh, kh, v, la, be, d_o, h0=h0, d_hT=d_hT, cu_seqlens=cu_seqlens,
+                                      nthreads=nthreads)
+    q = _f64(q_raw)
+    dk = q.shape[-1]
+    lead = q.shape[:-1]
+    k = _f64(k_raw, q.shape)
+    a = _f64(gate_pre, q.shape)
+    b = _f64(beta_pre, lead)
+    rows = int(np.prod(lead)) if lead else 1
+    dq, dk_, da, db = np.zeros_like(q), np.zeros_like(k), np.zeros_like(a), np.zeros_like(b)
+    rc = _load().kda_oracle_prologue_bwd(_ptr(q), _ptr(k), _ptr(a), _ptr(b), rows, dk, float(log_alpha_min),
+                                         float(eps), _ptr(dqh), _ptr(dkh), _ptr(dla), _ptr(dbe), _ptr(dq),
+                                         _ptr(dk_), _ptr(da), _ptr(db))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_prologue_bwd failed with code %d" % rc)
+    return dq, dk_, dv, da, db, dh0
 
 
 def decode_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, nthreads=None,

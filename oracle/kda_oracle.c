@@ -250,6 +250,54 @@ int kda_oracle_prologue(const double *q, const double *k, const double *a, const
     return 0;
 }
 
+/* Backward of the input prologue: the chain rule through the maps above, per
+ * row.  Given the gradients of the mapped values (dq_hat, dk_hat, dla, dbeta),
+ * returns those of the raw ones:
+ *     dq = (dq_hat - q_hat (q_hat . dq_hat)) / ||q||   where ||q|| > eps,
+ *     dq = dq_hat / eps                                 otherwise (q_hat = q / eps);
+ * dk likewise;
+ *     da = -sigmoid(a) dla   where -softplus(a) > lo (the floor does not bind),
+ *     da = 0                 otherwise;
+ *     db = beta (1 - beta) dbeta.
+ * Layouts as for kda_oracle_prologue.  Returns 0 or -2. */
+int kda_oracle_prologue_bwd(const double *q, const double *k, const double *a, const double *b,
+                            int64_t rows, int64_t dk, double lo, double eps,
+                            const double *dq_hat, const double *dk_hat, const double *dla,
+                            const double *dbeta, double *dq, double *dk_out, double *da, double *db)
+{
+    if (rows < 0 || dk <= 0 || !(eps > 0.0)) return -2;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *qr = q + r * dk, *kr = k + r * dk, *ar = a + r * dk;
+        const double *gq = dq_hat + r * dk, *gk = dk_hat + r * dk, *gl = dla + r * dk;
+        double nq = 0.0, nk = 0.0;
+        for (int64_t c = 0; c < dk; ++c) {
+            nq += qr[c] * qr[c];
+            nk += kr[c] * kr[c];
+        }
+        nq = sqrt(nq);
+        nk = sqrt(nk);
+        /* projections q_hat . dq_hat and k_hat . dk_hat (used only when ||.|| > eps) */
+        double pq = 0.0, pk = 0.0;
+        if (nq > eps)
+            for (int64_t c = 0; c < dk; ++c) pq += (qr[c] / nq) * gq[c];
+        if (nk > eps)
+            for (int64_t c = 0; c < dk; ++c) pk += (kr[c] / nk) * gk[c];
+        for (int64_t c = 0; c < dk; ++c) {
+            dq[r * dk + c] = nq > eps ? (gq[c] - (qr[c] / nq) * pq) / nq : gq[c] / eps;
+            dk_out[r * dk + c] = nk > eps ? (gk[c] - (kr[c] / nk) * pk) / nk : gk[c] / eps;
+            const double x = ar[c];
+            const double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+            const double e = exp(-fabs(x));
+            const double sg = x >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);   /* sigmoid(a) = d softplus / da */
+            da[r * dk + c] = -sp > lo ? -sg * gl[c] : 0.0;
+        }
+        const double e = exp(-fabs(b[r]));
+        const double be = b[r] >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
+        db[r] = be * (1.0 - be) * dbeta[r];
+    }
+    return 0;
+}
+
 /* Gradient of the KDA forward, for training.
  *
  * KimiLinear article (intl.cloud.baidu.com), sections 3 and 4.1: the chunkwise

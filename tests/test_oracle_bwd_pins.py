@@ -288,3 +288,45 @@ def test_gen_bwd_write_only_linear_attention(oracle_mod):
     for name, u, ref in (("dq", g[0], ref_dq), ("dk", g[1], ref_dk), ("dv", g[2], ref_dv),
                          ("dw", g[5], ref_dw), ("db", g[4], ref_db)):
         np.testing.assert_allclose(u, ref, rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_bwd_prologue_matches_central_finite_differences(oracle_mod):
+    """The forward on raw projections (oracle.fwd_prologue): every gradient of
+    oracle.bwd_prologue against central differences, with rows whose norm is
+    below eps (the eps branch), gates where the floor binds and where it does
+    not, and an empty sequence.  eps = 0.5 and the floor at -2 keep every
+    difference away from a branch point."""
+    T, H, dk, dv = 8, 2, 3, 2
+    cu = np.array([0, 5, 5, 8])
+    N = 3
+    r = rng0(111)
+    q = r.standard_normal((T, H, dk))
+    k = r.standard_normal((T, H, dk))
+    q[2, 0] *= 0.05 / np.linalg.norm(q[2, 0])       # below eps
+    k[6, 1] *= 0.1 / np.linalg.norm(k[6, 1])
+    v = r.standard_normal((T, H, dv))
+    a = r.uniform(-3.0, 1.0, (T, H, dk))
+    a[1, 0, 0], a[4, 1, 2] = 4.0, 6.0                # -softplus below the floor -2
+    b = r.standard_normal((T, H))
+    h0 = r.standard_normal((N, H, dk, dv))
+    lo, eps = -2.0, 0.5
+    Wo = r.standard_normal((T, H, dv))
+    Wh = r.standard_normal((N, H, dk, dv))
+    x = [q, k, v, a, b, h0]
+
+    def loss(z):
+        o, hT = oracle_mod.fwd_prologue(z[0], z[1], z[2], z[3], z[4], lo, h0=z[5], cu_seqlens=cu, eps=eps)
+        return float((o * Wo).sum() + (hT * Wh).sum())
+
+    g = oracle_mod.bwd_prologue(q, k, v, a, b, lo, Wo, h0=h0, d_hT=Wh, cu_seqlens=cu, eps=eps)
+    assert np.all(g[3][1, 0, 0] == 0.0) and np.all(g[3][4, 1, 2] == 0.0)
+    step = 1e-6
+    for ai in range(6):
+        fd = np.zeros_like(x[ai])
+        for idx in np.ndindex(x[ai].shape):
+            z = [y.copy() for y in x]
+            z[ai][idx] += step
+            lp = loss(z)
+            z[ai][idx] -= 2 * step
+            fd[idx] = (lp - loss(z)) / (2 * step)
+        np.testing.assert_allclose(g[ai], fd, rtol=1e-6, atol=1e-7, err_msg="input %d" % ai)
