@@ -373,6 +373,24 @@ def main():
             "hbm": {"alg_bytes_per_launch": bb, "achieved_gbs": bb / (bms * 1e-3) / 1e9,
                     "frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "workspace_bytes": ws.numel()}
+        if not args.no_prologue:
+            # the same gradients taken through the input prologue, on raw projections
+            del ws
+            dr = I.make_chunk_raw_inputs(cfg, device=dev, gate="uniform")
+            ws = torch.empty(kda.kda_chunk_bwd_prologue_workspace_size(1, T, H, dk, dv, 0, kda.KDA_BF16),
+                             dtype=torch.uint8, device=dev)
+            r4 = [dr[n].unsqueeze(0) for n in ("q_raw", "k_raw", "v", "gate_pre", "beta_pre")]
+            fnp = lambda: kda.kda_chunk_bwd_prologue(*r4, -30.0, go.unsqueeze(0), want_grad_h0=False, workspace=ws)
+            per_pb, _ = time_launches(fnp, args.steps, args.warmup, stream)
+            pbms = float(np.mean(per_pb))
+            out["backward"]["prologue"] = {
+                "workload": "kda_chunk_bwd_prologue on raw projections of the same shape (as the forward's "
+                            "prologue line), floor -30",
+                "ms_per_step": pbms, "tokens_per_s": T / (pbms * 1e-3), "vs_kda_backward_ms": pbms / bms,
+                "workspace_bytes": ws.numel()}
+            del dr, r4, ws
+            ws = torch.empty(kda.kda_chunk_bwd_workspace_size(1, T, H, dk, dv, 0, kda.KDA_BF16),
+                             dtype=torch.uint8, device=dev)
         if not args.no_decoupled:
             # separate erase and write strengths: beta erases, a write strength
             # drawn like beta from its own seed writes

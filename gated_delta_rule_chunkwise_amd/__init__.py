@@ -18,6 +18,7 @@ Entry points (same names as the C ABI):
     kda_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, cu_seqlens=None, ...)
     kda_gdn_chunk_bwd(q, k, v, log_alpha_or_None, beta, grad_o, ...)
     kda_chunk_bwd_decoupled(q, k, v, log_alpha, b_erase, w_write, grad_o, ...)
+    kda_chunk_bwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, grad_o, ...)
     kda_chunk_fwd_workspace_size(...), kda_chunk_bwd_workspace_size(...),
     kda_gdn_chunk_bwd_workspace_size(...),
     kda_status_string(code), kda_abi_version()
@@ -37,7 +38,8 @@ EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error"
                     "kda_chunk_fwd_prologue", "kda_decode_step_prologue", "kda_gdn_chunk_fwd",
                     "kda_gdn_decode_step", "kda_chunk_fwd_decoupled", "kda_decode_step_decoupled",
                     "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
-                    "kda_gdn_chunk_bwd_workspace_size", "kda_gdn_chunk_bwd", "kda_chunk_bwd_decoupled")
+                    "kda_gdn_chunk_bwd_workspace_size", "kda_gdn_chunk_bwd", "kda_chunk_bwd_decoupled",
+                    "kda_chunk_bwd_prologue_workspace_size", "kda_chunk_bwd_prologue")
 
 _lib = None
 
@@ -103,6 +105,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd_decoupled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                             vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
     lib.kda_chunk_bwd_decoupled.restype = ctypes.c_int
+    lib.kda_chunk_bwd_prologue_workspace_size.argtypes = list(lib.kda_chunk_fwd_workspace_size.argtypes)
+    lib.kda_chunk_bwd_prologue_workspace_size.restype = sz
+    lib.kda_chunk_bwd_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    lib.kda_chunk_bwd_prologue.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -292,6 +299,19 @@ def kda_gdn_chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0=None, grad_hT=None, c
                       gdn=True)
 
 
+def kda_chunk_bwd_prologue_workspace_size(B, T, H, d_k, d_v, num_seqs=0, io_dtype=KDA_BF16) -> int:
+    return int(load_library().kda_chunk_bwd_prologue_workspace_size(B, T, H, d_k, d_v, num_seqs, io_dtype))
+
+
+def kda_chunk_bwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, grad_o, h0=None, grad_hT=None,
+                           cu_seqlens=None, *, want_grad_h0=True, workspace=None):
+    """Gradients of kda_chunk_fwd_prologue with respect to its raw inputs.
+    Returns (dq_raw, dk_raw, dv, dgate_pre, dbeta_pre, dh0); dh0 is None when
+    want_grad_h0 is False."""
+    return _chunk_bwd(q_raw, k_raw, v, gate_pre, beta_pre, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0,
+                      workspace, gdn=False, log_alpha_min=float(log_alpha_min))
+
+
 def kda_chunk_bwd_decoupled(q, k, v, log_alpha, b_erase, w_write, grad_o, h0=None, grad_hT=None, cu_seqlens=None,
                             *, want_grad_h0=True, workspace=None):
     """Gradients of kda_chunk_fwd_decoupled: b_erase and w_write [B, T, H] in
@@ -302,7 +322,7 @@ def kda_chunk_bwd_decoupled(q, k, v, log_alpha, b_erase, w_write, grad_o, h0=Non
 
 
 def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_grad_h0, workspace, gdn,
-               w_write=None):
+               w_write=None, log_alpha_min=None):
     import torch
     lib = load_library()
     squeeze = q.dim() == 3
@@ -352,12 +372,19 @@ def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_g
     dh0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_grad_h0 else None
     io, gt = _dtype_code(q), _dtype_code(beta)
     nseq = N if cu_seqlens is not None else 0
-    size_fn = kda_gdn_chunk_bwd_workspace_size if gdn else kda_chunk_bwd_workspace_size
+    size_fn = kda_gdn_chunk_bwd_workspace_size if gdn else (
+        kda_chunk_bwd_prologue_workspace_size if log_alpha_min is not None else kda_chunk_bwd_workspace_size)
     ws_bytes = size_fn(B, T, H, dk, dv, nseq, io)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ws_len = workspace.numel() * workspace.element_size()
-    if w_write is not None:
+    if log_alpha_min is not None:
+        name = "kda_chunk_bwd_prologue"
+        rc = lib.kda_chunk_bwd_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), log_alpha_min,
+                                        _ptr(h0), _ptr(cu_seqlens), nseq, _ptr(grad_o), _ptr(grad_hT), _ptr(dq),
+                                        _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(db), _ptr(dh0), B, T, H, dk, dv, io,
+                                        gt, _ptr(workspace), ws_len, _stream_of(q))
+    elif w_write is not None:
         name = "kda_chunk_bwd_decoupled"
         dw = torch.empty_like(w_write)
         rc = lib.kda_chunk_bwd_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(w_write),

@@ -178,6 +178,12 @@ size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
     return kda::chunk_bwd_workspace_bytes(bwd_sizes(B, T, H, d_k, d_v, num_seqs, io_dtype));
 }
 
+size_t kda_chunk_bwd_prologue_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                             int32_t num_seqs, kda_dtype_t io_dtype) {
+    if (!bwd_sizes_ok(B, T, H, d_k, d_v, num_seqs, io_dtype)) return 0;
+    return kda::pro_chunk_bwd_workspace_bytes(bwd_sizes(B, T, H, d_k, d_v, num_seqs, io_dtype));
+}
+
 size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                         int32_t num_seqs, kda_dtype_t io_dtype) {
     if (!bwd_sizes_ok(B, T, H, d_k, d_v, num_seqs, io_dtype)) return 0;
@@ -188,15 +194,17 @@ size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t
 
 namespace {
 
-// gate_mode 0: log_alpha [.., d_k] (KDA); 1: [..] per (token, head); 2: none.
+// gate_mode 0: log_alpha [.., d_k] (KDA); 1: [..] per (token, head); 2: none;
+// 3: raw projections through the input prologue (gate_pre [.., d_k]; lo its floor).
 kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const void *log_alpha, const void *beta,
                             const float *h0, const int32_t *cu_seqlens, int32_t num_seqs, const void *grad_o,
                             const float *grad_hT, void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
                             void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H, int32_t d_k,
                             int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
                             size_t workspace_bytes, void *stream, int gate_mode, bool decoupled = false,
-                            const void *w_write = nullptr, void *grad_w_write = nullptr) {
+                            const void *w_write = nullptr, void *grad_w_write = nullptr, float lo = 0.f) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (gate_mode == 3 && !valid_floor(lo)) return KDA_ERR_INVALID_ARGUMENT;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
     if (H > 65535) return KDA_ERR_UNSUPPORTED;   // heads are a grid dimension of the per-chunk kernels
@@ -219,7 +227,8 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
         const uintptr_t gsz = dsize(gate_dtype);
         if (!beta || !grad_beta || !aligned_to(beta, gsz) || !aligned_to(grad_beta, gsz))
             return KDA_ERR_INVALID_ARGUMENT;
-        if (gate_mode == 0 && (!log_alpha || !aligned16(log_alpha) || !grad_log_alpha || !aligned16(grad_log_alpha)))
+        if ((gate_mode == 0 || gate_mode == 3) &&
+            (!log_alpha || !aligned16(log_alpha) || !grad_log_alpha || !aligned16(grad_log_alpha)))
             return KDA_ERR_INVALID_ARGUMENT;
         if (gate_mode == 1 && (!grad_log_alpha || !aligned_to(log_alpha, gsz) || !aligned_to(grad_log_alpha, gsz)))
             return KDA_ERR_INVALID_ARGUMENT;
@@ -230,7 +239,9 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
         return KDA_ERR_INVALID_ARGUMENT;
     kda::BwdArgs a = bwd_sizes(B, T, H, d_k, d_v, cu_seqlens ? num_seqs : 0, io_dtype);
     a.gate_bf16 = gate_dtype == KDA_BF16;
-    const size_t need = gate_mode == 0 ? kda::chunk_bwd_workspace_bytes(a) : kda::gdn_chunk_bwd_workspace_bytes(a);
+    const size_t need = gate_mode == 0   ? kda::chunk_bwd_workspace_bytes(a)
+                        : gate_mode == 3 ? kda::pro_chunk_bwd_workspace_bytes(a)
+                                         : kda::gdn_chunk_bwd_workspace_bytes(a);
     if (workspace_bytes < need || !workspace) return KDA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
     if (!have_tokens && !grad_h0) return KDA_OK;  // nothing to compute or write
@@ -244,8 +255,9 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
     a.dw_write = decoupled ? grad_w_write : nullptr;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     g_hip_error[0] = '\0';
-    const int rc = gate_mode == 0 ? kda::launch_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error))
-                                  : kda::launch_gdn_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error));
+    const int rc = gate_mode == 0   ? kda::launch_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error))
+                   : gate_mode == 3 ? kda::launch_pro_chunk_bwd(a, lo, stream, g_hip_error, sizeof(g_hip_error))
+                                    : kda::launch_gdn_chunk_bwd(a, stream, g_hip_error, sizeof(g_hip_error));
     return rc != 0 ? KDA_ERR_HIP : KDA_OK;
 }
 
@@ -262,6 +274,18 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k, grad_v,
                           grad_log_alpha, grad_beta, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype, workspace,
                           workspace_bytes, stream, 0);
+}
+
+kda_status_t kda_chunk_bwd_prologue(const void *q_raw, const void *k_raw, const void *v, const void *gate_pre,
+                                    const void *beta_pre, float log_alpha_min, const float *h0,
+                                    const int32_t *cu_seqlens, int32_t num_seqs, const void *grad_o,
+                                    const float *grad_hT, void *grad_q_raw, void *grad_k_raw, void *grad_v,
+                                    void *grad_gate_pre, void *grad_beta_pre, float *grad_h0, int32_t B, int32_t T,
+                                    int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                                    kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_bwd_impl(q_raw, k_raw, v, gate_pre, beta_pre, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q_raw,
+                          grad_k_raw, grad_v, grad_gate_pre, grad_beta_pre, grad_h0, B, T, H, d_k, d_v, io_dtype,
+                          gate_dtype, workspace, workspace_bytes, stream, 3, false, nullptr, nullptr, log_alpha_min);
 }
 
 kda_status_t kda_chunk_bwd_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,

@@ -874,13 +874,15 @@ template <int DK> struct alignas(16) GradBS {
     float dbK[DK / 16][kB];                  // per key tile: sum_c KA (dY S'^T) of a row
 };
 
-template <int DK, int DV, typename IO, typename GT>
+// KT: the type of k, dq and dk (the io type, or fp32 with bf16 v and dO when
+// the input prologue's fp32 mapped q and k are the inputs).
+template <int DK, int DV, typename IO, typename GT, typename KT>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(
-    const IO *__restrict__ k, const IO *__restrict__ v, const GT *__restrict__ log_alpha,
+    const KT *__restrict__ k, const IO *__restrict__ v, const GT *__restrict__ log_alpha,
     const GT *__restrict__ beta, const IO *__restrict__ d_o, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int64_t N, int64_t T, int H, int64_t nch, const float *__restrict__ recs,
     const float *__restrict__ Sc, const float *__restrict__ Uc, const float *__restrict__ dSc,
-    const float *__restrict__ dUc, const float *__restrict__ sflag, IO *__restrict__ dq, IO *__restrict__ dk,
+    const float *__restrict__ dUc, const float *__restrict__ sflag, KT *__restrict__ dq, KT *__restrict__ dk,
     IO *__restrict__ dv, GT *__restrict__ dla, GT *__restrict__ dbeta, const GT *__restrict__ wr,
     GT *__restrict__ dwr) {
     using R = BRec<DK>;
@@ -907,7 +909,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     float dgn1 = 0.f;                        // thread c < DK: sum_j dS_next[c,j] S'[c,j]
     {   // k and log alpha staged through the (still free) loop area; T from the record
         const size_t base = ((size_t)t0 * H + h) * DK, pitch = (size_t)H * DK;
-        Stage<kB, DK, 512, IO> sk;
+        Stage<kB, DK, 512, KT> sk;
         Stage<kB, DK, 512, GT> sl;
         Stage<kB, kB, 512, float> st;
         sk.load(k + base, pitch, nv, tid);
@@ -1167,8 +1169,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 const float ea = __builtin_amdgcn_exp2f(g), ei = __builtin_amdgcn_exp2f(-g);
                 const size_t o = ((t0 + r) * H + h) * DK + c;
                 const float ki = sm.r3.pt.KI[r][c];
-                dq[o] = from_f32<IO>(bad ? qnan : aQ[s][e] * ea);
-                dk[o] = from_f32<IO>(bad ? qnan : aK[s][e] * ea + aI[s][e] * ei);
+                dq[o] = from_f32<KT>(bad ? qnan : aQ[s][e] * ea);
+                dk[o] = from_f32<KT>(bad ? qnan : aK[s][e] * ea + aI[s][e] * ei);
                 dG = aQ[s][e] * sm.r3.pt.QA[r][c] + aK[s][e] * sm.KA[r][c] - aI[s][e] * ki;
                 kb = aB[s][e] * ki;
             }
@@ -1221,7 +1223,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     }
 }
 
-template <int DK, int DV, typename IO, typename GT>
+template <int DK, int DV, typename IO, typename GT, typename KT = IO>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const BwdLayout L = bwd_layout(a);
     uint8_t *ws = static_cast<uint8_t *>(a.workspace);
@@ -1232,7 +1234,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     float *dSc = reinterpret_cast<float *>(ws + L.dsc);
     float *dUc = reinterpret_cast<float *>(ws + L.duc);
     float *sflag = reinterpret_cast<float *>(ws + L.sflag);
-    const IO *q = static_cast<const IO *>(a.q), *k = static_cast<const IO *>(a.k), *v = static_cast<const IO *>(a.v);
+    const KT *q = static_cast<const KT *>(a.q), *k = static_cast<const KT *>(a.k);
+    const IO *v = static_cast<const IO *>(a.v);
     const GT *la = static_cast<const GT *>(a.log_alpha), *be = static_cast<const GT *>(a.beta);
     const GT *wr = static_cast<const GT *>(a.w_write);     // separate write strengths, or NULL
     const IO *dO = static_cast<const IO *>(a.d_o);
@@ -1240,7 +1243,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     if (a.varlen)
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
     if (L.nch > 0 && a.total_tokens > 0)
-        hipLaunchKernelGGL((bwd_prep_kernel<DK, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st, q, k,
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, KT, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st, q, k,
                            la, be, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs);
     const int64_t grid = chain_grid(a.num_seqs * a.H, DV / kSBV);   // per pass (a multiple of 8)
     if (grid > 0) {
@@ -1251,9 +1254,9 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
                            Sc, Uc, sflag, dSc, dUc, a.dh0, fb);
     }
     if (L.nch > 0 && a.total_tokens > 0)
-        hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st, k,
-                           v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, dSc, dUc,
-                           sflag, static_cast<IO *>(a.dq), static_cast<IO *>(a.dk), static_cast<IO *>(a.dv),
+        hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT, KT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st,
+                           k, v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, dSc,
+                           dUc, sflag, static_cast<KT *>(a.dq), static_cast<KT *>(a.dk), static_cast<IO *>(a.dv),
                            static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta), wr,
                            static_cast<GT *>(a.dw_write));
     return hipGetLastError();
@@ -1261,6 +1264,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
 
 template <int DK, int DV>
 hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t st) {
+    // the input prologue's pass: fp32 mapped q, k and gates with bf16 v and dO
+    if (a.qk_f32 && a.io_bf16) return launch_bwd_t<DK, DV, bf16_t, float, float>(a, st);
     if (a.io_bf16)
         return a.gate_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t>(a, st) : launch_bwd_t<DK, DV, bf16_t, float>(a, st);
     return a.gate_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a, st) : launch_bwd_t<DK, DV, float, float>(a, st);
@@ -1312,6 +1317,131 @@ __global__ __launch_bounds__(256) void gdn_finish_kernel(const float *__restrict
     }
 }
 
+// ----------------------------------------------------------------------------
+// Raw projections (the input prologue's entry point): the maps are applied in a
+// pass of their own, into fp32 buffers; the backward runs on the mapped inputs;
+// a last pass takes the chain rule back through the maps.  One wave per
+// (token, head) row, DK / 64 channels per lane.
+//   map:   q_hat = q / max(||q||, eps) (k likewise), log alpha =
+//          max(-softplus(a), lo), beta = sigmoid(b); the row's 1 / max(||.||,
+//          eps) kept, negated when ||.|| <= eps (then x_hat = x / eps);
+//   chain: dq = (dq_hat - q_hat (q_hat . dq_hat)) / ||q||, or dq_hat / eps;
+//          da = -sigmoid(a) dlog_alpha where the floor does not bind, else 0;
+//          db = beta (1 - beta) dbeta.
+template <int DK, typename IO, typename GT>
+__global__ __launch_bounds__(256) void pro_map_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
+                                                      const GT *__restrict__ a, const GT *__restrict__ b, int64_t rows,
+                                                      float lo, float *__restrict__ qh, float *__restrict__ kh,
+                                                      float *__restrict__ la, float *__restrict__ be,
+                                                      float *__restrict__ inq, float *__restrict__ ink) {
+    constexpr int CPL = DK / 64;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;                 // the whole wave: one row per wave
+    float qv[CPL], kv[CPL], sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        const int64_t o = row * DK + lane * CPL + cc;
+        qv[cc] = to_f32(q[o]);
+        kv[cc] = to_f32(k[o]);
+        sq += qv[cc] * qv[cc];
+        sk += kv[cc] * kv[cc];
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    const float iq = pro_inv_norm(sq), ik = pro_inv_norm(sk);
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        const int64_t o = row * DK + lane * CPL + cc;
+        qh[o] = qv[cc] * iq;
+        kh[o] = kv[cc] * ik;
+        la[o] = pro_log_alpha(to_f32(a[o]), lo);
+    }
+    if (lane == 0) {
+        const float e2 = kPrologueEps * kPrologueEps;
+        be[row] = pro_beta(to_f32(b[row]));
+        inq[row] = sq > e2 ? iq : -iq;
+        ink[row] = sk > e2 ? ik : -ik;
+    }
+}
+
+template <int DK, typename IO, typename GT>
+__global__ __launch_bounds__(256) void pro_chain_kernel(
+    const float *__restrict__ qh, const float *__restrict__ kh, const float *__restrict__ inq,
+    const float *__restrict__ ink, const GT *__restrict__ a, const float *__restrict__ be, float lo,
+    const float *__restrict__ dqh, const float *__restrict__ dkh, const float *__restrict__ dla,
+    const float *__restrict__ dbe, int64_t rows, IO *__restrict__ dq, IO *__restrict__ dk, GT *__restrict__ da,
+    GT *__restrict__ db) {
+    constexpr int CPL = DK / 64;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    float pq = 0.f, pk = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        const int64_t o = row * DK + lane * CPL + cc;
+        pq += qh[o] * dqh[o];
+        pk += kh[o] * dkh[o];
+    }
+    pq = wave_sum(pq);
+    pk = wave_sum(pk);
+    const float iq = inq[row], ik = ink[row];   // negative: the eps branch
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+        const int64_t o = row * DK + lane * CPL + cc;
+        const float gq = iq > 0.f ? (dqh[o] - qh[o] * pq) * iq : dqh[o] * -iq;
+        const float gk = ik > 0.f ? (dkh[o] - kh[o] * pk) * ik : dkh[o] * -ik;
+        dq[o] = from_f32<IO>(gq);
+        dk[o] = from_f32<IO>(gk);
+        const float x = to_f32(a[o]);
+        const float sp = fmaxf(x, 0.f) + pro_log1p_unit(__expf(-fabsf(x)));
+        da[o] = from_f32<GT>(-sp > lo ? -pro_beta(x) * dla[o] : 0.f);
+    }
+    if (lane == 0) db[row] = from_f32<GT>(be[row] * (1.f - be[row]) * dbe[row]);
+}
+
+// Offsets of the prologue pass's fp32 buffers after the backward's own workspace.
+struct ProLayout {
+    size_t qh, kh, la, dqh, dkh, dla, be, inq, ink, dbe, total;
+};
+ProLayout pro_layout(const BwdArgs &a) {
+    const size_t rows = (size_t)a.total_tokens * a.H;
+    const size_t big = (rows * a.d_k * 4 + 255) / 256 * 256, small = (rows * 4 + 255) / 256 * 256;
+    ProLayout P;
+    P.qh = 0; P.kh = big; P.la = 2 * big; P.dqh = 3 * big; P.dkh = 4 * big; P.dla = 5 * big;
+    P.be = 6 * big; P.inq = P.be + small; P.ink = P.inq + small; P.dbe = P.ink + small;
+    P.total = P.dbe + small;
+    return P;
+}
+
+template <int DK, typename IO, typename GT>
+hipError_t launch_pro_maps(const BwdArgs &a, float lo, uint8_t *x, const ProLayout &P, int64_t rows, bool chain,
+                           hipStream_t st) {
+    const int64_t nblk = (rows + 3) / 4;
+    auto at = [&](size_t off) { return reinterpret_cast<float *>(x + off); };
+    if (!chain)
+        hipLaunchKernelGGL((pro_map_kernel<DK, IO, GT>), dim3((unsigned)nblk), dim3(256), 0, st,
+                           static_cast<const IO *>(a.q), static_cast<const IO *>(a.k),
+                           static_cast<const GT *>(a.log_alpha), static_cast<const GT *>(a.beta), rows, lo, at(P.qh),
+                           at(P.kh), at(P.la), at(P.be), at(P.inq), at(P.ink));
+    else
+        hipLaunchKernelGGL((pro_chain_kernel<DK, IO, GT>), dim3((unsigned)nblk), dim3(256), 0, st, at(P.qh), at(P.kh),
+                           at(P.inq), at(P.ink), static_cast<const GT *>(a.log_alpha), at(P.be), lo, at(P.dqh),
+                           at(P.dkh), at(P.dla), at(P.dbe), rows, static_cast<IO *>(a.dq), static_cast<IO *>(a.dk),
+                           static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta));
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_pro_maps_t(const BwdArgs &a, float lo, uint8_t *x, const ProLayout &P, int64_t rows, bool chain,
+                             hipStream_t st) {
+    if (a.io_bf16)
+        return a.gate_bf16 ? launch_pro_maps<DK, bf16_t, bf16_t>(a, lo, x, P, rows, chain, st)
+                           : launch_pro_maps<DK, bf16_t, float>(a, lo, x, P, rows, chain, st);
+    return a.gate_bf16 ? launch_pro_maps<DK, float, bf16_t>(a, lo, x, P, rows, chain, st)
+                       : launch_pro_maps<DK, float, float>(a, lo, x, P, rows, chain, st);
+}
+
 size_t gdn_extra_bytes(const BwdArgs &a) {
     const size_t rows = (size_t)a.total_tokens * a.H;
     return (2 * rows * a.d_k * 4 + 255) / 256 * 256 + 2 * ((rows * 4 + 255) / 256 * 256);
@@ -1322,6 +1452,52 @@ size_t gdn_extra_bytes(const BwdArgs &a) {
 size_t chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total; }
 
 size_t gdn_chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total + gdn_extra_bytes(a); }
+
+size_t pro_chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total + pro_layout(a).total; }
+
+int launch_pro_chunk_bwd(const BwdArgs &a, float lo, void *stream, char *err, size_t err_len) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t base = bwd_layout(a).total;
+    const ProLayout P = pro_layout(a);
+    if (a.workspace_bytes < base + P.total) {
+        snprintf(err, err_len, "workspace too small");
+        return -1;
+    }
+    const int64_t rows = a.total_tokens * a.H;
+    if ((rows + 3) / 4 > 0x7fffffffLL) {
+        snprintf(err, err_len, "chunk_bwd_prologue grid too large");
+        return -1;
+    }
+    uint8_t *x = static_cast<uint8_t *>(a.workspace) + base;
+    auto fail = [&](hipError_t e) {
+        snprintf(err, err_len, "%s", hipGetErrorString(e));
+        return -1;
+    };
+    if (rows > 0) {
+        const hipError_t e = a.d_k == 128 ? launch_pro_maps_t<128>(a, lo, x, P, rows, false, st)
+                                          : launch_pro_maps_t<64>(a, lo, x, P, rows, false, st);
+        if (e != hipSuccess) return fail(e);
+    }
+    BwdArgs b = a;
+    b.q = x + P.qh;
+    b.k = x + P.kh;
+    b.log_alpha = x + P.la;
+    b.beta = x + P.be;
+    b.gate_bf16 = 0;
+    b.qk_f32 = 1;
+    b.dq = x + P.dqh;
+    b.dk = x + P.dkh;
+    b.dlog_alpha = x + P.dla;
+    b.dbeta = x + P.dbe;
+    b.workspace_bytes = base;
+    if (launch_chunk_bwd(b, stream, err, err_len) != 0) return -1;
+    if (rows > 0) {
+        const hipError_t e = a.d_k == 128 ? launch_pro_maps_t<128>(a, lo, x, P, rows, true, st)
+                                          : launch_pro_maps_t<64>(a, lo, x, P, rows, true, st);
+        if (e != hipSuccess) return fail(e);
+    }
+    return 0;
+}
 
 int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);

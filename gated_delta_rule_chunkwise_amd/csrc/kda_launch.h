@@ -61,11 +61,16 @@ struct BwdArgs {
     int64_t num_seqs, seq_len, total_tokens;
     int32_t H, d_k, d_v;
     int32_t io_bf16, gate_bf16, varlen;
+    int32_t qk_f32;             // q and k (and dq, dk) fp32 with bf16 v and dO (prologue pass)
     void *workspace;
     size_t workspace_bytes;
 };
 
 size_t chunk_bwd_workspace_bytes(const BwdArgs &a);
+// Raw projections: q, k, log_alpha, beta of a are the raw inputs (and dq, dk,
+// dlog_alpha, dbeta their gradients); lo is the gate floor.
+size_t pro_chunk_bwd_workspace_bytes(const BwdArgs &a);
+int launch_pro_chunk_bwd(const BwdArgs &a, float lo, void *stream, char *err, size_t err_len);
 int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len);
 // Scalar-gate form: log_alpha [.., H] (or nullptr: no decay), dlog_alpha likewise.
 size_t gdn_chunk_bwd_workspace_bytes(const BwdArgs &a);

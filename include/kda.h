@@ -305,6 +305,40 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            void *stream);
 
 /*
+ * Bytes of device workspace kda_chunk_bwd_prologue needs (arguments as for
+ * kda_chunk_bwd_workspace_size; 0 for invalid arguments): that of
+ * kda_chunk_bwd plus six fp32 [B*T*H, d_k] buffers and four fp32 [B*T*H]
+ * buffers (about 3 KiB more per token-head at d_k = 128).
+ */
+size_t kda_chunk_bwd_prologue_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                             int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+
+/*
+ * kda_chunk_bwd_prologue -- gradients of kda_chunk_fwd_prologue with respect
+ * to its raw inputs.  The maps of the input prologue are applied in a pass of
+ * their own into fp32 workspace buffers (q/max(||q||, eps), k likewise,
+ * max(-softplus(gate_pre), log_alpha_min), sigmoid(beta_pre)); the gradients
+ * of kda_chunk_bwd are taken at those fp32 values; a last pass applies the
+ * chain rule back through the maps:
+ *     grad_q_raw = (dq_hat - q_hat (q_hat . dq_hat)) / ||q||   (dq_hat / eps when ||q|| <= eps),
+ *     grad_gate_pre = -sigmoid(gate_pre) dlog_alpha where the floor does not bind, else 0,
+ *     grad_beta_pre = beta (1 - beta) dbeta.
+ * Arguments, numerics, range and errors as for kda_chunk_bwd, with the raw
+ * inputs and log_alpha_min as for kda_chunk_fwd_prologue, the gradients of the
+ * raw inputs in place of those of q, k, log_alpha, beta (same layouts and
+ * dtypes), and a workspace of kda_chunk_bwd_prologue_workspace_size() bytes.
+ */
+kda_status_t kda_chunk_bwd_prologue(const void *q_raw, const void *k_raw, const void *v,
+                                    const void *gate_pre, const void *beta_pre, float log_alpha_min,
+                                    const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
+                                    const void *grad_o, const float *grad_hT, void *grad_q_raw,
+                                    void *grad_k_raw, void *grad_v, void *grad_gate_pre,
+                                    void *grad_beta_pre, float *grad_h0, int32_t B, int32_t T,
+                                    int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
+                                    kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/*
  * kda_chunk_bwd_decoupled -- gradients of kda_chunk_fwd_decoupled (separate
  * erase strength b and write strength w per token and head):
  *

@@ -376,3 +376,34 @@ def test_decoupled_bwd_empty_without_state_is_noop(kda):
     lib = kda.load_library()
     assert bwd_dec(lib, T=0, q=None, k=None, v=None, la=None, beta=None, wr=None, dwr=None, go=None, dq=None,
                    dk=None, dv=None, dla=None, db=None, dh0=None) == 0
+
+
+def bwd_pro(lib, lo=-20.0, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, go=P, ghT=None, dq=P, dk=P, dv=P,
+             dla=P, db=P, dh0=P, B=1, T=128, H=2, dk_=128, dv_=128, io=1, gt=1, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_chunk_bwd_prologue(a["q"], a["k"], a["v"], a["la"], a["beta"], lo, a["h0"], a["cu"], a["N"],
+                                      a["go"], a["ghT"], a["dq"], a["dk"], a["dv"], a["dla"], a["db"], a["dh0"],
+                                      a["B"], a["T"], a["H"], a["dk_"], a["dv_"], a["io"], a["gt"], a["ws"],
+                                      a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lo=float("nan")), 1), (dict(lo=float("-inf")), 1), (dict(lo=0.5), 1),
+    (dict(dk_=96), 2), (dict(H=65536, T=1), 2), (dict(q=None), 1), (dict(la=P + 4), 1), (dict(dla=P + 8), 1),
+    (dict(beta=P + 1), 1), (dict(cu=P, N=2, B=2), 1), (dict(ws=None), 3),
+])
+def test_prologue_bwd_rejects(kda, kw, code):
+    lib = kda.load_library()
+    assert bwd_pro(lib, **kw) == code
+
+
+def test_prologue_bwd_workspace_size(kda):
+    # the backward's workspace plus six fp32 [rows, d_k] and four fp32 [rows] buffers
+    rows = 1000 * 2
+    base = kda.kda_chunk_bwd_workspace_size(1, 1000, 2, 128, 64, 0, kda.KDA_BF16)
+    w = kda.kda_chunk_bwd_prologue_workspace_size(1, 1000, 2, 128, 64, 0, kda.KDA_BF16)
+    assert base + 6 * rows * 128 * 4 + 4 * rows * 4 <= w <= base + 6 * rows * 128 * 4 + 4 * rows * 4 + 2560
+    assert kda.kda_chunk_bwd_prologue_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
+    need = kda.kda_chunk_bwd_prologue_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    assert bwd_pro(kda.load_library(), wsb=need - 1) == 3

@@ -346,3 +346,69 @@ def test_decoupled_bwd_c1_shape(kda):
     w = I.draw_strength(d["beta"].shape, 4400, d["beta"].dtype)
     go, ghT = I.make_upstream_grads(d, 4401)
     dec_check(kda, d, w, "bf16", go, ghT, what="decoupled bwd c1")
+
+
+# ------------------------------------------------------------------ input prologue
+# kda_chunk_bwd_prologue: gradients with respect to the raw projections,
+# against the oracle's backward of the forward on raw inputs (oracle.bwd_prologue).
+NAMES_PRO = ("dq_raw", "dk_raw", "dv", "dgate_pre", "dbeta_pre", "dh0")
+
+
+def pro_bwd_check(kda, d, io, lo, go, ghT, eps_rows=(), heads=None, what=""):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    out = kda.kda_chunk_bwd_prologue(dev["q_raw"], dev["k_raw"], dev["v"], dev["gate_pre"], dev["beta_pre"], lo,
+                                     go.to(DEV), h0=dev["h0"], grad_hT=None if ghT is None else ghT.to(DEV),
+                                     cu_seqlens=cu)
+    torch.cuda.synchronize()
+    out = [x.cpu() for x in out]
+    plain = dict(q=d["q_raw"], k=d["k_raw"], v=d["v"], log_alpha=d["gate_pre"], beta=d["beta_pre"], h0=d["h0"],
+                 lengths=d["lengths"], cu_seqlens=d["cu_seqlens"])
+    ref = to_oracle(plain, None, heads)
+    hs = slice(None) if heads is None else list(heads)
+    rows = torch.from_numpy(ref["rows"])
+    res = oracle.bwd_prologue(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], lo,
+                              f64(go[rows][:, hs]), h0=ref["h0"],
+                              d_hT=None if ghT is None else f64(ghT[:, hs]), cu_seqlens=ref["cu_seqlens"])
+    T = rows.numel()
+    keep = np.ones(T, bool)
+    for t, _ in eps_rows:
+        keep[t] = False
+    errs = {}
+    for name, x, r in zip(NAMES_PRO, out, res):
+        x = f64(x[:, hs] if name == "dh0" else x[rows][:, hs])
+        tol = F32_REL if (io == "f32" or name == "dh0") else BF16_REL
+        if name in ("dq_raw", "dk_raw"):
+            # rows in the eps branch are (dq_hat / eps): compare them on their own
+            for t, hh in eps_rows:
+                e = errors(x[t, hh], r[t, hh])
+                assert e["rel_max"] <= tol, "%s %s eps row %d: %s" % (what, name, t, e)
+            x, r = x[keep], r[keep]
+        elif name != "dh0":
+            x, r = x[keep], r[keep]
+        e = errors(x, r)
+        assert e["rel_max"] <= tol and e["rel_fro"] <= tol, "%s %s: %s (tol %g)" % (what, name, e, tol)
+        errs[name] = "%.1e/%.1e" % (e["rel_max"], e["rel_fro"])
+    log(what, errs)
+
+
+@pytest.mark.parametrize("io,dk,dv", [("bf16", 128, 128), ("bf16", 64, 128), ("f32", 128, 64), ("f32", 64, 64)])
+def test_prologue_bwd_ragged(kda, io, dk, dv):
+    """Ragged packed sequences with h0 and grad_hT, gate pre-activations N(0, 2^2)
+    with the floor at -3 (about 7% of gates on it), a zero query row and a zero
+    key row (the eps branch)."""
+    cfg = I.ChunkConfig("pro-bwd", io, io, H=3, dk=dk, dv=dv, h0=True, seed=4500 + dk + dv)
+    d = I.make_chunk_raw_inputs(cfg, lengths=[300, 64, 130, 1, 200, 0], gate_scale=2.0)
+    q, k = d["q_raw"].clone(), d["k_raw"].clone()
+    q[5, 0] = 0.0
+    k[7, 1] = 0.0
+    d["q_raw"], d["k_raw"] = q, k
+    go, ghT = I.make_upstream_grads(dict(d, q=d["q_raw"]), 4501)
+    pro_bwd_check(kda, d, io, -3.0, go, ghT, eps_rows=[(5, 0), (7, 1)],
+                  what="prologue bwd %s %dx%d" % (io, dk, dv))
+
+
+def test_prologue_bwd_c1_shape(kda):
+    d = I.make_chunk_raw_inputs(I.C1, gate_scale=2.0)
+    go, ghT = I.make_upstream_grads(dict(d, q=d["q_raw"]), 4600)
+    pro_bwd_check(kda, d, "bf16", -3.0, go, ghT, what="prologue bwd c1")
