@@ -10,8 +10,8 @@ on raw projections through the fused input prologue (kda_chunk_fwd_prologue)
 under "prologue"; the same shape with one decay per token and head (Gated
 DeltaNet) and with none (DeltaNet), through kda_gdn_chunk_fwd, under "gdn"; and
 with separate erase and write strengths (kda_chunk_fwd_decoupled) under
-"decoupled"; the gradients of the same prefill (kda_chunk_bwd) under
-"backward"; kda_chunk_fwd on the short (H=16, T=4096) and packed variable-length
+"decoupled"; the gradients of the same prefill (kda_chunk_bwd, and the
+scalar-gate, separate-strength and raw-projection backwards) under "backward"; kda_chunk_fwd on the short (H=16, T=4096) and packed variable-length
 (32 sequences of 512-8192 tokens, h0 given) workloads under "other_workloads".
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -328,8 +328,8 @@ def main():
     # ---------------- the other prefill workloads: short sequence and packed batch
     if not args.no_other:
         other = {}
-        for key, cfg in (("c1", I.C1), ("c2", I.C2)):
-            dd = I.make_chunk_inputs(cfg, device=dev)
+        for key, ocfg in (("c1", I.C1), ("c2", I.C2)):
+            dd = I.make_chunk_inputs(ocfg, device=dev)
             Tt, Hh = dd["q"].shape[0], dd["q"].shape[1]
             nseq = len(dd["lengths"])
             cu = dd["cu_seqlens"].to(dev) if nseq > 1 else None
@@ -340,7 +340,7 @@ def main():
             per_o, _ = time_launches(fno, args.steps, args.warmup, stream)
             oms = float(np.mean(per_o))
             ob = chunk_alg_bytes(Tt * Hh, nseq * Hh * (2 if dd["h0"] is not None else 1), dk, dv)
-            other[key] = {"workload": "kda_chunk_fwd, " + cfg.name + (" (%d sequences, %d tokens)" % (nseq, Tt)),
+            other[key] = {"workload": "kda_chunk_fwd, " + ocfg.name + (" (%d sequences, %d tokens)" % (nseq, Tt)),
                           "ms_per_step": oms, "tokens_per_s": Tt / (oms * 1e-3),
                           "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob}
             del dd, o2, h_T, cu
