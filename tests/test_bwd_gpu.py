@@ -412,3 +412,20 @@ def test_prologue_bwd_c1_shape(kda):
     d = I.make_chunk_raw_inputs(I.C1, gate_scale=2.0)
     go, ghT = I.make_upstream_grads(dict(d, q=d["q_raw"]), 4600)
     pro_bwd_check(kda, d, "bf16", -3.0, go, ghT, what="prologue bwd c1")
+
+
+def test_decoupled_bwd_c3_sampled_heads(kda):
+    """Full long-context size with a write strength drawn like beta (as the
+    benchmark times it); the oracle checks two whole heads."""
+    d = I.make_chunk_inputs(I.C3)
+    w = I.draw_strength(d["beta"].shape, 5200, d["beta"].dtype)
+    go, _ = I.make_upstream_grads(d, 3400, with_state=False)
+    dec_check(kda, d, w, "bf16", go, None, heads=[0, 31], what="decoupled bwd c3 heads 0,31")
+
+
+def test_prologue_bwd_c3_sampled_heads(kda):
+    """Full long-context size on raw projections, floor -30 (as the benchmark
+    times it); the oracle checks two whole heads."""
+    d = I.make_chunk_raw_inputs(I.C3, gate="uniform")
+    go, _ = I.make_upstream_grads(dict(d, q=d["q_raw"]), 3400, with_state=False)
+    pro_bwd_check(kda, d, "bf16", -30.0, go, None, heads=[0, 31], what="prologue bwd c3 heads 0,31")
