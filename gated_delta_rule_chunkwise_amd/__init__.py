@@ -19,6 +19,8 @@ Entry points (same names as the C ABI):
     kda_gdn_chunk_bwd(q, k, v, log_alpha_or_None, beta, grad_o, ...)
     kda_chunk_bwd_decoupled(q, k, v, log_alpha, b_erase, w_write, grad_o, ...)
     kda_chunk_bwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, grad_o, ...)
+    chunk_kda(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None)        (autograd: fwd + bwd)
+    chunk_gated_delta_rule(q, k, v, log_alpha_or_None, beta, ...)       (autograd, scalar gate)
     kda_chunk_fwd_workspace_size(...), kda_chunk_bwd_workspace_size(...),
     kda_gdn_chunk_bwd_workspace_size(...),
     kda_status_string(code), kda_abi_version()
@@ -484,3 +486,54 @@ gdn_chunk_fwd = kda_gdn_chunk_fwd
 gdn_decode_step = kda_gdn_decode_step
 chunk_fwd_decoupled = kda_chunk_fwd_decoupled
 decode_step_decoupled = kda_decode_step_decoupled
+
+
+# ---------------------------------------------------------------- autograd
+# Training use from PyTorch: the forward is kda_chunk_fwd (or kda_gdn_chunk_fwd)
+# and the backward kda_chunk_bwd (or kda_gdn_chunk_bwd); these wrappers only
+# connect the two to torch.autograd.
+def _autograd_function():
+    import torch
+
+    class _ChunkKDA(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, log_alpha, beta, h0, cu_seqlens, gdn):
+            fwd = kda_gdn_chunk_fwd if gdn else kda_chunk_fwd
+            o, h_T = fwd(q, k, v, log_alpha, beta, h0=h0, cu_seqlens=cu_seqlens)
+            ctx.save_for_backward(q, k, v, log_alpha, beta, h0, cu_seqlens)
+            ctx.gdn = gdn
+            return o, h_T
+
+        @staticmethod
+        def backward(ctx, grad_o, grad_hT):
+            q, k, v, log_alpha, beta, h0, cu_seqlens = ctx.saved_tensors
+            if grad_o is None:
+                grad_o = torch.zeros(v.shape, dtype=v.dtype, device=v.device)
+            bwd = kda_gdn_chunk_bwd if ctx.gdn else kda_chunk_bwd
+            dq, dk, dv, dla, db, dh0 = bwd(q, k, v, log_alpha, beta, grad_o.contiguous(), h0=h0,
+                                           grad_hT=None if grad_hT is None else grad_hT.contiguous(),
+                                           cu_seqlens=cu_seqlens, want_grad_h0=h0 is not None and ctx.needs_input_grad[5])
+            return dq, dk, dv, dla, db, dh0, None, None
+
+    return _ChunkKDA
+
+
+_CHUNK_KDA = None
+
+
+def chunk_kda(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None):
+    """KDA prefill with autograd: returns (o, h_T) as kda_chunk_fwd does, and
+    gradients flow to q, k, v, log_alpha, beta and h0 through kda_chunk_bwd."""
+    global _CHUNK_KDA
+    if _CHUNK_KDA is None:
+        _CHUNK_KDA = _autograd_function()
+    return _CHUNK_KDA.apply(q, k, v, log_alpha, beta, h0, cu_seqlens, False)
+
+
+def chunk_gated_delta_rule(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None):
+    """Gated DeltaNet (log_alpha [.., H]) or DeltaNet (log_alpha None) prefill
+    with autograd, through kda_gdn_chunk_fwd and kda_gdn_chunk_bwd."""
+    global _CHUNK_KDA
+    if _CHUNK_KDA is None:
+        _CHUNK_KDA = _autograd_function()
+    return _CHUNK_KDA.apply(q, k, v, log_alpha, beta, h0, cu_seqlens, True)

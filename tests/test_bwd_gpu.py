@@ -429,3 +429,24 @@ def test_prologue_bwd_c3_sampled_heads(kda):
     d = I.make_chunk_raw_inputs(I.C3, gate="uniform")
     go, _ = I.make_upstream_grads(dict(d, q=d["q_raw"]), 3400, with_state=False)
     pro_bwd_check(kda, d, "bf16", -30.0, go, None, heads=[0, 31], what="prologue bwd c3 heads 0,31")
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_autograd_wrapper_is_the_direct_calls(kda, gdn):
+    """chunk_kda / chunk_gated_delta_rule: loss.backward() gives exactly the
+    gradients of the direct backward call with grad_o, grad_hT = dL/do, dL/dh_T."""
+    cfg = I.ChunkConfig("autograd", "bf16", "f32", H=2, dk=128, dv=64, h0=True, seed=4700)
+    d = I.make_chunk_inputs(cfg, lengths=[150, 90])
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    la = g["log_alpha"][:, :, 0].contiguous() if gdn else g["log_alpha"]
+    leaves = [x.detach().clone().requires_grad_(True) for x in (g["q"], g["k"], g["v"], la, g["beta"], g["h0"])]
+    go, ghT = I.make_upstream_grads(d, 4701)
+    go, ghT = go.to(DEV), ghT.to(DEV)
+    fn = kda.chunk_gated_delta_rule if gdn else kda.chunk_kda
+    o, hT = fn(*leaves, cu_seqlens=g["cu_seqlens"])
+    ((o.float() * go.float()).sum() + (hT * ghT).sum()).backward()
+    bwd = kda.kda_gdn_chunk_bwd if gdn else kda.kda_chunk_bwd
+    ref = bwd(g["q"], g["k"], g["v"], la, g["beta"], go, h0=g["h0"], grad_hT=ghT, cu_seqlens=g["cu_seqlens"])
+    torch.cuda.synchronize()
+    for leaf, r, name in zip(leaves, ref, NAMES):
+        assert leaf.grad is not None and torch.equal(leaf.grad, r), name
