@@ -523,3 +523,35 @@ def test_long_sequence_segments(kda):
     o2, h2 = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=hh, h_T=hh)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(h1, h2) and h2.data_ptr() == hh.data_ptr()
+
+
+# ------------------------------------------------------------------ invariants at full size
+# Properties of the recurrence that hold at any size, checked on the GPU at the
+# long-context shape the benchmark times (no oracle needed): the value columns
+# of S evolve independently, and o, h_T are homogeneous in q and linear in
+# (v, h0) jointly.  Each value column's arithmetic is the same whichever block
+# it lands in, and scaling by 2 is exact, so both hold bitwise.
+def test_c3_value_column_permutation(kda):
+    d = I.make_chunk_inputs(I.C3)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    H, dv = g["v"].shape[1], g["v"].shape[2]
+    h0 = 0.1 * torch.randn((1, H, 128, dv), generator=torch.Generator().manual_seed(4800)).to(DEV)
+    perm = torch.randperm(dv, generator=torch.Generator().manual_seed(4801)).to(DEV)
+    o, hT = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=h0)
+    op, hp = kda.kda_chunk_fwd(g["q"], g["k"], g["v"][..., perm].contiguous(), g["log_alpha"], g["beta"],
+                               h0=h0[..., perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(op, o[..., perm]) and torch.equal(hp, hT[..., perm])
+
+
+def test_c3_homogeneity_and_linearity(kda):
+    d = I.make_chunk_inputs(I.C3)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    H, dv = g["v"].shape[1], g["v"].shape[2]
+    h0 = 0.1 * torch.randn((1, H, 128, dv), generator=torch.Generator().manual_seed(4900)).to(DEV)
+    o, hT = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=h0)
+    oq, hq = kda.kda_chunk_fwd(2 * g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=h0)
+    ov, hv = kda.kda_chunk_fwd(g["q"], g["k"], 2 * g["v"], g["log_alpha"], g["beta"], h0=2 * h0)
+    torch.cuda.synchronize()
+    assert torch.equal(oq, 2 * o) and torch.equal(hq, hT)        # o is linear in q; h_T does not see q
+    assert torch.equal(ov, 2 * o) and torch.equal(hv, 2 * hT)
