@@ -450,3 +450,19 @@ def test_autograd_wrapper_is_the_direct_calls(kda, gdn):
     torch.cuda.synchronize()
     for leaf, r, name in zip(leaves, ref, NAMES):
         assert leaf.grad is not None and torch.equal(leaf.grad, r), name
+
+
+def test_bwd_c3_linear_in_upstream_gradients(kda):
+    """At the long-context size: every gradient is linear in (grad_o, grad_hT)
+    for fixed inputs, and scaling by 2 is exact, so doubling both doubles every
+    output bitwise."""
+    d = I.make_chunk_inputs(I.C3)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    go, _ = I.make_upstream_grads(d, 3400, with_state=False)
+    go = go.to(DEV)
+    ghT = 0.1 * torch.randn((1, 32, 128, 128), generator=torch.Generator().manual_seed(5000)).to(DEV)
+    a = kda.kda_chunk_bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], go, grad_hT=ghT)
+    b = kda.kda_chunk_bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], 2 * go, grad_hT=2 * ghT)
+    torch.cuda.synchronize()
+    for name, x, y in zip(NAMES, a, b):
+        assert torch.equal(y, 2 * x), name
