@@ -407,3 +407,20 @@ def test_prologue_bwd_workspace_size(kda):
     assert kda.kda_chunk_bwd_prologue_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
     need = kda.kda_chunk_bwd_prologue_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
     assert bwd_pro(kda.load_library(), wsb=need - 1) == 3
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])
+def test_header_is_plain_c(tmp_path, lang, std):
+    """include/kda.h compiles as C99 and as C++ with warnings on: callers need
+    no torch, HIP or C++ types to use the ABI."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / "use.c"
+    src.write_text('#include "kda.h"\nint main(void) { return (int)kda_abi_version(); }\n')
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", os.path.join(root, "include"),
+                        "-x", lang, str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
