@@ -343,6 +343,17 @@ def main():
             other[key] = {"workload": "kda_chunk_fwd, " + ocfg.name + (" (%d sequences, %d tokens)" % (nseq, Tt)),
                           "ms_per_step": oms, "tokens_per_s": Tt / (oms * 1e-3),
                           "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob}
+            if key == "c2" and not args.no_backward:
+                # the packed batch's gradients (grad_o ~ N(0,1), grad_hT ~ N(0, 0.1^2))
+                go2, ghT2 = I.make_upstream_grads(dd, 3450, device=dev)
+                fnb2 = lambda: kda.kda_chunk_bwd(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], go2,
+                                                 h0=dd["h0"], grad_hT=ghT2, cu_seqlens=cu)
+                per_b2, _ = time_launches(fnb2, args.steps, args.warmup, stream)
+                b2 = float(np.mean(per_b2))
+                other[key]["backward"] = {"ms_per_step": b2, "tokens_per_s": Tt / (b2 * 1e-3),
+                                          "alg_flops_frac_fp32": bwd_alg_flops(Tt * Hh, dk, dv) / (b2 * 1e-3) / 1e12
+                                          / FP32_MFMA_PEAK_TFLOPS}
+                del go2, ghT2
             del dd, o2, h_T, cu
         out["other_workloads"] = other
 
