@@ -258,6 +258,16 @@ template <int ROWS, int COLS, int NT, typename X> struct Stage {
     }
 };
 
+// For the layouts without a per-channel gate: the chunk's log alpha per row,
+// one value per (token, head) (Gated DeltaNet) or 0 (DeltaNet), into gv[kB] by
+// the first kB threads; rows >= nv are 0.  The column scans read gv[r] in place
+// of a staged [row][channel] block.
+template <int GM, typename GT>
+__device__ __forceinline__ void load_gate_rows(float *gv, const GT *__restrict__ la, int64_t t0, int H, int h,
+                                               int nv, int tid) {
+    if (tid < kB) gv[tid] = (GM == kGatePerHead && tid < nv) ? to_f32(la[(t0 + tid) * H + h]) : 0.f;
+}
+
 // ----------------------------------------------------------------------------
 // Prep: one workgroup of 4 waves per (chunk, head).  The key channels are taken
 // 64 at a time (the column scan is per channel and the Gram products are sums
@@ -280,11 +290,13 @@ template <int DK> struct alignas(16) PrepBS {
     };
     float X[4][16][20];                      // per-wave product tile
     float beta[kB];
+    float gv[kB];                            // log alpha per row (scalar-gate layouts)
     float part[kSeg][CH];                    // segment totals of the column scan
     int flag;
 };
 
-template <int DK, typename IO, typename GT>
+// GM: gate layout (per key channel, per (token, head), or none).
+template <int DK, typename IO, typename GT, int GM>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
                                                        const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
                                                        const int32_t *__restrict__ cu,
@@ -317,11 +329,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
             Stage<kB, CH, 256, GT> sl;
             sq.load(q + base + c0, pitch, nv, tid);
             sk.load(k + base + c0, pitch, nv, tid);
-            sl.load(log_alpha + base + c0, pitch, nv, tid);
+            if constexpr (GM == kGatePerChannel) sl.load(log_alpha + base + c0, pitch, nv, tid);
             if (hf > 0) __syncthreads();     // the previous pass's reads of QA and KI are done
             sq.template store<S::HS>(&sm.g.QA[0][0], tid);
             sk.template store<S::KS>(&sm.KA[0][c0], tid);
-            sl.template store<S::HS>(&sm.g.KI[0][0], tid);
+            if constexpr (GM == kGatePerChannel) sl.template store<S::HS>(&sm.g.KI[0][0], tid);
+            else if (hf == 0) load_gate_rows<GM>(sm.gv, log_alpha, t0, H, h, nv, tid);
         }
         __syncthreads();
         {   // G (log2 units) per key channel, segment totals first
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
             for (int sg = p; sg < kSeg; sg += PT) {
                 const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
                 float l = 0.f;
-                for (int r = r0; r < r1; ++r) l += sm.g.KI[r][c] * kBL2E;
+                for (int r = r0; r < r1; ++r) l += (GM == kGatePerChannel ? sm.g.KI[r][c] : sm.gv[r]) * kBL2E;
                 sm.part[sg][c] = l;
             }
         }
@@ -348,7 +361,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
                 const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
                 float l = 0.f;
                 for (int r = r0; r < r1; ++r) {
-                    l += sm.g.KI[r][c] * kBL2E;
+                    l += (GM == kGatePerChannel ? sm.g.KI[r][c] : sm.gv[r]) * kBL2E;
                     const float G = pre + l;
                     const float ea = __builtin_amdgcn_exp2f(G - m2), ei = __builtin_amdgcn_exp2f(m2 - G);
                     const float kv = sm.KA[r][c0 + c];
@@ -866,6 +879,7 @@ template <int DK> struct alignas(16) GradBS {
     } r3;
     float beta[kB];                          // beta, or the erase strengths b
     float wv[kB];                            // the write strengths w (separate strengths only)
+    float gv[kB];                            // log alpha per row (scalar-gate layouts)
     float dbr[kB];
     float dbA[4][kB];
     float m2[DK], em[DK], eg[DK], egm[DK];
@@ -876,7 +890,7 @@ template <int DK> struct alignas(16) GradBS {
 
 // KT: the type of k, dq and dk (the io type, or fp32 with bf16 v and dO when
 // the input prologue's fp32 mapped q and k are the inputs).
-template <int DK, int DV, typename IO, typename GT, typename KT>
+template <int DK, int DV, typename IO, typename GT, typename KT, int GM>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const KT *__restrict__ k, const IO *__restrict__ v, const GT *__restrict__ log_alpha,
     const GT *__restrict__ beta, const IO *__restrict__ d_o, const int32_t *__restrict__ cu,
@@ -913,10 +927,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         Stage<kB, DK, 512, GT> sl;
         Stage<kB, kB, 512, float> st;
         sk.load(k + base, pitch, nv, tid);
-        sl.load(log_alpha + base, pitch, nv, tid);
+        if constexpr (GM == kGatePerChannel) sl.load(log_alpha + base, pitch, nv, tid);
         st.load(rec + R::T, kB, kB, tid);
         sk.template store<S::KS>(&sm.r3.pt.QA[0][0], tid);
-        sl.template store<S::KS>(&sm.r3.pt.KI[0][0], tid);
+        if constexpr (GM == kGatePerChannel) sl.template store<S::KS>(&sm.r3.pt.KI[0][0], tid);
+        else load_gate_rows<GM>(sm.gv, log_alpha, t0, H, h, nv, tid);
         st.template store<S::CS>(&sm.r2.m.T[0][0], tid);
     }
     __syncthreads();
@@ -929,7 +944,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     if (sc_p < kSeg) {   // G (log2 units), as the prep kernel forms it: segment totals
         const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
         float l = 0.f;
-        for (int r = r0; r < r1; ++r) l += sm.r3.pt.KI[r][sc_c] * kBL2E;
+        for (int r = r0; r < r1; ++r) l += (GM == kGatePerChannel ? sm.r3.pt.KI[r][sc_c] : sm.gv[r]) * kBL2E;
         sm.part[sc_p][sc_c] = l;
     }
     __syncthreads();
@@ -948,7 +963,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int r = r0; r < kSegRows + r0; ++r) {
             float ka = 0.f;
             if (r < r1) {
-                l += sm.r3.pt.KI[r][c] * kBL2E;
+                l += (GM == kGatePerChannel ? sm.r3.pt.KI[r][c] : sm.gv[r]) * kBL2E;
                 ka = sm.r3.pt.QA[r][c] * __builtin_amdgcn_exp2f((pre + l) - m2);
             }
             sm.KA[r][c] = ka;
@@ -1130,7 +1145,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     }
     __syncthreads();                         // dP, dM, QA, KI reads done
 
-    {   // G (log2 units) again, into the freed area
+    if constexpr (GM == kGatePerChannel) {   // G (log2 units) again, into the freed area
         Stage<kB, DK, 512, GT> sl;
         sl.load(log_alpha + ((size_t)t0 * H + h) * DK, (size_t)H * DK, nv, tid);
         sl.template store<DK>(&sm.r2.G2[0][0], tid);
@@ -1139,7 +1154,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     if (sc_p < kSeg) {   // segment totals, then G in place (as above)
         const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
         float l = 0.f;
-        for (int r = r0; r < r1; ++r) l += sm.r2.G2[r][sc_c] * kBL2E;
+        for (int r = r0; r < r1; ++r) l += (GM == kGatePerChannel ? sm.r2.G2[r][sc_c] : sm.gv[r]) * kBL2E;
         sm.part[sc_p][sc_c] = l;
     }
     __syncthreads();
@@ -1151,7 +1166,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
         float l = 0.f;
         for (int r = r0; r < r1; ++r) {
-            l += sm.r2.G2[r][sc_c] * kBL2E;
+            l += (GM == kGatePerChannel ? sm.r2.G2[r][sc_c] : sm.gv[r]) * kBL2E;
             sm.r2.G2[r][sc_c] = pre + l;
         }
     }
@@ -1218,12 +1233,27 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         float sacc = suf;
         for (int r = r1 - 1; r >= r0; --r) {
             sacc += sm.r3.pt.QA[r][c];
-            dla[((t0 + r) * H + h) * DK + c] = from_f32<GT>(bad ? qnan : sacc + dgn);
+            if constexpr (GM == kGatePerChannel) dla[((t0 + r) * H + h) * DK + c] = from_f32<GT>(bad ? qnan : sacc + dgn);
+            else sm.r2.G2[r][c] = sacc + dgn;   // G2 is free: summed over the channels below
         }
+    }
+    if constexpr (GM == kGatePerHead) {
+        // one gate shared by every key channel: its gradient is the channel sum,
+        // 8 threads per row over DK / 8 channels each, then an xor butterfly
+        // across the 8 (a fixed order: deterministic)
+        __syncthreads();
+        const int r = tid >> 3, sub = tid & 7;
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK / 8; ++i) x += sm.r2.G2[r][sub * (DK / 8) + i];
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 1);
+        if (sub == 0 && r < nv) dla[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
     }
 }
 
-template <int DK, int DV, typename IO, typename GT, typename KT = IO>
+template <int DK, int DV, typename IO, typename GT, typename KT = IO, int GM = kGatePerChannel>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const BwdLayout L = bwd_layout(a);
     uint8_t *ws = static_cast<uint8_t *>(a.workspace);
@@ -1243,7 +1273,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     if (a.varlen)
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
     if (L.nch > 0 && a.total_tokens > 0)
-        hipLaunchKernelGGL((bwd_prep_kernel<DK, KT, GT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st, q, k,
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, KT, GT, GM>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st, q, k,
                            la, be, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs);
     const int64_t grid = chain_grid(a.num_seqs * a.H, DV / kSBV);   // per pass (a multiple of 8)
     if (grid > 0) {
@@ -1254,7 +1284,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
                            Sc, Uc, sflag, dSc, dUc, a.dh0, fb);
     }
     if (L.nch > 0 && a.total_tokens > 0)
-        hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT, KT>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st,
+        hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT, KT, GM>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st,
                            k, v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, dSc,
                            dUc, sflag, static_cast<KT *>(a.dq), static_cast<KT *>(a.dk), static_cast<IO *>(a.dv),
                            static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta), wr,
@@ -1262,59 +1292,25 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int DK, int DV, int GM>
+hipError_t launch_bwd_gm(const BwdArgs &a, hipStream_t st) {
+    if (a.io_bf16)
+        return a.gate_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t, bf16_t, GM>(a, st)
+                           : launch_bwd_t<DK, DV, bf16_t, float, bf16_t, GM>(a, st);
+    return a.gate_bf16 ? launch_bwd_t<DK, DV, float, bf16_t, float, GM>(a, st)
+                       : launch_bwd_t<DK, DV, float, float, float, GM>(a, st);
+}
+
 template <int DK, int DV>
 hipError_t launch_bwd_dims(const BwdArgs &a, hipStream_t st) {
+    // scalar gates (Gated DeltaNet) or none (DeltaNet)
+    if (a.gate_mode == kGatePerHead) return launch_bwd_gm<DK, DV, kGatePerHead>(a, st);
+    if (a.gate_mode == kGateNone) return launch_bwd_gm<DK, DV, kGateNone>(a, st);
     // the input prologue's pass: fp32 mapped q, k and gates with bf16 v and dO
     if (a.qk_f32 && a.io_bf16) return launch_bwd_t<DK, DV, bf16_t, float, float>(a, st);
     if (a.io_bf16)
         return a.gate_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t>(a, st) : launch_bwd_t<DK, DV, bf16_t, float>(a, st);
     return a.gate_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a, st) : launch_bwd_t<DK, DV, float, float>(a, st);
-}
-
-// ----------------------------------------------------------------------------
-// Scalar gates (Gated DeltaNet: one log alpha per token and head; DeltaNet: none)
-// through the same kernels: the gate is broadcast over the key channels into an
-// fp32 buffer, beta converted to fp32, the backward run with fp32 gates, and
-// the channel gradients of log alpha summed per (token, head) in a fixed order.
-// This is exact by the chain rule: every channel's log alpha is the one value.
-
-// la_full[th][c] = log_alpha[th] (0 without a gate), beta32[th] = beta[th];
-// one thread per 4 channels (16-byte stores).
-template <typename GT>
-__global__ __launch_bounds__(256) void gdn_expand_kernel(const GT *__restrict__ log_alpha, const GT *__restrict__ beta,
-                                                         int64_t rows, int dk, float *__restrict__ la_full,
-                                                         float *__restrict__ beta32) {
-    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 consecutive elements of la_full
-    if (i4 >= rows * (dk / 4)) return;
-    const int64_t th = i4 / (dk / 4);
-    const float x = log_alpha ? to_f32(log_alpha[th]) : 0.f;
-    f32x4_t y;
-    y[0] = y[1] = y[2] = y[3] = x;
-    *reinterpret_cast<f32x4_t *>(la_full + 4 * i4) = y;
-    if (i4 % (dk / 4) == 0) beta32[th] = to_f32(beta[th]);
-}
-
-// grad_log_alpha[th] = sum_c dla32[th][c], grad_beta[th] = dbeta32[th].  A row
-// is summed by dk/4 lanes (16-byte loads), then across them by an xor
-// butterfly: a fixed order, so the result is deterministic.
-template <typename GT>
-__global__ __launch_bounds__(256) void gdn_finish_kernel(const float *__restrict__ dla32,
-                                                         const float *__restrict__ dbeta32, int64_t rows, int dk,
-                                                         GT *__restrict__ grad_log_alpha, GT *__restrict__ grad_beta) {
-    const int lpr = dk / 4;                                  // lanes per row: 32 or 16, dividing the wave
-    const int sub = threadIdx.x % lpr;
-    const int64_t th = ((int64_t)blockIdx.x * 256 + threadIdx.x) / lpr;
-    const bool ok = th < rows;
-    float v = 0.f;
-    if (grad_log_alpha && ok) {
-        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(dla32 + th * dk + 4 * sub);
-        v = (x[0] + x[1]) + (x[2] + x[3]);
-    }
-    for (int off = lpr / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (ok && sub == 0) {
-        if (grad_log_alpha) grad_log_alpha[th] = from_f32<GT>(v);
-        grad_beta[th] = from_f32<GT>(dbeta32[th]);
-    }
 }
 
 // ----------------------------------------------------------------------------
@@ -1442,16 +1438,16 @@ hipError_t launch_pro_maps_t(const BwdArgs &a, float lo, uint8_t *x, const ProLa
                        : launch_pro_maps<DK, float, float>(a, lo, x, P, rows, chain, st);
 }
 
-size_t gdn_extra_bytes(const BwdArgs &a) {
-    const size_t rows = (size_t)a.total_tokens * a.H;
-    return (2 * rows * a.d_k * 4 + 255) / 256 * 256 + 2 * ((rows * 4 + 255) / 256 * 256);
-}
 
 }  // namespace
 
 size_t chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total; }
 
-size_t gdn_chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total + gdn_extra_bytes(a); }
+// Scalar gates run the same kernels with the gate layout as a compile-time
+// parameter: the gate is read once per (token, head), and dlog_alpha is the
+// channel sum of the per-channel gradient (the chain rule: every channel's log
+// alpha is the one value), taken in the gradient kernel.
+size_t gdn_chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total; }
 
 size_t pro_chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total + pro_layout(a).total; }
 
@@ -1500,60 +1496,10 @@ int launch_pro_chunk_bwd(const BwdArgs &a, float lo, void *stream, char *err, si
 }
 
 int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const size_t base = bwd_layout(a).total;
-    if (a.workspace_bytes < base + gdn_extra_bytes(a)) {
-        snprintf(err, err_len, "workspace too small");
-        return -1;
-    }
-    const int64_t rows = a.total_tokens * a.H;
-    uint8_t *x = static_cast<uint8_t *>(a.workspace) + base;
-    const size_t full = (size_t)rows * a.d_k * 4;
-    float *la_full = reinterpret_cast<float *>(x);
-    float *dla32 = reinterpret_cast<float *>(x + full);
-    float *beta32 = reinterpret_cast<float *>(x + (2 * full + 255) / 256 * 256);
-    float *dbeta32 = reinterpret_cast<float *>(x + (2 * full + 255) / 256 * 256 + ((size_t)rows * 4 + 255) / 256 * 256);
-    if ((rows * (a.d_k / 4) + 255) / 256 > 0x7fffffffLL) {
-        snprintf(err, err_len, "gdn_chunk_bwd grid too large");
-        return -1;
-    }
-    if (rows > 0) {
-        const int64_t nblk = (rows * (a.d_k / 4) + 255) / 256;
-        if (a.gate_bf16)
-            hipLaunchKernelGGL(gdn_expand_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
-                               static_cast<const bf16_t *>(a.log_alpha), static_cast<const bf16_t *>(a.beta), rows,
-                               a.d_k, la_full, beta32);
-        else
-            hipLaunchKernelGGL(gdn_expand_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
-                               static_cast<const float *>(a.log_alpha), static_cast<const float *>(a.beta), rows,
-                               a.d_k, la_full, beta32);
-    }
     BwdArgs b = a;
-    b.log_alpha = la_full;
-    b.beta = beta32;
-    b.gate_bf16 = 0;
-    b.dlog_alpha = dla32;
-    b.dbeta = dbeta32;
-    b.workspace_bytes = base;
-    if (launch_chunk_bwd(b, stream, err, err_len) != 0) return -1;
-    if (rows > 0) {
-        const int64_t nblk = (rows * (a.d_k / 4) + 255) / 256;
-        const float *src_la = a.dlog_alpha ? dla32 : nullptr;
-        if (a.gate_bf16)
-            hipLaunchKernelGGL(gdn_finish_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st, dla32, dbeta32, rows,
-                               a.d_k, src_la ? static_cast<bf16_t *>(a.dlog_alpha) : nullptr,
-                               static_cast<bf16_t *>(a.dbeta));
-        else
-            hipLaunchKernelGGL(gdn_finish_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st, dla32, dbeta32, rows,
-                               a.d_k, src_la ? static_cast<float *>(a.dlog_alpha) : nullptr,
-                               static_cast<float *>(a.dbeta));
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) {
-            snprintf(err, err_len, "%s", hipGetErrorString(e));
-            return -1;
-        }
-    }
-    return 0;
+    b.gate_mode = a.log_alpha ? kGatePerHead : kGateNone;
+    if (!a.log_alpha) b.dlog_alpha = nullptr;
+    return launch_chunk_bwd(b, stream, err, err_len);
 }
 
 int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {

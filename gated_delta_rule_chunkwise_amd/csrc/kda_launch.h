@@ -62,6 +62,7 @@ struct BwdArgs {
     int32_t H, d_k, d_v;
     int32_t io_bf16, gate_bf16, varlen;
     int32_t qk_f32;             // q and k (and dq, dk) fp32 with bf16 v and dO (prologue pass)
+    int32_t gate_mode;          // 0: log_alpha per key channel; 1: per (token, head); 2: none
     void *workspace;
     size_t workspace_bytes;
 };

@@ -369,9 +369,8 @@ kda_status_t kda_chunk_bwd_decoupled(const void *q, const void *k, const void *v
 
 /*
  * Bytes of device workspace kda_gdn_chunk_bwd needs (arguments as for
- * kda_chunk_bwd_workspace_size; 0 for invalid arguments): that of
- * kda_chunk_bwd plus two fp32 [B*T*H, d_k] buffers and two fp32 [B*T*H]
- * buffers (about 1 KiB more per token-head at d_k = 128).
+ * kda_chunk_bwd_workspace_size; 0 for invalid arguments): the same as
+ * kda_chunk_bwd's.
  */
 size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
                                         int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
@@ -382,10 +381,9 @@ size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t
  * decay, section 2.1) when log_alpha is NULL.  The scalar gate is the
  * per-channel gate of kda_chunk_bwd with every channel equal to it, so by the
  * chain rule its gradient is the sum over the key channels of the per-channel
- * gradient; the library broadcasts the gate into the workspace, runs the
- * kernels of kda_chunk_bwd, and sums those channel gradients per (token, head)
- * in a fixed order.  Arguments, workspace, numerics, range and errors as for
- * kda_chunk_bwd except:
+ * gradient; the kernels of kda_chunk_bwd read the gate once per (token, head)
+ * and take that sum per (token, head) in a fixed order.  Arguments, workspace,
+ * numerics, range and errors as for kda_chunk_bwd except:
  *
  *   log_alpha       [B, T, H] gate_dtype, aligned to its element size; or NULL
  *                   for no decay
