@@ -26,8 +26,9 @@
  *   KDA is b_t = w_t = beta_t.  The generalised form with separate erase and
  *   write strengths (b_t, w_t) is the decoupled-gate variant that the Kimi
  *   Linear CoChat record quotes from citing papers ("Claims other papers make
- *   about this one"); it is kept here only so that a test can pin the pure
- *   linear-attention form of section 2.1 (b = 0, w = 1, a = 1) exactly.
+ *   about this one").  It is the reference of the separate-strength entry
+ *   points (forward and backward), and with b = 0, w = 1, a = 1 it gives the
+ *   pure linear-attention form of section 2.1 exactly, which a pin checks.
  *
  * Everything is fp64, with plain loops and no BLAS, no blocking and no
  * reordering beyond the three steps above.  Chains run in parallel threads;
