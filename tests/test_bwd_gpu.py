@@ -466,3 +466,21 @@ def test_bwd_c3_linear_in_upstream_gradients(kda):
     torch.cuda.synchronize()
     for name, x, y in zip(NAMES, a, b):
         assert torch.equal(y, 2 * x), name
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_bwd_near_range_limit(kda, io):
+    """A chunk in which key channel 0 decays by e^-150 in total (log_alpha =
+    -150/64 per token), just inside the fp32 range of the anchored factors
+    (about e^-160): the gradients still meet the tolerance there, and the other
+    chunks and heads are unaffected."""
+    cfg = I.ChunkConfig("near-limit", io, io, H=2, dk=64, dv=64, h0=True, seed=5100)
+    d = I.make_chunk_inputs(cfg, lengths=[192, 100])
+    la = d["log_alpha"].clone()
+    la[64:128, 0, 0] = -150.0 / 64
+    d["log_alpha"] = la.to(d["log_alpha"].dtype)
+    go, ghT = I.make_upstream_grads(d, 5101)
+    out = run_bwd(kda, d, go, ghT)
+    for g in out:
+        assert torch.isfinite(g.float()).all()
+    check(kda, d, io, go, ghT, what="near range limit %s" % io)
