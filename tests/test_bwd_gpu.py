@@ -114,6 +114,17 @@ def test_bwd_c3_sampled_heads(kda):
     check(kda, d, "bf16", go, None, heads=[0, 21], what="c3 heads 0,21")
 
 
+def test_bwd_max_heads(kda):
+    """H = 65,535, the largest head count the backward accepts (heads are a grid
+    dimension): workspace offsets past 2^32 bytes, a full chunk plus a one-token
+    tail, h0 and grad_hT given."""
+    cfg = I.ChunkConfig("maxh", "bf16", "bf16", H=65535, dk=64, dv=64, h0=True, seed=3460)
+    d = I.make_chunk_inputs(cfg, lengths=[65])
+    go, ghT = I.make_upstream_grads(d, 3461)
+    heads = [0, 1, 32767, 65534]
+    check(kda, d, "bf16", go, ghT, heads=heads, what="H=65535 heads %s" % heads)
+
+
 def test_bwd_c2_varlen_sampled(kda):
     """Full-size packed batch (32 sequences of 512-8192 tokens, h0 != 0, with
     grad_hT) in one call; the oracle checks three whole sequences, including the

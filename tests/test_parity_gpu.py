@@ -103,6 +103,25 @@ def test_c3_constant_decay_variant(kda):
     check_against_oracle(kda, d, "bf16", heads=[0, 5, 31], what="c3const")
 
 
+def test_max_heads(kda):
+    """H = 65,535, the largest head count the backward's grid admits: record
+    and state offsets past 2^32 bytes, a full chunk plus a one-token tail."""
+    cfg = I.ChunkConfig("maxh", "bf16", "bf16", H=65535, dk=64, dv=64, h0=True, seed=61)
+    d = I.make_chunk_inputs(cfg, lengths=[65])
+    heads = [0, 1, 32767, 65534]
+    check_against_oracle(kda, d, "bf16", heads=heads, what="H=65535 heads %s" % heads)
+
+
+def test_segments_of_one_chunk(kda):
+    """A long single sequence with 1,024 < H <= 2,048 runs in segments of one
+    chunk each (the record budget is 2,048 chunk-heads): three segments, the
+    last one ragged, with the state carried across both boundaries."""
+    cfg = I.ChunkConfig("seg1", "bf16", "bf16", H=1500, dk=128, dv=128, h0=True, seed=62)
+    d = I.make_chunk_inputs(cfg, lengths=[130])
+    heads = [0, 749, 1499]
+    check_against_oracle(kda, d, "bf16", heads=heads, what="H=1500 one-chunk segments heads %s" % heads)
+
+
 # ------------------------------------------------------------------ shapes / edge cases
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
