@@ -122,6 +122,30 @@ def test_segments_of_one_chunk(kda):
     check_against_oracle(kda, d, "bf16", heads=heads, what="H=1500 one-chunk segments heads %s" % heads)
 
 
+def test_long_sequence_past_2_32_elements(kda):
+    """One sequence of 1,050,000 tokens at H = 32, d = 128: q, k, v, log alpha
+    and o each hold 4.3e9 elements, past 2^32, so every token offset needs 64
+    bits.  It runs as 257 segments and ends in a 16-token chunk.  Inputs are
+    drawn on the device; the oracle checks two whole heads."""
+    T, heads = 1_050_000, [0, 31]
+    cfg = I.ChunkConfig("long", "bf16", "bf16", H=32, dk=128, dv=128, h0=True, seed=63)
+    d = I.make_chunk_inputs(cfg, device=DEV, lengths=[T])
+    assert d["q"].numel() > 2 ** 32
+    o, hT = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], h0=d["h0"])
+    torch.cuda.synchronize()
+    go, gh = o[:, heads].cpu(), hT[:, heads].cpu()
+    sub = {key: d[key][:, heads].cpu() for key in ("q", "k", "v", "log_alpha", "beta", "h0")}
+    sub["lengths"] = d["lengths"]
+    del d, o, hT
+    torch.cuda.empty_cache()
+    ref = to_oracle(sub)
+    ro, rh = oracle.fwd(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], h0=ref["h0"],
+                        cu_seqlens=ref["cu_seqlens"])
+    eo = assert_close(go, ro, "bf16", "T=1,050,000 o")
+    eh = assert_close(gh, rh, "bf16", "T=1,050,000 h_T")
+    log("T=1,050,000 heads %s" % heads, "o", eo, "h_T", eh)
+
+
 # ------------------------------------------------------------------ shapes / edge cases
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("io", ["bf16", "f32"])
