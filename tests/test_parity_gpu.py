@@ -268,6 +268,29 @@ def test_decode_full_size_three_steps(kda):
     log("decode S", eS)
 
 
+def test_decode_past_2_32_state_elements(kda):
+    """B = 4,100 sequences x H = 64 heads at d = 128: the fp32 state holds 4.3e9
+    elements (17 GB), past 2^32.  Drawn on the device; the oracle checks the
+    output and the updated state of the first, a middle and the last
+    (sequence, head) pair."""
+    cfg = I.DecodeConfig("decode past 2^32", "bf16", "bf16", B=4100, H=64, dk=128, dv=128, steps=1, seed=2400)
+    S = I.make_decode_state(cfg, device=DEV)
+    assert S.numel() > 2 ** 32
+    x = {n: t[0] for n, t in I.make_decode_step_inputs(cfg, 0, device=DEV).items()}
+    names = ("q", "k", "v", "log_alpha", "beta")
+    bs, hs = [0, 2049, 4099], [0, 31, 63]
+    S0 = S[bs, hs].cpu()
+    o = kda.kda_decode_step(*(x[n] for n in names), S)
+    torch.cuda.synchronize()
+    go, gS = o[bs, hs].cpu()[:, None], S[bs, hs].cpu()[:, None]
+    # the sampled pairs as a batch of 3 sequences with one head each
+    ro, rS = oracle.decode(*(f64(x[n][bs, hs].cpu()[:, None]) for n in names), f64(S0[:, None]))
+    eo = assert_close(go, ro, "bf16", "decode past 2^32 o")
+    eS = errors(gS, rS)
+    assert eS["rel_fro"] < 1e-5, eS
+    log("decode past 2^32", "o", eo, "S", eS)
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
 def test_decode_dims_fp32(kda, dk, dv):
     cfg = I.DecodeConfig("d", "f32", "f32", B=5, H=3, dk=dk, dv=dv, steps=4, seed=2100)
