@@ -153,6 +153,17 @@ def _check_dev(name, t, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _check_out(name, t, device, shape=None, dtype=None):
+    """A caller-supplied output or workspace: on the device, contiguous, and of
+    exactly the shape and dtype the call writes (workspace: any shape; its
+    byte length is checked by the library)."""
+    _check_dev(name, t, device)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, not %s" % (name, dtype, t.dtype))
+
+
 def kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, num_seqs=0, io_dtype=KDA_BF16) -> int:
     return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, num_seqs, io_dtype))
 
@@ -208,6 +219,8 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
             w_write = w_write.unsqueeze(0)
         if log_alpha is not None:
             log_alpha = log_alpha.unsqueeze(0)
+        if o is not None and o.dim() == 3:
+            o = o.unsqueeze(0)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -237,10 +250,16 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
             raise ValueError("h0 must be fp32 [N, H, d_k, d_v]")
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check_out("o", o, dev, (B, T, H, dv), q.dtype)
     if h_T is None and output_final_state:
         h_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif h_T is not None:
+        _check_out("h_T", h_T, dev, (N, H, dk, dv), torch.float32)
     io, gt = _dtype_code(q), _dtype_code(beta)
     ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, N if cu_seqlens is not None else 0, io)
+    if workspace is not None:
+        _check_out("workspace", workspace, dev)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -379,6 +398,8 @@ def _chunk_bwd(q, k, v, log_alpha, beta, grad_o, h0, grad_hT, cu_seqlens, want_g
     ws_bytes = size_fn(B, T, H, dk, dv, nseq, io)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_out("workspace", workspace, dev)
     ws_len = workspace.numel() * workspace.element_size()
     if log_alpha_min is not None:
         name = "kda_chunk_bwd_prologue"
@@ -445,6 +466,10 @@ def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min, gdn=False, w_wri
             _check_dev(name, t, dev)
     if log_alpha is not None and tuple(log_alpha.shape) != ((B, H) if gdn else (B, H, dk)):
         raise ValueError("log_alpha has the wrong shape")
+    if k.shape != q.shape or v.dim() != 3 or tuple(v.shape[:2]) != (B, H) or tuple(beta.shape) != (B, H):
+        raise ValueError("shape mismatch among q, k, v, beta")
+    if k.dtype != q.dtype or v.dtype != q.dtype or (log_alpha is not None and log_alpha.dtype != beta.dtype):
+        raise TypeError("q, k, v share one dtype; log_alpha and beta share one dtype")
     if w_write is not None:
         _check_dev("w_write", w_write, dev)
         if w_write.shape != beta.shape or w_write.dtype != beta.dtype:
@@ -453,6 +478,8 @@ def _decode_step(q, k, v, log_alpha, beta, S, o, log_alpha_min, gdn=False, w_wri
         raise ValueError("S must be fp32 [B, H, d_k, d_v]")
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check_out("o", o, dev, (B, H, dv), q.dtype)
     if w_write is not None:
         name = "kda_decode_step_decoupled"
         rc = lib.kda_decode_step_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),

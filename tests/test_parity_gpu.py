@@ -268,6 +268,34 @@ def test_decode_full_size_three_steps(kda):
     log("decode S", eS)
 
 
+def test_binding_rejects_bad_buffers(kda):
+    """Caller-supplied outputs and workspaces of the wrong shape, dtype or
+    device, and mismatched decode inputs, raise before anything is launched."""
+    cfg = I.ChunkConfig("rej", "bf16", "bf16", H=2, dk=64, dv=64, T=70, seed=64, h0=True)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in I.make_chunk_inputs(cfg).items()}
+    args = [d[n].unsqueeze(0) for n in ("q", "k", "v", "log_alpha", "beta")]
+    good, _ = kda.kda_chunk_fwd(*args)
+    bad = [dict(o=torch.empty(1, 70, 2, 32, dtype=torch.bfloat16, device=DEV)),
+           dict(o=torch.empty(1, 70, 2, 64, dtype=torch.float32, device=DEV)),
+           dict(h_T=torch.empty(1, 2, 64, 64)),
+           dict(workspace=torch.empty(1 << 20, dtype=torch.uint8))]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)):
+            kda.kda_chunk_fwd(*args, **kw)
+    dc = I.DecodeConfig("rej", "bf16", "bf16", B=3, H=2, dk=64, dv=64, steps=1, seed=2401)
+    S = I.make_decode_state(dc, device=DEV)
+    x = {n: t[0] for n, t in I.make_decode_step_inputs(dc, 0, device=DEV).items()}
+    S0 = S.clone()
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(x["q"], x["k"][:2], x["v"][:2], x["log_alpha"], x["beta"], S)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S,
+                            o=torch.empty(3, 2, 32, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
+    assert torch.equal(kda.kda_chunk_fwd(*args)[0], good)
+
+
 def test_decode_past_2_32_state_elements(kda):
     """B = 4,100 sequences x H = 64 heads at d = 128: the fp32 state holds 4.3e9
     elements (17 GB), past 2^32.  Drawn on the device; the oracle checks the
