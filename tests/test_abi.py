@@ -126,8 +126,16 @@ def test_decode_rejects(kda, kw, code):
 def test_binding_raises_without_gpu_tensors(kda):
     import torch
     x = torch.zeros(1, 64, 2, 64)
+    b = torch.zeros(1, 64, 2)
     with pytest.raises(ValueError):
-        kda.kda_chunk_fwd(x, x, x, x, torch.zeros(1, 64, 2))
+        kda.kda_chunk_fwd(x, x, x, x, b)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_bwd(x, x, x, x, b, x)
+    with pytest.raises(ValueError):
+        kda.chunk_kda(x, x, x, x, b)
+    s = torch.zeros(3, 2, 64)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(s, s, s, s, torch.zeros(3, 2), torch.zeros(3, 2, 64, 64))
 
 
 def chunk_pro(lib, lo=-20.0, **kw):
