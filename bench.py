@@ -11,8 +11,10 @@ under "prologue"; the same shape with one decay per token and head (Gated
 DeltaNet) and with none (DeltaNet), through kda_gdn_chunk_fwd, under "gdn"; and
 with separate erase and write strengths (kda_chunk_fwd_decoupled) under
 "decoupled"; the gradients of the same prefill (kda_chunk_bwd, and the
-scalar-gate, separate-strength and raw-projection backwards) under "backward"; kda_chunk_fwd on the short (H=16, T=4096) and packed variable-length
-(32 sequences of 512-8192 tokens, h0 given) workloads under "other_workloads".
+scalar-gate, separate-strength and raw-projection backwards) under "backward"; kda_chunk_fwd on the small fp32 (H=2, T=256, d=64), short (H=16, T=4096) and
+packed variable-length (32 sequences of 512-8192 tokens, h0 given) workloads
+under "other_workloads"; and the long-context prefill with one fast-forgetting
+key channel per head (log alpha = -3 per token) under "strong_decay".
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -80,7 +82,7 @@ def decode_alg_bytes(B, H, dk, dv, io_b=2, gate_b=2):
     return B * H * per_state
 
 
-CHUNK_SOURCES = ("kda_chunk.hip", "kda_chunk2.hip", "kda_chunk_common.h", "kda_device.h")
+CHUNK_SOURCES = ("kda_chunk.hip", "kda_chunk2.hip", "kda_fused.hip", "kda_chunk_common.h", "kda_plan.h", "kda_device.h")
 DECODE_SOURCES = ("kda_decode.hip", "kda_device.h")
 BWD_SOURCES = ("kda_bwd.hip", "kda_plan.h", "kda_device.h")
 
@@ -201,6 +203,7 @@ def main():
     ap.add_argument("--no-decoupled", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-other", action="store_true")
+    ap.add_argument("--no-strong", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -325,24 +328,43 @@ def main():
                          "alg_bytes_per_launch": db_}}
         del wv
 
+    # ---------------- strong decay: one fast-forgetting key channel per head
+    if not args.no_strong:
+        la_s = d["log_alpha"].clone()
+        la_s[:, :, 0] = -3.0   # channel 0 of every head: log alpha = -3 on every token
+        fns = lambda: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], la_s, d["beta"], o=o, h_T=hT)
+        per_s, _ = time_launches(fns, max(2, args.steps // 4), 1, stream)
+        sms = float(np.mean(per_s))
+        out["strong_decay"] = {
+            "workload": "kda_chunk_fwd on the same inputs with key channel 0 of every head at log alpha = -3 "
+                        "per token (a 192-nat decay per chunk on that channel)",
+            "ms_per_step": sms, "tokens_per_s": T / (sms * 1e-3), "vs_plain_ms": sms / ms}
+        del la_s
+
     # ---------------- the other prefill workloads: short sequence and packed batch
     if not args.no_other:
         other = {}
-        for key, ocfg in (("c1", I.C1), ("c2", I.C2)):
+        for key, ocfg in (("c0", I.C0), ("c1", I.C1), ("c2", I.C2)):
             dd = I.make_chunk_inputs(ocfg, device=dev)
             Tt, Hh = dd["q"].shape[0], dd["q"].shape[1]
+            odk, odv = dd["q"].shape[2], dd["v"].shape[2]
             nseq = len(dd["lengths"])
             cu = dd["cu_seqlens"].to(dev) if nseq > 1 else None
-            h_T = torch.empty((nseq, Hh, dk, dv), dtype=torch.float32, device=dev)
+            h_T = torch.empty((nseq, Hh, odk, odv), dtype=torch.float32, device=dev)
             o2 = torch.empty_like(dd["v"])
             fno = lambda: kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], h0=dd["h0"],
                                             cu_seqlens=cu, o=o2, h_T=h_T)
             per_o, _ = time_launches(fno, args.steps, args.warmup, stream)
             oms = float(np.mean(per_o))
-            ob = chunk_alg_bytes(Tt * Hh, nseq * Hh * (2 if dd["h0"] is not None else 1), dk, dv)
+            ob = chunk_alg_bytes(Tt * Hh, nseq * Hh * (2 if dd["h0"] is not None else 1), odk, odv,
+                                 io_b=dd["q"].element_size(), gate_b=dd["log_alpha"].element_size())
+            of = chunk_alg_flops(Tt * Hh, odk, odv)
             other[key] = {"workload": "kda_chunk_fwd, " + ocfg.name + (" (%d sequences, %d tokens)" % (nseq, Tt)),
                           "ms_per_step": oms, "tokens_per_s": Tt / (oms * 1e-3),
-                          "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob}
+                          "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob,
+                          "alg_flops_per_launch": of,
+                          "mfma_frac": of / (oms * 1e-3) / 1e12 /
+                          (BF16_MFMA_PEAK_TFLOPS if dd["q"].dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS)}
             if key == "c2" and not args.no_backward:
                 # the packed batch's gradients (grad_o ~ N(0,1), grad_hT ~ N(0, 0.1^2))
                 go2, ghT2 = I.make_upstream_grads(dd, 3450, device=dev)

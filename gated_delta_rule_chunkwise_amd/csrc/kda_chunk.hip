@@ -644,44 +644,60 @@ int pick_block_v(const ChunkArgs &a) {
 
 }  // namespace
 
-// Two-kernel path (kda_chunk2.hip): bf16 I/O.
+// Two-kernel path (kda_chunk2.hip): bf16 I/O at the dimensions the fused kernel
+// does not cover.
 size_t two_kernel_workspace_bytes(const ChunkArgs &a);
 hipError_t launch_chunk_fwd_two_kernel(const ChunkArgs &a, int bv, hipStream_t st);
 
-namespace {
-// bf16 I/O runs as prep + state kernels unless LIBKDA_FUSED=1 asks for the
-// single fused kernel (kept for fp32 I/O and for comparison).
-bool use_two_kernel(const ChunkArgs &a) {
-    if (!a.io_bf16) return false;
-    const char *env = getenv("LIBKDA_FUSED");
-    return !(env && atoi(env) == 1);
-}
-}  // namespace
+// Fused path (kda_fused.hip).
+bool fused_fwd_supported(const ChunkArgs &a);
+size_t fused_fwd_workspace_bytes(const ChunkArgs &a);
+bool fused_fwd_grid_ok(const ChunkArgs &a);
+hipError_t launch_fused_fwd(const ChunkArgs &a, hipStream_t st);
 
+// The workspace query does not know which entry point will use it, so it covers
+// both forward paths where the entry point decides between them.
 size_t chunk_fwd_workspace_bytes(const ChunkArgs &a) {
-    return a.io_bf16 ? two_kernel_workspace_bytes(a) : 0;
+    if (!a.io_bf16) return 0;
+    if (a.d_k == 128 && a.d_v == 128) {
+        const size_t f = fused_fwd_workspace_bytes(a), t = two_kernel_workspace_bytes(a);
+        return f > t ? f : t;
+    }
+    return two_kernel_workspace_bytes(a);
 }
 
 int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    // the state kernel pads the chains to a multiple of 8 (one group per XCD)
-    const int64_t nwg = (a.num_seqs * (int64_t)a.H + 7) / 8 * 8 * (a.d_v / 16);
-    if (nwg > 0x7fffffffLL) {
-        snprintf(err, err_len, "chunk_fwd grid too large");
-        return -1;
-    }
-    const int bv = pick_block_v(a);
     hipError_t e;
-    if (use_two_kernel(a) && a.total_tokens > 0) {
-        if (a.workspace_bytes < two_kernel_workspace_bytes(a)) {
+    if (fused_fwd_supported(a)) {
+        if (!fused_fwd_grid_ok(a)) {
+            snprintf(err, err_len, "chunk_fwd grid too large");
+            return -1;
+        }
+        if (a.workspace_bytes < chunk_fwd_workspace_bytes(a)) {
             snprintf(err, err_len, "workspace too small");
             return -1;
         }
-        e = launch_chunk_fwd_two_kernel(a, bv, st);
-    } else if (a.d_k == 128)
-        e = bv == 32 ? launch_types_pro<128, 32>(a, st) : launch_types_pro<128, 16>(a, st);
-    else
-        e = bv == 32 ? launch_types_pro<64, 32>(a, st) : launch_types_pro<64, 16>(a, st);
+        e = launch_fused_fwd(a, st);
+    } else {
+        // the state kernel pads the chains to a multiple of 8 (one group per XCD)
+        const int64_t nwg = (a.num_seqs * (int64_t)a.H + 7) / 8 * 8 * (a.d_v / 16);
+        if (nwg > 0x7fffffffLL) {
+            snprintf(err, err_len, "chunk_fwd grid too large");
+            return -1;
+        }
+        const int bv = pick_block_v(a);
+        if (a.io_bf16 && a.total_tokens > 0) {
+            if (a.workspace_bytes < chunk_fwd_workspace_bytes(a)) {
+                snprintf(err, err_len, "workspace too small");
+                return -1;
+            }
+            e = launch_chunk_fwd_two_kernel(a, bv, st);
+        } else if (a.d_k == 128)
+            e = bv == 32 ? launch_types_pro<128, 32>(a, st) : launch_types_pro<128, 16>(a, st);
+        else
+            e = bv == 32 ? launch_types_pro<64, 32>(a, st) : launch_types_pro<64, 16>(a, st);
+    }
     if (e != hipSuccess) {
         snprintf(err, err_len, "%s", hipGetErrorString(e));
         return -1;

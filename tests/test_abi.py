@@ -42,42 +42,56 @@ def test_version_and_status_strings(kda):
     assert kda.kda_last_hip_error() == ""
 
 
+def seg_state_bytes(chains, nseg, dk=128, dv=128):
+    """Per (chain, segment): start state, end state from zero (fp32 d_k x d_v) and
+    the segment's transition (fp32 d_k x d_k)."""
+    return chains * nseg * (2 * dk * dv + dk * dk) * 4
+
+
 def test_workspace_size(kda):
-    # bf16 I/O: one per-chunk record per (chunk, head) plus a small header;
-    # fp32 I/O needs none; unsupported sizes report 0.
-    # a record holds at least the decayed keys, queries and transposed keys
-    # (3 x 64 x 128 bf16) and at most ~96 KiB per chunk-head
-    two = kda.kda_chunk_fwd_workspace_size(2, 65536, 32, 128, 128, 0, kda.KDA_BF16)
-    assert 2 * 1024 * 32 * (3 * 64 * 128 * 2) <= two <= 2 * 1024 * 32 * 96 * 1024 + 4096
+    # bf16 I/O at d_k = d_v = 128: the query covers both forward paths (the input
+    # variants run the fused kernel, plain KDA the two-kernel path), so it is at
+    # least the fused kernel's segment states (chains split into segments to fill
+    # the GPU: about 256 workgroups, segments of at least 4 chunks, at least 3 of
+    # them) and at least the two-kernel records (below)
+    W = lambda *a: kda.kda_chunk_fwd_workspace_size(*a)
+    assert W(1, 1000, 2, 128, 128, 5, kda.KDA_BF16) >= 256   # packed: the fused kernel's sequence order
+    assert W(1, 65536, 32, 128, 128, 0, kda.KDA_BF16) >= seg_state_bytes(32, 8)
+    assert W(2, 65536, 32, 128, 128, 0, kda.KDA_BF16) >= seg_state_bytes(64, 4)
+    assert W(1, 4096, 16, 128, 128, 0, kda.KDA_BF16) >= seg_state_bytes(16, 16)
+    # bf16 I/O at other dimensions (two-kernel path): one per-chunk record per
+    # (chunk, head), at least the decayed keys, queries and transposed keys
+    # (3 x 64 x d_k bf16) and at most ~96 KiB per chunk-head, plus a small header
+    two = W(2, 65536, 32, 64, 64, 0, kda.KDA_BF16)
+    assert 2 * 1024 * 32 * (3 * 64 * 64 * 2) <= two <= 2 * 1024 * 32 * 96 * 1024 + 4096
     # one long sequence runs in segments of at most 2048 chunk-heads of records,
     # plus the fp32 state carried between them
-    big = kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_BF16)
-    carry = 32 * 128 * 128 * 4
-    assert 2048 * (3 * 64 * 128 * 2) + carry <= big <= 2048 * 96 * 1024 + carry + 4096
-    # a sequence that fits one segment is one pass
-    one = kda.kda_chunk_fwd_workspace_size(1, 4096, 32, 128, 128, 0, kda.KDA_BF16)
-    assert 64 * 32 * (3 * 64 * 128 * 2) <= one <= 64 * 32 * 96 * 1024 + 4096
-    assert kda.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, 0, kda.KDA_F32) == 0
-    assert kda.kda_chunk_fwd_workspace_size(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
+    big = W(1, 65536, 32, 64, 64, 0, kda.KDA_BF16)
+    carry = 32 * 64 * 64 * 4
+    assert 2048 * (3 * 64 * 64 * 2) + carry <= big <= 2048 * 96 * 1024 + carry + 4096
+    assert W(1, 65536, 32, 128, 128, 0, kda.KDA_F32) == 0
+    assert W(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
     # varlen: room for one partial chunk per sequence
-    v1 = kda.kda_chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
-    v0 = kda.kda_chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 0, kda.KDA_BF16)
+    v1 = W(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
+    v0 = W(1, 1000, 2, 64, 64, 0, kda.KDA_BF16)
     assert v1 > v0 > 0
 
 
 def test_chunk_fwd_requires_workspace(kda):
     lib = kda.load_library()
-    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
-    assert chunk(lib, ws=None, wsb=0) == 3
-    assert chunk(lib, ws=P, wsb=need - 1) == 3
-    assert chunk(lib, ws=P + 8, wsb=need) == 1   # misaligned workspace
+    # a single sequence of 64 chunks at H = 2 runs in segments: it needs workspace
+    need = kda.kda_chunk_fwd_workspace_size(1, 4096, 2, 128, 128, 0, kda.KDA_BF16)
+    assert need > 0
+    assert chunk(lib, T=4096, ws=None, wsb=0) == 3
+    assert chunk(lib, T=4096, ws=P, wsb=need - 1) == 3
+    assert chunk(lib, T=4096, ws=P + 8, wsb=need) == 1   # misaligned workspace
 
 
 P = 1 << 20   # a fake, 16-byte aligned "device" address; never dereferenced
 
 
 def chunk(lib, **kw):
-    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=4096, H=2,
              dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"], a["N"],
@@ -139,7 +153,7 @@ def test_binding_raises_without_gpu_tensors(kda):
 
 
 def chunk_pro(lib, lo=-20.0, **kw):
-    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=4096, H=2,
              dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
     a.update(kw)
     return lib.kda_chunk_fwd_prologue(a["q"], a["k"], a["v"], a["la"], a["beta"], lo, a["h0"], a["cu"],
@@ -157,7 +171,7 @@ def decode_pro(lib, lo=-20.0, **kw):
 @pytest.mark.parametrize("lo", [float("nan"), float("inf"), float("-inf"), 0.5, 1e-30])
 def test_prologue_rejects_bad_floor(kda, lo):
     lib = kda.load_library()
-    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    need = kda.kda_chunk_fwd_workspace_size(1, 4096, 2, 128, 128, 0, kda.KDA_BF16)
     assert chunk_pro(lib, lo=lo, ws=P, wsb=need) == 1
     assert decode_pro(lib, lo=lo) == 1
 
@@ -168,7 +182,7 @@ def test_prologue_rejects_bad_floor(kda, lo):
 ])
 def test_chunk_fwd_prologue_validates_like_chunk_fwd(kda, kw, code):
     lib = kda.load_library()
-    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    need = kda.kda_chunk_fwd_workspace_size(1, 4096, 2, 128, 128, 0, kda.KDA_BF16)
     a = dict(ws=P, wsb=need)
     a.update(kw)
     assert chunk_pro(lib, lo=0.0, **a) == code
@@ -185,7 +199,7 @@ def test_decode_prologue_validates_like_decode(kda, kw, code):
 
 
 def chunk_gdn(lib, **kw):
-    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=4096, H=2,
              dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
     a.update(kw)
     return lib.kda_gdn_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"], a["N"],
@@ -206,7 +220,7 @@ def decode_gdn(lib, **kw):
 ])
 def test_gdn_chunk_fwd_validates(kda, kw, code):
     lib = kda.load_library()
-    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    need = kda.kda_chunk_fwd_workspace_size(1, 4096, 2, 128, 128, 0, kda.KDA_BF16)
     a = dict(ws=P, wsb=need)
     a.update(kw)
     assert chunk_gdn(lib, **a) == code
@@ -231,7 +245,7 @@ def test_gdn_decode_validates(kda, kw, code):
 
 
 def chunk_dec(lib, wwr=P, **kw):
-    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=128, H=2,
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=4096, H=2,
              dk=128, dv=128, io=1, gt=1, ws=None, wsb=0)
     a.update(kw)
     return lib.kda_chunk_fwd_decoupled(a["q"], a["k"], a["v"], a["la"], a["beta"], wwr, a["h0"], a["cu"],
@@ -253,7 +267,7 @@ def decode_dec(lib, wwr=P, **kw):
 ])
 def test_decoupled_chunk_fwd_validates(kda, kw, code):
     lib = kda.load_library()
-    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, 0, kda.KDA_BF16)
+    need = kda.kda_chunk_fwd_workspace_size(1, 4096, 2, 128, 128, 0, kda.KDA_BF16)
     a = dict(ws=P, wsb=need)
     a.update(kw)
     assert chunk_dec(lib, **a) == code

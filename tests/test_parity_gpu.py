@@ -31,9 +31,9 @@ def log(*a):
     sys.stdout.flush()
 
 
-def run_gpu(kda, d, with_h0=True):
+def run_gpu(kda, d, with_h0=True, packed=False):
     dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
-    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 else None
+    cu = dev["cu_seqlens"] if len(d["lengths"]) > 1 or packed else None
     o, hT = kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
                               h0=dev["h0"] if with_h0 else None, cu_seqlens=cu)
     torch.cuda.synchronize()
@@ -67,13 +67,11 @@ def test_c1_bf16_full(kda):
     check_against_oracle(kda, d, "bf16", what="c1")
 
 
-def test_c2_varlen_sampled(kda):
-    """Full-size varlen batch (32 sequences, h0 != 0) in the launch the benchmark
-    times; the oracle checks 3 whole sequences (all heads), incl. the longest."""
+def test_c2_varlen_full(kda):
+    """Full-size varlen batch (32 sequences of 512-8192 tokens, h0 != 0) in the
+    launch the benchmark times; the oracle checks every sequence and head."""
     d = I.make_chunk_inputs(I.C2)
-    lens = d["lengths"]
-    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7})
-    check_against_oracle(kda, d, "bf16", seqs=seqs, what="c2 seqs %s" % seqs)
+    check_against_oracle(kda, d, "bf16", what="c2 all %d sequences" % len(d["lengths"]))
 
 
 @pytest.mark.parametrize("bv", ["16", "32"])
@@ -91,16 +89,17 @@ def test_block_width_variants(kda, bv, monkeypatch):
     check_against_oracle(kda, d, "f32", what="fp32 d_k=64 BV=%s" % bv)
 
 
-def test_c3_long_sampled_heads(kda):
-    """Full-size T = 65536 prefill; the oracle checks 2 whole heads end to end."""
+def test_c3_long_full(kda):
+    """Full-size T = 65536 prefill; the oracle checks all 32 heads end to end."""
     d = I.make_chunk_inputs(I.C3)
-    check_against_oracle(kda, d, "bf16", heads=[0, 31], what="c3 heads 0,31")
+    check_against_oracle(kda, d, "bf16", what="c3 all heads")
 
 
-def test_c3_constant_decay_variant(kda):
-    """Long-memory variant: one decay per (head, channel) held over time."""
-    d = I.make_chunk_inputs(I.C3, lengths=[8192], gate="uniform_const")
-    check_against_oracle(kda, d, "bf16", heads=[0, 5, 31], what="c3const")
+def test_c3_constant_decay_full(kda):
+    """Long-memory variant at full size (T = 65536, H = 32): one decay per
+    (head, channel), drawn in [0.5, 0.9999] and held over time; all heads."""
+    d = I.make_chunk_inputs(I.C3, gate="uniform_const")
+    check_against_oracle(kda, d, "bf16", what="c3 uniform_const all heads")
 
 
 def test_max_heads(kda):
@@ -242,30 +241,58 @@ def test_varlen_equals_separate_calls(kda):
             sub[x] = d[x][cu[n]:cu[n + 1]].contiguous()
         sub["h0"] = d["h0"][n:n + 1].contiguous()
         sub["lengths"] = [lens[n]]
-        on, hn = run_gpu(kda, sub)
+        sub["cu_seqlens"] = torch.tensor([0, lens[n]], dtype=d["cu_seqlens"].dtype)
+        on, hn = run_gpu(kda, sub, packed=True)
         assert torch.equal(on.reshape(-1, *on.shape[-2:]), o.reshape(-1, *o.shape[-2:])[cu[n]:cu[n + 1]])
         assert torch.equal(hn[0], hT[n])
 
 
 # ------------------------------------------------------------------ decode
-def test_decode_full_size_three_steps(kda):
+def _decode_block_as_fwd(x):
+    """A block of decode-step inputs [steps, B, H, d] as one packed prefill of B
+    sequences of `steps` tokens each ([B*steps, H, d], cu_seqlens): T decode
+    steps from a state equal a T-token forward from it (the oracle's pinned
+    decode-equals-forward invariant), so the oracle walks each (sequence, head)
+    chain through the whole block in one call, carrying its fp64 state."""
+    steps, B = x["q"].shape[0], x["q"].shape[1]
+    seq = lambda t: np.ascontiguousarray(f64(t).swapaxes(0, 1).reshape((B * steps,) + tuple(t.shape[2:])))
+    cu = np.arange(B + 1, dtype=np.int64) * steps
+    return {n: seq(x[n]) for n in ("q", "k", "v", "log_alpha", "beta")}, cu
+
+
+@pytest.mark.timeout(900)
+def test_decode_full_size_all_steps(kda):
+    """The decode workload at full size: B = 256, H = 32, d = 128, fp32 states
+    N(0, 0.1^2), 1000 steps with fresh seeded inputs (drawn on the device, as
+    the benchmark does).  Every step's o and the final S against the oracle, in
+    blocks of 100 steps with the oracle's fp64 state carried between blocks."""
     cfg = I.C4
-    S = I.make_decode_state(cfg)
-    Sg = S.to(DEV)
+    S = I.make_decode_state(cfg, device=DEV)
     Sref = f64(S)
-    steps = I.make_decode_step_inputs(cfg, 0, steps=3)
-    for s in range(3):
-        x = {n: t[s] for n, t in steps.items()}
-        o = kda.kda_decode_step(*(x[n].to(DEV) for n in ("q", "k", "v", "log_alpha", "beta")), Sg)
-        ro, Sref = oracle.decode(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["log_alpha"]),
-                                 f64(x["beta"]), Sref)
+    names = ("q", "k", "v", "log_alpha", "beta")
+    block, worst = 100, dict(max_abs=0.0, rel_fro=0.0)
+    od = torch.empty((cfg.B, cfg.H, cfg.dv), dtype=torch.bfloat16, device=DEV)
+    for s0 in range(0, cfg.steps, block):
+        n = min(block, cfg.steps - s0)
+        x = I.make_decode_step_inputs(cfg, s0, device=DEV, steps=n)
+        outs = torch.empty((n, cfg.B, cfg.H, cfg.dv), dtype=torch.bfloat16, device=DEV)
+        for s in range(n):
+            kda.kda_decode_step(*(x[nm][s] for nm in names), S, o=od)
+            outs[s].copy_(od)
         torch.cuda.synchronize()
-        e = assert_close(o.cpu(), ro, "bf16", "decode step %d o" % s)
-        log("decode step", s, e)
-    e = assert_close(Sg.cpu(), Sref, "bf16", "decode S")
-    eS = errors(Sg.cpu(), Sref)
+        go = outs.cpu()
+        xin, cu = _decode_block_as_fwd({nm: x[nm].cpu() for nm in names})
+        del x, outs
+        ro, Sref = oracle.fwd(xin["q"], xin["k"], xin["v"], xin["log_alpha"], xin["beta"], h0=Sref,
+                              cu_seqlens=cu)
+        ro = ro.reshape(cfg.B, n, cfg.H, cfg.dv).swapaxes(0, 1)
+        for s in range(n):
+            e = assert_close(go[s], ro[s], "bf16", "decode step %d o" % (s0 + s))
+            worst = {k: max(worst[k], e[k]) for k in worst}
+        log("decode steps %d-%d: worst so far %s" % (s0, s0 + n - 1, worst))
+    eS = errors(S.cpu(), Sref)
     assert eS["rel_fro"] < 1e-5, eS
-    log("decode S", eS)
+    log("decode all %d steps: worst o %s; final S %s" % (cfg.steps, worst, eS))
 
 
 def test_binding_rejects_bad_buffers(kda):
@@ -380,12 +407,12 @@ def check_prologue_against_oracle(kda, d, io, lo, seqs=None, heads=None, what=""
     return eo, eh
 
 
-def test_prologue_c3_sampled_heads(kda):
+def test_prologue_c3_full(kda):
     """The benchmarked prologue call: c3's full size (T = 65536, H = 32) on raw
     projections, gate pre-activations spanning decays 0.5-0.9999, floor -30;
-    the oracle checks 2 whole heads end to end."""
+    the oracle checks every head end to end."""
     d = I.make_chunk_raw_inputs(I.C3, gate="uniform")
-    check_prologue_against_oracle(kda, d, "bf16", -30.0, heads=[0, 31], what="prologue c3 heads 0,31")
+    check_prologue_against_oracle(kda, d, "bf16", -30.0, what="prologue c3 all heads")
 
 
 def test_prologue_c1_shape_bf16(kda):
@@ -501,12 +528,12 @@ def test_gdn_ragged_varlen(kda, gate, io, dk, dv):
     _gdn_check(kda, d, g, io, "gdn %s %s dk=%d dv=%d" % (gate, io, dk, dv))
 
 
-def test_gdn_c3_sampled_heads(kda):
+def test_gdn_c3_full(kda):
     """c3's full size with one decay per token and head (c3's per-channel draw,
-    first channel); the oracle checks 2 whole heads."""
+    first channel); the oracle checks every head."""
     d = I.make_chunk_inputs(I.C3)
     g = d["log_alpha"][:, :, 0].contiguous()
-    _gdn_check(kda, d, g, "bf16", "gdn c3 heads 0,31", heads=[0, 31])
+    _gdn_check(kda, d, g, "bf16", "gdn c3 all heads")
 
 
 @pytest.mark.parametrize("gate", ["scalar", "none"])
@@ -568,12 +595,12 @@ def test_decoupled_ragged_varlen(kda, case, io, dk, dv):
     _dec_check(kda, d, wv, io, "decoupled %s %s dk=%d dv=%d" % (case, io, dk, dv))
 
 
-def test_decoupled_c3_sampled_heads(kda):
+def test_decoupled_c3_full(kda):
     """c3's full size with the write strength drawn independently of beta; the
-    oracle checks 2 whole heads."""
+    oracle checks every head."""
     d = I.make_chunk_inputs(I.C3)
     wv = I.draw_strength(d["beta"].shape, 5200, d["beta"].dtype)
-    _dec_check(kda, d, wv, "bf16", "decoupled c3 heads 0,31", heads=[0, 31])
+    _dec_check(kda, d, wv, "bf16", "decoupled c3 all heads")
 
 
 def test_decoupled_decode(kda):
