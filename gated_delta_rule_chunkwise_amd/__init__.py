@@ -257,13 +257,13 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
     elif h_T is not None:
         _check_out("h_T", h_T, dev, (N, H, dk, dv), torch.float32)
     io, gt = _dtype_code(q), _dtype_code(beta)
-    ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, N if cu_seqlens is not None else 0, io)
+    nseq = N if cu_seqlens is not None else 0
+    ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, nseq, io)
     if workspace is not None:
         _check_out("workspace", workspace, dev)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    nseq = N if cu_seqlens is not None else 0
     if w_write is not None:
         name = "kda_chunk_fwd_decoupled"
         rc = lib.kda_chunk_fwd_decoupled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(w_write),

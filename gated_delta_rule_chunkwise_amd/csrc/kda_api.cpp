@@ -16,8 +16,8 @@ thread_local char g_hip_error[512] = "";
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
-bool valid_dtype(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
-uintptr_t dsize(kda_dtype_t t) { return t == KDA_F32 ? 4 : 2; }
+bool valid_dtype(int32_t t) { return t == KDA_F32 || t == KDA_BF16; }
+uintptr_t dsize(int32_t t) { return t == KDA_F32 ? 4 : 2; }
 
 // Products of the sizes must stay well inside int64 for device indexing.
 bool sizes_fit(int64_t a, int64_t b, int64_t c) {
@@ -35,11 +35,11 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
                             const void *beta, const void *w_write, const float *h0, const int32_t *cu_seqlens,
                             int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                            kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                            int32_t io_dtype, int32_t gate_dtype, void *workspace,
                             size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode);
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
                               const void *beta, const void *w_write, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
-                              int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
+                              int32_t d_v, int32_t io_dtype, int32_t gate_dtype, void *stream,
                               bool prologue, float lo, int gate_mode);
 
 }  // namespace
@@ -48,7 +48,7 @@ extern "C" {
 
 int32_t kda_abi_version(void) { return 1; }
 
-const char *kda_status_string(kda_status_t s) {
+const char *kda_status_string(int32_t s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";
         case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
@@ -62,10 +62,11 @@ const char *kda_status_string(kda_status_t s) {
 const char *kda_last_hip_error(void) { return g_hip_error; }
 
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                    int32_t num_seqs, kda_dtype_t io_dtype) {
-    (void)io_dtype;
+                                    int32_t num_seqs, int32_t io_dtype) {
     if (B <= 0 || T < 0 || H <= 0 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
-    if (!valid_dtype(io_dtype)) return 0;
+    if (!valid_dtype(io_dtype) || num_seqs < 0 || (num_seqs > 0 && B != 1)) return 0;
+    if (!sizes_fit((int64_t)B * T, H, d_k > d_v ? d_k : d_v)) return 0;
+    if (!sizes_fit(num_seqs > 0 ? num_seqs : B, H, (int64_t)d_k * d_v)) return 0;
     kda::ChunkArgs a = {};
     a.varlen = num_seqs > 0;
     a.num_seqs = num_seqs > 0 ? num_seqs : B;
@@ -79,8 +80,8 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
                            const void *beta, const float *h0, const int32_t *cu_seqlens,
                            int32_t num_seqs, void *o, float *h_T, int32_t B, int32_t T,
-                           int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                           kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                           int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                           int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
                           io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f, 0);
@@ -90,7 +91,7 @@ kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const 
                                     const void *gate_pre, const void *beta_pre, float log_alpha_min,
                                     const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                                     void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k,
-                                    int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                                    int32_t d_v, int32_t io_dtype, int32_t gate_dtype,
                                     void *workspace, size_t workspace_bytes, void *stream) {
     if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
     return chunk_fwd_impl(q_raw, k_raw, v, gate_pre, beta_pre, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k,
@@ -99,8 +100,8 @@ kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const 
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
                              const void *beta, float *S, void *o, int32_t B, int32_t H,
-                             int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                             kda_dtype_t gate_dtype, void *stream) {
+                             int32_t d_k, int32_t d_v, int32_t io_dtype,
+                             int32_t gate_dtype, void *stream) {
     return decode_step_impl(q, k, v, log_alpha, beta, nullptr, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
                             0.f, 0);
 }
@@ -108,7 +109,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
 kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v,
                                       const void *gate_pre, const void *beta_pre, float log_alpha_min,
                                       float *S, void *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
-                                      kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream) {
+                                      int32_t io_dtype, int32_t gate_dtype, void *stream) {
     if (!valid_floor(log_alpha_min)) return KDA_ERR_INVALID_ARGUMENT;
     return decode_step_impl(q_raw, k_raw, v, gate_pre, beta_pre, nullptr, S, o, B, H, d_k, d_v, io_dtype, gate_dtype,
                             stream, true, log_alpha_min, 0);
@@ -117,7 +118,7 @@ kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, cons
 kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
                                const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                                void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                               kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                               int32_t io_dtype, int32_t gate_dtype, void *workspace,
                                size_t workspace_bytes, void *stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
                           io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f,
@@ -126,7 +127,7 @@ kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
 
 kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
                                  const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
-                                 int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream) {
+                                 int32_t d_v, int32_t io_dtype, int32_t gate_dtype, void *stream) {
     return decode_step_impl(q, k, v, log_alpha, beta, nullptr, S, o, B, H, d_k, d_v, io_dtype, gate_dtype, stream, false,
                             0.f, log_alpha ? 1 : 2);
 }
@@ -134,8 +135,8 @@ kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, co
 kda_status_t kda_chunk_fwd_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
                                      const void *b_erase, const void *w_write, const float *h0,
                                      const int32_t *cu_seqlens, int32_t num_seqs, void *o, float *h_T, int32_t B,
-                                     int32_t T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                                     kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                                     int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                     int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                                      void *stream) {
     if ((int64_t)B * T > 0 && (!w_write || !aligned_to(w_write, dsize(gate_dtype))))
         return valid_dtype(gate_dtype) ? KDA_ERR_INVALID_ARGUMENT : KDA_ERR_UNSUPPORTED;
@@ -145,8 +146,8 @@ kda_status_t kda_chunk_fwd_decoupled(const void *q, const void *k, const void *v
 
 kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
                                        const void *b_erase, const void *w_write, float *S, void *o, int32_t B,
-                                       int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                                       kda_dtype_t gate_dtype, void *stream) {
+                                       int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                       int32_t gate_dtype, void *stream) {
     if (!w_write || !aligned_to(w_write, dsize(gate_dtype)))
         return valid_dtype(gate_dtype) ? KDA_ERR_INVALID_ARGUMENT : KDA_ERR_UNSUPPORTED;
     return decode_step_impl(q, k, v, log_alpha, b_erase, w_write, S, o, B, H, d_k, d_v, io_dtype, gate_dtype,
@@ -154,7 +155,7 @@ kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void 
 }
 
 static kda::BwdArgs bwd_sizes(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t num_seqs,
-                              kda_dtype_t io_dtype) {
+                              int32_t io_dtype) {
     kda::BwdArgs a = {};
     a.varlen = num_seqs > 0;
     a.num_seqs = num_seqs > 0 ? num_seqs : B;
@@ -166,26 +167,28 @@ static kda::BwdArgs bwd_sizes(int32_t B, int32_t T, int32_t H, int32_t d_k, int3
 }
 
 static bool bwd_sizes_ok(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t num_seqs,
-                         kda_dtype_t io_dtype) {
+                         int32_t io_dtype) {
     if (B <= 0 || T < 0 || H <= 0 || H > 65535 || !supported_dim(d_k) || !supported_dim(d_v)) return false;
     if (!valid_dtype(io_dtype)) return false;
-    return !(num_seqs < 0 || (num_seqs > 0 && B != 1));
+    if (num_seqs < 0 || (num_seqs > 0 && B != 1)) return false;
+    return sizes_fit((int64_t)B * T, H, d_k > d_v ? d_k : d_v) &&
+           sizes_fit(num_seqs > 0 ? num_seqs : B, H, (int64_t)d_k * d_v);
 }
 
 size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                    int32_t num_seqs, kda_dtype_t io_dtype) {
+                                    int32_t num_seqs, int32_t io_dtype) {
     if (!bwd_sizes_ok(B, T, H, d_k, d_v, num_seqs, io_dtype)) return 0;
     return kda::chunk_bwd_workspace_bytes(bwd_sizes(B, T, H, d_k, d_v, num_seqs, io_dtype));
 }
 
 size_t kda_chunk_bwd_prologue_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                             int32_t num_seqs, kda_dtype_t io_dtype) {
+                                             int32_t num_seqs, int32_t io_dtype) {
     if (!bwd_sizes_ok(B, T, H, d_k, d_v, num_seqs, io_dtype)) return 0;
     return kda::pro_chunk_bwd_workspace_bytes(bwd_sizes(B, T, H, d_k, d_v, num_seqs, io_dtype));
 }
 
 size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                        int32_t num_seqs, kda_dtype_t io_dtype) {
+                                        int32_t num_seqs, int32_t io_dtype) {
     if (!bwd_sizes_ok(B, T, H, d_k, d_v, num_seqs, io_dtype)) return 0;
     return kda::gdn_chunk_bwd_workspace_bytes(bwd_sizes(B, T, H, d_k, d_v, num_seqs, io_dtype));
 }
@@ -200,7 +203,7 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
                             const float *h0, const int32_t *cu_seqlens, int32_t num_seqs, const void *grad_o,
                             const float *grad_hT, void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
                             void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H, int32_t d_k,
-                            int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                            int32_t d_v, int32_t io_dtype, int32_t gate_dtype, void *workspace,
                             size_t workspace_bytes, void *stream, int gate_mode, bool decoupled = false,
                             const void *w_write = nullptr, void *grad_w_write = nullptr, float lo = 0.f) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
@@ -239,6 +242,8 @@ kda_status_t chunk_bwd_impl(const void *q, const void *k, const void *v, const v
         return KDA_ERR_INVALID_ARGUMENT;
     kda::BwdArgs a = bwd_sizes(B, T, H, d_k, d_v, cu_seqlens ? num_seqs : 0, io_dtype);
     a.gate_bf16 = gate_dtype == KDA_BF16;
+    if (!(gate_mode == 3 ? kda::pro_chunk_bwd_grids_fit(a) : kda::chunk_bwd_grids_fit(a)))
+        return KDA_ERR_UNSUPPORTED;
     const size_t need = gate_mode == 0   ? kda::chunk_bwd_workspace_bytes(a)
                         : gate_mode == 3 ? kda::pro_chunk_bwd_workspace_bytes(a)
                                          : kda::gdn_chunk_bwd_workspace_bytes(a);
@@ -269,7 +274,7 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                            const void *grad_o, const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
                            void *grad_log_alpha, void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
-                           int32_t d_k, int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                           int32_t d_k, int32_t d_v, int32_t io_dtype, int32_t gate_dtype,
                            void *workspace, size_t workspace_bytes, void *stream) {
     return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k, grad_v,
                           grad_log_alpha, grad_beta, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype, workspace,
@@ -281,8 +286,8 @@ kda_status_t kda_chunk_bwd_prologue(const void *q_raw, const void *k_raw, const 
                                     const int32_t *cu_seqlens, int32_t num_seqs, const void *grad_o,
                                     const float *grad_hT, void *grad_q_raw, void *grad_k_raw, void *grad_v,
                                     void *grad_gate_pre, void *grad_beta_pre, float *grad_h0, int32_t B, int32_t T,
-                                    int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                                    kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+                                    int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                    int32_t gate_dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return chunk_bwd_impl(q_raw, k_raw, v, gate_pre, beta_pre, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q_raw,
                           grad_k_raw, grad_v, grad_gate_pre, grad_beta_pre, grad_h0, B, T, H, d_k, d_v, io_dtype,
                           gate_dtype, workspace, workspace_bytes, stream, 3, false, nullptr, nullptr, log_alpha_min);
@@ -294,7 +299,7 @@ kda_status_t kda_chunk_bwd_decoupled(const void *q, const void *k, const void *v
                                      const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
                                      void *grad_log_alpha, void *grad_b_erase, void *grad_w_write, float *grad_h0,
                                      int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                     kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                                     int32_t io_dtype, int32_t gate_dtype, void *workspace,
                                      size_t workspace_bytes, void *stream) {
     return chunk_bwd_impl(q, k, v, log_alpha, b_erase, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k,
                           grad_v, grad_log_alpha, grad_b_erase, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype,
@@ -305,7 +310,7 @@ kda_status_t kda_gdn_chunk_bwd(const void *q, const void *k, const void *v, cons
                                const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                                const void *grad_o, const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
                                void *grad_log_alpha, void *grad_beta, float *grad_h0, int32_t B, int32_t T,
-                               int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                               int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype, int32_t gate_dtype,
                                void *workspace, size_t workspace_bytes, void *stream) {
     return chunk_bwd_impl(q, k, v, log_alpha, beta, h0, cu_seqlens, num_seqs, grad_o, grad_hT, grad_q, grad_k, grad_v,
                           grad_log_alpha, grad_beta, grad_h0, B, T, H, d_k, d_v, io_dtype, gate_dtype, workspace,
@@ -320,7 +325,7 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
                             const void *beta, const void *w_write, const float *h0, const int32_t *cu_seqlens,
                             int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                            kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                            int32_t io_dtype, int32_t gate_dtype, void *workspace,
                             size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -350,16 +355,17 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
     a.num_seqs = N; a.seq_len = T; a.total_tokens = (int64_t)B * T;
     a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.w_write = w_write;
+    a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
+    a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;
+    if (!kda::chunk_fwd_grids_fit(a)) return KDA_ERR_UNSUPPORTED;
     const size_t need = kda::chunk_fwd_workspace_bytes(a);
     if (need > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
     if (!have_tokens && !h_T) return KDA_OK;  // nothing to compute or write
-
-    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.w_write = w_write;
-    a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
-    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;
     g_hip_error[0] = '\0';
+
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     if (kda::launch_chunk_fwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
         return KDA_ERR_HIP;
     return KDA_OK;
@@ -367,7 +373,7 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
 
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
                               const void *beta, const void *w_write, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
-                              int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream,
+                              int32_t d_v, int32_t io_dtype, int32_t gate_dtype, void *stream,
                               bool prologue, float lo, int gate_mode) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -384,6 +390,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const
     a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
     a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;
+    if (!kda::decode_grids_fit(a)) return KDA_ERR_UNSUPPORTED;
     g_hip_error[0] = '\0';
     if (kda::launch_decode_step(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)
         return KDA_ERR_HIP;

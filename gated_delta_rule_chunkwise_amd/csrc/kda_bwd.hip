@@ -1460,7 +1460,7 @@ int launch_pro_chunk_bwd(const BwdArgs &a, float lo, void *stream, char *err, si
         return -1;
     }
     const int64_t rows = a.total_tokens * a.H;
-    if ((rows + 3) / 4 > 0x7fffffffLL) {
+    if (!pro_chunk_bwd_grids_fit(a)) {
         snprintf(err, err_len, "chunk_bwd_prologue grid too large");
         return -1;
     }
@@ -1502,10 +1502,22 @@ int launch_gdn_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_l
     return launch_chunk_bwd(b, stream, err, err_len);
 }
 
+// The prep and gradient kernels run (chunks, heads) grids of 256 and 512
+// threads, the state kernel up to two passes of the padded chains.
+bool chunk_bwd_grids_fit(const BwdArgs &a) {
+    const BwdLayout L = bwd_layout(a);
+    return grid_fits(L.nch, 512) && a.H <= kMaxGridY && grid_fits(2 * chain_grid(a.num_seqs * a.H, a.d_v / kSBV), kSP);
+}
+
+// The prologue's map kernels take four rows per 256-thread workgroup.
+bool pro_chunk_bwd_grids_fit(const BwdArgs &a) {
+    return chunk_bwd_grids_fit(a) && grid_fits((a.total_tokens * a.H + 3) / 4, 256);
+}
+
 int launch_chunk_bwd(const BwdArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const BwdLayout L = bwd_layout(a);
-    if (L.nch > 0x7fffffffLL || 2 * chain_grid(a.num_seqs * a.H, a.d_v / kSBV) > 0x7fffffffLL) {
+    if (!chunk_bwd_grids_fit(a)) {
         snprintf(err, err_len, "chunk_bwd grid too large");
         return -1;
     }

@@ -633,11 +633,7 @@ hipError_t launch_types_pro(const ChunkArgs &a, hipStream_t st) {
 
 // Value-column block width: 32 when that still gives at least two workgroups
 // per compute unit (less recomputation of the d_v-independent part), else 16.
-// LIBKDA_BLOCK_V=16|32 overrides the choice (used by the tests to cover both).
 int pick_block_v(const ChunkArgs &a) {
-    const char *env = getenv("LIBKDA_BLOCK_V");
-    const int forced = env ? atoi(env) : 0;
-    if (forced == 16 || forced == 32) return forced;
     const int64_t chains = a.num_seqs * (int64_t)a.H;
     return chains * (a.d_v / 32) >= 512 ? 32 : 16;
 }
@@ -647,12 +643,13 @@ int pick_block_v(const ChunkArgs &a) {
 // Two-kernel path (kda_chunk2.hip): bf16 I/O at the dimensions the fused kernel
 // does not cover.
 size_t two_kernel_workspace_bytes(const ChunkArgs &a);
+bool two_kernel_grids_fit(const ChunkArgs &a, int bv);
 hipError_t launch_chunk_fwd_two_kernel(const ChunkArgs &a, int bv, hipStream_t st);
 
 // Fused path (kda_fused.hip).
 bool fused_fwd_supported(const ChunkArgs &a);
 size_t fused_fwd_workspace_bytes(const ChunkArgs &a);
-bool fused_fwd_grid_ok(const ChunkArgs &a);
+bool fused_fwd_grids_fit(const ChunkArgs &a);
 hipError_t launch_fused_fwd(const ChunkArgs &a, hipStream_t st);
 
 // The workspace query does not know which entry point will use it, so it covers
@@ -660,32 +657,37 @@ hipError_t launch_fused_fwd(const ChunkArgs &a, hipStream_t st);
 size_t chunk_fwd_workspace_bytes(const ChunkArgs &a) {
     if (!a.io_bf16) return 0;
     if (a.d_k == 128 && a.d_v == 128) {
-        const size_t f = fused_fwd_workspace_bytes(a), t = two_kernel_workspace_bytes(a);
+        // packed batches always run the fused kernel; equal-length ones run it
+        // for the input variants and the two-kernel path for plain KDA
+        const size_t f = fused_fwd_workspace_bytes(a);
+        if (a.varlen) return f;
+        const size_t t = two_kernel_workspace_bytes(a);
         return f > t ? f : t;
     }
     return two_kernel_workspace_bytes(a);
 }
 
+bool chunk_fwd_grids_fit(const ChunkArgs &a) {
+    if (fused_fwd_supported(a)) return fused_fwd_grids_fit(a);
+    const int bv = pick_block_v(a);
+    if (a.io_bf16 && a.total_tokens > 0) return two_kernel_grids_fit(a, bv);
+    return grid_fits(a.num_seqs * (int64_t)a.H * (a.d_v / bv), kThreads);
+}
+
 int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (!chunk_fwd_grids_fit(a)) {
+        snprintf(err, err_len, "chunk_fwd grid too large");
+        return -1;
+    }
     hipError_t e;
     if (fused_fwd_supported(a)) {
-        if (!fused_fwd_grid_ok(a)) {
-            snprintf(err, err_len, "chunk_fwd grid too large");
-            return -1;
-        }
         if (a.workspace_bytes < chunk_fwd_workspace_bytes(a)) {
             snprintf(err, err_len, "workspace too small");
             return -1;
         }
         e = launch_fused_fwd(a, st);
     } else {
-        // the state kernel pads the chains to a multiple of 8 (one group per XCD)
-        const int64_t nwg = (a.num_seqs * (int64_t)a.H + 7) / 8 * 8 * (a.d_v / 16);
-        if (nwg > 0x7fffffffLL) {
-            snprintf(err, err_len, "chunk_fwd grid too large");
-            return -1;
-        }
         const int bv = pick_block_v(a);
         if (a.io_bf16 && a.total_tokens > 0) {
             if (a.workspace_bytes < chunk_fwd_workspace_bytes(a)) {

@@ -1120,6 +1120,16 @@ size_t record_bytes(int d_k, int d_v) {
 
 }  // namespace
 
+// The prep kernel runs one workgroup per chunk-head of a pass (a segment's when
+// the sequence runs in segments), the state kernel the padded chains times the
+// value-column blocks.
+bool two_kernel_grids_fit(const ChunkArgs &a, int bv) {
+    const int64_t segc = segment_chunks(a);
+    const int64_t nprep = (segc > 0 ? segc : max_chunks(a)) * a.H;
+    const int width = (a.d_k == 64 && bv == 32) ? 32 : 16;
+    return grid_fits(nprep, kThreads) && grid_fits(state_grid(a.num_seqs * (int64_t)a.H, a.d_v / width), kStateThreads);
+}
+
 size_t two_kernel_workspace_bytes(const ChunkArgs &a) {
     if (a.total_tokens <= 0) return 0;
     const int64_t segc = segment_chunks(a);

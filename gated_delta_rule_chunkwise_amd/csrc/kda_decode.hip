@@ -164,9 +164,11 @@ hipError_t launch_dims(const DecodeArgs &a, hipStream_t st) {
 
 }  // namespace
 
+bool decode_grids_fit(const DecodeArgs &a) { return grid_fits(a.B * (int64_t)a.H, kDecodeThreads); }
+
 int launch_decode_step(const DecodeArgs &a, void *stream, char *err, size_t err_len) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (a.B * (int64_t)a.H > 0x7fffffffLL) {
+    if (!decode_grids_fit(a)) {
         snprintf(err, err_len, "decode grid too large");
         return -1;
     }

@@ -1030,7 +1030,6 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t *__restric
 constexpr int64_t kFusedTargetBlocks = 256;   // one workgroup per compute unit
 constexpr int64_t kMinSegChunks = 4;          // shortest segment worth its transition pass
 constexpr int64_t kOrderMaxSeqs = 16384;      // longest-first order up to this many sequences
-constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kFT - 1;
 
 struct FusedPlan {
     int64_t chains;
@@ -1139,13 +1138,14 @@ bool fused_fwd_supported(const ChunkArgs &a) {
 
 size_t fused_fwd_workspace_bytes(const ChunkArgs &a) { return fused_plan(a).bytes; }
 
-// Largest grid any launch of the call uses, in workgroups (0 when nothing runs).
-int64_t fused_fwd_max_blocks(const ChunkArgs &a) {
+// Every launch of the call within the HIP limits: the chain kernels (one
+// workgroup per chain or segment), the sequence order and the segment scan.
+bool fused_fwd_grids_fit(const ChunkArgs &a) {
     const FusedPlan p = fused_plan(a);
-    return p.nseg >= 3 ? p.chains * p.nseg : p.chains;
+    if (!grid_fits(p.nseg >= 3 ? p.chains * p.nseg : p.chains, kFT)) return false;
+    if (p.order && !grid_fits((a.num_seqs + 255) / 256, 256)) return false;
+    return p.nseg < 3 || grid_fits(p.chains * (a.d_v / 16), 256);
 }
-
-bool fused_fwd_grid_ok(const ChunkArgs &a) { return fused_fwd_max_blocks(a) <= kMaxBlocks; }
 
 hipError_t launch_fused_fwd(const ChunkArgs &a, hipStream_t st) {
     return launch_fused_variants<128, 128>(a, st);

@@ -39,12 +39,22 @@ struct DecodeArgs {
     int32_t gate_mode;          // 0: log_alpha [B, H, d_k]; 1: [B, H]; 2: none
 };
 
+// HIP launch limits: gridDim.x * blockDim.x below 2^32 work-items, and a
+// second grid dimension of at most 65535 workgroups.
+constexpr int64_t kMaxWorkItems = (int64_t)1 << 32;
+constexpr int64_t kMaxGridY = 65535;
+inline bool grid_fits(int64_t blocks, int64_t threads) { return blocks >= 0 && blocks * threads < kMaxWorkItems; }
+
 // Both return 0 when the launch was enqueued, or -1 after a HIP error whose
 // text is copied into err (err_len bytes, NUL-terminated).
 int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len);
 int launch_decode_step(const DecodeArgs &a, void *stream, char *err, size_t err_len);
 // Workspace for these arguments (pointers are not read).
 size_t chunk_fwd_workspace_bytes(const ChunkArgs &a);
+// Whether every launch of the call stays within the HIP launch limits (host
+// check, made before any launch; pointers are not read).
+bool chunk_fwd_grids_fit(const ChunkArgs &a);
+bool decode_grids_fit(const DecodeArgs &a);
 
 struct BwdArgs {
     const void *q, *k, *v, *log_alpha, *beta;
@@ -68,6 +78,8 @@ struct BwdArgs {
 };
 
 size_t chunk_bwd_workspace_bytes(const BwdArgs &a);
+bool chunk_bwd_grids_fit(const BwdArgs &a);       // also the scalar-gate form
+bool pro_chunk_bwd_grids_fit(const BwdArgs &a);
 // Raw projections: q, k, log_alpha, beta of a are the raw inputs (and dq, dk,
 // dlog_alpha, dbeta their gradients); lo is the gate floor.
 size_t pro_chunk_bwd_workspace_bytes(const BwdArgs &a);

@@ -41,39 +41,47 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad size, misalignment */
-    KDA_ERR_UNSUPPORTED = 2,      /* d_k or d_v not in {64, 128}, unknown dtype    */
+    KDA_ERR_UNSUPPORTED = 2,      /* d_k or d_v not in {64, 128}, unknown dtype,
+                                     or a batch beyond HIP's launch limits (a
+                                     grid of 2^32 work-items or more)          */
     KDA_ERR_WORKSPACE = 3,        /* workspace smaller than the size query         */
     KDA_ERR_HIP = 4               /* a HIP launch reported an error                */
 } kda_status_t;
 
+/* Element types.  Calls take them as int32_t codes with these values (any
+ * other value is refused with KDA_ERR_UNSUPPORTED). */
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
 /* Version of this ABI; bumped on any incompatible change. */
 int32_t kda_abi_version(void);
 
-/* Static text for a status code (never NULL). */
-const char *kda_status_string(kda_status_t status);
+/* Static text for a status code (never NULL; "KDA_ERR_UNKNOWN" for any other value). */
+const char *kda_status_string(int32_t status);
 
 /* Text of the last KDA_ERR_HIP reported on the calling thread ("" if none). */
 const char *kda_last_hip_error(void);
 
 /*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none).
- * Arguments as for kda_chunk_fwd; num_seqs is the number of sequences (B when
- * no cu_seqlens is given).  With bf16 I/O the forward runs in two passes and
- * the workspace holds, per (chunk, head), the chunk's state-independent
- * operands: W and U0 (the UT transform already applied to the decayed keys and
- * to the values), the decayed queries and keys, the intra-chunk score block
- * and the per-channel decay scales -- about 92 KiB at d_k = d_v = 128, i.e.
- * about 1.4 KiB per token-head.  A single sequence (B = 1, no cu_seqlens)
- * longer than 2048 / H chunks runs in segments of that many chunks, so the
- * workspace then holds one segment's records (at most 2048 chunk-heads, about
- * 190 MB, sized to stay in the last-level cache) plus an fp32 state of
- * H x d_k x d_v.  fp32 I/O needs none.  The size depends only on the
- * arguments, never on tensor contents.
+ * Arguments as for kda_chunk_fwd; num_seqs is the number of sequences (0 when
+ * no cu_seqlens is given).  fp32 I/O needs none.  With bf16 I/O:
+ *  - a packed batch (num_seqs > 0) at d_k = d_v = 128 runs one fused kernel per
+ *    (sequence, head): the workspace holds the order in which the sequences
+ *    are taken (int32 per sequence, rounded up to 256 bytes);
+ *  - an equal-length batch at d_k = d_v = 128 may run either forward (plain KDA
+ *    runs two passes, the input variants the fused kernel), so the size covers
+ *    both: the two-pass records (per chunk and head, the chunk's
+ *    state-independent operands, about 1.4 KiB per token-head; a single
+ *    sequence longer than 2048 / H chunks runs in segments of that many chunks,
+ *    so at most 2048 chunk-heads, about 190 MB, plus an fp32 state of
+ *    H x d_k x d_v) and the fused kernel's segment states (a chain too long for
+ *    the parallelism of the GPU is cut into segments: three d_k x d_v fp32
+ *    matrices per segment, at most about 72 MiB in all);
+ *  - at d_k or d_v = 64 both kinds of batch run two passes (records as above).
+ * The size depends only on the arguments, never on tensor contents.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
-                                    int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+                                    int32_t d_v, int32_t num_seqs, int32_t io_dtype);
 
 /*
  * kda_chunk_fwd -- chunkwise KDA forward over a batch of sequences (prefill).
@@ -119,8 +127,8 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
                            const void *beta, const float *h0, const int32_t *cu_seqlens,
                            int32_t num_seqs, void *o, float *h_T, int32_t B, int32_t T,
-                           int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                           kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                           int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                           int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream);
 
 /*
@@ -141,8 +149,8 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
                              const void *beta, float *S, void *o, int32_t B, int32_t H,
-                             int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                             kda_dtype_t gate_dtype, void *stream);
+                             int32_t d_k, int32_t d_v, int32_t io_dtype,
+                             int32_t gate_dtype, void *stream);
 
 /*
  * kda_chunk_fwd_prologue -- kda_chunk_fwd on raw projections (fused input
@@ -170,7 +178,7 @@ kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const 
                                     const void *gate_pre, const void *beta_pre, float log_alpha_min,
                                     const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                                     void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k,
-                                    int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                                    int32_t d_v, int32_t io_dtype, int32_t gate_dtype,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -183,7 +191,7 @@ kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const 
 kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v,
                                       const void *gate_pre, const void *beta_pre, float log_alpha_min,
                                       float *S, void *o, int32_t B, int32_t H, int32_t d_k, int32_t d_v,
-                                      kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream);
+                                      int32_t io_dtype, int32_t gate_dtype, void *stream);
 
 /*
  * kda_gdn_chunk_fwd -- the scalar-gate members of the family through the same
@@ -200,7 +208,7 @@ kda_status_t kda_decode_step_prologue(const void *q_raw, const void *k_raw, cons
 kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
                                const void *beta, const float *h0, const int32_t *cu_seqlens, int32_t num_seqs,
                                void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                               kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *workspace,
+                               int32_t io_dtype, int32_t gate_dtype, void *workspace,
                                size_t workspace_bytes, void *stream);
 
 /*
@@ -210,7 +218,7 @@ kda_status_t kda_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
  */
 kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, const void *log_alpha,
                                  const void *beta, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
-                                 int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype, void *stream);
+                                 int32_t d_v, int32_t io_dtype, int32_t gate_dtype, void *stream);
 
 /*
  * kda_chunk_fwd_decoupled -- KDA with the update strength split into an erase
@@ -230,8 +238,8 @@ kda_status_t kda_gdn_decode_step(const void *q, const void *k, const void *v, co
 kda_status_t kda_chunk_fwd_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
                                      const void *b_erase, const void *w_write, const float *h0,
                                      const int32_t *cu_seqlens, int32_t num_seqs, void *o, float *h_T, int32_t B,
-                                     int32_t T, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                                     kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                                     int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                     int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
 /*
@@ -241,8 +249,8 @@ kda_status_t kda_chunk_fwd_decoupled(const void *q, const void *k, const void *v
  */
 kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void *v, const void *log_alpha,
                                        const void *b_erase, const void *w_write, float *S, void *o, int32_t B,
-                                       int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                                       kda_dtype_t gate_dtype, void *stream);
+                                       int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                       int32_t gate_dtype, void *stream);
 
 /*
  * Bytes of device workspace kda_chunk_bwd needs for these sizes (arguments as
@@ -256,7 +264,7 @@ kda_status_t kda_decode_step_decoupled(const void *q, const void *k, const void 
  * only on the arguments.
  */
 size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
-                                    int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+                                    int32_t d_v, int32_t num_seqs, int32_t io_dtype);
 
 /*
  * kda_chunk_bwd -- gradients of kda_chunk_fwd, for training.
@@ -300,8 +308,8 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            int32_t num_seqs, const void *grad_o, const float *grad_hT,
                            void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
                            void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
-                           int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                           kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                           int32_t d_k, int32_t d_v, int32_t io_dtype,
+                           int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream);
 
 /*
@@ -311,7 +319,7 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
  * buffers (about 3 KiB more per token-head at d_k = 128).
  */
 size_t kda_chunk_bwd_prologue_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
-                                             int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+                                             int32_t d_v, int32_t num_seqs, int32_t io_dtype);
 
 /*
  * kda_chunk_bwd_prologue -- gradients of kda_chunk_fwd_prologue with respect
@@ -334,8 +342,8 @@ kda_status_t kda_chunk_bwd_prologue(const void *q_raw, const void *k_raw, const 
                                     const void *grad_o, const float *grad_hT, void *grad_q_raw,
                                     void *grad_k_raw, void *grad_v, void *grad_gate_pre,
                                     void *grad_beta_pre, float *grad_h0, int32_t B, int32_t T,
-                                    int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                                    kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                                    int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                    int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                                     void *stream);
 
 /*
@@ -364,7 +372,7 @@ kda_status_t kda_chunk_bwd_decoupled(const void *q, const void *k, const void *v
                                      const float *grad_hT, void *grad_q, void *grad_k, void *grad_v,
                                      void *grad_log_alpha, void *grad_b_erase, void *grad_w_write,
                                      float *grad_h0, int32_t B, int32_t T, int32_t H, int32_t d_k,
-                                     int32_t d_v, kda_dtype_t io_dtype, kda_dtype_t gate_dtype,
+                                     int32_t d_v, int32_t io_dtype, int32_t gate_dtype,
                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -373,7 +381,7 @@ kda_status_t kda_chunk_bwd_decoupled(const void *q, const void *k, const void *v
  * kda_chunk_bwd's.
  */
 size_t kda_gdn_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
-                                        int32_t d_v, int32_t num_seqs, kda_dtype_t io_dtype);
+                                        int32_t d_v, int32_t num_seqs, int32_t io_dtype);
 
 /*
  * kda_gdn_chunk_bwd -- gradients of kda_gdn_chunk_fwd: Gated DeltaNet (one
@@ -396,8 +404,8 @@ kda_status_t kda_gdn_chunk_bwd(const void *q, const void *k, const void *v, cons
                                int32_t num_seqs, const void *grad_o, const float *grad_hT,
                                void *grad_q, void *grad_k, void *grad_v, void *grad_log_alpha,
                                void *grad_beta, float *grad_h0, int32_t B, int32_t T, int32_t H,
-                               int32_t d_k, int32_t d_v, kda_dtype_t io_dtype,
-                               kda_dtype_t gate_dtype, void *workspace, size_t workspace_bytes,
+                               int32_t d_k, int32_t d_v, int32_t io_dtype,
+                               int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                                void *stream);
 
 #ifdef __cplusplus

@@ -55,7 +55,7 @@ def test_workspace_size(kda):
     # the GPU: about 256 workgroups, segments of at least 4 chunks, at least 3 of
     # them) and at least the two-kernel records (below)
     W = lambda *a: kda.kda_chunk_fwd_workspace_size(*a)
-    assert W(1, 1000, 2, 128, 128, 5, kda.KDA_BF16) >= 256   # packed: the fused kernel's sequence order
+    assert W(1, 1000, 2, 128, 128, 5, kda.KDA_BF16) == 256   # packed: the fused kernel's sequence order
     assert W(1, 65536, 32, 128, 128, 0, kda.KDA_BF16) >= seg_state_bytes(32, 8)
     assert W(2, 65536, 32, 128, 128, 0, kda.KDA_BF16) >= seg_state_bytes(64, 4)
     assert W(1, 4096, 16, 128, 128, 0, kda.KDA_BF16) >= seg_state_bytes(16, 16)
@@ -125,6 +125,21 @@ def test_chunk_fwd_rejects(kda, kw, code):
 def test_chunk_fwd_empty_without_state_is_noop(kda):
     lib = kda.load_library()
     assert chunk(lib, T=0, q=None, k=None, v=None, la=None, beta=None, o=None, hT=None) == 0
+
+
+def test_calls_beyond_the_launch_limits_are_refused(kda):
+    """HIP launches at most 2^32 work-items per grid: at N * H = 2^19 chains of
+    d_v = 128 the forward's state kernel (1024 threads over 8 value-column
+    blocks per chain) would need 2^32, so the call is refused with
+    KDA_ERR_UNSUPPORTED before anything is enqueued (the fake pointers are
+    never touched).  Likewise the decode step at B * H = 2^24 (256 threads per
+    chain) and the backward at N * H = 2^20."""
+    lib = kda.load_library()
+    assert chunk(lib, B=1 << 14, H=32, T=64, ws=P, wsb=1 << 62) == 2
+    assert chunk(lib, B=(1 << 14) - 8, H=32, T=64, ws=None, wsb=0) == 3   # just below: only the workspace is missing
+    assert decode(lib, B=1 << 19, H=32) == 2
+    assert bwd(lib, B=1 << 15, H=32, T=64, ws=P, wsb=1 << 62) == 2
+    assert bwd(lib, B=(1 << 15) - 8, H=32, T=64, ws=None, wsb=0) == 3
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -74,19 +74,18 @@ def test_c2_varlen_full(kda):
     check_against_oracle(kda, d, "bf16", what="c2 all %d sequences" % len(d["lengths"]))
 
 
-@pytest.mark.parametrize("bv", ["16", "32"])
-def test_block_width_variants(kda, bv, monkeypatch):
-    """Both value-column block widths of the kernel, on the c1 shape and a
-    ragged varlen batch with h0."""
-    monkeypatch.setenv("LIBKDA_BLOCK_V", bv)
-    d = I.make_chunk_inputs(I.C1, lengths=[2000])
-    check_against_oracle(kda, d, "bf16", what="c1-like BV=%s" % bv)
-    cfg = I.ChunkConfig("bv", "bf16", "bf16", H=4, dk=128, dv=128, h0=True, seed=19)
-    d = I.make_chunk_inputs(cfg, lengths=[5, 700, 64, 129])
-    check_against_oracle(kda, d, "bf16", what="ragged BV=%s" % bv)
-    cfg = I.ChunkConfig("bv64", "f32", "f32", H=2, dk=64, dv=128, h0=True, seed=20)
-    d = I.make_chunk_inputs(cfg, lengths=[300, 17])
-    check_against_oracle(kda, d, "f32", what="fp32 d_k=64 BV=%s" % bv)
+@pytest.mark.parametrize("bv", [16, 32])
+def test_block_width_variants(kda, bv):
+    """Both value-column block widths of the paths that have two (fp32 I/O, and
+    bf16 at d_k = 64): a workgroup takes 32 value columns once the chains times
+    d_v / 32 reach 512, else 16, so the head count picks the width."""
+    for io, dk, dv, lens, seed in (("f32", 64, 128, [300, 17], 20), ("bf16", 64, 128, [5, 700, 64, 129], 19),
+                                   ("f32", 128, 128, [130, 3], 21)):
+        H = 128 // len(lens) if bv == 32 else 2
+        assert (len(lens) * H * (dv // 32) >= 512) == (bv == 32)
+        cfg = I.ChunkConfig("bv", io, io, H=H, dk=dk, dv=dv, h0=True, seed=seed)
+        d = I.make_chunk_inputs(cfg, lengths=lens)
+        check_against_oracle(kda, d, io, what="%s d_k=%d BV=%d" % (io, dk, bv))
 
 
 def test_c3_long_full(kda):
