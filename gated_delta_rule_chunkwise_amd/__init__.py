@@ -8,6 +8,7 @@ point raises.
 
 Entry points (same names as the C ABI):
     kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, ...)
+    kda_chunk_fwd_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, o=..., h_T=...)
     kda_decode_step(q, k, v, log_alpha, beta, S, o=None)
     kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, ...)
     kda_decode_step_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, S, o=None)
@@ -41,7 +42,8 @@ EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error"
                     "kda_gdn_decode_step", "kda_chunk_fwd_decoupled", "kda_decode_step_decoupled",
                     "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
                     "kda_gdn_chunk_bwd_workspace_size", "kda_gdn_chunk_bwd", "kda_chunk_bwd_decoupled",
-                    "kda_chunk_bwd_prologue_workspace_size", "kda_chunk_bwd_prologue")
+                    "kda_chunk_bwd_prologue_workspace_size", "kda_chunk_bwd_prologue",
+                    "kda_chunk_fwd_noalloc")
 
 _lib = None
 
@@ -76,6 +78,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                   ctypes.c_int, ctypes.c_int, vp, sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                          ctypes.c_int, ctypes.c_int, vp]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
                                     ctypes.c_int, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -181,6 +186,18 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None,
                       None)
 
 
+def kda_chunk_fwd_noalloc(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o, h_T=None):
+    """kda_chunk_fwd through the C entry point that allocates nothing: its
+    workspace is a scratch array the library holds on each device (80 MiB),
+    shared by every such call on the device, so calls that overlap in time on
+    one device race.  The caller passes the outputs o (and h_T, or None when
+    the final state is not wanted); this function allocates no device memory.
+    Raises KDAError (KDA_ERR_WORKSPACE) for calls that need more scratch
+    (bf16 at d_k or d_v = 64 with a large batch)."""
+    return _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, h_T is not None, None, None,
+                      noalloc=True)
+
+
 def kda_gdn_chunk_fwd(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, *, o=None, h_T=None,
                       output_final_state=True, workspace=None):
     """Gated DeltaNet (log_alpha [B, T, H], one decay per token and head) or
@@ -209,7 +226,7 @@ def kda_chunk_fwd_prologue(q_raw, k_raw, v, gate_pre, beta_pre, log_alpha_min, h
 
 
 def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_state, workspace,
-               log_alpha_min, gdn=False, w_write=None):
+               log_alpha_min, gdn=False, w_write=None, noalloc=False):
     import torch
     lib = load_library()
     squeeze = q.dim() == 3
@@ -258,6 +275,13 @@ def _chunk_fwd(q, k, v, log_alpha, beta, h0, cu_seqlens, o, h_T, output_final_st
         _check_out("h_T", h_T, dev, (N, H, dk, dv), torch.float32)
     io, gt = _dtype_code(q), _dtype_code(beta)
     nseq = N if cu_seqlens is not None else 0
+    if noalloc:
+        rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                                       _ptr(cu_seqlens), nseq, _ptr(o), _ptr(h_T), B, T, H, dk, dv, io, gt,
+                                       _stream_of(q))
+        if rc != KDA_OK:
+            raise KDAError(rc, "kda_chunk_fwd_noalloc", kda_last_hip_error())
+        return (o.squeeze(0) if squeeze else o), h_T
     ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, nseq, io)
     if workspace is not None:
         _check_out("workspace", workspace, dev)

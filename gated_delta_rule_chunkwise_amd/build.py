@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk2.hip", "kda_fused.hip", "kda_decode.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_chunk2.hip", "kda_fused.hip", "kda_decode.hip", "kda_bwd.hip",
+           "kda_noalloc.hip"]
 
 # The packed fp32 VALU forms are switched off for the device code, which is
 # written with scalar or float2 arithmetic only; hipcc's host pass warns that it

@@ -36,7 +36,8 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
                             int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                             int32_t io_dtype, int32_t gate_dtype, void *workspace,
-                            size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode);
+                            size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode,
+                            bool noalloc = false);
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v, const void *log_alpha,
                               const void *beta, const void *w_write, float *S, void *o, int32_t B, int32_t H, int32_t d_k,
                               int32_t d_v, int32_t io_dtype, int32_t gate_dtype, void *stream,
@@ -85,6 +86,15 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            void *stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
                           io_dtype, gate_dtype, workspace, workspace_bytes, stream, false, 0.f, 0);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *log_alpha,
+                                   const void *beta, const float *h0, const int32_t *cu_seqlens,
+                                   int32_t num_seqs, void *o, float *h_T, int32_t B, int32_t T,
+                                   int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                   int32_t gate_dtype, void *stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, nullptr, h0, cu_seqlens, num_seqs, o, h_T, B, T, H, d_k, d_v,
+                          io_dtype, gate_dtype, nullptr, 0, stream, false, 0.f, 0, true);
 }
 
 kda_status_t kda_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v,
@@ -326,7 +336,8 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
                             int32_t num_seqs,
                             void *o, float *h_T, int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                             int32_t io_dtype, int32_t gate_dtype, void *workspace,
-                            size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode) {
+                            size_t workspace_bytes, void *stream, bool prologue, float lo, int gate_mode,
+                            bool noalloc) {
     if (!valid_dtype(io_dtype) || !valid_dtype(gate_dtype)) return KDA_ERR_UNSUPPORTED;
     if (B <= 0 || T < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -355,15 +366,25 @@ kda_status_t chunk_fwd_impl(const void *q, const void *k, const void *v, const v
     a.num_seqs = N; a.seq_len = T; a.total_tokens = (int64_t)B * T;
     a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.io_bf16 = io_dtype == KDA_BF16; a.gate_bf16 = gate_dtype == KDA_BF16;
+    a.force_fused = noalloc;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.w_write = w_write;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.h_T = h_T;
     a.prologue = prologue; a.log_alpha_min = lo; a.gate_mode = gate_mode;
     if (!kda::chunk_fwd_grids_fit(a)) return KDA_ERR_UNSUPPORTED;
     const size_t need = kda::chunk_fwd_workspace_bytes(a);
-    if (need > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_WORKSPACE;
-    if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
+    if (noalloc) {
+        if (need > kda::kNoAllocScratchBytes) return KDA_ERR_WORKSPACE;
+    } else {
+        if (need > 0 && (workspace_bytes < need || !workspace)) return KDA_ERR_WORKSPACE;
+        if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
+    }
     if (!have_tokens && !h_T) return KDA_OK;  // nothing to compute or write
     g_hip_error[0] = '\0';
+    if (noalloc && need > 0) {
+        // the library-held scratch of the current device: no allocation
+        if (kda::noalloc_scratch(&workspace, g_hip_error, sizeof(g_hip_error)) != 0) return KDA_ERR_HIP;
+        workspace_bytes = kda::kNoAllocScratchBytes;
+    }
 
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     if (kda::launch_chunk_fwd(a, stream, g_hip_error, sizeof(g_hip_error)) != 0)

@@ -660,7 +660,7 @@ size_t chunk_fwd_workspace_bytes(const ChunkArgs &a) {
         // packed batches always run the fused kernel; equal-length ones run it
         // for the input variants and the two-kernel path for plain KDA
         const size_t f = fused_fwd_workspace_bytes(a);
-        if (a.varlen) return f;
+        if (a.varlen || a.force_fused) return f;
         const size_t t = two_kernel_workspace_bytes(a);
         return f > t ? f : t;
     }

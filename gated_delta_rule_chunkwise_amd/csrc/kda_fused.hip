@@ -1130,11 +1130,19 @@ hipError_t launch_fused_variants(const ChunkArgs &a, hipStream_t st) {
 // for packed batches and for the input variants (raw projections, scalar
 // gates, separate strengths); plain KDA over an equal-length batch runs the
 // two-kernel path (prep + state kernels), which is faster there.  A packed
-// batch gives bitwise the results of each of its sequences packed alone.
+// batch gives bitwise the results of each of its sequences packed alone.  The
+// forward that allocates nothing takes the fused kernel for every batch shape,
+// since its workspace (segment states of at most about 340 chains) is bounded.
 bool fused_fwd_supported(const ChunkArgs &a) {
     if (!a.io_bf16 || a.d_k != 128 || a.d_v != 128) return false;
-    return a.varlen || a.prologue || a.gate_mode != kGatePerChannel || a.w_write != nullptr;
+    return a.force_fused || a.varlen || a.prologue || a.gate_mode != kGatePerChannel || a.w_write != nullptr;
 }
+
+// Chains are split only when ceil(target / chains) >= 3, i.e. chains < target / 2,
+// and then chains * nseg < target + chains < 1.5 target: the segment states of
+// any call fit the scratch of the forward that allocates nothing.
+static_assert((size_t)(kFusedTargetBlocks + kFusedTargetBlocks / 2) * 3 * 128 * 128 * 4 <= kNoAllocScratchBytes,
+              "fused segment states exceed the no-allocation scratch");
 
 size_t fused_fwd_workspace_bytes(const ChunkArgs &a) { return fused_plan(a).bytes; }
 

@@ -22,6 +22,7 @@ struct ChunkArgs {
     int32_t prologue;           // q, k, log_alpha, beta are raw projections
     float log_alpha_min;        // floor of log alpha under the prologue
     int32_t gate_mode;          // 0: log_alpha [.., d_k]; 1: [..] per (token, head); 2: none
+    int32_t force_fused;        // bf16 at d_k = d_v = 128: the fused kernel for every batch shape
     void *workspace;
     size_t workspace_bytes;
 };
@@ -55,6 +56,12 @@ size_t chunk_fwd_workspace_bytes(const ChunkArgs &a);
 // check, made before any launch; pointers are not read).
 bool chunk_fwd_grids_fit(const ChunkArgs &a);
 bool decode_grids_fit(const DecodeArgs &a);
+
+// Size of the library-held device scratch of the forward that allocates nothing.
+constexpr size_t kNoAllocScratchBytes = (size_t)80 << 20;
+// Device address of the current device's scratch (looked up on the first call
+// per device); 0, or -1 after a HIP error whose text is copied into err.
+int noalloc_scratch(void **ptr, char *err, size_t err_len);
 
 struct BwdArgs {
     const void *q, *k, *v, *log_alpha, *beta;

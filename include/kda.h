@@ -19,7 +19,8 @@
  *  - All tensors are caller-owned DEVICE memory, contiguous and row-major with
  *    the shapes given below; base pointers must be 16-byte aligned, except beta
  *    and cu_seqlens, which need only their natural alignment.  The library never
- *    allocates, frees or retains a pointer, and keeps no global mutable state.
+ *    allocates, frees or retains a pointer, and keeps no global mutable state
+ *    apart from the device scratch of kda_chunk_fwd_noalloc.
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
  *    the legacy default stream).  KDA_OK means "validated and enqueued".
  *  - Every argument check runs on the host before any HIP call; on error nothing
@@ -130,6 +131,40 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
                            int32_t gate_dtype, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).
+ *
+ * Arguments, layouts, preconditions and results as for kda_chunk_fwd, without
+ * the workspace: the call uses a scratch array of 80 MiB that the library
+ * holds on each device it runs on (from the loading of its code object until
+ * the process ends; its address is looked up on the first call per device,
+ * with that device current).  It never calls hipMalloc, hipFree or any
+ * allocating routine.  The scratch is that of the CURRENT device, so `stream`
+ * and every tensor must belong to it.
+ *
+ * With bf16 I/O at d_k = d_v = 128 every batch shape runs the fused kernel
+ * (for packed batches and the input variants kda_chunk_fwd runs it too), whose
+ * workspace never exceeds the scratch; results agree with kda_chunk_fwd to the
+ * accuracy of either, and bitwise for packed batches.  fp32 I/O needs no
+ * scratch.  bf16 at d_k or d_v = 64 runs the two-pass forward of kda_chunk_fwd
+ * and is accepted while its workspace (kda_chunk_fwd_workspace_size) fits the
+ * scratch.
+ *
+ * Errors: as kda_chunk_fwd; KDA_ERR_WORKSPACE when the call would need more
+ * than the 80 MiB of scratch; KDA_ERR_HIP if the scratch's address cannot be
+ * found.  Every call on one device shares that device's scratch and leaves its
+ * contents behind (the forward reads none of it before writing it): calls that
+ * overlap in time on one device -- on different streams, or from different
+ * threads -- race and must not be issued; calls in order on one stream are safe.
+ */
+kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *log_alpha,
+                                   const void *beta, const float *h0, const int32_t *cu_seqlens,
+                                   int32_t num_seqs, void *o, float *h_T, int32_t B, int32_t T,
+                                   int32_t H, int32_t d_k, int32_t d_v, int32_t io_dtype,
+                                   int32_t gate_dtype, void *stream);
 
 /*
  * kda_decode_step -- one recurrent KDA step for B resident states (decode).

@@ -51,6 +51,10 @@ kda_status_t fwd(const Fwd &f) {
     return kda_chunk_fwd(f.q, f.k, f.v, f.la, f.beta, f.h0, f.cu, f.N, f.o, f.hT, f.B, f.T, f.H, f.dk, f.dv, f.io,
                          f.gt, f.ws, f.wsb, nullptr);
 }
+kda_status_t fwd_noalloc(const Fwd &f) {
+    return kda_chunk_fwd_noalloc(f.q, f.k, f.v, f.la, f.beta, f.h0, f.cu, f.N, f.o, f.hT, f.B, f.T, f.H, f.dk, f.dv,
+                                 f.io, f.gt, nullptr);
+}
 kda_status_t fwd_pro(const Fwd &f) {
     return kda_chunk_fwd_prologue(f.q, f.k, f.v, f.la, f.beta, f.lo, f.h0, f.cu, f.N, f.o, f.hT, f.B, f.T, f.H, f.dk,
                                   f.dv, f.io, f.gt, f.ws, f.wsb, nullptr);
@@ -165,6 +169,12 @@ void forward_cases() {
     EXPECT(fwd_gdn(with<Fwd>([](Fwd &a) { a.la = at(1); })), KDA_ERR_INVALID_ARGUMENT, 0);
     EXPECT(fwd_dec(with<Fwd>([](Fwd &a) { a.w = nullptr; })), KDA_ERR_INVALID_ARGUMENT, 0);
     EXPECT(fwd_dec(with<Fwd>([](Fwd &a) { a.w = at(1); })), KDA_ERR_INVALID_ARGUMENT, 0);
+
+    // the entry point without allocation: no workspace argument, a bounded scratch
+    EXPECT(fwd_noalloc(Fwd()), KDA_OK, 1);
+    EXPECT(fwd_noalloc(with<Fwd>([](Fwd &a) { a.q = at(4); })), KDA_ERR_INVALID_ARGUMENT, 0);
+    EXPECT(fwd_noalloc(with<Fwd>([](Fwd &a) { a.T = 1 << 20; a.H = 8; })), KDA_ERR_WORKSPACE, 0);
+    EXPECT(fwd_noalloc(with<Fwd>([](Fwd &a) { a.T = 1 << 20; a.H = 8; a.io = KDA_F32; })), KDA_OK, 1);
 
     // a HIP error: reported, with its text truncated to the buffer and NUL-terminated
     EXPECT(fwd(with<Fwd>([](Fwd &a) { a.H = 7; })), KDA_ERR_HIP, 1);

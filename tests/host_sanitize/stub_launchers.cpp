@@ -35,6 +35,11 @@ size_t chunk_fwd_workspace_bytes(const ChunkArgs &a) {
 }
 bool chunk_fwd_grids_fit(const ChunkArgs &a) { return a.num_seqs * (int64_t)a.H < ((int64_t)1 << 19); }
 bool decode_grids_fit(const DecodeArgs &a) { return a.B * (int64_t)a.H < ((int64_t)1 << 24); }
+int noalloc_scratch(void **ptr, char *, size_t) {
+    alignas(256) static unsigned char scratch_stub[256];
+    *ptr = scratch_stub;
+    return 0;
+}
 int launch_chunk_fwd(const ChunkArgs &a, void *, char *err, size_t err_len) { return record(a, err, err_len); }
 int launch_decode_step(const DecodeArgs &a, void *, char *err, size_t err_len) { return record(a, err, err_len); }
 

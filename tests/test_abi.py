@@ -142,6 +142,40 @@ def test_calls_beyond_the_launch_limits_are_refused(kda):
     assert bwd(lib, B=(1 << 15) - 8, H=32, T=64, ws=None, wsb=0) == 3
 
 
+def chunk_noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, la=P, beta=P, h0=None, cu=None, N=0, o=P, hT=P, B=1, T=4096, H=2,
+             dk=128, dv=128, io=1, gt=1)
+    a.update(kw)
+    return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["la"], a["beta"], a["h0"], a["cu"], a["N"],
+                                     a["o"], a["hT"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["io"],
+                                     a["gt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), 2), (dict(io=5), 2), (dict(B=0), 1), (dict(T=-1), 1), (dict(q=None), 1),
+    (dict(o=P + 8), 1), (dict(h0=P + 2), 1), (dict(beta=P + 1), 1), (dict(cu=P, N=2, B=2), 1),
+    (dict(N=3), 1), (dict(T=1 << 30, H=1 << 20), 1),
+])
+def test_chunk_fwd_noalloc_validates_like_chunk_fwd(kda, kw, code):
+    lib = kda.load_library()
+    assert chunk_noalloc(lib, **kw) == code == chunk(lib, **kw)
+
+
+def test_chunk_fwd_noalloc_rejects_calls_beyond_its_scratch(kda):
+    """bf16 at d = 64 runs the two-pass forward, whose per-chunk records for a
+    long batch exceed the 80 MiB scratch: KDA_ERR_WORKSPACE before any launch."""
+    lib = kda.load_library()
+    need = kda.kda_chunk_fwd_workspace_size(8, 8192, 32, 64, 64, 0, kda.KDA_BF16)
+    assert need > 80 << 20
+    assert chunk_noalloc(lib, B=8, T=8192, H=32, dk=64, dv=64) == 3
+    assert chunk_noalloc(lib, B=8, T=8192, H=32, dk=128, dv=64) == 3
+
+
+def test_chunk_fwd_noalloc_empty_without_state_is_noop(kda):
+    lib = kda.load_library()
+    assert chunk_noalloc(lib, T=0, q=None, k=None, v=None, la=None, beta=None, o=None, hT=None) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(dk=32), 2), (dict(dv=256), 2), (dict(B=0), 1), (dict(H=-1), 1), (dict(io=3), 2),
     (dict(S=None), 1), (dict(q=None), 1), (dict(o=None), 1), (dict(beta=None), 1),
