@@ -52,9 +52,16 @@
 // bitwise deterministic.
 //
 // Range: the anchored factors e^{+-(G-m)} reach e^{D/2}, D = max_c(-g_n[c]).
-// A chunk with D above about 160 (log2 units: kBwdMaxRange2) would overflow
-// fp32; the prep kernel flags it, and every gradient of that sequence and head
-// (dh0 included) comes out NaN: a loud result rather than a wrong one.
+// A chunk with D above about 159 nats (kBwdMaxRange2 in log2 units) would
+// overflow fp32, so the prep kernel runs it exact and marks its record: no
+// anchor (m = 0 for Q e^G and K e^G, m = g_n for K e^{g_n - G}, every factor at
+// most 1), M and P formed pair by pair with e^{G_r - G_i} <= 1, and in the
+// gradient kernel the intra-chunk parts of dq, dk and dG formed the same way:
+//     dq_r  += sum_{i<=r} dP[r,i] k_i E(r,i)
+//     dk_r  += sum_{i<r} dM[r,i] k_i E(r,i) + sum_{j>=r} (dP[j,r] q_j + dM[j,r] k_j) E(j,r)
+//     dG_r  += q_r (first sum) + k_r (second) - k_r (third)
+// per key channel, with E(r,i) = e^{G_r - G_i}.  The state passes need no
+// change: they read the factors e^m, e^{g_n}, e^{g_n-m} from the record.
 #include "kda_device.h"
 #include "kda_launch.h"
 #include "kda_plan.h"
@@ -150,7 +157,7 @@ template <int DK> struct BRec {
 
 struct BwdLayout {
     int64_t nch;                 // chunk slots (upper bound over sequences)
-    size_t plan, sflag, rec, sc, uc, dsc, duc, total;
+    size_t plan, rec, sc, uc, dsc, duc, total;
 };
 
 int64_t bwd_max_chunks(const BwdArgs &a) {
@@ -166,8 +173,7 @@ BwdLayout bwd_layout(const BwdArgs &a) {
     const size_t ch = (size_t)L.nch * a.H;
     const size_t recf = a.d_k == 128 ? rec_floats<128>() : rec_floats<64>();
     L.plan = 0;
-    L.sflag = plan_bytes(a.num_seqs);                        // [N, H] fp32: sequence out of range
-    L.rec = L.sflag + ((size_t)a.num_seqs * a.H * 4 + 255) / 256 * 256;
+    L.rec = plan_bytes(a.num_seqs);
     L.sc = L.rec + ch * recf * 4;
     L.uc = L.sc + ch * a.d_k * a.d_v * 4;
     L.dsc = L.uc + ch * kB * a.d_v * 4;
@@ -292,7 +298,8 @@ template <int DK> struct alignas(16) PrepBS {
     float beta[kB];
     float gv[kB];                            // log alpha per row (scalar-gate layouts)
     float part[kSeg][CH];                    // segment totals of the column scan
-    int flag;
+    float pre[256];                          // partial channel totals of the mode scan
+    int flag;                                // the chunk runs exact (see the header)
 };
 
 // GM: gate layout (per key channel, per (token, head), or none).
@@ -315,12 +322,37 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
 
     if (tid == 0) sm.flag = 0;
     if (tid < kB) sm.beta[tid] = tid < nv ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+    {   // the chunk's mode: exact once any key channel decays by more than kBwdMaxRange2
+        constexpr int NP = 256 / DK;         // threads per channel
+        const int c = tid % DK, p = tid / DK;
+        float l = 0.f;
+        if constexpr (GM == kGatePerChannel) {
+            for (int r = p; r < nv; r += NP) l += to_f32(log_alpha[((t0 + r) * H + h) * DK + c]);
+        } else if constexpr (GM == kGatePerHead) {
+            for (int r = p; r < nv; r += NP) l += to_f32(log_alpha[(t0 + r) * H + h]);
+        }
+        sm.pre[tid] = l;
+        __syncthreads();
+        if (tid < DK) {
+            float tot = 0.f;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) tot += sm.pre[tid + DK * i];
+            if (-tot * kBL2E > kBwdMaxRange2) sm.flag = 1;
+        }
+        __syncthreads();
+    }
+    const bool exact = sm.flag != 0;
     // Wave w accumulates tile (s, w) of P = lower(QA KI^T) and of
     // M = strictly-lower(KA KI^T) for block rows s >= w.
     constexpr int CH = S::CH, NH = DK / CH;
     f32x4_t accP[4], accM[4];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) accP[s4] = accM[s4] = zero4();
+    // exact mode: thread t owns the pairs (r, i <= r) numbered t + 256 j
+    constexpr int NPAIR = kB * (kB + 1) / 2, PPT = (NPAIR + 255) / 256;
+    float xP[PPT], xM[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) xP[j] = xM[j] = 0.f;
     const size_t base = ((size_t)t0 * H + h) * DK, pitch = (size_t)H * DK;
     for (int hf = 0; hf < NH; ++hf) {
         const int c0 = hf * CH;
@@ -348,7 +380,73 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
             }
         }
         __syncthreads();
-        {   // then the decayed operands in place
+        if (exact) {   // G in place of log alpha; then the pairs; then the operands without anchor
+            constexpr int PT = 256 / CH;
+            const int c = tid % CH, p = tid / CH;
+            float g2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < kSeg; ++i) g2 += sm.part[i][c];
+            for (int sg = p; sg < kSeg; sg += PT) {
+                float pre = 0.f;
+                for (int i = 0; i < sg; ++i) pre += sm.part[i][c];
+                const int r0 = sg * kSegRows, r1 = min(r0 + kSegRows, nv);
+                float l = 0.f;
+                for (int r = r0; r < r1; ++r) {
+                    l += (GM == kGatePerChannel ? sm.g.KI[r][c] : sm.gv[r]) * kBL2E;
+                    sm.g.KI[r][c] = pre + l;
+                }
+            }
+            __syncthreads();
+            // M[r,i] += sum_c k_rc k_ic e^{G_rc - G_ic} (i < r), P[r,i] += sum_c q_rc k_ic e^{...}
+            // (i <= r), over this pass's channels: every factor at most 1
+#pragma unroll
+            for (int j = 0; j < PPT; ++j) {
+                const int pi = tid + 256 * j;
+                int r = (int)((sqrtf(8.f * pi + 1.f) - 1.f) * 0.5f);
+                if ((r + 1) * (r + 2) / 2 <= pi) ++r;
+                if (r * (r + 1) / 2 > pi) --r;
+                const int i = pi - r * (r + 1) / 2;
+                if (pi < NPAIR && r < nv) {
+                    float sp = 0.f, sq = 0.f;
+                    for (int cc = 0; cc < CH; cc += 4) {
+                        const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(&sm.g.KI[r][cc]);
+                        const f32x4_t gi = *reinterpret_cast<const f32x4_t *>(&sm.g.KI[i][cc]);
+                        const f32x4_t kr = *reinterpret_cast<const f32x4_t *>(&sm.KA[r][c0 + cc]);
+                        const f32x4_t ki = *reinterpret_cast<const f32x4_t *>(&sm.KA[i][c0 + cc]);
+                        const f32x4_t qr = *reinterpret_cast<const f32x4_t *>(&sm.g.QA[r][cc]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float kk = ki[e] * __builtin_amdgcn_exp2f(gr[e] - gi[e]);
+                            sp += kr[e] * kk;
+                            sq += qr[e] * kk;
+                        }
+                    }
+                    xM[j] += i < r ? sp : 0.f;
+                    xP[j] += sq;
+                }
+            }
+            __syncthreads();
+            for (int sg = p; sg < kSeg; sg += PT) {
+                const int r0 = sg * kSegRows;
+                for (int r = r0; r < r0 + kSegRows; ++r) {
+                    float ea = 0.f, ei = 0.f;
+                    if (r < nv) {
+                        const float G = sm.g.KI[r][c];
+                        ea = __builtin_amdgcn_exp2f(G);
+                        ei = __builtin_amdgcn_exp2f(g2 - G);
+                    }
+                    const float kv = sm.KA[r][c0 + c];
+                    sm.g.QA[r][c] *= ea;
+                    sm.KA[r][c0 + c] = kv * ea;
+                    sm.g.KI[r][c] = kv * ei;
+                }
+            }
+            if (p == 0) {
+                rec[R::EM + c0 + c] = 1.f;
+                rec[R::EG + c0 + c] = __builtin_amdgcn_exp2f(g2);
+                rec[R::EGM + c0 + c] = 1.f;
+            }
+        } else {   // then the decayed operands in place
             constexpr int PT = 256 / CH;
             const int c = tid % CH, p = tid / CH;
             float g2 = 0.f;
@@ -371,7 +469,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
                 }
             }
             if (p == 0) {
-                if (-g2 > kBwdMaxRange2 || !(g2 == g2)) sm.flag = 1;
                 rec[R::EM + c0 + c] = __builtin_amdgcn_exp2f(m2);
                 rec[R::EG + c0 + c] = __builtin_amdgcn_exp2f(g2);
                 rec[R::EGM + c0 + c] = __builtin_amdgcn_exp2f(g2 - m2);
@@ -389,39 +486,72 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const IO *__restrict__ q,
         // the Gram products over these channels
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-            if (w <= s4) {
+            if (!exact && w <= s4) {
                 accP[s4] = mm<CH, S::HS, 1, 1, S::HS>(accP[s4], &sm.g.QA[16 * s4][0], &sm.g.KI[16 * w][0], lane);
                 accM[s4] = mm<CH, S::KS, 1, 1, S::HS>(accM[s4], &sm.KA[16 * s4][c0], &sm.g.KI[16 * w][0], lane);
             }
         }
     }
-    if (tid == 0) rec[R::FLAG] = sm.flag ? 1.f : 0.f;
-    // P and M to the record (tiles above the diagonal are zero)
-    f32x4_t mt[4];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const bool isM = s >= 4;
-        const int Rt = s & 3, It = w;
-        f32x4_t acc = isM ? accM[Rt] : accP[Rt];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * Rt + acc_row(lane, e), c = 16 * It + acc_col(lane);
-            const bool keep = isM ? r > c : r >= c;
-            acc[e] = keep ? acc[e] : 0.f;
-            rec[(isM ? R::M : R::P) + r * kB + c] = acc[e];
+    if (tid == 0) rec[R::FLAG] = exact ? 1.f : 0.f;
+    if (exact) {   // P and M from the pairs, zero above the diagonal; A = diag(beta) M
+        for (int i = tid; i < kB * kB; i += 256) {
+            if (i % kB > i / kB) {
+                rec[R::P + i] = 0.f;
+                rec[R::M + i] = 0.f;
+            }
         }
-        if (isM) mt[s & 3] = acc;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int pi = tid + 256 * j;
+            int r = (int)((sqrtf(8.f * pi + 1.f) - 1.f) * 0.5f);
+            if ((r + 1) * (r + 2) / 2 <= pi) ++r;
+            if (r * (r + 1) / 2 > pi) --r;
+            const int i = pi - r * (r + 1) / 2;
+            if (pi < NPAIR) {
+                rec[R::P + r * kB + i] = xP[j];
+                rec[R::M + r * kB + i] = xM[j];
+            }
+        }
+        __syncthreads();   // QA and KI no longer read
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int pi = tid + 256 * j;
+            int r = (int)((sqrtf(8.f * pi + 1.f) - 1.f) * 0.5f);
+            if ((r + 1) * (r + 2) / 2 <= pi) ++r;
+            if (r * (r + 1) / 2 > pi) --r;
+            const int i = pi - r * (r + 1) / 2;
+            if (pi < NPAIR) sm.t.A[r][i] = sm.beta[r] * xM[j];
+        }
+        for (int i = tid; i < kB * kB; i += 256)
+            if (i % kB > i / kB) sm.t.A[i / kB][i % kB] = 0.f;
     }
-    __syncthreads();   // QA and KI no longer read
-    // A = diag(beta) M into the inversion area; KA <- diag(beta) KA for W.
+    if (!exact) {   // P and M to the record (tiles above the diagonal are zero); A = diag(beta) M
+        f32x4_t mt[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 8; ++s) {
+            const bool isM = s >= 4;
+            const int Rt = s & 3, It = w;
+            f32x4_t acc = isM ? accM[Rt] : accP[Rt];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * s + acc_row(lane, e), c = 16 * w + acc_col(lane);
-            sm.t.A[r][c] = sm.beta[r] * mt[s][e];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * Rt + acc_row(lane, e), c = 16 * It + acc_col(lane);
+                const bool keep = isM ? r > c : r >= c;
+                acc[e] = keep ? acc[e] : 0.f;
+                rec[(isM ? R::M : R::P) + r * kB + c] = acc[e];
+            }
+            if (isM) mt[s & 3] = acc;
+        }
+        __syncthreads();   // QA and KI no longer read
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * s + acc_row(lane, e), c = 16 * w + acc_col(lane);
+                sm.t.A[r][c] = sm.beta[r] * mt[s][e];
+            }
         }
     }
+    // KA <- diag(beta) KA for W
     for (int i = tid; i < kB * DK; i += 256) {
         const int r = i / DK, c = i % DK;
         sm.KA[r][c] *= sm.beta[r];
@@ -593,7 +723,7 @@ __device__ __forceinline__ void fwd_state_body(FwdBS<DK, BV> &sm, int64_t id, co
                                                const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
                                                int64_t N, int64_t T, int H, int64_t nch,
                                                const float *__restrict__ recs, float *__restrict__ Sc,
-                                               float *__restrict__ Uc, float *__restrict__ sflag) {
+                                               float *__restrict__ Uc) {
     using R = BRec<DK>;
     using S = FwdBS<DK, BV>;
     constexpr int NVB = DV / BV;
@@ -642,7 +772,6 @@ __device__ __forceinline__ void fwd_state_body(FwdBS<DK, BV> &sm, int64_t id, co
         fetch_a(0);
         pK.load(rec_of(0) + R::KI, lt);
     }
-    float anybad = 0.f;
     for (int ci = 0; ci < nchunks; ++ci) {
         const int64_t slot = slot0 + ci;
         if (loader) {
@@ -656,7 +785,6 @@ __device__ __forceinline__ void fwd_state_body(FwdBS<DK, BV> &sm, int64_t id, co
         }
         __syncthreads();
         const float *em = sm.cv, *eg = sm.cv + DK, *egm = sm.cv + 2 * DK;
-        if (tid == 0) anybad = fmaxf(anybad, sm.cv[3 * DK]);
         if (loader) {
 #pragma unroll
             for (int s = 0; s < SK; ++s) put4<DK, S::KS>(&sm.KI[0][0], lt + kLT * s, pK.r[s]);
@@ -693,9 +821,6 @@ __device__ __forceinline__ void fwd_state_body(FwdBS<DK, BV> &sm, int64_t id, co
         }
         __syncthreads();
     }
-    // One flag per (sequence, head): any chunk out of range makes every
-    // gradient of the chain NaN (the gradient kernel reads it).
-    if (vb == 0 && tid == 0) sflag[n * H + h] = anybad;
 }
 
 // Reverse state-gradient pass: same roles, chunks in reverse order.
@@ -798,7 +923,6 @@ __device__ __forceinline__ void rev_state_body(RevBS<DK, BV> &sm, int64_t id, co
             if (ci > 0) pWQ.load(rec_of(ci - 1) + R::W, lt);
             block_out_t<kB, BV, S::CS, kLT>(dUc + ((size_t)h * nch + slot) * kB * DV + j0, DV, &sm.dUt[0][0], lt);
         } else {   // dS <- Diag(e^m) (QA^T dO - W^T dU) + Diag(e^{g_n}) dS
-            const bool bad = sm.cv[3 * DK] != 0.f;
 #pragma unroll
             for (int ct = w; ct < DK / 16; ct += 4) {
 #pragma unroll
@@ -809,8 +933,7 @@ __device__ __forceinline__ void rev_state_body(RevBS<DK, BV> &sm, int64_t id, co
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int c = 16 * ct + acc_row(lane, e), j = 16 * jt + acc_col(lane);
-                        const float x = em[c] * (a[e] - b[e]) + eg[c] * sm.dSt[j][c];
-                        sm.dSt[j][c] = bad ? __builtin_nanf("") : x;
+                        sm.dSt[j][c] = em[c] * (a[e] - b[e]) + eg[c] * sm.dSt[j][c];
                     }
                 }
             }
@@ -843,13 +966,13 @@ __global__ __launch_bounds__(kSP) void bwd_state_kernel(const IO *__restrict__ v
                                                         const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
                                                         int H, int64_t nch, const float *__restrict__ recs,
                                                         float *__restrict__ Sc, float *__restrict__ Uc,
-                                                        float *__restrict__ sflag, float *__restrict__ dSc,
+                                                        float *__restrict__ dSc,
                                                         float *__restrict__ dUc, float *__restrict__ dh0,
                                                         int64_t fwd_blocks) {
     __shared__ StateBS<DK, BV> sm;
     const int64_t id = blockIdx.x;
     if (id < fwd_blocks)
-        fwd_state_body<DK, DV, BV, IO, GT>(sm.f, id, v, beta, h0, cu, chunk_off, N, T, H, nch, recs, Sc, Uc, sflag);
+        fwd_state_body<DK, DV, BV, IO, GT>(sm.f, id, v, beta, h0, cu, chunk_off, N, T, H, nch, recs, Sc, Uc);
     else
         rev_state_body<DK, DV, BV, IO>(sm.r, id - fwd_blocks, d_o, d_hT, cu, chunk_off, N, T, H, nch, recs, dSc, dUc,
                                        dh0);
@@ -892,11 +1015,11 @@ template <int DK> struct alignas(16) GradBS {
 // the input prologue's fp32 mapped q and k are the inputs).
 template <int DK, int DV, typename IO, typename GT, typename KT, int GM>
 __global__ __launch_bounds__(512) void bwd_grad_kernel(
-    const KT *__restrict__ k, const IO *__restrict__ v, const GT *__restrict__ log_alpha,
+    const KT *__restrict__ q, const KT *__restrict__ k, const IO *__restrict__ v, const GT *__restrict__ log_alpha,
     const GT *__restrict__ beta, const IO *__restrict__ d_o, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int64_t N, int64_t T, int H, int64_t nch, const float *__restrict__ recs,
     const float *__restrict__ Sc, const float *__restrict__ Uc, const float *__restrict__ dSc,
-    const float *__restrict__ dUc, const float *__restrict__ sflag, KT *__restrict__ dq, KT *__restrict__ dk,
+    const float *__restrict__ dUc, KT *__restrict__ dq, KT *__restrict__ dk,
     IO *__restrict__ dv, GT *__restrict__ dla, GT *__restrict__ dbeta, const GT *__restrict__ wr,
     GT *__restrict__ dwr) {
     using R = BRec<DK>;
@@ -910,6 +1033,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const float *rec = recs + ((size_t)h * nch + chunk) * R::FLOATS;
     const size_t ch = (size_t)h * nch + chunk;
+    const bool exact = rec[R::FLAG] != 0.f;  // the chunk's mode, as the prep kernel chose it
     constexpr int NCT = DK / 16;             // key-column tiles
     constexpr int NOWN = 4 * NCT / 8;        // (row, key) tiles per wave
 
@@ -956,8 +1080,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             g2 += sm.part[i][c];
             if (i < sc_p) pre += sm.part[i][c];
         }
-        const float m2 = 0.5f * g2;
-        if (sc_p == 0) sm.m2[c] = m2;
+        // anchors: m = g_n / 2 for both factors; in exact mode none for K e^G and
+        // g_n for K e^{g_n - G} (m2 holds the latter)
+        const float m2 = exact ? 0.f : 0.5f * g2;
+        if (sc_p == 0) sm.m2[c] = exact ? g2 : m2;
         const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
         float l = 0.f;
         for (int r = r0; r < kSegRows + r0; ++r) {
@@ -982,7 +1108,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const float *uc = Uc + ch * kB * DV;
     const float *dsc = dSc + ch * DK * DV;
     const float *duc = dUc + ch * kB * DV;
-    const bool bad = sflag[n * H + h] != 0.f;
 
     // The next 16-column block's operands are requested (into registers) before
     // the current block's products.
@@ -1020,10 +1145,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 const int r = 16 * rt + acc_row(lane, e), j = acc_col(lane);
                 sm.r3.lp.dY[r][j] = a[e];
                 dbp[e] += a[e] * sm.r3.lp.V[r][j];
-                if (r < nv) {
-                    const float x = bad ? __builtin_nanf("") : (wr ? sm.wv[r] : sm.beta[r]) * a[e];
-                    dv[((t0 + r) * H + h) * DV + j0 + j] = from_f32<IO>(x);
-                }
+                if (r < nv) dv[((t0 + r) * H + h) * DV + j0 + j] = from_f32<IO>((wr ? sm.wv[r] : sm.beta[r]) * a[e]);
             }
         }
         __syncthreads();
@@ -1107,12 +1229,19 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             sm.r2.m.dM[r][c] = 0.f;
         }
     }
-    {
+    if (!exact) {   // the record's QA and KI
         Stage<kB, DK, 512, float> sq, si;
         sq.load(rec + R::QA, DK, kB, tid);
         si.load(rec + R::KI, DK, kB, tid);
         sq.template store<S::KS>(&sm.r3.pt.QA[0][0], tid);
         si.template store<S::KS>(&sm.r3.pt.KI[0][0], tid);
+    } else {        // exact mode: k and q themselves (QA and KI areas)
+        const size_t base = ((size_t)t0 * H + h) * DK, pitch = (size_t)H * DK;
+        Stage<kB, DK, 512, KT> sk, sq;
+        sk.load(k + base, pitch, nv, tid);
+        sq.load(q + base, pitch, nv, tid);
+        sk.template store<S::KS>(&sm.r3.pt.QA[0][0], tid);
+        sq.template store<S::KS>(&sm.r3.pt.KI[0][0], tid);
     }
     __syncthreads();
 
@@ -1122,7 +1251,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
         const float *dP = &sm.r2.m.T[0][0];
         const float *dM = &sm.r2.m.dM[0][0];
-        aQ[s] = mm<kB, S::CS, 1, S::KS, 1>(aQ[s], dP + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
+        if (!exact) aQ[s] = mm<kB, S::CS, 1, S::KS, 1>(aQ[s], dP + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {   // sum_c KA[r,c] (dY S'^T)[r,c] over this tile's 16 columns
             float x = sm.KA[16 * rt + acc_row(lane, e)][16 * ct + acc_col(lane)] * aK[s][e];
@@ -1132,29 +1261,37 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             x += __shfl_xor(x, 8);
             if ((lane & 15) == 0) sm.dbK[ct][16 * rt + acc_row(lane, e)] = x;
         }
-        f32x4_t t = zero4();
-        t = mm<kB, S::CS, 1, S::KS, 1>(t, dM + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
+        // the intra-chunk parts (dM KI, dP^T QA + dM^T KA) on the matrix cores;
+        // in exact mode they are formed pair by pair below
+        f32x4_t t = zero4(), u = zero4();
+        if (!exact) {
+            t = mm<kB, S::CS, 1, S::KS, 1>(t, dM + 16 * rt * S::CS, &sm.r3.pt.KI[0][16 * ct], lane);
+            u = mm<kB, 1, S::CS, S::KS, 1>(u, dP + 16 * rt, &sm.r3.pt.QA[0][16 * ct], lane);
+            u = mm<kB, 1, S::CS, S::KS, 1>(u, dM + 16 * rt, &sm.KA[0][16 * ct], lane);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) aK[s][e] = t[e] - sm.beta[16 * rt + acc_row(lane, e)] * aK[s][e];
-        f32x4_t u = zero4();
-        u = mm<kB, 1, S::CS, S::KS, 1>(u, dP + 16 * rt, &sm.r3.pt.QA[0][16 * ct], lane);
-        u = mm<kB, 1, S::CS, S::KS, 1>(u, dM + 16 * rt, &sm.KA[0][16 * ct], lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) u[e] += sm.egm[16 * ct + acc_col(lane)] * aB[s][e];
         aI[s] = u;
     }
-    __syncthreads();                         // dP, dM, QA, KI reads done
+    __syncthreads();                         // dP, dM, QA, KI reads done (exact mode: KA's)
 
-    if constexpr (GM == kGatePerChannel) {   // G (log2 units) again, into the freed area
+    // G (log2 units) again: into the freed area, or in exact mode (where dP and
+    // dM are still needed) over KA
+    float *Gp = exact ? &sm.KA[0][0] : &sm.r2.G2[0][0];
+    const int gl = exact ? S::KS : DK;
+    if constexpr (GM == kGatePerChannel) {
         Stage<kB, DK, 512, GT> sl;
         sl.load(log_alpha + ((size_t)t0 * H + h) * DK, (size_t)H * DK, nv, tid);
-        sl.template store<DK>(&sm.r2.G2[0][0], tid);
+        if (exact) sl.template store<S::KS>(Gp, tid);
+        else sl.template store<DK>(Gp, tid);
     }
     __syncthreads();
     if (sc_p < kSeg) {   // segment totals, then G in place (as above)
         const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
         float l = 0.f;
-        for (int r = r0; r < r1; ++r) l += (GM == kGatePerChannel ? sm.r2.G2[r][sc_c] : sm.gv[r]) * kBL2E;
+        for (int r = r0; r < r1; ++r) l += (GM == kGatePerChannel ? Gp[r * gl + sc_c] : sm.gv[r]) * kBL2E;
         sm.part[sc_p][sc_c] = l;
     }
     __syncthreads();
@@ -1166,31 +1303,89 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
         float l = 0.f;
         for (int r = r0; r < r1; ++r) {
-            l += (GM == kGatePerChannel ? sm.r2.G2[r][sc_c] : sm.gv[r]) * kBL2E;
-            sm.r2.G2[r][sc_c] = pre + l;
+            l += (GM == kGatePerChannel ? Gp[r * gl + sc_c] : sm.gv[r]) * kBL2E;
+            Gp[r * gl + sc_c] = pre + l;
         }
     }
     __syncthreads();
-    const float qnan = __builtin_nanf("");
+    if (!exact) {
 #pragma unroll
-    for (int s = 0; s < NOWN; ++s) {
-        const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
+        for (int s = 0; s < NOWN; ++s) {
+            const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rt + acc_row(lane, e), c = 16 * ct + acc_col(lane);
-            float dG = 0.f, kb = 0.f;
-            if (r < nv) {
-                const float g = sm.r2.G2[r][c] - sm.m2[c];
-                const float ea = __builtin_amdgcn_exp2f(g), ei = __builtin_amdgcn_exp2f(-g);
-                const size_t o = ((t0 + r) * H + h) * DK + c;
-                const float ki = sm.r3.pt.KI[r][c];
-                dq[o] = from_f32<KT>(bad ? qnan : aQ[s][e] * ea);
-                dk[o] = from_f32<KT>(bad ? qnan : aK[s][e] * ea + aI[s][e] * ei);
-                dG = aQ[s][e] * sm.r3.pt.QA[r][c] + aK[s][e] * sm.KA[r][c] - aI[s][e] * ki;
-                kb = aB[s][e] * ki;
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + acc_row(lane, e), c = 16 * ct + acc_col(lane);
+                float dG = 0.f, kb = 0.f;
+                if (r < nv) {
+                    const float g = sm.r2.G2[r][c] - sm.m2[c];
+                    const float ea = __builtin_amdgcn_exp2f(g), ei = __builtin_amdgcn_exp2f(-g);
+                    const size_t o = ((t0 + r) * H + h) * DK + c;
+                    const float ki = sm.r3.pt.KI[r][c];
+                    dq[o] = from_f32<KT>(aQ[s][e] * ea);
+                    dk[o] = from_f32<KT>(aK[s][e] * ea + aI[s][e] * ei);
+                    dG = aQ[s][e] * sm.r3.pt.QA[r][c] + aK[s][e] * sm.KA[r][c] - aI[s][e] * ki;
+                    kb = aB[s][e] * ki;
+                }
+                sm.r3.pt.QA[r][c] = dG;
+                sm.r3.pt.KI[r][c] = kb;
             }
-            sm.r3.pt.QA[r][c] = dG;
-            sm.r3.pt.KI[r][c] = kb;
+        }
+    } else {
+        // Exact mode.  With E(r, i) = e^{G_rc - G_ic} <= 1 (i <= r) per channel c,
+        // the intra-chunk products P = sum_c q_r k_i E and M = sum_c k_r k_i E
+        // (i < r) give, for this element (r, c):
+        //   dq_x  = sum_{i<=r} dP[r,i] k_i E(r,i)
+        //   dk_r  = sum_{i<r}  dM[r,i] k_i E(r,i)
+        //   dk_i  = sum_{j>=r} (dP[j,r] q_j + dM[j,r] k_j) E(j,r)
+        //   dG_x  = q_r dq_x + k_r dk_r - k_r dk_i
+        // and the state-side operands are Q e^G, K e^G, K e^{g_n - G} (no anchor).
+        const float *dP = &sm.r2.m.T[0][0];
+        const float *dM = &sm.r2.m.dM[0][0];
+        const float *kk = &sm.r3.pt.QA[0][0];
+        const float *qq = &sm.r3.pt.KI[0][0];
+        float xg[NOWN][4], xb[NOWN][4];
+#pragma unroll
+        for (int s = 0; s < NOWN; ++s) {
+            const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + acc_row(lane, e), c = 16 * ct + acc_col(lane);
+                float dG = 0.f, kb = 0.f;
+                if (r < nv) {
+                    const float Gr = Gp[r * gl + c];
+                    float dqx = 0.f, dkr = 0.f, dki = 0.f;
+                    for (int i = 0; i <= r; ++i) {
+                        const float ki = kk[i * S::KS + c] * __builtin_amdgcn_exp2f(Gr - Gp[i * gl + c]);
+                        dqx += dP[r * S::CS + i] * ki;
+                        dkr += dM[r * S::CS + i] * ki;
+                    }
+                    for (int j = r; j < nv; ++j) {
+                        const float x = dP[j * S::CS + r] * qq[j * S::KS + c] + dM[j * S::CS + r] * kk[j * S::KS + c];
+                        dki += x * __builtin_amdgcn_exp2f(Gp[j * gl + c] - Gr);
+                    }
+                    const float ea = __builtin_amdgcn_exp2f(Gr), ei = __builtin_amdgcn_exp2f(sm.m2[c] - Gr);
+                    const float kr = kk[r * S::KS + c], qr = qq[r * S::KS + c];
+                    const size_t o = ((t0 + r) * H + h) * DK + c;
+                    dq[o] = from_f32<KT>(aQ[s][e] * ea + dqx);
+                    dk[o] = from_f32<KT>(aK[s][e] * ea + aI[s][e] * ei + dkr + dki);
+                    dG = aQ[s][e] * (qr * ea) + aK[s][e] * (kr * ea) - aI[s][e] * (kr * ei) + qr * dqx + kr * dkr -
+                         kr * dki;
+                    kb = aB[s][e] * (kr * ei);
+                }
+                xg[s][e] = dG;
+                xb[s][e] = kb;
+            }
+        }
+        __syncthreads();   // k and q no longer read
+#pragma unroll
+        for (int s = 0; s < NOWN; ++s) {
+            const int ti = w + 8 * s, rt = ti / NCT, ct = ti % NCT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + acc_row(lane, e), c = 16 * ct + acc_col(lane);
+                sm.r3.pt.QA[r][c] = xg[s][e];
+                sm.r3.pt.KI[r][c] = xb[s][e];
+            }
         }
     }
     __syncthreads();
@@ -1212,11 +1407,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int i = 0; i < DK / 16; ++i) kx += sm.dbK[i][r];
         const float ma = (sm.dbA[0][r] + sm.dbA[1][r]) + (sm.dbA[2][r] + sm.dbA[3][r]);
         if (wr) {   // separate strengths: the V term is the write strength's, the rest the erase's
-            dwr[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : sm.dbr[r]);
-            dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : ma - kx);
+            dwr[(t0 + r) * H + h] = from_f32<GT>(sm.dbr[r]);
+            dbeta[(t0 + r) * H + h] = from_f32<GT>(ma - kx);
         } else {
             const float x = (sm.dbr[r] - kx) + ma;
-            dbeta[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
+            dbeta[(t0 + r) * H + h] = from_f32<GT>(x);
         }
     }
     __syncthreads();
@@ -1228,12 +1423,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             kbs += sm.partk[i][c];
             if (i > sc_p) suf += sm.part[i][c];
         }
-        const float dgn = sm.egm[c] * (sm.dgn1[c] + kbs);
+        // dg_n = e^{g_n} sum_j dS_next S + e^{g_n - m} sum_r (U dS_next^T) KI, with
+        // dgn1 = sum_j dS_next S' and S' = e^m S (m = 0 in exact mode)
+        const float dgn = exact ? sm.eg[c] * sm.dgn1[c] + sm.egm[c] * kbs : sm.egm[c] * (sm.dgn1[c] + kbs);
         const int r0 = sc_p * kSegRows, r1 = min(r0 + kSegRows, nv);
         float sacc = suf;
         for (int r = r1 - 1; r >= r0; --r) {
             sacc += sm.r3.pt.QA[r][c];
-            if constexpr (GM == kGatePerChannel) dla[((t0 + r) * H + h) * DK + c] = from_f32<GT>(bad ? qnan : sacc + dgn);
+            if constexpr (GM == kGatePerChannel) dla[((t0 + r) * H + h) * DK + c] = from_f32<GT>(sacc + dgn);
             else sm.r2.G2[r][c] = sacc + dgn;   // G2 is free: summed over the channels below
         }
     }
@@ -1249,7 +1446,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         x += __shfl_xor(x, 4);
         x += __shfl_xor(x, 2);
         x += __shfl_xor(x, 1);
-        if (sub == 0 && r < nv) dla[(t0 + r) * H + h] = from_f32<GT>(bad ? qnan : x);
+        if (sub == 0 && r < nv) dla[(t0 + r) * H + h] = from_f32<GT>(x);
     }
 }
 
@@ -1263,7 +1460,6 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     float *Uc = reinterpret_cast<float *>(ws + L.uc);
     float *dSc = reinterpret_cast<float *>(ws + L.dsc);
     float *dUc = reinterpret_cast<float *>(ws + L.duc);
-    float *sflag = reinterpret_cast<float *>(ws + L.sflag);
     const KT *q = static_cast<const KT *>(a.q), *k = static_cast<const KT *>(a.k);
     const IO *v = static_cast<const IO *>(a.v);
     const GT *la = static_cast<const GT *>(a.log_alpha), *be = static_cast<const GT *>(a.beta);
@@ -1281,12 +1477,12 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
         // the replay's U takes the write strengths (beta when they are tied)
         hipLaunchKernelGGL((bwd_state_kernel<DK, DV, kSBV, IO, GT>), dim3((unsigned)(fb + grid)), dim3(kSP), 0, st, v,
                            wr ? wr : be, a.h0, dO, a.d_hT, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs,
-                           Sc, Uc, sflag, dSc, dUc, a.dh0, fb);
+                           Sc, Uc, dSc, dUc, a.dh0, fb);
     }
     if (L.nch > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT, KT, GM>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st,
-                           k, v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, dSc,
-                           dUc, sflag, static_cast<KT *>(a.dq), static_cast<KT *>(a.dk), static_cast<IO *>(a.dv),
+                           q, k, v, la, be, dO, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc,
+                           dSc, dUc, static_cast<KT *>(a.dq), static_cast<KT *>(a.dk), static_cast<IO *>(a.dv),
                            static_cast<GT *>(a.dlog_alpha), static_cast<GT *>(a.dbeta), wr,
                            static_cast<GT *>(a.dw_write));
     return hipGetLastError();

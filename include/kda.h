@@ -331,11 +331,12 @@ size_t kda_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
  *
  * Outputs must not alias inputs or one another.  Numerics: every product and
  * accumulation is fp32 (fp32 matrix cores); outputs are rounded to their dtype
- * with round-to-nearest-even.  Range: a chunk in which some key channel decays
- * by more than about e^-160 in total (sum of log_alpha over the chunk below
- * about -160) is outside the fp32 range of the chunk factors; every gradient
- * of that sequence and head, grad_h0 included, is then NaN (never a silently
- * wrong value).  Deterministic: no atomics; the same inputs give
+ * with round-to-nearest-even.  Range: any finite log_alpha <= 0.  A chunk in
+ * which some key channel decays by more than about e^-159 in total (sum of
+ * log_alpha over the chunk below about -159) is outside the fp32 range of the
+ * anchored chunk factors and is computed exactly instead: the decay between
+ * each pair of its tokens is formed directly (a factor at most 1), more slowly
+ * but to the same accuracy.  Deterministic: no atomics; the same inputs give
  * bitwise identical outputs.
  */
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,

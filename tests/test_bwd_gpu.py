@@ -178,23 +178,47 @@ def test_bwd_bitwise_determinism(kda):
         assert torch.equal(x, y), name
 
 
-def test_bwd_out_of_range_chunk_is_nan(kda):
-    """A chunk whose key channel 0 decays by e^-192 (log_alpha = -3 on 64 tokens)
-    is outside the backward's fp32 range: every gradient of that sequence and
-    head is NaN; the other sequence is unaffected and matches the oracle."""
-    cfg = I.ChunkConfig("reset", "bf16", "bf16", H=2, dk=64, dv=64, h0=True, seed=3700)
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("case", ["one channel -3", "one channel -30", "all channels -30", "single tokens -30"])
+def test_bwd_strong_decay_chunks(kda, case, io):
+    """Chunks whose decay leaves the fp32 range of the anchored factors (a key
+    channel decaying by more than about e^-159 within 64 tokens) run exact:
+    pairwise decay factors e^{G_r - G_i} <= 1 and state-side operands without
+    anchor.  Every gradient still matches the oracle, for log alpha down to
+    -30 per token: on one channel over a whole chunk (-3: e^-192 in total;
+    -30: e^-1920), on every channel of a head over a chunk, and at single
+    tokens on every channel and head."""
+    cfg = I.ChunkConfig("strong-bwd", io, io, H=2, dk=64, dv=64, h0=True, seed=3700)
     d = I.make_chunk_inputs(cfg, lengths=[192, 100])
     la = d["log_alpha"].clone()
-    la[64:128, 0, 0] = -3.0
-    d["log_alpha"] = la
+    if case == "one channel -3":
+        la[64:128, 0, 0] = -3.0
+    elif case == "one channel -30":
+        la[64:128, 0, 0] = -30.0
+    elif case == "all channels -30":
+        la[64:128, 1, :] = -30.0
+    else:
+        la[[5, 70, 200, 250]] = -30.0
+    d["log_alpha"] = la.to(d["log_alpha"].dtype)
     go, ghT = I.make_upstream_grads(d, 3701)
     out = run_bwd(kda, d, go, ghT)
     for name, g in zip(NAMES, out):
-        bad = g[0, 0] if name == "dh0" else g[:192, 0]
-        assert torch.isnan(bad.float()).all(), name
-        ok = g[0, 1] if name == "dh0" else g[:192, 1]
-        assert torch.isfinite(ok.float()).all(), name
-    check(kda, d, "bf16", go, ghT, seqs=[1], what="other sequence")
+        assert torch.isfinite(g.float()).all(), name
+    check(kda, d, io, go, ghT, what="strong decay (%s) %s" % (case, io))
+
+
+def test_bwd_strong_decay_d128_varlen(kda):
+    """The same at d_k = d_v = 128 in a ragged packed batch: log alpha = -30 on
+    a quarter of the key channels over a whole chunk of one sequence, and -5 on
+    one channel over most of another."""
+    cfg = I.ChunkConfig("strong-bwd-128", "bf16", "bf16", H=2, dk=128, dv=128, h0=True, seed=3710)
+    d = I.make_chunk_inputs(cfg, lengths=[130, 64, 1, 260])
+    la = d["log_alpha"].clone()
+    la[0:64, 1, 0:32] = -30.0
+    la[200:380, 0, 77] = -5.0
+    d["log_alpha"] = la
+    go, ghT = I.make_upstream_grads(d, 3711)
+    check(kda, d, "bf16", go, ghT, what="strong decay d128 varlen")
 
 
 def test_bwd_matches_forward_directional_derivative(kda):
@@ -405,17 +429,21 @@ def pro_bwd_check(kda, d, io, lo, go, ghT, eps_rows=(), heads=None, what=""):
 
 @pytest.mark.parametrize("io,dk,dv", [("bf16", 128, 128), ("bf16", 64, 128), ("f32", 128, 64), ("f32", 64, 64)])
 def test_prologue_bwd_ragged(kda, io, dk, dv):
-    """Ragged packed sequences with h0 and grad_hT, gate pre-activations N(0, 2^2)
-    with the floor at -3 (about 7% of gates on it), a zero query row and a zero
-    key row (the eps branch)."""
+    """Ragged packed sequences with h0 and grad_hT, gate pre-activations N(0, 2^2),
+    the floor at -20 with gates driven onto it over whole chunks (as the
+    forward's prologue tests do: those chunks run exact), a zero query row and
+    a zero key row (the eps branch)."""
     cfg = I.ChunkConfig("pro-bwd", io, io, H=3, dk=dk, dv=dv, h0=True, seed=4500 + dk + dv)
     d = I.make_chunk_raw_inputs(cfg, lengths=[300, 64, 130, 1, 200, 0], gate_scale=2.0)
-    q, k = d["q_raw"].clone(), d["k_raw"].clone()
+    q, k, a = d["q_raw"].clone(), d["k_raw"].clone(), d["gate_pre"].clone()
     q[5, 0] = 0.0
     k[7, 1] = 0.0
-    d["q_raw"], d["k_raw"] = q, k
+    a[10] = 60.0                  # -softplus(60) = -60, floored to -20 on every channel
+    a[70:75] = 40.0
+    a[300:364, 1, :3] = 25.0      # sequence 1, head 1: a whole chunk on the floor
+    d["q_raw"], d["k_raw"], d["gate_pre"] = q, k, a.to(d["gate_pre"].dtype)
     go, ghT = I.make_upstream_grads(dict(d, q=d["q_raw"]), 4501)
-    pro_bwd_check(kda, d, io, -3.0, go, ghT, eps_rows=[(5, 0), (7, 1)],
+    pro_bwd_check(kda, d, io, -20.0, go, ghT, eps_rows=[(5, 0), (7, 1)],
                   what="prologue bwd %s %dx%d" % (io, dk, dv))
 
 
