@@ -244,16 +244,28 @@ def main():
     alg_f = chunk_alg_flops(tok_heads, dk, dv)
     digest = source_digest(CHUNK_SOURCES)
     traffic = load_traffic("chunk_fwd_prefill_h32_t65536_traffic.json", digest)
-    # one kda_chunk_fwd call = chunk_prep_kernel + chunk_state_kernel on one stream
-    roof = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+    counters = load_mfma_counters("chunk_fwd_prefill_h32_t65536_traffic.json", digest)
+    # one kda_chunk_fwd call = chunk_prep_kernel + chunk_state_kernel on one stream.
+    # The metric is matrix-core utilisation: algorithmic flops per call over the
+    # time per call, against the bf16 dense peak.  By arithmetic intensity
+    # (about 110 flop/B against the chip's 312) the bytes bind first: the HBM
+    # view is kept alongside.  "traffic" is FETCH_SIZE + WRITE_SIZE per call
+    # (bytes leaving L2, Infinity Cache hits included) scaled by a plain copy.
+    roof = {"bound": "mfma", "achieved": alg_f / (ms * 1e-3) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "traffic": traffic,
+            "traffic_counted": "FETCH_SIZE + WRITE_SIZE (L2 misses, Infinity Cache hits included), bytes per call",
+            "counter_busy_frac": None if counters is None else counters["busy_pct"] / 100.0,
             "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,128,bf16,bf16,false,0> + "
                       "chunk_state_kernel<128,128,16,bf16,bf16,false,0>",
-            "alg_bytes_per_launch": alg_b}
+            "alg_flops_per_launch": alg_f}
+    hbm = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg_b,
+           "floor_ms": alg_b / (HBM_PEAK_GBS * 1e9) * 1e3}
     mfma = {"alg_flops_per_launch": alg_f, "achieved_tflops": alg_f / (ms * 1e-3) / 1e12,
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
             "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-            "counters": load_mfma_counters("chunk_fwd_prefill_h32_t65536_traffic.json", digest)}
+            "counters": counters}
 
     out = {"metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -262,7 +274,7 @@ def main():
                                   "log_alpha=log U(0.5,0.9999)",
                       "B": 1, "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": 64,
                       "parallelism": "single GPU"},
-           "roofline": roof, "mfma": mfma, "source_digest": digest}
+           "roofline": roof, "hbm": hbm, "mfma": mfma, "source_digest": digest}
 
     # ---------------- the same prefill on raw projections (fused input prologue)
     if not args.no_prologue:
@@ -344,7 +356,12 @@ def main():
     # ---------------- the other prefill workloads: short sequence and packed batch
     if not args.no_other:
         other = {}
-        for key, ocfg in (("c0", I.C0), ("c1", I.C1), ("c2", I.C2)):
+        profile_name = {"c0": "chunk_fwd_fp32_h2_t256_d64", "c1": "chunk_fwd_h16_t4096",
+                        "c2": "chunk_fwd_varlen_n32_h32", "c1_fp32": "chunk_fwd_fp32_h16_t4096_d128"}
+        # c1's shape with fp32 I/O at d = 128: the chunkwise fp32 forward
+        c1_f32 = I.ChunkConfig("fp32 B=1 H=16 T=4096 d=128 (c1's shape and draws in fp32)", "f32", "f32",
+                               H=16, dk=128, dv=128, T=4096, seed=I.C1.seed)
+        for key, ocfg in (("c0", I.C0), ("c1", I.C1), ("c2", I.C2), ("c1_fp32", c1_f32)):
             dd = I.make_chunk_inputs(ocfg, device=dev)
             Tt, Hh = dd["q"].shape[0], dd["q"].shape[1]
             odk, odv = dd["q"].shape[2], dd["v"].shape[2]
@@ -364,7 +381,8 @@ def main():
                           "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob,
                           "alg_flops_per_launch": of,
                           "mfma_frac": of / (oms * 1e-3) / 1e12 /
-                          (BF16_MFMA_PEAK_TFLOPS if dd["q"].dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS)}
+                          (BF16_MFMA_PEAK_TFLOPS if dd["q"].dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS),
+                          "traffic": load_traffic(profile_name[key] + "_traffic.json", digest)}
             if key == "c2" and not args.no_backward:
                 # the packed batch's gradients (grad_o ~ N(0,1), grad_hT ~ N(0, 0.1^2))
                 go2, ghT2 = I.make_upstream_grads(dd, 3450, device=dev)

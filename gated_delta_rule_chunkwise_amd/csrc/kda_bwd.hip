@@ -723,7 +723,7 @@ __device__ __forceinline__ void fwd_state_body(FwdBS<DK, BV> &sm, int64_t id, co
                                                const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
                                                int64_t N, int64_t T, int H, int64_t nch,
                                                const float *__restrict__ recs, float *__restrict__ Sc,
-                                               float *__restrict__ Uc) {
+                                               float *__restrict__ Uc, float *__restrict__ hT) {
     using R = BRec<DK>;
     using S = FwdBS<DK, BV>;
     constexpr int NVB = DV / BV;
@@ -820,6 +820,12 @@ __device__ __forceinline__ void fwd_state_body(FwdBS<DK, BV> &sm, int64_t id, co
             }
         }
         __syncthreads();
+    }
+    if (hT) {   // the state after the last chunk (the forward's h_T)
+        for (int i = tid; i < DK * BV; i += kSP) {
+            const int c = i / BV, j = i % BV;
+            hT[(((size_t)n * H + h) * DK + c) * DV + j0 + j] = sm.St[j][c];
+        }
     }
 }
 
@@ -968,11 +974,11 @@ __global__ __launch_bounds__(kSP) void bwd_state_kernel(const IO *__restrict__ v
                                                         float *__restrict__ Sc, float *__restrict__ Uc,
                                                         float *__restrict__ dSc,
                                                         float *__restrict__ dUc, float *__restrict__ dh0,
-                                                        int64_t fwd_blocks) {
+                                                        int64_t fwd_blocks, float *__restrict__ hT) {
     __shared__ StateBS<DK, BV> sm;
     const int64_t id = blockIdx.x;
     if (id < fwd_blocks)
-        fwd_state_body<DK, DV, BV, IO, GT>(sm.f, id, v, beta, h0, cu, chunk_off, N, T, H, nch, recs, Sc, Uc);
+        fwd_state_body<DK, DV, BV, IO, GT>(sm.f, id, v, beta, h0, cu, chunk_off, N, T, H, nch, recs, Sc, Uc, hT);
     else
         rev_state_body<DK, DV, BV, IO>(sm.r, id - fwd_blocks, d_o, d_hT, cu, chunk_off, N, T, H, nch, recs, dSc, dUc,
                                        dh0);
@@ -1477,7 +1483,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
         // the replay's U takes the write strengths (beta when they are tied)
         hipLaunchKernelGGL((bwd_state_kernel<DK, DV, kSBV, IO, GT>), dim3((unsigned)(fb + grid)), dim3(kSP), 0, st, v,
                            wr ? wr : be, a.h0, dO, a.d_hT, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs,
-                           Sc, Uc, dSc, dUc, a.dh0, fb);
+                           Sc, Uc, dSc, dUc, a.dh0, fb, nullptr);
     }
     if (L.nch > 0 && a.total_tokens > 0)
         hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, IO, GT, KT, GM>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(512), 0, st,
@@ -1635,9 +1641,201 @@ hipError_t launch_pro_maps_t(const BwdArgs &a, float lo, uint8_t *x, const ProLa
 }
 
 
+// ----------------------------------------------------------------------------
+// fp32 forward at d_k = 128, chunkwise on the fp32 matrix cores.  The backward's
+// prep kernel writes each chunk-head's record (QA, KI, W, T, P, the factors;
+// exact mode beyond the anchored range), its forward replay walks each chain
+// and stores every chunk's start state S and U (and h_T), and the output kernel
+// below forms every chunk's read-out in parallel:
+//     O = QA Diag(e^m) S + P U
+// (the chunk form of section 3.1 of the KimiLinear article; m = 0 in exact
+// mode).  Every product is fp32.
+template <int DK> struct alignas(16) OutBS {
+    static constexpr int KS = DK + 4, CS = kB + 4, BS = 32 + 4;
+    float QA[kB][KS];                        // QA Diag(e^m)
+    float P[kB][CS];
+    float S[DK][BS];                         // 32 columns of the chunk's start state
+    float U[kB][BS];                         // the same 32 columns of U
+};
+
+template <int DK, int DV, typename IO>
+__global__ __launch_bounds__(256) void fwd_out_kernel(const int32_t *__restrict__ cu,
+                                                      const int32_t *__restrict__ chunk_off, int64_t N, int64_t T,
+                                                      int H, int64_t nch, const float *__restrict__ recs,
+                                                      const float *__restrict__ Sc, const float *__restrict__ Uc,
+                                                      IO *__restrict__ o) {
+    using R = BRec<DK>;
+    using S = OutBS<DK>;
+    __shared__ S sm;
+    const int64_t chunk = blockIdx.x;
+    const int h = blockIdx.y;
+    int64_t n, t0;
+    int nv;
+    if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const size_t ch = (size_t)h * nch + chunk;
+    const float *rec = recs + ch * R::FLOATS;
+    for (int i = tid; i < kB * DK / 4; i += 256) {
+        const int r = i / (DK / 4), c = (i % (DK / 4)) * 4;
+        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(rec + R::QA + r * DK + c);
+        const f32x4_t e = *reinterpret_cast<const f32x4_t *>(rec + R::EM + c);
+        *reinterpret_cast<f32x4_t *>(&sm.QA[r][c]) = x * e;
+    }
+    for (int i = tid; i < kB * kB / 4; i += 256) {
+        const int r = i / (kB / 4), c = (i % (kB / 4)) * 4;
+        *reinterpret_cast<f32x4_t *>(&sm.P[r][c]) = *reinterpret_cast<const f32x4_t *>(rec + R::P + r * kB + c);
+    }
+    const float *sc = Sc + ch * DK * DV;
+    const float *uc = Uc + ch * kB * DV;
+    for (int j0 = 0; j0 < DV; j0 += 32) {
+        __syncthreads();                     // the previous block's reads are done
+        for (int i = tid; i < DK * 8; i += 256) {
+            const int r = i / 8, c = (i % 8) * 4;
+            *reinterpret_cast<f32x4_t *>(&sm.S[r][c]) =
+                *reinterpret_cast<const f32x4_t *>(sc + (size_t)r * DV + j0 + c);
+        }
+        for (int i = tid; i < kB * 8; i += 256) {
+            const int r = i / 8, c = (i % 8) * 4;
+            *reinterpret_cast<f32x4_t *>(&sm.U[r][c]) =
+                *reinterpret_cast<const f32x4_t *>(uc + (size_t)r * DV + j0 + c);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {     // wave w: row tile w
+            f32x4_t acc = zero4();
+            acc = mm<DK, S::KS, 1, S::BS, 1>(acc, &sm.QA[16 * w][0], &sm.S[0][16 * ct], lane);
+            acc = mm<kB, S::CS, 1, S::BS, 1>(acc, &sm.P[16 * w][0], &sm.U[0][16 * ct], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + acc_row(lane, e), j = j0 + 16 * ct + acc_col(lane);
+                if (r < nv) o[((t0 + r) * H + h) * DV + j] = from_f32<IO>(acc[e]);
+            }
+        }
+    }
+}
+
+// Workspace of the fp32 forward: the varlen plan, the records, S and U per
+// chunk-head, and the input prologue's mapped q, k, log alpha (fp32 [rows][d_k])
+// and beta and inverse norms (fp32 [rows]), always reserved since the size
+// query does not know the entry point.
+struct F32FwdLayout {
+    int64_t nch;
+    size_t plan, rec, sc, uc, qh, kh, la, be, inq, ink, total;
+};
+F32FwdLayout f32_fwd_layout(const ChunkArgs &a) {
+    F32FwdLayout L = {};
+    if (a.total_tokens <= 0) return L;       // no tokens: h_T = h0, no workspace
+    L.nch = a.varlen ? (a.total_tokens + kB - 1) / kB + a.num_seqs : a.num_seqs * ((a.seq_len + kB - 1) / kB);
+    const size_t ch = (size_t)L.nch * a.H;
+    const size_t rows = (size_t)a.total_tokens * a.H;
+    const size_t big = (rows * a.d_k * 4 + 255) / 256 * 256, small = (rows * 4 + 255) / 256 * 256;
+    L.plan = 0;
+    L.rec = plan_bytes(a.num_seqs);
+    L.sc = L.rec + ch * rec_floats<128>() * 4;
+    L.uc = L.sc + ch * a.d_k * a.d_v * 4;
+    L.qh = L.uc + ch * kB * a.d_v * 4;
+    L.kh = L.qh + big;
+    L.la = L.kh + big;
+    L.be = L.la + big;
+    L.inq = L.be + small;
+    L.ink = L.inq + small;
+    L.total = L.ink + small;
+    return L;
+}
+
+// h_T = h0 (or zeros) for a call without tokens.
+__global__ __launch_bounds__(256) void state_pass_kernel(const float *__restrict__ h0, float *__restrict__ h_T,
+                                                         int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) h_T[i] = h0 ? h0[i] : 0.f;
+}
+
+template <int DV, typename GT, int GM>
+hipError_t launch_f32_fwd_t(const ChunkArgs &a, const float *q, const float *k, const GT *la, const GT *be,
+                            hipStream_t st) {
+    constexpr int DK = 128;
+    const F32FwdLayout L = f32_fwd_layout(a);
+    if (a.total_tokens <= 0) {
+        const int64_t n = a.num_seqs * a.H * (int64_t)DK * DV;
+        if (a.h_T && n > 0)
+            hipLaunchKernelGGL(state_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.h0, a.h_T, n);
+        return hipGetLastError();
+    }
+    uint8_t *ws = static_cast<uint8_t *>(a.workspace);
+    int32_t *chunk_off = a.varlen ? reinterpret_cast<int32_t *>(ws + L.plan) : nullptr;
+    float *recs = reinterpret_cast<float *>(ws + L.rec);
+    float *Sc = reinterpret_cast<float *>(ws + L.sc);
+    float *Uc = reinterpret_cast<float *>(ws + L.uc);
+    const GT *wr = static_cast<const GT *>(a.w_write);
+    const int64_t T = a.seq_len;
+    const bool tokens = a.total_tokens > 0 && L.nch > 0;
+    if (a.varlen)
+        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.num_seqs, chunk_off);
+    if (tokens)
+        hipLaunchKernelGGL((bwd_prep_kernel<DK, float, GT, GM>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st,
+                           q, k, la, be, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs);
+    const int64_t grid = chain_grid(a.num_seqs * a.H, DV / kSBV);
+    if (grid > 0)   // the replay only (every block id below fwd_blocks)
+        hipLaunchKernelGGL((bwd_state_kernel<DK, DV, kSBV, float, GT>), dim3((unsigned)grid), dim3(kSP), 0, st,
+                           static_cast<const float *>(a.v), wr ? wr : be, a.h0, (const float *)nullptr,
+                           (const float *)nullptr, a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc,
+                           (float *)nullptr, (float *)nullptr, (float *)nullptr, grid, a.h_T);
+    if (tokens)
+        hipLaunchKernelGGL((fwd_out_kernel<DK, DV, float>), dim3((unsigned)L.nch, (unsigned)a.H), dim3(256), 0, st,
+                           a.cu_seqlens, chunk_off, a.num_seqs, T, a.H, L.nch, recs, Sc, Uc, static_cast<float *>(a.o));
+    return hipGetLastError();
+}
+
+template <int DV, typename GT>
+hipError_t launch_f32_fwd_gate(const ChunkArgs &a, hipStream_t st) {
+    const float *q = static_cast<const float *>(a.q), *k = static_cast<const float *>(a.k);
+    const GT *la = static_cast<const GT *>(a.log_alpha), *be = static_cast<const GT *>(a.beta);
+    if (a.gate_mode == kGatePerHead) return launch_f32_fwd_t<DV, GT, kGatePerHead>(a, q, k, la, be, st);
+    if (a.gate_mode == kGateNone) return launch_f32_fwd_t<DV, GT, kGateNone>(a, q, k, la, be, st);
+    return launch_f32_fwd_t<DV, GT, kGatePerChannel>(a, q, k, la, be, st);
+}
+
+// Raw projections: mapped (q/|q|, k/|k|, floored -softplus gate, sigmoid beta)
+// into the workspace first, then the forward on the mapped fp32 values.
+template <int DV, typename GT>
+hipError_t launch_f32_fwd_prologue(const ChunkArgs &a, hipStream_t st) {
+    const F32FwdLayout L = f32_fwd_layout(a);
+    uint8_t *ws = static_cast<uint8_t *>(a.workspace);
+    auto at = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+    const int64_t rows = a.total_tokens * a.H;
+    if (rows > 0)
+        hipLaunchKernelGGL((pro_map_kernel<128, float, GT>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                           static_cast<const float *>(a.q), static_cast<const float *>(a.k),
+                           static_cast<const GT *>(a.log_alpha), static_cast<const GT *>(a.beta), rows,
+                           a.log_alpha_min, at(L.qh), at(L.kh), at(L.la), at(L.be), at(L.inq), at(L.ink));
+    return launch_f32_fwd_t<DV, float, kGatePerChannel>(a, at(L.qh), at(L.kh), at(L.la), at(L.be), st);
+}
+
+template <int DV>
+hipError_t launch_f32_fwd_dv(const ChunkArgs &a, hipStream_t st) {
+    if (a.prologue)
+        return a.gate_bf16 ? launch_f32_fwd_prologue<DV, bf16_t>(a, st) : launch_f32_fwd_prologue<DV, float>(a, st);
+    return a.gate_bf16 ? launch_f32_fwd_gate<DV, bf16_t>(a, st) : launch_f32_fwd_gate<DV, float>(a, st);
+}
+
 }  // namespace
 
 size_t chunk_bwd_workspace_bytes(const BwdArgs &a) { return bwd_layout(a).total; }
+
+size_t f32_fwd_workspace_bytes(const ChunkArgs &a) { return f32_fwd_layout(a).total; }
+
+// The prep and output kernels run (chunks, heads) grids of 256 threads, the
+// replay the padded chains, the prologue's map four rows per workgroup.
+bool f32_fwd_grids_fit(const ChunkArgs &a) {
+    const F32FwdLayout L = f32_fwd_layout(a);
+    return grid_fits(L.nch, 256) && a.H <= kMaxGridY && grid_fits(chain_grid(a.num_seqs * a.H, a.d_v / kSBV), kSP) &&
+           grid_fits((a.total_tokens * a.H + 3) / 4, 256) &&
+           grid_fits((a.num_seqs * a.H * a.d_k * (int64_t)a.d_v + 255) / 256, 256);
+}
+
+hipError_t launch_f32_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
+    return a.d_v == 128 ? launch_f32_fwd_dv<128>(a, st) : launch_f32_fwd_dv<64>(a, st);
+}
 
 // Scalar gates run the same kernels with the gate layout as a compile-time
 // parameter: the gate is read once per (token, head), and dlog_alpha is the

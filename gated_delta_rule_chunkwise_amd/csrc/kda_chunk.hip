@@ -1,6 +1,7 @@
 // kda_chunk.hip -- chunkwise KDA forward (prefill), one fused kernel.
-// This kernel serves fp32 I/O; bf16 I/O runs the prep + state kernels of
-// kda_chunk2.hip (LIBKDA_FUSED=1 selects this one for comparison).
+// This kernel serves fp32 I/O at d_k = 64 (and a call without tokens that only
+// passes h0 on to h_T); bf16 I/O runs the kernels of kda_chunk2.hip and
+// kda_fused.hip, fp32 I/O at d_k = 128 those of kda_bwd.hip.
 //
 // Method (KimiLinear article, section 3.1: intra-chunk part by matrix products,
 // inter-chunk part carried by the recurrent state; Kimi Linear abstract on the
@@ -38,9 +39,9 @@
 // Precision: products that feed the recurrence (T, X, U, P) use hi/lo-split
 // bf16 operands (hi*hi + hi*lo + lo*hi on the matrix cores).  With bf16 I/O the
 // decayed key/query operands and Diag(e^m) S are single bf16; with fp32 I/O they
-// are split too (SPLIT instances).  For fp32 I/O with d_k = 128 the split
-// operands do not fit in LDS, and that instance runs the exact token-by-token
-// update for every chunk.
+// are split too (SPLIT instances).  fp32 I/O at d_k = 128 does not come here:
+// the split operands would not fit in LDS, and it runs chunkwise on the fp32
+// matrix cores instead (kda_bwd.hip).
 #include "kda_chunk_common.h"
 #include "kda_launch.h"
 
@@ -85,14 +86,9 @@ struct alignas(16) ChunkSmem {
     float W8[4][8][8];                         // 8x8 merge scratch, per wave
 };
 
-template <int BV>
-struct alignas(16) ExactSmem {
-    float red[4][TokenRed<BV>::N];
-};
-
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
 // (input prologue; lo is the floor of log alpha).
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM, bool DEC>
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
@@ -104,8 +100,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     constexpr int NT = BV / 16;     // 16-column tiles per block
     constexpr int STW = StateTiles<DK, BV>::STW;
     typedef ChunkSmem<DK, BV, SPLIT> Sm;
-    typedef typename std::conditional<EXACT, ExactSmem<BV>, Sm>::type Smem;
-    __shared__ Smem smem;
+    __shared__ Sm smem;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
@@ -140,11 +135,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
     }
 
-    if constexpr (EXACT) {
-        for (int64_t tk = bos; tk < eos; ++tk)
-            token_update<DK, BV, IO, GT, PRO, GM, DEC>(Sacc, smem.red, q, k, v, log_alpha, beta, wr, o, tk, H, h, DV,
-                                                       col0, w, lg, lr, lo);
-    } else {
+    {
         Sm &sm = smem;
         // Upper blocks of T and P are never written: zero them once.
         for (int idx = tid; idx < 2 * kC * Sm::TS; idx += kThreads) {
@@ -597,27 +588,31 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     }
 }
 
-template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool EXACT, bool PRO, int GM, bool DEC>
+template <int DK, int BV, typename IO, typename GT, bool SPLIT, bool PRO, int GM, bool DEC>
 hipError_t launch_t(const ChunkArgs &a, hipStream_t st) {
     const int64_t chains = a.num_seqs * (int64_t)a.H;
     const int64_t nwg = chains * (a.d_v / BV);
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, EXACT, PRO, GM, DEC>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, BV, IO, GT, SPLIT, PRO, GM, DEC>), dim3((unsigned)nwg),
                        dim3(kThreads), 0, st, (const IO *)a.q, (const IO *)a.k, (const IO *)a.v,
                        (const GT *)a.log_alpha, (const GT *)a.beta, (const GT *)a.w_write, a.h0, a.cu_seqlens, (IO *)a.o, a.h_T, a.seq_len, a.H, a.d_v, chains,
                        a.log_alpha_min);
     return hipGetLastError();
 }
 
-// bf16 I/O: single-bf16 decayed operands.  fp32 I/O: split operands (d_k = 64)
-// or the exact token path (d_k = 128).
+// bf16 I/O: single-bf16 decayed operands.  fp32 I/O: split operands (d_k = 64;
+// at d_k = 128 the fp32 forward runs chunkwise on the fp32 matrix cores, in
+// kda_bwd.hip, and never reaches this kernel).
 template <int DK, int BV, bool PRO, int GM, bool DEC>
 hipError_t launch_types(const ChunkArgs &a, hipStream_t st) {
     if (a.io_bf16)
-        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, false, PRO, GM, DEC>(a, st)
-                           : launch_t<DK, BV, bf16_t, float, false, false, PRO, GM, DEC>(a, st);
-    constexpr bool EX = DK == 128;
-    return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, !EX, EX, PRO, GM, DEC>(a, st)
-                       : launch_t<DK, BV, float, float, !EX, EX, PRO, GM, DEC>(a, st);
+        return a.gate_bf16 ? launch_t<DK, BV, bf16_t, bf16_t, false, PRO, GM, DEC>(a, st)
+                           : launch_t<DK, BV, bf16_t, float, false, PRO, GM, DEC>(a, st);
+    if constexpr (DK == 128) {
+        return hipErrorInvalidValue;
+    } else {
+        return a.gate_bf16 ? launch_t<DK, BV, float, bf16_t, true, PRO, GM, DEC>(a, st)
+                           : launch_t<DK, BV, float, float, true, PRO, GM, DEC>(a, st);
+    }
 }
 
 // The input variants that exist: per-channel gates with or without the prologue
@@ -646,6 +641,11 @@ size_t two_kernel_workspace_bytes(const ChunkArgs &a);
 bool two_kernel_grids_fit(const ChunkArgs &a, int bv);
 hipError_t launch_chunk_fwd_two_kernel(const ChunkArgs &a, int bv, hipStream_t st);
 
+// fp32 I/O at d_k = 128 (kda_bwd.hip): chunkwise on the fp32 matrix cores.
+size_t f32_fwd_workspace_bytes(const ChunkArgs &a);
+bool f32_fwd_grids_fit(const ChunkArgs &a);
+hipError_t launch_f32_chunk_fwd(const ChunkArgs &a, hipStream_t st);
+
 // Fused path (kda_fused.hip).
 bool fused_fwd_supported(const ChunkArgs &a);
 size_t fused_fwd_workspace_bytes(const ChunkArgs &a);
@@ -655,7 +655,7 @@ hipError_t launch_fused_fwd(const ChunkArgs &a, hipStream_t st);
 // The workspace query does not know which entry point will use it, so it covers
 // both forward paths where the entry point decides between them.
 size_t chunk_fwd_workspace_bytes(const ChunkArgs &a) {
-    if (!a.io_bf16) return 0;
+    if (!a.io_bf16) return a.d_k == 128 ? f32_fwd_workspace_bytes(a) : 0;
     if (a.d_k == 128 && a.d_v == 128) {
         // packed batches always run the fused kernel; equal-length ones run it
         // for the input variants and the two-kernel path for plain KDA
@@ -669,6 +669,7 @@ size_t chunk_fwd_workspace_bytes(const ChunkArgs &a) {
 
 bool chunk_fwd_grids_fit(const ChunkArgs &a) {
     if (fused_fwd_supported(a)) return fused_fwd_grids_fit(a);
+    if (!a.io_bf16 && a.d_k == 128) return f32_fwd_grids_fit(a);
     const int bv = pick_block_v(a);
     if (a.io_bf16 && a.total_tokens > 0) return two_kernel_grids_fit(a, bv);
     return grid_fits(a.num_seqs * (int64_t)a.H * (a.d_v / bv), kThreads);
@@ -687,6 +688,12 @@ int launch_chunk_fwd(const ChunkArgs &a, void *stream, char *err, size_t err_len
             return -1;
         }
         e = launch_fused_fwd(a, st);
+    } else if (!a.io_bf16 && a.d_k == 128) {
+        if (a.workspace_bytes < chunk_fwd_workspace_bytes(a)) {
+            snprintf(err, err_len, "workspace too small");
+            return -1;
+        }
+        e = launch_f32_chunk_fwd(a, st);
     } else {
         const int bv = pick_block_v(a);
         if (a.io_bf16 && a.total_tokens > 0) {

@@ -1127,15 +1127,16 @@ hipError_t launch_fused_variants(const ChunkArgs &a, hipStream_t st) {
 
 // bf16 I/O at d_k = d_v = 128 runs the fused kernel.
 // Which forward runs a call: the fused kernel takes bf16 I/O at d_k = d_v = 128
-// for packed batches and for the input variants (raw projections, scalar
-// gates, separate strengths); plain KDA over an equal-length batch runs the
-// two-kernel path (prep + state kernels), which is faster there.  A packed
+// for packed batches, raw projections and separate write strengths (whose
+// long-context outputs need its hi/lo and scaled fp16 operands to stay within
+// the bf16 bound); plain KDA and the scalar gates over an equal-length batch run
+// the two-kernel path (prep + state kernels), which is faster there.  A packed
 // batch gives bitwise the results of each of its sequences packed alone.  The
 // forward that allocates nothing takes the fused kernel for every batch shape,
-// since its workspace (segment states of at most about 340 chains) is bounded.
+// since its workspace (segment states of at most about 380 chains) is bounded.
 bool fused_fwd_supported(const ChunkArgs &a) {
     if (!a.io_bf16 || a.d_k != 128 || a.d_v != 128) return false;
-    return a.force_fused || a.varlen || a.prologue || a.gate_mode != kGatePerChannel || a.w_write != nullptr;
+    return a.force_fused || a.varlen || a.prologue || a.w_write != nullptr;
 }
 
 // Chains are split only when ceil(target / chains) >= 3, i.e. chains < target / 2,

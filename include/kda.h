@@ -65,12 +65,18 @@ const char *kda_last_hip_error(void);
 /*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none).
  * Arguments as for kda_chunk_fwd; num_seqs is the number of sequences (0 when
- * no cu_seqlens is given).  fp32 I/O needs none.  With bf16 I/O:
+ * no cu_seqlens is given).  With fp32 I/O: none at d_k = 64 (one fused kernel);
+ * at d_k = 128 the chunkwise fp32 forward keeps per chunk-head its fp32 record
+ * (about 148 KiB), the chunk's start state and U (64 KiB and 32 KiB at
+ * d_v = 128), and per token-head the input prologue's mapped q, k and log alpha
+ * (about 1.5 KiB): about 5.3 KiB per token-head in all, 0 without tokens.
+ * With bf16 I/O:
  *  - a packed batch (num_seqs > 0) at d_k = d_v = 128 runs one fused kernel per
  *    (sequence, head): the workspace holds the order in which the sequences
  *    are taken (int32 per sequence, rounded up to 256 bytes);
  *  - an equal-length batch at d_k = d_v = 128 may run either forward (plain KDA
- *    runs two passes, the input variants the fused kernel), so the size covers
+ *    and the scalar gates run two passes, the other input variants the fused
+ *    kernel), so the size covers
  *    both: the two-pass records (per chunk and head, the chunk's
  *    state-independent operands, about 1.4 KiB per token-head; a single
  *    sequence longer than 2048 / H chunks runs in segments of that many chunks,
@@ -119,10 +125,12 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
  *               on return are unspecified.  Two calls in flight at once on
  *               different streams must not share one workspace.
  *
- * Numerics: the state and every accumulation are fp32; products of chunk
- * operands run on bf16 matrix cores with hi/lo-split operands where precision
- * needs it; o is rounded to io_dtype with round-to-nearest-even.  Accuracy is
- * specified for log_alpha >= -30 per token; smaller values act as a reset.
+ * Numerics: the state and every accumulation are fp32.  With bf16 I/O the
+ * products of chunk operands run on bf16 matrix cores with hi/lo-split (or
+ * power-of-two-scaled fp16) operands where precision needs it; with fp32 I/O
+ * they are split bf16 (d_k = 64) or fp32 on the fp32 matrix cores (d_k = 128).
+ * o is rounded to io_dtype with round-to-nearest-even.  Accuracy is specified
+ * for log_alpha >= -30 per token; smaller values act as a reset.
  * Deterministic: the same inputs give bitwise identical outputs.
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
@@ -148,13 +156,15 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  * With bf16 I/O at d_k = d_v = 128 every batch shape runs the fused kernel
  * (for packed batches and the input variants kda_chunk_fwd runs it too), whose
  * workspace never exceeds the scratch; results agree with kda_chunk_fwd to the
- * accuracy of either, and bitwise for packed batches.  fp32 I/O needs no
- * scratch.  bf16 at d_k or d_v = 64 runs the two-pass forward of kda_chunk_fwd
- * and is accepted while its workspace (kda_chunk_fwd_workspace_size) fits the
- * scratch.
+ * accuracy of either, and bitwise for packed batches.  The other calls run
+ * the kernels of kda_chunk_fwd (bitwise its results) and are accepted while
+ * their workspace (kda_chunk_fwd_workspace_size) fits the scratch: fp32 at
+ * d_k = 64 needs none, fp32 at d_k = 128 and bf16 at d_k or d_v = 64 grow with
+ * the batch.
  *
  * Errors: as kda_chunk_fwd; KDA_ERR_WORKSPACE when the call would need more
- * than the 80 MiB of scratch; KDA_ERR_HIP if the scratch's address cannot be
+ * than the 80 MiB of scratch (bf16 at d = 64, or fp32 at d_k = 128, with a
+ * large batch); KDA_ERR_HIP if the scratch's address cannot be
  * found.  Every call on one device shares that device's scratch and leaves its
  * contents behind (the forward reads none of it before writing it): calls that
  * overlap in time on one device -- on different streams, or from different

@@ -69,7 +69,15 @@ def test_workspace_size(kda):
     big = W(1, 65536, 32, 64, 64, 0, kda.KDA_BF16)
     carry = 32 * 64 * 64 * 4
     assert 2048 * (3 * 64 * 64 * 2) + carry <= big <= 2048 * 96 * 1024 + carry + 4096
-    assert W(1, 65536, 32, 128, 128, 0, kda.KDA_F32) == 0
+    # fp32 I/O: none at d_k = 64 (one fused kernel); at d_k = 128 the chunkwise
+    # fp32 path keeps per chunk-head its fp32 record (3 x 64 x d_k + 3 x 64 x 64
+    # + 3 x d_k floats), the chunk's start state and U, and per token-head the
+    # input prologue's mapped q, k, log alpha and beta
+    assert W(1, 65536, 32, 64, 64, 0, kda.KDA_F32) == 0
+    per = 4 * (3 * 64 * 128 + 3 * 64 * 64 + 3 * 128 + 128 * 128 + 64 * 128) + 64 * 4 * (3 * 128 + 3)
+    f32 = W(1, 4096, 16, 128, 128, 0, kda.KDA_F32)
+    assert 64 * 16 * per <= f32 <= 64 * 16 * (per + 1024) + 4096
+    assert W(1, 0, 16, 128, 128, 0, kda.KDA_F32) == 0     # no tokens: h_T = h0 only
     assert W(1, 100, 2, 96, 128, 0, kda.KDA_BF16) == 0
     # varlen: room for one partial chunk per sequence
     v1 = W(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)

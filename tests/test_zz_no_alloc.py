@@ -79,8 +79,9 @@ def test_noalloc_packed_matches_chunk_fwd_bitwise(kda):
 
 
 def test_noalloc_fp32_and_d64_match_chunk_fwd_bitwise(kda):
-    """fp32 I/O (no scratch) and bf16 at d = 64 (the two-pass forward, its
-    records in the scratch) run the kernels of kda_chunk_fwd: bitwise equal."""
+    """fp32 I/O (at d_k = 128 the chunkwise fp32 forward, its records, states
+    and U in the scratch) and bf16 at d = 64 (the two-pass forward, its records
+    in the scratch) run the kernels of kda_chunk_fwd: bitwise equal."""
     for io, dk, dv, lens, seed in (("f32", 128, 128, [300], 55), ("bf16", 64, 64, [2048, 2048], 56),
                                    ("bf16", 64, 128, [777], 57)):
         cfg = I.ChunkConfig("noalloc", io, io, H=2, dk=dk, dv=dv, h0=True, seed=seed)
