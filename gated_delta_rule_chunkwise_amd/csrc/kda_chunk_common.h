@@ -343,6 +343,24 @@ struct ChunkRegs {
         if (DEC && w == 0) wt = to_f32(wr[(tbase + (l < nv ? l : nv - 1)) * H + h]);
     }
 
+    // Rows past the end of a partial chunk as if absent: zero keys, queries and
+    // (mapped) gates, so that they add nothing to any sum or product.  Called
+    // after prepare() (which maps the gates) on partial chunks only.
+    __device__ __forceinline__ void zero_tail(int nv, int w) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (8 * w + i >= nv) {
+                la[i] = vsplat<GV>((GT)0.f);
+                kk[i] = vsplat<IV>((IO)0.f);
+                qq[i] = vsplat<IV>((IO)0.f);
+                if constexpr (PRO) {
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc) lf[i][cc] = 0.f;
+                }
+            }
+        }
+    }
+
     // The prologue maps of the loaded chunk (nothing without PRO); called once
     // per load, where the inputs are first used, so that a load issued ahead is
     // not waited for early.

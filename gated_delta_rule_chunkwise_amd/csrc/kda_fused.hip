@@ -253,10 +253,13 @@ __device__ __forceinline__ f32x4_t mfma3(const bf16x8_t &ah, const bf16x8_t &al,
 //   X = K.e^G S,  O^T = S^T (Q.e^G)^T            (WITH_O)
 //   Y = w.V - b.X,  U = T Y,  O^T += U^T P^T, o    (WITH_O)
 //   S <- Diag(e^{g_n}) S + (K.e^{g_n-G})^T U
-template <int DK, int DV, int NT, bool WITH_O, bool HAS_V, typename IO>
+// issue(p), p = 0..3, is called at four points of the phase (the next chunk's
+// input loads).
+template <int DK, int DV, int NT, bool WITH_O, bool HAS_V, typename IO, typename LF>
 __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[DK / 16][NT], int col0,
                                             float isk, float isq,
-                                            IO *__restrict__ o, int64_t tbase, int nv, int H, int h, int l) {
+                                            IO *__restrict__ o, int64_t tbase, int nv, int H, int h, int l,
+                                            LF &&issue) {
     constexpr int NKS = DK / 32, MT = DK / 16;
     const int lr = l & 15, lg = l >> 4;
     float mx = 0.f;
@@ -266,6 +269,7 @@ __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(S[mt][nt][e]));
+    issue(0);
     const float ss = pow2_scale(wave_max(mx)), iss = 1.f / ss;
     f32x4_t X[4][NT];
 #pragma unroll
@@ -284,6 +288,7 @@ __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[
             for (int nt = 0; nt < NT; ++nt) X[tt][nt] = mfma16h(ke, sf[ks][nt], X[tt][nt]);
         }
     }
+    issue(1);
     // Y = w.V - b.X (rows 16tt + 4lg + e)
     const float xs = isk * iss;
     f32x4_t Y[4][NT];
@@ -333,6 +338,7 @@ __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[
                 mu = fmaxf(mu, fabsf(U[tt][nt][e]));
             }
     }
+    issue(2);
     const float su = pow2_scale(wave_max(mu)), isu = 1.f / su;
     f16x8_t uf[2][NT];
 #pragma unroll
@@ -382,6 +388,7 @@ __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[
             }
         }
     }
+    issue(3);
     // S <- Diag(e^{g_n}) S + (KIn^T U) / (sk su)
     const float cs = isk * isu;
 #pragma unroll
@@ -637,6 +644,34 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
             vr[i] = *reinterpret_cast<const VV *>(v + ((tb + rr) * H + h) * (int64_t)DV + l * CPV);
         }
     };
+    // The next chunk's inputs, issued in four parts spread over the state phase
+    // (gates and strengths, keys, queries, values), so that the waves are not
+    // held at one point while the loads drain through the memory pipeline.
+    typedef typename ChunkRegs<DK, 16, IO, GT, PRO, GM, DEC>::GV GVt;
+    typedef typename ChunkRegs<DK, 16, IO, GT, PRO, GM, DEC>::IV IVt;
+    auto load_part = [&](int part, int64_t tb, int nvv, int l) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * w + i, rr = r < nvv ? r : nvv - 1;
+            const int64_t row = (tb + rr) * H + h;
+            const int64_t base = row * (int64_t)DK + l * CPL;
+            if (part == 0) {
+                if constexpr (GM == kGatePerChannel) in.la[i] = *reinterpret_cast<const GVt *>(la + base);
+                else in.la[i] = vsplat<GVt>(GM == kGatePerHead ? la[row] : (GT)0.f);
+            } else if (part == 1) {
+                in.kk[i] = *reinterpret_cast<const IVt *>(k + base);
+            } else if (part == 2) {
+                in.qq[i] = *reinterpret_cast<const IVt *>(q + base);
+            } else {
+                vr[i] = *reinterpret_cast<const VV *>(v + row * (int64_t)DV + l * CPV);
+            }
+        }
+        if (part == 0 && w == 0) {
+            const int64_t row = (tb + (l < nvv ? l : nvv - 1)) * H + h;
+            in.bt = to_f32(be[row]);
+            if (DEC) in.wt = to_f32(wrp[row]);
+        }
+    };
     if (tk.t0 < tk.t1) load_in(tk.t0, (int)((tk.t1 - tk.t0) < kC ? (tk.t1 - tk.t0) : kC), l0);
 
     for (int64_t tbase = tk.t0; tbase < tk.t1; tbase += kC) {
@@ -649,18 +684,16 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
         // ======== cumsum (log2 units), strengths, largest |k| and |q|
         in.prepare(w, a.lo);
         const bool partial = nv < kC;
+        if (partial) in.zero_tail(nv, w);   // rows past the end: zero keys, queries, gates
         float G[8][CPL], mk = 0.f, mq = 0.f;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const bool valid = !partial || 8 * w + i < nv;
-                const float x = valid ? in.gate(i, cc) * kLog2e : 0.f;
+                const float x = in.gate(i, cc) * kLog2e;
                 G[i][cc] = i ? G[i - 1][cc] + x : x;
-                if (valid) {
-                    mk = fmaxf(mk, fabsf(in.kval(i, cc)));
-                    mq = fmaxf(mq, fabsf(in.qval(i, cc)));
-                }
+                mk = fmaxf(mk, fabsf(in.kval(i, cc)));
+                mq = fmaxf(mq, fabsf(in.qval(i, cc)));
             }
             sm.tot[l * CPL + cc][w] = G[7][cc];
         }
@@ -717,7 +750,56 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
         }
 
         // ======== operands: Gram (bf16, anchored at m) and state phase (fp16, scaled)
-        {
+        if (!wbig) {   // no channel beyond the range in this wave: one form for all
+            float emk[CPL], emq[CPL], egk[CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float em = kexp2<false>(m[cc]);
+                emk[cc] = em * sk;
+                emq[cc] = em * sq;
+                egk[cc] = kexp2<false>(gn[cc] - m[cc]) * sk;
+            }
+            f16x4_t kit[CPL][2];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * w + i;
+                bf16x2_t ka2, qh2, ql2, kh2, kl2;
+                f16x2_t ke2, qe2;
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const float kv = in.kval(i, cc), qv = in.qval(i, cc);
+                    const float g = G[i][cc] - m[cc];
+                    const float e1 = kexp2<false>(g), e2 = kexp2<false>(-g);
+                    const float ka = kv * e1, qa = qv * e1, ki = kv * e2;
+                    bf16_t hh, ll;
+                    ka2[cc] = (bf16_t)ka;
+                    split_bf16(qa, hh, ll);
+                    qh2[cc] = hh;
+                    ql2[cc] = ll;
+                    split_bf16(ki, hh, ll);
+                    kh2[cc] = hh;
+                    kl2[cc] = ll;
+                    ke2[cc] = (f16_t)(ka * emk[cc]);
+                    qe2[cc] = (f16_t)(qa * emq[cc]);
+                    kit[cc][i >> 2][i & 3] = (f16_t)(ki * egk[cc]);
+                }
+                const int c0 = l * CPL, s0 = kslot(c0);
+                *reinterpret_cast<bf16x2_t *>(&sm.g.KA[r][c0]) = ka2;
+                *reinterpret_cast<bf16x2_t *>(&sm.g.KI[0][r][c0]) = kh2;
+                *reinterpret_cast<bf16x2_t *>(&sm.g.KI[1][r][c0]) = kl2;
+                *reinterpret_cast<f16x2_t *>(&sm.KE[r][s0]) = ke2;
+                if (need_o) {
+                    *reinterpret_cast<bf16x2_t *>(&sm.g.QA[0][r][c0]) = qh2;
+                    *reinterpret_cast<bf16x2_t *>(&sm.g.QA[1][r][c0]) = ql2;
+                    *reinterpret_cast<f16x2_t *>(&sm.QE[r][s0]) = qe2;
+                }
+            }
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    *reinterpret_cast<f16x4_t *>(&sm.KIt[l * CPL + cc][kslot(8 * w + 4 * half)]) = kit[cc][half];
+        } else {
             float Em[CPL], Egm[CPL];
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
@@ -902,9 +984,15 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
         const bool more = tbase + kC < tk.t1;
         const int64_t tn = tbase + kC;
         const int nvn = more ? (int)((tk.t1 - tn) < kC ? (tk.t1 - tn) : kC) : 0;
-        if (more) load_in(tn, nvn, l);
-        if (HAS_STATE)
-            state_chunk<DK, DV, NTX, WITH_O, HAS_V, IO>(sm, S, col0, 1.f / sk, 1.f / sq, o, tbase, nv, H, h, l);
+        auto issue = [&](int part) {
+            if (more) load_part(part, tn, nvn, l);
+        };
+        if (HAS_STATE) {
+            state_chunk<DK, DV, NTX, WITH_O, HAS_V, IO>(sm, S, col0, 1.f / sk, 1.f / sq, o, tbase, nv, H, h, l, issue);
+        } else {
+#pragma unroll
+            for (int part = 0; part < 4; ++part) issue(part);
+        }
     }
 
     if (HAS_STATE && dst) {
