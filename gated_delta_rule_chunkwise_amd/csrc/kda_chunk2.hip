@@ -24,8 +24,10 @@
 //   chunk_state_kernel  one workgroup per (sequence, head, block of BV value
 //                       columns): walks the chunks of its sequence, keeping the
 //                       fp32 state block in registers, and streams the records.
-// Chunks whose in-chunk decay exceeds the matrix-core range are flagged by the
-// prep kernel and run token by token in the state kernel.
+// A key channel whose in-chunk decay exceeds the anchored range (80 nats) leaves
+// the Gram products; the prep kernel adds its pairs exactly (e^{G_r - G_i} <= 1)
+// and gives its state-side operands no anchor (K.e^G, Q.e^G, K.e^{g_n - G}), so
+// every chunk takes the same path through the state kernel.
 //
 // Compile-time input variants of both kernels: PRO (raw projections mapped as
 // they are read), GM (gate per key channel, per token and head, or none) and
@@ -129,6 +131,8 @@ struct alignas(16) PrepSmem {
     float tot[DK][kWaves];
     float beta[kC];
     float wr[kC];                              // separate write strengths (DEC)
+    float nrm[2][kC];                          // PRO: inverse norms of q and k per row
+    uint8_t big[DK];                           // channel left out of the Gram products
 };
 
 // ---------------------------------------------------------------------------------
@@ -190,8 +194,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
     if (w == 0) sm.beta[l] = (l < nv) ? in.bt : 0.f;
     if (DEC && w == 0) sm.wr[l] = (l < nv) ? in.wt : 0.f;
     lds_barrier();
-    float m2[CPL];
-    bool big = false;
+    // Anchors: m = g_n / 2 for both factors of the Gram products.  A channel
+    // whose chunk decay exceeds kMaxRange2 ("big") leaves the Gram products (its
+    // KI columns are zero there) and its pairs are added exactly below; its
+    // state-side operands take no anchor: K e^G and Q e^G (mA = 0) and
+    // K e^{g_n - G} (mI = g_n), every factor at most 1.
+    float mA2[CPL], mI2[CPL];
+    bool bigc[CPL];
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) {
         const int c = l * CPL + cc;
@@ -204,19 +213,34 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
             all += tw[ww];
             if (ww < w) pre += tw[ww];
         }
-        m2[cc] = 0.5f * all;
 #pragma unroll
         for (int i = 0; i < 8; ++i) csum[i][cc] += pre;
-        big = big || !(-all <= kMaxRange2);
+        bigc[cc] = !(-all <= kMaxRange2);    // also true for NaN
+        mA2[cc] = bigc[cc] ? 0.f : 0.5f * all;
+        mI2[cc] = bigc[cc] ? all : 0.5f * all;
         if (w == 0) {
-            gCol[c] = kexp2<false>(m2[cc]);
+            gCol[c] = kexp2<false>(mA2[cc]);
             gCol[DK + c] = kexp2<false>(all);
-            gCol[2 * DK + c] = kexp2<false>(all - m2[cc]);
+            gCol[2 * DK + c] = kexp2<false>(all - mI2[cc]);
         }
     }
-    const bool slow = __ballot(big) != 0;   // same totals in every wave: uniform
-    if (tid == 0) gFlag[0] = slow ? 1 : 0;
-    if (slow) return;                        // the state kernel runs this chunk token by token
+    bool lbig = false;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) lbig = lbig || bigc[cc];
+    const bool anybig = __ballot(lbig) != 0;   // same channels in every wave: uniform
+    if (tid == 0) gFlag[0] = 0;
+    if (anybig) {   // for the exact pairs below
+        if (w == 0) {
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) sm.big[l * CPL + cc] = bigc[cc] ? 1 : 0;
+        }
+        if constexpr (PRO) {
+            if (l < 8) {
+                sm.nrm[0][8 * w + l] = in.qs[l];
+                sm.nrm[1][8 * w + l] = in.ks[l];
+            }
+        }
+    }
 
     // ---- decayed operands: LDS for the Gram products, KI^T to the record
     bf16_t kak[8][CPL];                      // this lane's KA values, for KA^T later
@@ -232,10 +256,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
                 if (partial && 8 * w + i >= nv) x = 0.f;
                 al[i] = kexp2<false>(x);
             }
-            e1[0][cc] = kexp2<false>(csum[0][cc] - m2[cc]);
+            e1[0][cc] = kexp2<false>(csum[0][cc] - mA2[cc]);
 #pragma unroll
             for (int i = 1; i < 8; ++i) e1[i][cc] = e1[i - 1][cc] * al[i];
-            e2[7][cc] = kexp2<false>(m2[cc] - csum[7][cc]);
+            e2[7][cc] = kexp2<false>(mI2[cc] - csum[7][cc]);
 #pragma unroll
             for (int i = 6; i >= 0; --i) e2[i][cc] = e2[i + 1][cc] * al[i + 1];
         }
@@ -257,8 +281,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
                 const float kv = in.kval(i, cc), qv = in.qval(i, cc);
                 ka[cc] = (bf16_t)(kv * e1[i][cc]);
                 qa[cc] = (bf16_t)(qv * e1[i][cc]);
-                ki[cc] = (bf16_t)(kv * e2[i][cc]);
-                kit[cc][i] = ki[cc];
+                kit[cc][i] = (bf16_t)(kv * e2[i][cc]);
+                ki[cc] = bigc[cc] ? (bf16_t)0.f : kit[cc][i];   // big channels: out of the Gram
                 kak[i][cc] = ka[cc];
             }
             if constexpr (CPL == 2) {
@@ -301,12 +325,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
         // A tiles as A[r][i] (rows of KA, columns of KI); P tiles transposed,
         // P^T[i][r] (rows of KI, columns of QA), so that the accumulator is the
         // 16x16x16 operand layout the record stores
-        auto gram = [&](int tile, f32x4_t &acc, bool &isP, int &R, int &I) {
-            isP = tile >= 10;
+        auto gram = [&](int tile, f32x4_t &acc) {
+            const bool isP = tile >= 10;
+            int R, I;
             lower_block(isP ? tile - 10 : tile, R, I);
             const bf16_t *xh = isP ? &sm.QA[16 * R + lr][8 * lg] : &sm.KA[16 * R + lr][8 * lg];
             const bf16_t *kh = &sm.KI[16 * I + lr][8 * lg];
-            acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8_t xa = lds_ld8(xh + 32 * ks), kb = lds_ld8(kh + 32 * ks);
@@ -331,16 +355,113 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
                 store_split4(reinterpret_cast<bf16_t *>(dst), reinterpret_cast<bf16_t *>(dst + RL::TILE), x);
             }
         };
-        f32x4_t a0, a1;
-        bool p0, p1;
-        int R0, I0, R1, I1;
-        gram(w, a0, p0, R0, I0);
-        gram(w + 8, a1, p1, R1, I1);
-        finish(p0, R0, I0, a0);
-        finish(p1, R1, I1, a1);
-        if (w < 4) {
-            gram(w + 16, a0, p0, R0, I0);
-            finish(p0, R0, I0, a0);
+        // tiles w, w + 8 and (waves 0-3) w + 16: 0-9 are the lower 16x16 blocks of
+        // A, 10-19 those of P (accumulated transposed)
+        constexpr int NTL = 3;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            if (t == 2 && w >= 4) break;
+            const int tile = w + 8 * t;
+            const bool isP = tile >= 10;
+            int R, I;
+            lower_block(isP ? tile - 10 : tile, R, I);
+            f32x4_t acc = zero4();
+            gram(tile, acc);
+            finish(isP, R, I, acc);
+        }
+    }
+    if (anybig) {
+        // Exact pairs of the channels left out of the Gram products, 16 channels
+        // at a time, staged as fp32 G, K, Q [64][16] over QA (the inversion
+        // starts later) from the inputs themselves:
+        //   A[r,i] += beta_r sum_c k_rc k_ic e^{G_rc - G_ic}  (i < r)
+        //   P[r,i] +=        sum_c q_rc k_ic e^{G_rc - G_ic}  (i <= r)
+        // with K = Q = 0 for the other channels of a group; every factor is at
+        // most 1.  A is in LDS; P's tiles are read back from the record.
+        __syncthreads();   // the Gram operands are consumed; P's tiles are written
+        float *xG = reinterpret_cast<float *>(&sm.t);
+        float *xK = xG + kC * 16, *xQ = xK + kC * 16;
+        static_assert(3 * kC * 16 * 4 <= sizeof(sm.t), "staging fits in the area of QA");
+        constexpr int NPAIR = kC * (kC + 1) / 2, PPT = (NPAIR + kThreads - 1) / kThreads;
+        float sA[PPT], sP[PPT];
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) sA[j] = sP[j] = 0.f;
+        const int64_t rp = (int64_t)H * DK;   // row pitch of q, k and per-channel gates
+#pragma unroll 1
+        for (int g = 0; g < DK / 16; ++g) {
+            const uint4 bw = *reinterpret_cast<const uint4 *>(&sm.big[16 * g]);
+            if ((bw.x | bw.y | bw.z | bw.w) == 0) continue;   // no big channel here (uniform)
+            if (tid < 16) {   // G (log2 units) of channel 16g + tid over the chunk
+                const int c = 16 * g + tid;
+                float G = 0.f;
+                for (int r = 0; r < kC; ++r) {
+                    float x = 0.f;
+                    if (r < nv) {
+                        if constexpr (GM == kGatePerChannel)
+                            x = log_decay<PRO, GM>(to_f32(log_alpha[(t0 + r) * rp + (int64_t)h * DK + c]), lo);
+                        else if constexpr (GM == kGatePerHead)
+                            x = log_decay<PRO, GM>(to_f32(log_alpha[(t0 + r) * H + h]), lo);
+                    }
+                    G += x * kLog2e;
+                    xG[r * 16 + tid] = G;
+                }
+            }
+            for (int e = tid; e < kC * 16; e += kThreads) {
+                const int r = e >> 4, cl = e & 15, c = 16 * g + cl;
+                float kv = 0.f, qv = 0.f;
+                if (r < nv && sm.big[c]) {
+                    const int64_t o = (t0 + r) * rp + (int64_t)h * DK + c;
+                    kv = to_f32(k[o]);
+                    qv = to_f32(q[o]);
+                    if constexpr (PRO) {
+                        qv *= sm.nrm[0][r];
+                        kv *= sm.nrm[1][r];
+                    }
+                }
+                xK[e] = kv;
+                xQ[e] = qv;
+            }
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < PPT; ++j) {
+                const int p = tid + kThreads * j;
+                int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+                if ((r + 1) * (r + 2) / 2 <= p) ++r;
+                if (r * (r + 1) / 2 > p) --r;
+                const int i = p - r * (r + 1) / 2;
+                if (p < NPAIR && r < nv) {
+                    float a = 0.f, b = 0.f;
+#pragma unroll 4
+                    for (int c = 0; c < 16; ++c) {
+                        const float kk = xK[i * 16 + c] * kexp2<false>(xG[r * 16 + c] - xG[i * 16 + c]);
+                        a += xK[r * 16 + c] * kk;
+                        b += xQ[r * 16 + c] * kk;
+                    }
+                    sA[j] += i < r ? a : 0.f;
+                    sP[j] += b;
+                }
+            }
+            lds_barrier();   // read before the next group overwrites the area
+        }
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int p = tid + kThreads * j;
+            int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+            if ((r + 1) * (r + 2) / 2 <= p) ++r;
+            if (r * (r + 1) / 2 > p) --r;
+            const int i = p - r * (r + 1) / 2;
+            if (p < NPAIR && r < nv) {
+                if (i < r) sm.A[r][i] += sm.beta[r] * sA[j];
+                // P[r][i] in tile (r/16, i/16): lane (r%16) + 16 ((i%16)/4), element i%4
+                const int ln = (r & 15) + 16 * ((i & 15) >> 2);
+                bf16_t *ph = reinterpret_cast<bf16_t *>(rec + RL::PT + (size_t)p_tile(r >> 4, i >> 4) * 2 * RL::TILE +
+                                                        ln * 8) + (i & 3);
+                bf16_t *pl = ph + RL::TILE / 2;
+                bf16_t hh, ll;
+                split_bf16((float)*ph + (float)*pl + sP[j], hh, ll);
+                *ph = hh;
+                *pl = ll;
+            }
         }
     }
     lds_barrier();
@@ -631,23 +752,17 @@ struct alignas(16) StateSmem {
     uint8_t ring[2][Slot<DK, DV, BV>::BYTES];
     bf16_t S[BV][KS];          // (Diag(e^m) S)^T, single bf16
     bf16_t U[2][BV][TS];       // hi/lo of U^T
-    float red[4][TokenRed<BV>::N];  // token path
 };
 
 // Barrier for a wave whose outstanding LDS operations (ring writes) need not be
 // complete yet; a later lds_barrier() orders them.
 __device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ int slot_flag(const uint8_t *slot, size_t off) {
-    return *reinterpret_cast<const int32_t *>(slot + off);
-}
-
 template <int DK, int DV, int BV> struct StateRole {
     typedef Slot<DK, DV, BV> SL;
     static constexpr int NT = BV / 16, STW = StateTiles<DK, BV>::STW;
     bf16x8_t kit[STW][2];     // KI^T fragments of the wave's state tiles
     f32x4_t cm[STW], cg[STW], cgm[STW];
-    int flag;
 
     __device__ __forceinline__ void load_cm(const uint8_t *slot, int w, int lg) {
         const float *col = reinterpret_cast<const float *>(slot + SL::COL);
@@ -656,7 +771,6 @@ template <int DK, int DV, int BV> struct StateRole {
             const int mt = (w * STW + i) / NT;
             cm[i] = *reinterpret_cast<const f32x4_t *>(col + 16 * mt + 4 * lg);
         }
-        flag = slot_flag(slot, SL::FLAG);
     }
     __device__ __forceinline__ void load_kit(const uint8_t *slot, int w, int ln, int lg) {
         const float *col = reinterpret_cast<const float *>(slot + SL::COL);
@@ -679,7 +793,6 @@ template <int DK, int DV, int BV> struct OutRole {
     bf16x8_t wn[NKS], qa[NKS];  // fragments (rb, ks) of -W and QA
     bf16x4_t ph[4], pl[4];      // tiles (rb, I) of P^T, I <= rb (hi, lo)
     f32x4_t u0[NT];             // accumulator tiles (rb, nt) of U0
-    int flag;
 
     __device__ __forceinline__ void load_wq(const uint8_t *slot, int rb, int ln) {
         const uint8_t *a = slot + RL::WN + (size_t)(rb * NKS) * RL::FRAG + ln * 16;
@@ -692,7 +805,6 @@ template <int DK, int DV, int BV> struct OutRole {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             u0[nt] = *reinterpret_cast<const f32x4_t *>(slot + SL::U0 + (size_t)(rb * NT + nt) * RL::FRAG + ln * 16);
-        flag = slot_flag(slot, SL::FLAG);
     }
     __device__ __forceinline__ void load_p(const uint8_t *slot, int rb, int ln) {
 #pragma unroll
@@ -745,28 +857,19 @@ __device__ __forceinline__ void state_role_loop(StateSmem<DK, DV, BV> &sm, const
         int tl_;
         asm volatile("v_mov_b32 %0, %1" : "=v"(tl_) : "v"(tid));
         const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
-        const int64_t tbase = cr.bos + (int64_t)j * kC;
-        const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-        const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
-        if (slow) {
-            for (int r = 0; r < nv; ++r)
-                token_update<DK, BV, IO, GT, PRO, GM, DEC>(Sacc, sm.red, q, k, v, log_alpha, beta, wr, o, tbase + r,
-                                                           H, h, DV, col0, w, lg, lr, lo);
-        } else {
-            // S' = Diag(e^m) S, transposed, to LDS
+        // S' = Diag(e^m) S, transposed, to LDS
 #pragma unroll
-            for (int i = 0; i < STW; ++i) {
-                const int st = w * STW + i, mt = st / NT, nt = st % NT;
-                bf16x4_t sv;
+        for (int i = 0; i < STW; ++i) {
+            const int st = w * STW + i, mt = st / NT, nt = st % NT;
+            bf16x4_t sv;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[e] = (bf16_t)(R.cm[i][e] * Sacc[i][e]);
-                *reinterpret_cast<bf16x4_t *>(&sm.S[nt * 16 + lr][16 * mt + 4 * lg]) = sv;
-            }
+            for (int e = 0; e < 4; ++e) sv[e] = (bf16_t)(R.cm[i][e] * Sacc[i][e]);
+            *reinterpret_cast<bf16x4_t *>(&sm.S[nt * 16 + lr][16 * mt + 4 * lg]) = sv;
         }
         lds_barrier();  // B1: S' visible
         lds_barrier();  // B2: U visible; slot (j+1)%2 holds record j+1
         R.load_cm(sm.ring[(j + 1) & 1], w, lg);   // e^m of chunk j+1, read during the update
-        if (!slow) {
+        {
             // S <- Diag(e^{g_n}) S + Diag(e^{g_n - m}) KI^T U
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
@@ -818,16 +921,8 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
         const int lr = tl_ & 15, lg = (tl_ & 63) >> 4;
         const int64_t tbase = cr.bos + (int64_t)j * kC;
         const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-        const bool slow = __builtin_amdgcn_readfirstlane(R.flag) != 0;
-        if (slow) {
-            // the state role runs the chunk token by token: two barriers per token
-            for (int r = 0; r < nv; ++r) {
-                lds_barrier();
-                lds_barrier();
-            }
-        }
         lds_barrier();  // B1: S' visible
-        if (!slow) {
+        {
             // U = U0 - W S' (rows 16rb..16rb+15, to LDS) and Z^T = S'^T QA^T
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -854,7 +949,7 @@ __device__ __forceinline__ void output_role_loop(StateSmem<DK, DV, BV> &sm, cons
         }
         lds_barrier();  // B2: U visible; slot (j+1)%2 holds record j+1
         R.load_wq(sm.ring[(j + 1) & 1], rb, tl_ & 63);
-        if (!slow) {
+        {
             // O^T = Z^T + U^T P^T (blocks left of the diagonal): lane holds O[16rb + lr][16nt + 4lg + e]
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -922,21 +1017,14 @@ __device__ __forceinline__ void loader_store(const u32x4_t (&buf)[N], uint8_t *s
 // ring write of record j+1 and the fetch of record j+3 spread over it.
 template <int DK, int DV, int BV, int N>
 __device__ __forceinline__ void loader_chunk(StateSmem<DK, DV, BV> &sm, u32x4_t (&buf)[N], const uint8_t *rec3,
-                                             int jj, int nv, int nt0, int lid) {
+                                             int jj, int nt0, int lid) {
     typedef Slot<DK, DV, BV> SL;
-    const bool slow = __builtin_amdgcn_readfirstlane(slot_flag(sm.ring[jj & 1], SL::FLAG)) != 0;
     uint8_t *dst = sm.ring[(jj + 1) & 1];
     // record jj+1 to its slot in two halves, at the start of the chunk and after
     // B1 (complete at B2), each followed by the fetch of the same half of record
     // jj+3 into the registers it frees
     loader_store<DK, DV, BV, 0, SL::F1>(buf, dst, nt0, lid);
     loader_fetch<DK, DV, BV, 0, SL::F1>(buf, rec3, nt0, lid);
-    if (slow) {
-        for (int r = 0; r < nv; ++r) {
-            plain_barrier();
-            plain_barrier();
-        }
-    }
     plain_barrier();  // B1
     loader_store<DK, DV, BV, SL::F1, SL::ITERS>(buf, dst, nt0, lid);
     loader_fetch<DK, DV, BV, SL::F1, SL::ITERS>(buf, rec3, nt0, lid);
@@ -964,16 +1052,8 @@ __device__ __forceinline__ void loader_role_loop(StateSmem<DK, DV, BV> &sm, cons
     lds_barrier();  // ring slot 0 holds record 0
     // two chunks per iteration so that the buffers keep fixed registers
     for (int j = 0; j < nch; j += 2) {
-        {
-            const int64_t tbase = cr.bos + (int64_t)j * kC;
-            const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-            loader_chunk<DK, DV, BV>(sm, a, rec_of(j + 3), j, nv, nt0, lid);
-        }
-        if (j + 1 < nch) {
-            const int64_t tbase = cr.bos + (int64_t)(j + 1) * kC;
-            const int nv = (int)((cr.eos - tbase) < kC ? (cr.eos - tbase) : kC);
-            loader_chunk<DK, DV, BV>(sm, b, rec_of(j + 4), j + 1, nv, nt0, lid);
-        }
+        loader_chunk<DK, DV, BV>(sm, a, rec_of(j + 3), j, nt0, lid);
+        if (j + 1 < nch) loader_chunk<DK, DV, BV>(sm, b, rec_of(j + 4), j + 1, nt0, lid);
     }
 }
 
