@@ -131,9 +131,153 @@ struct alignas(16) PrepSmem {
     float tot[DK][kWaves];
     float beta[kC];
     float wr[kC];                              // separate write strengths (DEC)
-    float nrm[2][kC];                          // PRO: inverse norms of q and k per row
-    uint8_t big[DK];                           // channel left out of the Gram products
+    float nrm[2][kC];                          // PRO: inverse norms of q and k per row (big channels only)
 };
+
+// Numbering of the key channels left out of the Gram products ("big": chunk
+// decay beyond the anchored range) in channel order, the same in every wave.
+template <int DK> struct BigNumbering {
+    int slot[DK / 64];   // number of each of this lane's channels among the big ones
+    int nb;              // number of big channels (uniform)
+    __device__ __forceinline__ void init(const bool (&bigc)[DK / 64], int l) {
+        constexpr int CPL = DK / 64;
+        // channel l*CPL + cc comes after the big channels of lanes < l
+        const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+        int s0 = 0;
+        nb = 0;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const uint64_t msk = __ballot(bigc[cc]);
+            s0 += __popcll(msk & below);
+            nb += __popcll(msk);
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            slot[cc] = s0;
+            s0 += bigc[cc] ? 1 : 0;
+        }
+    }
+};
+
+// Exact pairs of the big channels,
+//   A[r,i] += beta_r sum_c k_rc k_ic e^{G_rc - G_ic}  (i < r)
+//   P[r,i] +=        sum_c q_rc k_ic e^{G_rc - G_ic}  (i <= r)
+// every factor at most 1, taken 16 channels at a time from fp32 [64][16] rows of
+// G (log2 units), K and Q, so one fast-forgetting channel costs one channel's
+// pairs.  With at most 16 big channels the rows were staged in the area of A
+// during operand formation, from the registers that held them; otherwise each
+// group is staged here over the area of QA from the inputs (G by one wave-wide
+// inclusive scan of the chunk's gates).  The sums are left in the area of QA as
+// a 64x64 fp32 matrix: the A part (without beta) below the diagonal, the P part
+// on and above it (transposed), for the Gram epilogue.  Called by every wave
+// after the Gram operands are consumed; returns after a barrier.
+template <int DK, bool PRO, int GM, typename Sm, typename IO, typename GT>
+__device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64], const BigNumbering<DK> &bn,
+                                            const IO *__restrict__ q, const IO *__restrict__ k,
+                                            const GT *__restrict__ log_alpha, int64_t t0, int nv, int H, int h,
+                                            float lo, int w, int l, int tid) {
+    constexpr int CPL = DK / 64;
+    const int nb = bn.nb;
+    const bool staged = nb <= 16;
+    float *xG = staged ? reinterpret_cast<float *>(&sm.A[0][0]) : reinterpret_cast<float *>(&sm.t);
+    float *xK = xG + kC * 16, *xQ = xK + kC * 16;
+    float *xS = reinterpret_cast<float *>(&sm.t);
+    static_assert(kC * kC * 4 <= sizeof(sm.t), "staging and sums fit in the area of QA");
+    static_assert(3 * kC * 16 * 4 <= sizeof(sm.A), "staging fits in the area of A");
+    const int64_t rp = (int64_t)H * DK;   // row pitch of q, k and per-channel gates
+    constexpr int NPAIR = kC * (kC + 1) / 2, PPT = (NPAIR + kThreads - 1) / kThreads;
+    float sA[PPT], sP[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) sA[j] = sP[j] = 0.f;
+    __shared__ int32_t chan[16];   // the channel of number g0 + j
+#pragma unroll 1
+    for (int g0 = 0; g0 < nb; g0 += 16) {
+        const int cnt = nb - g0 < 16 ? nb - g0 : 16;
+        if (!staged) {
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int j = bn.slot[cc] - g0;
+                if (w == 0 && bigc[cc] && j >= 0 && j < 16) chan[j] = l * CPL + cc;
+            }
+            lds_barrier();
+            // G of numbers g0 + 2w and g0 + 2w + 1: lane r holds token r
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * w + jj;
+                if (j < cnt) {   // uniform per wave
+                    const int c = chan[j];
+                    float x = 0.f;
+                    if (l < nv) {
+                        if constexpr (GM == kGatePerChannel)
+                            x = log_decay<PRO, GM>(to_f32(log_alpha[(t0 + l) * rp + (int64_t)h * DK + c]), lo);
+                        else if constexpr (GM == kGatePerHead)
+                            x = log_decay<PRO, GM>(to_f32(log_alpha[(t0 + l) * H + h]), lo);
+                    }
+                    x *= kLog2e;
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const float y = __shfl_up(x, d);
+                        if (l >= d) x += y;
+                    }
+                    xG[l * 16 + j] = x;
+                }
+            }
+            // K and Q (with the input prologue: times the rows' inverse norms)
+            for (int e = tid; e < kC * 16; e += kThreads) {
+                const int r = e >> 4, j = e & 15;
+                float kv = 0.f, qv = 0.f;
+                if (r < nv && j < cnt) {
+                    const int64_t o = (t0 + r) * rp + (int64_t)h * DK + chan[j];
+                    kv = to_f32(k[o]);
+                    qv = to_f32(q[o]);
+                    if constexpr (PRO) {
+                        qv *= sm.nrm[0][r];
+                        kv *= sm.nrm[1][r];
+                    }
+                }
+                xK[e] = kv;
+                xQ[e] = qv;
+            }
+            lds_barrier();
+        }
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int p = tid + kThreads * j;
+            int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+            if ((r + 1) * (r + 2) / 2 <= p) ++r;
+            if (r * (r + 1) / 2 > p) --r;
+            const int i = p - r * (r + 1) / 2;
+            if (p < NPAIR && r < nv) {
+                float a = 0.f, b = 0.f;
+                for (int c = 0; c < cnt; ++c) {
+                    const float kk = xK[i * 16 + c] * kexp2<false>(xG[r * 16 + c] - xG[i * 16 + c]);
+                    a += xK[r * 16 + c] * kk;
+                    b += xQ[r * 16 + c] * kk;
+                }
+                sA[j] += a;
+                sP[j] += b;
+            }
+        }
+        if (!staged) lds_barrier();   // staging read before it is overwritten
+    }
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int p = tid + kThreads * j;
+        if (p < NPAIR) {
+            int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+            if ((r + 1) * (r + 2) / 2 <= p) ++r;
+            if (r * (r + 1) / 2 > p) --r;
+            const int i = p - r * (r + 1) / 2;
+            if (i < r) {
+                xS[r * kC + i] = sA[j];
+                xS[i * kC + r] = sP[j];
+            } else {
+                xS[r * kC + r] = sP[j];
+            }
+        }
+    }
+    lds_barrier();
+}
 
 // ---------------------------------------------------------------------------------
 // Prep: one workgroup (8 waves) per (chunk, head).
@@ -141,7 +285,7 @@ struct alignas(16) PrepSmem {
 // (input prologue; lo is the floor of log alpha).  GM: gate layout.  DEC: beta
 // erases and wr writes (decoupled strengths): A and W take beta, U0 takes wr.
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
-__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
+__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
     const int32_t *__restrict__ cu,
@@ -228,20 +372,35 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) lbig = lbig || bigc[cc];
     const bool anybig = __ballot(lbig) != 0;   // same channels in every wave: uniform
-    if (tid == 0) gFlag[0] = 0;
-    if (anybig) {   // for the exact pairs below
-        if (w == 0) {
+    BigNumbering<DK> bn;
+    if (anybig) {
+        bn.init(bigc, l);
+        if (bn.nb <= 16) {   // stage the big channels' G, K, Q rows for the exact pairs
+            float *xG = reinterpret_cast<float *>(&sm.A[0][0]);
+            float *xK = xG + kC * 16, *xQ = xK + kC * 16;
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) sm.big[l * CPL + cc] = bigc[cc] ? 1 : 0;
-        }
-        if constexpr (PRO) {
-            if (l < 8) {
-                sm.nrm[0][8 * w + l] = in.qs[l];
-                sm.nrm[1][8 * w + l] = in.ks[l];
+            for (int cc = 0; cc < CPL; ++cc) {
+                if (bigc[cc]) {
+                    const int j = bn.slot[cc];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = 8 * w + i;
+                        const bool valid = r < nv;
+                        xG[r * 16 + j] = csum[i][cc];
+                        xK[r * 16 + j] = valid ? in.kval(i, cc) : 0.f;
+                        xQ[r * 16 + j] = valid ? in.qval(i, cc) : 0.f;
+                    }
+                }
             }
         }
     }
-
+    if (tid == 0) gFlag[0] = 0;
+    if constexpr (PRO) {
+        if (anybig && l < 8) {   // for the exact pairs of the big channels
+            sm.nrm[0][8 * w + l] = in.qs[l];
+            sm.nrm[1][8 * w + l] = in.ks[l];
+        }
+    }
     // ---- decayed operands: LDS for the Gram products, KI^T to the record
     bf16_t kak[8][CPL];                      // this lane's KA values, for KA^T later
     {
@@ -337,20 +496,27 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
                 acc = isP ? mfma16(kb, xa, acc) : mfma16(xa, kb, acc);
             }
         };
+        // With big channels (anybig), xS below holds their exact pair sums: the A
+        // part below the diagonal, the P part on and above it (transposed).
+        const float *xS = reinterpret_cast<const float *>(&sm.t);
         auto finish = [&](bool isP, int R, int I, const f32x4_t &acc) {
             if (!isP) {
                 const int i = 16 * I + lr;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * R + 4 * lg + e;
-                    sm.A[r][i] = (i < r) ? sm.beta[r] * acc[e] : 0.f;
+                    const float x = anybig ? acc[e] + xS[r * kC + i] : acc[e];
+                    sm.A[r][i] = (i < r) ? sm.beta[r] * x : 0.f;
                 }
             } else {
                 // lane holds P^T[16I + 4lg + e][16R + lr] = P[r][i], kept for i <= r
                 const int r = 16 * R + lr;
                 f32x4_t x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (16 * I + 4 * lg + e <= r) ? acc[e] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * lg + e;
+                    x[e] = (i <= r) ? (anybig ? acc[e] + xS[i * kC + r] : acc[e]) : 0.f;
+                }
                 uint8_t *dst = rec + RL::PT + (size_t)p_tile(R, I) * 2 * RL::TILE + l * 8;
                 store_split4(reinterpret_cast<bf16_t *>(dst), reinterpret_cast<bf16_t *>(dst + RL::TILE), x);
             }
@@ -358,109 +524,36 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(
         // tiles w, w + 8 and (waves 0-3) w + 16: 0-9 are the lower 16x16 blocks of
         // A, 10-19 those of P (accumulated transposed)
         constexpr int NTL = 3;
+        if (!anybig) {
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-            if (t == 2 && w >= 4) break;
-            const int tile = w + 8 * t;
-            const bool isP = tile >= 10;
-            int R, I;
-            lower_block(isP ? tile - 10 : tile, R, I);
-            f32x4_t acc = zero4();
-            gram(tile, acc);
-            finish(isP, R, I, acc);
-        }
-    }
-    if (anybig) {
-        // Exact pairs of the channels left out of the Gram products, 16 channels
-        // at a time, staged as fp32 G, K, Q [64][16] over QA (the inversion
-        // starts later) from the inputs themselves:
-        //   A[r,i] += beta_r sum_c k_rc k_ic e^{G_rc - G_ic}  (i < r)
-        //   P[r,i] +=        sum_c q_rc k_ic e^{G_rc - G_ic}  (i <= r)
-        // with K = Q = 0 for the other channels of a group; every factor is at
-        // most 1.  A is in LDS; P's tiles are read back from the record.
-        __syncthreads();   // the Gram operands are consumed; P's tiles are written
-        float *xG = reinterpret_cast<float *>(&sm.t);
-        float *xK = xG + kC * 16, *xQ = xK + kC * 16;
-        static_assert(3 * kC * 16 * 4 <= sizeof(sm.t), "staging fits in the area of QA");
-        constexpr int NPAIR = kC * (kC + 1) / 2, PPT = (NPAIR + kThreads - 1) / kThreads;
-        float sA[PPT], sP[PPT];
-#pragma unroll
-        for (int j = 0; j < PPT; ++j) sA[j] = sP[j] = 0.f;
-        const int64_t rp = (int64_t)H * DK;   // row pitch of q, k and per-channel gates
-#pragma unroll 1
-        for (int g = 0; g < DK / 16; ++g) {
-            const uint4 bw = *reinterpret_cast<const uint4 *>(&sm.big[16 * g]);
-            if ((bw.x | bw.y | bw.z | bw.w) == 0) continue;   // no big channel here (uniform)
-            if (tid < 16) {   // G (log2 units) of channel 16g + tid over the chunk
-                const int c = 16 * g + tid;
-                float G = 0.f;
-                for (int r = 0; r < kC; ++r) {
-                    float x = 0.f;
-                    if (r < nv) {
-                        if constexpr (GM == kGatePerChannel)
-                            x = log_decay<PRO, GM>(to_f32(log_alpha[(t0 + r) * rp + (int64_t)h * DK + c]), lo);
-                        else if constexpr (GM == kGatePerHead)
-                            x = log_decay<PRO, GM>(to_f32(log_alpha[(t0 + r) * H + h]), lo);
-                    }
-                    G += x * kLog2e;
-                    xG[r * 16 + tid] = G;
-                }
+            for (int t = 0; t < NTL; ++t) {
+                if (t == 2 && w >= 4) break;
+                const int tile = w + 8 * t;
+                const bool isP = tile >= 10;
+                int R, I;
+                lower_block(isP ? tile - 10 : tile, R, I);
+                f32x4_t acc = zero4();
+                gram(tile, acc);
+                finish(isP, R, I, acc);
             }
-            for (int e = tid; e < kC * 16; e += kThreads) {
-                const int r = e >> 4, cl = e & 15, c = 16 * g + cl;
-                float kv = 0.f, qv = 0.f;
-                if (r < nv && sm.big[c]) {
-                    const int64_t o = (t0 + r) * rp + (int64_t)h * DK + c;
-                    kv = to_f32(k[o]);
-                    qv = to_f32(q[o]);
-                    if constexpr (PRO) {
-                        qv *= sm.nrm[0][r];
-                        kv *= sm.nrm[1][r];
-                    }
-                }
-                xK[e] = kv;
-                xQ[e] = qv;
-            }
-            lds_barrier();
+        } else {
+            f32x4_t accs[NTL];
 #pragma unroll
-            for (int j = 0; j < PPT; ++j) {
-                const int p = tid + kThreads * j;
-                int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-                if ((r + 1) * (r + 2) / 2 <= p) ++r;
-                if (r * (r + 1) / 2 > p) --r;
-                const int i = p - r * (r + 1) / 2;
-                if (p < NPAIR && r < nv) {
-                    float a = 0.f, b = 0.f;
-#pragma unroll 4
-                    for (int c = 0; c < 16; ++c) {
-                        const float kk = xK[i * 16 + c] * kexp2<false>(xG[r * 16 + c] - xG[i * 16 + c]);
-                        a += xK[r * 16 + c] * kk;
-                        b += xQ[r * 16 + c] * kk;
-                    }
-                    sA[j] += i < r ? a : 0.f;
-                    sP[j] += b;
-                }
+            for (int t = 0; t < NTL; ++t) {
+                accs[t] = zero4();
+                if (t < 2 || w < 4) gram(w + 8 * t, accs[t]);
             }
-            lds_barrier();   // read before the next group overwrites the area
-        }
+            lds_barrier();   // the Gram operands are consumed
+            exact_pairs<DK, PRO, GM>(sm, bigc, bn, q, k, log_alpha, t0, nv, H, h, lo, w, l, tid);
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
-            const int p = tid + kThreads * j;
-            int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-            if ((r + 1) * (r + 2) / 2 <= p) ++r;
-            if (r * (r + 1) / 2 > p) --r;
-            const int i = p - r * (r + 1) / 2;
-            if (p < NPAIR && r < nv) {
-                if (i < r) sm.A[r][i] += sm.beta[r] * sA[j];
-                // P[r][i] in tile (r/16, i/16): lane (r%16) + 16 ((i%16)/4), element i%4
-                const int ln = (r & 15) + 16 * ((i & 15) >> 2);
-                bf16_t *ph = reinterpret_cast<bf16_t *>(rec + RL::PT + (size_t)p_tile(r >> 4, i >> 4) * 2 * RL::TILE +
-                                                        ln * 8) + (i & 3);
-                bf16_t *pl = ph + RL::TILE / 2;
-                bf16_t hh, ll;
-                split_bf16((float)*ph + (float)*pl + sP[j], hh, ll);
-                *ph = hh;
-                *pl = ll;
+            for (int t = 0; t < NTL; ++t) {
+                if (t < 2 || w < 4) {
+                    const int tile = w + 8 * t;
+                    const bool isP = tile >= 10;
+                    int R, I;
+                    lower_block(isP ? tile - 10 : tile, R, I);
+                    finish(isP, R, I, accs[t]);
+                }
             }
         }
     }

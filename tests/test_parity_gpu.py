@@ -190,6 +190,40 @@ def test_strong_decay_bf16_two_pass(kda, gate_io):
     check_against_oracle(kda, d, "bf16", what="strong decay bf16 gates=%s" % gate_io)
 
 
+@pytest.mark.parametrize("gate_io", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_strong_decay_two_kernel_single_sequence(kda, gate_io, dk, dv):
+    """One sequence (no cu_seqlens: the prep + state kernels at any d_k) whose
+    chunks mix ordinary decay with channels beyond the matrix-core range: a reset
+    of every channel (more than 16 such channels, staged from the inputs), a few
+    channels over a whole chunk (staged from registers) and one channel inside the
+    partial last chunk."""
+    cfg = I.ChunkConfig("strong2k", "bf16", gate_io, H=3, dk=dk, dv=dv, T=300, h0=True, seed=19)
+    d = I.make_chunk_inputs(cfg)
+    la = d["log_alpha"].clone()
+    la[10] = -30.0                 # every channel of every head: a reset in chunk 0
+    la[70:75] = -28.0              # chunk 1
+    la[130:194, 1, :3] = -2.0      # chunk 2 of head 1, three channels (sum -128)
+    la[200:230, :, 7] = -4.0       # chunk 3, one channel
+    la[260:290, 2, 9] = -4.0       # the partial chunk 4 of head 2
+    d["log_alpha"] = la.to(d["log_alpha"].dtype)
+    check_against_oracle(kda, d, "bf16", what="strong decay, one sequence, d=%d/%d gates=%s" % (dk, dv, gate_io))
+
+
+def test_strong_decay_prologue_single_sequence(kda):
+    """The same on raw projections at d_k = 64 (prep + state kernels with the
+    input prologue): gate pre-activations whose floored log decay leaves some
+    channels beyond the matrix-core range."""
+    cfg = I.ChunkConfig("strongpro", "bf16", "bf16", H=2, dk=64, dv=64, T=200, h0=True, seed=21)
+    d = I.make_chunk_raw_inputs(cfg)
+    ga = d["gate_pre"].clone()
+    ga[64:128, :, :4] = -40.0      # -softplus(-40) ~ 0: no decay ...
+    ga[64:128, 1, 5] = 6.0         # ... and one channel at log alpha ~ -6 per token
+    ga[150:180, 0, 2] = 8.0
+    d["gate_pre"] = ga.to(d["gate_pre"].dtype)
+    check_prologue_against_oracle(kda, d, "bf16", -20.0, what="strong decay prologue d=64")
+
+
 def test_beta_negative_eigenvalue_range(kda):
     cfg = I.ChunkConfig("beta2", "f32", "f32", H=2, dk=128, dv=128, T=257, seed=14)
     d = I.make_chunk_inputs(cfg)
