@@ -350,12 +350,15 @@ def main():
         out["strong_decay"] = {
             "workload": "kda_chunk_fwd on the same inputs with key channel 0 of every head at log alpha = -3 "
                         "per token (a 192-nat decay per chunk on that channel)",
-            "ms_per_step": sms, "tokens_per_s": T / (sms * 1e-3), "vs_plain_ms": sms / ms}
+            "ms_per_step": sms, "tokens_per_s": T / (sms * 1e-3), "vs_plain_ms": sms / ms,
+            "traffic": load_traffic("chunk_fwd_strong_decay_prefill_h32_t65536_traffic.json", digest)}
         del la_s
 
     # ---------------- the other prefill workloads: short sequence and packed batch
     if not args.no_other:
         other = {}
+        # fp32 I/O at d = 128 runs on the backward's kernels (kda_bwd.hip)
+        f32_digest = source_digest(CHUNK_SOURCES + ("kda_bwd.hip",))
         profile_name = {"c0": "chunk_fwd_fp32_h2_t256_d64", "c1": "chunk_fwd_h16_t4096",
                         "c2": "chunk_fwd_varlen_n32_h32", "c1_fp32": "chunk_fwd_fp32_h16_t4096_d128"}
         # c1's shape with fp32 I/O at d = 128: the chunkwise fp32 forward
@@ -382,7 +385,8 @@ def main():
                           "alg_flops_per_launch": of,
                           "mfma_frac": of / (oms * 1e-3) / 1e12 /
                           (BF16_MFMA_PEAK_TFLOPS if dd["q"].dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS),
-                          "traffic": load_traffic(profile_name[key] + "_traffic.json", digest)}
+                          "traffic": load_traffic(profile_name[key] + "_traffic.json",
+                                                  f32_digest if key == "c1_fp32" else digest)}
             if key == "c2" and not args.no_backward:
                 # the packed batch's gradients (grad_o ~ N(0,1), grad_hT ~ N(0, 0.1^2))
                 go2, ghT2 = I.make_upstream_grads(dd, 3450, device=dev)
