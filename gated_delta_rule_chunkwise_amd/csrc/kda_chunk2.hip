@@ -129,6 +129,7 @@ struct alignas(16) PrepSmem {
         bf16_t Vt[DV][TS];                     // V^T
     };
     float tot[DK][kWaves];
+    float gs[kC];                              // scalar gates: the in-chunk cumsum per row (log2 units)
     float beta[kC];
     float wr[kC];                              // separate write strengths (DEC)
     float nrm[2][kC];                          // PRO: inverse norms of q and k per row (big channels only)
@@ -282,8 +283,12 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
 // ---------------------------------------------------------------------------------
 // Prep: one workgroup (8 waves) per (chunk, head).
 // PRO: q, k, log_alpha and beta are raw projections, mapped as they are read
-// (input prologue; lo is the floor of log alpha).  GM: gate layout.  DEC: beta
-// erases and wr writes (decoupled strengths): A and W take beta, U0 takes wr.
+// (input prologue; lo is the floor of log alpha).  GM: gate layout; with one
+// decay per (token, head) (or none) the decay of a pair is a scalar, so A and P
+// are plain products of the raw keys and queries with the mask e^{G_r - G_i}
+// applied to the fp32 results, and the state-side operands take no anchor.
+// DEC: beta erases and wr writes (decoupled strengths): A and W take beta, U0
+// takes wr.
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
@@ -294,6 +299,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     constexpr int CPL = DK / 64;
     constexpr int CPV = DV / 64;
     constexpr int NKS = DK / 32;
+    constexpr bool SG = GM != kGatePerChannel;   // one decay per (token, head), or none
     typedef PrepSmem<DK, DV> Sm;
     typedef Rec<DK, DV> RL;
     __shared__ Sm sm;
@@ -359,13 +365,28 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) csum[i][cc] += pre;
-        bigc[cc] = !(-all <= kMaxRange2);    // also true for NaN
-        mA2[cc] = bigc[cc] ? 0.f : 0.5f * all;
-        mI2[cc] = bigc[cc] ? all : 0.5f * all;
+        if constexpr (SG) {
+            // one decay per row: the Gram products run on the raw keys and
+            // queries with the pairwise decay applied to the fp32 products, so
+            // no channel leaves them; the state side takes no anchor
+            bigc[cc] = false;
+            mA2[cc] = 0.f;
+            mI2[cc] = all;
+        } else {
+            bigc[cc] = !(-all <= kMaxRange2);    // also true for NaN
+            mA2[cc] = bigc[cc] ? 0.f : 0.5f * all;
+            mI2[cc] = bigc[cc] ? all : 0.5f * all;
+        }
         if (w == 0) {
             gCol[c] = kexp2<false>(mA2[cc]);
             gCol[DK + c] = kexp2<false>(all);
             gCol[2 * DK + c] = kexp2<false>(all - mI2[cc]);
+        }
+    }
+    if constexpr (SG) {
+        if (l == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm.gs[8 * w + i] = csum[i][0];
         }
     }
     bool lbig = false;
@@ -438,11 +459,19 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 const float kv = in.kval(i, cc), qv = in.qval(i, cc);
-                ka[cc] = (bf16_t)(kv * e1[i][cc]);
-                qa[cc] = (bf16_t)(qv * e1[i][cc]);
                 kit[cc][i] = (bf16_t)(kv * e2[i][cc]);
-                ki[cc] = bigc[cc] ? (bf16_t)0.f : kit[cc][i];   // big channels: out of the Gram
-                kak[i][cc] = ka[cc];
+                if constexpr (SG) {   // Gram operands K and Q; Q e^G staged in KI's area for the record
+                    const bool valid = 8 * w + i < nv;
+                    ka[cc] = valid ? (bf16_t)kv : (bf16_t)0.f;
+                    qa[cc] = valid ? (bf16_t)qv : (bf16_t)0.f;
+                    ki[cc] = (bf16_t)(qv * e1[i][cc]);
+                    kak[i][cc] = (bf16_t)(kv * e1[i][cc]);
+                } else {
+                    ka[cc] = (bf16_t)(kv * e1[i][cc]);
+                    qa[cc] = (bf16_t)(qv * e1[i][cc]);
+                    ki[cc] = bigc[cc] ? (bf16_t)0.f : kit[cc][i];   // big channels: out of the Gram
+                    kak[i][cc] = ka[cc];
+                }
             }
             if constexpr (CPL == 2) {
                 bf16x2_t p;
@@ -475,7 +504,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
         const int pc = tid + kThreads * it;
         const int f = pc >> 6, ln = pc & 63;
         const int rb = f / NKS, ks = f % NKS;
-        const bf16x8_t x = lds_ld8(&sm.QA[16 * rb + (ln & 15)][32 * ks + 8 * (ln >> 4)]);
+        const bf16x8_t x = SG ? lds_ld8(&sm.KI[16 * rb + (ln & 15)][32 * ks + 8 * (ln >> 4)])
+                              : lds_ld8(&sm.QA[16 * rb + (ln & 15)][32 * ks + 8 * (ln >> 4)]);
         *reinterpret_cast<bf16x8_t *>(rec + RL::QA + f * RL::FRAG + ln * 16) = x;
     }
 
@@ -489,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
             int R, I;
             lower_block(isP ? tile - 10 : tile, R, I);
             const bf16_t *xh = isP ? &sm.QA[16 * R + lr][8 * lg] : &sm.KA[16 * R + lr][8 * lg];
-            const bf16_t *kh = &sm.KI[16 * I + lr][8 * lg];
+            const bf16_t *kh = SG ? &sm.KA[16 * I + lr][8 * lg] : &sm.KI[16 * I + lr][8 * lg];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8_t xa = lds_ld8(xh + 32 * ks), kb = lds_ld8(kh + 32 * ks);
@@ -505,7 +535,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * R + 4 * lg + e;
-                    const float x = anybig ? acc[e] + xS[r * kC + i] : acc[e];
+                    float x = anybig ? acc[e] + xS[r * kC + i] : acc[e];
+                    if constexpr (SG) x *= kexp2<false>(sm.gs[r] - sm.gs[i]);   // at most 1 for i < r
                     sm.A[r][i] = (i < r) ? sm.beta[r] * x : 0.f;
                 }
             } else {
@@ -515,7 +546,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 16 * I + 4 * lg + e;
-                    x[e] = (i <= r) ? (anybig ? acc[e] + xS[i * kC + r] : acc[e]) : 0.f;
+                    float y = anybig ? acc[e] + xS[i * kC + r] : acc[e];
+                    if constexpr (SG) y *= kexp2<false>(sm.gs[r] - sm.gs[i]);   // at most 1 for i <= r
+                    x[e] = (i <= r) ? y : 0.f;
                 }
                 uint8_t *dst = rec + RL::PT + (size_t)p_tile(R, I) * 2 * RL::TILE + l * 8;
                 store_split4(reinterpret_cast<bf16_t *>(dst), reinterpret_cast<bf16_t *>(dst + RL::TILE), x);

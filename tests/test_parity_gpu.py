@@ -561,6 +561,28 @@ def test_gdn_ragged_varlen(kda, gate, io, dk, dv):
     _gdn_check(kda, d, g, io, "gdn %s %s dk=%d dv=%d" % (gate, io, dk, dv))
 
 
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_gdn_single_sequence_strong(kda, gate, dk, dv):
+    """One sequence (prep + state kernels, where the scalar gate makes the Gram
+    blocks plain products of the raw keys and queries under a pairwise decay
+    mask): a reset, a whole chunk at log alpha = -6 per token (384 nats), and a
+    partial last chunk; with no gate, values scaled so that |o| stays below 1."""
+    cfg = I.ChunkConfig("gdn1", "bf16", "bf16", H=3, dk=dk, dv=dv, T=300, h0=True, seed=43)
+    d = I.make_chunk_inputs(cfg)
+    g = None
+    if gate == "scalar":
+        g = d["log_alpha"][:, :, 0].float().clone()
+        g[10] = -30.0
+        g[64:128, 1] = -6.0
+        g[270:280, 2] = -5.0
+        g = g.to(d["log_alpha"].dtype).contiguous()
+    else:
+        d["v"] = (d["v"].float() * 0.35).to(d["v"].dtype)
+        d["h0"] = d["h0"] * 0.35
+    _gdn_check(kda, d, g, "bf16", "gdn one sequence %s dk=%d" % (gate, dk))
+
+
 def test_gdn_c3_full(kda):
     """c3's full size with one decay per token and head (c3's per-channel draw,
     first channel); the oracle checks every head."""
