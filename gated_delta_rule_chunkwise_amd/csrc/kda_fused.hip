@@ -30,9 +30,12 @@
 // Work decomposition.  One workgroup of 8 waves owns one (sequence, head) chain,
 // or one segment of it, with all d_v value columns: nothing is shared between
 // workgroups.  Per chunk, all waves form the operands and the Gram blocks; waves
-// 0-3 solve T while waves 4-7 convert P; then every wave advances its 16 value
-// columns of the state (fp32, registers) while the next chunk's inputs are in
-// flight.  The state's accumulator tiles are used directly as matrix-core
+// 0-3 invert the four diagonal 16x16 blocks of I + A while waves 4-7 convert P
+// and the blocks of A below the diagonal to fp16; then every wave advances its
+// 16 value columns of the state (fp32, registers) while the next chunk's inputs
+// are in flight.  T = (I + A)^{-1} is never formed: each wave solves
+// (I + A) U = Y for its columns by substitution over the four token tiles,
+// U_R = D_R (Y_R - sum_{I<R} A_RI U_I) with D_R the inverted diagonal blocks.  The state's accumulator tiles are used directly as matrix-core
 // operands: the k index of each 32-wide step is permuted (slot 8g+4h+i holds
 // index 16h+4g+i) so that an accumulator pair is one operand fragment; the
 // shared operands are stored in LDS in that order.
@@ -48,13 +51,13 @@
 // recurrence regrouped, not approximated.
 //
 // Precision.  The Gram products take K.e^{G-m} as single bf16 and Q.e^{G-m},
-// K.e^{m-G} as hi/lo bf16 pairs (about 2^-16 relative).  T is solved in fp32 on
-// its diagonal blocks and with hi/lo operands off them.  The state products
-// (X = K.e^G S, Q.e^G S, T Y, P U, (K.e^{g_n-G})^T U) run on fp16 operands,
-// each scaled by a power of two to the top of the fp16 range (the state and Y,
-// U per wave, K and Q per chunk, T and P per row), which keeps 11 significant
-// bits whatever the magnitudes; every scale is undone exactly on the fp32
-// accumulators.
+// K.e^{m-G} as hi/lo bf16 pairs (about 2^-16 relative).  The diagonal blocks
+// of I + A are inverted in fp32.  The state products (X = K.e^G S, Q.e^G S,
+// the substitution for U, P U, (K.e^{g_n-G})^T U) run on fp16 operands, each
+// scaled by a power of two to the top of the fp16 range (the state per wave,
+// each token tile's right-hand side and U per wave, K and Q per chunk, A, D and
+// P per row), which keeps 11 significant bits whatever the magnitudes; every
+// scale is undone exactly on the fp32 accumulators.
 #include "kda_chunk_common.h"
 #include "kda_launch.h"
 #include "kda_plan.h"
@@ -107,9 +110,8 @@ template <int DK, int DV> struct alignas(16) FusedSmem {
                     float K[kC][XQ];
                     float Q[kC][XQ];
                 } x;
-                struct {                // UT transform scratch
-                    bf16_t T[2][kC][TS];
-                    bf16_t Tt[2][kC][kC + 4];
+                struct {                // inverses of the diagonal blocks of I + A
+                    float D[4][16][17];
                     float T8[4][2][8][8];
                     float W8[4][8][8];
                 } t;
@@ -122,10 +124,11 @@ template <int DK, int DV> struct alignas(16) FusedSmem {
     f16_t KIt[DK][TS];                  // (K.e^{g_n-G})^T . sk
     union {
         float tot[DK][kFW];             // per-wave sums of log2 alpha (cumsum phase only)
-        f16_t T16[kC][TS];              // T, rows scaled by 1 / rsT
+        f16_t AD16[kC][TS];             // A below the diagonal blocks (rows scaled by 1 / rsA) and
+                                        // the diagonal blocks' inverses D (rows scaled by 1 / rsD)
     };
     f16_t P16[kC][TS];                  // P, rows scaled by 1 / rsP
-    float rsT[kC], rsP[kC];             // row scales (powers of 2)
+    float rsA[kC], rsD[kC], rsP[kC];    // row scales (powers of 2)
     float egn[DK];                      // e^{g_n}
     float beta[kC];                     // erase strength b (= beta)
     float wr[kC];                       // write strength w (= beta unless decoupled)
@@ -234,6 +237,13 @@ __device__ __forceinline__ f16x8_t pair_h(const f32x4_t &a, const f32x4_t &b, fl
 }
 
 __device__ __forceinline__ f16x8_t lds_ld8h(const f16_t *p) { return *reinterpret_cast<const f16x8_t *>(p); }
+__device__ __forceinline__ f16x4_t lds_ld4h(const f16_t *p) { return *reinterpret_cast<const f16x4_t *>(p); }
+
+// D(16x16) += A(16x16) B(16x16) on fp16 operands: lane l holds A[l%16][4(l/16)+i],
+// B[4(l/16)+i][l%16] and D[4(l/16)+i][l%16], so an accumulator tile is a B operand.
+__device__ __forceinline__ f32x4_t mfma16h16(const f16x4_t &a, const f16x4_t &b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
 
 // acc += A B with hi/lo bf16 A and B (hi*hi + hi*lo + lo*hi).
 __device__ __forceinline__ f32x4_t mfma3(const bf16x8_t &ah, const bf16x8_t &al, const bf16x8_t &bh,
@@ -247,11 +257,12 @@ __device__ __forceinline__ f32x4_t mfma3(const bf16x8_t &ah, const bf16x8_t &al,
 // One chunk of the state recurrence for NT 16-column tiles of the state held by
 // this wave (columns col0.. of the value space, or of Phi when HAS_V is false).
 // The state-side products run on fp16 operands scaled by powers of two: the
-// state by ss (this wave's columns), Y and U by sy and su, the shared operands
-// by sk, sq and the row scales of T and P; every scale is undone exactly on the
-// fp32 accumulators.
+// state by ss (this wave's columns), each token tile of the right-hand side and
+// of U by its own power of two and U again by su, the shared operands
+// by sk, sq and the row scales of A, D and P; every scale is undone exactly on
+// the fp32 accumulators.
 //   X = K.e^G S,  O^T = S^T (Q.e^G)^T            (WITH_O)
-//   Y = w.V - b.X,  U = T Y,  O^T += U^T P^T, o    (WITH_O)
+//   Y = w.V - b.X,  (I + A) U = Y,  O^T += U^T P^T, o    (WITH_O)
 //   S <- Diag(e^{g_n}) S + (K.e^{g_n-G})^T U
 // issue(p), p = 0..3, is called at four points of the phase (the next chunk's
 // input loads).
@@ -292,7 +303,6 @@ __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[
     // Y = w.V - b.X (rows 16tt + 4lg + e)
     const float xs = isk * iss;
     f32x4_t Y[4][NT];
-    float my = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const f32x4_t bb = *reinterpret_cast<const f32x4_t *>(&sm.beta[16 * tt + 4 * lg]);
@@ -302,41 +312,65 @@ __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[
             bf16x4_t vv;
             if (HAS_V) vv = lds_ld4(&sm.r.Vt[col0 + 16 * nt + lr][16 * tt + 4 * lg]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float y = (HAS_V ? ww[e] * (float)vv[e] : 0.f) - bb[e] * (X[tt][nt][e] * xs);
-                Y[tt][nt][e] = y;
-                my = fmaxf(my, fabsf(y));
-            }
+            for (int e = 0; e < 4; ++e)
+                Y[tt][nt][e] = (HAS_V ? ww[e] * (float)vv[e] : 0.f) - bb[e] * (X[tt][nt][e] * xs);
         }
     }
-    const float sy = pow2_scale(wave_max(my)), isy = 1.f / sy;
-    f16x8_t yf[2][NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        yf[0][nt] = pair_h(Y[0][nt], Y[1][nt], sy);
-        yf[1][nt] = pair_h(Y[2][nt], Y[3][nt], sy);
-    }
-    // U = T Y (T lower triangular: token tile tt needs k-steps <= tt/2)
+    // U = (I + A)^{-1} Y by substitution over the four 16-token tiles,
+    //   U_R = D_R (Y_R - sum_{I<R} A_RI U_I),   D_R = (I + A_RR)^{-1},
+    // on 16x16x16 fp16 products (a U tile's accumulator layout is the B
+    // operand layout); each tile's right-hand side and U take their own power
+    // of two, undone on the fp32 accumulators with the row scales of A and D.
     f32x4_t U[4][NT];
+    f16x4_t uh[3][NT];
+    float isub[3];
     float mu = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int R = 0; R < 4; ++R) {
+        const f32x4_t ra = *reinterpret_cast<const f32x4_t *>(&sm.rsA[16 * R + 4 * lg]);
+        const f32x4_t rd = *reinterpret_cast<const f32x4_t *>(&sm.rsD[16 * R + 4 * lg]);
+        f32x4_t yp[NT];
+        float m = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) U[tt][nt] = zero4();
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4_t z = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 <= (tt >> 1); ++k2) {
-            const f16x8_t tf = lds_ld8h(&sm.T16[16 * tt + lr][32 * k2 + 8 * lg]);
+            for (int I = 0; I < R; ++I) {
+                const f16x4_t a = lds_ld4h(&sm.AD16[16 * R + lr][16 * I + 4 * lg]);
+                const f32x4_t pr = mfma16h16(a, uh[I][nt], zero4());
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) U[tt][nt] = mfma16h(tf, yf[k2][nt], U[tt][nt]);
-        }
-        const f32x4_t rt = *reinterpret_cast<const f32x4_t *>(&sm.rsT[16 * tt + 4 * lg]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+                for (int e = 0; e < 4; ++e) z[e] += pr[e] * isub[I];
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                U[tt][nt][e] *= rt[e] * isy;
-                mu = fmaxf(mu, fabsf(U[tt][nt][e]));
+                yp[nt][e] = Y[R][nt][e] - z[e] * ra[e];
+                m = fmaxf(m, fabsf(yp[nt][e]));
             }
+        }
+        const float sy = pow2_scale(wave_max(m)), isy = 1.f / sy;
+        const f16x4_t dd = lds_ld4h(&sm.AD16[16 * R + lr][16 * R + 4 * lg]);
+        float mR = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f16x4_t yh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yh[e] = (f16_t)(yp[nt][e] * sy);
+            U[R][nt] = mfma16h16(dd, yh, zero4());
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                U[R][nt][e] *= rd[e] * isy;
+                mR = fmaxf(mR, fabsf(U[R][nt][e]));
+            }
+        }
+        mu = fmaxf(mu, mR);
+        if (R < 3) {
+            const float s = pow2_scale(wave_max(mR));
+            isub[R] = 1.f / s;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) uh[R][nt][e] = (f16_t)(U[R][nt][e] * s);
+        }
     }
     issue(2);
     const float su = pow2_scale(wave_max(mu)), isu = 1.f / su;
@@ -410,14 +444,13 @@ __device__ __forceinline__ void state_chunk(FusedSmem<DK, DV> &sm, f32x4_t (&S)[
     }
 }
 
-// T = (I + A)^{-1} for the b-scaled strictly lower A in sm.r.A (fp32): the four
-// diagonal 16x16 blocks by substitution (waves 0-3, as two 8x8 solves and a
-// merge), the off-diagonal blocks by block products on the matrix cores (waves
-// 0-1, hi/lo operands).  Leaves hi/lo T in sm.r.t.T (lower blocks only).  Waves
-// 4-7 run `other` meanwhile.  Every wave takes part in the barriers.
+// D_R = (I + A_RR)^{-1} for the four diagonal 16x16 blocks of the b-scaled
+// strictly lower A in sm.r.ap.A (fp32), each by two 8x8 forward substitutions
+// and a merge (waves 0-3, one block each), into sm.r.t.D.  Waves 4-7 run
+// `other` meanwhile.  Every wave takes part in the closing barrier.  The blocks
+// below the diagonal are not inverted: the state phase solves with A and D.
 template <typename Sm, typename F>
-__device__ __forceinline__ void ut_transform(Sm &sm, int w, int l, F &&other) {
-    const int lr = l & 15, lg = l >> 4;
+__device__ __forceinline__ void diag_inverse(Sm &sm, int w, int l, F &&other) {
     if (w < 4) {
         const int R = w;
         float(*t8)[8][8] = sm.r.t.T8[R];
@@ -469,75 +502,9 @@ __device__ __forceinline__ void ut_transform(Sm &sm, int w, int l, F &&other) {
         }
         const float vals[4] = {t8[0][i8][j8], 0.f, tba, t8[1][i8][j8]};
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const int rr = 16 * R + 8 * (qd >> 1) + i8, cc = 16 * R + 8 * (qd & 1) + j8;
-            bf16_t hh, ll;
-            split_bf16(vals[qd], hh, ll);
-            sm.r.t.T[0][rr][cc] = hh;
-            sm.r.t.T[1][rr][cc] = ll;
-            sm.r.t.Tt[0][cc][rr] = hh;
-            sm.r.t.Tt[1][cc][rr] = ll;
-        }
+        for (int qd = 0; qd < 4; ++qd) sm.r.t.D[R][8 * (qd >> 1) + i8][8 * (qd & 1) + j8] = vals[qd];
     } else {
         other();
-    }
-    lds_barrier();
-    if (w < 2) {
-        constexpr int TS = Sm::TS;
-        const int b = w;
-        f32x4_t t10 = zero4();
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-            const int R = 2 * pr;
-            bf16x4_t ah, al;
-            load_split4(&sm.r.ap.A[16 * (R + 1) + lr][16 * R + 4 * lg], ah, al);
-            f32x4_t wacc = mma4(zero4(), ah, al, lds_ld4(&sm.r.t.Tt[0][16 * R + lr][16 * R + 4 * lg]),
-                                lds_ld4(&sm.r.t.Tt[1][16 * R + lr][16 * R + 4 * lg]));
-            bf16x4_t wh, wl;
-            split4(wacc, wh, wl);
-            f32x4_t tacc = mma4(zero4(), lds_ld4(&sm.r.t.T[0][16 * (R + 1) + lr][16 * (R + 1) + 4 * lg]),
-                                lds_ld4(&sm.r.t.T[1][16 * (R + 1) + lr][16 * (R + 1) + 4 * lg]), wh, wl);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tacc[e] = -tacc[e];
-            store_tile_split(&sm.r.t.T[0][0][0], &sm.r.t.T[1][0][0], TS, 16 * (R + 1), 16 * R, tacc, lr, lg);
-            if (pr == 0) t10 = tacc;
-        }
-        wave_lds_sync();
-        f32x4_t w2[2];
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2) {
-            const int aa = 2 + a2;
-            bf16x4_t ah, al;
-            w2[a2] = zero4();
-            if (b == 0) {
-                load_split4(&sm.r.ap.A[16 * aa + lr][4 * lg], ah, al);
-                w2[a2] = mma4(w2[a2], ah, al, lds_ld4(&sm.r.t.Tt[0][lr][4 * lg]), lds_ld4(&sm.r.t.Tt[1][lr][4 * lg]));
-                bf16x4_t th, tl;
-                split4(t10, th, tl);
-                load_split4(&sm.r.ap.A[16 * aa + lr][16 + 4 * lg], ah, al);
-                w2[a2] = mma4(w2[a2], ah, al, th, tl);
-            } else {
-                load_split4(&sm.r.ap.A[16 * aa + lr][16 + 4 * lg], ah, al);
-                w2[a2] = mma4(w2[a2], ah, al, lds_ld4(&sm.r.t.Tt[0][16 + lr][16 + 4 * lg]),
-                              lds_ld4(&sm.r.t.Tt[1][16 + lr][16 + 4 * lg]));
-            }
-        }
-        bf16x4_t w2h[2], w2l[2];
-        split4(w2[0], w2h[0], w2l[0]);
-        split4(w2[1], w2h[1], w2l[1]);
-        f32x4_t t2b = mma4(zero4(), lds_ld4(&sm.r.t.T[0][32 + lr][32 + 4 * lg]),
-                           lds_ld4(&sm.r.t.T[1][32 + lr][32 + 4 * lg]), w2h[0], w2l[0]);
-        f32x4_t t3b = mma4(zero4(), lds_ld4(&sm.r.t.T[0][48 + lr][32 + 4 * lg]),
-                           lds_ld4(&sm.r.t.T[1][48 + lr][32 + 4 * lg]), w2h[0], w2l[0]);
-        t3b = mma4(t3b, lds_ld4(&sm.r.t.T[0][48 + lr][48 + 4 * lg]), lds_ld4(&sm.r.t.T[1][48 + lr][48 + 4 * lg]),
-                   w2h[1], w2l[1]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            t2b[e] = -t2b[e];
-            t3b[e] = -t3b[e];
-        }
-        store_tile_split(&sm.r.t.T[0][0][0], &sm.r.t.T[1][0][0], TS, 32, 16 * b, t2b, lr, lg);
-        store_tile_split(&sm.r.t.T[0][0][0], &sm.r.t.T[1][0][0], TS, 48, 16 * b, t3b, lr, lg);
     }
     lds_barrier();
 }
@@ -566,31 +533,50 @@ template <typename Sm> __device__ __forceinline__ void p_convert(Sm &sm, int t) 
     }
 }
 
-// T (hi/lo, lower blocks) to fp16 rows scaled by powers of two, k index in slot
-// order (all waves, t = 0..511: row t/8, columns 8(t%8)..+7).
-template <typename Sm> __device__ __forceinline__ void t_convert(Sm &sm, int t) {
-    const int r = t >> 3, b = t & 7, ks = b >> 2, hh = (b & 3) >> 1, g0 = 2 * (b & 1);
-    const bf16x8_t th = lds_ld8(&sm.r.t.T[0][r][8 * b]);
-    const bf16x8_t tl = lds_ld8(&sm.r.t.T[1][r][8 * b]);
-    const bool low = (b >> 1) <= (r >> 4);
-    float x[8], mx = 0.f;
+// A below the diagonal blocks (fp32) to fp16 rows scaled by powers of two, in
+// natural column order (waves 4-7, t = 0..255: row t/4, columns 16(t%4)..+15;
+// block rows 1-3 only).
+template <typename Sm> __device__ __forceinline__ void a_convert(Sm &sm, int t) {
+    const int r = t >> 2, b = t & 3, R = r >> 4;
+    float x[16], mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        x[j] = low ? (float)th[j] + (float)tl[j] : 0.f;
+    for (int j = 0; j < 16; ++j) {
+        x[j] = b < R ? sm.r.ap.A[r][16 * b + j] : 0.f;
         mx = fmaxf(mx, fabsf(x[j]));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 1));
     mx = fmaxf(mx, __shfl_xor(mx, 2));
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
     const float sc = pow2_scale(mx);
-    if (b == 0) sm.rsT[r] = 1.f / sc;
+    if (b == 0) sm.rsA[r] = 1.f / sc;
+    if (b < R) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        f16x4_t y;
+        for (int g = 0; g < 4; ++g) {
+            f16x4_t y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = (f16_t)(x[4 * half + i] * sc);
-        *reinterpret_cast<f16x4_t *>(&sm.T16[r][32 * ks + 8 * (g0 + half) + 4 * hh]) = y;
+            for (int i = 0; i < 4; ++i) y[i] = (f16_t)(x[4 * g + i] * sc);
+            *reinterpret_cast<f16x4_t *>(&sm.AD16[r][16 * b + 4 * g]) = y;
+        }
     }
+}
+
+// The diagonal blocks' inverses (fp32) to fp16 rows scaled by powers of two
+// (t = 0..255: row t/4, columns 16(r/16) + 4(t%4)..+3).
+template <typename Sm> __device__ __forceinline__ void d_convert(Sm &sm, int t) {
+    const int r = t >> 2, b = t & 3, R = r >> 4;
+    float x[4], mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = sm.r.t.D[R][r & 15][4 * b + i];
+        mx = fmaxf(mx, fabsf(x[i]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    const float sc = pow2_scale(mx);
+    if (b == 0) sm.rsD[r] = 1.f / sc;
+    f16x4_t y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = (f16_t)(x[i] * sc);
+    *reinterpret_cast<f16x4_t *>(&sm.AD16[r][16 * R + 4 * b]) = y;
 }
 
 constexpr float kBig = 80.f;              // chunk decay (nats) beyond which a channel leaves the Gram products
@@ -965,11 +951,13 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
             lds_barrier();
         }
 
-        // ======== T = (I + A)^{-1} (waves 0-3) while waves 4-7 convert P; then T
-        ut_transform(sm, w, l, [&] {
+        // ======== D_R = (I + A_RR)^{-1} (waves 0-3) while waves 4-7 convert P and
+        // the blocks of A below the diagonal; then D to fp16
+        diag_inverse(sm, w, l, [&] {
             if (need_o) p_convert(sm, tid - 256);
+            a_convert(sm, tid - 256);
         });
-        t_convert(sm, tid);
+        if (tid < 256) d_convert(sm, tid);
         // V^T over A and P, which the transform has consumed (rows past the chunk zero)
 #pragma unroll
         for (int cv = 0; cv < CPV; ++cv) {
