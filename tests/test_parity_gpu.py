@@ -101,6 +101,18 @@ def test_c3_constant_decay_full(kda):
     check_against_oracle(kda, d, "bf16", what="c3 uniform_const all heads")
 
 
+def test_c3_strong_decay_full(kda):
+    """The strong-decay case the benchmark times, at full size: the long-context
+    workload with key channel 0 of every head at log alpha = -3 on every token
+    (192 nats per chunk on that channel, which leaves the Gram products and has
+    its pairs summed exactly); the oracle checks all 32 heads."""
+    d = I.make_chunk_inputs(I.C3)
+    la = d["log_alpha"].clone()
+    la[:, :, 0] = -3.0
+    d["log_alpha"] = la
+    check_against_oracle(kda, d, "bf16", what="c3 strong decay all heads")
+
+
 def test_max_heads(kda):
     """H = 65,535, the largest head count the backward's grid admits: record
     and state offsets past 2^32 bytes, a full chunk plus a one-token tail."""
