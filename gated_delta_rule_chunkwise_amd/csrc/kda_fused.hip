@@ -745,6 +745,21 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
                 emq[cc] = em * sq;
                 egk[cc] = kexp2<false>(gn[cc] - m[cc]) * sk;
             }
+            // e^{G-m} and e^{m-G} along this wave's eight rows as running products
+            // of the per-token decays (one exponential per token and channel)
+            float ex1[8][CPL], ex2[8][CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                float al[8];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) al[i] = kexp2<false>(in.gate(i, cc) * kLog2e);
+                ex1[0][cc] = kexp2<false>(G[0][cc] - m[cc]);
+                ex2[7][cc] = kexp2<false>(m[cc] - G[7][cc]);
+#pragma unroll
+                for (int i = 1; i < 8; ++i) ex1[i][cc] = ex1[i - 1][cc] * al[i];
+#pragma unroll
+                for (int i = 6; i >= 0; --i) ex2[i][cc] = ex2[i + 1][cc] * al[i + 1];
+            }
             f16x4_t kit[CPL][2];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -754,8 +769,7 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
                     const float kv = in.kval(i, cc), qv = in.qval(i, cc);
-                    const float g = G[i][cc] - m[cc];
-                    const float e1 = kexp2<false>(g), e2 = kexp2<false>(-g);
+                    const float e1 = ex1[i][cc], e2 = ex2[i][cc];
                     const float ka = kv * e1, qa = qv * e1, ki = kv * e2;
                     bf16_t hh, ll;
                     ka2[cc] = (bf16_t)ka;
