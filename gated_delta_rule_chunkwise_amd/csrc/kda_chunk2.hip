@@ -96,11 +96,36 @@ int64_t max_chunks(const ChunkArgs &a) {
 constexpr int64_t kSegRecords = 2048;
 
 // Chunks per segment, or 0 when the call runs as one pass.
+int64_t pipe_chunks(const ChunkArgs &a);
 int64_t segment_chunks(const ChunkArgs &a) {
-    if (a.varlen || a.num_seqs != 1) return 0;
+    if (a.varlen || a.num_seqs != 1 || pipe_chunks(a) > 0) return 0;
     const int64_t per = kSegRecords / a.H;
     const int64_t nch = (a.seq_len + kC - 1) / kC;
     return (per >= 1 && nch > per) ? per : 0;
+}
+
+// Pipelined segments (chunk_pipe_kernel) for one sequence whose state pass
+// has at most half as many workgroups as the chip has compute units (256):
+// d_k = 128, per-channel or per-head gates, input as given.  Each segment holds
+// half the sequence, at most kPipeRecords chunk-heads, so that the two record
+// buffers together stay within the last-level cache; sequences shorter than
+// kPipeMinChunks chunks run as one pass.  (Measured at H = 16: two segments
+// beat four or eight, since a prep workgroup alone on its compute unit hides
+// less of its latency than two.)
+constexpr int64_t kPipeStateBlocks = 128;
+constexpr int64_t kPipeRecords = 1024;
+constexpr int64_t kPipeMinChunks = 16;
+int64_t state_grid(int64_t chains, int nvb);
+
+// Chunks per pipelined segment, or 0 when the call does not pipeline.
+int64_t pipe_chunks(const ChunkArgs &a) {
+    if (a.varlen || a.num_seqs != 1 || a.d_k != 128 || a.prologue || a.w_write) return 0;
+    if (state_grid(a.H, a.d_v / 16) > kPipeStateBlocks) return 0;
+    const int64_t nch = (a.seq_len + kC - 1) / kC;
+    if (nch < kPipeMinChunks) return 0;
+    int64_t per = (nch + 1) / 2;
+    if (per * a.H > kPipeRecords) per = kPipeRecords / a.H;
+    return per >= 1 ? per : 0;
 }
 
 size_t carry_bytes(const ChunkArgs &a) { return ((size_t)a.H * a.d_k * a.d_v * 4 + 255) / 256 * 256; }
@@ -289,8 +314,10 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
 // applied to the fp32 results, and the state-side operands take no anchor.
 // DEC: beta erases and wr writes (decoupled strengths): A and W take beta, U0
 // takes wr.
+// The body of one prep workgroup (threads 0..kThreads-1) for chunk-head bid.
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
-__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
+__device__ __forceinline__ void prep_body(
+    PrepSmem<DK, DV> &sm, const unsigned bid,
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
     const int32_t *__restrict__ cu,
@@ -302,17 +329,16 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     constexpr bool SG = GM != kGatePerChannel;   // one decay per (token, head), or none
     typedef PrepSmem<DK, DV> Sm;
     typedef Rec<DK, DV> RL;
-    __shared__ Sm sm;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int64_t chunk = blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
+    const int64_t chunk = bid / H;
+    const int h = (int)(bid % H);
     int64_t n, t0;
     int nv;
     if (!locate_chunk(chunk, cu, chunk_off, N, T, n, t0, nv)) return;
-    uint8_t *rec = recs + (size_t)blockIdx.x * RL::BYTES;
+    uint8_t *rec = recs + (size_t)bid * RL::BYTES;
     float *gCol = reinterpret_cast<float *>(rec + RL::COL);
     int32_t *gFlag = reinterpret_cast<int32_t *>(rec + RL::FLAG);
 
@@ -807,6 +833,18 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     }
 }
 
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
+__global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
+    const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, uint8_t *__restrict__ recs, int64_t N, int64_t T, int32_t H,
+    float lo) {
+    __shared__ PrepSmem<DK, DV> sm;
+    prep_body<DK, DV, IO, GT, PRO, GM, DEC>(sm, blockIdx.x, q, k, v, log_alpha, beta, wr, cu, chunk_off, recs, N, T,
+                                            H, lo);
+}
+
 // ---------------------------------------------------------------------------------
 // State: one workgroup of 16 waves per (sequence, head, BV value columns).  The
 // waves split into three roles with the same barrier sequence per chunk:
@@ -1197,20 +1235,21 @@ __device__ __forceinline__ bool state_block(int64_t id, int64_t chains, int nvb,
 }
 int64_t state_grid(int64_t chains, int nvb) { return (chains + kXcds - 1) / kXcds * kXcds * nvb; }
 
+// The body of one state workgroup (all kStateThreads threads) for block id bid.
 template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM, bool DEC>
-__global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
+__device__ __forceinline__ void state_body(
+    StateSmem<DK, DV, BV> &sm, const unsigned bid,
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
     const float *__restrict__ h0,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ chunk_off,
     const uint8_t *__restrict__ recs, IO *__restrict__ o, float *__restrict__ h_T, int64_t seq_len,
     int32_t H, int64_t num_chains, float lo) {
-    __shared__ StateSmem<DK, DV, BV> sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int64_t chain;
     int vb;
-    if (!state_block(blockIdx.x, num_chains, DV / BV, chain, vb)) return;
+    if (!state_block(bid, num_chains, DV / BV, chain, vb)) return;
     ChainRange cr;
     cr.n = chain / H;
     cr.h = (int)(chain % H);
@@ -1231,6 +1270,64 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
         output_role_loop<DK, DV, BV, IO>(sm, cr, o, H, w - 4, tid);
     else
         loader_role_loop<DK, DV, BV>(sm, cr, recs, H, tid - 512);
+}
+
+template <int DK, int DV, int BV, typename IO, typename GT, bool PRO, int GM, bool DEC>
+__global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
+    const float *__restrict__ h0,
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ chunk_off,
+    const uint8_t *__restrict__ recs, IO *__restrict__ o, float *__restrict__ h_T, int64_t seq_len,
+    int32_t H, int64_t num_chains, float lo) {
+    __shared__ StateSmem<DK, DV, BV> sm;
+    state_body<DK, DV, BV, IO, GT, PRO, GM, DEC>(sm, blockIdx.x, q, k, v, log_alpha, beta, wr, h0, cu_seqlens,
+                                                 chunk_off, recs, o, h_T, seq_len, H, num_chains, lo);
+}
+
+// Pipelined segments: one launch runs the state pass of segment j on its own
+// blocks and the prep pass of segment j+1 on the rest, so the compute units the
+// state pass leaves free (it has one workgroup per compute unit and fewer
+// workgroups than half the chip) prepare the next records meanwhile.  The two
+// halves share nothing: the state blocks read segment j's records and the prep
+// blocks write segment j+1's into the other buffer.  A prep block runs on its
+// first kWaves waves; the others end at once (a wave-uniform branch, so they
+// reach no barrier), and a barrier counts only the waves still running.
+template <typename IO, typename GT> struct StatePart {
+    const IO *q, *k, *v;
+    const GT *log_alpha, *beta;
+    const float *h0;
+    const uint8_t *recs;
+    IO *o;
+    float *h_T;
+    int64_t seq_len;
+    int64_t blocks;   // workgroups of the state pass
+};
+template <typename IO, typename GT> struct PrepPart {
+    const IO *q, *k, *v;
+    const GT *log_alpha, *beta;
+    uint8_t *recs;
+    int64_t seq_len;
+};
+template <int DK, int DV> union PipeSmem {
+    StateSmem<DK, DV, 16> st;
+    PrepSmem<DK, DV> pr;
+};
+
+template <int DK, int DV, typename IO, typename GT, int GM>
+__global__ __launch_bounds__(kStateThreads) void chunk_pipe_kernel(const StatePart<IO, GT> sp,
+                                                                   const PrepPart<IO, GT> pp, int32_t H, float lo) {
+    __shared__ PipeSmem<DK, DV> sm;
+    if (blockIdx.x < sp.blocks) {
+        state_body<DK, DV, 16, IO, GT, false, GM, false>(sm.st, blockIdx.x, sp.q, sp.k, sp.v, sp.log_alpha, sp.beta,
+                                                          nullptr, sp.h0, nullptr, nullptr, sp.recs, sp.o, sp.h_T,
+                                                          sp.seq_len, H, H, lo);
+    } else {
+        if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kWaves) return;   // uniform per wave
+        prep_body<DK, DV, IO, GT, false, GM, false>(sm.pr, blockIdx.x - (unsigned)sp.blocks, pp.q, pp.k, pp.v,
+                                                     pp.log_alpha, pp.beta, nullptr, nullptr, nullptr, pp.recs, 1,
+                                                     pp.seq_len, H, lo);
+    }
 }
 
 // One prep pass and one state pass over the tokens described by a, with the
@@ -1267,32 +1364,88 @@ hipError_t launch_pass(const ChunkArgs &a, int bv, int32_t *chunk_off, uint8_t *
     return hipGetLastError();
 }
 
+// The arguments of segment [t0, t0 + len) of a single sequence.
+template <int DK, int DV, typename IO, typename GT, int GM>
+ChunkArgs segment_args(const ChunkArgs &a, int64_t t0, int64_t len, float *carry) {
+    const int64_t H = a.H;
+    ChunkArgs s = a;
+    s.seq_len = len;
+    s.total_tokens = len;
+    s.q = (const IO *)a.q + t0 * H * DK;
+    s.k = (const IO *)a.k + t0 * H * DK;
+    s.v = (const IO *)a.v + t0 * H * DV;
+    s.o = (IO *)a.o + t0 * H * DV;
+    if (GM == kGatePerChannel) s.log_alpha = (const GT *)a.log_alpha + t0 * H * DK;
+    else if (GM == kGatePerHead) s.log_alpha = (const GT *)a.log_alpha + t0 * H;
+    s.beta = (const GT *)a.beta + t0 * H;
+    if (a.w_write) s.w_write = (const GT *)a.w_write + t0 * H;
+    s.h0 = t0 == 0 ? a.h0 : carry;
+    s.h_T = t0 + len >= a.seq_len ? a.h_T : carry;
+    return s;
+}
+
+// Pipelined segments of segc chunks: the prep pass of segment 0, then per
+// segment j one launch with the state pass of j and the prep pass of j + 1
+// (records alternating between two buffers), the last segment's state pass on
+// its own.  The state crosses segments in fp32 through carry, as with plain
+// segments.
+template <int DK, int DV, typename IO, typename GT, int GM>
+hipError_t launch_pipelined(const ChunkArgs &a, int64_t segc, float *carry, uint8_t *recs0, hipStream_t st) {
+    const int64_t seg = segc * kC;
+    uint8_t *recs[2] = {recs0, recs0 + (size_t)segc * a.H * Rec<DK, DV>::BYTES};
+    const int64_t nseg = (a.seq_len + seg - 1) / seg;
+    const int64_t blocks = state_grid(a.H, DV / 16);
+    auto seg_len = [&](int64_t j) { return a.seq_len - j * seg < seg ? a.seq_len - j * seg : seg; };
+    {
+        const ChunkArgs p = segment_args<DK, DV, IO, GT, GM>(a, 0, seg_len(0), carry);
+        const int64_t nprep = (p.seq_len + kC - 1) / kC * a.H;
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, DV, IO, GT, false, GM, false>), dim3((unsigned)nprep), dim3(kThreads),
+                           0, st, (const IO *)p.q, (const IO *)p.k, (const IO *)p.v, (const GT *)p.log_alpha,
+                           (const GT *)p.beta, (const GT *)nullptr, (const int32_t *)nullptr,
+                           (const int32_t *)nullptr, recs[0], (int64_t)1, p.seq_len, a.H, a.log_alpha_min);
+    }
+    for (int64_t j = 0; j < nseg; ++j) {
+        const ChunkArgs s = segment_args<DK, DV, IO, GT, GM>(a, j * seg, seg_len(j), carry);
+        if (j + 1 == nseg) {
+            hipLaunchKernelGGL((chunk_state_kernel<DK, DV, 16, IO, GT, false, GM, false>), dim3((unsigned)blocks),
+                               dim3(kStateThreads), 0, st, (const IO *)s.q, (const IO *)s.k, (const IO *)s.v,
+                               (const GT *)s.log_alpha, (const GT *)s.beta, (const GT *)nullptr, s.h0,
+                               (const int32_t *)nullptr, (const int32_t *)nullptr, (const uint8_t *)recs[j & 1],
+                               (IO *)s.o, s.h_T, s.seq_len, a.H, (int64_t)a.H, a.log_alpha_min);
+            break;
+        }
+        const ChunkArgs p = segment_args<DK, DV, IO, GT, GM>(a, (j + 1) * seg, seg_len(j + 1), carry);
+        const StatePart<IO, GT> sp{(const IO *)s.q, (const IO *)s.k, (const IO *)s.v, (const GT *)s.log_alpha,
+                                   (const GT *)s.beta, s.h0, recs[j & 1], (IO *)s.o, s.h_T, s.seq_len, blocks};
+        const PrepPart<IO, GT> pp{(const IO *)p.q, (const IO *)p.k, (const IO *)p.v, (const GT *)p.log_alpha,
+                                  (const GT *)p.beta, recs[(j + 1) & 1], p.seq_len};
+        const int64_t nprep = (p.seq_len + kC - 1) / kC * a.H;
+        hipLaunchKernelGGL((chunk_pipe_kernel<DK, DV, IO, GT, GM>), dim3((unsigned)(blocks + nprep)),
+                           dim3(kStateThreads), 0, st, sp, pp, a.H, a.log_alpha_min);
+    }
+    return hipGetLastError();
+}
+
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 hipError_t launch_two_kernel(const ChunkArgs &a, int bv, hipStream_t st) {
     uint8_t *ws = reinterpret_cast<uint8_t *>(a.workspace);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + kHeaderBytes);
     uint8_t *after_plan = ws + kHeaderBytes + plan_bytes(a.num_seqs);
+    if constexpr (DK == 128 && !PRO && !DEC) {
+        const int64_t pc = pipe_chunks(a);
+        if (pc > 0)
+            return launch_pipelined<DK, DV, IO, GT, GM>(a, pc, reinterpret_cast<float *>(after_plan),
+                                                        after_plan + carry_bytes(a), st);
+    }
     const int64_t segc = segment_chunks(a);
     if (segc == 0) return launch_pass<DK, DV, IO, GT, PRO, GM, DEC>(a, bv, chunk_off, after_plan, st);
     // segments of one sequence: the state is carried in the workspace
     float *carry = reinterpret_cast<float *>(after_plan);
     uint8_t *recs = after_plan + carry_bytes(a);
-    const int64_t seg = segc * kC, H = a.H;
+    const int64_t seg = segc * kC;
     for (int64_t t0 = 0; t0 < a.seq_len; t0 += seg) {
         const int64_t len = a.seq_len - t0 < seg ? a.seq_len - t0 : seg;
-        ChunkArgs s = a;
-        s.seq_len = len;
-        s.total_tokens = len;
-        s.q = (const IO *)a.q + t0 * H * DK;
-        s.k = (const IO *)a.k + t0 * H * DK;
-        s.v = (const IO *)a.v + t0 * H * DV;
-        s.o = (IO *)a.o + t0 * H * DV;
-        if (GM == kGatePerChannel) s.log_alpha = (const GT *)a.log_alpha + t0 * H * DK;
-        else if (GM == kGatePerHead) s.log_alpha = (const GT *)a.log_alpha + t0 * H;
-        s.beta = (const GT *)a.beta + t0 * H;
-        if (a.w_write) s.w_write = (const GT *)a.w_write + t0 * H;
-        s.h0 = t0 == 0 ? a.h0 : carry;
-        s.h_T = t0 + len >= a.seq_len ? a.h_T : carry;
+        const ChunkArgs s = segment_args<DK, DV, IO, GT, GM>(a, t0, len, carry);
         const hipError_t e = launch_pass<DK, DV, IO, GT, PRO, GM, DEC>(s, bv, chunk_off, recs, st);
         if (e != hipSuccess) return e;
     }
@@ -1330,6 +1483,8 @@ size_t record_bytes(int d_k, int d_v) {
 // the sequence runs in segments), the state kernel the padded chains times the
 // value-column blocks.
 bool two_kernel_grids_fit(const ChunkArgs &a, int bv) {
+    const int64_t pc = pipe_chunks(a);
+    if (pc > 0) return grid_fits(state_grid(a.H, a.d_v / 16) + pc * a.H, kStateThreads);
     const int64_t segc = segment_chunks(a);
     const int64_t nprep = (segc > 0 ? segc : max_chunks(a)) * a.H;
     const int width = (a.d_k == 64 && bv == 32) ? 32 : 16;
@@ -1338,6 +1493,10 @@ bool two_kernel_grids_fit(const ChunkArgs &a, int bv) {
 
 size_t two_kernel_workspace_bytes(const ChunkArgs &a) {
     if (a.total_tokens <= 0) return 0;
+    const int64_t pc = pipe_chunks(a);
+    if (pc > 0)
+        return kHeaderBytes + plan_bytes(a.num_seqs) + carry_bytes(a) +
+               2 * (size_t)pc * a.H * record_bytes(a.d_k, a.d_v);
     const int64_t segc = segment_chunks(a);
     if (segc > 0)
         return kHeaderBytes + plan_bytes(a.num_seqs) + carry_bytes(a) +

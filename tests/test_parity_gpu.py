@@ -713,6 +713,55 @@ def test_long_sequence_segments(kda):
     assert torch.equal(o1, o2) and torch.equal(h1, h2) and h2.data_ptr() == hh.data_ptr()
 
 
+# ------------------------------------------------------------------ pipelined segments
+# A single sequence at d_k = 128 whose state pass has at most 128 workgroups
+# (one per compute unit, half the chip) runs as two or more segments of at most
+# 1,024 chunk-heads, each launch running the state pass of one segment beside
+# the prep pass of the next.
+def test_pipelined_segments(kda):
+    """H = 16, d = 128, T = 8333 (131 chunks: segments of 64, 64 and 3
+    chunks, the last with a 13-token tail), h0 given; a near-reset across the
+    first segment boundary and one fast-forgetting channel inside the second
+    segment, whose records a combined launch prepares; then h_T written over
+    h0 in place."""
+    cfg = I.ChunkConfig("pipe", "bf16", "bf16", H=16, dk=128, dv=128, T=8333, seed=71, h0=True)
+    d = I.make_chunk_inputs(cfg)
+    la = d["log_alpha"].clone()
+    la[4090:4100] = -30.0          # tokens on both sides of the first boundary (4096)
+    la[5000:5064, 5, 11] = -3.0    # one channel of head 5 over a chunk of segment 2
+    d["log_alpha"] = la
+    check_against_oracle(kda, d, "bf16", what="pipelined segments H=16 T=%d" % cfg.T)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    o1, h1 = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=g["h0"])
+    hh = g["h0"].clone()
+    o2, h2 = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], h0=hh, h_T=hh)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2) and h2.data_ptr() == hh.data_ptr()
+
+
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("H,dv,T", [(5, 128, 2000), (32, 64, 1100)])
+def test_pipelined_segments_variants(kda, gate, H, dv, T):
+    """The pipelined launches with per-channel, per-head and no gates; H = 5
+    (state blocks padded to 8 chains, the padding blocks ending at once; two
+    segments of 16 chunks, the second ragged) and H = 32 at d_v = 64 (exactly
+    128 state blocks; segments of 9 and 9 chunks, the second ragged)."""
+    cfg = I.ChunkConfig("pipev", "bf16", "bf16", H=H, dk=128, dv=dv, T=T, seed=72, h0=True)
+    d = I.make_chunk_inputs(cfg)
+    if gate == "channel":
+        check_against_oracle(kda, d, "bf16", what="pipelined H=%d dv=%d T=%d" % (H, dv, T))
+        return
+    g = None
+    if gate == "scalar":
+        g = d["log_alpha"][:, :, 0].float().clone()
+        g[600:610] = -30.0
+        g = g.to(d["log_alpha"].dtype).contiguous()
+    else:
+        d["v"] = (d["v"].float() * 0.35).to(d["v"].dtype)
+        d["h0"] = d["h0"] * 0.35
+    _gdn_check(kda, d, g, "bf16", "pipelined gdn %s H=%d dv=%d T=%d" % (gate, H, dv, T))
+
+
 # ------------------------------------------------------------------ invariants at full size
 # Properties of the recurrence that hold at any size, checked on the GPU at the
 # long-context shape the benchmark times (no oracle needed): the value columns
