@@ -81,7 +81,11 @@ const char *kda_last_hip_error(void);
  *    state-independent operands, about 1.4 KiB per token-head; a single
  *    sequence longer than 2048 / H chunks runs in segments of that many chunks,
  *    so at most 2048 chunk-heads, about 190 MB, plus an fp32 state of
- *    H x d_k x d_v) and the fused kernel's segment states (a chain too long for
+ *    H x d_k x d_v; at d_k = 128 a single sequence of at least 16 chunks whose
+ *    state pass has at most 128 workgroups (H <= 16 at d_v = 128, H <= 32 at
+ *    d_v = 64) runs instead in segments of half its chunks, at most 1024
+ *    chunk-heads each, with two record buffers and the same fp32 state) and
+ *    the fused kernel's segment states (a chain too long for
  *    the parallelism of the GPU is cut into segments: three d_k x d_v fp32
  *    matrices per segment, at most about 72 MiB in all);
  *  - at d_k or d_v = 64 both kinds of batch run two passes (records as above).
