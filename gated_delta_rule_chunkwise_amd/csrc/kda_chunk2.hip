@@ -158,6 +158,8 @@ struct alignas(16) PrepSmem {
     float beta[kC];
     float wr[kC];                              // separate write strengths (DEC)
     float nrm[2][kC];                          // PRO: inverse norms of q and k per row (big channels only)
+    int32_t chan[16];                          // exact pairs: the channels of the current group
+    int32_t xbig[2];                           // paired prep: any big channel, their count
 };
 
 // Numbering of the key channels left out of the Gram products ("big": chunk
@@ -197,14 +199,18 @@ template <int DK> struct BigNumbering {
 // a 64x64 fp32 matrix: the A part (without beta) below the diagonal, the P part
 // on and above it (transposed), for the Gram epilogue.  Called by every wave
 // after the Gram operands are consumed; returns after a barrier.
-template <int DK, bool PRO, int GM, typename Sm, typename IO, typename GT>
-__device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64], const BigNumbering<DK> &bn,
+// PAIRED: two chunk-heads share the workgroup (and its barriers), so every
+// barrier here is taken for nbU channels, the larger count of the two; a half
+// with fewer (or none) does empty work between them.
+template <int DK, bool PRO, int GM, bool PAIRED, typename Sm, typename IO, typename GT>
+__device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64], const BigNumbering<DK> &bn, int nbU,
                                             const IO *__restrict__ q, const IO *__restrict__ k,
                                             const GT *__restrict__ log_alpha, int64_t t0, int nv, int H, int h,
                                             float lo, int w, int l, int tid) {
     constexpr int CPL = DK / 64;
     const int nb = bn.nb;
     const bool staged = nb <= 16;
+    const bool bars = PAIRED || !staged;   // the staging barriers are taken
     float *xG = staged ? reinterpret_cast<float *>(&sm.A[0][0]) : reinterpret_cast<float *>(&sm.t);
     float *xK = xG + kC * 16, *xQ = xK + kC * 16;
     float *xS = reinterpret_cast<float *>(&sm.t);
@@ -215,17 +221,20 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
     float sA[PPT], sP[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) sA[j] = sP[j] = 0.f;
-    __shared__ int32_t chan[16];   // the channel of number g0 + j
+    int32_t *chan = sm.chan;   // the channel of number g0 + j
 #pragma unroll 1
-    for (int g0 = 0; g0 < nb; g0 += 16) {
-        const int cnt = nb - g0 < 16 ? nb - g0 : 16;
-        if (!staged) {
+    for (int g0 = 0; g0 < nbU; g0 += 16) {
+        const int cnt = nb - g0 < 0 ? 0 : nb - g0 < 16 ? nb - g0 : 16;
+        if (bars) {
+            if (!staged) {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const int j = bn.slot[cc] - g0;
-                if (w == 0 && bigc[cc] && j >= 0 && j < 16) chan[j] = l * CPL + cc;
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const int j = bn.slot[cc] - g0;
+                    if (w == 0 && bigc[cc] && j >= 0 && j < 16) chan[j] = l * CPL + cc;
+                }
             }
             lds_barrier();
+            if (!staged) {
             // G of numbers g0 + 2w and g0 + 2w + 1: lane r holds token r
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
@@ -264,6 +273,7 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
                 xK[e] = kv;
                 xQ[e] = qv;
             }
+            }
             lds_barrier();
         }
 #pragma unroll
@@ -284,7 +294,7 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
                 sP[j] += b;
             }
         }
-        if (!staged) lds_barrier();   // staging read before it is overwritten
+        if (bars) lds_barrier();   // staging read before it is overwritten
     }
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
@@ -314,10 +324,15 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
 // applied to the fp32 results, and the state-side operands take no anchor.
 // DEC: beta erases and wr writes (decoupled strengths): A and W take beta, U0
 // takes wr.
-// The body of one prep workgroup (threads 0..kThreads-1) for chunk-head bid.
-template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
+// The body of one prep workgroup (threads tid = 0..kThreads-1) for chunk-head
+// bid.  PAIRED: two chunk-heads share a workgroup of 2 kThreads threads, each
+// half with its own LDS; every barrier is the whole workgroup's, so both halves
+// take the same barriers: the choice of Gram path and the number of exact-pair
+// groups follow the larger need of the two (partner: the other half's LDS, or
+// null when the other half has no chunk-head).
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC, bool PAIRED = false>
 __device__ __forceinline__ void prep_body(
-    PrepSmem<DK, DV> &sm, const unsigned bid,
+    PrepSmem<DK, DV> &sm, const PrepSmem<DK, DV> *partner, const int tid, const unsigned bid,
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const GT *__restrict__ log_alpha, const GT *__restrict__ beta, const GT *__restrict__ wr,
     const int32_t *__restrict__ cu,
@@ -330,7 +345,6 @@ __device__ __forceinline__ void prep_body(
     typedef PrepSmem<DK, DV> Sm;
     typedef Rec<DK, DV> RL;
 
-    const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
     const int64_t chunk = bid / H;
@@ -420,8 +434,9 @@ __device__ __forceinline__ void prep_body(
     for (int cc = 0; cc < CPL; ++cc) lbig = lbig || bigc[cc];
     const bool anybig = __ballot(lbig) != 0;   // same channels in every wave: uniform
     BigNumbering<DK> bn;
+    bn.nb = 0;
+    if (anybig || PAIRED) bn.init(bigc, l);
     if (anybig) {
-        bn.init(bigc, l);
         if (bn.nb <= 16) {   // stage the big channels' G, K, Q rows for the exact pairs
             float *xG = reinterpret_cast<float *>(&sm.A[0][0]);
             float *xK = xG + kC * 16, *xQ = xK + kC * 16;
@@ -442,6 +457,10 @@ __device__ __forceinline__ void prep_body(
         }
     }
     if (tid == 0) gFlag[0] = 0;
+    if (PAIRED && tid == 0) {   // read by the other half after the next barrier
+        sm.xbig[0] = anybig ? 1 : 0;
+        sm.xbig[1] = bn.nb;
+    }
     if constexpr (PRO) {
         if (anybig && l < 8) {   // for the exact pairs of the big channels
             sm.nrm[0][8 * w + l] = in.qs[l];
@@ -583,7 +602,15 @@ __device__ __forceinline__ void prep_body(
         // tiles w, w + 8 and (waves 0-3) w + 16: 0-9 are the lower 16x16 blocks of
         // A, 10-19 those of P (accumulated transposed)
         constexpr int NTL = 3;
-        if (!anybig) {
+        bool anyU = anybig;
+        int nbU = bn.nb;
+        if (PAIRED && partner != nullptr) {   // the same in every lane and wave of both halves
+            const int pbig = __builtin_amdgcn_readfirstlane(partner->xbig[0]);
+            const int pnb = __builtin_amdgcn_readfirstlane(partner->xbig[1]);
+            anyU = anyU || pbig != 0;
+            nbU = nbU > pnb ? nbU : pnb;
+        }
+        if (!anyU) {
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
                 if (t == 2 && w >= 4) break;
@@ -603,7 +630,7 @@ __device__ __forceinline__ void prep_body(
                 if (t < 2 || w < 4) gram(w + 8 * t, accs[t]);
             }
             lds_barrier();   // the Gram operands are consumed
-            exact_pairs<DK, PRO, GM>(sm, bigc, bn, q, k, log_alpha, t0, nv, H, h, lo, w, l, tid);
+            exact_pairs<DK, PRO, GM, PAIRED>(sm, bigc, bn, nbU, q, k, log_alpha, t0, nv, H, h, lo, w, l, tid);
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
                 if (t < 2 || w < 4) {
@@ -841,8 +868,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_prep_kernel(
     const int32_t *__restrict__ chunk_off, uint8_t *__restrict__ recs, int64_t N, int64_t T, int32_t H,
     float lo) {
     __shared__ PrepSmem<DK, DV> sm;
-    prep_body<DK, DV, IO, GT, PRO, GM, DEC>(sm, blockIdx.x, q, k, v, log_alpha, beta, wr, cu, chunk_off, recs, N, T,
-                                            H, lo);
+    prep_body<DK, DV, IO, GT, PRO, GM, DEC>(sm, nullptr, threadIdx.x, blockIdx.x, q, k, v, log_alpha, beta, wr, cu,
+                                            chunk_off, recs, N, T, H, lo);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1289,10 +1316,12 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
 // blocks and the prep pass of segment j+1 on the rest, so the compute units the
 // state pass leaves free (it has one workgroup per compute unit and fewer
 // workgroups than half the chip) prepare the next records meanwhile.  The two
-// halves share nothing: the state blocks read segment j's records and the prep
-// blocks write segment j+1's into the other buffer.  A prep block runs on its
-// first kWaves waves; the others end at once (a wave-uniform branch, so they
-// reach no barrier), and a barrier counts only the waves still running.
+// parts share nothing: the state blocks read segment j's records and the prep
+// blocks write segment j+1's into the other buffer.  A prep block takes two
+// chunk-heads, one per half of its 16 waves, each half with its own LDS, so a
+// compute unit prepares two at a time as with the prep kernel.  A half without
+// a chunk-head (an odd count) ends at once, on a wave-uniform branch, so it
+// reaches no barrier; a barrier counts only the waves still running.
 template <typename IO, typename GT> struct StatePart {
     const IO *q, *k, *v;
     const GT *log_alpha, *beta;
@@ -1308,10 +1337,11 @@ template <typename IO, typename GT> struct PrepPart {
     const GT *log_alpha, *beta;
     uint8_t *recs;
     int64_t seq_len;
+    unsigned count;   // chunk-heads of the segment
 };
 template <int DK, int DV> union PipeSmem {
     StateSmem<DK, DV, 16> st;
-    PrepSmem<DK, DV> pr;
+    PrepSmem<DK, DV> pr[2];
 };
 
 template <int DK, int DV, typename IO, typename GT, int GM>
@@ -1323,10 +1353,14 @@ __global__ __launch_bounds__(kStateThreads) void chunk_pipe_kernel(const StatePa
                                                           nullptr, sp.h0, nullptr, nullptr, sp.recs, sp.o, sp.h_T,
                                                           sp.seq_len, H, H, lo);
     } else {
-        if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kWaves) return;   // uniform per wave
-        prep_body<DK, DV, IO, GT, false, GM, false>(sm.pr, blockIdx.x - (unsigned)sp.blocks, pp.q, pp.k, pp.v,
-                                                     pp.log_alpha, pp.beta, nullptr, nullptr, nullptr, pp.recs, 1,
-                                                     pp.seq_len, H, lo);
+        // waves 0-7 take chunk-head 2b, waves 8-15 chunk-head 2b + 1
+        const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= kWaves ? 1 : 0;
+        const unsigned bid = 2 * (blockIdx.x - (unsigned)sp.blocks) + half;
+        if (bid >= pp.count) return;   // uniform per wave
+        const PrepSmem<DK, DV> *partner = (bid ^ 1u) < pp.count ? &sm.pr[half ^ 1] : nullptr;
+        prep_body<DK, DV, IO, GT, false, GM, false, true>(sm.pr[half], partner, threadIdx.x & (kThreads - 1), bid,
+                                                           pp.q, pp.k, pp.v, pp.log_alpha, pp.beta, nullptr, nullptr,
+                                                           nullptr, pp.recs, 1, pp.seq_len, H, lo);
     }
 }
 
@@ -1417,10 +1451,10 @@ hipError_t launch_pipelined(const ChunkArgs &a, int64_t segc, float *carry, uint
         const ChunkArgs p = segment_args<DK, DV, IO, GT, GM>(a, (j + 1) * seg, seg_len(j + 1), carry);
         const StatePart<IO, GT> sp{(const IO *)s.q, (const IO *)s.k, (const IO *)s.v, (const GT *)s.log_alpha,
                                    (const GT *)s.beta, s.h0, recs[j & 1], (IO *)s.o, s.h_T, s.seq_len, blocks};
-        const PrepPart<IO, GT> pp{(const IO *)p.q, (const IO *)p.k, (const IO *)p.v, (const GT *)p.log_alpha,
-                                  (const GT *)p.beta, recs[(j + 1) & 1], p.seq_len};
         const int64_t nprep = (p.seq_len + kC - 1) / kC * a.H;
-        hipLaunchKernelGGL((chunk_pipe_kernel<DK, DV, IO, GT, GM>), dim3((unsigned)(blocks + nprep)),
+        const PrepPart<IO, GT> pp{(const IO *)p.q, (const IO *)p.k, (const IO *)p.v, (const GT *)p.log_alpha,
+                                  (const GT *)p.beta, recs[(j + 1) & 1], p.seq_len, (unsigned)nprep};
+        hipLaunchKernelGGL((chunk_pipe_kernel<DK, DV, IO, GT, GM>), dim3((unsigned)(blocks + (nprep + 1) / 2)),
                            dim3(kStateThreads), 0, st, sp, pp, a.H, a.log_alpha_min);
     }
     return hipGetLastError();
@@ -1484,7 +1518,7 @@ size_t record_bytes(int d_k, int d_v) {
 // value-column blocks.
 bool two_kernel_grids_fit(const ChunkArgs &a, int bv) {
     const int64_t pc = pipe_chunks(a);
-    if (pc > 0) return grid_fits(state_grid(a.H, a.d_v / 16) + pc * a.H, kStateThreads);
+    if (pc > 0) return grid_fits(state_grid(a.H, a.d_v / 16) + (pc * a.H + 1) / 2, kStateThreads);
     const int64_t segc = segment_chunks(a);
     const int64_t nprep = (segc > 0 ? segc : max_chunks(a)) * a.H;
     const int width = (a.d_k == 64 && bv == 32) ? 32 : 16;

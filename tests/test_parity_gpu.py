@@ -739,6 +739,32 @@ def test_pipelined_segments(kda):
     assert torch.equal(o1, o2) and torch.equal(h1, h2) and h2.data_ptr() == hh.data_ptr()
 
 
+def test_pipelined_paired_prep_strong_decay(kda):
+    """The combined launch prepares two chunk-heads per workgroup (chunk-heads
+    2i and 2i + 1: consecutive heads of a chunk, or the last head of one chunk
+    and the first of the next), which must agree on the Gram path and the
+    number of exact-pair groups.  H = 5, T = 1940 (31 chunks: segments of 16 and
+    15 chunks, the second with a 20-token tail and an odd 75 chunk-heads, so
+    its last workgroup prepares one).  In chunk 2 of the second segment: head 1
+    past the anchored range on every channel (128 big channels, staged from
+    the inputs) beside head 0 with none; head 2 with three big channels
+    (staged from registers) beside head 3 with none; head 4 with three beside
+    head 0 of chunk 3 with twenty.  In the partial last chunk head 4, the lone chunk-head, has one;
+    segment 0 (the prep kernel alone) has a near-reset too."""
+    cfg = I.ChunkConfig("pipepair", "bf16", "bf16", H=5, dk=128, dv=128, T=1940, seed=73, h0=True)
+    d = I.make_chunk_inputs(cfg)
+    la = d["log_alpha"].clone()
+    c2 = 1024 + 128                  # chunk 2 of the second segment
+    la[300, 2] = -30.0               # segment 0, head 2: a reset
+    la[c2 + 5:c2 + 8, 1] = -30.0     # head 1: every channel, over 80 nats
+    la[c2:c2 + 64, 2, 4:7] = -2.0    # head 2: three channels, -128 each
+    la[c2:c2 + 64, 4, 0:3] = -2.0    # head 4: three channels
+    la[c2 + 64:c2 + 128, 0, 20:40] = -2.0   # head 0 of chunk 3: twenty channels
+    la[1920:1940, 4, 9] = -5.0       # head 4, partial last chunk: -100 on one channel
+    d["log_alpha"] = la
+    check_against_oracle(kda, d, "bf16", what="pipelined paired prep, strong decay")
+
+
 @pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
 @pytest.mark.parametrize("H,dv,T", [(5, 128, 2000), (32, 64, 1100)])
 def test_pipelined_segments_variants(kda, gate, H, dv, T):
