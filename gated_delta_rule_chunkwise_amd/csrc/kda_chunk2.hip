@@ -110,8 +110,7 @@ int64_t segment_chunks(const ChunkArgs &a) {
 // half the sequence, at most kPipeRecords chunk-heads, so that the two record
 // buffers together stay within the last-level cache; sequences shorter than
 // kPipeMinChunks chunks run as one pass.  (Measured at H = 16: two segments
-// beat four or eight, since a prep workgroup alone on its compute unit hides
-// less of its latency than two.)
+// beat four or eight, each launch boundary costing a few microseconds.)
 constexpr int64_t kPipeStateBlocks = 128;
 constexpr int64_t kPipeRecords = 1024;
 constexpr int64_t kPipeMinChunks = 16;
