@@ -826,9 +826,8 @@ __device__ __forceinline__ void prep_body(
                 }
             }
         }
-        const int ncol = isW ? DK / 16 : DV / 16;
-        for (int ct = 0; ct < ncol; ++ct) {
-            const bf16_t *bsrc = isW ? &sm.KAt[16 * ct + lr][8 * lg] : &sm.Vt[16 * ct + lr][8 * lg];
+        // one 16-column tile of Tb times the operand rows at src
+        auto tb_tile = [&](const bf16_t *bsrc) {
             f32x4_t acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -838,10 +837,19 @@ __device__ __forceinline__ void prep_body(
                     acc = mfma16(tlo[ks], b, acc);
                 }
             }
-            if (isW) {
+            return acc;
+        };
+        if (isW) {
+#pragma unroll
+            for (int ct = 0; ct < DK / 16; ++ct) {
+                const f32x4_t acc = tb_tile(&sm.KAt[16 * ct + lr][8 * lg]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sm.KA[16 * rb + 4 * lg + e][16 * ct + lr] = (bf16_t)(-acc[e]);
-            } else {
+            }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < DV / 16; ++ct) {
+                const f32x4_t acc = tb_tile(&sm.Vt[16 * ct + lr][8 * lg]);
                 *reinterpret_cast<f32x4_t *>(rec + RL::U0 + (size_t)(rb * (DV / 16) + ct) * RL::FRAG + l * 16) = acc;
             }
         }
