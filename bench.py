@@ -191,6 +191,26 @@ def cpu_baseline_bwd(d, go, heads, T_sample, H_total):
                       "%.1f s); tokens/s = token-heads/s / %d heads" % (heads, T_sample, tok_heads, dt, H_total)}
 
 
+# Workloads that --only can select, each timed by one section of main().
+ONLY = ("c3", "prologue", "gdn_gated", "gdn_deltanet", "decoupled", "strong", "c0", "c1", "c2", "c1_fp32",
+        "bwd", "bwd_prologue", "bwd_decoupled", "bwd_gdn", "bwd_c2", "decode")
+
+
+def time_pipelined(fn, calls, stream):
+    """Mean time per call of `calls` back-to-back calls between one event pair:
+    the device time per call once the host's per-call marshalling overlaps the
+    previous call (for calls too short to hide it one at a time)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +229,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--only", choices=ONLY, default=None,
+                    help="time one workload alone (for per-workload profiler runs); the JSON line then "
+                         "holds that entry and the number of entry-point calls made")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -226,6 +249,10 @@ def main():
     kda.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    calls = {}   # entry-point calls made per workload (for profiler runs)
+
+    def want(name, skip_flag=False):
+        return (args.only is None and not skip_flag) or args.only == name
 
     # ---------------- chunk_fwd on the long-context prefill workload
     cfg = I.C3
@@ -235,10 +262,14 @@ def main():
     hT = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
     args_c = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
     fn = lambda: kda.kda_chunk_fwd(*args_c, o=o, h_T=hT)
-    per, wall = time_launches(fn, args.steps, args.warmup, stream)
-    ms = float(np.mean(per))
-    print("chunk_fwd per-launch ms: mean %.4f median %.4f min %.4f" % (ms, np.median(per), min(per)),
-          file=sys.stderr, flush=True)
+    if want("c3"):
+        per, wall = time_launches(fn, args.steps, args.warmup, stream)
+        calls["c3"] = args.steps + args.warmup
+        ms = float(np.mean(per))
+        print("chunk_fwd per-launch ms: mean %.4f median %.4f min %.4f" % (ms, np.median(per), min(per)),
+              file=sys.stderr, flush=True)
+    else:
+        ms = float("nan")
     tok_heads = T * H
     alg_b = chunk_alg_bytes(tok_heads, H, dk, dv)
     alg_f = chunk_alg_flops(tok_heads, dk, dv)
@@ -246,28 +277,33 @@ def main():
     traffic = load_traffic("chunk_fwd_prefill_h32_t65536_traffic.json", digest)
     counters = load_mfma_counters("chunk_fwd_prefill_h32_t65536_traffic.json", digest)
     # one kda_chunk_fwd call = chunk_prep_kernel + chunk_state_kernel on one stream.
-    # The metric is matrix-core utilisation: algorithmic flops per call over the
-    # time per call, against the bf16 dense peak.  By arithmetic intensity
-    # (about 110 flop/B against the chip's 312) the bytes bind first: the HBM
-    # view is kept alongside.  "traffic" is FETCH_SIZE + WRITE_SIZE per call
-    # (bytes leaving L2, Infinity Cache hits included) scaled by a plain copy.
-    roof = {"bound": "mfma", "achieved": alg_f / (ms * 1e-3) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-            "traffic": traffic,
+    # Roofline: the call's arithmetic intensity (algorithmic flops over
+    # algorithmic bytes, about 110 flop/B) lies below the chip's ridge point
+    # (2,500 TFLOP/s over 8 TB/s = 312 flop/B), so the bytes bind first and the
+    # roofline is HBM's; at that intensity the matrix cores can be at most
+    # 110/312 = 35% busy.  The metric's matrix-core share (algorithmic, and
+    # counter-measured) is reported under "mfma".  "traffic" is FETCH_SIZE +
+    # WRITE_SIZE per call (bytes leaving L2, Infinity Cache hits included)
+    # scaled by a plain copy.
+    roof = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
             "traffic_counted": "FETCH_SIZE + WRITE_SIZE (L2 misses, Infinity Cache hits included), bytes per call",
-            "counter_busy_frac": None if counters is None else counters["busy_pct"] / 100.0,
             "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,128,bf16,bf16,false,0> + "
                       "chunk_state_kernel<128,128,16,bf16,bf16,false,0>",
-            "alg_flops_per_launch": alg_f}
+            "alg_bytes_per_launch": alg_b, "alg_flops_per_launch": alg_f,
+            "arith_intensity_flop_per_byte": alg_f / alg_b,
+            "ridge_flop_per_byte": BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)}
     hbm = {"bound": "hbm", "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg_b,
            "floor_ms": alg_b / (HBM_PEAK_GBS * 1e9) * 1e3}
     mfma = {"alg_flops_per_launch": alg_f, "achieved_tflops": alg_f / (ms * 1e-3) / 1e12,
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
             "frac": alg_f / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "frac_attainable_at_intensity": alg_f / alg_b / (BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)),
+            "counter_busy_frac": None if counters is None else counters["busy_pct"] / 100.0,
             "counters": counters}
 
-    out = {"metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+    out = {} if not want("c3") else {"metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "kda_chunk_fwd bf16 B=1 H=32 T=65536 d_k=d_v=128 chunk=64, "
@@ -277,12 +313,13 @@ def main():
            "roofline": roof, "hbm": hbm, "mfma": mfma, "source_digest": digest}
 
     # ---------------- the same prefill on raw projections (fused input prologue)
-    if not args.no_prologue:
+    if want("prologue", args.no_prologue):
         dr = I.make_chunk_raw_inputs(cfg, device=dev, gate="uniform")
         args_p = (dr["q_raw"], dr["k_raw"], dr["v"], dr["gate_pre"], dr["beta_pre"])
         lo = -30.0
         fnp = lambda: kda.kda_chunk_fwd_prologue(*args_p, lo, o=o, h_T=hT)
         per_p, _ = time_launches(fnp, args.steps, args.warmup, stream)
+        calls["prologue"] = args.steps + args.warmup
         pms = float(np.mean(per_p))
         # a separate prologue pass would read q, k, the gate and beta raw and write
         # them back mapped: twice their bytes per token-head
@@ -303,14 +340,17 @@ def main():
         del dr, args_p
 
     # ---------------- scalar gates: Gated DeltaNet and DeltaNet on the same shape
-    if not args.no_gdn:
+    if want("gdn_gated", args.no_gdn) or want("gdn_deltanet", args.no_gdn):
         g = d["log_alpha"][:, :, 0].contiguous()   # c3's draw, one decay per (token, head)
         gdn = {"workload": "kda_gdn_chunk_fwd bf16 B=1 H=32 T=65536 d_k=d_v=128 chunk=64, log_alpha "
                            "[T, H] = the first channel of the same per-channel draw; and with "
                            "log_alpha = NULL (DeltaNet)"}
         for key, gate, ng in (("gated", g, 1), ("deltanet", None, 0)):
+            if not want("gdn_" + key, args.no_gdn):
+                continue
             fng = lambda: kda.kda_gdn_chunk_fwd(d["q"], d["k"], d["v"], gate, d["beta"], o=o, h_T=hT)
             per_g, _ = time_launches(fng, args.steps, args.warmup, stream)
+            calls["gdn_" + key] = args.steps + args.warmup
             gms = float(np.mean(per_g))
             gb = chunk_alg_bytes(tok_heads, H, dk, dv, gate_per_th=ng)
             gdn[key] = {"ms_per_step": gms, "tokens_per_s": T / (gms * 1e-3), "vs_plain_ms": gms / ms,
@@ -323,11 +363,12 @@ def main():
         del g
 
     # ---------------- separate erase and write strengths on the same inputs
-    if not args.no_decoupled:
+    if want("decoupled", args.no_decoupled):
         wv = I.draw_strength(d["beta"].shape, 5200, d["beta"].dtype, device=dev)
         fnd = lambda: kda.kda_chunk_fwd_decoupled(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], wv,
                                                   o=o, h_T=hT)
         per_d, _ = time_launches(fnd, args.steps, args.warmup, stream)
+        calls["decoupled"] = args.steps + args.warmup
         dms_ = float(np.mean(per_d))
         db_ = alg_b + tok_heads * 2       # plus the write strength, 2 B per token-head
         out["decoupled"] = {
@@ -341,11 +382,12 @@ def main():
         del wv
 
     # ---------------- strong decay: one fast-forgetting key channel per head
-    if not args.no_strong:
+    if want("strong", args.no_strong):
         la_s = d["log_alpha"].clone()
         la_s[:, :, 0] = -3.0   # channel 0 of every head: log alpha = -3 on every token
         fns = lambda: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], la_s, d["beta"], o=o, h_T=hT)
         per_s, _ = time_launches(fns, max(2, args.steps // 4), 1, stream)
+        calls["strong"] = max(2, args.steps // 4) + 1
         sms = float(np.mean(per_s))
         out["strong_decay"] = {
             "workload": "kda_chunk_fwd on the same inputs with key channel 0 of every head at log alpha = -3 "
@@ -355,7 +397,8 @@ def main():
         del la_s
 
     # ---------------- the other prefill workloads: short sequence and packed batch
-    if not args.no_other:
+    other_keys = ("c0", "c1", "c2", "c1_fp32")
+    if any(want(k, args.no_other) for k in other_keys) or want("bwd_c2", args.no_other or args.no_backward):
         other = {}
         # fp32 I/O at d = 128 runs on the backward's kernels (kda_bwd.hip)
         f32_digest = source_digest(CHUNK_SOURCES + ("kda_bwd.hip",))
@@ -365,6 +408,10 @@ def main():
         c1_f32 = I.ChunkConfig("fp32 B=1 H=16 T=4096 d=128 (c1's shape and draws in fp32)", "f32", "f32",
                                H=16, dk=128, dv=128, T=4096, seed=I.C1.seed)
         for key, ocfg in (("c0", I.C0), ("c1", I.C1), ("c2", I.C2), ("c1_fp32", c1_f32)):
+            fwd_on = want(key, args.no_other)
+            bwd_on = key == "c2" and want("bwd_c2", args.no_other or args.no_backward)
+            if not (fwd_on or bwd_on):
+                continue
             dd = I.make_chunk_inputs(ocfg, device=dev)
             Tt, Hh = dd["q"].shape[0], dd["q"].shape[1]
             odk, odv = dd["q"].shape[2], dd["v"].shape[2]
@@ -374,25 +421,37 @@ def main():
             o2 = torch.empty_like(dd["v"])
             fno = lambda: kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], h0=dd["h0"],
                                             cu_seqlens=cu, o=o2, h_T=h_T)
-            per_o, _ = time_launches(fno, args.steps, args.warmup, stream)
-            oms = float(np.mean(per_o))
             ob = chunk_alg_bytes(Tt * Hh, nseq * Hh * (2 if dd["h0"] is not None else 1), odk, odv,
                                  io_b=dd["q"].element_size(), gate_b=dd["log_alpha"].element_size())
             of = chunk_alg_flops(Tt * Hh, odk, odv)
-            other[key] = {"workload": "kda_chunk_fwd, " + ocfg.name + (" (%d sequences, %d tokens)" % (nseq, Tt)),
-                          "ms_per_step": oms, "tokens_per_s": Tt / (oms * 1e-3),
-                          "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob,
-                          "alg_flops_per_launch": of,
-                          "mfma_frac": of / (oms * 1e-3) / 1e12 /
-                          (BF16_MFMA_PEAK_TFLOPS if dd["q"].dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS),
-                          "traffic": load_traffic(profile_name[key] + "_traffic.json",
-                                                  f32_digest if key == "c1_fp32" else digest)}
-            if key == "c2" and not args.no_backward:
+            other[key] = {}
+            if fwd_on:
+                per_o, _ = time_launches(fno, args.steps, args.warmup, stream)
+                oms = float(np.mean(per_o))
+                # the same calls back to back: the device time per call once the
+                # host's marshalling of one call overlaps the previous one
+                npipe = 4 * args.steps
+                pipe = time_pipelined(fno, npipe, stream)
+                calls[key] = args.steps + args.warmup + 1 + npipe
+                other[key] = {"workload": "kda_chunk_fwd, " + ocfg.name + (" (%d sequences, %d tokens)" % (nseq, Tt)),
+                              "ms_per_step": oms, "tokens_per_s_per_call_events": Tt / (oms * 1e-3),
+                              "ms_per_call_pipelined": pipe, "tokens_per_s": Tt / (pipe * 1e-3),
+                              "timing": "ms_per_step: one event pair around each call (host marshalling "
+                                        "included when the call is shorter than it); tokens_per_s: %d calls "
+                                        "back to back between one event pair" % npipe,
+                              "hbm_frac": ob / (pipe * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": ob,
+                              "alg_flops_per_launch": of,
+                              "mfma_frac": of / (pipe * 1e-3) / 1e12 /
+                              (BF16_MFMA_PEAK_TFLOPS if dd["q"].dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS),
+                              "traffic": load_traffic(profile_name[key] + "_traffic.json",
+                                                      f32_digest if key == "c1_fp32" else digest)}
+            if bwd_on:
                 # the packed batch's gradients (grad_o ~ N(0,1), grad_hT ~ N(0, 0.1^2))
                 go2, ghT2 = I.make_upstream_grads(dd, 3450, device=dev)
                 fnb2 = lambda: kda.kda_chunk_bwd(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], go2,
                                                  h0=dd["h0"], grad_hT=ghT2, cu_seqlens=cu)
                 per_b2, _ = time_launches(fnb2, args.steps, args.warmup, stream)
+                calls["bwd_c2"] = args.steps + args.warmup
                 b2 = float(np.mean(per_b2))
                 other[key]["backward"] = {"ms_per_step": b2, "tokens_per_s": Tt / (b2 * 1e-3),
                                           "alg_flops_frac_fp32": bwd_alg_flops(Tt * Hh, dk, dv) / (b2 * 1e-3) / 1e12
@@ -402,13 +461,17 @@ def main():
         out["other_workloads"] = other
 
     # ---------------- backward of the same prefill
-    if not args.no_backward:
+    if any(want(k, args.no_backward) for k in ("bwd", "bwd_prologue", "bwd_decoupled", "bwd_gdn")):
         go, _ = I.make_upstream_grads(d, 3400, device=dev, with_state=False)
         ws = torch.empty(kda.kda_chunk_bwd_workspace_size(1, T, H, dk, dv, 0, kda.KDA_BF16),
                          dtype=torch.uint8, device=dev)
         a4 = [x.unsqueeze(0) for x in args_c]
         fnb = lambda: kda.kda_chunk_bwd(*a4, go.unsqueeze(0), want_grad_h0=False, workspace=ws)
+        bms = float("nan")
+        out["backward"] = {}
+    if want("bwd", args.no_backward):
         per_b, _ = time_launches(fnb, args.steps, args.warmup, stream)
+        calls["bwd"] = args.steps + args.warmup
         bms = float(np.mean(per_b))
         bf = bwd_alg_flops(tok_heads, dk, dv)
         bb = bwd_alg_bytes(tok_heads, dk, dv)
@@ -428,7 +491,8 @@ def main():
             "hbm": {"alg_bytes_per_launch": bb, "achieved_gbs": bb / (bms * 1e-3) / 1e9,
                     "frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},
             "workspace_bytes": ws.numel()}
-        if not args.no_prologue:
+    if "backward" in out:
+        if want("bwd_prologue", args.no_backward or args.no_prologue):
             # the same gradients taken through the input prologue, on raw projections
             del ws
             dr = I.make_chunk_raw_inputs(cfg, device=dev, gate="uniform")
@@ -437,6 +501,7 @@ def main():
             r4 = [dr[n].unsqueeze(0) for n in ("q_raw", "k_raw", "v", "gate_pre", "beta_pre")]
             fnp = lambda: kda.kda_chunk_bwd_prologue(*r4, -30.0, go.unsqueeze(0), want_grad_h0=False, workspace=ws)
             per_pb, _ = time_launches(fnp, args.steps, args.warmup, stream)
+            calls["bwd_prologue"] = args.steps + args.warmup
             pbms = float(np.mean(per_pb))
             out["backward"]["prologue"] = {
                 "workload": "kda_chunk_bwd_prologue on raw projections of the same shape (as the forward's "
@@ -446,18 +511,19 @@ def main():
             del dr, r4, ws
             ws = torch.empty(kda.kda_chunk_bwd_workspace_size(1, T, H, dk, dv, 0, kda.KDA_BF16),
                              dtype=torch.uint8, device=dev)
-        if not args.no_decoupled:
+        if want("bwd_decoupled", args.no_backward or args.no_decoupled):
             # separate erase and write strengths: beta erases, a write strength
             # drawn like beta from its own seed writes
             wv4 = I.draw_strength(d["beta"].shape, 5200, d["beta"].dtype, device=dev).unsqueeze(0)
             fnd = lambda: kda.kda_chunk_bwd_decoupled(*a4, wv4, go.unsqueeze(0), want_grad_h0=False, workspace=ws)
             per_db, _ = time_launches(fnd, args.steps, args.warmup, stream)
+            calls["bwd_decoupled"] = args.steps + args.warmup
             dbms = float(np.mean(per_db))
             out["backward"]["decoupled"] = {
                 "workload": "kda_chunk_bwd_decoupled on the same inputs, beta as the erase strength",
                 "ms_per_step": dbms, "tokens_per_s": T / (dbms * 1e-3), "vs_kda_backward_ms": dbms / bms}
             del wv4
-        if not args.no_gdn:
+        if want("bwd_gdn", args.no_backward or args.no_gdn):
             # the scalar-gate backward (Gated DeltaNet) on the same inputs, the
             # gate being the first channel of the per-channel draw
             del ws
@@ -467,18 +533,19 @@ def main():
             fng = lambda: kda.kda_gdn_chunk_bwd(a4[0], a4[1], a4[2], g4, a4[4], go.unsqueeze(0),
                                                 want_grad_h0=False, workspace=ws)
             per_gb, _ = time_launches(fng, args.steps, args.warmup, stream)
+            calls["bwd_gdn"] = args.steps + args.warmup
             gbms = float(np.mean(per_gb))
             out["backward"]["gdn"] = {
                 "workload": "kda_gdn_chunk_bwd, log_alpha [T, H] = the first channel of the same draw",
                 "ms_per_step": gbms, "tokens_per_s": T / (gbms * 1e-3), "vs_kda_backward_ms": gbms / bms,
                 "workspace_bytes": ws.numel()}
             del g4
-        if not args.no_cpu_baseline:
+        if args.only is None and not args.no_cpu_baseline:
             out["backward"]["cpu_baseline"] = cpu_baseline_bwd(d, go, 2, 16384, H)
         del go, ws, a4
 
     # ---------------- decode step
-    if not args.no_decode:
+    if want("decode", args.no_decode):
         dcfg = I.C4
         S = I.make_decode_state(dcfg, device=dev)
         nst = args.decode_steps
@@ -495,6 +562,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / nst
+        calls["decode"] = min(3, nst) + nst
         db = decode_alg_bytes(dcfg.B, dcfg.H, dcfg.dk, dcfg.dv)
         gbs = db / (dms * 1e-3) / 1e9
         out["decode"] = {"workload": "kda_decode_step bf16 B=256 H=32 d=128 fp32 S (512 MiB), "
@@ -508,8 +576,10 @@ def main():
         del xs, S
 
     # ---------------- CPU baseline: the oracle on a bounded sample
-    if not args.no_cpu_baseline:
+    if args.only is None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_chunk(d, args.cpu_heads, args.cpu_tokens, H)
+    if args.only is not None:
+        out = {"only": args.only, "calls": calls.get(args.only), "entries": out}
     print(json.dumps(out), flush=True)
 
 
