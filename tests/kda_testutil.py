@@ -22,6 +22,23 @@ def errors(out, ref):
                 rel_max=float(np.abs(d).max() / np.abs(ref).max()) if d.size and np.abs(ref).max() > 0 else 0.0)
 
 
+def bf16_rounding_stats(out, ref):
+    """How bf16 outputs compare with the oracle rounded to bf16 (diagnostic
+    only; the tolerance is the one above): the share of elements equal to the
+    rounded oracle value, the largest error that rounding alone makes
+    (|rn(ref) - ref|, up to 3.9e-3 for |o| in [1, 2)), and the largest excess
+    of an element's error over that rounding error (|out - ref| - |rn(ref) - ref|),
+    i.e. the path's own arithmetic at its worst element."""
+    ref = f64(ref)
+    o = f64(out)
+    r = torch.as_tensor(ref).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    if o.size == 0:
+        return dict(exact=1.0, max_rounding=0.0, max_excess=0.0)
+    rnd = np.abs(r - ref)
+    exc = np.abs(o - ref) - rnd
+    return dict(exact=float((o == r).mean()), max_rounding=float(rnd.max()), max_excess=float(exc.max()))
+
+
 def assert_close(out, ref, io, what=""):
     e = errors(out, ref)
     if io == "bf16":

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from kda_testutil import assert_close, errors, f64, to_oracle
+from kda_testutil import assert_close, bf16_rounding_stats, errors, f64, to_oracle
 
 from gated_delta_rule_chunkwise_amd import inputs as I
 
@@ -52,7 +52,10 @@ def check_against_oracle(kda, d, io, seqs=None, heads=None, what=""):
     gh = hT[sq][:, hs]
     eo = assert_close(go, ro, io, what + " o")
     eh = assert_close(gh, rh, io, what + " h_T")
-    log(what, "o", eo, "h_T", eh)
+    if io == "bf16":
+        log(what, "o", eo, "h_T", eh, "o against the oracle rounded to bf16:", bf16_rounding_stats(go, ro))
+    else:
+        log(what, "o", eo, "h_T", eh)
     return eo, eh
 
 
