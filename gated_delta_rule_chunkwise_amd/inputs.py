@@ -13,7 +13,13 @@ Recipe (per token and head unless stated):
     0.5 and 0.9999), or the same uniform draw held constant over time per
     (head, channel) ("uniform_const", the long-memory variant);
   * h0 = N(0, 0.1^2) per sequence when requested, else absent (zeros);
-  * varlen lengths are integers drawn uniformly from [lo, hi] inclusive.
+  * varlen lengths are integers drawn uniformly from [lo, hi] inclusive, always
+    by the host's generator (seeded like the call), so that a batch drawn on
+    the GPU has the same lengths as the same batch drawn on the host; the
+    call's own generator takes the same draw too and discards it, so the
+    values that follow keep their stream.  (The host's and the GPU's
+    generators give different numbers for one seed: the same recipe drawn on
+    the two devices gives equally distributed but different values.)
 Draw order for one call: lengths, q, k, v, beta, log_alpha, h0.
 
 Raw projections (for the entry points with the input prologue) are the same
@@ -104,13 +110,15 @@ def draw_gate(shape, gate: str, g, device):
     raise ValueError("unknown gate " + gate)
 
 
-def seq_lengths(cfg: ChunkConfig, g=None, device="cpu"):
+def seq_lengths(cfg: ChunkConfig, g=None, device="cpu", seed: Optional[int] = None):
     if cfg.lengths is None:
         return [cfg.T] * cfg.B
     n, lo, hi = cfg.lengths
+    seed = cfg.seed if seed is None else seed
     if g is None:
-        g = _gen(cfg.seed, device)
-    return torch.randint(lo, hi + 1, (n,), generator=g, device=device).tolist()
+        g = _gen(seed, device)
+    torch.randint(lo, hi + 1, (n,), generator=g, device=device)   # the call's stream moves on
+    return torch.randint(lo, hi + 1, (n,), generator=_gen(seed, "cpu")).tolist()
 
 
 def make_chunk_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None,
@@ -121,7 +129,7 @@ def make_chunk_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = None
     seed = cfg.seed if seed is None else seed
     g = _gen(seed, device)
     if lengths is None:
-        lengths = seq_lengths(cfg, g, device)
+        lengths = seq_lengths(cfg, g, device, seed)
     gate = cfg.gate if gate is None else gate
     want_h0 = cfg.h0 if h0 is None else h0
     T = int(sum(lengths))
@@ -178,7 +186,7 @@ def make_chunk_raw_inputs(cfg: ChunkConfig, device="cpu", seed: Optional[int] = 
     seed = cfg.seed if seed is None else seed
     g = _gen(seed, device)
     if lengths is None:
-        lengths = seq_lengths(cfg, g, device)
+        lengths = seq_lengths(cfg, g, device, seed)
     want_h0 = cfg.h0 if h0 is None else h0
     T = int(sum(lengths))
     H, dk, dv = cfg.H, cfg.dk, cfg.dv
