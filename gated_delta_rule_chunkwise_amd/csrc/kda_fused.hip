@@ -42,13 +42,16 @@
 //
 // Segments.  A chain too long for the parallelism the GPU needs is cut into
 // segments.  The state at a segment's end is an affine map of the state at its
-// start, S_end = Phi S_start + S_loc.  A first kernel runs every segment but the
+// start, S_end = Phi S_start + S_loc.  A first kernel runs the first segment of
+// every chain exactly from h0 (its o, and its end state, which is the second
+// segment's start state), and beside it every segment but the first and the
 // last from the pair (S_loc, Phi) = (0, I) (waves 0-3 the d_v columns of S_loc,
 // waves 4-7 the d_k columns of Phi, the same chunk step with no value input for
-// Phi); a short scan from h0 gives each segment's start state; a last kernel runs
-// every segment from its start state and writes o and h_T.  Each column of S and
-// Phi evolves independently under the same chunk step, so this is the
-// recurrence regrouped, not approximated.
+// Phi); a short scan from the second segment's start state gives the start
+// states of the rest; a last kernel runs every segment but the first from its
+// start state and writes o and h_T.  The two launches then hold the same
+// number of workgroups.  Each column of S and Phi evolves independently under
+// the same chunk step, so this is the recurrence regrouped, not approximated.
 //
 // Precision.  The Gram products take K.e^{G-m} as single bf16 and Q.e^{G-m},
 // K.e^{m-G} as hi/lo bf16 pairs (about 2^-16 relative).  The diagonal blocks
@@ -144,13 +147,13 @@ struct FusedArgs {
     const int32_t *order;    // single pass: sequences by decreasing length, or null (natural order)
     void *o;
     float *h_T;
-    float *seg_in;           // [chains][nseg][DK*DV]  start state of each segment
-    float *seg_loc;          // [chains][nseg][DK*DV]  end state of a segment run from zero
-    float *seg_phi;          // [chains][nseg][DK*DK]  transition of a segment
+    float *seg_in;           // [chains][nseg - 1][DK*DV]  start state of segment 1 + i
+    float *seg_loc;          // [chains][nseg - 2][DK*DV]  end state of segment 1 + i run from zero
+    float *seg_phi;          // [chains][nseg - 2][DK*DK]  transition of segment 1 + i
     int64_t N, T;
     int32_t H;
     int32_t nseg, seg_chunks;
-    int32_t pass;            // 0: one pass; 1: window 1; 2: window 2
+    int32_t pass;            // 0: one pass; 1: first launch of a segmented call; 2: last launch
     float lo;
 };
 
@@ -172,13 +175,15 @@ __device__ __forceinline__ Task fused_task(const FusedArgs &a) {
         t.n = a.order ? (int64_t)a.order[r] : r;
         t.chain = t.n * a.H + t.h;
     } else {
-        if (a.pass == 1) {   // transitions of segments 0 .. nseg - 2
-            t.chain = id / (a.nseg - 1);
-            t.seg = (int)(id % (a.nseg - 1));
+        if (a.pass == 1 && id < chains) {   // segment 0 of chain id, exactly from h0
+            t.chain = id;
+        } else if (a.pass == 1) {           // transitions of segments 1 .. nseg - 2
+            t.chain = (id - chains) / (a.nseg - 2);
+            t.seg = 1 + (int)((id - chains) % (a.nseg - 2));
             t.phi = true;
-        } else {             // outputs of every segment
-            t.chain = id / a.nseg;
-            t.seg = (int)(id % a.nseg);
+        } else {                            // outputs of segments 1 .. nseg - 1
+            t.chain = id / (a.nseg - 1);
+            t.seg = 1 + (int)(id % (a.nseg - 1));
         }
         t.n = t.chain / a.H;
         t.h = (int)(t.chain % a.H);
@@ -1010,8 +1015,20 @@ __device__ __forceinline__ void chain_loop(FusedSmem<DK, DV> &sm, const FusedArg
     }
 }
 
-// Window 1 of a segmented call: every segment but the last runs from (S, Phi) =
-// (0, I) and stores its end state S_loc and its transition Phi.
+// A chain, or a segment of one, with o: every wave holds DV / 8 value columns
+// of the state (16 at d_v = 128), from src (or zero) to dst (if given).
+template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
+__device__ __forceinline__ void out_task(FusedSmem<DK, DV> &sm, const FusedArgs &a, const Task &tk, int w, int tid,
+                                         const float *src, float *dst) {
+    static_assert(DV == 128, "eight waves of 16 value columns");
+    chain_loop<DK, DV, IO, GT, PRO, GM, DEC, DV / 128, true, true, true>(sm, a, tk, w, tid, w * (DV / 8), src, false,
+                                                                         dst, DV, true);
+}
+
+// First launch of a segmented call: blocks below the chain count run segment
+// 0 of their chain exactly from h0 (o, and its end state as the start state of
+// segment 1); the others run segments 1 .. nseg - 2 from (S, Phi) = (0, I) and
+// store the end state S_loc and the transition Phi.
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kFT, 1) void fused_phi_kernel(const FusedArgs a) {
     typedef FusedSmem<DK, DV> Sm;
@@ -1021,7 +1038,12 @@ __global__ __launch_bounds__(kFT, 1) void fused_phi_kernel(const FusedArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Task tk = fused_task(a);
     const size_t sv = (size_t)DK * DV, sp = (size_t)DK * DK;
-    const int64_t slot = tk.chain * a.nseg + tk.seg;
+    if (!tk.phi) {
+        out_task<DK, DV, IO, GT, PRO, GM, DEC>(sm, a, tk, w, tid, a.h0 ? a.h0 + tk.chain * sv : nullptr,
+                                               a.seg_in + tk.chain * (a.nseg - 1) * sv);
+        return;
+    }
+    const int64_t slot = tk.chain * (a.nseg - 2) + (tk.seg - 1);
     if (w < 4)   // S from zero over the segment
         chain_loop<DK, DV, IO, GT, PRO, GM, DEC, DV / 64, false, true, true>(
             sm, a, tk, w, tid, w * (DV / 4), nullptr, false, a.seg_loc + slot * sv, DV, false);
@@ -1030,8 +1052,8 @@ __global__ __launch_bounds__(kFT, 1) void fused_phi_kernel(const FusedArgs a) {
             sm, a, tk, w, tid, (w - 4) * (DK / 4), nullptr, true, a.seg_phi + slot * sp, DK, false);
 }
 
-// One pass (pass 0) or window 2 (every segment from its start state): o, and
-// h_T at the end of the chain.  Every wave holds 16 value columns of the state.
+// One pass (pass 0), or the last launch of a segmented call (segments 1 ..
+// nseg - 1 from their start states): o, and h_T at the end of the chain.
 template <int DK, int DV, typename IO, typename GT, bool PRO, int GM, bool DEC>
 __global__ __launch_bounds__(kFT, 1) void fused_out_kernel(const FusedArgs a) {
     typedef FusedSmem<DK, DV> Sm;
@@ -1044,25 +1066,22 @@ __global__ __launch_bounds__(kFT, 1) void fused_out_kernel(const FusedArgs a) {
     const float *src;
     float *dst;
     if (a.pass == 2) {
-        src = tk.seg == 0 ? (a.h0 ? a.h0 + tk.chain * sv : nullptr) : a.seg_in + (tk.chain * a.nseg + tk.seg) * sv;
+        src = a.seg_in + (tk.chain * (a.nseg - 1) + (tk.seg - 1)) * sv;
         dst = (tk.seg == a.nseg - 1 && a.h_T) ? a.h_T + tk.chain * sv : nullptr;
     } else {
         src = a.h0 ? a.h0 + tk.chain * sv : nullptr;
         dst = a.h_T ? a.h_T + tk.chain * sv : nullptr;
     }
-    // every wave holds DV / 8 value columns of the state (16 at d_v = 128)
-    static_assert(DV == 128, "eight waves of 16 value columns");
-    chain_loop<DK, DV, IO, GT, PRO, GM, DEC, DV / 128, true, true, true>(sm, a, tk, w, tid, w * (DV / 8), src, false,
-                                                                         dst, DV, true);
+    out_task<DK, DV, IO, GT, PRO, GM, DEC>(sm, a, tk, w, tid, src, dst);
 }
 
-// Start states of segments 1 .. nseg - 1 of every chain:
-// S_in[s + 1] = Phi[s] S_in[s] + S_loc[s] for s = 0 .. nseg - 2, S_in[0] = h0 (or
-// zero), in fp32 on the fp32 matrix cores.  One workgroup per (chain, 16 value
-// columns): the columns are independent.
+// Start states of segments 2 .. nseg - 1 of every chain, from that of segment
+// 1 (the exact end state of segment 0):
+// S_in[s + 1] = Phi[s] S_in[s] + S_loc[s] for s = 1 .. nseg - 2, in fp32 on the
+// fp32 matrix cores.  One workgroup per (chain, 16 value columns): the columns
+// are independent.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__ h0, float *__restrict__ seg_in,
-                                                       const float *__restrict__ seg_loc,
+__global__ __launch_bounds__(256) void seg_scan_kernel(float *__restrict__ seg_in, const float *__restrict__ seg_loc,
                                                        const float *__restrict__ seg_phi, int nseg) {
     constexpr int NCB = DV / 16, MTW = DK / 64;   // row tiles per wave
     __shared__ float xin[DK][17];
@@ -1070,12 +1089,12 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__
     const int col0 = 16 * (int)(blockIdx.x % NCB);
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
     const size_t sv = (size_t)DK * DV, sp = (size_t)DK * DK;
-    for (int idx = tid; idx < DK * 16; idx += 256)
-        xin[idx >> 4][idx & 15] = h0 ? h0[chain * sv + (size_t)(idx >> 4) * DV + col0 + (idx & 15)] : 0.f;
-    for (int s = 0; s + 1 < nseg; ++s) {
+    const float *in1 = seg_in + chain * (nseg - 1) * sv;
+    for (int idx = tid; idx < DK * 16; idx += 256) xin[idx >> 4][idx & 15] = in1[(size_t)(idx >> 4) * DV + col0 + (idx & 15)];
+    for (int s = 1; s + 1 < nseg; ++s) {
         __syncthreads();
-        const float *phi = seg_phi + (chain * nseg + s) * sp;
-        const float *loc = seg_loc + (chain * nseg + s) * sv;
+        const float *phi = seg_phi + (chain * (nseg - 2) + (s - 1)) * sp;
+        const float *loc = seg_loc + (chain * (nseg - 2) + (s - 1)) * sv;
         f32x4_t acc[MTW];
 #pragma unroll
         for (int j = 0; j < MTW; ++j) {
@@ -1088,7 +1107,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__
                                                               xin[4 * kk + lg][lr], acc[j], 0, 0, 0);
         }
         __syncthreads();
-        float *out = seg_in + (chain * nseg + s + 1) * sv;
+        float *out = seg_in + (chain * (nseg - 1) + s) * sv;
 #pragma unroll
         for (int j = 0; j < MTW; ++j) {
             const int mt = wv + 4 * j;
@@ -1134,8 +1153,10 @@ FusedPlan fused_plan(const ChunkArgs &a) {
     p.nseg = 1;
     p.seg_chunks = 0;
     if (!a.varlen && p.chains > 0) {
+        // both launches of a segmented call run chains * (nseg - 1) <= target
+        // workgroups, one round on the chip
         const int64_t nch = (a.seq_len + kC - 1) / kC;
-        int64_t ns = (kFusedTargetBlocks + p.chains - 1) / p.chains;
+        int64_t ns = kFusedTargetBlocks / p.chains + 1;
         if (ns > nch / kMinSegChunks) ns = nch / kMinSegChunks;
         if (ns >= 3) {
             const int64_t sc = (nch + ns - 1) / ns;
@@ -1151,13 +1172,14 @@ FusedPlan fused_plan(const ChunkArgs &a) {
     p.order_off = off;
     if (p.order) off += plan_bytes(a.num_seqs);
     const size_t sv = (size_t)a.d_k * a.d_v * 4, sp = (size_t)a.d_k * a.d_k * 4;
-    const size_t slots = p.nseg >= 3 ? (size_t)p.chains * p.nseg : 0;
+    const size_t in_slots = p.nseg >= 3 ? (size_t)p.chains * (p.nseg - 1) : 0;
+    const size_t mid_slots = p.nseg >= 3 ? (size_t)p.chains * (p.nseg - 2) : 0;
     p.in_off = off;
-    off += slots * sv;
+    off += in_slots * sv;
     p.loc_off = off;
-    off += slots * sv;
+    off += mid_slots * sv;
     p.phi_off = off;
-    off += slots * sp;
+    off += mid_slots * sp;
     p.bytes = off;
     return p;
 }
@@ -1190,10 +1212,10 @@ hipError_t launch_fused_t(const ChunkArgs &a, hipStream_t st) {
     f.pass = 1;
     hipLaunchKernelGGL((fused_phi_kernel<DK, DV, IO, GT, PRO, GM, DEC>), dim3((unsigned)(p.chains * (p.nseg - 1))),
                        dim3(kFT), 0, st, f);
-    hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3((unsigned)(p.chains * (DV / 16))), dim3(256), 0, st, a.h0,
-                       f.seg_in, (const float *)f.seg_loc, (const float *)f.seg_phi, p.nseg);
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV>), dim3((unsigned)(p.chains * (DV / 16))), dim3(256), 0, st, f.seg_in,
+                       (const float *)f.seg_loc, (const float *)f.seg_phi, p.nseg);
     f.pass = 2;
-    hipLaunchKernelGGL((fused_out_kernel<DK, DV, IO, GT, PRO, GM, DEC>), dim3((unsigned)(p.chains * p.nseg)),
+    hipLaunchKernelGGL((fused_out_kernel<DK, DV, IO, GT, PRO, GM, DEC>), dim3((unsigned)(p.chains * (p.nseg - 1))),
                        dim3(kFT), 0, st, f);
     return hipGetLastError();
 }
@@ -1229,10 +1251,12 @@ bool fused_fwd_supported(const ChunkArgs &a) {
     return a.force_fused || a.varlen || a.prologue || a.w_write != nullptr;
 }
 
-// Chains are split only when ceil(target / chains) >= 3, i.e. chains < target / 2,
-// and then chains * nseg < target + chains < 1.5 target: the segment states of
-// any call fit the scratch of the forward that allocates nothing.
-static_assert((size_t)(kFusedTargetBlocks + kFusedTargetBlocks / 2) * 3 * 128 * 128 * 4 <= kNoAllocScratchBytes,
+// Chains are split only when nseg = floor(target / chains) + 1 >= 3, i.e. chains
+// <= target / 2, and then chains * (nseg - 1) <= target.  The segment states
+// take chains * (3 nseg - 5) = 3 chains (nseg - 1) - 2 chains < 3 target
+// matrices of d_k x d_v (or d_k x d_k) fp32: those of any call fit the scratch
+// of the forward that allocates nothing.
+static_assert((size_t)3 * kFusedTargetBlocks * 128 * 128 * 4 <= kNoAllocScratchBytes,
               "fused segment states exceed the no-allocation scratch");
 
 size_t fused_fwd_workspace_bytes(const ChunkArgs &a) { return fused_plan(a).bytes; }
@@ -1241,7 +1265,7 @@ size_t fused_fwd_workspace_bytes(const ChunkArgs &a) { return fused_plan(a).byte
 // workgroup per chain or segment), the sequence order and the segment scan.
 bool fused_fwd_grids_fit(const ChunkArgs &a) {
     const FusedPlan p = fused_plan(a);
-    if (!grid_fits(p.nseg >= 3 ? p.chains * p.nseg : p.chains, kFT)) return false;
+    if (!grid_fits(p.nseg >= 3 ? p.chains * (p.nseg - 1) : p.chains, kFT)) return false;
     if (p.order && !grid_fits((a.num_seqs + 255) / 256, 256)) return false;
     return p.nseg < 3 || grid_fits(p.chains * (a.d_v / 16), 256);
 }

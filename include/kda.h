@@ -86,8 +86,10 @@ const char *kda_last_hip_error(void);
  *    d_v = 64) runs instead in segments of half its chunks, at most 1024
  *    chunk-heads each, with two record buffers and the same fp32 state) and
  *    the fused kernel's segment states (a chain too long for
- *    the parallelism of the GPU is cut into segments: three d_k x d_v fp32
- *    matrices per segment, at most about 72 MiB in all);
+ *    the parallelism of the GPU is cut into segments: a start state for each
+ *    segment but the first, and an end state and a transition for each
+ *    segment but the first and the last, d_k x d_v or d_k x d_k fp32 each,
+ *    at most 48 MiB in all);
  *  - at d_k or d_v = 64 both kinds of batch run two passes (records as above).
  * The size depends only on the arguments, never on tensor contents.
  */
