@@ -463,6 +463,29 @@ def test_prologue_c3_full(kda):
     check_prologue_against_oracle(kda, d, "bf16", -30.0, what="prologue c3 all heads")
 
 
+@pytest.mark.parametrize("B,H,T", [(4, 32, 1024), (2, 43, 768), (1, 85, 1024), (3, 43, 512), (1, 2, 4096)])
+def test_fused_segment_plans(kda, B, H, T):
+    """Equal-length batches on raw projections (the fused kernel) across its
+    segment plans, h0 given: 128 chains (3 segments), 86 (3), 85 (4), 129 (one
+    pass) and 2 chains of 64 chunks (16 segments of 4 chunks).  A segmented
+    call runs each chain's first segment exactly from h0 beside the
+    transitions of the middle segments, then the rest from the scanned start
+    states."""
+    cfg = I.ChunkConfig("segplan", "bf16", "bf16", H=H, dk=128, dv=128, h0=True, seed=7100 + B * H)
+    d = I.make_chunk_raw_inputs(cfg, lengths=[T] * B)
+    lo = -30.0
+    as4 = lambda x: x.reshape(B, T, *x.shape[1:]).to(DEV)
+    o, hT = kda.kda_chunk_fwd_prologue(as4(d["q_raw"]), as4(d["k_raw"]), as4(d["v"]), as4(d["gate_pre"]),
+                                       as4(d["beta_pre"]), lo, h0=d["h0"].to(DEV))
+    torch.cuda.synchronize()
+    ref = to_oracle(_raw_as_plain(d))
+    ro, rh = oracle.fwd_prologue(ref["q"], ref["k"], ref["v"], ref["log_alpha"], ref["beta"], lo,
+                                 h0=ref["h0"], cu_seqlens=ref["cu_seqlens"])
+    eo = assert_close(o.cpu().reshape(B * T, H, 128), ro, "bf16", "segment plan %dx%dx%d o" % (B, H, T))
+    eh = assert_close(hT.cpu(), rh, "bf16", "segment plan %dx%dx%d h_T" % (B, H, T))
+    log("segment plan B=%d H=%d T=%d" % (B, H, T), "o", eo, "h_T", eh)
+
+
 def test_prologue_c1_shape_bf16(kda):
     """c1's shape (bf16, H=16, T=4096, d=128) on raw projections; gate
     pre-activations N(0, 2^2) with floor -3, so about 7% of gates sit on it."""
