@@ -190,17 +190,21 @@ template <int DK> struct BigNumbering {
 //   A[r,i] += beta_r sum_c k_rc k_ic e^{G_rc - G_ic}  (i < r)
 //   P[r,i] +=        sum_c q_rc k_ic e^{G_rc - G_ic}  (i <= r)
 // every factor at most 1, taken 16 channels at a time from fp32 [64][16] rows of
-// G (log2 units), K and Q, so one fast-forgetting channel costs one channel's
-// pairs.  With at most 16 big channels the rows were staged in the area of A
+// G (log2 units), K and Q (row pitch kXS = 17 floats, so that the lanes of a
+// wave, which take consecutive columns i of one row r, read distinct banks),
+// so one fast-forgetting channel costs one channel's pairs.  With at most 16 big channels the rows were staged in the area of A
 // during operand formation, from the registers that held them; otherwise each
 // group is staged here over the area of QA from the inputs (G by one wave-wide
 // inclusive scan of the chunk's gates).  The sums are left in the area of QA as
-// a 64x64 fp32 matrix: the A part (without beta) below the diagonal, the P part
-// on and above it (transposed), for the Gram epilogue.  Called by every wave
+// a 64x64 fp32 matrix of row pitch kSS = 65: the A part (without beta) below
+// the diagonal, the P part on and above it (transposed), for the Gram epilogue.  Called by every wave
 // after the Gram operands are consumed; returns after a barrier.
 // PAIRED: two chunk-heads share the workgroup (and its barriers), so every
 // barrier here is taken for nbU channels, the larger count of the two; a half
 // with fewer (or none) does empty work between them.
+constexpr int kXS = 17;       // row pitch (floats) of the staged G, K, Q rows of the big channels
+constexpr int kSS = kC + 1;   // row pitch (floats) of the exact pair sums
+
 template <int DK, bool PRO, int GM, bool PAIRED, typename Sm, typename IO, typename GT>
 __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64], const BigNumbering<DK> &bn, int nbU,
                                             const IO *__restrict__ q, const IO *__restrict__ k,
@@ -211,15 +215,27 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
     const bool staged = nb <= 16;
     const bool bars = PAIRED || !staged;   // the staging barriers are taken
     float *xG = staged ? reinterpret_cast<float *>(&sm.A[0][0]) : reinterpret_cast<float *>(&sm.t);
-    float *xK = xG + kC * 16, *xQ = xK + kC * 16;
+    float *xK = xG + kC * kXS, *xQ = xK + kC * kXS;
     float *xS = reinterpret_cast<float *>(&sm.t);
-    static_assert(kC * kC * 4 <= sizeof(sm.t), "staging and sums fit in the area of QA");
-    static_assert(3 * kC * 16 * 4 <= sizeof(sm.A), "staging fits in the area of A");
+    static_assert(kC * kSS * 4 <= sizeof(sm.t) && 3 * kC * kXS * 4 <= sizeof(sm.t),
+                  "staging and sums fit in the area of QA");
+    static_assert(3 * kC * kXS * 4 <= sizeof(sm.A), "staging fits in the area of A");
     const int64_t rp = (int64_t)H * DK;   // row pitch of q, k and per-channel gates
     constexpr int NPAIR = kC * (kC + 1) / 2, PPT = (NPAIR + kThreads - 1) / kThreads;
     float sA[PPT], sP[PPT];
+    int pr[PPT], pc[PPT];   // the pairs (r, i) of this thread, p = tid + kThreads j
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) sA[j] = sP[j] = 0.f;
+    for (int j = 0; j < PPT; ++j) {
+        sA[j] = sP[j] = 0.f;
+        const int p = tid + kThreads * j;
+        // r = floor((sqrt(8p + 1) - 1) / 2), from the hardware square root and
+        // corrected by one either way
+        int r = (int)((__builtin_amdgcn_sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+        if ((r + 1) * (r + 2) / 2 <= p) ++r;
+        if (r * (r + 1) / 2 > p) --r;
+        pr[j] = r;
+        pc[j] = p - r * (r + 1) / 2;
+    }
     int32_t *chan = sm.chan;   // the channel of number g0 + j
 #pragma unroll 1
     for (int g0 = 0; g0 < nbU; g0 += 16) {
@@ -253,12 +269,12 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
                         const float y = __shfl_up(x, d);
                         if (l >= d) x += y;
                     }
-                    xG[l * 16 + j] = x;
+                    xG[l * kXS + j] = x;
                 }
             }
             // K and Q (with the input prologue: times the rows' inverse norms)
             for (int e = tid; e < kC * 16; e += kThreads) {
-                const int r = e >> 4, j = e & 15;
+                const int r = e >> 4, j = e & 15, x = r * kXS + j;
                 float kv = 0.f, qv = 0.f;
                 if (r < nv && j < cnt) {
                     const int64_t o = (t0 + r) * rp + (int64_t)h * DK + chan[j];
@@ -269,8 +285,8 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
                         kv *= sm.nrm[1][r];
                     }
                 }
-                xK[e] = kv;
-                xQ[e] = qv;
+                xK[x] = kv;
+                xQ[x] = qv;
             }
             }
             lds_barrier();
@@ -278,16 +294,13 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
             const int p = tid + kThreads * j;
-            int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-            if ((r + 1) * (r + 2) / 2 <= p) ++r;
-            if (r * (r + 1) / 2 > p) --r;
-            const int i = p - r * (r + 1) / 2;
+            const int r = pr[j], i = pc[j];
             if (p < NPAIR && r < nv) {
                 float a = 0.f, b = 0.f;
                 for (int c = 0; c < cnt; ++c) {
-                    const float kk = xK[i * 16 + c] * kexp2<false>(xG[r * 16 + c] - xG[i * 16 + c]);
-                    a += xK[r * 16 + c] * kk;
-                    b += xQ[r * 16 + c] * kk;
+                    const float kk = xK[i * kXS + c] * kexp2<false>(xG[r * kXS + c] - xG[i * kXS + c]);
+                    a += xK[r * kXS + c] * kk;
+                    b += xQ[r * kXS + c] * kk;
                 }
                 sA[j] += a;
                 sP[j] += b;
@@ -299,15 +312,12 @@ __device__ __forceinline__ void exact_pairs(Sm &sm, const bool (&bigc)[DK / 64],
     for (int j = 0; j < PPT; ++j) {
         const int p = tid + kThreads * j;
         if (p < NPAIR) {
-            int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-            if ((r + 1) * (r + 2) / 2 <= p) ++r;
-            if (r * (r + 1) / 2 > p) --r;
-            const int i = p - r * (r + 1) / 2;
+            const int r = pr[j], i = pc[j];
             if (i < r) {
-                xS[r * kC + i] = sA[j];
-                xS[i * kC + r] = sP[j];
+                xS[r * kSS + i] = sA[j];
+                xS[i * kSS + r] = sP[j];
             } else {
-                xS[r * kC + r] = sP[j];
+                xS[r * kSS + r] = sP[j];
             }
         }
     }
@@ -438,7 +448,7 @@ __device__ __forceinline__ void prep_body(
     if (anybig) {
         if (bn.nb <= 16) {   // stage the big channels' G, K, Q rows for the exact pairs
             float *xG = reinterpret_cast<float *>(&sm.A[0][0]);
-            float *xK = xG + kC * 16, *xQ = xK + kC * 16;
+            float *xK = xG + kC * kXS, *xQ = xK + kC * kXS;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 if (bigc[cc]) {
@@ -447,9 +457,9 @@ __device__ __forceinline__ void prep_body(
                     for (int i = 0; i < 8; ++i) {
                         const int r = 8 * w + i;
                         const bool valid = r < nv;
-                        xG[r * 16 + j] = csum[i][cc];
-                        xK[r * 16 + j] = valid ? in.kval(i, cc) : 0.f;
-                        xQ[r * 16 + j] = valid ? in.qval(i, cc) : 0.f;
+                        xG[r * kXS + j] = csum[i][cc];
+                        xK[r * kXS + j] = valid ? in.kval(i, cc) : 0.f;
+                        xQ[r * kXS + j] = valid ? in.qval(i, cc) : 0.f;
                     }
                 }
             }
@@ -579,7 +589,7 @@ __device__ __forceinline__ void prep_body(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * R + 4 * lg + e;
-                    float x = anybig ? acc[e] + xS[r * kC + i] : acc[e];
+                    float x = anybig ? acc[e] + xS[r * kSS + i] : acc[e];
                     if constexpr (SG) x *= kexp2<false>(sm.gs[r] - sm.gs[i]);   // at most 1 for i < r
                     sm.A[r][i] = (i < r) ? sm.beta[r] * x : 0.f;
                 }
@@ -590,7 +600,7 @@ __device__ __forceinline__ void prep_body(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 16 * I + 4 * lg + e;
-                    float y = anybig ? acc[e] + xS[i * kC + r] : acc[e];
+                    float y = anybig ? acc[e] + xS[i * kSS + r] : acc[e];
                     if constexpr (SG) y *= kexp2<false>(sm.gs[r] - sm.gs[i]);   // at most 1 for i <= r
                     x[e] = (i <= r) ? y : 0.f;
                 }
